@@ -1,0 +1,117 @@
+"""Seeded synthetic workloads for the gated linear attention forward pass.
+
+This module only draws random inputs; it holds none of the method's arithmetic and is
+shared by the GPU tests, the oracle tests and the benchmark.  Every tensor is drawn on
+the CPU with a ``torch.Generator`` seeded explicitly, so the same (workload, seed) gives
+the same bytes on any machine.
+
+Recipe (per workload): draw ``q``, ``k``, ``v`` in that order as fp32 N(0, 1), divide by
+``sqrt(scale_dim)`` in fp32, and round to the input dtype (bf16 rounds to nearest even);
+then draw the gate pre-activations.  Gates are stored as fp32 logs:
+
+* ``channel``: ``log_alpha = logsigmoid(x) / 16``, ``x ~ N(0, 1)``, ``[B, H, L, Dk]``.
+* ``head_const``: ``log_alpha[h] = log(1 - 2^(-5-h))`` rounded to fp32, ``[H]``
+  (a fixed decay per head, RetNet style).
+* ``head``: ``log_alpha = logsigmoid(a)``, ``a ~ N(3, 1)``, ``[B, H, L]`` and the input
+  gate ``log_ig = logsigmoid(b)``, ``b ~ N(0, 1)``, ``[B, H, L]`` (sigmoid forget and
+  input gates of the mLSTM variant).
+* ``none``: no gate.
+"""
+from __future__ import annotations
+
+import hashlib
+import math
+from dataclasses import dataclass, replace
+from typing import Optional
+
+import torch
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    L: int
+    Dk: int
+    Dv: int
+    chunk: int
+    dtype: str = "bf16"          # q, k, v dtype: "bf16" or "f32"
+    gate: str = "none"           # none | channel | head | head_const
+    input_gate: bool = False     # log input gate [B, H, L]
+    scale_dim: Optional[int] = None  # inputs are N(0,1)/sqrt(scale_dim); default Dk
+    final_state: bool = True
+    gate_shift: float = 3.0      # mean of the forget pre-activation for gate == "head"
+    channel_gate_div: float = 16.0
+
+    def with_(self, **kw) -> "Workload":
+        return replace(self, **kw)
+
+    @property
+    def head_tokens(self) -> int:
+        return self.B * self.H * self.L
+
+
+# The five workloads the method is measured on (sizes, dtypes, gate kinds and chunk sizes).
+WORKLOADS = {
+    "ungated_f32_L256": Workload("ungated_f32_L256", 1, 1, 256, 64, 64, 64, dtype="f32", gate="none"),
+    "gla_bf16_B8H16L2048": Workload("gla_bf16_B8H16L2048", 8, 16, 2048, 128, 128, 64, gate="channel"),
+    "retnet_bf16_B4H8L8192": Workload("retnet_bf16_B4H8L8192", 4, 8, 8192, 128, 128, 128, gate="head_const"),
+    "long_gla_bf16_H16L32768_C64": Workload("long_gla_bf16_H16L32768_C64", 1, 16, 32768, 128, 128, 64,
+                                             gate="channel"),
+    "long_gla_bf16_H16L32768_C256": Workload("long_gla_bf16_H16L32768_C256", 1, 16, 32768, 128, 128, 256,
+                                              gate="channel"),
+    "mlstm_sig_bf16_B8H8L8192": Workload("mlstm_sig_bf16_B8H8L8192", 8, 8, 8192, 256, 512, 256, gate="head",
+                                          input_gate=True, scale_dim=256),
+}
+HEADLINE = "gla_bf16_B8H16L2048"
+
+
+def _dt(name: str):
+    return {"bf16": torch.bfloat16, "f32": torch.float32}[name]
+
+
+def make_inputs(w: Workload, seed: int = 0, device="cpu") -> dict:
+    """Draw the inputs of workload ``w``.  Returns a dict with ``q, k, v`` (input dtype),
+    ``log_alpha`` (fp32 or None), ``log_ig`` (fp32 or None) and ``sha256`` of all bytes."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    B, H, L, Dk, Dv = w.B, w.H, w.L, w.Dk, w.Dv
+    sd = float(w.scale_dim or Dk)
+    div = torch.tensor(math.sqrt(sd), dtype=torch.float32)
+    dt = _dt(w.dtype)
+    q = (torch.randn(B, H, L, Dk, generator=g, dtype=torch.float32) / div).to(dt)
+    k = (torch.randn(B, H, L, Dk, generator=g, dtype=torch.float32) / div).to(dt)
+    v = (torch.randn(B, H, L, Dv, generator=g, dtype=torch.float32) / div).to(dt)
+    la = None
+    li = None
+    if w.gate == "channel":
+        x = torch.randn(B, H, L, Dk, generator=g, dtype=torch.float32)
+        la = torch.nn.functional.logsigmoid(x) / w.channel_gate_div
+    elif w.gate == "head_const":
+        la = torch.tensor([math.log1p(-(2.0 ** (-5 - h))) for h in range(H)], dtype=torch.float64).float()
+    elif w.gate == "head":
+        a = torch.randn(B, H, L, generator=g, dtype=torch.float32) + w.gate_shift
+        la = torch.nn.functional.logsigmoid(a)
+    elif w.gate != "none":
+        raise ValueError(w.gate)
+    if w.input_gate:
+        b = torch.randn(B, H, L, generator=g, dtype=torch.float32)
+        li = torch.nn.functional.logsigmoid(b)
+    h = hashlib.sha256()
+    for t in (q, k, v, la, li):
+        if t is not None:
+            h.update(t.contiguous().view(torch.uint8).numpy().tobytes() if t.dtype != torch.bfloat16
+                     else t.contiguous().view(torch.int16).numpy().tobytes())
+    out = dict(q=q, k=k, v=v, log_alpha=la, log_ig=li, sha256=h.hexdigest())
+    if device != "cpu":
+        for key in ("q", "k", "v", "log_alpha", "log_ig"):
+            if out[key] is not None:
+                out[key] = out[key].to(device)
+    return out
+
+
+def custom(B, H, L, Dk, Dv, chunk, dtype="bf16", gate="channel", input_gate=False, **kw) -> Workload:
+    """A workload of arbitrary shape with the same value distributions."""
+    return Workload("custom_B%dH%dL%dDk%dDv%dC%d_%s_%s" % (B, H, L, Dk, Dv, chunk, dtype, gate), B, H, L, Dk,
+                    Dv, chunk, dtype=dtype, gate=gate, input_gate=input_gate, **kw)

@@ -1,0 +1,3 @@
+"""fp64 CPU oracle for the gated linear attention forward pass (test infrastructure only)."""
+from .oracle import (GATE_KINDS, build, bruteforce_ungated, chunkwise_form, expand_gate,  # noqa: F401
+                     final_state_closed_form, load_library, parallel_form, recurrent, threads)

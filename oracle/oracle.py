@@ -1,0 +1,236 @@
+"""fp64 oracle for the gated linear attention forward pass.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this module.  The GPU library never
+imports, links or calls it, and it imports nothing from the GPU library.
+
+Forms (all fp64, computed from the exact input values):
+
+* :func:`recurrent` -- the definition: the token recurrence
+  ``S_t = diag(alpha_t) S_{t-1} + i_t k_t^T v_t``, ``o_t = q_t S_t`` in plain C
+  (``gla_oracle.c``).  A matrix-valued state updated by one rank-1 write and read by one
+  vector-matrix product per token [Hardware-Efficient Training of Linear Attention Models,
+  talk summary, 4:04 and 7:36]; gates as the data-dependent generalisation [Gated Linear
+  Attention Transformers with Hardware-Efficient Training, abstract].
+* :func:`parallel_form` -- the quadratic ("parallel") form of the same map: causal
+  pairwise scores times values, with the gate entering as a per-channel decay between the
+  two positions [talk summary, 7:36].  Tiny inputs only.
+* :func:`chunkwise_form` -- the chunkwise algorithm written plainly: split the sequence
+  into chunks of ``C`` tokens, carry the state only across chunk boundaries, and inside
+  a chunk add the masked pairwise term [talk summary, 11:58; Tiled Flash Linear
+  Attention, abstract, for arbitrary chunk sizes].  Tiny inputs only.
+* :func:`bruteforce_ungated` -- causal sums ``o_t = sum_{s<=t} (q_t . k_s) v_s`` in
+  Python loops, the textbook ungated case.  Tiny inputs only.
+
+Gate kinds (how a stored gate broadcasts to the per-channel log decay):
+``"none"`` (zero), ``"channel"`` ``[B,H,L,Dk]``, ``"head"`` ``[B,H,L]`` (one decay per
+head and token), ``"head_const"`` ``[H]`` (one fixed decay per head).  The optional input
+gate ``log_ig`` is ``[B,H,L]``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "gla_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lock = threading.Lock()
+_lib = None
+
+GATE_KINDS = ("none", "channel", "head", "head_const")
+
+
+def build(force: bool = False) -> str:
+    """Compile ``gla_oracle.c`` into ``liboracle.so`` with gcc (CPU only)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-shared", "-fPIC", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def load_library(path: str):
+    """Open a compiled oracle library at ``path`` and declare its signatures."""
+    lib = ctypes.CDLL(path)
+    dp = ctypes.POINTER(ctypes.c_double)
+    lib.gla_oracle_recurrent.argtypes = [dp, dp, dp, dp, dp, dp, dp, dp] + [ctypes.c_long] * 5
+    lib.gla_oracle_recurrent.restype = ctypes.c_int
+    lib.gla_oracle_threads.restype = ctypes.c_int
+    lib.gla_oracle_threads.argtypes = []
+    return lib
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            _lib = load_library(build())
+    return _lib
+
+
+def threads() -> int:
+    """OpenMP threads :func:`recurrent` runs on."""
+    return int(_load().gla_oracle_threads())
+
+
+def _f64(x):
+    """Exact conversion of a torch tensor (bf16/fp32/fp64) or array to a C-contiguous fp64 array."""
+    if x is None:
+        return None
+    if hasattr(x, "detach"):  # torch tensor: bf16 -> fp32 -> fp64 is exact
+        import torch
+
+        x = x.detach().to("cpu")
+        if x.dtype == torch.bfloat16 or x.dtype == torch.float16:
+            x = x.float()
+        x = x.double().numpy()
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def expand_gate(gate_kind: str, log_alpha, B: int, H: int, L: int, Dk: int) -> np.ndarray:
+    """Broadcast a stored log gate to the per-channel log decay ``[B,H,L,Dk]`` (fp64)."""
+    if gate_kind not in GATE_KINDS:
+        raise ValueError("unknown gate kind %r" % (gate_kind,))
+    if gate_kind == "none":
+        return np.zeros((B, H, L, Dk))
+    a = _f64(log_alpha)
+    if gate_kind == "channel":
+        assert a.shape == (B, H, L, Dk), a.shape
+        return a
+    if gate_kind == "head":
+        assert a.shape == (B, H, L), a.shape
+        return np.ascontiguousarray(np.broadcast_to(a[..., None], (B, H, L, Dk)))
+    assert a.shape == (H,), a.shape
+    return np.ascontiguousarray(np.broadcast_to(a[None, :, None, None], (B, H, L, Dk)))
+
+
+def recurrent(q, k, v, gate_kind="none", log_alpha=None, log_ig=None, initial_state=None, lib=None):
+    """The definition, in C: returns ``(out [B,H,L,Dv], final_state [B,H,Dk,Dv])`` in fp64.
+    ``lib`` selects another compiled copy of the oracle (used by tests that plant a mistake
+    in a copy of the C source to show the pins catch it)."""
+    q64, k64, v64 = _f64(q), _f64(k), _f64(v)
+    B, H, L, Dk = q64.shape
+    Dv = v64.shape[-1]
+    assert k64.shape == q64.shape and v64.shape == (B, H, L, Dv)
+    la = expand_gate(gate_kind, log_alpha, B, H, L, Dk)
+    li = _f64(log_ig)
+    if li is not None:
+        assert li.shape == (B, H, L)
+    s0 = _f64(initial_state)
+    if s0 is not None:
+        assert s0.shape == (B, H, Dk, Dv)
+    out = np.empty((B, H, L, Dv))
+    fin = np.empty((B, H, Dk, Dv))
+    dp = ctypes.POINTER(ctypes.c_double)
+
+    def p(a):
+        return None if a is None else a.ctypes.data_as(dp)
+
+    rc = (lib or _load()).gla_oracle_recurrent(p(q64), p(k64), p(v64), p(la), p(li), p(s0), p(out), p(fin),
+                                      B, H, L, Dk, Dv)
+    if rc != 0:
+        raise RuntimeError("gla_oracle_recurrent failed (%d)" % rc)
+    return out, fin
+
+
+def parallel_form(q, k, v, gate_kind="none", log_alpha=None, log_ig=None, initial_state=None):
+    """Quadratic form: ``o_t = sum_{s<=t} sum_d q_td k_sd exp(G_td - G_sd) i_s v_s
+    + (q_t * exp(G_t)) S0``, where ``G`` is the inclusive running sum of the log decay
+    from the start of the sequence.  Per-channel gates make the mask carry a channel
+    index, so the pairwise score keeps its sum over ``d`` inside the decay.
+    Returns ``out`` only (fp64).  O(L^2 Dk): tiny inputs."""
+    q64, k64, v64 = _f64(q), _f64(k), _f64(v)
+    B, H, L, Dk = q64.shape
+    la = expand_gate(gate_kind, log_alpha, B, H, L, Dk)
+    ig = np.ones((B, H, L)) if log_ig is None else np.exp(_f64(log_ig))
+    G = np.cumsum(la, axis=2)  # [B,H,L,Dk]
+    out = np.zeros(v64.shape)
+    causal = np.tril(np.ones((L, L), dtype=bool))
+    for b in range(B):
+        for h in range(H):
+            # decay[t, s, d] = exp(G_td - G_sd), only used where s <= t (so the exponent is <= 0
+            # for gates <= 0); the upper triangle is masked before the exponent is taken.
+            diff = G[b, h][:, None, :] - G[b, h][None, :, :]
+            diff = np.where(causal[:, :, None], diff, -np.inf)
+            scores = np.einsum("td,sd,tsd->ts", q64[b, h], k64[b, h], np.exp(diff))
+            out[b, h] = (scores * ig[b, h][None, :]) @ v64[b, h]
+            if initial_state is not None:
+                s0 = _f64(initial_state)[b, h]
+                out[b, h] += (q64[b, h] * np.exp(G[b, h])) @ s0
+    return out
+
+
+def chunkwise_form(q, k, v, chunk: int, gate_kind="none", log_alpha=None, log_ig=None,
+                   initial_state=None):
+    """Chunkwise algorithm, plainly: for each chunk of ``chunk`` tokens (the last may be
+    shorter), with ``b`` the inclusive running sum of the log decay inside the chunk and
+    ``g`` its value at the chunk's last token:
+
+        o_t   = (q_t * exp(b_t)) S_in + sum_{s<=t in chunk} [sum_d q_td k_sd exp(b_td - b_sd)] i_s v_s
+        S_out = diag(exp(g)) S_in + sum_{s in chunk} (k_s * exp(g - b_s))^T i_s v_s
+
+    Returns ``(out, final_state)`` in fp64."""
+    q64, k64, v64 = _f64(q), _f64(k), _f64(v)
+    B, H, L, Dk = q64.shape
+    Dv = v64.shape[-1]
+    la = expand_gate(gate_kind, log_alpha, B, H, L, Dk)
+    ig = np.ones((B, H, L)) if log_ig is None else np.exp(_f64(log_ig))
+    out = np.zeros((B, H, L, Dv))
+    fin = np.zeros((B, H, Dk, Dv))
+    s0 = None if initial_state is None else _f64(initial_state)
+    for b_ in range(B):
+        for h in range(H):
+            S = np.zeros((Dk, Dv)) if s0 is None else s0[b_, h].copy()
+            for c0 in range(0, L, chunk):
+                c1 = min(L, c0 + chunk)
+                qc, kc, vc = q64[b_, h, c0:c1], k64[b_, h, c0:c1], v64[b_, h, c0:c1]
+                ic = ig[b_, h, c0:c1]
+                bcum = np.cumsum(la[b_, h, c0:c1], axis=0)  # [n, Dk]
+                g = bcum[-1]
+                n = c1 - c0
+                inter = (qc * np.exp(bcum)) @ S
+                intra = np.zeros((n, Dv))
+                for t in range(n):
+                    for s in range(t + 1):
+                        score = np.sum(qc[t] * kc[s] * np.exp(bcum[t] - bcum[s]))
+                        intra[t] += score * ic[s] * vc[s]
+                out[b_, h, c0:c1] = inter + intra
+                S = np.exp(g)[:, None] * S + ((kc * np.exp(g[None, :] - bcum)) * ic[:, None]).T @ vc
+            fin[b_, h] = S
+    return out, fin
+
+
+def bruteforce_ungated(q, k, v):
+    """Ungated causal sums ``o_t = sum_{s<=t} (q_t . k_s) v_s`` with Python loops (fp64)."""
+    q64, k64, v64 = _f64(q), _f64(k), _f64(v)
+    B, H, L, Dk = q64.shape
+    Dv = v64.shape[-1]
+    out = np.zeros((B, H, L, Dv))
+    for b in range(B):
+        for h in range(H):
+            for t in range(L):
+                acc = [0.0] * Dv
+                for s in range(t + 1):
+                    dot = 0.0
+                    for d in range(Dk):
+                        dot += float(q64[b, h, t, d]) * float(k64[b, h, s, d])
+                    for c in range(Dv):
+                        acc[c] += dot * float(v64[b, h, s, c])
+                out[b, h, t] = acc
+    return out
+
+
+def final_state_closed_form(k, v, gate_kind="none", log_alpha=None, log_ig=None):
+    """``S_L = sum_t diag(exp(G_{L-1} - G_t)) i_t k_t^T v_t`` (zero initial state), fp64."""
+    k64, v64 = _f64(k), _f64(v)
+    B, H, L, Dk = k64.shape
+    la = expand_gate(gate_kind, log_alpha, B, H, L, Dk)
+    ig = np.ones((B, H, L)) if log_ig is None else np.exp(_f64(log_ig))
+    G = np.cumsum(la, axis=2)
+    w = np.exp(G[:, :, -1:, :] - G) * ig[..., None]  # [B,H,L,Dk]
+    return np.einsum("bhtd,bhtc->bhdc", k64 * w, v64)
