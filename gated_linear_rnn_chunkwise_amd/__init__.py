@@ -1,0 +1,209 @@
+"""Chunkwise gated linear attention forward pass for AMD MI355X (gfx950).
+
+A thin ctypes binding over the C ABI of ``libgla.so`` (declared in ``include/gla.h``):
+this module only marshals arguments (device pointers, sizes, the current HIP stream);
+every step of the computation runs in the library's HIP kernels.  PyTorch supplies device
+memory and streams.  If the built library is missing, :func:`load` raises: there is no
+fallback implementation.
+
+    import gated_linear_rnn_chunkwise_amd as gla
+    out, final_state = gla.fwd(q, k, v, log_alpha, chunk=64)
+
+Gate kinds follow the shape of ``log_alpha``: ``None`` (ungated), ``[B,H,L,Dk]``
+(per channel), ``[B,H,L]`` (per head and token) or ``[H]`` (fixed per head).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import Optional
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgla.so")
+
+GLA_OK, GLA_ERR_INVALID_ARG, GLA_ERR_UNSUPPORTED, GLA_ERR_WORKSPACE, GLA_ERR_HIP = 0, -1, -2, -3, -4
+DTYPE_BF16, DTYPE_F32 = 0, 1
+GATE_NONE, GATE_CHANNEL, GATE_HEAD, GATE_HEAD_CONST = 0, 1, 2, 3
+GATE_NAMES = {"none": GATE_NONE, "channel": GATE_CHANNEL, "head": GATE_HEAD, "head_const": GATE_HEAD_CONST}
+
+# Entry points declared in include/gla.h.
+EXPORTS = ("gla_fwd", "gla_fwd_ex", "gla_workspace_size", "gla_query_plan", "gla_status_string", "gla_version")
+
+
+class GlaDesc(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int32), ("H", ctypes.c_int32), ("L", ctypes.c_int32), ("Dk", ctypes.c_int32),
+        ("Dv", ctypes.c_int32), ("chunk", ctypes.c_int32), ("in_dtype", ctypes.c_int32),
+        ("gate_kind", ctypes.c_int32),
+        ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+        ("log_alpha", ctypes.c_void_p), ("log_ig", ctypes.c_void_p), ("initial_state", ctypes.c_void_p),
+        ("out", ctypes.c_void_p), ("final_state", ctypes.c_void_p),
+        ("seg_chunks", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+class GlaPlan(ctypes.Structure):
+    _fields_ = [
+        ("seg_chunks", ctypes.c_int32), ("n_seg", ctypes.c_int32), ("dv_tiles", ctypes.c_int32),
+        ("tiles_per_chunk", ctypes.c_int32), ("grid_state", ctypes.c_int32), ("grid_scan", ctypes.c_int32),
+        ("grid_out", ctypes.c_int32), ("reserved", ctypes.c_int32), ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+class GlaError(RuntimeError):
+    def __init__(self, status: int, what: str = ""):
+        self.status = status
+        super().__init__("%s: %s (status %d)" % (what or "gla", status_string(status), status))
+
+
+_lock = threading.Lock()
+_lib = None
+
+
+def load(path: str = LIB_PATH):
+    """Load ``libgla.so`` (built by ``gated_linear_rnn_chunkwise_amd.build``); raises if it is missing."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(path):
+            raise RuntimeError("libgla.so not built: run `python -m gated_linear_rnn_chunkwise_amd.build` "
+                               "(expected at %s)" % path)
+        lib = ctypes.CDLL(path)
+        vp, i32 = ctypes.c_void_p, ctypes.c_int
+        lib.gla_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]
+        lib.gla_fwd.restype = i32
+        lib.gla_fwd_ex.argtypes = [ctypes.POINTER(GlaDesc), vp]
+        lib.gla_fwd_ex.restype = i32
+        lib.gla_workspace_size.argtypes = [ctypes.POINTER(GlaDesc), ctypes.POINTER(ctypes.c_size_t)]
+        lib.gla_workspace_size.restype = i32
+        lib.gla_query_plan.argtypes = [ctypes.POINTER(GlaDesc), ctypes.POINTER(GlaPlan)]
+        lib.gla_query_plan.restype = i32
+        lib.gla_status_string.argtypes = [i32]
+        lib.gla_status_string.restype = ctypes.c_char_p
+        lib.gla_version.argtypes = []
+        lib.gla_version.restype = i32
+        _lib = lib
+        return lib
+
+
+def status_string(status: int) -> str:
+    return load().gla_status_string(int(status)).decode()
+
+
+def version() -> int:
+    return int(load().gla_version())
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return int(t.data_ptr())
+
+
+def gate_kind_of(log_alpha, B: int, H: int, L: int, Dk: int) -> int:
+    if log_alpha is None:
+        return GATE_NONE
+    shape = tuple(log_alpha.shape)
+    if shape == (B, H, L, Dk):
+        return GATE_CHANNEL
+    if shape == (B, H, L):
+        return GATE_HEAD
+    if shape == (H,):
+        return GATE_HEAD_CONST
+    raise ValueError("log_alpha shape %s matches no gate layout for B=%d H=%d L=%d Dk=%d" % (shape, B, H, L, Dk))
+
+
+def make_desc(q, k, v, log_alpha=None, log_ig=None, initial_state=None, out=None, final_state=None, chunk=64,
+              seg_chunks=0, workspace=None, workspace_bytes=0, gate_kind=None) -> GlaDesc:
+    """Fill a :class:`GlaDesc` from tensors (shapes read from q and v)."""
+    import torch
+
+    B, H, L, Dk = q.shape
+    Dv = v.shape[-1]
+    d = GlaDesc()
+    d.B, d.H, d.L, d.Dk, d.Dv, d.chunk = B, H, L, Dk, Dv, int(chunk)
+    if q.dtype == torch.bfloat16:
+        d.in_dtype = DTYPE_BF16
+    elif q.dtype == torch.float32:
+        d.in_dtype = DTYPE_F32
+    else:
+        raise TypeError("q, k, v must be bf16 or fp32, got %s" % q.dtype)
+    d.gate_kind = gate_kind_of(log_alpha, B, H, L, Dk) if gate_kind is None else int(gate_kind)
+    d.q, d.k, d.v = _ptr(q), _ptr(k), _ptr(v)
+    d.log_alpha, d.log_ig, d.initial_state = _ptr(log_alpha), _ptr(log_ig), _ptr(initial_state)
+    d.out, d.final_state = _ptr(out), _ptr(final_state)
+    d.seg_chunks = int(seg_chunks)
+    d.reserved = 0
+    d.workspace = _ptr(workspace)
+    d.workspace_bytes = int(workspace_bytes)
+    return d
+
+
+def _check_tensors(q, k, v, *others):
+    import torch
+
+    for t in (q, k, v) + tuple(o for o in others if o is not None):
+        if not t.is_cuda:
+            raise ValueError("all tensors must be on the GPU")
+        if not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share a dtype")
+    for t in others:
+        if t is not None and t.dtype != torch.float32:
+            raise TypeError("gates, states and outputs are fp32")
+
+
+def fwd(q, k, v, log_alpha=None, *, log_ig=None, initial_state=None, chunk: int = 64, final_state: bool = True,
+        seg_chunks: int = 0, out=None, workspace=None, stream=None):
+    """Gated linear attention forward on the current HIP stream.
+
+    Returns ``(out [B,H,L,Dv] fp32, final_state [B,H,Dk,Dv] fp32 or None)``."""
+    import torch
+
+    lib = load()
+    B, H, L, Dk = q.shape
+    Dv = v.shape[-1]
+    if out is None:
+        out = torch.empty((B, H, L, Dv), dtype=torch.float32, device=q.device)
+    fin = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=q.device) if final_state else None
+    _check_tensors(q, k, v, log_alpha, log_ig, initial_state, out, fin)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    d = make_desc(q, k, v, log_alpha, log_ig, initial_state, out, fin, chunk, seg_chunks, workspace, ws_bytes)
+    s = stream if stream is not None else torch.cuda.current_stream(q.device)
+    st = lib.gla_fwd_ex(ctypes.byref(d), ctypes.c_void_p(s.cuda_stream))
+    if st != GLA_OK:
+        raise GlaError(st, "gla_fwd_ex")
+    return out, fin
+
+
+def fwd_headline(q, k, v, log_alpha, out, final_state, chunk: int = 64, stream=None) -> int:
+    """The 13-argument entry point ``gla_fwd`` (bf16 inputs, per-channel gate or None); returns the status."""
+    import torch
+
+    B, H, L, Dk = q.shape
+    Dv = v.shape[-1]
+    s = stream if stream is not None else torch.cuda.current_stream(q.device)
+    return int(load().gla_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(out), _ptr(final_state), B, H, L,
+                              Dk, Dv, int(chunk), ctypes.c_void_p(s.cuda_stream)))
+
+
+def plan(desc: GlaDesc) -> GlaPlan:
+    p = GlaPlan()
+    st = load().gla_query_plan(ctypes.byref(desc), ctypes.byref(p))
+    if st != GLA_OK:
+        raise GlaError(st, "gla_query_plan")
+    return p
+
+
+def workspace_size(desc: GlaDesc) -> int:
+    n = ctypes.c_size_t(0)
+    st = load().gla_workspace_size(ctypes.byref(desc), ctypes.byref(n))
+    if st != GLA_OK:
+        raise GlaError(st, "gla_workspace_size")
+    return int(n.value)

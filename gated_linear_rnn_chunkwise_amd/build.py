@@ -1,0 +1,54 @@
+"""Build the HIP library ``libgla.so`` in-tree for gfx950.
+
+Usage: ``python -m gated_linear_rnn_chunkwise_amd.build`` (or call :func:`build`).
+Every call compiles from source: the kernels (``csrc/gla_kernels.hip``) and the C ABI
+(``csrc/gla_api.cpp``) are compiled in parallel and linked into one shared library.
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(HERE, "libgla.so")
+BUILD_DIR = os.path.join(HERE, "_build")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ARCH = "gfx950"
+
+COMMON = [
+    "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
+    # never emit packed fp32 VALU instructions
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-I", INCLUDE, "-I", CSRC, "-Wall", "-Wno-unused-variable", "-Wno-unused-but-set-variable",
+]
+SOURCES = ["gla_kernels.hip", "gla_api.cpp"]
+
+
+def _compile(src: str) -> str:
+    obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
+    cmd = [HIPCC] + COMMON + ["-c", os.path.join(CSRC, src), "-o", obj]
+    if src.endswith(".cpp"):
+        cmd[1:1] = ["-x", "hip"]
+    subprocess.check_call(cmd)
+    return obj
+
+
+def build(verbose: bool = True) -> str:
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+        objs = list(ex.map(_compile, SOURCES))
+    tmp = LIB + ".tmp%d" % os.getpid()
+    subprocess.check_call([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + objs)
+    os.replace(tmp, LIB)
+    if verbose:
+        print("built", LIB, file=sys.stderr)
+    return LIB
+
+
+if __name__ == "__main__":
+    build()

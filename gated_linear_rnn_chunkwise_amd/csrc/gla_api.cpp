@@ -1,0 +1,222 @@
+// gla_api.cpp -- the C ABI declared in gla.h: argument validation, launch planning,
+// workspace handling and dispatch to the gfx950 kernels.
+//
+// Validation runs entirely on the host before any HIP call, so every error path can be
+// exercised without a GPU.  Planning picks how many sequence segments to process in
+// parallel: when (batch x heads x value tiles) already fills the GPU the sequence is one
+// segment and no state is written to memory; otherwise the sequence is cut into segments
+// whose boundary states are formed by a state kernel and joined by a scan.  This is the
+// trade of memory movement against parallelism named in the GLA abstract (Gated Linear
+// Attention Transformers with Hardware-Efficient Training), and sequence-level
+// parallelism for small batches (talk summary, 59:59).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "gla.h"
+#include "gla_layout.h"
+
+namespace gla {
+hipError_t launch_forward(const KArgs &a, bool f32, int dk, hipStream_t st);
+}
+
+namespace {
+
+constexpr int kTargetWorkgroups = 256;     // one per compute unit on MI355X
+constexpr int64_t kSmallProblem = 65536;   // head-tokens below which segmenting does not pay
+
+struct Plan {
+    int nt, nc, ndv, seg_chunks, nseg, seg_len;
+    int grid_state, grid_scan, grid_out;
+    size_t ws_state_bytes, ws_decay_bytes, ws_bytes;
+    uint32_t lds_out, lds_state;
+};
+
+inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline size_t align256(size_t x) { return (x + 255u) & ~size_t(255u); }
+
+// Argument checks (no HIP call).  Returns GLA_OK or an error status.
+int validate(const gla_desc *d) {
+    if (!d) return GLA_ERR_INVALID_ARG;
+    if (!d->q || !d->k || !d->v || !d->out) return GLA_ERR_INVALID_ARG;
+    if (d->B <= 0 || d->H <= 0 || d->L <= 0 || d->Dk <= 0 || d->Dv <= 0 || d->chunk <= 0) return GLA_ERR_INVALID_ARG;
+    if (d->seg_chunks < 0 || d->reserved != 0) return GLA_ERR_INVALID_ARG;
+    if (d->in_dtype != GLA_DTYPE_BF16 && d->in_dtype != GLA_DTYPE_F32) return GLA_ERR_INVALID_ARG;
+    if (d->gate_kind < GLA_GATE_NONE || d->gate_kind > GLA_GATE_HEAD_CONST) return GLA_ERR_INVALID_ARG;
+    if ((d->gate_kind == GLA_GATE_NONE) != (d->log_alpha == nullptr)) return GLA_ERR_INVALID_ARG;
+    const void *ptrs[] = {d->q, d->k, d->v, d->out, d->log_alpha, d->log_ig, d->initial_state, d->final_state,
+                          d->workspace};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p)) return GLA_ERR_INVALID_ARG;
+    if (d->workspace && d->workspace_bytes == 0) return GLA_ERR_INVALID_ARG;
+    // size products in int64 with headroom: element counts must stay below 2^40
+    const int64_t lim = int64_t(1) << 40;
+    const int64_t bh = int64_t(d->B) * d->H;
+    if (bh > (int64_t(1) << 24)) return GLA_ERR_INVALID_ARG;
+    if (bh * d->L > lim / std::max(d->Dk, d->Dv)) return GLA_ERR_INVALID_ARG;
+    if (bh * int64_t(d->Dk) * d->Dv > lim) return GLA_ERR_INVALID_ARG;
+    return GLA_OK;
+}
+
+// Support matrix and launch plan.  Returns GLA_OK, GLA_ERR_UNSUPPORTED.
+int make_plan(const gla_desc *d, Plan *p) {
+    if (d->Dk != 64 && d->Dk != 128 && d->Dk != 256) return GLA_ERR_UNSUPPORTED;
+    if (d->Dv % gla::kDvTile != 0 || d->Dv > 4096) return GLA_ERR_UNSUPPORTED;
+    if (d->chunk % gla::kTile != 0 || d->chunk > gla::kMaxChunk) return GLA_ERR_UNSUPPORTED;
+    const bool f32 = d->in_dtype == GLA_DTYPE_F32;
+    const bool ch = d->gate_kind == GLA_GATE_CHANNEL;
+    p->nt = d->chunk / gla::kTile;
+    p->nc = (d->L + d->chunk - 1) / d->chunk;
+    p->ndv = d->Dv / gla::kDvTile;
+    const int64_t bh = int64_t(d->B) * d->H;
+    const int64_t wg1 = bh * p->ndv;
+    int sc;
+    if (d->seg_chunks > 0) {
+        sc = std::min(d->seg_chunks, p->nc);
+    } else if (wg1 >= kTargetWorkgroups || bh * d->L <= kSmallProblem) {
+        sc = p->nc;
+    } else {
+        const int64_t want = (kTargetWorkgroups + wg1 - 1) / wg1;
+        const int64_t nseg = std::min<int64_t>(want, p->nc);
+        sc = (int)((p->nc + nseg - 1) / nseg);
+    }
+    p->seg_chunks = sc;
+    p->nseg = (p->nc + sc - 1) / sc;
+    p->seg_len = sc * d->chunk;
+    const int64_t g3 = bh * p->nseg * p->ndv;
+    const int64_t g1 = p->nseg > 1 ? bh * (p->nseg - 1) * p->ndv : 0;
+    if (g3 > INT32_MAX || g1 > INT32_MAX) return GLA_ERR_UNSUPPORTED;
+    p->grid_out = (int)g3;
+    p->grid_state = (int)g1;
+    p->grid_scan = p->nseg > 1 ? (int)(bh * ((int64_t(d->Dk) * d->Dv + 1023) / 1024)) : 0;
+    const int opb = f32 ? 4 : 2;
+    p->lds_out = gla::lds_plan(opb, d->Dk, ch, p->nt).total;
+    p->lds_state = gla::lds_plan(opb, d->Dk, ch, 1).total;
+    if (p->lds_out > gla::kMaxLds || p->lds_state > gla::kMaxLds) return GLA_ERR_UNSUPPORTED;
+    const size_t nsm = (size_t)(p->nseg - 1);
+    p->ws_state_bytes = align256(size_t(bh) * nsm * size_t(d->Dk) * size_t(d->Dv) * 4u);
+    p->ws_decay_bytes = align256(size_t(bh) * nsm * size_t(d->Dk) * 4u);
+    p->ws_bytes = p->nseg > 1 ? p->ws_state_bytes + p->ws_decay_bytes : 0;
+    return GLA_OK;
+}
+
+int checked_plan(const gla_desc *d, Plan *p) {
+    const int st = validate(d);
+    if (st != GLA_OK) return st;
+    return make_plan(d, p);
+}
+
+}  // namespace
+
+extern "C" {
+
+int gla_version(void) { return GLA_VERSION; }
+
+const char *gla_status_string(int status) {
+    switch (status) {
+        case GLA_OK: return "ok";
+        case GLA_ERR_INVALID_ARG: return "invalid argument";
+        case GLA_ERR_UNSUPPORTED: return "unsupported configuration";
+        case GLA_ERR_WORKSPACE: return "workspace too small or allocation failed";
+        case GLA_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+int gla_workspace_size(const gla_desc *d, size_t *bytes) {
+    if (!bytes) return GLA_ERR_INVALID_ARG;
+    Plan p;
+    const int st = checked_plan(d, &p);
+    if (st != GLA_OK) return st;
+    *bytes = p.ws_bytes;
+    return GLA_OK;
+}
+
+int gla_query_plan(const gla_desc *d, gla_plan *out) {
+    if (!out) return GLA_ERR_INVALID_ARG;
+    Plan p;
+    const int st = checked_plan(d, &p);
+    if (st != GLA_OK) return st;
+    out->seg_chunks = p.seg_chunks;
+    out->n_seg = p.nseg;
+    out->dv_tiles = p.ndv;
+    out->tiles_per_chunk = p.nt;
+    out->grid_state = p.grid_state;
+    out->grid_scan = p.grid_scan;
+    out->grid_out = p.grid_out;
+    out->reserved = 0;
+    out->workspace_bytes = p.ws_bytes;
+    return GLA_OK;
+}
+
+int gla_fwd_ex(const gla_desc *d, void *stream) {
+    Plan p;
+    const int st = checked_plan(d, &p);
+    if (st != GLA_OK) return st;
+    if (d->workspace && d->workspace_bytes < p.ws_bytes) return GLA_ERR_WORKSPACE;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+
+    void *ws = nullptr;
+    bool owned = false;
+    if (p.ws_bytes > 0) {
+        if (d->workspace) {
+            ws = d->workspace;
+        } else {
+            if (hipMallocAsync(&ws, p.ws_bytes, s) != hipSuccess || !ws) {
+                (void)hipGetLastError();
+                return GLA_ERR_WORKSPACE;
+            }
+            owned = true;
+        }
+    }
+
+    gla::KArgs a{};
+    a.q = d->q;
+    a.k = d->k;
+    a.v = d->v;
+    a.la = d->log_alpha;
+    a.li = d->log_ig;
+    a.s0 = d->initial_state;
+    a.out = d->out;
+    a.fin = d->final_state;
+    a.ws_state = ws ? reinterpret_cast<float *>(ws) : nullptr;
+    a.ws_decay = ws ? reinterpret_cast<float *>(reinterpret_cast<char *>(ws) + p.ws_state_bytes) : nullptr;
+    a.B = d->B;
+    a.H = d->H;
+    a.L = d->L;
+    a.Dv = d->Dv;
+    a.chunk = d->chunk;
+    a.nt = p.nt;
+    a.gate = d->gate_kind;
+    a.seg_len = p.seg_len;
+    a.nseg = p.nseg;
+    a.ndv = p.ndv;
+    a.nwg = p.grid_out;
+
+    const hipError_t err = gla::launch_forward(a, d->in_dtype == GLA_DTYPE_F32, d->Dk, s);
+    if (owned) (void)hipFreeAsync(ws, s);
+    return err == hipSuccess ? GLA_OK : GLA_ERR_HIP;
+}
+
+int gla_fwd(const void *q, const void *k, const void *v, const float *log_alpha, void *out, float *final_state,
+            int B, int H, int L, int Dk, int Dv, int chunk, void *stream) {
+    gla_desc d{};
+    d.B = B;
+    d.H = H;
+    d.L = L;
+    d.Dk = Dk;
+    d.Dv = Dv;
+    d.chunk = chunk;
+    d.in_dtype = GLA_DTYPE_BF16;
+    d.gate_kind = log_alpha ? GLA_GATE_CHANNEL : GLA_GATE_NONE;
+    d.q = q;
+    d.k = k;
+    d.v = v;
+    d.log_alpha = log_alpha;
+    d.out = reinterpret_cast<float *>(out);
+    d.final_state = final_state;
+    return gla_fwd_ex(&d, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,101 @@
+// gla_layout.h -- sizes shared by the host planner and the gfx950 kernels.
+//
+// One workgroup = 4 waves of 64 lanes.  A workgroup owns one (batch, head), one sequence
+// segment and one 64-column slice of the value dimension; wave w owns 16 of those columns.
+// Tokens are processed in 64-token tiles (a chunk of C > 64 tokens is C/64 tiles, the
+// tiled large-chunk scheme of Tiled Flash Linear Attention, abstract); key channels are
+// processed in slabs of 64 lanes x CPL channels.
+#pragma once
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__HIPCC__)
+#define GLA_HD __host__ __device__
+#else
+#define GLA_HD
+#endif
+
+namespace gla {
+
+constexpr int kTile = 64;       // tokens per tile
+constexpr int kThreads = 256;   // 4 waves
+constexpr int kDvTile = 64;     // value columns per workgroup
+constexpr int kMaxChunk = 512;  // largest chunk size
+constexpr uint32_t kMaxLds = 160u * 1024u;  // LDS per CU on gfx950
+
+// Channels handled by one lane in a slab: 2 for 16-bit operands and Dk >= 128, else 1.
+GLA_HD inline int chan_per_lane(int opb, int dk) { return (opb == 2 && dk >= 128) ? 2 : 1; }
+
+// Byte offsets of the workgroup's LDS arrays (dynamic shared memory).
+struct LdsPlan {
+    uint32_t q;       // [nq][64][rp]  QD (per-channel gate) or raw q (scalar gate); nq = slabs if nt > 1
+    uint32_t k;       // [64][rp]      KO (per-channel) or raw k (scalar)
+    uint32_t qi;      // [64][rp]      q scaled to the chunk start
+    uint32_t kst;     // [slab][ktp]   k scaled to the tile end, transposed, in MFMA k-slot order
+    uint32_t pbuf;    // [4][2][64][8] masked score tile, MFMA A-operand order
+    uint32_t vb;      // [2][4][64][8] value tile, MFMA B-operand order
+    uint32_t voff;    // same, value tile of an earlier key tile (nt > 1)
+    uint32_t prevke;  // [nt-1][nslab][64][rp] k scaled to its tile end, earlier tiles (per-channel, nt > 1)
+    uint32_t ablk;    // [4][slab] fp32 decay of each 16-token sub-block (per-channel)
+    uint32_t ainv;    // [4][slab] fp32 reciprocal of ablk
+    uint32_t qtf;     // [4][dk]   fp32 decay from the tile start to each sub-block start (per-channel, nt > 1)
+    uint32_t atile;   // [nt][dk]  fp32 decay across each tile of the chunk (per-channel); [nt] (scalar)
+    uint32_t aseg;    // [dk]      fp32 decay across the segment (segment-state kernel)
+    uint32_t brow;    // [nt*64]   fp32 log2 running decay from the chunk start (scalar gates)
+    uint32_t lrow;    // [nt*64]   fp32 log2 input gate (scalar gates)
+    uint32_t total;
+};
+
+GLA_HD inline LdsPlan lds_plan(int opb, int dk, bool per_channel, int nt) {
+    const int cpl = chan_per_lane(opb, dk);
+    const int slab = 64 * cpl;
+    const int nslab = dk / slab;
+    const int rp = slab + 16 / opb;
+    const int ktp = 64 + 16 / opb;
+    const uint32_t a64 = 64u * (uint32_t)rp * (uint32_t)opb;
+    const bool mt = nt > 1;
+    uint32_t off = 0;
+    LdsPlan p{};
+#define GLA_TAKE(field, bytes)                      \
+    do {                                            \
+        p.field = off;                              \
+        off += ((uint32_t)(bytes) + 255u) & ~255u;  \
+    } while (0)
+    GLA_TAKE(q, a64 * (uint32_t)(mt ? nslab : 1));
+    GLA_TAKE(k, a64);
+    GLA_TAKE(qi, a64);
+    GLA_TAKE(kst, (uint32_t)slab * (uint32_t)ktp * (uint32_t)opb);
+    GLA_TAKE(pbuf, 4096u * (uint32_t)opb);
+    GLA_TAKE(vb, 4096u * (uint32_t)opb);
+    if (mt) GLA_TAKE(voff, 4096u * (uint32_t)opb);
+    if (mt && per_channel) GLA_TAKE(prevke, a64 * (uint32_t)nslab * (uint32_t)(nt - 1));
+    if (per_channel) {
+        GLA_TAKE(ablk, 4u * slab * 4u);
+        GLA_TAKE(ainv, 4u * slab * 4u);
+        if (mt) GLA_TAKE(qtf, 4u * dk * 4u);
+    }
+    GLA_TAKE(atile, (uint32_t)nt * (uint32_t)(per_channel ? dk : 1) * 4u);
+    GLA_TAKE(aseg, (uint32_t)dk * 4u);
+    GLA_TAKE(brow, (uint32_t)nt * 64u * 4u);
+    GLA_TAKE(lrow, (uint32_t)nt * 64u * 4u);
+#undef GLA_TAKE
+    p.total = off;
+    return p;
+}
+
+// Arguments of the three kernels.
+struct KArgs {
+    const void *q, *k, *v;
+    const float *la, *li, *s0;
+    float *out, *fin;
+    float *ws_state;  // [BH][nseg-1][Dk][Dv]: local segment states, then (in place) their prefix states
+    float *ws_decay;  // [BH][nseg-1][Dk]: decay across each segment
+    int B, H, L, Dv;
+    int chunk, nt;    // chunk size and 64-token tiles per chunk
+    int gate;         // enum gla_gate
+    int seg_len;      // tokens per segment (a multiple of the chunk size)
+    int nseg, ndv;    // segments; 64-column value tiles
+    int nwg;          // workgroups of the launch (for the XCD-aware remap)
+};
+
+}  // namespace gla

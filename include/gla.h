@@ -1,0 +1,146 @@
+/*
+ * gla.h -- C ABI of the MI355X (gfx950) chunkwise gated linear attention forward pass.
+ *
+ * The operation.  For every batch b and head h, with a Dk x Dv fp32 state S (zero, or
+ * the given initial state, before the first token):
+ *
+ *     S_t = diag(alpha_t) S_{t-1} + i_t k_t^T v_t ,     o_t = q_t S_t .
+ *
+ * Softmax-free attention is a linear recurrence over a matrix-valued state [Hardware-
+ * Efficient Training of Linear Attention Models, talk summary, 4:04]; gated linear
+ * attention lets a data-dependent gate alpha_t in (0,1]^Dk decay the state [Gated Linear
+ * Attention Transformers with Hardware-Efficient Training, abstract]; the optional scalar
+ * input gate i_t is the sigmoid input gate of the mLSTM variant [Tiled Flash Linear
+ * Attention, abstract].  The gate decays the rows (key channels) of the state before the
+ * current token is written; there is no scale factor and no normaliser.
+ *
+ * How it is computed.  Chunkwise: the sequence is cut into chunks of `chunk` tokens;
+ * inside a chunk the causal pairwise term is a masked matrix product and the state enters
+ * through one product with the chunk's queries; between chunks the state is carried by a
+ * recurrence [talk summary, 11:58].  Chunks larger than 64 tokens are split again into
+ * 64-token query and key tiles [Tiled Flash Linear Attention, abstract].  The result is
+ * the same map as the recurrence; only floating-point rounding differs.
+ *
+ * Numbers.  q, k, v are bf16 or fp32; gates are fp32 natural logs; the output, the
+ * states and all accumulation are fp32.  With bf16 inputs the products that involve a
+ * computed operand (gate-rescaled q and k, the masked score matrix, the carried state)
+ * take fp16 operands on the matrix cores; with fp32 inputs every operand stays fp32.
+ *
+ * Layout and ownership.  Every tensor is dense, row-major and contiguous on the device,
+ * with the shapes given below, and 16-byte aligned.  The caller owns all memory; the
+ * library never frees or keeps a pointer it is given.  Inputs are not modified.
+ *
+ * Gate values.  log_alpha and log_ig must be finite or -infinity is NOT accepted: use a
+ * large negative finite value (for example -1e4) for a gate of zero.  Gates are expected
+ * to be <= 0 (alpha, i in (0, 1]); positive log gates are computed as given but may
+ * overflow.  NaN inputs propagate to the outputs.  Values are not checked on the host.
+ *
+ * Asynchrony and errors.  Every call validates its arguments on the host before any HIP
+ * call; on a validation error it returns a negative status, launches nothing and writes
+ * nothing.  Otherwise it enqueues its kernels on `stream` (a hipStream_t; NULL is the
+ * default stream) and returns without synchronising; outputs are valid once the stream
+ * has completed the work.  GLA_ERR_HIP reports launch-time errors only.  The library has
+ * no mutable global state besides a per-device property cache; calls are re-entrant.
+ */
+#ifndef GLA_H
+#define GLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GLA_VERSION 10000 /* major * 10000 + minor * 100 + patch */
+
+/* Status codes.  0 is success; errors are negative. */
+enum gla_status {
+    GLA_OK = 0,
+    GLA_ERR_INVALID_ARG = -1, /* NULL required pointer, size <= 0, misaligned pointer,
+                                 size product overflow, gate layout inconsistent with kind */
+    GLA_ERR_UNSUPPORTED = -2, /* valid but outside the support matrix below */
+    GLA_ERR_WORKSPACE = -3,   /* caller workspace too small, or workspace allocation failed */
+    GLA_ERR_HIP = -4          /* a HIP launch or runtime call failed */
+};
+
+/* Element type of q, k and v. */
+enum gla_dtype { GLA_DTYPE_BF16 = 0, GLA_DTYPE_F32 = 1 };
+
+/* How log_alpha is laid out and broadcast to the per-channel decay of the state rows. */
+enum gla_gate {
+    GLA_GATE_NONE = 0,       /* log_alpha == NULL: alpha = 1 (plain linear attention) */
+    GLA_GATE_CHANNEL = 1,    /* [B, H, L, Dk]: one decay per key channel (GLA) */
+    GLA_GATE_HEAD = 2,       /* [B, H, L]: one decay per head and token (mLSTM forget gate) */
+    GLA_GATE_HEAD_CONST = 3  /* [H]: one fixed decay per head (RetNet-style) */
+};
+
+/* Full description of one forward call. */
+typedef struct gla_desc {
+    int32_t B, H, L, Dk, Dv; /* batch, heads, sequence length, key and value head dims */
+    int32_t chunk;           /* chunk size C of the chunkwise algorithm */
+    int32_t in_dtype;        /* enum gla_dtype of q, k, v */
+    int32_t gate_kind;       /* enum gla_gate */
+    const void *q;           /* [B, H, L, Dk] in_dtype */
+    const void *k;           /* [B, H, L, Dk] in_dtype */
+    const void *v;           /* [B, H, L, Dv] in_dtype */
+    const float *log_alpha;  /* layout per gate_kind; must be NULL iff gate_kind == NONE */
+    const float *log_ig;     /* [B, H, L] log input gate, or NULL (i_t = 1) */
+    const float *initial_state; /* [B, H, Dk, Dv] state before token 0, or NULL (zero) */
+    float *out;              /* [B, H, L, Dv] output */
+    float *final_state;      /* [B, H, Dk, Dv] state after token L-1, or NULL */
+    int32_t seg_chunks;      /* chunks per sequence segment; 0 = chosen by the library.
+                                Segments are processed in parallel and joined by a scan of
+                                their boundary states (see gla_fwd_ex). */
+    int32_t reserved;        /* must be 0 */
+    void *workspace;         /* device scratch or NULL (the library allocates it on the stream) */
+    size_t workspace_bytes;  /* size of `workspace` */
+} gla_desc;
+
+/* What a call would launch (for tests, profiling and the benchmark). */
+typedef struct gla_plan {
+    int32_t seg_chunks;      /* chunks per segment actually used */
+    int32_t n_seg;           /* number of sequence segments */
+    int32_t dv_tiles;        /* value-dimension tiles of 64 columns */
+    int32_t tiles_per_chunk; /* 64-token tiles per chunk */
+    int32_t grid_state;      /* workgroups of the segment-state kernel (0 if not launched) */
+    int32_t grid_scan;       /* workgroups of the segment-scan kernel (0 if not launched) */
+    int32_t grid_out;        /* workgroups of the chunk-output kernel */
+    int32_t reserved;
+    size_t workspace_bytes;  /* device scratch the call needs (0 = none) */
+} gla_plan;
+
+/* Forward pass with the headline argument list.  q, k, v: bf16 [B,H,L,Dk|Dv];
+ * log_alpha: fp32 [B,H,L,Dk] per-channel log gate, or NULL for no gate; out: fp32
+ * [B,H,L,Dv]; final_state: fp32 [B,H,Dk,Dv] or NULL; chunk: chunk size; stream: hipStream_t.
+ * Any scratch it needs is allocated and freed stream-ordered on `stream`.
+ * Returns a gla_status. */
+int gla_fwd(const void *q, const void *k, const void *v, const float *log_alpha, void *out,
+            float *final_state, int B, int H, int L, int Dk, int Dv, int chunk, void *stream);
+
+/* General forward pass: input dtype, every gate kind, input gate, initial state, segment
+ * length and caller workspace.  When d->workspace is NULL and scratch is needed it is
+ * allocated and freed stream-ordered on `stream`; otherwise d->workspace_bytes must be at
+ * least what gla_workspace_size reports, else GLA_ERR_WORKSPACE.
+ * Support matrix (else GLA_ERR_UNSUPPORTED): chunk a multiple of 64 in [64, 1024];
+ * Dk in {64, 128, 256}; Dv a multiple of 64 up to 4096; any L >= 1; a per-channel gate
+ * with chunk > 64 needs Dk <= 128.  Returns a gla_status. */
+int gla_fwd_ex(const gla_desc *d, void *stream);
+
+/* Scratch bytes gla_fwd_ex needs for `d` (no HIP call).  Returns a gla_status. */
+int gla_workspace_size(const gla_desc *d, size_t *bytes);
+
+/* Launch plan gla_fwd_ex would use for `d` (no HIP call).  Returns a gla_status. */
+int gla_query_plan(const gla_desc *d, gla_plan *plan);
+
+/* Static English text for a status code (never NULL). */
+const char *gla_status_string(int status);
+
+/* GLA_VERSION of the built library. */
+int gla_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GLA_H */

@@ -1,0 +1,226 @@
+"""GPU parity: the HIP library (through its C ABI) against the fp64 oracle.
+
+Bar (written here, applied to every output element compared):
+  bf16 inputs: max |gpu - oracle| <= 1e-2 * RMS(oracle)
+  fp32 inputs: max |gpu - oracle| <= 1e-4 * RMS(oracle)
+RMS is over the whole compared tensor (all batches, heads, tokens and columns, or all sampled
+heads at full size); the final state is compared against its own RMS with the same factor.
+Inputs come from the shared seeded generators; the oracle sees the same bytes.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gated_linear_rnn_chunkwise_amd import inputs as gin
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"bf16": 1e-2, "f32": 1e-4}
+
+
+def rel_err(got, ref):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    rms = float(np.sqrt(np.mean(ref * ref)))
+    return float(np.max(np.abs(got - ref))) / max(rms, 1e-300)
+
+
+def gate_name(w):
+    return w.gate
+
+
+def run_gpu(gla, d, w, chunk=None, seg_chunks=0, initial_state=None, final_state=True):
+    dev = "cuda"
+    q, k, v = (d[x].to(dev) for x in "qkv")
+    la = None if d["log_alpha"] is None else d["log_alpha"].to(dev)
+    li = None if d["log_ig"] is None else d["log_ig"].to(dev)
+    s0 = None if initial_state is None else initial_state.to(dev)
+    out, fin = gla.fwd(q, k, v, la, log_ig=li, initial_state=s0, chunk=chunk or w.chunk,
+                       final_state=final_state, seg_chunks=seg_chunks)
+    torch.cuda.synchronize()
+    return out.cpu().double().numpy(), None if fin is None else fin.cpu().double().numpy()
+
+
+def run_oracle(d, w, initial_state=None, heads=None):
+    sel = (lambda x: x) if heads is None else (lambda x: x if x is None else x.reshape(-1, *x.shape[2:])[heads][None])
+    gate = w.gate
+    la = d["log_alpha"]
+    if heads is not None and gate == "head_const":
+        H = w.H
+        # [H] gate: pick each sampled head's value and present the heads as one batch row
+        la = torch.stack([la[hh % H] for hh in heads])
+        q, k, v = (sel(d[x]) for x in "qkv")
+        return oracle.recurrent(q, k, v, "head_const", la, sel(d["log_ig"]), sel(initial_state))
+    return oracle.recurrent(sel(d["q"]), sel(d["k"]), sel(d["v"]), gate, sel(la) if gate != "head_const" else la,
+                            sel(d["log_ig"]), sel(initial_state))
+
+
+def check(w, got, ref, what="out"):
+    e = rel_err(got, ref)
+    assert e <= TOL[w.dtype], "%s: %s max|err|/RMS = %.3e > %.0e" % (w.name, what, e, TOL[w.dtype])
+    return e
+
+
+# ------------------------------------------------------------------------------ small shapes
+SMALL = []
+for dtype in ("bf16", "f32"):
+    for gate, ig in (("channel", False), ("none", False), ("head", True), ("head_const", False), ("channel", True)):
+        for Dk, Dv in ((64, 64), (128, 128), (256, 64)):
+            for chunk in (64, 128, 256):
+                if dtype == "f32" and (Dk == 256 or chunk > 128):
+                    continue
+                if dtype == "f32" and gate == "channel" and Dk >= 128 and chunk > 64:
+                    continue  # LDS budget: unsupported
+                if gate == "channel" and Dk == 256 and chunk > 128:
+                    continue
+                SMALL.append((dtype, gate, ig, Dk, Dv, chunk))
+
+
+@pytest.mark.parametrize("dtype,gate,ig,Dk,Dv,chunk", SMALL)
+@pytest.mark.parametrize("L", [1, 100, 333])
+def test_small_shapes(gpu_lib, dtype, gate, ig, Dk, Dv, chunk, L):
+    w = gin.custom(2, 2, L, Dk, Dv, chunk, dtype=dtype, gate=gate, input_gate=ig)
+    d = gin.make_inputs(w, seed=L)
+    out, fin = run_gpu(gpu_lib, d, w)
+    ref, rfin = run_oracle(d, w)
+    check(w, out, ref)
+    check(w, fin, rfin, "final_state")
+
+
+@pytest.mark.parametrize("gate,ig,chunk", [("channel", False, 64), ("channel", True, 128), ("head", True, 256),
+                                           ("head_const", False, 128), ("none", False, 64)])
+@pytest.mark.parametrize("seg_chunks", [1, 2, 3])
+def test_sequence_segments(gpu_lib, gate, ig, chunk, seg_chunks):
+    # several segments exercise the segment-state and segment-scan kernels; seg_chunks = 1 is
+    # one state per chunk (the chunk-state / chunk-scan / chunk-output decomposition)
+    w = gin.custom(1, 3, 1000, 128, 128, chunk, gate=gate, input_gate=ig)
+    d = gin.make_inputs(w, seed=7)
+    s0 = torch.randn(1, 3, 128, 128, generator=torch.Generator().manual_seed(3)) * 0.1
+    out, fin = run_gpu(gpu_lib, d, w, seg_chunks=seg_chunks, initial_state=s0)
+    ref, rfin = run_oracle(d, w, initial_state=s0)
+    check(w, out, ref)
+    check(w, fin, rfin, "final_state")
+
+
+def test_segment_modes_agree(gpu_lib):
+    w = gin.custom(1, 2, 2048, 128, 128, 64, gate="channel")
+    d = gin.make_inputs(w, seed=11)
+    outs = [run_gpu(gpu_lib, d, w, seg_chunks=s)[0] for s in (1, 4, 32)]
+    ref, _ = run_oracle(d, w)
+    for o in outs:
+        check(w, o, ref)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("gate,chunk", [("channel", 64), ("channel", 128), ("head", 64), ("head", 256)])
+def test_gate_zero_keeps_only_current_token(gpu_lib, dtype, gate, chunk):
+    # alpha -> 0 (log gate -1e4 underflows to an exact zero): o_t = (q_t . k_t) v_t
+    w = gin.custom(1, 2, 200, 64, 64, chunk, dtype=dtype, gate=gate)
+    d = gin.make_inputs(w, seed=5)
+    d["log_alpha"] = torch.full_like(d["log_alpha"], -1e4)
+    out, fin = run_gpu(gpu_lib, d, w)
+    ref, rfin = run_oracle(d, w)
+    check(w, out, ref)
+    check(w, fin, rfin, "final_state")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("scale", [0.3, 1.5, 6.0])
+def test_strong_per_channel_decay(gpu_lib, dtype, scale):
+    # large decay spans inside 16-token blocks take the exact diagonal path for some blocks
+    w = gin.custom(1, 2, 257, 128, 64, 64, dtype=dtype, gate="channel")
+    d = gin.make_inputs(w, seed=9)
+    d["log_alpha"] = (d["log_alpha"] * 16.0 * scale).float()
+    out, fin = run_gpu(gpu_lib, d, w)
+    ref, rfin = run_oracle(d, w)
+    check(w, out, ref)
+    check(w, fin, rfin, "final_state")
+
+
+def test_ungated_zero_gate_matches_no_gate(gpu_lib):
+    w = gin.custom(1, 2, 300, 128, 128, 64, gate="channel")
+    d = gin.make_inputs(w, seed=2)
+    d0 = dict(d)
+    d0["log_alpha"] = torch.zeros_like(d["log_alpha"])
+    a, _ = run_gpu(gpu_lib, d0, w)
+    wn = w.with_(gate="none")
+    dn = dict(d)
+    dn["log_alpha"] = None
+    b, _ = run_gpu(gpu_lib, dn, wn)
+    ref = oracle.bruteforce_ungated(d["q"][:, :, :40], d["k"][:, :, :40], d["v"][:, :, :40])
+    check(w, a[:, :, :40], ref)
+    check(w, b[:, :, :40], ref)
+
+
+def test_deterministic(gpu_lib):
+    w = gin.custom(2, 4, 777, 128, 128, 64, gate="channel", input_gate=True)
+    d = gin.make_inputs(w, seed=1)
+    a, fa = run_gpu(gpu_lib, d, w, seg_chunks=3)
+    b, fb = run_gpu(gpu_lib, d, w, seg_chunks=3)
+    assert np.array_equal(a, b) and np.array_equal(fa, fb)
+
+
+def test_headline_entry_point_matches_general(gpu_lib):
+    w = gin.custom(2, 2, 300, 128, 128, 64, gate="channel")
+    d = gin.make_inputs(w, seed=4)
+    q, k, v, la = (d[x].cuda() for x in ("q", "k", "v", "log_alpha"))
+    out = torch.empty(2, 2, 300, 128, device="cuda")
+    fin = torch.empty(2, 2, 128, 128, device="cuda")
+    st = gpu_lib.fwd_headline(q, k, v, la, out, fin, chunk=64)
+    assert st == 0
+    o2, f2 = gpu_lib.fwd(q, k, v, la, chunk=64)
+    torch.cuda.synchronize()
+    assert torch.equal(out, o2) and torch.equal(fin, f2)
+    # ungated through the headline entry point
+    st = gpu_lib.fwd_headline(q, k, v, None, out, None, chunk=64)
+    torch.cuda.synchronize()
+    assert st == 0
+    ref = oracle.bruteforce_ungated(d["q"][:, :, :32], d["k"][:, :, :32], d["v"][:, :, :32])
+    check(w, out.cpu().double().numpy()[:, :, :32], ref)
+
+
+def test_caller_workspace(gpu_lib):
+    w = gin.custom(1, 2, 1500, 128, 128, 64, gate="channel")
+    d = gin.make_inputs(w, seed=6)
+    q, k, v, la = (d[x].cuda() for x in ("q", "k", "v", "log_alpha"))
+    desc = gpu_lib.make_desc(q, k, v, la, chunk=64, seg_chunks=4)
+    nbytes = gpu_lib.workspace_size(desc)
+    assert nbytes > 0
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    o1, f1 = gpu_lib.fwd(q, k, v, la, chunk=64, seg_chunks=4, workspace=ws)
+    o2, f2 = gpu_lib.fwd(q, k, v, la, chunk=64, seg_chunks=4)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(f1, f2)
+    small = torch.empty(nbytes - 256, dtype=torch.uint8, device="cuda")
+    with pytest.raises(gpu_lib.GlaError) as ei:
+        gpu_lib.fwd(q, k, v, la, chunk=64, seg_chunks=4, workspace=small)
+    assert ei.value.status == gpu_lib.GLA_ERR_WORKSPACE
+
+
+# ------------------------------------------------------------------------------ full-size workloads
+FULL = [
+    ("ungated_f32_L256", None),
+    ("gla_bf16_B8H16L2048", [0, 37, 127]),
+    ("retnet_bf16_B4H8L8192", [0, 7, 20, 31]),
+    ("long_gla_bf16_H16L32768_C64", [0, 9, 15]),
+    ("long_gla_bf16_H16L32768_C256", [0, 9, 15]),
+    ("mlstm_sig_bf16_B8H8L8192", [0, 45]),
+]
+
+
+@pytest.mark.parametrize("name,heads", FULL, ids=[f[0] for f in FULL])
+def test_full_workload_sampled_heads(gpu_lib, name, heads):
+    w = gin.WORKLOADS[name]
+    d = gin.make_inputs(w, seed=0)
+    out, fin = run_gpu(gpu_lib, d, w)
+    if heads is None:
+        ref, rfin = run_oracle(d, w)
+        check(w, out, ref)
+        check(w, fin, rfin, "final_state")
+        return
+    ref, rfin = run_oracle(d, w, heads=heads)
+    got = out.reshape(-1, *out.shape[2:])[heads][None]
+    gfin = fin.reshape(-1, *fin.shape[2:])[heads][None]
+    check(w, got, ref)
+    check(w, gfin, rfin, "final_state")
