@@ -1,0 +1,257 @@
+#!/usr/bin/env python3
+"""Benchmark of the chunkwise gated linear attention forward pass on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one forward pass of the whole hot path (every kernel the library launches for
+the workload) over one batch of synthetic, seeded inputs that are already resident in HBM.
+W untimed steps run first; then exactly K steps are timed between two device
+synchronisations.  Two input sets alternate between steps so successive steps do not
+re-read the same bytes from the 256 MB last-level cache.  Prints one JSON line.
+
+Reported beside the throughput:
+* ``roofline`` of the dominant kernel: algorithmic bytes per launch over the mean launch
+  duration (HIP events recorded on the stream the kernels run on), against the 8 TB/s
+  HBM peak; ``traffic`` is the measured HBM traffic of that kernel from rocprofv3
+  counters (profiles/), or null when the counters were taken on other kernel source.
+* ``cpu_baseline``: the fp64 oracle (the plain token recurrence) timed on this host's
+  cores on the same workload, converted to the same unit.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 / fp16 matrix peak
+METRIC = "GLA fwd tokens/s and TFLOP/s (% bf16 MFMA peak), B8 H16 L2048 D128 bf16"
+KERNEL_SRC = os.path.join(ROOT, "gated_linear_rnn_chunkwise_amd", "csrc", "gla_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic_flops(w) -> float:
+    """Inter-chunk products (K^T V and Q S: 4 Dk Dv per head-token) plus the causal
+    intra-chunk score and value products ((C+1)(Dk+Dv) per head-token on average)."""
+    return float(w.B * w.H * w.L) * (4.0 * w.Dk * w.Dv + (w.chunk + 1) * (w.Dk + w.Dv))
+
+
+def io_floor_bytes(w) -> float:
+    """Bytes every implementation must move: q, k, v and the gates read once, the fp32
+    output written once, the fp32 final state written once."""
+    ib = 4 if w.dtype == "f32" else 2
+    gate = {"channel": 4 * w.Dk, "head": 4, "head_const": 0, "none": 0}[w.gate] + (4 if w.input_gate else 0)
+    per_ht = ib * (2 * w.Dk + w.Dv) + gate + 4 * w.Dv
+    return float(w.B * w.H * w.L) * per_ht + (w.B * w.H * w.Dk * w.Dv * 4 if w.final_state else 0)
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch of the dominant kernel from committed rocprofv3 counters, if
+    they were taken on the current kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = rec.get(workload)
+    if not ent or ent.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def cpu_baseline(w, d, budget_s: float = 20.0) -> dict:
+    """Time the fp64 oracle on a bounded sample of (batch, head) pairs of the workload."""
+    import numpy as np
+
+    import oracle
+
+    BH = w.B * w.H
+    # size the sample from a one-head probe so the timed part stays near budget_s
+    def prep(nheads):
+        sel = lambda t: None if t is None else t.reshape(-1, *t.shape[2:])[:nheads][None]
+        la = d["log_alpha"]
+        if w.gate == "head_const":
+            la = torch_stack_heads(la, w.H, nheads)
+            gate_in = la
+        else:
+            gate_in = sel(la)
+        q, k, v = (oracle.oracle._f64(sel(d[x])) for x in "qkv")
+        la64 = oracle.expand_gate(w.gate, gate_in, 1, nheads, w.L, w.Dk)
+        li = oracle.oracle._f64(sel(d["log_ig"]))
+        return q, k, v, la64, li
+
+    def run(nheads):
+        q, k, v, la64, li = prep(nheads)
+        t0 = time.perf_counter()
+        oracle.recurrent(q, k, v, "channel", la64, li)
+        return time.perf_counter() - t0
+
+    threads = oracle.threads()
+    probe_heads = min(BH, threads)
+    t_probe = run(probe_heads)
+    per_round = t_probe  # one head per thread
+    rounds = max(1, min(int(budget_s / max(per_round, 1e-6)), math.ceil(BH / threads)))
+    nheads = min(BH, rounds * threads)
+    t = run(nheads) if nheads != probe_heads else t_probe
+    head_tokens_per_s = nheads * w.L / t
+    tokens_per_s = head_tokens_per_s / w.H  # tokens = batch x sequence positions
+    return {
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": "%d of %d (batch, head) pairs, full length %d, fp64 token recurrence, %.2f s"
+                  % (nheads, BH, w.L, t),
+    }
+
+
+def torch_stack_heads(la, H, nheads):
+    import torch
+
+    return torch.stack([la[i % H] for i in range(nheads)])
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--seg-chunks", type=int, default=0)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py measures one GPU: the forward pass here is single-GPU work (see the sharding "
+              "design notes); run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import gated_linear_rnn_chunkwise_amd as gla
+    from gated_linear_rnn_chunkwise_amd import inputs as gin
+
+    wname = args.workload or gin.HEADLINE
+    w = gin.WORKLOADS[wname]
+    lib = gla.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    log("bench: generating inputs for", wname)
+    host = [gin.make_inputs(w, seed=args.seed + i) for i in range(2)]
+    sets = []
+    for h in host:
+        sets.append({k: (v.to(dev) if hasattr(v, "to") else v) for k, v in h.items() if v is not None})
+    out = torch.empty((w.B, w.H, w.L, w.Dv), dtype=torch.float32, device=dev)
+    fin = torch.empty((w.B, w.H, w.Dk, w.Dv), dtype=torch.float32, device=dev) if w.final_state else None
+    descs = []
+    for s in sets:
+        descs.append(gla.make_desc(s["q"], s["k"], s["v"], s.get("log_alpha"), s.get("log_ig"), None, out, fin,
+                                   w.chunk, args.seg_chunks))
+    plan = gla.plan(descs[0])
+    ws = None
+    if plan.workspace_bytes:
+        ws = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=dev)
+        for dsc in descs:
+            dsc.workspace, dsc.workspace_bytes = ws.data_ptr(), plan.workspace_bytes
+    stream = torch.cuda.current_stream(dev)
+    sptr = __import__("ctypes").c_void_p(stream.cuda_stream)
+    import ctypes
+
+    def step(i):
+        st = lib.gla_fwd_ex(ctypes.byref(descs[i & 1]), sptr)
+        if st != 0:
+            raise gla.GlaError(st, "gla_fwd_ex")
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        ev[i][0].record(stream)
+        step(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / K
+    launch_ms = [a.elapsed_time(b) for a, b in ev]
+    mean_launch_ms = sum(launch_ms) / K
+
+    tokens = w.B * w.L
+    value = tokens / (ms_per_step * 1e-3)
+    flops = algorithmic_flops(w)
+    io = io_floor_bytes(w)
+    tflops = flops / (ms_per_step * 1e-3) / 1e12
+
+    # Dominant kernel: the chunk-output kernel.  With one segment it is the only launch of
+    # a step, so the events around the call time exactly that kernel.
+    if plan.n_seg == 1:
+        kbytes = io
+        scope = "chunk_output_kernel"
+    else:
+        kbytes = io + w.B * w.H * (plan.n_seg - 1) * w.Dk * w.Dv * 4.0 * 3 \
+            + 2.0 * w.B * w.H * (plan.n_seg - 1) * w.L / plan.n_seg * (w.Dk * 2 + w.Dv) * (4 if w.dtype == "f32" else 2)
+        scope = "step (segment-state, segment-scan and chunk-output kernels)"
+    achieved = kbytes / (mean_launch_ms * 1e-3) / 1e9
+    traffic = measured_traffic(wname) if plan.n_seg == 1 else None
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic, "kernel": scope,
+            "algorithmic_bytes_per_launch": kbytes, "mean_launch_ms": round(mean_launch_ms, 5)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("bench: timing the fp64 oracle on host cores")
+        cpu = cpu_baseline(w, host[0])
+
+    rec = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": wname, "B": w.B, "H": w.H, "L": w.L, "Dk": w.Dk, "Dv": w.Dv, "chunk": w.chunk,
+                   "gate": w.gate, "input_gate": w.input_gate, "in_dtype": w.dtype,
+                   "matrix_operands": "fp16 from bf16" if w.dtype == "bf16" else "fp32",
+                   "accumulate": "fp32", "out_dtype": "fp32", "n_seg": plan.n_seg,
+                   "workgroups": plan.grid_out},
+        "head_tokens_per_s": value * w.H,
+        "tflops": round(tflops, 2),
+        "pct_bf16_mfma_peak": round(100.0 * tflops / BF16_MFMA_PEAK_TFLOPS, 2),
+        "io_floor_gbps": round(io / (ms_per_step * 1e-3) / 1e9, 1),
+        "pct_hbm_peak_io_floor": round(100.0 * io / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -29,7 +29,7 @@ constexpr int64_t kSmallProblem = 65536;   // head-tokens below which segmenting
 struct Plan {
     int nt, nc, ndv, seg_chunks, nseg, seg_len;
     int grid_state, grid_scan, grid_out;
-    size_t ws_state_bytes, ws_decay_bytes, ws_bytes;
+    size_t ws_state_bytes, ws_decay_bytes, ws_ke_bytes, ws_bytes;
     uint32_t lds_out, lds_state;
 };
 
@@ -97,7 +97,9 @@ int make_plan(const gla_desc *d, Plan *p) {
     const size_t nsm = (size_t)(p->nseg - 1);
     p->ws_state_bytes = align256(size_t(bh) * nsm * size_t(d->Dk) * size_t(d->Dv) * 4u);
     p->ws_decay_bytes = align256(size_t(bh) * nsm * size_t(d->Dk) * 4u);
-    p->ws_bytes = p->nseg > 1 ? p->ws_state_bytes + p->ws_decay_bytes : 0;
+    if (p->nseg <= 1) p->ws_state_bytes = p->ws_decay_bytes = 0;
+    p->ws_ke_bytes = align256(size_t(g3) * (size_t)gla::ke_scratch_bytes(opb, d->Dk, ch, p->nt));
+    p->ws_bytes = p->ws_state_bytes + p->ws_decay_bytes + p->ws_ke_bytes;
     return GLA_OK;
 }
 
@@ -182,6 +184,7 @@ int gla_fwd_ex(const gla_desc *d, void *stream) {
     a.fin = d->final_state;
     a.ws_state = ws ? reinterpret_cast<float *>(ws) : nullptr;
     a.ws_decay = ws ? reinterpret_cast<float *>(reinterpret_cast<char *>(ws) + p.ws_state_bytes) : nullptr;
+    a.ws_ke = ws ? reinterpret_cast<char *>(ws) + p.ws_state_bytes + p.ws_decay_bytes : nullptr;
     a.B = d->B;
     a.H = d->H;
     a.L = d->L;

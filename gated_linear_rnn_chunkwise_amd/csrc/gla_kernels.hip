@@ -20,14 +20,21 @@
 // With one segment (enough (batch, head, value-tile) work to fill the GPU) only the last
 // kernel runs and no state ever goes to memory.
 //
+// Work split of a workgroup (4 waves): wave w owns 16 value columns for all matrix
+// products, and prepares the gate-scaled operands of the tile's 16-token block w.
+//
 // Numerics.  Gates are applied in the product domain: per-step decays alpha = 2^(log2e *
 // log_alpha) are multiplied into running products, so every factor that multiplies an
 // operand is <= 1, except the key factor of a diagonal 16x16 block, which is bounded by
 // the block's own decay span (checked; a block whose span is too large is computed exactly
 // on the vector ALU instead).  Scalar gates (none / per head) keep q and k raw in the
 // score product and multiply each score by its exact decay afterwards.  Operands computed
-// from bf16 inputs are fp16 (range-checked by construction); fp32 inputs keep fp32
-// operands.  Accumulation, states and outputs are fp32.
+// from bf16 inputs are fp16; fp32 inputs keep fp32 operands.  Accumulation, states and
+// outputs are fp32.
+//
+// Global memory is read and written through buffer resources whose size is the valid
+// extent of the (batch, head) slice: rows past the sequence end read as zero and their
+// stores are dropped by the hardware range check.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -41,10 +48,15 @@ namespace gla {
 typedef _Float16 f16;
 typedef f16 f16x8 __attribute__((ext_vector_type(8)));
 typedef f16 f16x4 __attribute__((ext_vector_type(4)));
+typedef f16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kRsrcFlags = 0x00020000;  // raw buffer, 32-bit data format (gfx9 family)
 
 // ------------------------------------------------------------------------------------
 // Instance configuration.
@@ -59,6 +71,7 @@ struct Cfg {
     using Half = typename std::conditional<F32, f32x4, f16x4>::type;
     using InT = typename std::conditional<F32, float, uint16_t>::type;
     static constexpr int OPB = F32 ? 4 : 2;
+    static constexpr int IB = F32 ? 4 : 2;      // input element bytes
     static constexpr int CPL = (!F32 && DK >= 128) ? 2 : 1;
     static constexpr int SLAB = 64 * CPL;
     static constexpr int NSLAB = DK / SLAB;
@@ -67,8 +80,8 @@ struct Cfg {
     static constexpr int NBD = DK / 16;         // 16-row blocks of the state
     static constexpr int KSTEP = SLAB / 32;     // 32-deep MFMA steps per slab
     static constexpr int NBS = SLAB / 16;       // 16-row state blocks per slab
-    // Smallest decay of a 16-token sub-block whose diagonal block still uses the matrix
-    // cores: the key operand there is scaled by up to 1/decay (2^8 for fp16 operands).
+    // Smallest decay of a 16-token block whose diagonal block still uses the matrix cores:
+    // the key operand there is scaled by up to 1/decay (2^8 for fp16 operands).
     static constexpr float kMinDiagDecay = F32 ? 1e-30f : 0.00390625f;
 };
 
@@ -79,9 +92,31 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
+// Barrier that also makes this workgroup's earlier global stores visible to its other waves.
+__device__ __forceinline__ void full_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
 __device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float frcp(float x) { return __builtin_amdgcn_rcpf(x); }
-__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+__device__ __forceinline__ float bf_lo(uint32_t x) { return __uint_as_float(x << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void *p, uint64_t bytes) {
+    const uint32_t n = bytes > 0xffffffffull ? 0xffffffffu : (uint32_t)bytes;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)n, kRsrcFlags);
+}
+__device__ __forceinline__ uint32_t bld32(rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
+}
+__device__ __forceinline__ u32x2 bld64(rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0);
+}
+template <int AUX = 0>
+__device__ __forceinline__ u32x4 bld128(rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, AUX);
+}
 
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
@@ -148,106 +183,136 @@ __device__ __forceinline__ typename C::Frag scale8(const typename C::Frag &f, co
     }
     return r;
 }
+// 8 consecutive operands from global memory through a buffer resource.
+template <class C, int AUX>
+__device__ __forceinline__ typename C::Frag gld8(rsrc_t r, uint32_t off) {
+    if constexpr (C::F32) {
+        const u32x4 a = bld128<AUX>(r, off), b = bld128<AUX>(r, off + 16);
+        return f32x8{__uint_as_float(a[0]), __uint_as_float(a[1]), __uint_as_float(a[2]), __uint_as_float(a[3]),
+                     __uint_as_float(b[0]), __uint_as_float(b[1]), __uint_as_float(b[2]), __uint_as_float(b[3])};
+    } else {
+        const u32x4 a = bld128<AUX>(r, off);
+        return __builtin_bit_cast(f16x8, a);
+    }
+}
+// 8 consecutive raw inputs (bf16 or fp32) from global memory as operands.
+template <class C>
+__device__ __forceinline__ typename C::Frag gld8_in(rsrc_t r, uint32_t off) {
+    if constexpr (C::F32) {
+        return gld8<C, 0>(r, off);
+    } else {
+        const u32x4 x = bld128(r, off);
+        typename C::Frag f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            f[2 * e] = (f16)bf_lo(x[e]);
+            f[2 * e + 1] = (f16)bf_hi(x[e]);
+        }
+        return f;
+    }
+}
 
 // ------------------------------------------------------------------------------------
 // Raw input of one unit (64-token tile x one slab of key channels), prefetched into
 // registers.  Thread (wave w, lane) holds rows 16w..16w+15 of the tile for its CPL key
 // channels; value pieces are rows 4*(tid>>4)+e, columns 4*(tid&15)..+3 of the 64x64 tile.
-template <bool F32, int CPL>
-struct InPack;
-template <>
-struct InPack<false, 2> {
-    uint32_t x;
-    __device__ float get(int c) const { return c == 0 ? __uint_as_float(x << 16) : __uint_as_float(x & 0xffff0000u); }
-};
-template <>
-struct InPack<false, 1> {
-    uint16_t x;
-    __device__ float get(int) const { return bf16_to_f32(x); }
-};
-template <>
-struct InPack<true, 1> {
-    float x;
-    __device__ float get(int) const { return x; }
-};
-
-template <bool F32>
-struct VPiece;
-template <>
-struct VPiece<false> {
-    uint2 x;
-    __device__ float get(int j) const {
-        const uint32_t w = (j < 2) ? x.x : x.y;
-        return (j & 1) ? __uint_as_float(w & 0xffff0000u) : __uint_as_float(w << 16);
-    }
-};
-template <>
-struct VPiece<true> {
-    float4 x;
-    __device__ float get(int j) const { return j == 0 ? x.x : j == 1 ? x.y : j == 2 ? x.z : x.w; }
-};
-
 template <class C>
 struct Raw {
-    InPack<C::F32, C::CPL> q[16], k[16];
-    float la[C::CH ? 16 : 1][C::CPL];
-    float las, lis;  // scalar log gate / log input gate of row (tile start + lane)
-    VPiece<C::F32> v[4];
+    uint32_t q[16], k[16];              // CPL channels (bf16 pair, bf16 in the low half, or fp32 bits)
+    float la[C::CH ? 16 : 1][C::CPL];   // per-channel log gates
+    float las, lis;                     // log gate / log input gate of row (tile start + lane)
+    uint32_t v[4][C::F32 ? 4 : 2];      // 4 values of one row
+    __device__ float qf(int r, int c) const { return C::F32 ? __uint_as_float(q[r]) : (c ? bf_hi(q[r]) : bf_lo(q[r])); }
+    __device__ float kf(int r, int c) const { return C::F32 ? __uint_as_float(k[r]) : (c ? bf_hi(k[r]) : bf_lo(k[r])); }
+    __device__ float vf(int e, int j) const {
+        if constexpr (C::F32) return __uint_as_float(v[e][j]);
+        else return (j & 1) ? bf_hi(v[e][j >> 1]) : bf_lo(v[e][j >> 1]);
+    }
 };
 
-// Per-(batch, head) base pointers and gate addressing.
-template <class C>
-struct Base {
-    const typename C::InT *q, *k, *v;
-    const float *la;  // per-channel: [L][Dk]; head: [L]; head_const: one value; none: null
-    const float *li;  // [L] or null
-    int L, Dv, gate;
+// Buffer resources of one (batch, head) slice.
+struct Rs {
+    rsrc_t q, k, v, la, li, out;
+    int gate, L;
+    bool has_li;
 };
+
+template <class C>
+__device__ __forceinline__ Rs make_rs(const KArgs &a, int bh, int h) {
+    Rs r;
+    const size_t bhL = (size_t)bh * a.L;
+    const uint64_t L = (uint64_t)a.L;
+    r.q = make_rsrc(reinterpret_cast<const char *>(a.q) + bhL * C::DK * C::IB, L * C::DK * C::IB);
+    r.k = make_rsrc(reinterpret_cast<const char *>(a.k) + bhL * C::DK * C::IB, L * C::DK * C::IB);
+    r.v = make_rsrc(reinterpret_cast<const char *>(a.v) + bhL * a.Dv * C::IB, L * a.Dv * C::IB);
+    r.out = make_rsrc(a.out + bhL * a.Dv, L * a.Dv * 4);
+    if (a.gate == GLA_GATE_CHANNEL)
+        r.la = make_rsrc(a.la + bhL * C::DK, L * C::DK * 4);
+    else if (a.gate == GLA_GATE_HEAD)
+        r.la = make_rsrc(a.la + bhL, L * 4);
+    else if (a.gate == GLA_GATE_HEAD_CONST)
+        r.la = make_rsrc(a.la + h, 4);
+    else
+        r.la = make_rsrc(a.out, 0);  // reads return zero
+    r.li = a.li ? make_rsrc(a.li + bhL, L * 4) : make_rsrc(a.out, 0);
+    r.gate = a.gate;
+    r.L = a.L;
+    r.has_li = a.li != nullptr;
+    return r;
+}
 
 template <class C, bool WQ>
-__device__ __forceinline__ void load_unit(Raw<C> &r, const Base<C> &b, int T0, int sl, bool with_v, int w,
-                                          int lane, int tid, int dv0) {
-    using P = InPack<C::F32, C::CPL>;
+__device__ __forceinline__ void load_unit(Raw<C> &r, const Rs &rs, int T0, int sl, bool with_v, int w, int lane,
+                                          int tid, int dv0, int Dv) {
     const int ch0 = sl * C::SLAB + C::CPL * lane;
+    const uint32_t row0 = (uint32_t)(T0 + 16 * w);
+    const uint32_t qoff = (row0 * C::DK + ch0) * C::IB;
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) {
-        const int t = T0 + 16 * w + rr;
-        const bool ok = t < b.L;
-        const size_t off = (size_t)t * C::DK + ch0;
-        if constexpr (WQ) r.q[rr].x = ok ? *reinterpret_cast<const decltype(P::x) *>(b.q + off) : decltype(P::x)(0);
-        r.k[rr].x = ok ? *reinterpret_cast<const decltype(P::x) *>(b.k + off) : decltype(P::x)(0);
+        const uint32_t off = qoff + rr * C::DK * C::IB;
+        if constexpr (C::CPL == 2 || C::F32) {
+            if constexpr (WQ) r.q[rr] = bld32(rs.q, off);
+            r.k[rr] = bld32(rs.k, off);
+        } else {
+            if constexpr (WQ) r.q[rr] = __builtin_amdgcn_raw_buffer_load_b16(rs.q, (int)off, 0, 0);
+            r.k[rr] = __builtin_amdgcn_raw_buffer_load_b16(rs.k, (int)off, 0, 0);
+        }
         if constexpr (C::CH) {
+            const uint32_t goff = (row0 * C::DK + ch0 + rr * C::DK) * 4u;
             if constexpr (C::CPL == 2) {
-                const float2 g2 = ok ? *reinterpret_cast<const float2 *>(b.la + off) : make_float2(0.f, 0.f);
-                r.la[rr][0] = g2.x;
-                r.la[rr][1] = g2.y;
+                const u32x2 g2 = bld64(rs.la, goff);
+                r.la[rr][0] = __uint_as_float(g2[0]);
+                r.la[rr][1] = __uint_as_float(g2[1]);
             } else {
-                r.la[rr][0] = ok ? b.la[off] : 0.f;
+                r.la[rr][0] = __uint_as_float(bld32(rs.la, goff));
             }
         }
     }
-    {
-        const int t = T0 + lane;
-        const bool ok = t < b.L;
-        float x = 0.f;
-        if constexpr (!C::CH) {
-            if (ok && b.gate == GLA_GATE_HEAD) x = b.la[t];
-            if (ok && b.gate == GLA_GATE_HEAD_CONST) x = b.la[0];
-        }
-        r.las = x;
-        r.lis = (ok && b.li) ? b.li[t] : 0.f;
+    const uint32_t t = (uint32_t)(T0 + lane);
+    if constexpr (!C::CH) {
+        // per head: [L]; fixed per head: one value, valid while the row exists
+        if (rs.gate == GLA_GATE_HEAD)
+            r.las = __uint_as_float(bld32(rs.la, t * 4u));
+        else if (rs.gate == GLA_GATE_HEAD_CONST)
+            r.las = (int)t < rs.L ? __uint_as_float(bld32(rs.la, 0)) : 0.f;
+        else
+            r.las = 0.f;
     }
+    r.lis = __uint_as_float(bld32(rs.li, t * 4u));
     if (with_v) {
-        const int c0 = dv0 + 4 * (tid & 15);
+        const uint32_t c0 = dv0 + 4 * (tid & 15);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const int t = T0 + 4 * (tid >> 4) + e;
-            const bool ok = t < b.L;
-            const typename C::InT *p = b.v + (size_t)t * b.Dv + c0;
-            if constexpr (C::F32)
-                r.v[e].x = ok ? *reinterpret_cast<const float4 *>(p) : make_float4(0.f, 0.f, 0.f, 0.f);
-            else
-                r.v[e].x = ok ? *reinterpret_cast<const uint2 *>(p) : make_uint2(0u, 0u);
+            const uint32_t off = ((uint32_t)(T0 + 4 * (tid >> 4) + e) * Dv + c0) * C::IB;
+            if constexpr (C::F32) {
+                const u32x4 x = bld128(rs.v, off);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) r.v[e][j] = x[j];
+            } else {
+                const u32x2 x = bld64(rs.v, off);
+                r.v[e][0] = x[0];
+                r.v[e][1] = x[1];
+            }
         }
     }
 }
@@ -265,7 +330,7 @@ __device__ __forceinline__ void v_to_lds(const Raw<C> &r, typename C::OpT *sV, i
     for (int j = 0; j < 4; ++j) {
         H h4;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) h4[e] = (OpT)r.v[e].get(j);
+        for (int e = 0; e < 4; ++e) h4[e] = (OpT)r.vf(e, j);
         *reinterpret_cast<H *>(sV + ((p * 4 + g) * 64 + c0 + j) * 8 + hh * 4) = h4;
     }
 }
@@ -273,72 +338,89 @@ __device__ __forceinline__ void v_to_lds(const Raw<C> &r, typename C::OpT *sV, i
 // Slot of token s (0..63 in the tile) in the k-slot order of the value and key^T operands.
 __device__ __forceinline__ int kslot(int s) { return (((s >> 5) * 4 + ((s >> 2) & 3)) * 8) + ((s >> 4) & 1) * 4 + (s & 3); }
 
+// CPL operands of one row into LDS.
+template <class C>
+__device__ __forceinline__ void st_row(typename C::OpT *row, const float *x) {
+    if constexpr (C::CPL == 2) {
+        *reinterpret_cast<f16x2 *>(row) = f16x2{(f16)x[0], (f16)x[1]};
+    } else {
+        *row = (typename C::OpT)x[0];
+    }
+}
+
 // ------------------------------------------------------------------------------------
-// Gate preparation for one unit, per-channel gate.  Thread rows r of sub-block w.
-// Outputs (all factors <= 1 except 1/ablk):
-//   eq[r] = decay from the sub-block start through row r (inclusive), ek[r] = decay after
-//   row r to the sub-block end; ablk/ainv in LDS; pre = decay of the sub-blocks before w,
-//   post = after w; at = decay of the whole tile.
+// Per-channel gate of one unit.  Thread rows r of 16-token block w:
+//   eq[r] = decay from the block start through row r (inclusive), ek[r] = decay after row r
+//   to the block end; ab[u] = decay across block u (exchanged through LDS); at = decay
+//   across the tile.
 template <class C>
 struct ChGate {
     float eq[16][C::CPL], ek[16][C::CPL];
+    float ab[4][C::CPL];
     float pre[C::CPL], post[C::CPL], at[C::CPL];
     bool harsh;
 };
 
 template <class C>
-__device__ __forceinline__ void ch_gate(ChGate<C> &G, const Raw<C> &r, float *sAb, float *sAi, int w, int lane) {
-    float al[16][C::CPL];
-#pragma unroll
-    for (int rr = 0; rr < 16; ++rr)
-#pragma unroll
-        for (int c = 0; c < C::CPL; ++c) al[rr][c] = fexp2(r.la[rr][c] * kLog2e);
+__device__ __forceinline__ void ch_gate(ChGate<C> &G, const Raw<C> &r, float *sAb, int w, int lane) {
 #pragma unroll
     for (int c = 0; c < C::CPL; ++c) {
         float run = 1.f;
 #pragma unroll
         for (int rr = 0; rr < 16; ++rr) {
-            run *= al[rr][c];
+            const float al = fexp2(r.la[rr][c] * kLog2e);
+            G.ek[rr][c] = al;  // alpha, turned into the suffix product below
+            run *= al;
             G.eq[rr][c] = run;
         }
         run = 1.f;
 #pragma unroll
         for (int rr = 15; rr >= 0; --rr) {
+            const float al = G.ek[rr][c];
             G.ek[rr][c] = run;
-            run *= al[rr][c];
+            run *= al;
         }
     }
     bool small = false;
-#pragma unroll
-    for (int c = 0; c < C::CPL; ++c) {
-        const float aw = G.eq[15][c];
-        sAb[w * C::SLAB + C::CPL * lane + c] = aw;
-        sAi[w * C::SLAB + C::CPL * lane + c] = frcp(aw);
-        small |= !(aw >= C::kMinDiagDecay);
+    const int chl = C::CPL * lane;
+    if constexpr (C::CPL == 2) {
+        *reinterpret_cast<float2 *>(sAb + w * C::SLAB + chl) = make_float2(G.eq[15][0], G.eq[15][1]);
+    } else {
+        sAb[w * C::SLAB + chl] = G.eq[15][0];
     }
+#pragma unroll
+    for (int c = 0; c < C::CPL; ++c) small |= !(G.eq[15][c] >= C::kMinDiagDecay);
     G.harsh = __ballot(small) != 0ull;
     lds_barrier();
 #pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        if constexpr (C::CPL == 2) {
+            const float2 x = lds_ld<float2>(sAb + u * C::SLAB + chl);
+            G.ab[u][0] = x.x;
+            G.ab[u][1] = x.y;
+        } else {
+            G.ab[u][0] = sAb[u * C::SLAB + chl];
+        }
+    }
+#pragma unroll
     for (int c = 0; c < C::CPL; ++c) {
-        float pre = 1.f, post = 1.f, all = 1.f;
+        float pre = 1.f, post = 1.f;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            const float au = sAb[u * C::SLAB + C::CPL * lane + c];
-            all *= au;
-            if (u < w) pre *= au;
-            if (u > w) post *= au;
+            if (u < w) pre *= G.ab[u][c];
+            if (u > w) post *= G.ab[u][c];
         }
         G.pre[c] = pre;
         G.post[c] = post;
-        G.at[c] = all;
+        G.at[c] = pre * G.eq[15][c] * post;
     }
 }
 
-// Exact diagonal 16x16 score block of sub-block w over this slab's channels, for a
-// sub-block whose decay span is too large for scaled matrix-core operands: every pair
-// s <= t gets sum_d q_td k_sd 2^(u_td - u_sd) i_s with u the log2 running decay.
+// Exact diagonal 16x16 score block of block w over this slab's channels, for a block whose
+// decay span is too large for scaled matrix-core operands: every pair s <= t gets
+// sum_d q_td k_sd 2^(u_td - u_sd) i_s with u the log2 running decay.
 template <class C>
-__device__ void ch_diag_exact(f32x4 &acc, const Raw<C> &r, const float ig[16], int lane) {
+__device__ __forceinline__ void ch_diag_exact(f32x4 &acc, const Raw<C> &r, const float *ig, int lane) {
     float u[16][C::CPL];
 #pragma unroll
     for (int c = 0; c < C::CPL; ++c) {
@@ -356,7 +438,7 @@ __device__ void ch_diag_exact(f32x4 &acc, const Raw<C> &r, const float ig[16], i
         for (int t = s; t < 16; ++t) {
             float part = 0.f;
 #pragma unroll
-            for (int c = 0; c < C::CPL; ++c) part += r.q[t].get(c) * r.k[s].get(c) * fexp2(u[t][c] - u[s][c]);
+            for (int c = 0; c < C::CPL; ++c) part += r.qf(t, c) * r.kf(s, c) * fexp2(u[t][c] - u[s][c]);
             const float tot = wave_sum(part * ig[s]);
             if (c16 == t && g == (s >> 2)) acc[s & 3] += tot;
         }
@@ -364,18 +446,43 @@ __device__ void ch_diag_exact(f32x4 &acc, const Raw<C> &r, const float ig[16], i
 }
 
 // ------------------------------------------------------------------------------------
-// The pairs of 16-token blocks (query block i, key block j <= i) of a diagonal tile that
-// each wave computes; wave w always owns the diagonal pair (w, w).
-__device__ __forceinline__ void pair_of(int w, int k, int &i, int &j) {
-    // k = 0: (w, w); k = 1, 2: off-diagonal pairs; (-1) when absent.
-    const int tab[4][2][2] = {{{1, 0}, {3, 2}}, {{2, 0}, {3, 1}}, {{2, 1}, {-1, -1}}, {{3, 0}, {-1, -1}}};
-    if (k == 0) {
-        i = w;
-        j = w;
+// Score blocks of a diagonal tile: pairs (query block i, key block j <= i).  Wave w computes
+// three pairs (waves 2 and 3 repeat one pair to keep the instruction stream uniform; its
+// result is not stored).  Operand rows (per-channel gate):
+//   diagonal (w, w):         KD block w  x  QD block w
+//   adjacent (i, i-1):       KO block i-1 x  QD block i
+//   (2,0), (3,1), (3,0):     referenced to the end of block 1 through X
+struct Pairs {
+    int i[3], j[3];
+    int arow[3], brow[3];  // row offsets in the selected arrays
+    bool ax[3], bx[3];     // operand from X instead of (KO | KD | raw k) / (QD | raw q)
+};
+__device__ __forceinline__ void set_pair(Pairs &P, int kp, int i, int j, bool ch) {
+    P.i[kp] = i;
+    P.j[kp] = j;
+    if (ch && j + 1 < i) {
+        // keys of block j and queries of block i referenced to the end of block 1
+        P.ax[kp] = j == 0;
+        P.arow[kp] = j == 0 ? 0 : 16 * j;
+        P.bx[kp] = i == 3;
+        P.brow[kp] = i == 3 ? 16 : 16 * i;
     } else {
-        i = tab[w][k - 1][0];
-        j = tab[w][k - 1][1];
+        P.ax[kp] = false;
+        P.arow[kp] = 16 * j;
+        P.bx[kp] = false;
+        P.brow[kp] = 16 * i;
     }
+}
+__device__ __forceinline__ Pairs make_pairs(int w, bool ch) {
+    Pairs P;
+    set_pair(P, 0, w, w, ch);
+    switch (w) {
+        case 0: set_pair(P, 1, 1, 0, ch); set_pair(P, 2, 3, 2, ch); break;
+        case 1: set_pair(P, 1, 2, 0, ch); set_pair(P, 2, 3, 1, ch); break;
+        case 2: set_pair(P, 1, 2, 1, ch); set_pair(P, 2, 2, 1, ch); break;
+        default: set_pair(P, 1, 3, 0, ch); set_pair(P, 2, 3, 0, ch); break;
+    }
+    return P;
 }
 
 // ------------------------------------------------------------------------------------
@@ -384,25 +491,26 @@ template <class C>
 __global__ __launch_bounds__(256, 1) void chunk_output_kernel(KArgs a) {
     using OpT = typename C::OpT;
     using Frag = typename C::Frag;
-    using InT = typename C::InT;
+    using Half = typename C::Half;
     extern __shared__ __align__(256) unsigned char smem[];
     const LdsPlan lp = lds_plan(C::OPB, C::DK, C::CH, a.nt);
     OpT *sQ = reinterpret_cast<OpT *>(smem + lp.q);
     OpT *sK = reinterpret_cast<OpT *>(smem + lp.k);
+    OpT *sKD = reinterpret_cast<OpT *>(smem + lp.kd);
+    OpT *sX = reinterpret_cast<OpT *>(smem + lp.x);
     OpT *sQI = reinterpret_cast<OpT *>(smem + lp.qi);
     OpT *sKT = reinterpret_cast<OpT *>(smem + lp.kst);
     OpT *sP = reinterpret_cast<OpT *>(smem + lp.pbuf);
     OpT *sV = reinterpret_cast<OpT *>(smem + lp.vb);
     OpT *sVo = reinterpret_cast<OpT *>(smem + lp.voff);
-    OpT *sPK = reinterpret_cast<OpT *>(smem + lp.prevke);
     float *sAb = reinterpret_cast<float *>(smem + lp.ablk);
-    float *sAi = reinterpret_cast<float *>(smem + lp.ainv);
     float *sQTF = reinterpret_cast<float *>(smem + lp.qtf);
     float *sAt = reinterpret_cast<float *>(smem + lp.atile);
     float *sBr = reinterpret_cast<float *>(smem + lp.brow);
     float *sLr = reinterpret_cast<float *>(smem + lp.lrow);
 
-    int id = xcd_remap((int)blockIdx.x, a.nwg);
+    const int wg = (int)blockIdx.x;
+    int id = xcd_remap(wg, a.nwg);
     const int dvt = id % a.ndv;
     id /= a.ndv;
     const int seg = id % a.nseg;
@@ -415,20 +523,13 @@ __global__ __launch_bounds__(256, 1) void chunk_output_kernel(KArgs a) {
     const int col = dv0 + 16 * w + c16;  // value column of this lane's accumulators
     const int t_begin = seg * a.seg_len;
     const int t_end = min(L, t_begin + a.seg_len);
-    const size_t bhL = (size_t)bh * L;
-
-    Base<C> b;
-    b.q = reinterpret_cast<const InT *>(a.q) + bhL * C::DK;
-    b.k = reinterpret_cast<const InT *>(a.k) + bhL * C::DK;
-    b.v = reinterpret_cast<const InT *>(a.v) + bhL * Dv;
-    b.la = a.gate == GLA_GATE_CHANNEL ? a.la + bhL * C::DK
-           : a.gate == GLA_GATE_HEAD  ? a.la + bhL
-           : a.gate == GLA_GATE_HEAD_CONST ? a.la + h
-                                           : nullptr;
-    b.li = a.li ? a.li + bhL : nullptr;
-    b.L = L;
-    b.Dv = Dv;
-    b.gate = a.gate;
+    const int chl = C::CPL * lane;
+    const Rs rs = make_rs<C>(a, bh, h);
+    rsrc_t rke = make_rsrc(a.out, 0);
+    if constexpr (C::CH && C::MT) {
+        const uint64_t kb = ke_scratch_bytes(C::OPB, C::DK, true, a.nt);
+        rke = make_rsrc(reinterpret_cast<char *>(a.ws_ke) + (uint64_t)wg * kb, kb);
+    }
 
     // State S[d][col], d = 16n + 4g + e, held across chunks in registers.
     f32x4 S[C::NBD];
@@ -448,7 +549,7 @@ __global__ __launch_bounds__(256, 1) void chunk_output_kernel(KArgs a) {
     f32x4 dS[C::MT ? C::NBD : 1];
 
     Raw<C> raw;
-    if (t_begin < t_end) load_unit<C, true>(raw, b, t_begin, 0, true, w, lane, tid, dv0);
+    if (t_begin < t_end) load_unit<C, true>(raw, rs, t_begin, 0, true, w, lane, tid, dv0, Dv);
 
     for (int c0 = t_begin; c0 < t_end; c0 += a.chunk) {
         float Wc[C::NSLAB][C::CPL];  // per-channel decay from the chunk start to the tile start
@@ -472,71 +573,89 @@ __global__ __launch_bounds__(256, 1) void chunk_output_kernel(KArgs a) {
 #pragma unroll
             for (int i = 0; i < 3; ++i) Pd[i] = f32x4{0.f, 0.f, 0.f, 0.f};
             float Tt = 0.f;  // scalar gates: log2 decay across this tile
+            Frag vfr[2];
+            bool harsh = false;
 
 #pragma unroll 1
             for (int sl = 0; sl < C::NSLAB; ++sl) {
                 OpT *sQs = sQ + (C::MT ? sl : 0) * 64 * C::RP;
-                bool harsh = false;
-                float ekr[16];  // scalar gates: key factor (tile end reference, input gate)
                 // ---------------- preparation of this unit -> LDS
                 if (sl == 0) v_to_lds<C>(raw, sV, tid);
                 if constexpr (C::CH) {
                     ChGate<C> G;
-                    ch_gate<C>(G, raw, sAb, sAi, w, lane);
+                    ch_gate<C>(G, raw, sAb, w, lane);
                     harsh = G.harsh;
                     float ig[16];
-                    {
+                    if (rs.has_li) {
                         const float y = raw.lis * kLog2e;
 #pragma unroll
                         for (int rr = 0; rr < 16; ++rr) ig[rr] = fexp2(__shfl(y, 16 * w + rr));
+                    } else {
+#pragma unroll
+                        for (int rr = 0; rr < 16; ++rr) ig[rr] = 1.f;
                     }
-                    if (harsh) ch_diag_exact<C>(Pd[0], raw, ig, lane);
-                    float fqi[C::CPL];
+                    if (harsh) {
+                        f32x4 t = Pd[0];
+                        ch_diag_exact<C>(t, raw, ig, lane);
+                        Pd[0] = t;
+                    }
+                    float fqi[C::CPL], ainv[C::CPL], xs[C::CPL];
 #pragma unroll
                     for (int c = 0; c < C::CPL; ++c) {
                         fqi[c] = Wc[sl][c] * G.pre[c];
-                        const int d = sl * C::SLAB + C::CPL * lane + c;
+                        ainv[c] = frcp(G.eq[15][c]);
+                        xs[c] = w == 0 ? G.ab[1][c] : G.ab[2][c];  // X scale for waves 0 and 3
+                        const int d = sl * C::SLAB + chl + c;
                         if (w == 0) sAt[tau * C::DK + d] = G.at[c];
                         if constexpr (C::MT) sQTF[w * C::DK + d] = G.pre[c];
                         Wc[sl][c] *= G.at[c];
                     }
-                    const int chl = C::CPL * lane;
-                    OpT *pk = nullptr;
-                    if constexpr (C::MT) {
-                        if (tau < a.nt - 1) pk = sPK + (size_t)((tau * C::NSLAB + sl) * 64) * C::RP;
-                    }
+                    const bool mt_store = C::MT && tau < a.nt - 1;
 #pragma unroll
                     for (int g4 = 0; g4 < 4; ++g4) {
-                        typename C::Half kt4[C::CPL];
+                        Half kt4[C::CPL];
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
                             const int rr = 4 * g4 + e;
                             const int row = 16 * w + rr;
-                            OpT qd[C::CPL], ko[C::CPL], qi[C::CPL], ke[C::CPL];
+                            float qd[C::CPL], ko[C::CPL], kd[C::CPL], qi[C::CPL], ke[C::CPL], xv[C::CPL];
 #pragma unroll
                             for (int c = 0; c < C::CPL; ++c) {
-                                const float qf = raw.q[rr].get(c) * G.eq[rr][c];
-                                const float kf = raw.k[rr].get(c) * G.ek[rr][c] * ig[rr];
-                                qd[c] = (OpT)qf;
-                                ko[c] = (OpT)kf;
-                                qi[c] = (OpT)(qf * fqi[c]);
-                                ke[c] = (OpT)(kf * G.post[c]);
-                                kt4[c][e] = ke[c];
+                                qd[c] = raw.qf(rr, c) * G.eq[rr][c];
+                                ko[c] = raw.kf(rr, c) * ig[rr] * G.ek[rr][c];
+                                kd[c] = ko[c] * ainv[c];
+                                qi[c] = qd[c] * fqi[c];
+                                ke[c] = ko[c] * G.post[c];
+                                xv[c] = (w == 0 ? ko[c] : qd[c]) * xs[c];
+                                kt4[c][e] = (OpT)ke[c];
                             }
-#pragma unroll
-                            for (int c = 0; c < C::CPL; ++c) {
-                                sQs[row * C::RP + chl + c] = qd[c];
-                                sK[row * C::RP + chl + c] = ko[c];
-                                sQI[row * C::RP + chl + c] = qi[c];
-                                if constexpr (C::MT) {
-                                    if (pk) pk[row * C::RP + chl + c] = ke[c];
+                            st_row<C>(sQs + row * C::RP + chl, qd);
+                            st_row<C>(sK + row * C::RP + chl, ko);
+                            st_row<C>(sKD + row * C::RP + chl, kd);
+                            st_row<C>(sQI + row * C::RP + chl, qi);
+                            if (w == 0) st_row<C>(sX + rr * C::RP + chl, xv);
+                            if (w == 3) st_row<C>(sX + (16 + rr) * C::RP + chl, xv);
+                            if constexpr (C::MT) {
+                                if (mt_store) {
+                                    const uint32_t off = (uint32_t)(((tau * 64 + row) * C::DK + sl * C::SLAB + chl) * C::OPB);
+                                    uint32_t bits;
+                                    if constexpr (C::CPL == 2) {
+                                        bits = __builtin_bit_cast(uint32_t, f16x2{(f16)ke[0], (f16)ke[1]});
+                                    } else if constexpr (C::F32) {
+                                        bits = __float_as_uint(ke[0]);
+                                    } else {
+                                        bits = (uint32_t)__builtin_bit_cast(uint16_t, (f16)ke[0]);
+                                    }
+                                    if constexpr (C::OPB == 2 && C::CPL == 1)
+                                        __builtin_amdgcn_raw_buffer_store_b16((uint16_t)bits, rke, (int)off, 0, 0);
+                                    else
+                                        __builtin_amdgcn_raw_buffer_store_b32(bits, rke, (int)off, 0, 0);
                                 }
                             }
                         }
 #pragma unroll
                         for (int c = 0; c < C::CPL; ++c)
-                            *reinterpret_cast<typename C::Half *>(sKT + (chl + c) * C::KTP + kslot(16 * w + 4 * g4)) =
-                                kt4[c];
+                            *reinterpret_cast<Half *>(sKT + (chl + c) * C::KTP + kslot(16 * w + 4 * g4)) = kt4[c];
                     }
                 } else {
                     // scalar gates: running log2 decay over the tile's rows (lane = row)
@@ -548,39 +667,37 @@ __global__ __launch_bounds__(256, 1) void chunk_output_kernel(KArgs a) {
                         sBr[kTile * tau + lane] = Bc + bl;
                         sLr[kTile * tau + lane] = y;
                     }
-                    float eb[16];
-#pragma unroll
-                    for (int rr = 0; rr < 16; ++rr) {
-                        const float blr = __shfl(bl, 16 * w + rr);
-                        const float yr = __shfl(y, 16 * w + rr);
-                        eb[rr] = fexp2(Bc + blr);
-                        ekr[rr] = fexp2(Tt - blr + yr);
-                    }
-                    const int chl = C::CPL * lane;
 #pragma unroll
                     for (int g4 = 0; g4 < 4; ++g4) {
-                        typename C::Half kt4[C::CPL];
+                        Half kt4[C::CPL];
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
                             const int rr = 4 * g4 + e;
                             const int row = 16 * w + rr;
+                            const float blr = __shfl(bl, 16 * w + rr);
+                            const float eb = fexp2(Bc + blr);
+                            const float ekr = fexp2(Tt - blr + __shfl(y, 16 * w + rr));
+                            float qv[C::CPL], kv[C::CPL], qi[C::CPL];
 #pragma unroll
                             for (int c = 0; c < C::CPL; ++c) {
-                                const float qf = raw.q[rr].get(c);
-                                const float kf = raw.k[rr].get(c);
-                                sQs[row * C::RP + chl + c] = (OpT)qf;
-                                sK[row * C::RP + chl + c] = (OpT)kf;
-                                sQI[row * C::RP + chl + c] = (OpT)(qf * eb[rr]);
-                                kt4[c][e] = (OpT)(kf * ekr[rr]);
+                                qv[c] = raw.qf(rr, c);
+                                kv[c] = raw.kf(rr, c);
+                                qi[c] = qv[c] * eb;
+                                kt4[c][e] = (OpT)(kv[c] * ekr);
                             }
+                            st_row<C>(sQs + row * C::RP + chl, qv);
+                            st_row<C>(sK + row * C::RP + chl, kv);
+                            st_row<C>(sQI + row * C::RP + chl, qi);
                         }
 #pragma unroll
                         for (int c = 0; c < C::CPL; ++c)
-                            *reinterpret_cast<typename C::Half *>(sKT + (chl + c) * C::KTP + kslot(16 * w + 4 * g4)) =
-                                kt4[c];
+                            *reinterpret_cast<Half *>(sKT + (chl + c) * C::KTP + kslot(16 * w + 4 * g4)) = kt4[c];
                     }
                 }
-                lds_barrier();
+                if constexpr (C::CH && C::MT)
+                    full_barrier();  // also publishes this tile's key scratch to the other waves
+                else
+                    lds_barrier();
 
                 // ---------------- prefetch the next unit while this one computes
                 {
@@ -593,7 +710,37 @@ __global__ __launch_bounds__(256, 1) void chunk_output_kernel(KArgs a) {
                     } else if (c0 + a.chunk < t_end) {
                         Tn = c0 + a.chunk;
                     }
-                    if (Tn >= 0) load_unit<C, true>(raw, b, Tn, sn, sn == 0, w, lane, tid, dv0);
+                    if (Tn >= 0) load_unit<C, true>(raw, rs, Tn, sn, sn == 0, w, lane, tid, dv0, Dv);
+                }
+
+                if (sl == 0) {
+#pragma unroll
+                    for (int p = 0; p < 2; ++p) vfr[p] = ld8<C>(sV + ((p * 4 + g) * 64 + 16 * w + c16) * 8);
+                }
+
+                // ---------------- diagonal-tile score blocks (transposed): P^T(j,i) over this slab
+                {
+                    const Pairs pr = make_pairs(w, C::CH);
+                    const OpT *pa[3], *pb[3];
+#pragma unroll
+                    for (int kp = 0; kp < 3; ++kp) {
+                        const OpT *ka = (C::CH && kp == 0) ? sKD : (pr.ax[kp] ? sX : sK);
+                        pa[kp] = ka + (pr.arow[kp] + c16) * C::RP;
+                        pb[kp] = (pr.bx[kp] ? sX : sQs) + (pr.brow[kp] + c16) * C::RP;
+                    }
+#pragma unroll
+                    for (int m = 0; m < C::KSTEP; ++m) {
+                        const int ch = 32 * m + 8 * g;
+                        Frag af[3], bf[3];
+#pragma unroll
+                        for (int kp = 0; kp < 3; ++kp) {
+                            af[kp] = ld8<C>(pa[kp] + ch);
+                            bf[kp] = ld8<C>(pb[kp] + ch);
+                        }
+                        if (!harsh) Pd[0] = mma(af[0], bf[0], Pd[0]);
+                        Pd[1] = mma(af[1], bf[1], Pd[1]);
+                        Pd[2] = mma(af[2], bf[2], Pd[2]);
+                    }
                 }
 
                 // ---------------- inter-chunk term: O += QI . S (rows of this slab)
@@ -609,113 +756,94 @@ __global__ __launch_bounds__(256, 1) void chunk_output_kernel(KArgs a) {
                         }
                     }
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const OpT *row = sQI + (16 * i + c16) * C::RP;
-#pragma unroll
-                        for (int m = 0; m < C::KSTEP; ++m) {
-                            const Frag af = ld4x2<C>(row + 32 * m + 4 * g, row + 32 * m + 16 + 4 * g);
-                            O[i] = mma(af, sb[m], O[i]);
-                        }
-                    }
-                }
-
-                // ---------------- diagonal-tile score blocks (transposed): P^T(j,i) over this slab
-#pragma unroll
-                for (int kp = 0; kp < 3; ++kp) {
-                    int i, j;
-                    pair_of(w, kp, i, j);
-                    if (i < 0) continue;
-                    if (kp == 0 && harsh) continue;  // computed exactly during preparation
-                    f32x4 acc = Pd[kp];
-                    const OpT *krow = sK + (16 * j + c16) * C::RP;
-                    const OpT *qrow = sQs + (16 * i + c16) * C::RP;
-#pragma unroll
                     for (int m = 0; m < C::KSTEP; ++m) {
-                        const int ch = 32 * m + 8 * g;
-                        Frag af = ld8<C>(krow + ch);
-                        Frag bf = ld8<C>(qrow + ch);
-                        if constexpr (C::CH) {
-                            if (i == j) {
-                                af = scale8<C>(af, lds_ld<f32x4>(sAi + w * C::SLAB + ch),
-                                               lds_ld<f32x4>(sAi + w * C::SLAB + ch + 4));
-                            } else if (j + 1 < i) {
-                                f32x4 r0 = lds_ld<f32x4>(sAb + (j + 1) * C::SLAB + ch);
-                                f32x4 r1 = lds_ld<f32x4>(sAb + (j + 1) * C::SLAB + ch + 4);
-                                if (j + 2 < i) {
-                                    r0 *= lds_ld<f32x4>(sAb + (j + 2) * C::SLAB + ch);
-                                    r1 *= lds_ld<f32x4>(sAb + (j + 2) * C::SLAB + ch + 4);
-                                }
-                                bf = scale8<C>(bf, r0, r1);
-                            }
+                        Frag qa[4];
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const OpT *row = sQI + (16 * i + c16) * C::RP + 32 * m + 4 * g;
+                            qa[i] = ld4x2<C>(row, row + 16);
                         }
-                        acc = mma(af, bf, acc);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) O[i] = mma(qa[i], sb[m], O[i]);
                     }
-                    Pd[kp] = acc;
                 }
 
                 // ---------------- chunk-state contribution of this tile (rows of this slab)
+                {
+                    f32x4 acc[C::NBS];
 #pragma unroll
-                for (int n = 0; n < C::NBS; ++n) {
-                    const int nn = sl * C::NBS + n;
-                    f32x4 at;
-                    if constexpr (C::CH) {
-                        at = lds_ld<f32x4>(sAt + tau * C::DK + sl * C::SLAB + 16 * n + 4 * g);
-                    } else {
-                        const float x = fexp2(Tt);
-                        at = f32x4{x, x, x, x};
+                    for (int n = 0; n < C::NBS; ++n) {
+                        const int nn = sl * C::NBS + n;
+                        f32x4 at;
+                        if constexpr (C::CH) {
+                            at = lds_ld<f32x4>(sAt + tau * C::DK + sl * C::SLAB + 16 * n + 4 * g);
+                        } else {
+                            const float x = fexp2(Tt);
+                            at = f32x4{x, x, x, x};
+                        }
+                        acc[n] = (C::MT ? dS[nn] : S[nn]) * at;
                     }
-                    f32x4 acc = C::MT ? dS[nn] : S[nn];
-                    acc *= at;
-                    const OpT *kt = sKT + (16 * n + c16) * C::KTP;
 #pragma unroll
                     for (int p = 0; p < 2; ++p) {
-                        const Frag af = ld8<C>(kt + (p * 4 + g) * 8);
-                        const Frag bf = ld8<C>(sV + ((p * 4 + g) * 64 + 16 * w + c16) * 8);
-                        acc = mma(af, bf, acc);
+                        Frag ka[C::NBS];
+#pragma unroll
+                        for (int n = 0; n < C::NBS; ++n) ka[n] = ld8<C>(sKT + (16 * n + c16) * C::KTP + (p * 4 + g) * 8);
+#pragma unroll
+                        for (int n = 0; n < C::NBS; ++n) acc[n] = mma(ka[n], vfr[p], acc[n]);
                     }
-                    if constexpr (C::MT)
-                        dS[nn] = acc;
-                    else
-                        S[nn] = acc;
+#pragma unroll
+                    for (int n = 0; n < C::NBS; ++n) {
+                        const int nn = sl * C::NBS + n;
+                        if constexpr (C::MT)
+                            dS[nn] = acc[n];
+                        else
+                            S[nn] = acc[n];
+                    }
                 }
-                lds_barrier();
+                if (sl + 1 < C::NSLAB) lds_barrier();  // the next slab rewrites the slab arrays
             }  // slabs
 
             // ---------------- diagonal tile: mask, store scores, multiply by values
+            {
+                const Pairs pr = make_pairs(w, C::CH);
 #pragma unroll
-            for (int kp = 0; kp < 3; ++kp) {
-                int i, j;
-                pair_of(w, kp, i, j);
-                if (i < 0) continue;
-                typename C::Half pv;
+                for (int kp = 0; kp < 3; ++kp) {
+                    if (kp == 2 && w >= 2) continue;  // repeated pair
+                    const int i = pr.i[kp], j = pr.j[kp];
+                    Half pv;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int s = 4 * g + e;  // key row in block j
-                    float x = Pd[kp][e];
-                    if (i == j && s > c16) x = 0.f;
-                    if constexpr (!C::CH) {
-                        if (!(i == j && s > c16)) {
-                            const int ts = kTile * tau + 16 * i + c16, ss = kTile * tau + 16 * j + s;
-                            x *= fexp2(sBr[ts] - sBr[ss] + sLr[ss]);
+                    for (int e = 0; e < 4; ++e) {
+                        const int s = 4 * g + e;  // key row in block j
+                        const bool masked = i == j && s > c16;
+                        float x = masked ? 0.f : Pd[kp][e];
+                        if constexpr (!C::CH) {
+                            if (!masked) {
+                                const int ts = kTile * tau + 16 * i + c16, ss = kTile * tau + 16 * j + s;
+                                x *= fexp2(sBr[ts] - sBr[ss] + sLr[ss]);
+                            }
                         }
+                        pv[e] = (OpT)x;
                     }
-                    pv[e] = (OpT)x;
+                    *reinterpret_cast<Half *>(sP + ((i * 2 + (j >> 1)) * 64 + lane) * 8 + 4 * (j & 1)) = pv;
                 }
-                *reinterpret_cast<typename C::Half *>(sP + ((i * 2 + (j >> 1)) * 64 + lane) * 8 + 4 * (j & 1)) = pv;
-            }
-            if (w == 0 || w == 2) {  // key blocks after the query block stay zero
-                const typename C::Half z{(OpT)0.f, (OpT)0.f, (OpT)0.f, (OpT)0.f};
-                *reinterpret_cast<typename C::Half *>(sP + ((w * 2 + (w >> 1)) * 64 + lane) * 8 + 4) = z;
+                if (w == 0 || w == 2) {  // key blocks after the query block stay zero
+                    const Half z{(OpT)0.f, (OpT)0.f, (OpT)0.f, (OpT)0.f};
+                    *reinterpret_cast<Half *>(sP + ((w * 2 + (w >> 1)) * 64 + lane) * 8 + 4) = z;
+                }
             }
             lds_barrier();
+            {
+                Frag pa[6];
+                pa[0] = ld8<C>(sP + ((0 * 2 + 0) * 64 + lane) * 8);
+                pa[1] = ld8<C>(sP + ((1 * 2 + 0) * 64 + lane) * 8);
+                pa[2] = ld8<C>(sP + ((2 * 2 + 0) * 64 + lane) * 8);
+                pa[3] = ld8<C>(sP + ((3 * 2 + 0) * 64 + lane) * 8);
+                pa[4] = ld8<C>(sP + ((2 * 2 + 1) * 64 + lane) * 8);
+                pa[5] = ld8<C>(sP + ((3 * 2 + 1) * 64 + lane) * 8);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int np = (i >> 1) + 1;
-                for (int p = 0; p < np; ++p) {
-                    const Frag af = ld8<C>(sP + ((i * 2 + p) * 64 + lane) * 8);
-                    const Frag bf = ld8<C>(sV + ((p * 4 + g) * 64 + 16 * w + c16) * 8);
-                    O[i] = mma(af, bf, O[i]);
-                }
+                for (int i = 0; i < 4; ++i) O[i] = mma(pa[i], vfr[0], O[i]);
+                O[2] = mma(pa[4], vfr[1], O[2]);
+                O[3] = mma(pa[5], vfr[1], O[3]);
             }
 
             // ---------------- earlier tiles of the same chunk (large chunks)
@@ -726,15 +854,19 @@ __global__ __launch_bounds__(256, 1) void chunk_output_kernel(KArgs a) {
                     {
                         Raw<C> vr;
                         const int Tk = c0 + kTile * kj;
-                        const int cq = dv0 + 4 * (tid & 15);
+                        const uint32_t cq = dv0 + 4 * (tid & 15);
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
-                            const int t = Tk + 4 * (tid >> 4) + e;  // always < L (an earlier, full tile)
-                            const InT *p = b.v + (size_t)t * Dv + cq;
-                            if constexpr (C::F32)
-                                vr.v[e].x = *reinterpret_cast<const float4 *>(p);
-                            else
-                                vr.v[e].x = *reinterpret_cast<const uint2 *>(p);
+                            const uint32_t off = ((uint32_t)(Tk + 4 * (tid >> 4) + e) * Dv + cq) * C::IB;
+                            if constexpr (C::F32) {
+                                const u32x4 x = bld128(rs.v, off);
+#pragma unroll
+                                for (int jj = 0; jj < 4; ++jj) vr.v[e][jj] = x[jj];
+                            } else {
+                                const u32x2 x = bld64(rs.v, off);
+                                vr.v[e][0] = x[0];
+                                vr.v[e][1] = x[1];
+                            }
                         }
                         v_to_lds<C>(vr, sVo, tid);
                     }
@@ -748,6 +880,7 @@ __global__ __launch_bounds__(256, 1) void chunk_output_kernel(KArgs a) {
                         for (int m = 0; m < C::KSTEP; ++m) {
                             const int ch = 32 * m + 8 * g;
                             Frag bf = ld8<C>(qrow + ch);
+                            Frag af[4];
                             if constexpr (C::CH) {
                                 const int d = sl * C::SLAB + ch;
                                 f32x4 f0 = lds_ld<f32x4>(sQTF + w * C::DK + d);
@@ -757,36 +890,22 @@ __global__ __launch_bounds__(256, 1) void chunk_output_kernel(KArgs a) {
                                     f1 *= lds_ld<f32x4>(sAt + tp * C::DK + d + 4);
                                 }
                                 bf = scale8<C>(bf, f0, f1);
+#pragma unroll
+                                for (int j = 0; j < 4; ++j)
+                                    af[j] = gld8<C, 1>(rke, (uint32_t)(((kj * 64 + 16 * j + c16) * C::DK + d) * C::OPB));
+                            } else {
+#pragma unroll
+                                for (int j = 0; j < 4; ++j)
+                                    af[j] = gld8_in<C>(rs.k, (uint32_t)(((c0 + kTile * kj + 16 * j + c16) * C::DK +
+                                                                         sl * C::SLAB + ch) * C::IB));
                             }
 #pragma unroll
-                            for (int j = 0; j < 4; ++j) {
-                                Frag af;
-                                if constexpr (C::CH) {
-                                    af = ld8<C>(sPK + (size_t)((kj * C::NSLAB + sl) * 64 + 16 * j + c16) * C::RP + ch);
-                                } else {
-                                    const int t = c0 + kTile * kj + 16 * j + c16;
-                                    const InT *kp = b.k + (size_t)t * C::DK + sl * C::SLAB + ch;
-                                    if constexpr (C::F32) {
-                                        const float4 x0 = *reinterpret_cast<const float4 *>(kp);
-                                        const float4 x1 = *reinterpret_cast<const float4 *>(kp + 4);
-                                        af = f32x8{x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-                                    } else {
-                                        const uint4 x = *reinterpret_cast<const uint4 *>(kp);
-                                        const uint32_t wv[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-                                        for (int e = 0; e < 4; ++e) {
-                                            af[2 * e] = (OpT)__uint_as_float(wv[e] << 16);
-                                            af[2 * e + 1] = (OpT)__uint_as_float(wv[e] & 0xffff0000u);
-                                        }
-                                    }
-                                }
-                                Po[j] = mma(af, bf, Po[j]);
-                            }
+                            for (int j = 0; j < 4; ++j) Po[j] = mma(af[j], bf, Po[j]);
                         }
                     }
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
-                        typename C::Half pv;
+                        Half pv;
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
                             float x = Po[j][e];
@@ -796,30 +915,32 @@ __global__ __launch_bounds__(256, 1) void chunk_output_kernel(KArgs a) {
                             }
                             pv[e] = (OpT)x;
                         }
-                        *reinterpret_cast<typename C::Half *>(sP + ((w * 2 + (j >> 1)) * 64 + lane) * 8 + 4 * (j & 1)) =
-                            pv;
+                        *reinterpret_cast<Half *>(sP + ((w * 2 + (j >> 1)) * 64 + lane) * 8 + 4 * (j & 1)) = pv;
                     }
                     lds_barrier();
+                    {
+                        Frag vo[2], pa[8];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
+                        for (int p = 0; p < 2; ++p) vo[p] = ld8<C>(sVo + ((p * 4 + g) * 64 + 16 * w + c16) * 8);
 #pragma unroll
-                        for (int p = 0; p < 2; ++p) {
-                            const Frag af = ld8<C>(sP + ((i * 2 + p) * 64 + lane) * 8);
-                            const Frag bf = ld8<C>(sVo + ((p * 4 + g) * 64 + 16 * w + c16) * 8);
-                            O[i] = mma(af, bf, O[i]);
-                        }
+                        for (int q = 0; q < 8; ++q) pa[q] = ld8<C>(sP + (q * 64 + lane) * 8);
+#pragma unroll
+                        for (int p = 0; p < 2; ++p)
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) O[i] = mma(pa[i * 2 + p], vo[p], O[i]);
                     }
                 }
             }
 
-            // ---------------- store the tile's outputs
+            // ---------------- store the tile's outputs (rows past the sequence end are dropped)
+            {
+                const uint32_t ob = ((uint32_t)(T0 + 4 * g) * Dv + col) * 4u;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
+                for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int t = T0 + 16 * i + 4 * g + e;
-                    if (t < L) a.out[(bhL + t) * Dv + col] = O[i][e];
-                }
+                    for (int e = 0; e < 4; ++e)
+                        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(O[i][e]), rs.out,
+                                                              (int)(ob + (uint32_t)((16 * i + e) * Dv * 4)), 0, 0);
             }
             if constexpr (!C::CH) Bc += Tt;
             lds_barrier();  // LDS tile arrays are rewritten by the next unit
@@ -859,13 +980,12 @@ template <class C>
 __global__ __launch_bounds__(256, 1) void segment_state_kernel(KArgs a) {
     using OpT = typename C::OpT;
     using Frag = typename C::Frag;
-    using InT = typename C::InT;
+    using Half = typename C::Half;
     extern __shared__ __align__(256) unsigned char smem[];
     const LdsPlan lp = lds_plan(C::OPB, C::DK, C::CH, 1);
     OpT *sKT = reinterpret_cast<OpT *>(smem + lp.kst);
     OpT *sV = reinterpret_cast<OpT *>(smem + lp.vb);
     float *sAb = reinterpret_cast<float *>(smem + lp.ablk);
-    float *sAi = reinterpret_cast<float *>(smem + lp.ainv);
     float *sAt = reinterpret_cast<float *>(smem + lp.atile);
     float *sAs = reinterpret_cast<float *>(smem + lp.aseg);
 
@@ -883,20 +1003,8 @@ __global__ __launch_bounds__(256, 1) void segment_state_kernel(KArgs a) {
     const int col = dv0 + 16 * w + c16;
     const int t_begin = seg * a.seg_len;
     const int t_end = min(L, t_begin + a.seg_len);
-    const size_t bhL = (size_t)bh * L;
-
-    Base<C> b;
-    b.q = nullptr;
-    b.k = reinterpret_cast<const InT *>(a.k) + bhL * C::DK;
-    b.v = reinterpret_cast<const InT *>(a.v) + bhL * Dv;
-    b.la = a.gate == GLA_GATE_CHANNEL ? a.la + bhL * C::DK
-           : a.gate == GLA_GATE_HEAD  ? a.la + bhL
-           : a.gate == GLA_GATE_HEAD_CONST ? a.la + h
-                                           : nullptr;
-    b.li = a.li ? a.li + bhL : nullptr;
-    b.L = L;
-    b.Dv = Dv;
-    b.gate = a.gate;
+    const int chl = C::CPL * lane;
+    const Rs rs = make_rs<C>(a, bh, h);
 
     if constexpr (C::CH) {
         for (int d = tid; d < C::DK; d += kThreads) sAs[d] = 1.f;
@@ -907,21 +1015,24 @@ __global__ __launch_bounds__(256, 1) void segment_state_kernel(KArgs a) {
     for (int n = 0; n < C::NBD; ++n) dS[n] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     Raw<C> raw;
-    load_unit<C, false>(raw, b, t_begin, 0, true, w, lane, tid, dv0);
+    load_unit<C, false>(raw, rs, t_begin, 0, true, w, lane, tid, dv0, Dv);
     for (int T0 = t_begin; T0 < t_end; T0 += kTile) {
         float Tt = 0.f;
+        Frag vfr[2];
 #pragma unroll 1
         for (int sl = 0; sl < C::NSLAB; ++sl) {
             if (sl == 0) v_to_lds<C>(raw, sV, tid);
-            const int chl = C::CPL * lane;
             if constexpr (C::CH) {
                 ChGate<C> G;
-                ch_gate<C>(G, raw, sAb, sAi, w, lane);
+                ch_gate<C>(G, raw, sAb, w, lane);
                 float ig[16];
-                {
+                if (rs.has_li) {
                     const float y = raw.lis * kLog2e;
 #pragma unroll
                     for (int rr = 0; rr < 16; ++rr) ig[rr] = fexp2(__shfl(y, 16 * w + rr));
+                } else {
+#pragma unroll
+                    for (int rr = 0; rr < 16; ++rr) ig[rr] = 1.f;
                 }
 #pragma unroll
                 for (int c = 0; c < C::CPL; ++c) {
@@ -933,17 +1044,17 @@ __global__ __launch_bounds__(256, 1) void segment_state_kernel(KArgs a) {
                 }
 #pragma unroll
                 for (int g4 = 0; g4 < 4; ++g4) {
-                    typename C::Half kt4[C::CPL];
+                    Half kt4[C::CPL];
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int rr = 4 * g4 + e;
 #pragma unroll
                         for (int c = 0; c < C::CPL; ++c)
-                            kt4[c][e] = (OpT)(raw.k[rr].get(c) * G.ek[rr][c] * ig[rr] * G.post[c]);
+                            kt4[c][e] = (OpT)(raw.kf(rr, c) * ig[rr] * G.ek[rr][c] * G.post[c]);
                     }
 #pragma unroll
                     for (int c = 0; c < C::CPL; ++c)
-                        *reinterpret_cast<typename C::Half *>(sKT + (chl + c) * C::KTP + kslot(16 * w + 4 * g4)) = kt4[c];
+                        *reinterpret_cast<Half *>(sKT + (chl + c) * C::KTP + kslot(16 * w + 4 * g4)) = kt4[c];
                 }
             } else {
                 const float x = raw.las * kLog2e;
@@ -952,17 +1063,17 @@ __global__ __launch_bounds__(256, 1) void segment_state_kernel(KArgs a) {
                 Tt = __shfl(bl, 63);
 #pragma unroll
                 for (int g4 = 0; g4 < 4; ++g4) {
-                    typename C::Half kt4[C::CPL];
+                    Half kt4[C::CPL];
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int rr = 4 * g4 + e;
                         const float f = fexp2(Tt - __shfl(bl, 16 * w + rr) + __shfl(y, 16 * w + rr));
 #pragma unroll
-                        for (int c = 0; c < C::CPL; ++c) kt4[c][e] = (OpT)(raw.k[rr].get(c) * f);
+                        for (int c = 0; c < C::CPL; ++c) kt4[c][e] = (OpT)(raw.kf(rr, c) * f);
                     }
 #pragma unroll
                     for (int c = 0; c < C::CPL; ++c)
-                        *reinterpret_cast<typename C::Half *>(sKT + (chl + c) * C::KTP + kslot(16 * w + 4 * g4)) = kt4[c];
+                        *reinterpret_cast<Half *>(sKT + (chl + c) * C::KTP + kslot(16 * w + 4 * g4)) = kt4[c];
                 }
             }
             lds_barrier();
@@ -974,8 +1085,13 @@ __global__ __launch_bounds__(256, 1) void segment_state_kernel(KArgs a) {
                 } else if (T0 + kTile < t_end) {
                     Tn = T0 + kTile;
                 }
-                if (Tn >= 0) load_unit<C, false>(raw, b, Tn, sn, sn == 0, w, lane, tid, dv0);
+                if (Tn >= 0) load_unit<C, false>(raw, rs, Tn, sn, sn == 0, w, lane, tid, dv0, Dv);
             }
+            if (sl == 0) {
+#pragma unroll
+                for (int p = 0; p < 2; ++p) vfr[p] = ld8<C>(sV + ((p * 4 + g) * 64 + 16 * w + c16) * 8);
+            }
+            f32x4 acc[C::NBS];
 #pragma unroll
             for (int n = 0; n < C::NBS; ++n) {
                 const int nn = sl * C::NBS + n;
@@ -986,16 +1102,18 @@ __global__ __launch_bounds__(256, 1) void segment_state_kernel(KArgs a) {
                     const float x = fexp2(Tt);
                     at = f32x4{x, x, x, x};
                 }
-                f32x4 acc = dS[nn] * at;
-                const OpT *kt = sKT + (16 * n + c16) * C::KTP;
-#pragma unroll
-                for (int p = 0; p < 2; ++p) {
-                    const Frag af = ld8<C>(kt + (p * 4 + g) * 8);
-                    const Frag bf = ld8<C>(sV + ((p * 4 + g) * 64 + 16 * w + c16) * 8);
-                    acc = mma(af, bf, acc);
-                }
-                dS[nn] = acc;
+                acc[n] = dS[nn] * at;
             }
+#pragma unroll
+            for (int p = 0; p < 2; ++p) {
+                Frag ka[C::NBS];
+#pragma unroll
+                for (int n = 0; n < C::NBS; ++n) ka[n] = ld8<C>(sKT + (16 * n + c16) * C::KTP + (p * 4 + g) * 8);
+#pragma unroll
+                for (int n = 0; n < C::NBS; ++n) acc[n] = mma(ka[n], vfr[p], acc[n]);
+            }
+#pragma unroll
+            for (int n = 0; n < C::NBS; ++n) dS[sl * C::NBS + n] = acc[n];
             lds_barrier();
         }
         if constexpr (!C::CH) Bs += Tt;

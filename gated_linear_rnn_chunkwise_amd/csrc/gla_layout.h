@@ -28,21 +28,22 @@ GLA_HD inline int chan_per_lane(int opb, int dk) { return (opb == 2 && dk >= 128
 
 // Byte offsets of the workgroup's LDS arrays (dynamic shared memory).
 struct LdsPlan {
-    uint32_t q;       // [nq][64][rp]  QD (per-channel gate) or raw q (scalar gate); nq = slabs if nt > 1
-    uint32_t k;       // [64][rp]      KO (per-channel) or raw k (scalar)
-    uint32_t qi;      // [64][rp]      q scaled to the chunk start
-    uint32_t kst;     // [slab][ktp]   k scaled to the tile end, transposed, in MFMA k-slot order
-    uint32_t pbuf;    // [4][2][64][8] masked score tile, MFMA A-operand order
-    uint32_t vb;      // [2][4][64][8] value tile, MFMA B-operand order
-    uint32_t voff;    // same, value tile of an earlier key tile (nt > 1)
-    uint32_t prevke;  // [nt-1][nslab][64][rp] k scaled to its tile end, earlier tiles (per-channel, nt > 1)
-    uint32_t ablk;    // [4][slab] fp32 decay of each 16-token sub-block (per-channel)
-    uint32_t ainv;    // [4][slab] fp32 reciprocal of ablk
-    uint32_t qtf;     // [4][dk]   fp32 decay from the tile start to each sub-block start (per-channel, nt > 1)
-    uint32_t atile;   // [nt][dk]  fp32 decay across each tile of the chunk (per-channel); [nt] (scalar)
-    uint32_t aseg;    // [dk]      fp32 decay across the segment (segment-state kernel)
-    uint32_t brow;    // [nt*64]   fp32 log2 running decay from the chunk start (scalar gates)
-    uint32_t lrow;    // [nt*64]   fp32 log2 input gate (scalar gates)
+    uint32_t q;      // [nq][64][rp] q scaled to its 16-token block start (per-channel gate) or raw q (scalar);
+                     //              nq = slabs when a chunk has several tiles, else 1
+    uint32_t k;      // [64][rp]     k scaled to its block end (per-channel) or raw k (scalar)
+    uint32_t kd;     // [64][rp]     k scaled to its block start: key operand of diagonal blocks (per-channel)
+    uint32_t x;      // [32][rp]     block-0 keys and block-3 queries referenced to the end of block 1 (per-channel)
+    uint32_t qi;     // [64][rp]     q scaled to the chunk start
+    uint32_t kst;    // [slab][ktp]  k scaled to the tile end, transposed, in MFMA k-slot order
+    uint32_t pbuf;   // [4][2][64][8] masked score tile, MFMA A-operand order
+    uint32_t vb;     // [2][4][64][8] value tile, MFMA B-operand order
+    uint32_t voff;   // same, value tile of an earlier key tile (several tiles per chunk)
+    uint32_t ablk;   // [4][slab] fp32 decay across each 16-token block (per-channel)
+    uint32_t qtf;    // [4][dk]   fp32 decay from the tile start to each block start (per-channel, several tiles)
+    uint32_t atile;  // [nt][dk]  fp32 decay across each tile of the chunk (per-channel)
+    uint32_t aseg;   // [dk]      fp32 decay across the segment (segment-state kernel)
+    uint32_t brow;   // [nt*64]   fp32 log2 running decay from the chunk start (scalar gates)
+    uint32_t lrow;   // [nt*64]   fp32 log2 input gate (scalar gates)
     uint32_t total;
 };
 
@@ -63,15 +64,17 @@ GLA_HD inline LdsPlan lds_plan(int opb, int dk, bool per_channel, int nt) {
     } while (0)
     GLA_TAKE(q, a64 * (uint32_t)(mt ? nslab : 1));
     GLA_TAKE(k, a64);
+    if (per_channel) {
+        GLA_TAKE(kd, a64);
+        GLA_TAKE(x, a64 / 2);
+    }
     GLA_TAKE(qi, a64);
     GLA_TAKE(kst, (uint32_t)slab * (uint32_t)ktp * (uint32_t)opb);
     GLA_TAKE(pbuf, 4096u * (uint32_t)opb);
     GLA_TAKE(vb, 4096u * (uint32_t)opb);
     if (mt) GLA_TAKE(voff, 4096u * (uint32_t)opb);
-    if (mt && per_channel) GLA_TAKE(prevke, a64 * (uint32_t)nslab * (uint32_t)(nt - 1));
     if (per_channel) {
         GLA_TAKE(ablk, 4u * slab * 4u);
-        GLA_TAKE(ainv, 4u * slab * 4u);
         if (mt) GLA_TAKE(qtf, 4u * dk * 4u);
     }
     GLA_TAKE(atile, (uint32_t)nt * (uint32_t)(per_channel ? dk : 1) * 4u);
@@ -83,6 +86,12 @@ GLA_HD inline LdsPlan lds_plan(int opb, int dk, bool per_channel, int nt) {
     return p;
 }
 
+// Global scratch per chunk-output workgroup: keys of the earlier tiles of the current chunk
+// scaled to their tile end (per-channel gate with several tiles per chunk), [nt-1][64][dk].
+GLA_HD inline uint64_t ke_scratch_bytes(int opb, int dk, bool per_channel, int nt) {
+    return (per_channel && nt > 1) ? (uint64_t)(nt - 1) * 64u * (uint64_t)dk * (uint64_t)opb : 0u;
+}
+
 // Arguments of the three kernels.
 struct KArgs {
     const void *q, *k, *v;
@@ -90,6 +99,7 @@ struct KArgs {
     float *out, *fin;
     float *ws_state;  // [BH][nseg-1][Dk][Dv]: local segment states, then (in place) their prefix states
     float *ws_decay;  // [BH][nseg-1][Dk]: decay across each segment
+    void *ws_ke;      // [nwg][nt-1][64][Dk] operand scratch (per-channel gate, several tiles per chunk)
     int B, H, L, Dv;
     int chunk, nt;    // chunk size and 64-token tiles per chunk
     int gate;         // enum gla_gate

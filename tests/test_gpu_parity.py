@@ -184,7 +184,8 @@ def test_caller_workspace(gpu_lib):
     w = gin.custom(1, 2, 1500, 128, 128, 64, gate="channel")
     d = gin.make_inputs(w, seed=6)
     q, k, v, la = (d[x].cuda() for x in ("q", "k", "v", "log_alpha"))
-    desc = gpu_lib.make_desc(q, k, v, la, chunk=64, seg_chunks=4)
+    out = torch.empty(1, 2, 1500, 128, device="cuda")
+    desc = gpu_lib.make_desc(q, k, v, la, out=out, chunk=64, seg_chunks=4)
     nbytes = gpu_lib.workspace_size(desc)
     assert nbytes > 0
     ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
