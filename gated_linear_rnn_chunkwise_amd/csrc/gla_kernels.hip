@@ -420,7 +420,7 @@ __device__ __forceinline__ void ch_gate(ChGate<C> &G, const Raw<C> &r, float *sA
 // decay span is too large for scaled matrix-core operands: every pair s <= t gets
 // sum_d q_td k_sd 2^(u_td - u_sd) i_s with u the log2 running decay.
 template <class C>
-__device__ __forceinline__ void ch_diag_exact(f32x4 &acc, const Raw<C> &r, const float *ig, int lane) {
+__device__ __attribute__((noinline)) f32x4 ch_diag_exact(f32x4 acc, Raw<C> r, int lane, bool has_li) {
     float u[16][C::CPL];
 #pragma unroll
     for (int c = 0; c < C::CPL; ++c) {
@@ -432,17 +432,28 @@ __device__ __forceinline__ void ch_diag_exact(f32x4 &acc, const Raw<C> &r, const
         }
     }
     const int c16 = lane & 15, g = lane >> 4;
+    const int w = lane;  // unused
+    (void)w;
+    const float y = r.lis * kLog2e;
+    const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    float ig[16];
 #pragma unroll
+    for (int rr = 0; rr < 16; ++rr) ig[rr] = has_li ? fexp2(__shfl(y, 16 * wv + rr)) : 1.f;
     for (int s = 0; s < 16; ++s) {
-#pragma unroll
         for (int t = s; t < 16; ++t) {
             float part = 0.f;
 #pragma unroll
             for (int c = 0; c < C::CPL; ++c) part += r.qf(t, c) * r.kf(s, c) * fexp2(u[t][c] - u[s][c]);
             const float tot = wave_sum(part * ig[s]);
-            if (c16 == t && g == (s >> 2)) acc[s & 3] += tot;
+            if (c16 == t && g == (s >> 2)) {
+                if ((s & 3) == 0) acc[0] += tot;
+                else if ((s & 3) == 1) acc[1] += tot;
+                else if ((s & 3) == 2) acc[2] += tot;
+                else acc[3] += tot;
+            }
         }
     }
+    return acc;
 }
 
 // ------------------------------------------------------------------------------------
@@ -594,11 +605,7 @@ __global__ __launch_bounds__(256, 1) void chunk_output_kernel(KArgs a) {
 #pragma unroll
                         for (int rr = 0; rr < 16; ++rr) ig[rr] = 1.f;
                     }
-                    if (harsh) {
-                        f32x4 t = Pd[0];
-                        ch_diag_exact<C>(t, raw, ig, lane);
-                        Pd[0] = t;
-                    }
+                    if (harsh) Pd[0] = ch_diag_exact<C>(Pd[0], raw, lane, rs.has_li);
                     float fqi[C::CPL], ainv[C::CPL], xs[C::CPL];
 #pragma unroll
                     for (int c = 0; c < C::CPL; ++c) {
@@ -973,6 +980,547 @@ __global__ __launch_bounds__(256, 1) void chunk_output_kernel(KArgs a) {
 }
 
 // ------------------------------------------------------------------------------------
+// Warp-specialised chunk output for 64-token chunks whose key channels fit one slab.
+// grid = BH * nseg * ndv workgroups of 512 threads.  Waves 4..7 (producers) load chunk k+1
+// and prepare its gate-scaled operands while waves 0..3 (consumers) run the matrix
+// products of chunk k; every SIMD holds one producer and one consumer wave, so the
+// vector-ALU gate work and the matrix-core work of neighbouring chunks overlap.  Two
+// barriers per chunk:
+//   phase A  consumers: score blocks of chunk k (q, k single buffers), inter-chunk term (qi)
+//            producers: gates of chunk k+1; key^T, values and decays into buffer (k+1)&1
+//   B1
+//   phase B  consumers: scores x values, state update (buffer k&1), output store
+//            producers: q, k, qi of chunk k+1 into the single buffers
+//   B2
+// Producer lane mapping: lane = (row block g = lane>>4, channel group c16 = lane&15); wave pw
+// covers channels CPL*(16*pw + c16) .. +CPL-1 for all 64 rows, so the four block decays of a
+// channel meet inside one wave (no barrier for the exchange).
+
+template <class C>
+__device__ __forceinline__ void load_unit_p(Raw<C> &r, const Rs &rs, int T0, int pw, int lane, int dv0, int Dv) {
+    const int g = lane >> 4, c16 = lane & 15;
+    const int ch0 = C::CPL * (16 * pw + c16);
+    const uint32_t row0 = (uint32_t)(T0 + 16 * g);
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) {
+        const uint32_t off = ((row0 + rr) * C::DK + ch0) * C::IB;
+        if constexpr (C::CPL == 2 || C::F32) {
+            r.q[rr] = bld32(rs.q, off);
+            r.k[rr] = bld32(rs.k, off);
+        } else {
+            r.q[rr] = __builtin_amdgcn_raw_buffer_load_b16(rs.q, (int)off, 0, 0);
+            r.k[rr] = __builtin_amdgcn_raw_buffer_load_b16(rs.k, (int)off, 0, 0);
+        }
+        if constexpr (C::CH) {
+            const uint32_t goff = ((row0 + rr) * C::DK + ch0) * 4u;
+            if constexpr (C::CPL == 2) {
+                const u32x2 g2 = bld64(rs.la, goff);
+                r.la[rr][0] = __uint_as_float(g2[0]);
+                r.la[rr][1] = __uint_as_float(g2[1]);
+            } else {
+                r.la[rr][0] = __uint_as_float(bld32(rs.la, goff));
+            }
+        }
+    }
+    const uint32_t t = (uint32_t)(T0 + lane);
+    if constexpr (!C::CH) {
+        if (rs.gate == GLA_GATE_HEAD)
+            r.las = __uint_as_float(bld32(rs.la, t * 4u));
+        else if (rs.gate == GLA_GATE_HEAD_CONST)
+            r.las = (int)t < rs.L ? __uint_as_float(bld32(rs.la, 0)) : 0.f;
+        else
+            r.las = 0.f;
+    }
+    r.lis = __uint_as_float(bld32(rs.li, t * 4u));
+    const int tp = 64 * pw + lane;
+    const uint32_t c0 = dv0 + 4 * (tp & 15);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const uint32_t off = ((uint32_t)(T0 + 4 * (tp >> 4) + e) * Dv + c0) * C::IB;
+        if constexpr (C::F32) {
+            const u32x4 x = bld128(rs.v, off);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) r.v[e][j] = x[j];
+        } else {
+            const u32x2 x = bld64(rs.v, off);
+            r.v[e][0] = x[0];
+            r.v[e][1] = x[1];
+        }
+    }
+}
+
+// CPL operands of one row packed into 32 bits (fp16 pair / one fp16 / one fp32).
+template <class C>
+__device__ __forceinline__ uint32_t pack_ops(const float *x) {
+    if constexpr (C::F32) {
+        return __float_as_uint(x[0]);
+    } else if constexpr (C::CPL == 2) {
+        return __builtin_bit_cast(uint32_t, f16x2{(f16)x[0], (f16)x[1]});
+    } else {
+        return (uint32_t)__builtin_bit_cast(uint16_t, (f16)x[0]);
+    }
+}
+template <class C>
+__device__ __forceinline__ void st_packed(typename C::OpT *row, uint32_t v) {
+    if constexpr (C::F32 || C::CPL == 2)
+        *reinterpret_cast<uint32_t *>(row) = v;
+    else
+        *reinterpret_cast<uint16_t *>(row) = (uint16_t)v;
+}
+
+template <class C>
+struct ProdVals {
+    uint32_t qd[16], ko[16], qi[16];  // packed operands of rows 16g+rr for phase B
+};
+
+// Exact diagonal-block partial scores of the producer wave's channels in 16-token blocks
+// whose decay is too strong for scaled fp16 operands (rare; kept out of line so the common
+// path keeps its registers).  For every pair s <= t of block gg: the sum over this wave's
+// strongly decayed channels of q_td k_sd 2^(u_td - u_sd) i_s, u the log2 running decay.
+template <class C>
+__device__ __attribute__((noinline)) void ws_exact_blocks(Raw<C> raw, float *sXa, uint64_t hb, int pw, int lane,
+                                                          bool has_li) {
+    const int g = lane >> 4, c16 = lane & 15;
+    if (((hb >> (16 * g)) & 0xffffull) == 0ull) return;
+    float u[16][C::CPL], hcm[C::CPL];
+#pragma unroll
+    for (int c = 0; c < C::CPL; ++c) {
+        float run = 0.f, prod = 1.f;
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+            run += raw.la[rr][c] * kLog2e;
+            u[rr][c] = run;
+            prod *= fexp2(raw.la[rr][c] * kLog2e);
+        }
+        hcm[c] = !(prod >= C::kMinDiagDecay) ? 1.f : 0.f;
+    }
+    const float y = raw.lis * kLog2e;
+    float ig[16];
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) ig[rr] = has_li ? fexp2(__shfl(y, 16 * g + rr)) : 1.f;
+    float *dst = sXa + (pw * 4 + g) * 136;
+    for (int t = 0; t < 16; ++t) {
+        for (int s2 = 0; s2 <= t; ++s2) {
+            float part = 0.f;
+#pragma unroll
+            for (int c = 0; c < C::CPL; ++c)
+                part += hcm[c] * raw.qf(t, c) * raw.kf(s2, c) * fexp2(u[t][c] - u[s2][c]);
+            part *= ig[s2];
+#pragma unroll
+            for (int m = 1; m < 16; m <<= 1) part += __shfl_xor(part, m);
+            const int idx = t * (t + 1) / 2 + s2;
+            if (c16 == (idx & 15)) dst[idx] = part;
+        }
+    }
+}
+
+// Producer phase A: gates of one chunk, key^T and values into buffer nb, q/k/qi values kept
+// for phase B.  Returns nothing; writes LDS only.
+template <class C>
+__device__ __forceinline__ void ws_produce_a(ProdVals<C> &pv, const Raw<C> &raw, const LdsPlanWs &lp,
+                                             unsigned char *smem, int nb, int pw, int lane, bool has_li) {
+    using OpT = typename C::OpT;
+    using Half = typename C::Half;
+    const int g = lane >> 4, c16 = lane & 15;
+    const int ch0 = C::CPL * (16 * pw + c16);
+    OpT *sKT = reinterpret_cast<OpT *>(smem + (lp.dbl + (nb) * lp.dstride + lp.kst));
+    float *sAb = reinterpret_cast<float *>(smem + (lp.dbl + (nb) * lp.dstride + lp.ab));
+    float *sAi = reinterpret_cast<float *>(smem + (lp.dbl + (nb) * lp.dstride + lp.ainv));
+    float *sAt = reinterpret_cast<float *>(smem + (lp.dbl + (nb) * lp.dstride + lp.at));
+    v_to_lds<C>(raw, reinterpret_cast<OpT *>(smem + (lp.dbl + (nb) * lp.dstride + lp.vb)), 64 * pw + lane);
+
+    float ig[16];
+    {
+        const float y = raw.lis * kLog2e;
+        if constexpr (C::CH) {
+            if (has_li) {
+#pragma unroll
+                for (int rr = 0; rr < 16; ++rr) ig[rr] = fexp2(__shfl(y, 16 * g + rr));
+            } else {
+#pragma unroll
+                for (int rr = 0; rr < 16; ++rr) ig[rr] = 1.f;
+            }
+        }
+    }
+
+    if constexpr (C::CH) {
+        float eq[16][C::CPL], ek[16][C::CPL];
+#pragma unroll
+        for (int c = 0; c < C::CPL; ++c) {
+            float run = 1.f;
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr) {
+                const float al = fexp2(raw.la[rr][c] * kLog2e);
+                ek[rr][c] = al;
+                run *= al;
+                eq[rr][c] = run;
+            }
+            run = 1.f;
+#pragma unroll
+            for (int rr = 15; rr >= 0; --rr) {
+                const float al = ek[rr][c];
+                ek[rr][c] = run;
+                run *= al;
+            }
+        }
+        float pre[C::CPL], post[C::CPL];
+        bool hc[C::CPL];
+        bool any_h = false;
+#pragma unroll
+        for (int c = 0; c < C::CPL; ++c) {
+            const float ag = eq[15][c];
+            float p0 = 1.f, p1 = 1.f, all = 1.f;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const float au = __shfl(ag, 16 * u + c16);
+                all *= au;
+                if (u < g) p0 *= au;
+                if (u > g) p1 *= au;
+            }
+            pre[c] = p0;
+            post[c] = p1;
+            hc[c] = !(ag >= C::kMinDiagDecay);
+            any_h |= hc[c];
+            sAb[g * C::SLAB + ch0 + c] = ag;
+            sAi[g * C::SLAB + ch0 + c] = hc[c] ? 0.f : frcp(ag);
+            if (g == 0) sAt[ch0 + c] = all;
+        }
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+            Half kt4[C::CPL];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int rr = 4 * g4 + e;
+                float qd[C::CPL], ko[C::CPL], qi[C::CPL];
+#pragma unroll
+                for (int c = 0; c < C::CPL; ++c) {
+                    qd[c] = raw.qf(rr, c) * eq[rr][c];
+                    ko[c] = raw.kf(rr, c) * ig[rr] * ek[rr][c];
+                    qi[c] = qd[c] * pre[c];
+                    kt4[c][e] = (OpT)(ko[c] * post[c]);
+                }
+                pv.qd[rr] = pack_ops<C>(qd);
+                pv.ko[rr] = pack_ops<C>(ko);
+                pv.qi[rr] = pack_ops<C>(qi);
+            }
+#pragma unroll
+            for (int c = 0; c < C::CPL; ++c)
+                *reinterpret_cast<Half *>(sKT + (ch0 + c) * C::KTP + kslot(16 * g + 4 * g4)) = kt4[c];
+        }
+        // exact diagonal-block partial scores over this wave's channels that are too strongly decayed
+        const uint64_t hb = __ballot(any_h);
+        int *sXf = reinterpret_cast<int *>(smem + (lp.dbl + (nb) * lp.dstride + lp.xflag));
+        if (hb != 0ull) ws_exact_blocks<C>(raw, reinterpret_cast<float *>(smem + (lp.dbl + (nb) * lp.dstride + lp.xact)), hb, pw, lane, has_li);
+        if (lane < 4) sXf[pw * 4 + lane] = ((hb >> (16 * lane)) & 0xffffull) != 0ull ? 1 : 0;
+    } else {
+        // scalar gates: running log2 decay over the tile's rows (lane = row)
+        float *sBr = sAb;  // [64] log2 running decay, row 63 = decay across the tile
+        float *sLr = sAi;  // [64] log2 input gate
+        const float x = raw.las * kLog2e;
+        const float y = raw.lis * kLog2e;
+        const float bl = scan_incl(x, lane);
+        const float Tt = __shfl(bl, 63);
+        if (pw == 0) {
+            sBr[lane] = bl;
+            sLr[lane] = y;
+        }
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+            Half kt4[C::CPL];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int rr = 4 * g4 + e;
+                const float blr = __shfl(bl, 16 * g + rr);
+                const float eb = fexp2(blr);
+                const float ekr = fexp2(Tt - blr + __shfl(y, 16 * g + rr));
+                float qv[C::CPL], kv[C::CPL], qi[C::CPL];
+#pragma unroll
+                for (int c = 0; c < C::CPL; ++c) {
+                    qv[c] = raw.qf(rr, c);
+                    kv[c] = raw.kf(rr, c);
+                    qi[c] = qv[c] * eb;
+                    kt4[c][e] = (OpT)(kv[c] * ekr);
+                }
+                pv.qd[rr] = pack_ops<C>(qv);
+                pv.ko[rr] = pack_ops<C>(kv);
+                pv.qi[rr] = pack_ops<C>(qi);
+            }
+#pragma unroll
+            for (int c = 0; c < C::CPL; ++c)
+                *reinterpret_cast<Half *>(sKT + (ch0 + c) * C::KTP + kslot(16 * g + 4 * g4)) = kt4[c];
+        }
+    }
+}
+
+// Producer phase B: q, k, qi of the prepared chunk into the single buffers.
+template <class C>
+__device__ __forceinline__ void ws_produce_b(const ProdVals<C> &pv, const LdsPlanWs &lp, unsigned char *smem,
+                                             int pw, int lane) {
+    using OpT = typename C::OpT;
+    const int g = lane >> 4, c16 = lane & 15;
+    const int ch0 = C::CPL * (16 * pw + c16);
+    OpT *sQ = reinterpret_cast<OpT *>(smem + lp.q);
+    OpT *sK = reinterpret_cast<OpT *>(smem + lp.k);
+    OpT *sQI = reinterpret_cast<OpT *>(smem + lp.qi);
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) {
+        const int row = 16 * g + rr;
+        st_packed<C>(sQ + row * C::RP + ch0, pv.qd[rr]);
+        st_packed<C>(sK + row * C::RP + ch0, pv.ko[rr]);
+        st_packed<C>(sQI + row * C::RP + ch0, pv.qi[rr]);
+    }
+}
+
+template <class C>
+__global__ __launch_bounds__(512, 1) void chunk_output_ws_kernel(KArgs a) {
+    static_assert(!C::MT && C::NSLAB == 1, "single-tile, single-slab configuration");
+    using OpT = typename C::OpT;
+    using Frag = typename C::Frag;
+    using Half = typename C::Half;
+    extern __shared__ __align__(256) unsigned char smem[];
+    const LdsPlanWs lp = lds_plan_ws(C::OPB, C::DK);
+
+    int id = xcd_remap((int)blockIdx.x, a.nwg);
+    const int dvt = id % a.ndv;
+    id /= a.ndv;
+    const int seg = id % a.nseg;
+    const int bh = id / a.nseg;
+    const int h = bh % a.H;
+    const int tid = (int)threadIdx.x, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int L = a.L, Dv = a.Dv;
+    const int dv0 = dvt * kDvTile;
+    const int t_begin = seg * a.seg_len;
+    const int t_end = min(L, t_begin + a.seg_len);
+    const int nch = (t_end - t_begin + kTile - 1) / kTile;
+    const Rs rs = make_rs<C>(a, bh, h);
+
+    if (w >= 4) {
+        // ============================ producers
+        const int pw = w - 4;
+        Raw<C> raw;
+        ProdVals<C> pv;
+        load_unit_p<C>(raw, rs, t_begin, pw, lane, dv0, Dv);
+        ws_produce_a<C>(pv, raw, lp, smem, 0, pw, lane, rs.has_li);
+        if (nch > 1) load_unit_p<C>(raw, rs, t_begin + kTile, pw, lane, dv0, Dv);
+        ws_produce_b<C>(pv, lp, smem, pw, lane);
+        lds_barrier();
+        for (int kc = 0; kc < nch; ++kc) {
+            const bool has_next = kc + 1 < nch;
+            if (has_next) {
+                ws_produce_a<C>(pv, raw, lp, smem, (kc + 1) & 1, pw, lane, rs.has_li);
+                if (kc + 2 < nch) load_unit_p<C>(raw, rs, t_begin + kTile * (kc + 2), pw, lane, dv0, Dv);
+            }
+            lds_barrier();  // B1
+            if (has_next) ws_produce_b<C>(pv, lp, smem, pw, lane);
+            lds_barrier();  // B2
+        }
+        return;
+    }
+
+    // ================================ consumers
+    const int cw = w;
+    const int col = dv0 + 16 * cw + c16;
+    const OpT *sQ = reinterpret_cast<const OpT *>(smem + lp.q);
+    const OpT *sK = reinterpret_cast<const OpT *>(smem + lp.k);
+    const OpT *sQI = reinterpret_cast<const OpT *>(smem + lp.qi);
+    OpT *sP = reinterpret_cast<OpT *>(smem + lp.pbuf);
+
+    f32x4 S[C::NBD];
+#pragma unroll
+    for (int n = 0; n < C::NBD; ++n) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int d = 16 * n + 4 * g + e;
+            float x = 0.f;
+            if (seg > 0)
+                x = a.ws_state[(((size_t)bh * (a.nseg - 1) + (seg - 1)) * C::DK + d) * Dv + col];
+            else if (a.s0)
+                x = a.s0[((size_t)bh * C::DK + d) * Dv + col];
+            S[n][e] = x;
+        }
+    }
+    lds_barrier();  // chunk 0 prepared
+
+    // this wave's score blocks: (query block i, key block j); pair 0 is the diagonal (cw, cw)
+    int pi[3], pj[3];
+    pi[0] = cw;
+    pj[0] = cw;
+    switch (cw) {
+        case 0: pi[1] = 1; pj[1] = 0; pi[2] = 3; pj[2] = 2; break;
+        case 1: pi[1] = 2; pj[1] = 0; pi[2] = 3; pj[2] = 1; break;
+        case 2: pi[1] = 2; pj[1] = 1; pi[2] = 2; pj[2] = 1; break;
+        default: pi[1] = 3; pj[1] = 0; pi[2] = 3; pj[2] = 0; break;
+    }
+
+    for (int kc = 0; kc < nch; ++kc) {
+        const int b = kc & 1;
+        const int T0 = t_begin + kTile * kc;
+        const OpT *sKT = reinterpret_cast<const OpT *>(smem + (lp.dbl + (b) * lp.dstride + lp.kst));
+        const OpT *sV = reinterpret_cast<const OpT *>(smem + (lp.dbl + (b) * lp.dstride + lp.vb));
+        const float *sAb = reinterpret_cast<const float *>(smem + (lp.dbl + (b) * lp.dstride + lp.ab));
+        const float *sAi = reinterpret_cast<const float *>(smem + (lp.dbl + (b) * lp.dstride + lp.ainv));
+        const float *sAt = reinterpret_cast<const float *>(smem + (lp.dbl + (b) * lp.dstride + lp.at));
+
+        // ---------------- phase A: score blocks P^T(j, i) over the key channels
+        f32x4 Pd[3];
+#pragma unroll
+        for (int kp = 0; kp < 3; ++kp) Pd[kp] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int m = 0; m < C::KSTEP; ++m) {
+            const int ch = 32 * m + 8 * g;
+            Frag af[3], bf[3];
+#pragma unroll
+            for (int kp = 0; kp < 3; ++kp) {
+                af[kp] = ld8<C>(sK + (16 * pj[kp] + c16) * C::RP + ch);
+                bf[kp] = ld8<C>(sQ + (16 * pi[kp] + c16) * C::RP + ch);
+            }
+            if constexpr (C::CH) {
+                af[0] = scale8<C>(af[0], lds_ld<f32x4>(sAi + cw * C::SLAB + ch), lds_ld<f32x4>(sAi + cw * C::SLAB + ch + 4));
+#pragma unroll
+                for (int kp = 1; kp < 3; ++kp) {
+                    if (pj[kp] + 1 < pi[kp]) {
+                        f32x4 r0 = lds_ld<f32x4>(sAb + (pj[kp] + 1) * C::SLAB + ch);
+                        f32x4 r1 = lds_ld<f32x4>(sAb + (pj[kp] + 1) * C::SLAB + ch + 4);
+                        if (pj[kp] + 2 < pi[kp]) {
+                            r0 *= lds_ld<f32x4>(sAb + (pj[kp] + 2) * C::SLAB + ch);
+                            r1 *= lds_ld<f32x4>(sAb + (pj[kp] + 2) * C::SLAB + ch + 4);
+                        }
+                        bf[kp] = scale8<C>(bf[kp], r0, r1);
+                    }
+                }
+            }
+#pragma unroll
+            for (int kp = 0; kp < 3; ++kp) Pd[kp] = mma(af[kp], bf[kp], Pd[kp]);
+        }
+        if constexpr (C::CH) {
+            // channels of strongly decayed blocks: exact partial scores from the producers
+            const float *sXa = reinterpret_cast<const float *>(smem + (lp.dbl + (b) * lp.dstride + lp.xact));
+            const int *sXf = reinterpret_cast<const int *>(smem + (lp.dbl + (b) * lp.dstride + lp.xflag));
+#pragma unroll 1
+            for (int pw = 0; pw < 4; ++pw) {
+                if (sXf[pw * 4 + cw]) {
+                    const float *src = sXa + (pw * 4 + cw) * 136;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int s2 = 4 * g + e;
+                        if (s2 <= c16) Pd[0][e] += src[c16 * (c16 + 1) / 2 + s2];
+                    }
+                }
+            }
+        }
+        // mask, decay (scalar gates), store scores in MFMA A-operand order
+#pragma unroll
+        for (int kp = 0; kp < 3; ++kp) {
+            if (kp == 2 && cw >= 2) continue;  // repeated pair
+            const int i = pi[kp], j = pj[kp];
+            Half pvv;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int s2 = 4 * g + e;
+                const bool masked = i == j && s2 > c16;
+                float x = masked ? 0.f : Pd[kp][e];
+                if constexpr (!C::CH) {
+                    if (!masked) x *= fexp2(sAb[16 * i + c16] - sAb[16 * j + s2] + sAi[16 * j + s2]);
+                }
+                pvv[e] = (OpT)x;
+            }
+            *reinterpret_cast<Half *>(sP + ((i * 2 + (j >> 1)) * 64 + lane) * 8 + 4 * (j & 1)) = pvv;
+        }
+        if (cw == 0 || cw == 2) {
+            const Half z{(OpT)0.f, (OpT)0.f, (OpT)0.f, (OpT)0.f};
+            *reinterpret_cast<Half *>(sP + ((cw * 2 + (cw >> 1)) * 64 + lane) * 8 + 4) = z;
+        }
+        // inter-chunk term: O = QI . S
+        f32x4 O[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) O[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        {
+            Frag sb[C::KSTEP];
+#pragma unroll
+            for (int m = 0; m < C::KSTEP; ++m) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    sb[m][e] = (OpT)S[2 * m][e];
+                    sb[m][e + 4] = (OpT)S[2 * m + 1][e];
+                }
+            }
+#pragma unroll
+            for (int m = 0; m < C::KSTEP; ++m) {
+                Frag qa[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const OpT *row = sQI + (16 * i + c16) * C::RP + 32 * m + 4 * g;
+                    qa[i] = ld4x2<C>(row, row + 16);
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) O[i] = mma(qa[i], sb[m], O[i]);
+            }
+        }
+        lds_barrier();  // B1: scores stored; producers may rewrite q, k, qi
+
+        // ---------------- phase B: scores x values, state update, output
+        Frag vfr[2];
+#pragma unroll
+        for (int p = 0; p < 2; ++p) vfr[p] = ld8<C>(sV + ((p * 4 + g) * 64 + 16 * cw + c16) * 8);
+        {
+            Frag pa[6];
+            pa[0] = ld8<C>(sP + ((0 * 2 + 0) * 64 + lane) * 8);
+            pa[1] = ld8<C>(sP + ((1 * 2 + 0) * 64 + lane) * 8);
+            pa[2] = ld8<C>(sP + ((2 * 2 + 0) * 64 + lane) * 8);
+            pa[3] = ld8<C>(sP + ((3 * 2 + 0) * 64 + lane) * 8);
+            pa[4] = ld8<C>(sP + ((2 * 2 + 1) * 64 + lane) * 8);
+            pa[5] = ld8<C>(sP + ((3 * 2 + 1) * 64 + lane) * 8);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) O[i] = mma(pa[i], vfr[0], O[i]);
+            O[2] = mma(pa[4], vfr[1], O[2]);
+            O[3] = mma(pa[5], vfr[1], O[3]);
+        }
+        {
+            f32x4 acc[C::NBD];
+#pragma unroll
+            for (int n = 0; n < C::NBD; ++n) {
+                f32x4 at;
+                if constexpr (C::CH) {
+                    at = lds_ld<f32x4>(sAt + 16 * n + 4 * g);
+                } else {
+                    const float x = fexp2(sAb[63]);
+                    at = f32x4{x, x, x, x};
+                }
+                acc[n] = S[n] * at;
+            }
+#pragma unroll
+            for (int p = 0; p < 2; ++p) {
+                Frag ka[C::NBD];
+#pragma unroll
+                for (int n = 0; n < C::NBD; ++n) ka[n] = ld8<C>(sKT + (16 * n + c16) * C::KTP + (p * 4 + g) * 8);
+#pragma unroll
+                for (int n = 0; n < C::NBD; ++n) acc[n] = mma(ka[n], vfr[p], acc[n]);
+            }
+#pragma unroll
+            for (int n = 0; n < C::NBD; ++n) S[n] = acc[n];
+        }
+        {
+            const uint32_t ob = ((uint32_t)(T0 + 4 * g) * Dv + col) * 4u;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(O[i][e]), rs.out,
+                                                          (int)(ob + (uint32_t)((16 * i + e) * Dv * 4)), 0, 0);
+        }
+        lds_barrier();  // B2
+    }
+
+    if (seg == a.nseg - 1 && a.fin) {
+#pragma unroll
+        for (int n = 0; n < C::NBD; ++n)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) a.fin[((size_t)bh * C::DK + 16 * n + 4 * g + e) * Dv + col] = S[n][e];
+    }
+}
+
+// ------------------------------------------------------------------------------------
 // segment_state_kernel: grid = BH * (nseg - 1) * ndv.  The state segment `seg` produces
 // from zero, sum_s diag(decay from s to the segment end) i_s k_s^T v_s, accumulated tile by
 // tile (dS <- diag(tile decay) dS + K~^T V), and the decay across the segment.
@@ -1172,14 +1720,23 @@ static hipError_t launch_cfg(const KArgs &a, hipStream_t st) {
         hipLaunchKernelGGL(segment_scan_kernel, dim3(nx, a.B * a.H), dim3(kThreads), 0, st, a, C::DK);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
-    const LdsPlan l3 = lds_plan(C::OPB, C::DK, C::CH, a.nt);
-    err = hipFuncSetAttribute(reinterpret_cast<const void *>(&chunk_output_kernel<C>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)l3.total);
-    if (err != hipSuccess) return err;
     KArgs a3 = a;
     a3.nwg = (a.B * a.H) * a.nseg * a.ndv;
-    hipLaunchKernelGGL(chunk_output_kernel<C>, dim3(a3.nwg), dim3(kThreads), l3.total, st, a3);
-    return hipGetLastError();
+    if constexpr (!C::MT && C::NSLAB == 1) {
+        const LdsPlanWs lw = lds_plan_ws(C::OPB, C::DK);
+        err = hipFuncSetAttribute(reinterpret_cast<const void *>(&chunk_output_ws_kernel<C>),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)lw.total);
+        if (err != hipSuccess) return err;
+        hipLaunchKernelGGL(chunk_output_ws_kernel<C>, dim3(a3.nwg), dim3(2 * kThreads), lw.total, st, a3);
+        return hipGetLastError();
+    } else {
+        const LdsPlan l3 = lds_plan(C::OPB, C::DK, C::CH, a.nt);
+        err = hipFuncSetAttribute(reinterpret_cast<const void *>(&chunk_output_kernel<C>),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)l3.total);
+        if (err != hipSuccess) return err;
+        hipLaunchKernelGGL(chunk_output_kernel<C>, dim3(a3.nwg), dim3(kThreads), l3.total, st, a3);
+        return hipGetLastError();
+    }
 }
 
 template <bool F32, int DK>

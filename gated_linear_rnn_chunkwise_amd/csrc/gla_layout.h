@@ -86,6 +86,71 @@ GLA_HD inline LdsPlan lds_plan(int opb, int dk, bool per_channel, int nt) {
     return p;
 }
 
+// LDS of the warp-specialised chunk-output kernel (64-token chunks, one slab): four
+// producer waves prepare chunk k+1 while four consumer waves run the matrix products of
+// chunk k.  Arrays read by the consumers only before the mid-iteration barrier are single
+// (q, k, qi); arrays read after it are double-buffered by chunk parity.
+struct LdsPlanWs {
+    uint32_t q, k, qi;  // [64][rp] single buffers
+    // double-buffered block: buffer b starts at dbl + b * dstride; offsets inside a buffer:
+    uint32_t dbl, dstride;
+    uint32_t kst;   // [slab][ktp]
+    uint32_t vb;    // [4096] value tile
+    uint32_t ab;    // [4][slab] fp32 decay across each 16-token block (per-channel); [64] log2 running
+                    //           decay of each row (scalar gates)
+    uint32_t ainv;  // [4][slab] fp32 1/decay of each block, 0 for channels handled exactly (per-channel);
+                    //           [64] log2 input gate of each row (scalar gates)
+    uint32_t at;    // [slab] fp32 decay across the tile (per-channel)
+    uint32_t xact;  // [4 producer waves][4 blocks][136] fp32 exact diagonal-block partial scores
+    uint32_t xflag; // [4][4] int32: partial present
+    uint32_t pbuf;  // [4096] masked score tile
+    uint32_t total;
+};
+
+GLA_HD inline LdsPlanWs lds_plan_ws(int opb, int dk) {
+    const int cpl = chan_per_lane(opb, dk);
+    const int slab = 64 * cpl;
+    const int rp = slab + 16 / opb;
+    const int ktp = 64 + 16 / opb;
+    const uint32_t a64 = 64u * (uint32_t)rp * (uint32_t)opb;
+    auto al = [](uint32_t x) { return (x + 255u) & ~255u; };
+    LdsPlanWs p{};
+    uint32_t off = 0;
+    p.q = off;
+    off += al(a64);
+    p.k = off;
+    off += al(a64);
+    p.qi = off;
+    off += al(a64);
+    uint32_t in = 0;
+    p.kst = in;
+    in += al((uint32_t)slab * (uint32_t)ktp * (uint32_t)opb);
+    p.vb = in;
+    in += al(4096u * (uint32_t)opb);
+    p.ab = in;
+    in += al(4u * (uint32_t)slab * 4u);
+    p.ainv = in;
+    in += al(4u * (uint32_t)slab * 4u);
+    p.at = in;
+    in += al((uint32_t)slab * 4u);
+    p.xact = in;
+    in += al(4u * 4u * 136u * 4u);
+    p.xflag = in;
+    in += al(16u * 4u);
+    p.dbl = off;
+    p.dstride = in;
+    off += 2u * in;
+    p.pbuf = off;
+    off += al(4096u * (uint32_t)opb);
+    p.total = off;
+    return p;
+}
+
+// The warp-specialised kernel handles 64-token chunks whose key channels fit one slab.
+GLA_HD inline bool use_ws_kernel(int opb, int dk, int nt) {
+    return nt == 1 && dk / (64 * chan_per_lane(opb, dk)) == 1;
+}
+
 // Global scratch per chunk-output workgroup: keys of the earlier tiles of the current chunk
 // scaled to their tile end (per-channel gate with several tiles per chunk), [nt-1][64][dk].
 GLA_HD inline uint64_t ke_scratch_bytes(int opb, int dk, bool per_channel, int nt) {
