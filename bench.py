@@ -96,28 +96,34 @@ def cpu_baseline(w, d, budget_s: float = 20.0) -> dict:
         li = oracle.oracle._f64(sel(d["log_ig"]))
         return q, k, v, la64, li
 
-    def run(nheads):
+    def run(nheads, min_time=0.0):
         q, k, v, la64, li = prep(nheads)
-        t0 = time.perf_counter()
-        oracle.recurrent(q, k, v, "channel", la64, li)
-        return time.perf_counter() - t0
+        reps, t = 0, 0.0
+        while True:
+            t0 = time.perf_counter()
+            oracle.recurrent(q, k, v, "channel", la64, li)
+            t += time.perf_counter() - t0
+            reps += 1
+            if t >= min_time or reps >= 200:
+                return t, reps
 
     threads = oracle.threads()
     probe_heads = min(BH, threads)
-    t_probe = run(probe_heads)
-    per_round = t_probe  # one head per thread
-    rounds = max(1, min(int(budget_s / max(per_round, 1e-6)), math.ceil(BH / threads)))
+    t_probe, _ = run(probe_heads)  # one head per thread
+    rounds = max(1, min(int(budget_s / max(t_probe, 1e-6)), math.ceil(BH / threads)))
     nheads = min(BH, rounds * threads)
-    t = run(nheads) if nheads != probe_heads else t_probe
-    head_tokens_per_s = nheads * w.L / t
+    # the whole sample is repeated until about half the budget has run, so a workload the
+    # host finishes quickly is still timed over seconds
+    t, reps = run(nheads, min_time=0.5 * budget_s)
+    head_tokens_per_s = reps * nheads * w.L / t
     tokens_per_s = head_tokens_per_s / w.H  # tokens = batch x sequence positions
     return {
         "value": tokens_per_s,
         "unit": "tokens/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": "%d of %d (batch, head) pairs, full length %d, fp64 token recurrence, %.2f s"
-                  % (nheads, BH, w.L, t),
+        "sample": "%d of %d (batch, head) pairs at full length %d, %d repetition(s), fp64 token recurrence, "
+                  "%.2f s" % (nheads, BH, w.L, reps, t),
     }
 
 
@@ -125,6 +131,23 @@ def torch_stack_heads(la, H, nheads):
     import torch
 
     return torch.stack([la[i % H] for i in range(nheads)])
+
+
+COPY_PROBE_BYTES = 256 << 20
+
+
+def copy_probe(torch, steps):
+    """A plain device-to-device copy of COPY_PROBE_BYTES per launch: reads and writes that
+    many bytes of HBM.  Its FETCH_SIZE / WRITE_SIZE counter readings convert the counters'
+    units into bytes for the kernels measured the same way."""
+    dev = torch.device("cuda:0")
+    n = COPY_PROBE_BYTES // 4
+    src = [torch.rand(n, device=dev) for _ in range(2)]
+    dst = torch.empty(n, device=dev)
+    for i in range(max(steps, 1)):
+        dst.copy_(src[i & 1])
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_per_launch": COPY_PROBE_BYTES, "launches": max(steps, 1)}), flush=True)
 
 
 def main():
@@ -136,6 +159,8 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seg-chunks", type=int, default=0)
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a plain device copy of known size (HBM counter calibration)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -144,6 +169,10 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.copy_probe:
+        copy_probe(torch, args.steps)
+        return
 
     import gated_linear_rnn_chunkwise_amd as gla
     from gated_linear_rnn_chunkwise_amd import inputs as gin
@@ -208,7 +237,7 @@ def main():
     # a step, so the events around the call time exactly that kernel.
     if plan.n_seg == 1:
         kbytes = io
-        scope = "chunk_output_kernel"
+        scope = "chunk-output kernel (the only launch of a step)"
     else:
         kbytes = io + w.B * w.H * (plan.n_seg - 1) * w.Dk * w.Dv * 4.0 * 3 \
             + 2.0 * w.B * w.H * (plan.n_seg - 1) * w.L / plan.n_seg * (w.Dk * 2 + w.Dv) * (4 if w.dtype == "f32" else 2)
