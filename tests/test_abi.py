@@ -156,6 +156,12 @@ def test_automatic_segmentation(lib, B, H, L, Dv, chunk, expect_seg):
 
 
 def test_lds_limit_reported_as_unsupported(lib):
-    # per-channel gate with large chunks keeps earlier tiles' keys in LDS: too big for Dk=256, C=512
-    assert status(lib, desc(Dk=256, chunk=512))[0] == gla.GLA_ERR_UNSUPPORTED
-    assert status(lib, desc(Dk=128, chunk=256))[0] == gla.GLA_OK
+    # fp32 operands with a per-channel gate and several tiles per chunk need more than the
+    # 160 KB of LDS of a compute unit; the bf16 cases of the same shapes fit
+    assert status(lib, desc(Dk=128, chunk=128, in_dtype=gla.DTYPE_F32))[0] == gla.GLA_ERR_UNSUPPORTED
+    assert status(lib, desc(Dk=256, chunk=128, in_dtype=gla.DTYPE_F32, gate_kind=gla.GATE_HEAD))[0] == \
+        gla.GLA_ERR_UNSUPPORTED
+    assert status(lib, desc(Dk=128, chunk=64, in_dtype=gla.DTYPE_F32))[0] == gla.GLA_OK
+    assert status(lib, desc(Dk=256, chunk=64, in_dtype=gla.DTYPE_F32))[0] == gla.GLA_OK
+    assert status(lib, desc(Dk=128, chunk=512))[0] == gla.GLA_OK
+    assert status(lib, desc(Dk=256, chunk=512))[0] == gla.GLA_OK

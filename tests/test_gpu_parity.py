@@ -67,20 +67,32 @@ SMALL = []
 for dtype in ("bf16", "f32"):
     for gate, ig in (("channel", False), ("none", False), ("head", True), ("head_const", False), ("channel", True)):
         for Dk, Dv in ((64, 64), (128, 128), (256, 64)):
-            for chunk in (64, 128, 256):
-                if dtype == "f32" and (Dk == 256 or chunk > 128):
-                    continue
-                if dtype == "f32" and gate == "channel" and Dk >= 128 and chunk > 64:
-                    continue  # LDS budget: unsupported
-                if gate == "channel" and Dk == 256 and chunk > 128:
-                    continue
+            for chunk in (64, 128, 256, 512):
                 SMALL.append((dtype, gate, ig, Dk, Dv, chunk))
+
+
+def supported(gla, w):
+    """Status of the library's own support check for a workload (no GPU work)."""
+    d = gin.make_inputs(w.with_(L=1), seed=0)
+    t = {k: v for k, v in d.items()}
+    out = torch.empty(w.B, w.H, 1, w.Dv)
+    desc = gla.make_desc(t["q"], t["k"], t["v"], t["log_alpha"], t["log_ig"], None, out, None, w.chunk)
+    try:
+        gla.workspace_size(desc)
+        return True
+    except gla.GlaError as e:
+        assert e.status == gla.GLA_ERR_UNSUPPORTED
+        return False
 
 
 @pytest.mark.parametrize("dtype,gate,ig,Dk,Dv,chunk", SMALL)
 @pytest.mark.parametrize("L", [1, 100, 333])
 def test_small_shapes(gpu_lib, dtype, gate, ig, Dk, Dv, chunk, L):
     w = gin.custom(2, 2, L, Dk, Dv, chunk, dtype=dtype, gate=gate, input_gate=ig)
+    if not supported(gpu_lib, w):
+        # fp32 operands with several tiles per chunk: more LDS than a compute unit has
+        assert dtype == "f32" and chunk > 64
+        pytest.skip("configuration reported unsupported (LDS budget)")
     d = gin.make_inputs(w, seed=L)
     out, fin = run_gpu(gpu_lib, d, w)
     ref, rfin = run_oracle(d, w)
