@@ -146,10 +146,9 @@ GLA_HD inline LdsPlanWs lds_plan_ws(int opb, int dk) {
     return p;
 }
 
-// The warp-specialised kernel handles 64-token chunks whose key channels fit one slab.
-GLA_HD inline bool use_ws_kernel(int opb, int dk, int nt) {
-    return nt == 1 && dk / (64 * chan_per_lane(opb, dk)) == 1;
-}
+// The warp-specialised kernel runs every 64-token-chunk case whose key channels fit one
+// slab (bf16 with Dk <= 128, fp32 with Dk = 64); the launcher makes the same choice.
+GLA_HD inline bool use_ws_kernel(int opb, int dk, int nt) { return nt == 1 && dk == 64 * chan_per_lane(opb, dk); }
 
 // Global scratch per chunk-output workgroup: keys of the earlier tiles of the current chunk
 // scaled to their tile end (per-channel gate with several tiles per chunk), [nt-1][64][dk].

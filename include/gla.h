@@ -30,17 +30,20 @@
  * with the shapes given below, and 16-byte aligned.  The caller owns all memory; the
  * library never frees or keeps a pointer it is given.  Inputs are not modified.
  *
- * Gate values.  log_alpha and log_ig must be finite or -infinity is NOT accepted: use a
- * large negative finite value (for example -1e4) for a gate of zero.  Gates are expected
- * to be <= 0 (alpha, i in (0, 1]); positive log gates are computed as given but may
- * overflow.  NaN inputs propagate to the outputs.  Values are not checked on the host.
+ * Gate values.  log_alpha and log_ig must be finite; -infinity is not accepted (the
+ * kernels form differences of running sums of log gates, and -inf - -inf is NaN).  For a
+ * gate of zero pass a large negative finite value such as -1e4, whose exponential is an
+ * exact zero in fp32.  Gates are expected to be <= 0 (alpha, i in (0, 1]); positive log
+ * gates are computed as given but may overflow.  NaN inputs propagate to the outputs.
+ * Values are not checked on the host.
  *
  * Asynchrony and errors.  Every call validates its arguments on the host before any HIP
  * call; on a validation error it returns a negative status, launches nothing and writes
  * nothing.  Otherwise it enqueues its kernels on `stream` (a hipStream_t; NULL is the
  * default stream) and returns without synchronising; outputs are valid once the stream
  * has completed the work.  GLA_ERR_HIP reports launch-time errors only.  The library has
- * no mutable global state besides a per-device property cache; calls are re-entrant.
+ * no mutable global state; calls are re-entrant.  Two calls that share an output, a final
+ * state or a caller workspace must not run concurrently.
  */
 #ifndef GLA_H
 #define GLA_H
@@ -122,9 +125,12 @@ int gla_fwd(const void *q, const void *k, const void *v, const float *log_alpha,
  * length and caller workspace.  When d->workspace is NULL and scratch is needed it is
  * allocated and freed stream-ordered on `stream`; otherwise d->workspace_bytes must be at
  * least what gla_workspace_size reports, else GLA_ERR_WORKSPACE.
- * Support matrix (else GLA_ERR_UNSUPPORTED): chunk a multiple of 64 in [64, 1024];
- * Dk in {64, 128, 256}; Dv a multiple of 64 up to 4096; any L >= 1; a per-channel gate
- * with chunk > 64 needs Dk <= 128.  Returns a gla_status. */
+ * Support matrix (else GLA_ERR_UNSUPPORTED): chunk a multiple of 64 in [64, 512];
+ * Dk in {64, 128, 256}; Dv a multiple of 64 up to 4096; any L >= 1; and the operand tiles
+ * of one workgroup must fit the 160 KB of LDS of a compute unit, which excludes fp32
+ * inputs with chunk > 64 when Dk >= 128 under a per-channel gate, and fp32 inputs with
+ * chunk > 64 when Dk = 256 under any gate (bf16 inputs fit at every listed shape).
+ * Returns a gla_status. */
 int gla_fwd_ex(const gla_desc *d, void *stream);
 
 /* Scratch bytes gla_fwd_ex needs for `d` (no HIP call).  Returns a gla_status. */
