@@ -1300,19 +1300,21 @@ __global__ __launch_bounds__(512, 1) void chunk_output_ws_kernel(KArgs a) {
         const int pw = w - 4;
         Raw<C> raw;
         ProdVals<C> pv;
+        // The loop body is unconditional: in the last iteration the producers prepare a chunk
+        // past the segment end into buffers no consumer reads again, and the prefetch two
+        // chunks ahead reads rows past the (batch, head) extent as zero through the buffer
+        // range check.  Conditional loads would make the compiler merge register copies
+        // that wait for the whole prefetch as soon as it is issued.
         load_unit_p<C>(raw, rs, t_begin, pw, lane, dv0, Dv);
         ws_produce_a<C>(pv, raw, lp, smem, 0, pw, lane, rs.has_li);
-        if (nch > 1) load_unit_p<C>(raw, rs, t_begin + kTile, pw, lane, dv0, Dv);
+        load_unit_p<C>(raw, rs, t_begin + kTile, pw, lane, dv0, Dv);
         ws_produce_b<C>(pv, lp, smem, pw, lane);
         lds_barrier();
         for (int kc = 0; kc < nch; ++kc) {
-            const bool has_next = kc + 1 < nch;
-            if (has_next) {
-                ws_produce_a<C>(pv, raw, lp, smem, (kc + 1) & 1, pw, lane, rs.has_li);
-                if (kc + 2 < nch) load_unit_p<C>(raw, rs, t_begin + kTile * (kc + 2), pw, lane, dv0, Dv);
-            }
+            ws_produce_a<C>(pv, raw, lp, smem, (kc + 1) & 1, pw, lane, rs.has_li);
+            load_unit_p<C>(raw, rs, t_begin + kTile * (kc + 2), pw, lane, dv0, Dv);
             lds_barrier();  // B1
-            if (has_next) ws_produce_b<C>(pv, lp, smem, pw, lane);
+            ws_produce_b<C>(pv, lp, smem, pw, lane);
             lds_barrier();  // B2
         }
         return;
