@@ -64,6 +64,10 @@ int make_plan(const gla_desc *d, Plan *p) {
     if (d->Dk != 64 && d->Dk != 128 && d->Dk != 256) return GLA_ERR_UNSUPPORTED;
     if (d->Dv % gla::kDvTile != 0 || d->Dv > 4096) return GLA_ERR_UNSUPPORTED;
     if (d->chunk % gla::kTile != 0 || d->chunk > gla::kMaxChunk) return GLA_ERR_UNSUPPORTED;
+    // Kernels address one (batch, head) slice through a buffer resource with 32-bit byte
+    // offsets, and prefetch up to two chunks past the segment end.
+    if ((int64_t(d->L) + 2 * gla::kMaxChunk) * std::max(d->Dk, d->Dv) * 4 >= (int64_t(1) << 32))
+        return GLA_ERR_UNSUPPORTED;
     const bool f32 = d->in_dtype == GLA_DTYPE_F32;
     const bool ch = d->gate_kind == GLA_GATE_CHANNEL;
     p->nt = d->chunk / gla::kTile;

@@ -262,8 +262,8 @@ __device__ __forceinline__ Rs make_rs(const KArgs &a, int bh, int h) {
 }
 
 template <class C, bool WQ>
-__device__ __forceinline__ void load_unit(Raw<C> &r, const Rs &rs, int T0, int sl, bool with_v, int w, int lane,
-                                          int tid, int dv0, int Dv) {
+__device__ __forceinline__ void load_unit(Raw<C> &r, const Rs &rs, int T0, int sl, int w, int lane, int tid, int dv0,
+                                          int Dv) {
     const int ch0 = sl * C::SLAB + C::CPL * lane;
     const uint32_t row0 = (uint32_t)(T0 + 16 * w);
     const uint32_t qoff = (row0 * C::DK + ch0) * C::IB;
@@ -299,7 +299,7 @@ __device__ __forceinline__ void load_unit(Raw<C> &r, const Rs &rs, int T0, int s
             r.las = 0.f;
     }
     r.lis = __uint_as_float(bld32(rs.li, t * 4u));
-    if (with_v) {
+    {
         const uint32_t c0 = dv0 + 4 * (tid & 15);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -560,7 +560,7 @@ __global__ __launch_bounds__(256, 1) void chunk_output_kernel(KArgs a) {
     f32x4 dS[C::MT ? C::NBD : 1];
 
     Raw<C> raw;
-    if (t_begin < t_end) load_unit<C, true>(raw, rs, t_begin, 0, true, w, lane, tid, dv0, Dv);
+    load_unit<C, true>(raw, rs, t_begin, 0, w, lane, tid, dv0, Dv);
 
     for (int c0 = t_begin; c0 < t_end; c0 += a.chunk) {
         float Wc[C::NSLAB][C::CPL];  // per-channel decay from the chunk start to the tile start
@@ -706,18 +706,19 @@ __global__ __launch_bounds__(256, 1) void chunk_output_kernel(KArgs a) {
                 else
                     lds_barrier();
 
-                // ---------------- prefetch the next unit while this one computes
+                // ---------------- prefetch the next unit while this one computes.  Issued
+                // unconditionally (after the last unit it reads rows past the segment, which
+                // are never used; past the (batch, head) extent the range check returns zero),
+                // so the compiler does not merge register copies that wait for the loads.
                 {
-                    int Tn = -1, sn = 0;
+                    int Tn = c0 + a.chunk, sn = 0;
                     if (sl + 1 < C::NSLAB) {
                         Tn = T0;
                         sn = sl + 1;
                     } else if (tau + 1 < ntile) {
                         Tn = T0 + kTile;
-                    } else if (c0 + a.chunk < t_end) {
-                        Tn = c0 + a.chunk;
                     }
-                    if (Tn >= 0) load_unit<C, true>(raw, rs, Tn, sn, sn == 0, w, lane, tid, dv0, Dv);
+                    load_unit<C, true>(raw, rs, Tn, sn, w, lane, tid, dv0, Dv);
                 }
 
                 if (sl == 0) {
@@ -1565,7 +1566,7 @@ __global__ __launch_bounds__(256, 1) void segment_state_kernel(KArgs a) {
     for (int n = 0; n < C::NBD; ++n) dS[n] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     Raw<C> raw;
-    load_unit<C, false>(raw, rs, t_begin, 0, true, w, lane, tid, dv0, Dv);
+    load_unit<C, false>(raw, rs, t_begin, 0, w, lane, tid, dv0, Dv);
     for (int T0 = t_begin; T0 < t_end; T0 += kTile) {
         float Tt = 0.f;
         Frag vfr[2];
@@ -1628,14 +1629,13 @@ __global__ __launch_bounds__(256, 1) void segment_state_kernel(KArgs a) {
             }
             lds_barrier();
             {
-                int Tn = -1, sn = 0;
+                // unconditional prefetch, as in the chunk-output kernel
+                int Tn = T0 + kTile, sn = 0;
                 if (sl + 1 < C::NSLAB) {
                     Tn = T0;
                     sn = sl + 1;
-                } else if (T0 + kTile < t_end) {
-                    Tn = T0 + kTile;
                 }
-                if (Tn >= 0) load_unit<C, false>(raw, rs, Tn, sn, sn == 0, w, lane, tid, dv0, Dv);
+                load_unit<C, false>(raw, rs, Tn, sn, w, lane, tid, dv0, Dv);
             }
             if (sl == 0) {
 #pragma unroll

@@ -126,7 +126,9 @@ int gla_fwd(const void *q, const void *k, const void *v, const float *log_alpha,
  * allocated and freed stream-ordered on `stream`; otherwise d->workspace_bytes must be at
  * least what gla_workspace_size reports, else GLA_ERR_WORKSPACE.
  * Support matrix (else GLA_ERR_UNSUPPORTED): chunk a multiple of 64 in [64, 512];
- * Dk in {64, 128, 256}; Dv a multiple of 64 up to 4096; any L >= 1; and the operand tiles
+ * Dk in {64, 128, 256}; Dv a multiple of 64 up to 4096; L >= 1 with
+ * (L + 1024) * max(Dk, Dv) * 4 < 2^32 (one (batch, head) slice is addressed with 32-bit
+ * byte offsets, which allows L up to about 1M for Dv = 1024); and the operand tiles
  * of one workgroup must fit the 160 KB of LDS of a compute unit, which excludes fp32
  * inputs with chunk > 64 when Dk >= 128 under a per-channel gate, and fp32 inputs with
  * chunk > 64 when Dk = 256 under any gate (bf16 inputs fit at every listed shape).

@@ -114,11 +114,19 @@ def test_headline_entry_point_validates(lib):
 
 
 @pytest.mark.parametrize("kw", [dict(Dk=96), dict(Dk=32), dict(Dv=96), dict(Dv=32), dict(chunk=32), dict(chunk=96),
-                                dict(chunk=1024), dict(Dv=4160)])
+                                dict(chunk=1024), dict(Dv=4160), dict(B=1, H=1, L=(1 << 23) - 1024)])
 def test_unsupported_shapes(lib, kw):
     d = desc(**kw)
     assert status(lib, d)[0] == gla.GLA_ERR_UNSUPPORTED
     assert fwd_status(lib, d) == gla.GLA_ERR_UNSUPPORTED
+
+
+def test_longest_sequence_of_a_slice(lib):
+    # one (batch, head) slice is addressed with 32-bit byte offsets: (L + 1024) * max(Dk, Dv) * 4 < 2^32
+    assert status(lib, desc(B=1, H=1, L=(1 << 23) - 1025))[0] == gla.GLA_OK
+    assert status(lib, desc(B=1, H=1, L=(1 << 23) - 1024))[0] == gla.GLA_ERR_UNSUPPORTED
+    assert status(lib, desc(B=1, H=1, L=(1 << 20) - 1025, Dv=1024))[0] == gla.GLA_OK
+    assert status(lib, desc(B=1, H=1, L=(1 << 20) - 1024, Dv=1024))[0] == gla.GLA_ERR_UNSUPPORTED
 
 
 def test_caller_workspace_too_small(lib):
