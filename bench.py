@@ -159,6 +159,8 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seg-chunks", type=int, default=0)
+    ap.add_argument("--tile-pairs", action="store_true",
+                    help="chunks > 64 tokens in the tile-pair (tiled large-chunk) form")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain device copy of known size (HBM counter calibration)")
     args = ap.parse_args()
@@ -193,7 +195,7 @@ def main():
     descs = []
     for s in sets:
         descs.append(gla.make_desc(s["q"], s["k"], s["v"], s.get("log_alpha"), s.get("log_ig"), None, out, fin,
-                                   w.chunk, args.seg_chunks))
+                                   w.chunk, args.seg_chunks, tile_pairs=args.tile_pairs))
     plan = gla.plan(descs[0])
     ws = None
     if plan.workspace_bytes:
@@ -270,6 +272,7 @@ def main():
                    "gate": w.gate, "input_gate": w.input_gate, "in_dtype": w.dtype,
                    "matrix_operands": "fp16 from bf16" if w.dtype == "bf16" else "fp32",
                    "accumulate": "fp32", "out_dtype": "fp32", "n_seg": plan.n_seg,
+                   "tile_pairs": bool(plan.tile_pairs),
                    "workgroups": plan.grid_out},
         "head_tokens_per_s": value * w.H,
         "tflops": round(tflops, 2),

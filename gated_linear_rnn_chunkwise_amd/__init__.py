@@ -25,6 +25,7 @@ LIB_PATH = os.path.join(_HERE, "libgla.so")
 GLA_OK, GLA_ERR_INVALID_ARG, GLA_ERR_UNSUPPORTED, GLA_ERR_WORKSPACE, GLA_ERR_HIP = 0, -1, -2, -3, -4
 DTYPE_BF16, DTYPE_F32 = 0, 1
 GATE_NONE, GATE_CHANNEL, GATE_HEAD, GATE_HEAD_CONST = 0, 1, 2, 3
+FLAG_TILE_PAIRS = 1
 GATE_NAMES = {"none": GATE_NONE, "channel": GATE_CHANNEL, "head": GATE_HEAD, "head_const": GATE_HEAD_CONST}
 
 # Entry points declared in include/gla.h.
@@ -39,7 +40,7 @@ class GlaDesc(ctypes.Structure):
         ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
         ("log_alpha", ctypes.c_void_p), ("log_ig", ctypes.c_void_p), ("initial_state", ctypes.c_void_p),
         ("out", ctypes.c_void_p), ("final_state", ctypes.c_void_p),
-        ("seg_chunks", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("seg_chunks", ctypes.c_int32), ("flags", ctypes.c_int32),
         ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
     ]
 
@@ -48,7 +49,7 @@ class GlaPlan(ctypes.Structure):
     _fields_ = [
         ("seg_chunks", ctypes.c_int32), ("n_seg", ctypes.c_int32), ("dv_tiles", ctypes.c_int32),
         ("tiles_per_chunk", ctypes.c_int32), ("grid_state", ctypes.c_int32), ("grid_scan", ctypes.c_int32),
-        ("grid_out", ctypes.c_int32), ("reserved", ctypes.c_int32), ("workspace_bytes", ctypes.c_size_t),
+        ("grid_out", ctypes.c_int32), ("tile_pairs", ctypes.c_int32), ("workspace_bytes", ctypes.c_size_t),
     ]
 
 
@@ -119,7 +120,7 @@ def gate_kind_of(log_alpha, B: int, H: int, L: int, Dk: int) -> int:
 
 
 def make_desc(q, k, v, log_alpha=None, log_ig=None, initial_state=None, out=None, final_state=None, chunk=64,
-              seg_chunks=0, workspace=None, workspace_bytes=0, gate_kind=None) -> GlaDesc:
+              seg_chunks=0, workspace=None, workspace_bytes=0, gate_kind=None, tile_pairs=False) -> GlaDesc:
     """Fill a :class:`GlaDesc` from tensors (shapes read from q and v)."""
     import torch
 
@@ -138,7 +139,7 @@ def make_desc(q, k, v, log_alpha=None, log_ig=None, initial_state=None, out=None
     d.log_alpha, d.log_ig, d.initial_state = _ptr(log_alpha), _ptr(log_ig), _ptr(initial_state)
     d.out, d.final_state = _ptr(out), _ptr(final_state)
     d.seg_chunks = int(seg_chunks)
-    d.reserved = 0
+    d.flags = FLAG_TILE_PAIRS if tile_pairs else 0
     d.workspace = _ptr(workspace)
     d.workspace_bytes = int(workspace_bytes)
     return d
@@ -160,10 +161,11 @@ def _check_tensors(q, k, v, *others):
 
 
 def fwd(q, k, v, log_alpha=None, *, log_ig=None, initial_state=None, chunk: int = 64, final_state: bool = True,
-        seg_chunks: int = 0, out=None, workspace=None, stream=None):
+        seg_chunks: int = 0, out=None, workspace=None, stream=None, tile_pairs: bool = False):
     """Gated linear attention forward on the current HIP stream.
 
-    Returns ``(out [B,H,L,Dv] fp32, final_state [B,H,Dk,Dv] fp32 or None)``."""
+    ``tile_pairs`` selects the tiled large-chunk form for chunks of more than 64 tokens
+    (``GLA_FLAG_TILE_PAIRS``).  Returns ``(out [B,H,L,Dv] fp32, final_state [B,H,Dk,Dv] fp32 or None)``."""
     import torch
 
     lib = load()
@@ -174,7 +176,8 @@ def fwd(q, k, v, log_alpha=None, *, log_ig=None, initial_state=None, chunk: int 
     fin = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=q.device) if final_state else None
     _check_tensors(q, k, v, log_alpha, log_ig, initial_state, out, fin)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    d = make_desc(q, k, v, log_alpha, log_ig, initial_state, out, fin, chunk, seg_chunks, workspace, ws_bytes)
+    d = make_desc(q, k, v, log_alpha, log_ig, initial_state, out, fin, chunk, seg_chunks, workspace, ws_bytes,
+                  tile_pairs=tile_pairs)
     s = stream if stream is not None else torch.cuda.current_stream(q.device)
     st = lib.gla_fwd_ex(ctypes.byref(d), ctypes.c_void_p(s.cuda_stream))
     if st != GLA_OK:

@@ -28,6 +28,7 @@ constexpr int64_t kSmallProblem = 65536;   // head-tokens below which segmenting
 
 struct Plan {
     int nt, nc, ndv, seg_chunks, nseg, seg_len;
+    int knt;  // 64-token tiles per chunk as the kernels run it: nt with tile pairs, else 1
     int grid_state, grid_scan, grid_out;
     size_t ws_state_bytes, ws_decay_bytes, ws_ke_bytes, ws_bytes;
     uint32_t lds_out, lds_state;
@@ -41,7 +42,7 @@ int validate(const gla_desc *d) {
     if (!d) return GLA_ERR_INVALID_ARG;
     if (!d->q || !d->k || !d->v || !d->out) return GLA_ERR_INVALID_ARG;
     if (d->B <= 0 || d->H <= 0 || d->L <= 0 || d->Dk <= 0 || d->Dv <= 0 || d->chunk <= 0) return GLA_ERR_INVALID_ARG;
-    if (d->seg_chunks < 0 || d->reserved != 0) return GLA_ERR_INVALID_ARG;
+    if (d->seg_chunks < 0 || (d->flags & ~int32_t(GLA_FLAG_TILE_PAIRS)) != 0) return GLA_ERR_INVALID_ARG;
     if (d->in_dtype != GLA_DTYPE_BF16 && d->in_dtype != GLA_DTYPE_F32) return GLA_ERR_INVALID_ARG;
     if (d->gate_kind < GLA_GATE_NONE || d->gate_kind > GLA_GATE_HEAD_CONST) return GLA_ERR_INVALID_ARG;
     if ((d->gate_kind == GLA_GATE_NONE) != (d->log_alpha == nullptr)) return GLA_ERR_INVALID_ARG;
@@ -71,6 +72,8 @@ int make_plan(const gla_desc *d, Plan *p) {
     const bool f32 = d->in_dtype == GLA_DTYPE_F32;
     const bool ch = d->gate_kind == GLA_GATE_CHANNEL;
     p->nt = d->chunk / gla::kTile;
+    // Without tile pairs the state is advanced tile by tile: the kernels walk 64-token chunks.
+    p->knt = (d->flags & GLA_FLAG_TILE_PAIRS) ? p->nt : 1;
     p->nc = (d->L + d->chunk - 1) / d->chunk;
     p->ndv = d->Dv / gla::kDvTile;
     const int64_t bh = int64_t(d->B) * d->H;
@@ -95,15 +98,15 @@ int make_plan(const gla_desc *d, Plan *p) {
     p->grid_state = (int)g1;
     p->grid_scan = p->nseg > 1 ? (int)(bh * ((int64_t(d->Dk) * d->Dv + 1023) / 1024)) : 0;
     const int opb = f32 ? 4 : 2;
-    p->lds_out = gla::use_ws_kernel(opb, d->Dk, p->nt) ? gla::lds_plan_ws(opb, d->Dk).total
-                                                      : gla::lds_plan(opb, d->Dk, ch, p->nt).total;
+    p->lds_out = gla::use_ws_kernel(opb, d->Dk, p->knt) ? gla::lds_plan_ws(opb, d->Dk).total
+                                                       : gla::lds_plan(opb, d->Dk, ch, p->knt).total;
     p->lds_state = gla::lds_plan(opb, d->Dk, ch, 1).total;
     if (p->lds_out > gla::kMaxLds || p->lds_state > gla::kMaxLds) return GLA_ERR_UNSUPPORTED;
     const size_t nsm = (size_t)(p->nseg - 1);
     p->ws_state_bytes = align256(size_t(bh) * nsm * size_t(d->Dk) * size_t(d->Dv) * 4u);
     p->ws_decay_bytes = align256(size_t(bh) * nsm * size_t(d->Dk) * 4u);
     if (p->nseg <= 1) p->ws_state_bytes = p->ws_decay_bytes = 0;
-    p->ws_ke_bytes = align256(size_t(g3) * (size_t)gla::ke_scratch_bytes(opb, d->Dk, ch, p->nt));
+    p->ws_ke_bytes = align256(size_t(g3) * (size_t)gla::ke_scratch_bytes(opb, d->Dk, ch, p->knt));
     p->ws_bytes = p->ws_state_bytes + p->ws_decay_bytes + p->ws_ke_bytes;
     return GLA_OK;
 }
@@ -152,7 +155,7 @@ int gla_query_plan(const gla_desc *d, gla_plan *out) {
     out->grid_state = p.grid_state;
     out->grid_scan = p.grid_scan;
     out->grid_out = p.grid_out;
-    out->reserved = 0;
+    out->tile_pairs = p.knt > 1 ? 1 : 0;
     out->workspace_bytes = p.ws_bytes;
     return GLA_OK;
 }
@@ -194,8 +197,8 @@ int gla_fwd_ex(const gla_desc *d, void *stream) {
     a.H = d->H;
     a.L = d->L;
     a.Dv = d->Dv;
-    a.chunk = d->chunk;
-    a.nt = p.nt;
+    a.chunk = gla::kTile * p.knt;
+    a.nt = p.knt;
     a.gate = d->gate_kind;
     a.seg_len = p.seg_len;
     a.nseg = p.nseg;

@@ -165,7 +165,7 @@ struct KArgs {
     float *ws_decay;  // [BH][nseg-1][Dk]: decay across each segment
     void *ws_ke;      // [nwg][nt-1][64][Dk] operand scratch (per-channel gate, several tiles per chunk)
     int B, H, L, Dv;
-    int chunk, nt;    // chunk size and 64-token tiles per chunk
+    int chunk, nt;    // chunk size as the kernels run it and its 64-token tiles
     int gate;         // enum gla_gate
     int seg_len;      // tokens per segment (a multiple of the chunk size)
     int nseg, ndv;    // segments; 64-column value tiles

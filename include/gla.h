@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define GLA_VERSION 10000 /* major * 10000 + minor * 100 + patch */
+#define GLA_VERSION 10100 /* major * 10000 + minor * 100 + patch */
 
 /* Status codes.  0 is success; errors are negative. */
 enum gla_status {
@@ -78,6 +78,17 @@ enum gla_gate {
     GLA_GATE_HEAD_CONST = 3  /* [H]: one fixed decay per head (RetNet-style) */
 };
 
+/* Bits of gla_desc.flags. */
+enum gla_flag {
+    /* Chunks of more than 64 tokens compute the terms between the 64-token tiles of a chunk
+     * as tile pairs against the state at the chunk start (the tiled large-chunk form of
+     * Tiled Flash Linear Attention).  Without the flag the state is advanced after every
+     * 64-token tile and those terms come through it; both forms give the same result up to
+     * rounding, and without the flag fewer operations are needed because the state never
+     * leaves the registers. */
+    GLA_FLAG_TILE_PAIRS = 1
+};
+
 /* Full description of one forward call. */
 typedef struct gla_desc {
     int32_t B, H, L, Dk, Dv; /* batch, heads, sequence length, key and value head dims */
@@ -95,7 +106,7 @@ typedef struct gla_desc {
     int32_t seg_chunks;      /* chunks per sequence segment; 0 = chosen by the library.
                                 Segments are processed in parallel and joined by a scan of
                                 their boundary states (see gla_fwd_ex). */
-    int32_t reserved;        /* must be 0 */
+    int32_t flags;           /* gla_flag bits; other bits set -> GLA_ERR_INVALID_ARG */
     void *workspace;         /* device scratch or NULL (the library allocates it on the stream) */
     size_t workspace_bytes;  /* size of `workspace` */
 } gla_desc;
@@ -105,11 +116,11 @@ typedef struct gla_plan {
     int32_t seg_chunks;      /* chunks per segment actually used */
     int32_t n_seg;           /* number of sequence segments */
     int32_t dv_tiles;        /* value-dimension tiles of 64 columns */
-    int32_t tiles_per_chunk; /* 64-token tiles per chunk */
+    int32_t tiles_per_chunk; /* 64-token tiles per chunk (chunk / 64) */
     int32_t grid_state;      /* workgroups of the segment-state kernel (0 if not launched) */
     int32_t grid_scan;       /* workgroups of the segment-scan kernel (0 if not launched) */
     int32_t grid_out;        /* workgroups of the chunk-output kernel */
-    int32_t reserved;
+    int32_t tile_pairs;      /* 1 if the tile-pair form runs (GLA_FLAG_TILE_PAIRS and chunk > 64) */
     size_t workspace_bytes;  /* device scratch the call needs (0 = none) */
 } gla_plan;
 
@@ -128,11 +139,10 @@ int gla_fwd(const void *q, const void *k, const void *v, const float *log_alpha,
  * Support matrix (else GLA_ERR_UNSUPPORTED): chunk a multiple of 64 in [64, 512];
  * Dk in {64, 128, 256}; Dv a multiple of 64 up to 4096; L >= 1 with
  * (L + 1024) * max(Dk, Dv) * 4 < 2^32 (one (batch, head) slice is addressed with 32-bit
- * byte offsets, which allows L up to about 1M for Dv = 1024); and the operand tiles
- * of one workgroup must fit the 160 KB of LDS of a compute unit, which excludes fp32
- * inputs with chunk > 64 when Dk >= 128 under a per-channel gate, and fp32 inputs with
- * chunk > 64 when Dk = 256 under any gate (bf16 inputs fit at every listed shape).
- * Returns a gla_status. */
+ * byte offsets, which allows L up to about 1M for Dv = 1024); and the operand tiles of
+ * one workgroup must fit the 160 KB of LDS of a compute unit.  That last rule only bites
+ * with GLA_FLAG_TILE_PAIRS and fp32 inputs: chunk > 64 is then unsupported for Dk = 256,
+ * and for Dk = 128 under a per-channel gate.  Returns a gla_status. */
 int gla_fwd_ex(const gla_desc *d, void *stream);
 
 /* Scratch bytes gla_fwd_ex needs for `d` (no HIP call).  Returns a gla_status. */

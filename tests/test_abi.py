@@ -40,7 +40,10 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert gla.version() == 10000
+    # the version the header declares
+    hdr = open(os.path.join(ROOT, "include", "gla.h")).read()
+    declared = int(re.search(r"#define GLA_VERSION (\d+)", hdr).group(1))
+    assert gla.version() == declared
     for st, txt in [(0, "ok"), (-1, "invalid argument"), (-2, "unsupported configuration"),
                     (-3, "workspace too small or allocation failed"), (-4, "HIP runtime error")]:
         assert gla.status_string(st) == txt
@@ -51,7 +54,7 @@ def desc(**kw):
     d = gla.GlaDesc()
     base = dict(B=2, H=3, L=100, Dk=128, Dv=128, chunk=64, in_dtype=gla.DTYPE_BF16, gate_kind=gla.GATE_CHANNEL,
                 q=A, k=A, v=A, log_alpha=A, log_ig=None, initial_state=None, out=A, final_state=None,
-                seg_chunks=0, reserved=0, workspace=None, workspace_bytes=0)
+                seg_chunks=0, flags=0, workspace=None, workspace_bytes=0)
     base.update(kw)
     for key, val in base.items():
         setattr(d, key, val)
@@ -78,7 +81,7 @@ def test_valid_descriptor_plans(lib):
 
 @pytest.mark.parametrize("field,value", [
     ("q", None), ("k", None), ("v", None), ("out", None),
-    ("B", 0), ("H", -1), ("L", 0), ("Dk", 0), ("Dv", 0), ("chunk", 0), ("seg_chunks", -1), ("reserved", 1),
+    ("B", 0), ("H", -1), ("L", 0), ("Dk", 0), ("Dv", 0), ("chunk", 0), ("seg_chunks", -1), ("flags", 2), ("flags", -1),
     ("in_dtype", 7), ("gate_kind", 9), ("log_alpha", None),
     ("q", A + 2), ("v", A + 8), ("out", A + 4), ("log_alpha", A + 4), ("final_state", A + 12),
     ("initial_state", A + 1), ("log_ig", A + 2),
@@ -164,12 +167,31 @@ def test_automatic_segmentation(lib, B, H, L, Dv, chunk, expect_seg):
 
 
 def test_lds_limit_reported_as_unsupported(lib):
-    # fp32 operands with a per-channel gate and several tiles per chunk need more than the
-    # 160 KB of LDS of a compute unit; the bf16 cases of the same shapes fit
-    assert status(lib, desc(Dk=128, chunk=128, in_dtype=gla.DTYPE_F32))[0] == gla.GLA_ERR_UNSUPPORTED
-    assert status(lib, desc(Dk=256, chunk=128, in_dtype=gla.DTYPE_F32, gate_kind=gla.GATE_HEAD))[0] == \
+    # the tile-pair form keeps a whole chunk's query tiles in LDS: fp32 operands with a
+    # per-channel gate (Dk = 128) or Dk = 256 need more than the 160 KB of a compute unit
+    TP = gla.FLAG_TILE_PAIRS
+    assert status(lib, desc(Dk=128, chunk=128, in_dtype=gla.DTYPE_F32, flags=TP))[0] == gla.GLA_ERR_UNSUPPORTED
+    assert status(lib, desc(Dk=256, chunk=128, in_dtype=gla.DTYPE_F32, gate_kind=gla.GATE_HEAD, flags=TP))[0] == \
         gla.GLA_ERR_UNSUPPORTED
-    assert status(lib, desc(Dk=128, chunk=64, in_dtype=gla.DTYPE_F32))[0] == gla.GLA_OK
-    assert status(lib, desc(Dk=256, chunk=64, in_dtype=gla.DTYPE_F32))[0] == gla.GLA_OK
-    assert status(lib, desc(Dk=128, chunk=512))[0] == gla.GLA_OK
-    assert status(lib, desc(Dk=256, chunk=512))[0] == gla.GLA_OK
+    assert status(lib, desc(Dk=128, chunk=128, in_dtype=gla.DTYPE_F32, gate_kind=gla.GATE_HEAD, flags=TP))[0] == \
+        gla.GLA_OK
+    # the same shapes without tile pairs walk 64-token tiles and fit
+    assert status(lib, desc(Dk=128, chunk=128, in_dtype=gla.DTYPE_F32))[0] == gla.GLA_OK
+    assert status(lib, desc(Dk=256, chunk=512, in_dtype=gla.DTYPE_F32))[0] == gla.GLA_OK
+    assert status(lib, desc(Dk=128, chunk=64, in_dtype=gla.DTYPE_F32, flags=TP))[0] == gla.GLA_OK
+    assert status(lib, desc(Dk=256, chunk=64, in_dtype=gla.DTYPE_F32, flags=TP))[0] == gla.GLA_OK
+    for f in (0, TP):
+        assert status(lib, desc(Dk=128, chunk=512, flags=f))[0] == gla.GLA_OK
+        assert status(lib, desc(Dk=256, chunk=512, flags=f))[0] == gla.GLA_OK
+
+
+def test_tile_pair_flag_in_plan(lib):
+    for chunk in (64, 128, 256, 512):
+        p0 = gla.plan(desc(chunk=chunk))
+        p1 = gla.plan(desc(chunk=chunk, flags=gla.FLAG_TILE_PAIRS))
+        assert p0.tiles_per_chunk == p1.tiles_per_chunk == chunk // 64
+        assert p0.tile_pairs == 0 and p1.tile_pairs == (1 if chunk > 64 else 0)
+        assert p0.workspace_bytes == 0
+        # per-channel gate, tile pairs: keys of the earlier tiles of a chunk go to scratch
+        assert p1.workspace_bytes == (0 if chunk == 64 else
+                                      (p1.grid_out * (chunk // 64 - 1) * 64 * 128 * 2 + 255) // 256 * 256)

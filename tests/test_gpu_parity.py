@@ -30,14 +30,14 @@ def gate_name(w):
     return w.gate
 
 
-def run_gpu(gla, d, w, chunk=None, seg_chunks=0, initial_state=None, final_state=True):
+def run_gpu(gla, d, w, chunk=None, seg_chunks=0, initial_state=None, final_state=True, tile_pairs=False):
     dev = "cuda"
     q, k, v = (d[x].to(dev) for x in "qkv")
     la = None if d["log_alpha"] is None else d["log_alpha"].to(dev)
     li = None if d["log_ig"] is None else d["log_ig"].to(dev)
     s0 = None if initial_state is None else initial_state.to(dev)
     out, fin = gla.fwd(q, k, v, la, log_ig=li, initial_state=s0, chunk=chunk or w.chunk,
-                       final_state=final_state, seg_chunks=seg_chunks)
+                       final_state=final_state, seg_chunks=seg_chunks, tile_pairs=tile_pairs)
     torch.cuda.synchronize()
     return out.cpu().double().numpy(), None if fin is None else fin.cpu().double().numpy()
 
@@ -71,12 +71,13 @@ for dtype in ("bf16", "f32"):
                 SMALL.append((dtype, gate, ig, Dk, Dv, chunk))
 
 
-def supported(gla, w):
+def supported(gla, w, tile_pairs=False):
     """Status of the library's own support check for a workload (no GPU work)."""
     d = gin.make_inputs(w.with_(L=1), seed=0)
     t = {k: v for k, v in d.items()}
     out = torch.empty(w.B, w.H, 1, w.Dv)
-    desc = gla.make_desc(t["q"], t["k"], t["v"], t["log_alpha"], t["log_ig"], None, out, None, w.chunk)
+    desc = gla.make_desc(t["q"], t["k"], t["v"], t["log_alpha"], t["log_ig"], None, out, None, w.chunk,
+                         tile_pairs=tile_pairs)
     try:
         gla.workspace_size(desc)
         return True
@@ -89,12 +90,25 @@ def supported(gla, w):
 @pytest.mark.parametrize("L", [1, 100, 333])
 def test_small_shapes(gpu_lib, dtype, gate, ig, Dk, Dv, chunk, L):
     w = gin.custom(2, 2, L, Dk, Dv, chunk, dtype=dtype, gate=gate, input_gate=ig)
-    if not supported(gpu_lib, w):
-        # fp32 operands with several tiles per chunk: more LDS than a compute unit has
-        assert dtype == "f32" and chunk > 64
-        pytest.skip("configuration reported unsupported (LDS budget)")
+    assert supported(gpu_lib, w)
     d = gin.make_inputs(w, seed=L)
     out, fin = run_gpu(gpu_lib, d, w)
+    ref, rfin = run_oracle(d, w)
+    check(w, out, ref)
+    check(w, fin, rfin, "final_state")
+
+
+@pytest.mark.parametrize("dtype,gate,ig,Dk,Dv,chunk", [c for c in SMALL if c[5] > 64])
+@pytest.mark.parametrize("L", [100, 333])
+def test_small_shapes_tile_pairs(gpu_lib, dtype, gate, ig, Dk, Dv, chunk, L):
+    # the tiled large-chunk form: terms between the 64-token tiles of a chunk as tile pairs
+    w = gin.custom(2, 2, L, Dk, Dv, chunk, dtype=dtype, gate=gate, input_gate=ig)
+    if not supported(gpu_lib, w, tile_pairs=True):
+        # fp32 operands with several tiles per chunk: more LDS than a compute unit has
+        assert dtype == "f32"
+        pytest.skip("configuration reported unsupported (LDS budget)")
+    d = gin.make_inputs(w, seed=L)
+    out, fin = run_gpu(gpu_lib, d, w, tile_pairs=True)
     ref, rfin = run_oracle(d, w)
     check(w, out, ref)
     check(w, fin, rfin, "final_state")
@@ -103,13 +117,14 @@ def test_small_shapes(gpu_lib, dtype, gate, ig, Dk, Dv, chunk, L):
 @pytest.mark.parametrize("gate,ig,chunk", [("channel", False, 64), ("channel", True, 128), ("head", True, 256),
                                            ("head_const", False, 128), ("none", False, 64)])
 @pytest.mark.parametrize("seg_chunks", [1, 2, 3])
-def test_sequence_segments(gpu_lib, gate, ig, chunk, seg_chunks):
+@pytest.mark.parametrize("tile_pairs", [False, True])
+def test_sequence_segments(gpu_lib, gate, ig, chunk, seg_chunks, tile_pairs):
     # several segments exercise the segment-state and segment-scan kernels; seg_chunks = 1 is
     # one state per chunk (the chunk-state / chunk-scan / chunk-output decomposition)
     w = gin.custom(1, 3, 1000, 128, 128, chunk, gate=gate, input_gate=ig)
     d = gin.make_inputs(w, seed=7)
     s0 = torch.randn(1, 3, 128, 128, generator=torch.Generator().manual_seed(3)) * 0.1
-    out, fin = run_gpu(gpu_lib, d, w, seg_chunks=seg_chunks, initial_state=s0)
+    out, fin = run_gpu(gpu_lib, d, w, seg_chunks=seg_chunks, initial_state=s0, tile_pairs=tile_pairs)
     ref, rfin = run_oracle(d, w, initial_state=s0)
     check(w, out, ref)
     check(w, fin, rfin, "final_state")
@@ -126,12 +141,15 @@ def test_segment_modes_agree(gpu_lib):
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("gate,chunk", [("channel", 64), ("channel", 128), ("head", 64), ("head", 256)])
-def test_gate_zero_keeps_only_current_token(gpu_lib, dtype, gate, chunk):
+@pytest.mark.parametrize("tile_pairs", [False, True])
+def test_gate_zero_keeps_only_current_token(gpu_lib, dtype, gate, chunk, tile_pairs):
     # alpha -> 0 (log gate -1e4 underflows to an exact zero): o_t = (q_t . k_t) v_t
     w = gin.custom(1, 2, 200, 64, 64, chunk, dtype=dtype, gate=gate)
     d = gin.make_inputs(w, seed=5)
     d["log_alpha"] = torch.full_like(d["log_alpha"], -1e4)
-    out, fin = run_gpu(gpu_lib, d, w)
+    if not supported(gpu_lib, w, tile_pairs):
+        pytest.skip("configuration reported unsupported (LDS budget)")
+    out, fin = run_gpu(gpu_lib, d, w, tile_pairs=tile_pairs)
     ref, rfin = run_oracle(d, w)
     check(w, out, ref)
     check(w, fin, rfin, "final_state")
@@ -213,20 +231,24 @@ def test_caller_workspace(gpu_lib):
 
 # ------------------------------------------------------------------------------ full-size workloads
 FULL = [
-    ("ungated_f32_L256", None),
-    ("gla_bf16_B8H16L2048", [0, 37, 127]),
-    ("retnet_bf16_B4H8L8192", [0, 7, 20, 31]),
-    ("long_gla_bf16_H16L32768_C64", [0, 9, 15]),
-    ("long_gla_bf16_H16L32768_C256", [0, 9, 15]),
-    ("mlstm_sig_bf16_B8H8L8192", [0, 45]),
+    ("ungated_f32_L256", None, False),
+    ("gla_bf16_B8H16L2048", [0, 37, 127], False),
+    ("retnet_bf16_B4H8L8192", [0, 7, 20, 31], False),
+    ("retnet_bf16_B4H8L8192", [3, 30], True),
+    ("long_gla_bf16_H16L32768_C64", [0, 9, 15], False),
+    ("long_gla_bf16_H16L32768_C256", [0, 9, 15], False),
+    ("long_gla_bf16_H16L32768_C256", [4], True),
+    ("mlstm_sig_bf16_B8H8L8192", [0, 45], False),
+    ("mlstm_sig_bf16_B8H8L8192", [63], True),
 ]
 
 
-@pytest.mark.parametrize("name,heads", FULL, ids=[f[0] for f in FULL])
-def test_full_workload_sampled_heads(gpu_lib, name, heads):
+@pytest.mark.parametrize("name,heads,tile_pairs", FULL,
+                         ids=[f[0] + ("_tile_pairs" if f[2] else "") for f in FULL])
+def test_full_workload_sampled_heads(gpu_lib, name, heads, tile_pairs):
     w = gin.WORKLOADS[name]
     d = gin.make_inputs(w, seed=0)
-    out, fin = run_gpu(gpu_lib, d, w)
+    out, fin = run_gpu(gpu_lib, d, w, tile_pairs=tile_pairs)
     if heads is None:
         ref, rfin = run_oracle(d, w)
         check(w, out, ref)
