@@ -236,13 +236,19 @@ def main():
     tflops = flops / (ms_per_step * 1e-3) / 1e12
 
     # Dominant kernel: the chunk-output kernel.  With one segment it is the only launch of
-    # a step, so the events around the call time exactly that kernel.
+    # a step, so the events around the call time exactly that kernel.  With several
+    # segments the step also runs the segment-state kernel (k, v and gates of all but the
+    # last segment in, one fp32 state and decay per segment boundary out) and the scan
+    # (boundary states in and out); the roofline then covers the whole step.
     if plan.n_seg == 1:
         kbytes = io
         scope = "chunk-output kernel (the only launch of a step)"
     else:
-        kbytes = io + w.B * w.H * (plan.n_seg - 1) * w.Dk * w.Dv * 4.0 * 3 \
-            + 2.0 * w.B * w.H * (plan.n_seg - 1) * w.L / plan.n_seg * (w.Dk * 2 + w.Dv) * (4 if w.dtype == "f32" else 2)
+        ib = 4 if w.dtype == "f32" else 2
+        gate = {"channel": 4 * w.Dk, "head": 4, "head_const": 0, "none": 0}[w.gate] + (4 if w.input_gate else 0)
+        bnd = w.B * w.H * (plan.n_seg - 1)
+        kbytes = io + 4.0 * bnd * (w.Dk * w.Dv + w.Dk) * 4 \
+            + float(w.B * w.H * w.L) * (plan.n_seg - 1) / plan.n_seg * (ib * (w.Dk + w.Dv) + gate)
         scope = "step (segment-state, segment-scan and chunk-output kernels)"
     achieved = kbytes / (mean_launch_ms * 1e-3) / 1e9
     traffic = measured_traffic(wname) if plan.n_seg == 1 else None
