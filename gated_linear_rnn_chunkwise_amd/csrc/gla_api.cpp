@@ -98,8 +98,12 @@ int make_plan(const gla_desc *d, Plan *p) {
     p->grid_state = (int)g1;
     p->grid_scan = p->nseg > 1 ? (int)(bh * ((int64_t(d->Dk) * d->Dv + 1023) / 1024)) : 0;
     const int opb = f32 ? 4 : 2;
-    p->lds_out = gla::use_ws_kernel(opb, d->Dk, p->knt) ? gla::lds_plan_ws(opb, d->Dk).total
-                                                       : gla::lds_plan(opb, d->Dk, ch, p->knt).total;
+    if (gla::use_sg_kernel(opb, d->Dk, p->knt, ch))
+        p->lds_out = gla::lds_plan_sg(d->Dk).total;
+    else if (gla::use_ws_kernel(opb, d->Dk, p->knt))
+        p->lds_out = gla::lds_plan_ws(opb, d->Dk).total;
+    else
+        p->lds_out = gla::lds_plan(opb, d->Dk, ch, p->knt).total;
     p->lds_state = gla::lds_plan(opb, d->Dk, ch, 1).total;
     if (p->lds_out > gla::kMaxLds || p->lds_state > gla::kMaxLds) return GLA_ERR_UNSUPPORTED;
     const size_t nsm = (size_t)(p->nseg - 1);

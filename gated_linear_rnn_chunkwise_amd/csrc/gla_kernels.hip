@@ -1524,6 +1524,360 @@ __global__ __launch_bounds__(512, 1) void chunk_output_ws_kernel(KArgs a) {
 }
 
 // ------------------------------------------------------------------------------------
+// Warp-specialised chunk output for scalar gates (none, per head and token, fixed per
+// head) with bf16 inputs, 64-token chunks and Dk = 256.  grid = BH * nseg * ndv
+// workgroups of 512 threads.
+//
+// Producers (waves 4..7): lane (row block g = lane>>4, channel group c16 = lane&15) of
+// wave pw holds channels 4*(16*pw + c16) .. +3 of the 16 rows of block g, so it owns four
+// consecutive tokens of each channel for the transposed key operand.  Consumers (waves
+// 0..3): 16 value columns each, the Dk x 16 state in registers.  Per tile k:
+//   phase A  consumers: score blocks (q, k), O = diag(2^b) (q . S), state update
+//            S <- 2^T S + (k 2^(T - b + l))^T v    (q, k, k^T: single buffers;
+//            values and row decays: buffer k&1)
+//            producers: decay scan, values and row decays of tile k+1 into buffer (k+1)&1,
+//            fp16 q, k and scaled k^T of tile k+1 into registers; loads of tile k+2
+//   B1
+//   phase B  consumers: masked scores x values, output stores
+//            producers: q, k, k^T of tile k+1 into the single buffers
+//   B2
+// With a scalar gate the queries need no scaling to the tile start: the inter-chunk
+// product takes raw q and its output rows are scaled by 2^(b_t) in fp32.
+//
+// LDS layouts.  q and k rows hold their channels permuted inside each 32-channel group
+// (sg_perm) so that the 8 channels one lane feeds to the q . S product, which follow the
+// state accumulators' row order, are 16 contiguous bytes; the score products see q and k
+// under the same permutation, which leaves their dot products unchanged.  Rows of k^T
+// keep their 16-byte groups XOR-swizzled by (row >> 4) & 7, which spreads the producers'
+// transposed writes over the LDS banks while the consumers' reads stay conflict-free.
+
+// Position of channel c inside its 32-channel group.
+__device__ __forceinline__ int sg_perm(int c) { return 8 * ((c & 15) >> 2) + 4 * ((c >> 4) & 1) + (c & 3); }
+// Offset (in fp16 elements) of token slot s of row r of k^T.
+__device__ __forceinline__ int sg_kt(int r, int s) { return r * 72 + ((((s >> 3) ^ (r >> 4)) & 7) << 3) + (s & 7); }
+
+template <class C>
+struct RawSg {
+    u32x2 q[16], k[16];  // 4 bf16 channels of rows 16g + rr
+    uint32_t v[4][2];    // 4 values of one row
+    float las, lis;      // log gate and log input gate of row (tile start + lane)
+};
+
+template <class C>
+__device__ __forceinline__ void load_unit_sg(RawSg<C> &r, const Rs &rs, int T0, int pw, int lane, int dv0, int Dv) {
+    const int g = lane >> 4, c16 = lane & 15;
+    const int ch0 = 4 * (16 * pw + c16);
+    const uint32_t row0 = (uint32_t)(T0 + 16 * g);
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) {
+        const uint32_t off = ((row0 + rr) * C::DK + ch0) * 2u;
+        r.q[rr] = bld64(rs.q, off);
+        r.k[rr] = bld64(rs.k, off);
+    }
+    const uint32_t t = (uint32_t)(T0 + lane);
+    if (rs.gate == GLA_GATE_HEAD) {
+        r.las = __uint_as_float(bld32(rs.la, t * 4u));
+    } else if (rs.gate == GLA_GATE_HEAD_CONST) {
+        const float x = __uint_as_float(bld32(rs.la, 0));
+        r.las = (int)t < rs.L ? x : 0.f;
+    } else {
+        r.las = 0.f;
+    }
+    r.lis = __uint_as_float(bld32(rs.li, t * 4u));
+    const int tp = 64 * pw + lane;
+    const uint32_t c0 = dv0 + 4 * (tp & 15);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const uint32_t off = ((uint32_t)(T0 + 4 * (tp >> 4) + e) * Dv + c0) * 2u;
+        const u32x2 x = bld64(rs.v, off);
+        r.v[e][0] = x[0];
+        r.v[e][1] = x[1];
+    }
+}
+
+template <class C>
+struct ProdSg {
+    u32x2 qh[16], kh[16];  // fp16 q, k of rows 16g + rr (4 channels)
+    f16x4 kt[4][4];        // [channel][token group]: scaled keys of 4 consecutive tokens
+};
+
+// Phase A: values and row decays into buffer nb, operands of the tile into registers.
+template <class C>
+__device__ __forceinline__ void sg_produce_a(ProdSg<C> &pv, const RawSg<C> &raw, const LdsPlanSg &lp,
+                                             unsigned char *smem, int nb, int pw, int lane) {
+    const int g = lane >> 4;
+    // values in MFMA B-operand order (as v_to_lds)
+    {
+        f16 *sV = reinterpret_cast<f16 *>(smem + lp.vb) + nb * 4096;
+        const int tid = 64 * pw + lane;
+        const int quad = tid >> 4;
+        const int p = quad >> 3, hh = (quad >> 2) & 1, gq = quad & 3;
+        const int c0 = 4 * (tid & 15);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            f16x4 h4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) h4[e] = (f16)((j & 1) ? bf_hi(raw.v[e][j >> 1]) : bf_lo(raw.v[e][j >> 1]));
+            *reinterpret_cast<f16x4 *>(sV + ((p * 4 + gq) * 64 + c0 + j) * 8 + hh * 4) = h4;
+        }
+    }
+    // running log2 decay over the tile's rows (lane = row) and the key weights
+    const float x = raw.las * kLog2e;
+    const float y = raw.lis * kLog2e;
+    const float bl = scan_incl(x, lane);
+    const float T = __shfl(bl, 63);
+    if (pw == 0) {
+        float *sR = reinterpret_cast<float *>(smem + lp.rows) + nb * 128;
+        sR[lane] = bl;
+        sR[64 + lane] = y;
+    }
+    const float wk = fexp2(T - bl + y);  // weight of key row `lane` in the state update
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) {
+        const float w = __shfl(wk, 16 * g + rr);
+        float qf[4], kf[4];
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            qf[2 * c] = bf_lo(raw.q[rr][c]);
+            qf[2 * c + 1] = bf_hi(raw.q[rr][c]);
+            kf[2 * c] = bf_lo(raw.k[rr][c]);
+            kf[2 * c + 1] = bf_hi(raw.k[rr][c]);
+        }
+        pv.qh[rr] = u32x2{__builtin_bit_cast(uint32_t, f16x2{(f16)qf[0], (f16)qf[1]}),
+                          __builtin_bit_cast(uint32_t, f16x2{(f16)qf[2], (f16)qf[3]})};
+        pv.kh[rr] = u32x2{__builtin_bit_cast(uint32_t, f16x2{(f16)kf[0], (f16)kf[1]}),
+                          __builtin_bit_cast(uint32_t, f16x2{(f16)kf[2], (f16)kf[3]})};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) pv.kt[c][rr >> 2][rr & 3] = (f16)(kf[c] * w);
+    }
+}
+
+// Phase B: q, k and the scaled keys^T of the prepared tile into the single buffers.
+template <class C>
+__device__ __forceinline__ void sg_produce_b(const ProdSg<C> &pv, const LdsPlanSg &lp, unsigned char *smem, int pw,
+                                             int lane) {
+    const int g = lane >> 4, c16 = lane & 15;
+    const int ch0 = 4 * (16 * pw + c16);
+    const int pc = (ch0 & ~31) + sg_perm(ch0 & 31);
+    f16 *sQ = reinterpret_cast<f16 *>(smem + lp.q);
+    f16 *sK = reinterpret_cast<f16 *>(smem + lp.k);
+    f16 *sKT = reinterpret_cast<f16 *>(smem + lp.kst);
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) {
+        const int row = 16 * g + rr;
+        *reinterpret_cast<u32x2 *>(sQ + row * (C::DK + 8) + pc) = pv.qh[rr];
+        *reinterpret_cast<u32x2 *>(sK + row * (C::DK + 8) + pc) = pv.kh[rr];
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4)
+            *reinterpret_cast<f16x4 *>(sKT + sg_kt(ch0 + c, kslot(16 * g + 4 * g4))) = pv.kt[c][g4];
+}
+
+template <class C>
+__global__ __launch_bounds__(512, 1) void chunk_output_sg_kernel(KArgs a) {
+    static_assert(!C::F32 && !C::CH && !C::MT && C::DK == 256, "bf16, scalar gate, 64-token tiles, Dk = 256");
+    constexpr int DK = C::DK;
+    constexpr int RP = DK + 8;
+    constexpr int KSTEP = DK / 32;
+    constexpr int NBD = DK / 16;
+    extern __shared__ __align__(256) unsigned char smem[];
+    const LdsPlanSg lp = lds_plan_sg(DK);
+
+    int id = xcd_remap((int)blockIdx.x, a.nwg);
+    const int dvt = id % a.ndv;
+    id /= a.ndv;
+    const int seg = id % a.nseg;
+    const int bh = id / a.nseg;
+    const int h = bh % a.H;
+    const int tid = (int)threadIdx.x, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int L = a.L, Dv = a.Dv;
+    const int dv0 = dvt * kDvTile;
+    const int t_begin = seg * a.seg_len;
+    const int t_end = min(L, t_begin + a.seg_len);
+    const int nch = (t_end - t_begin + kTile - 1) / kTile;
+    const Rs rs = make_rs<C>(a, bh, h);
+
+    if (w >= 4) {
+        // ============================ producers
+        // Unconditional loop body, as in the per-channel kernel: the last iteration prepares
+        // a tile past the segment into buffers no consumer reads again, and the prefetch two
+        // tiles ahead reads rows past the (batch, head) extent as zero.
+        const int pw = w - 4;
+        RawSg<C> raw;
+        ProdSg<C> pv;
+        load_unit_sg<C>(raw, rs, t_begin, pw, lane, dv0, Dv);
+        sg_produce_a<C>(pv, raw, lp, smem, 0, pw, lane);
+        load_unit_sg<C>(raw, rs, t_begin + kTile, pw, lane, dv0, Dv);
+        sg_produce_b<C>(pv, lp, smem, pw, lane);
+        lds_barrier();
+        for (int kc = 0; kc < nch; ++kc) {
+            sg_produce_a<C>(pv, raw, lp, smem, (kc + 1) & 1, pw, lane);
+            load_unit_sg<C>(raw, rs, t_begin + kTile * (kc + 2), pw, lane, dv0, Dv);
+            lds_barrier();  // B1
+            sg_produce_b<C>(pv, lp, smem, pw, lane);
+            lds_barrier();  // B2
+        }
+        return;
+    }
+
+    // ================================ consumers
+    const int cw = w;
+    const int col = dv0 + 16 * cw + c16;
+    const f16 *sQ = reinterpret_cast<const f16 *>(smem + lp.q);
+    const f16 *sK = reinterpret_cast<const f16 *>(smem + lp.k);
+    const f16 *sKT = reinterpret_cast<const f16 *>(smem + lp.kst);
+    f16 *sP = reinterpret_cast<f16 *>(smem + lp.pbuf);
+
+    f32x4 S[NBD];
+#pragma unroll
+    for (int n = 0; n < NBD; ++n) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int d = 16 * n + 4 * g + e;
+            float x = 0.f;
+            if (seg > 0)
+                x = a.ws_state[(((size_t)bh * (a.nseg - 1) + (seg - 1)) * DK + d) * Dv + col];
+            else if (a.s0)
+                x = a.s0[((size_t)bh * DK + d) * Dv + col];
+            S[n][e] = x;
+        }
+    }
+    lds_barrier();  // tile 0 prepared
+
+    // this wave's score blocks (query block i, key block j); pair 0 is the diagonal
+    int pi[3], pj[3];
+    pi[0] = cw;
+    pj[0] = cw;
+    switch (cw) {
+        case 0: pi[1] = 1; pj[1] = 0; pi[2] = 3; pj[2] = 2; break;
+        case 1: pi[1] = 2; pj[1] = 0; pi[2] = 3; pj[2] = 1; break;
+        case 2: pi[1] = 2; pj[1] = 1; pi[2] = 2; pj[2] = 1; break;
+        default: pi[1] = 3; pj[1] = 0; pi[2] = 3; pj[2] = 0; break;
+    }
+
+    for (int kc = 0; kc < nch; ++kc) {
+        const int b = kc & 1;
+        const int T0 = t_begin + kTile * kc;
+        const f16 *sV = reinterpret_cast<const f16 *>(smem + lp.vb) + b * 4096;
+        const float *sB = reinterpret_cast<const float *>(smem + lp.rows) + b * 128;
+        const float *sL = sB + 64;
+
+        // ---------------- phase A: score blocks P^T(j, i)
+        f32x4 Pd[3];
+#pragma unroll
+        for (int kp = 0; kp < 3; ++kp) Pd[kp] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int m = 0; m < KSTEP; ++m) {
+            const int ch = 32 * m + 8 * g;
+            f16x8 af[3], bf[3];
+#pragma unroll
+            for (int kp = 0; kp < 3; ++kp) {
+                af[kp] = lds_ld<f16x8>(sK + (16 * pj[kp] + c16) * RP + ch);
+                bf[kp] = lds_ld<f16x8>(sQ + (16 * pi[kp] + c16) * RP + ch);
+            }
+#pragma unroll
+            for (int kp = 0; kp < 3; ++kp) Pd[kp] = mma(af[kp], bf[kp], Pd[kp]);
+        }
+        // inter-chunk term O = diag(2^b) (q . S): the permuted q row holds, at 32m + 8g,
+        // channels 32m + 4g + e and 32m + 16 + 4g + e, the rows of state blocks 2m and 2m+1
+        f32x4 O[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) O[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int m = 0; m < KSTEP; ++m) {
+            f16x8 sb;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                sb[e] = (f16)S[2 * m][e];
+                sb[e + 4] = (f16)S[2 * m + 1][e];
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                O[i] = mma(lds_ld<f16x8>(sQ + (16 * i + c16) * RP + 32 * m + 8 * g), sb, O[i]);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const f32x4 bq = lds_ld<f32x4>(sB + 16 * i + 4 * g);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) O[i][e] *= fexp2(bq[e]);
+        }
+        // mask and exact decay of the scores, stored in MFMA A-operand order
+#pragma unroll
+        for (int kp = 0; kp < 3; ++kp) {
+            if (kp == 2 && cw >= 2) continue;  // repeated pair
+            const int i = pi[kp], j = pj[kp];
+            const float bt = sB[16 * i + c16];
+            f16x4 pvv;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int s2 = 4 * g + e;
+                const bool masked = i == j && s2 > c16;
+                const float x = Pd[kp][e] * fexp2(bt - sB[16 * j + s2] + sL[16 * j + s2]);
+                pvv[e] = (f16)(masked ? 0.f : x);
+            }
+            *reinterpret_cast<f16x4 *>(sP + ((i * 2 + (j >> 1)) * 64 + lane) * 8 + 4 * (j & 1)) = pvv;
+        }
+        if (cw == 0 || cw == 2) {
+            const f16x4 z{(f16)0.f, (f16)0.f, (f16)0.f, (f16)0.f};
+            *reinterpret_cast<f16x4 *>(sP + ((cw * 2 + (cw >> 1)) * 64 + lane) * 8 + 4) = z;
+        }
+        // state update S <- 2^T S + K~^T V
+        f16x8 vfr[2];
+#pragma unroll
+        for (int p = 0; p < 2; ++p) vfr[p] = lds_ld<f16x8>(sV + ((p * 4 + g) * 64 + 16 * cw + c16) * 8);
+        {
+            const float at = fexp2(sB[63]);
+#pragma unroll
+            for (int n = 0; n < NBD; ++n) S[n] *= at;
+#pragma unroll
+            for (int p = 0; p < 2; ++p) {
+#pragma unroll
+                for (int n = 0; n < NBD; ++n) {
+                    const int r = 16 * n + c16;
+                    S[n] = mma(lds_ld<f16x8>(sKT + sg_kt(r, (p * 4 + g) * 8)), vfr[p], S[n]);
+                }
+            }
+        }
+        lds_barrier();  // B1: scores stored; q, k, k^T free for the next tile
+
+        // ---------------- phase B: scores x values, output
+        {
+            f16x8 pa[6];
+            pa[0] = lds_ld<f16x8>(sP + ((0 * 2 + 0) * 64 + lane) * 8);
+            pa[1] = lds_ld<f16x8>(sP + ((1 * 2 + 0) * 64 + lane) * 8);
+            pa[2] = lds_ld<f16x8>(sP + ((2 * 2 + 0) * 64 + lane) * 8);
+            pa[3] = lds_ld<f16x8>(sP + ((3 * 2 + 0) * 64 + lane) * 8);
+            pa[4] = lds_ld<f16x8>(sP + ((2 * 2 + 1) * 64 + lane) * 8);
+            pa[5] = lds_ld<f16x8>(sP + ((3 * 2 + 1) * 64 + lane) * 8);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) O[i] = mma(pa[i], vfr[0], O[i]);
+            O[2] = mma(pa[4], vfr[1], O[2]);
+            O[3] = mma(pa[5], vfr[1], O[3]);
+        }
+        {
+            const uint32_t ob = ((uint32_t)(T0 + 4 * g) * Dv + col) * 4u;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(O[i][e]), rs.out,
+                                                          (int)(ob + (uint32_t)((16 * i + e) * Dv * 4)), 0, 0);
+        }
+        lds_barrier();  // B2
+    }
+
+    if (seg == a.nseg - 1 && a.fin) {
+#pragma unroll
+        for (int n = 0; n < NBD; ++n)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) a.fin[((size_t)bh * DK + 16 * n + 4 * g + e) * Dv + col] = S[n][e];
+    }
+}
+
+// ------------------------------------------------------------------------------------
 // segment_state_kernel: grid = BH * (nseg - 1) * ndv.  The state segment `seg` produces
 // from zero, sum_s diag(decay from s to the segment end) i_s k_s^T v_s, accumulated tile by
 // tile (dS <- diag(tile decay) dS + K~^T V), and the decay across the segment.
@@ -1724,7 +2078,14 @@ static hipError_t launch_cfg(const KArgs &a, hipStream_t st) {
     }
     KArgs a3 = a;
     a3.nwg = (a.B * a.H) * a.nseg * a.ndv;
-    if constexpr (!C::MT && C::NSLAB == 1) {
+    if constexpr (!C::F32 && !C::CH && !C::MT && C::DK == 256) {
+        const LdsPlanSg lg = lds_plan_sg(C::DK);
+        err = hipFuncSetAttribute(reinterpret_cast<const void *>(&chunk_output_sg_kernel<C>),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)lg.total);
+        if (err != hipSuccess) return err;
+        hipLaunchKernelGGL(chunk_output_sg_kernel<C>, dim3(a3.nwg), dim3(2 * kThreads), lg.total, st, a3);
+        return hipGetLastError();
+    } else if constexpr (!C::MT && C::NSLAB == 1) {
         const LdsPlanWs lw = lds_plan_ws(C::OPB, C::DK);
         err = hipFuncSetAttribute(reinterpret_cast<const void *>(&chunk_output_ws_kernel<C>),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)lw.total);

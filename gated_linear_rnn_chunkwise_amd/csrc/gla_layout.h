@@ -150,6 +150,45 @@ GLA_HD inline LdsPlanWs lds_plan_ws(int opb, int dk) {
 // slab (bf16 with Dk <= 128, fp32 with Dk = 64); the launcher makes the same choice.
 GLA_HD inline bool use_ws_kernel(int opb, int dk, int nt) { return nt == 1 && dk == 64 * chan_per_lane(opb, dk); }
 
+// LDS of the scalar-gate warp-specialised kernel (bf16 inputs, 64-token chunks, Dk = 256).
+// q, k and the scaled keys^T are single buffers (consumers read them before the mid-tile
+// barrier); values and row decays are double-buffered by tile parity.
+struct LdsPlanSg {
+    uint32_t q;     // [64][dk + 8] fp16 q, channels permuted inside 32-channel groups
+    uint32_t k;     // [64][dk + 8] fp16 k, same permutation
+    uint32_t kst;   // [dk][72] fp16 keys scaled to the tile end, transposed, k-slot order, swizzled
+    uint32_t vb;    // [2][4096] fp16 value tiles
+    uint32_t rows;  // [2][128] fp32: log2 running decay of each row, then log2 input gate
+    uint32_t pbuf;  // [4096] fp16 masked scores
+    uint32_t total;
+};
+
+GLA_HD inline LdsPlanSg lds_plan_sg(int dk) {
+    auto al = [](uint32_t x) { return (x + 255u) & ~255u; };
+    LdsPlanSg p{};
+    uint32_t off = 0;
+    p.q = off;
+    off += al(64u * (uint32_t)(dk + 8) * 2u);
+    p.k = off;
+    off += al(64u * (uint32_t)(dk + 8) * 2u);
+    p.kst = off;
+    off += al((uint32_t)dk * 72u * 2u);
+    p.vb = off;
+    off += al(2u * 4096u * 2u);
+    p.rows = off;
+    off += al(2u * 128u * 4u);
+    p.pbuf = off;
+    off += al(4096u * 2u);
+    p.total = off;
+    return p;
+}
+
+// The scalar-gate kernel runs bf16 inputs with Dk = 256, 64-token tiles and no per-channel
+// gate; the launcher makes the same choice.
+GLA_HD inline bool use_sg_kernel(int opb, int dk, int nt, bool per_channel) {
+    return opb == 2 && nt == 1 && dk == 256 && !per_channel;
+}
+
 // Global scratch per chunk-output workgroup: keys of the earlier tiles of the current chunk
 // scaled to their tile end (per-channel gate with several tiles per chunk), [nt-1][64][dk].
 GLA_HD inline uint64_t ke_scratch_bytes(int opb, int dk, bool per_channel, int nt) {

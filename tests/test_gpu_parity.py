@@ -130,6 +130,18 @@ def test_sequence_segments(gpu_lib, gate, ig, chunk, seg_chunks, tile_pairs):
     check(w, fin, rfin, "final_state")
 
 
+@pytest.mark.parametrize("gate,ig", [("head", True), ("head_const", False), ("none", False)])
+@pytest.mark.parametrize("seg_chunks", [1, 3])
+def test_sequence_segments_dk256(gpu_lib, gate, ig, seg_chunks):
+    w = gin.custom(1, 2, 700, 256, 128, 64, gate=gate, input_gate=ig, scale_dim=256)
+    d = gin.make_inputs(w, seed=8)
+    s0 = torch.randn(1, 2, 256, 128, generator=torch.Generator().manual_seed(4)) * 0.05
+    out, fin = run_gpu(gpu_lib, d, w, seg_chunks=seg_chunks, initial_state=s0)
+    ref, rfin = run_oracle(d, w, initial_state=s0)
+    check(w, out, ref)
+    check(w, fin, rfin, "final_state")
+
+
 def test_segment_modes_agree(gpu_lib):
     w = gin.custom(1, 2, 2048, 128, 128, 64, gate="channel")
     d = gin.make_inputs(w, seed=11)
