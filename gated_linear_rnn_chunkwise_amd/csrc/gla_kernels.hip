@@ -234,6 +234,7 @@ struct Raw {
 struct Rs {
     rsrc_t q, k, v, la, li, out;
     int gate, L;
+    uint32_t gstride;  // bytes between the scalar gates of consecutive rows (0: one value or none)
     bool has_li;
 };
 
@@ -257,6 +258,7 @@ __device__ __forceinline__ Rs make_rs(const KArgs &a, int bh, int h) {
     r.li = a.li ? make_rsrc(a.li + bhL, L * 4) : make_rsrc(a.out, 0);
     r.gate = a.gate;
     r.L = a.L;
+    r.gstride = a.gate == GLA_GATE_HEAD ? 4u : 0u;
     r.has_li = a.li != nullptr;
     return r;
 }
@@ -1574,15 +1576,10 @@ __device__ __forceinline__ void load_unit_sg(RawSg<C> &r, const Rs &rs, int T0, 
         r.q[rr] = bld64(rs.q, off);
         r.k[rr] = bld64(rs.k, off);
     }
+    // One branch-free load for every scalar gate kind: per token (stride 4), fixed per head
+    // (stride 0, masked past the sequence end where it is used), none (empty resource).
     const uint32_t t = (uint32_t)(T0 + lane);
-    if (rs.gate == GLA_GATE_HEAD) {
-        r.las = __uint_as_float(bld32(rs.la, t * 4u));
-    } else if (rs.gate == GLA_GATE_HEAD_CONST) {
-        const float x = __uint_as_float(bld32(rs.la, 0));
-        r.las = (int)t < rs.L ? x : 0.f;
-    } else {
-        r.las = 0.f;
-    }
+    r.las = __uint_as_float(bld32(rs.la, t * rs.gstride));
     r.lis = __uint_as_float(bld32(rs.li, t * 4u));
     const int tp = 64 * pw + lane;
     const uint32_t c0 = dv0 + 4 * (tp & 15);
@@ -1604,7 +1601,7 @@ struct ProdSg {
 // Phase A: values and row decays into buffer nb, operands of the tile into registers.
 template <class C>
 __device__ __forceinline__ void sg_produce_a(ProdSg<C> &pv, const RawSg<C> &raw, const LdsPlanSg &lp,
-                                             unsigned char *smem, int nb, int pw, int lane) {
+                                             unsigned char *smem, int nb, int pw, int lane, bool row_valid) {
     const int g = lane >> 4;
     // values in MFMA B-operand order (as v_to_lds)
     {
@@ -1622,7 +1619,7 @@ __device__ __forceinline__ void sg_produce_a(ProdSg<C> &pv, const RawSg<C> &raw,
         }
     }
     // running log2 decay over the tile's rows (lane = row) and the key weights
-    const float x = raw.las * kLog2e;
+    const float x = row_valid ? raw.las * kLog2e : 0.f;
     const float y = raw.lis * kLog2e;
     const float bl = scan_incl(x, lane);
     const float T = __shfl(bl, 63);
@@ -1705,20 +1702,31 @@ __global__ __launch_bounds__(512, 1) void chunk_output_sg_kernel(KArgs a) {
         // Unconditional loop body, as in the per-channel kernel: the last iteration prepares
         // a tile past the segment into buffers no consumer reads again, and the prefetch two
         // tiles ahead reads rows past the (batch, head) extent as zero.
+        // Two register sets for the raw tiles, alternating over an unrolled pair of
+        // iterations, so the prefetch never has to be copied into the other set (a copy
+        // waits for the load).  Each iteration has two barriers, as the consumers'; the
+        // uniform breaks end the loop after exactly nch iterations.
         const int pw = w - 4;
-        RawSg<C> raw;
+        RawSg<C> ra, rb;
         ProdSg<C> pv;
-        load_unit_sg<C>(raw, rs, t_begin, pw, lane, dv0, Dv);
-        sg_produce_a<C>(pv, raw, lp, smem, 0, pw, lane);
-        load_unit_sg<C>(raw, rs, t_begin + kTile, pw, lane, dv0, Dv);
+        load_unit_sg<C>(ra, rs, t_begin, pw, lane, dv0, Dv);
+        sg_produce_a<C>(pv, ra, lp, smem, 0, pw, lane, t_begin + lane < L);
+        load_unit_sg<C>(rb, rs, t_begin + kTile, pw, lane, dv0, Dv);
         sg_produce_b<C>(pv, lp, smem, pw, lane);
         lds_barrier();
-        for (int kc = 0; kc < nch; ++kc) {
-            sg_produce_a<C>(pv, raw, lp, smem, (kc + 1) & 1, pw, lane);
-            load_unit_sg<C>(raw, rs, t_begin + kTile * (kc + 2), pw, lane, dv0, Dv);
+        for (int kc = 0;; kc += 2) {
+            sg_produce_a<C>(pv, rb, lp, smem, (kc + 1) & 1, pw, lane, t_begin + kTile * (kc + 1) + lane < L);
+            load_unit_sg<C>(ra, rs, t_begin + kTile * (kc + 2), pw, lane, dv0, Dv);
             lds_barrier();  // B1
             sg_produce_b<C>(pv, lp, smem, pw, lane);
             lds_barrier();  // B2
+            if (kc + 1 >= nch) break;
+            sg_produce_a<C>(pv, ra, lp, smem, (kc + 2) & 1, pw, lane, t_begin + kTile * (kc + 2) + lane < L);
+            load_unit_sg<C>(rb, rs, t_begin + kTile * (kc + 3), pw, lane, dv0, Dv);
+            lds_barrier();  // B1
+            sg_produce_b<C>(pv, lp, smem, pw, lane);
+            lds_barrier();  // B2
+            if (kc + 2 >= nch) break;
         }
         return;
     }
