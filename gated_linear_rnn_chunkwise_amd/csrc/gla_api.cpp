@@ -24,10 +24,11 @@ hipError_t launch_forward(const KArgs &a, bool f32, int dk, hipStream_t st);
 namespace {
 
 constexpr int kTargetWorkgroups = 256;     // one per compute unit on MI355X
+constexpr int kTargetStateWorkgroups = 768;  // the segment-state kernel fits three per compute unit
 constexpr int64_t kSmallProblem = 65536;   // head-tokens below which segmenting does not pay
 
 struct Plan {
-    int nt, nc, ndv, seg_chunks, nseg, seg_len;
+    int nt, nc, ndv, seg_chunks, nseg, seg_len, nsub;
     int knt;  // 64-token tiles per chunk as the kernels run it: nt with tile pairs, else 1
     int grid_state, grid_scan, grid_out;
     size_t ws_state_bytes, ws_decay_bytes, ws_ke_bytes, ws_bytes;
@@ -91,8 +92,23 @@ int make_plan(const gla_desc *d, Plan *p) {
     p->seg_chunks = sc;
     p->nseg = (p->nc + sc - 1) / sc;
     p->seg_len = sc * d->chunk;
+    // Segment boundary states are sums of sub-segment states, computed by more workgroups
+    // than there are boundaries: nsub is the largest divisor of the tiles per segment that
+    // keeps the state grid near kTargetStateWorkgroups.
+    p->nsub = 1;
+    if (p->nseg > 1) {
+        const int64_t base = bh * (p->nseg - 1) * p->ndv;
+        const int tiles = p->seg_len / gla::kTile;
+        const int64_t want = std::max<int64_t>(1, (kTargetStateWorkgroups + base - 1) / base);
+        for (int d = (int)std::min<int64_t>(want, tiles); d >= 1; --d)
+            if (tiles % d == 0) {
+                p->nsub = d;
+                break;
+            }
+    }
+    const int64_t nss = int64_t(p->nseg - 1) * p->nsub;
     const int64_t g3 = bh * p->nseg * p->ndv;
-    const int64_t g1 = p->nseg > 1 ? bh * (p->nseg - 1) * p->ndv : 0;
+    const int64_t g1 = p->nseg > 1 ? bh * nss * p->ndv : 0;
     if (g3 > INT32_MAX || g1 > INT32_MAX) return GLA_ERR_UNSUPPORTED;
     p->grid_out = (int)g3;
     p->grid_state = (int)g1;
@@ -104,11 +120,10 @@ int make_plan(const gla_desc *d, Plan *p) {
         p->lds_out = gla::lds_plan_ws(opb, d->Dk).total;
     else
         p->lds_out = gla::lds_plan(opb, d->Dk, ch, p->knt).total;
-    p->lds_state = gla::lds_plan(opb, d->Dk, ch, 1).total;
+    p->lds_state = gla::lds_plan_state(opb, d->Dk).total;
     if (p->lds_out > gla::kMaxLds || p->lds_state > gla::kMaxLds) return GLA_ERR_UNSUPPORTED;
-    const size_t nsm = (size_t)(p->nseg - 1);
-    p->ws_state_bytes = align256(size_t(bh) * nsm * size_t(d->Dk) * size_t(d->Dv) * 4u);
-    p->ws_decay_bytes = align256(size_t(bh) * nsm * size_t(d->Dk) * 4u);
+    p->ws_state_bytes = align256(size_t(bh) * size_t(nss) * size_t(d->Dk) * size_t(d->Dv) * 4u);
+    p->ws_decay_bytes = align256(size_t(bh) * size_t(nss) * size_t(d->Dk) * 4u);
     if (p->nseg <= 1) p->ws_state_bytes = p->ws_decay_bytes = 0;
     p->ws_ke_bytes = align256(size_t(g3) * (size_t)gla::ke_scratch_bytes(opb, d->Dk, ch, p->knt));
     p->ws_bytes = p->ws_state_bytes + p->ws_decay_bytes + p->ws_ke_bytes;
@@ -206,6 +221,7 @@ int gla_fwd_ex(const gla_desc *d, void *stream) {
     a.gate = d->gate_kind;
     a.seg_len = p.seg_len;
     a.nseg = p.nseg;
+    a.nsub = p.nsub;
     a.ndv = p.ndv;
     a.nwg = p.grid_out;
 

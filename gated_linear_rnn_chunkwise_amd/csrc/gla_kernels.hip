@@ -553,7 +553,7 @@ __global__ __launch_bounds__(256, 1) void chunk_output_kernel(KArgs a) {
             const int d = 16 * n + 4 * g + e;
             float x = 0.f;
             if (seg > 0)
-                x = a.ws_state[(((size_t)bh * (a.nseg - 1) + (seg - 1)) * C::DK + d) * Dv + col];
+                x = a.ws_state[(((size_t)bh * (a.nseg - 1) * a.nsub + seg * a.nsub - 1) * C::DK + d) * Dv + col];
             else if (a.s0)
                 x = a.s0[((size_t)bh * C::DK + d) * Dv + col];
             S[n][e] = x;
@@ -1339,7 +1339,7 @@ __global__ __launch_bounds__(512, 1) void chunk_output_ws_kernel(KArgs a) {
             const int d = 16 * n + 4 * g + e;
             float x = 0.f;
             if (seg > 0)
-                x = a.ws_state[(((size_t)bh * (a.nseg - 1) + (seg - 1)) * C::DK + d) * Dv + col];
+                x = a.ws_state[(((size_t)bh * (a.nseg - 1) * a.nsub + seg * a.nsub - 1) * C::DK + d) * Dv + col];
             else if (a.s0)
                 x = a.s0[((size_t)bh * C::DK + d) * Dv + col];
             S[n][e] = x;
@@ -1747,7 +1747,7 @@ __global__ __launch_bounds__(512, 1) void chunk_output_sg_kernel(KArgs a) {
             const int d = 16 * n + 4 * g + e;
             float x = 0.f;
             if (seg > 0)
-                x = a.ws_state[(((size_t)bh * (a.nseg - 1) + (seg - 1)) * DK + d) * Dv + col];
+                x = a.ws_state[(((size_t)bh * (a.nseg - 1) * a.nsub + seg * a.nsub - 1) * DK + d) * Dv + col];
             else if (a.s0)
                 x = a.s0[((size_t)bh * DK + d) * Dv + col];
             S[n][e] = x;
@@ -1886,27 +1886,29 @@ __global__ __launch_bounds__(512, 1) void chunk_output_sg_kernel(KArgs a) {
 }
 
 // ------------------------------------------------------------------------------------
-// segment_state_kernel: grid = BH * (nseg - 1) * ndv.  The state segment `seg` produces
-// from zero, sum_s diag(decay from s to the segment end) i_s k_s^T v_s, accumulated tile by
-// tile (dS <- diag(tile decay) dS + K~^T V), and the decay across the segment.
+// segment_state_kernel: grid = BH * (nseg - 1) * nsub * ndv.  The state sub-segment j (of
+// seg_len / nsub tokens) produces from zero, sum_s diag(decay from s to the sub-segment end)
+// i_s k_s^T v_s, accumulated tile by tile (dS <- diag(tile decay) dS + K~^T V), and the decay
+// across the sub-segment.
 template <class C>
 __global__ __launch_bounds__(256, 1) void segment_state_kernel(KArgs a) {
     using OpT = typename C::OpT;
     using Frag = typename C::Frag;
     using Half = typename C::Half;
     extern __shared__ __align__(256) unsigned char smem[];
-    const LdsPlan lp = lds_plan(C::OPB, C::DK, C::CH, 1);
+    const LdsPlanState lp = lds_plan_state(C::OPB, C::DK);
     OpT *sKT = reinterpret_cast<OpT *>(smem + lp.kst);
     OpT *sV = reinterpret_cast<OpT *>(smem + lp.vb);
     float *sAb = reinterpret_cast<float *>(smem + lp.ablk);
     float *sAt = reinterpret_cast<float *>(smem + lp.atile);
     float *sAs = reinterpret_cast<float *>(smem + lp.aseg);
 
-    const int nsm = a.nseg - 1;
+    const int nsm = (a.nseg - 1) * a.nsub;
+    const int sub_len = a.seg_len / a.nsub;
     int id = xcd_remap((int)blockIdx.x, a.nwg);
     const int dvt = id % a.ndv;
     id /= a.ndv;
-    const int seg = id % nsm;
+    const int seg = id % nsm;  // sub-segment
     const int bh = id / nsm;
     const int h = bh % a.H;
     const int tid = (int)threadIdx.x, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
@@ -1914,8 +1916,8 @@ __global__ __launch_bounds__(256, 1) void segment_state_kernel(KArgs a) {
     const int L = a.L, Dv = a.Dv;
     const int dv0 = dvt * kDvTile;
     const int col = dv0 + 16 * w + c16;
-    const int t_begin = seg * a.seg_len;
-    const int t_end = min(L, t_begin + a.seg_len);
+    const int t_begin = seg * sub_len;
+    const int t_end = min(L, t_begin + sub_len);
     const int chl = C::CPL * lane;
     const Rs rs = make_rs<C>(a, bh, h);
 
@@ -2043,15 +2045,16 @@ __global__ __launch_bounds__(256, 1) void segment_state_kernel(KArgs a) {
 }
 
 // ------------------------------------------------------------------------------------
-// segment_scan_kernel: grid (ceil(Dk*Dv/1024), BH).  S_in[0] = initial state (or 0);
-// S_in[j+1] = diag(decay_j) S_in[j] + local_j, written over local_j.
+// segment_scan_kernel: grid (ceil(Dk*Dv/1024), BH).  Carries the state over the
+// sub-segments, S <- diag(decay_j) S + local_j from the initial state (or 0), and writes the
+// state entering segment s (after sub-segment s*nsub - 1) over that sub-segment's entry.
 __global__ __launch_bounds__(256) void segment_scan_kernel(KArgs a, int dk) {
     const int bh = (int)blockIdx.y;
     const size_t n = (size_t)dk * a.Dv;
     const size_t idx = ((size_t)blockIdx.x * kThreads + threadIdx.x) * 4;
     if (idx >= n) return;
     const int d = (int)(idx / a.Dv);
-    const int nsm = a.nseg - 1;
+    const int nsm = (a.nseg - 1) * a.nsub;
     float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
     if (a.s0) s = *reinterpret_cast<const float4 *>(a.s0 + (size_t)bh * n + idx);
     for (int j = 0; j < nsm; ++j) {
@@ -2062,7 +2065,7 @@ __global__ __launch_bounds__(256) void segment_scan_kernel(KArgs a, int dk) {
         s.y = s.y * dec + x.y;
         s.z = s.z * dec + x.z;
         s.w = s.w * dec + x.w;
-        *p = s;
+        if ((j + 1) % a.nsub == 0) *p = s;
     }
 }
 
@@ -2072,12 +2075,12 @@ template <class C>
 static hipError_t launch_cfg(const KArgs &a, hipStream_t st) {
     hipError_t err;
     if (a.nseg > 1) {
-        const LdsPlan l1 = lds_plan(C::OPB, C::DK, C::CH, 1);
+        const LdsPlanState l1 = lds_plan_state(C::OPB, C::DK);
         err = hipFuncSetAttribute(reinterpret_cast<const void *>(&segment_state_kernel<C>),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)l1.total);
         if (err != hipSuccess) return err;
         KArgs a1 = a;
-        a1.nwg = (a.B * a.H) * (a.nseg - 1) * a.ndv;
+        a1.nwg = (a.B * a.H) * (a.nseg - 1) * a.nsub * a.ndv;
         hipLaunchKernelGGL(segment_state_kernel<C>, dim3(a1.nwg), dim3(kThreads), l1.total, st, a1);
         if ((err = hipGetLastError()) != hipSuccess) return err;
         const int nx = (C::DK * a.Dv + 1023) / 1024;

@@ -86,6 +86,32 @@ GLA_HD inline LdsPlan lds_plan(int opb, int dk, bool per_channel, int nt) {
     return p;
 }
 
+// LDS of the segment-state kernel: keys^T scaled to the tile end and the value tile of one
+// slab, the per-channel block and tile decays, and the running decay across the segment.
+struct LdsPlanState {
+    uint32_t kst, vb, ablk, atile, aseg, total;
+};
+
+GLA_HD inline LdsPlanState lds_plan_state(int opb, int dk) {
+    const int slab = 64 * chan_per_lane(opb, dk);
+    const int ktp = 64 + 16 / opb;
+    auto al = [](uint32_t x) { return (x + 255u) & ~255u; };
+    LdsPlanState p{};
+    uint32_t off = 0;
+    p.kst = off;
+    off += al((uint32_t)slab * (uint32_t)ktp * (uint32_t)opb);
+    p.vb = off;
+    off += al(4096u * (uint32_t)opb);
+    p.ablk = off;
+    off += al(4u * (uint32_t)slab * 4u);
+    p.atile = off;
+    off += al((uint32_t)dk * 4u);
+    p.aseg = off;
+    off += al((uint32_t)dk * 4u);
+    p.total = off;
+    return p;
+}
+
 // LDS of the warp-specialised chunk-output kernel (64-token chunks, one slab): four
 // producer waves prepare chunk k+1 while four consumer waves run the matrix products of
 // chunk k.  Arrays read by the consumers only before the mid-iteration barrier are single
@@ -200,14 +226,16 @@ struct KArgs {
     const void *q, *k, *v;
     const float *la, *li, *s0;
     float *out, *fin;
-    float *ws_state;  // [BH][nseg-1][Dk][Dv]: local segment states, then (in place) their prefix states
-    float *ws_decay;  // [BH][nseg-1][Dk]: decay across each segment
+    float *ws_state;  // [BH][(nseg-1)*nsub][Dk][Dv]: local sub-segment states; the scan writes the
+                      // state entering segment s over entry s*nsub-1
+    float *ws_decay;  // [BH][(nseg-1)*nsub][Dk]: decay across each sub-segment
     void *ws_ke;      // [nwg][nt-1][64][Dk] operand scratch (per-channel gate, several tiles per chunk)
     int B, H, L, Dv;
     int chunk, nt;    // chunk size as the kernels run it and its 64-token tiles
     int gate;         // enum gla_gate
     int seg_len;      // tokens per segment (a multiple of the chunk size)
     int nseg, ndv;    // segments; 64-column value tiles
+    int nsub;         // sub-segments per segment in the segment-state kernel
     int nwg;          // workgroups of the launch (for the XCD-aware remap)
 };
 
