@@ -319,6 +319,26 @@ __device__ __forceinline__ void load_unit(Raw<C> &r, const Rs &rs, int T0, int s
     }
 }
 
+// Slot of token s (0..63 in the tile) in the k-slot order of the value and key^T operands.
+__device__ __forceinline__ int kslot(int s) { return (((s >> 5) * 4 + ((s >> 2) & 3)) * 8) + ((s >> 4) & 1) * 4 + (s & 3); }
+
+// LDS bank spreading.  Rows of key^T keep their 8-slot groups XOR-swizzled by (row >> 4) & 7
+// (the producers write four tokens of 16 channels whose rows are 2 or 4 apart); columns of
+// the value tile are XOR-swizzled by (column >> 3) & 3 (the producers write columns 4 apart).
+// Readers apply the same maps and still read 16 contiguous bytes per lane.
+template <class C>
+__device__ __forceinline__ int kt_off(int r, int s) {
+    return r * C::KTP + ((((s >> 3) ^ (r >> 4)) & 7) << 3) + (s & 7);
+}
+__device__ __forceinline__ int vsw(int c) { return c ^ ((c >> 3) & 3); }
+// Position of channel c inside its 32-channel group in q, k and qi rows of the
+// warp-specialised kernels: the 8 channels one lane feeds to the q . S product (which follow
+// the state accumulators' rows 4g + e of two 16-row blocks) become 16 contiguous bytes.
+// Scores see q and k under the same permutation, which leaves their dot products unchanged.
+__device__ __forceinline__ int chperm(int c) {
+    return (c & ~31) + 8 * ((c & 15) >> 2) + 4 * ((c >> 4) & 1) + (c & 3);
+}
+
 // Value tile into LDS in MFMA operand order: [p][g][c][8], element (hh*4+e) of slot
 // (p, g, c) is row 32p + 16hh + 4g + e, column c.  Thread tid holds rows 4*(tid>>4)+e.
 template <class C>
@@ -333,12 +353,11 @@ __device__ __forceinline__ void v_to_lds(const Raw<C> &r, typename C::OpT *sV, i
         H h4;
 #pragma unroll
         for (int e = 0; e < 4; ++e) h4[e] = (OpT)r.vf(e, j);
-        *reinterpret_cast<H *>(sV + ((p * 4 + g) * 64 + c0 + j) * 8 + hh * 4) = h4;
+        *reinterpret_cast<H *>(sV + ((p * 4 + g) * 64 + vsw(c0 + j)) * 8 + hh * 4) = h4;
     }
 }
 
-// Slot of token s (0..63 in the tile) in the k-slot order of the value and key^T operands.
-__device__ __forceinline__ int kslot(int s) { return (((s >> 5) * 4 + ((s >> 2) & 3)) * 8) + ((s >> 4) & 1) * 4 + (s & 3); }
+
 
 // CPL operands of one row into LDS.
 template <class C>
@@ -664,7 +683,7 @@ __global__ __launch_bounds__(256, 1) void chunk_output_kernel(KArgs a) {
                         }
 #pragma unroll
                         for (int c = 0; c < C::CPL; ++c)
-                            *reinterpret_cast<Half *>(sKT + (chl + c) * C::KTP + kslot(16 * w + 4 * g4)) = kt4[c];
+                            *reinterpret_cast<Half *>(sKT + kt_off<C>(chl + c, kslot(16 * w + 4 * g4))) = kt4[c];
                     }
                 } else {
                     // scalar gates: running log2 decay over the tile's rows (lane = row)
@@ -700,7 +719,7 @@ __global__ __launch_bounds__(256, 1) void chunk_output_kernel(KArgs a) {
                         }
 #pragma unroll
                         for (int c = 0; c < C::CPL; ++c)
-                            *reinterpret_cast<Half *>(sKT + (chl + c) * C::KTP + kslot(16 * w + 4 * g4)) = kt4[c];
+                            *reinterpret_cast<Half *>(sKT + kt_off<C>(chl + c, kslot(16 * w + 4 * g4))) = kt4[c];
                     }
                 }
                 if constexpr (C::CH && C::MT)
@@ -725,7 +744,7 @@ __global__ __launch_bounds__(256, 1) void chunk_output_kernel(KArgs a) {
 
                 if (sl == 0) {
 #pragma unroll
-                    for (int p = 0; p < 2; ++p) vfr[p] = ld8<C>(sV + ((p * 4 + g) * 64 + 16 * w + c16) * 8);
+                    for (int p = 0; p < 2; ++p) vfr[p] = ld8<C>(sV + ((p * 4 + g) * 64 + vsw(16 * w + c16)) * 8);
                 }
 
                 // ---------------- diagonal-tile score blocks (transposed): P^T(j,i) over this slab
@@ -797,7 +816,7 @@ __global__ __launch_bounds__(256, 1) void chunk_output_kernel(KArgs a) {
                     for (int p = 0; p < 2; ++p) {
                         Frag ka[C::NBS];
 #pragma unroll
-                        for (int n = 0; n < C::NBS; ++n) ka[n] = ld8<C>(sKT + (16 * n + c16) * C::KTP + (p * 4 + g) * 8);
+                        for (int n = 0; n < C::NBS; ++n) ka[n] = ld8<C>(sKT + kt_off<C>(16 * n + c16, (p * 4 + g) * 8));
 #pragma unroll
                         for (int n = 0; n < C::NBS; ++n) acc[n] = mma(ka[n], vfr[p], acc[n]);
                     }
@@ -931,7 +950,7 @@ __global__ __launch_bounds__(256, 1) void chunk_output_kernel(KArgs a) {
                     {
                         Frag vo[2], pa[8];
 #pragma unroll
-                        for (int p = 0; p < 2; ++p) vo[p] = ld8<C>(sVo + ((p * 4 + g) * 64 + 16 * w + c16) * 8);
+                        for (int p = 0; p < 2; ++p) vo[p] = ld8<C>(sVo + ((p * 4 + g) * 64 + vsw(16 * w + c16)) * 8);
 #pragma unroll
                         for (int q = 0; q < 8; ++q) pa[q] = ld8<C>(sP + (q * 64 + lane) * 8);
 #pragma unroll
@@ -1184,8 +1203,9 @@ __device__ __forceinline__ void ws_produce_a(ProdVals<C> &pv, const Raw<C> &raw,
             post[c] = p1;
             hc[c] = !(ag >= C::kMinDiagDecay);
             any_h |= hc[c];
-            sAb[g * C::SLAB + ch0 + c] = ag;
-            sAi[g * C::SLAB + ch0 + c] = hc[c] ? 0.f : frcp(ag);
+            // block decays scale q and k fragments: stored in the rows' chperm channel order
+            sAb[g * C::SLAB + chperm(ch0 + c)] = ag;
+            sAi[g * C::SLAB + chperm(ch0 + c)] = hc[c] ? 0.f : frcp(ag);
             if (g == 0) sAt[ch0 + c] = all;
         }
 #pragma unroll
@@ -1208,7 +1228,7 @@ __device__ __forceinline__ void ws_produce_a(ProdVals<C> &pv, const Raw<C> &raw,
             }
 #pragma unroll
             for (int c = 0; c < C::CPL; ++c)
-                *reinterpret_cast<Half *>(sKT + (ch0 + c) * C::KTP + kslot(16 * g + 4 * g4)) = kt4[c];
+                *reinterpret_cast<Half *>(sKT + kt_off<C>(ch0 + c, kslot(16 * g + 4 * g4))) = kt4[c];
         }
         // exact diagonal-block partial scores over this wave's channels that are too strongly decayed
         const uint64_t hb = __ballot(any_h);
@@ -1250,7 +1270,7 @@ __device__ __forceinline__ void ws_produce_a(ProdVals<C> &pv, const Raw<C> &raw,
             }
 #pragma unroll
             for (int c = 0; c < C::CPL; ++c)
-                *reinterpret_cast<Half *>(sKT + (ch0 + c) * C::KTP + kslot(16 * g + 4 * g4)) = kt4[c];
+                *reinterpret_cast<Half *>(sKT + kt_off<C>(ch0 + c, kslot(16 * g + 4 * g4))) = kt4[c];
         }
     }
 }
@@ -1261,16 +1281,16 @@ __device__ __forceinline__ void ws_produce_b(const ProdVals<C> &pv, const LdsPla
                                              int pw, int lane) {
     using OpT = typename C::OpT;
     const int g = lane >> 4, c16 = lane & 15;
-    const int ch0 = C::CPL * (16 * pw + c16);
+    const int pc = chperm(C::CPL * (16 * pw + c16));  // rows hold channels in chperm order
     OpT *sQ = reinterpret_cast<OpT *>(smem + lp.q);
     OpT *sK = reinterpret_cast<OpT *>(smem + lp.k);
     OpT *sQI = reinterpret_cast<OpT *>(smem + lp.qi);
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) {
         const int row = 16 * g + rr;
-        st_packed<C>(sQ + row * C::RP + ch0, pv.qd[rr]);
-        st_packed<C>(sK + row * C::RP + ch0, pv.ko[rr]);
-        st_packed<C>(sQI + row * C::RP + ch0, pv.qi[rr]);
+        st_packed<C>(sQ + row * C::RP + pc, pv.qd[rr]);
+        st_packed<C>(sK + row * C::RP + pc, pv.ko[rr]);
+        st_packed<C>(sQI + row * C::RP + pc, pv.qi[rr]);
     }
 }
 
@@ -1454,10 +1474,7 @@ __global__ __launch_bounds__(512, 1) void chunk_output_ws_kernel(KArgs a) {
             for (int m = 0; m < C::KSTEP; ++m) {
                 Frag qa[4];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const OpT *row = sQI + (16 * i + c16) * C::RP + 32 * m + 4 * g;
-                    qa[i] = ld4x2<C>(row, row + 16);
-                }
+                for (int i = 0; i < 4; ++i) qa[i] = ld8<C>(sQI + (16 * i + c16) * C::RP + 32 * m + 8 * g);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) O[i] = mma(qa[i], sb[m], O[i]);
             }
@@ -1467,7 +1484,7 @@ __global__ __launch_bounds__(512, 1) void chunk_output_ws_kernel(KArgs a) {
         // ---------------- phase B: scores x values, state update, output
         Frag vfr[2];
 #pragma unroll
-        for (int p = 0; p < 2; ++p) vfr[p] = ld8<C>(sV + ((p * 4 + g) * 64 + 16 * cw + c16) * 8);
+        for (int p = 0; p < 2; ++p) vfr[p] = ld8<C>(sV + ((p * 4 + g) * 64 + vsw(16 * cw + c16)) * 8);
         {
             Frag pa[6];
             pa[0] = ld8<C>(sP + ((0 * 2 + 0) * 64 + lane) * 8);
@@ -1498,7 +1515,7 @@ __global__ __launch_bounds__(512, 1) void chunk_output_ws_kernel(KArgs a) {
             for (int p = 0; p < 2; ++p) {
                 Frag ka[C::NBD];
 #pragma unroll
-                for (int n = 0; n < C::NBD; ++n) ka[n] = ld8<C>(sKT + (16 * n + c16) * C::KTP + (p * 4 + g) * 8);
+                for (int n = 0; n < C::NBD; ++n) ka[n] = ld8<C>(sKT + kt_off<C>(16 * n + c16, (p * 4 + g) * 8));
 #pragma unroll
                 for (int n = 0; n < C::NBD; ++n) acc[n] = mma(ka[n], vfr[p], acc[n]);
             }
@@ -1545,18 +1562,8 @@ __global__ __launch_bounds__(512, 1) void chunk_output_ws_kernel(KArgs a) {
 //   B2
 // With a scalar gate the queries need no scaling to the tile start: the inter-chunk
 // product takes raw q and its output rows are scaled by 2^(b_t) in fp32.
-//
-// LDS layouts.  q and k rows hold their channels permuted inside each 32-channel group
-// (sg_perm) so that the 8 channels one lane feeds to the q . S product, which follow the
-// state accumulators' row order, are 16 contiguous bytes; the score products see q and k
-// under the same permutation, which leaves their dot products unchanged.  Rows of k^T
-// keep their 16-byte groups XOR-swizzled by (row >> 4) & 7, which spreads the producers'
-// transposed writes over the LDS banks while the consumers' reads stay conflict-free.
-
-// Position of channel c inside its 32-channel group.
-__device__ __forceinline__ int sg_perm(int c) { return 8 * ((c & 15) >> 2) + 4 * ((c >> 4) & 1) + (c & 3); }
-// Offset (in fp16 elements) of token slot s of row r of k^T.
-__device__ __forceinline__ int sg_kt(int r, int s) { return r * 72 + ((((s >> 3) ^ (r >> 4)) & 7) << 3) + (s & 7); }
+// q and k rows hold their channels in the chperm order, k^T and the value tile use the
+// kt_off and vsw swizzles.
 
 template <class C>
 struct RawSg {
@@ -1615,7 +1622,7 @@ __device__ __forceinline__ void sg_produce_a(ProdSg<C> &pv, const RawSg<C> &raw,
             f16x4 h4;
 #pragma unroll
             for (int e = 0; e < 4; ++e) h4[e] = (f16)((j & 1) ? bf_hi(raw.v[e][j >> 1]) : bf_lo(raw.v[e][j >> 1]));
-            *reinterpret_cast<f16x4 *>(sV + ((p * 4 + gq) * 64 + c0 + j) * 8 + hh * 4) = h4;
+            *reinterpret_cast<f16x4 *>(sV + ((p * 4 + gq) * 64 + vsw(c0 + j)) * 8 + hh * 4) = h4;
         }
     }
     // running log2 decay over the tile's rows (lane = row) and the key weights
@@ -1655,7 +1662,7 @@ __device__ __forceinline__ void sg_produce_b(const ProdSg<C> &pv, const LdsPlanS
                                              int lane) {
     const int g = lane >> 4, c16 = lane & 15;
     const int ch0 = 4 * (16 * pw + c16);
-    const int pc = (ch0 & ~31) + sg_perm(ch0 & 31);
+    const int pc = chperm(ch0);
     f16 *sQ = reinterpret_cast<f16 *>(smem + lp.q);
     f16 *sK = reinterpret_cast<f16 *>(smem + lp.k);
     f16 *sKT = reinterpret_cast<f16 *>(smem + lp.kst);
@@ -1669,7 +1676,7 @@ __device__ __forceinline__ void sg_produce_b(const ProdSg<C> &pv, const LdsPlanS
     for (int c = 0; c < 4; ++c)
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4)
-            *reinterpret_cast<f16x4 *>(sKT + sg_kt(ch0 + c, kslot(16 * g + 4 * g4))) = pv.kt[c][g4];
+            *reinterpret_cast<f16x4 *>(sKT + kt_off<C>(ch0 + c, kslot(16 * g + 4 * g4))) = pv.kt[c][g4];
 }
 
 template <class C>
@@ -1835,7 +1842,7 @@ __global__ __launch_bounds__(512, 1) void chunk_output_sg_kernel(KArgs a) {
         // state update S <- 2^T S + K~^T V
         f16x8 vfr[2];
 #pragma unroll
-        for (int p = 0; p < 2; ++p) vfr[p] = lds_ld<f16x8>(sV + ((p * 4 + g) * 64 + 16 * cw + c16) * 8);
+        for (int p = 0; p < 2; ++p) vfr[p] = lds_ld<f16x8>(sV + ((p * 4 + g) * 64 + vsw(16 * cw + c16)) * 8);
         {
             const float at = fexp2(sB[63]);
 #pragma unroll
@@ -1845,7 +1852,7 @@ __global__ __launch_bounds__(512, 1) void chunk_output_sg_kernel(KArgs a) {
 #pragma unroll
                 for (int n = 0; n < NBD; ++n) {
                     const int r = 16 * n + c16;
-                    S[n] = mma(lds_ld<f16x8>(sKT + sg_kt(r, (p * 4 + g) * 8)), vfr[p], S[n]);
+                    S[n] = mma(lds_ld<f16x8>(sKT + kt_off<C>(r, (p * 4 + g) * 8)), vfr[p], S[n]);
                 }
             }
         }
@@ -1891,7 +1898,7 @@ __global__ __launch_bounds__(512, 1) void chunk_output_sg_kernel(KArgs a) {
 // i_s k_s^T v_s, accumulated tile by tile (dS <- diag(tile decay) dS + K~^T V), and the decay
 // across the sub-segment.
 template <class C>
-__global__ __launch_bounds__(256, 1) void segment_state_kernel(KArgs a) {
+__global__ __launch_bounds__(256, 3) void segment_state_kernel(KArgs a) {
     using OpT = typename C::OpT;
     using Frag = typename C::Frag;
     using Half = typename C::Half;
@@ -1969,7 +1976,7 @@ __global__ __launch_bounds__(256, 1) void segment_state_kernel(KArgs a) {
                     }
 #pragma unroll
                     for (int c = 0; c < C::CPL; ++c)
-                        *reinterpret_cast<Half *>(sKT + (chl + c) * C::KTP + kslot(16 * w + 4 * g4)) = kt4[c];
+                        *reinterpret_cast<Half *>(sKT + kt_off<C>(chl + c, kslot(16 * w + 4 * g4))) = kt4[c];
                 }
             } else {
                 const float x = raw.las * kLog2e;
@@ -1988,7 +1995,7 @@ __global__ __launch_bounds__(256, 1) void segment_state_kernel(KArgs a) {
                     }
 #pragma unroll
                     for (int c = 0; c < C::CPL; ++c)
-                        *reinterpret_cast<Half *>(sKT + (chl + c) * C::KTP + kslot(16 * w + 4 * g4)) = kt4[c];
+                        *reinterpret_cast<Half *>(sKT + kt_off<C>(chl + c, kslot(16 * w + 4 * g4))) = kt4[c];
                 }
             }
             lds_barrier();
@@ -2003,7 +2010,7 @@ __global__ __launch_bounds__(256, 1) void segment_state_kernel(KArgs a) {
             }
             if (sl == 0) {
 #pragma unroll
-                for (int p = 0; p < 2; ++p) vfr[p] = ld8<C>(sV + ((p * 4 + g) * 64 + 16 * w + c16) * 8);
+                for (int p = 0; p < 2; ++p) vfr[p] = ld8<C>(sV + ((p * 4 + g) * 64 + vsw(16 * w + c16)) * 8);
             }
             f32x4 acc[C::NBS];
 #pragma unroll
@@ -2022,7 +2029,7 @@ __global__ __launch_bounds__(256, 1) void segment_state_kernel(KArgs a) {
             for (int p = 0; p < 2; ++p) {
                 Frag ka[C::NBS];
 #pragma unroll
-                for (int n = 0; n < C::NBS; ++n) ka[n] = ld8<C>(sKT + (16 * n + c16) * C::KTP + (p * 4 + g) * 8);
+                for (int n = 0; n < C::NBS; ++n) ka[n] = ld8<C>(sKT + kt_off<C>(16 * n + c16, (p * 4 + g) * 8));
 #pragma unroll
                 for (int n = 0; n < C::NBS; ++n) acc[n] = mma(ka[n], vfr[p], acc[n]);
             }
