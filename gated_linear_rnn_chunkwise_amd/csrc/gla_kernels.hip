@@ -1294,7 +1294,7 @@ __device__ __forceinline__ void ws_produce_b(const ProdVals<C> &pv, const LdsPla
     }
 }
 
-template <class C>
+template <class C, bool LI>
 __global__ __launch_bounds__(512, 1) void chunk_output_ws_kernel(KArgs a) {
     static_assert(!C::MT && C::NSLAB == 1, "single-tile, single-slab configuration");
     using OpT = typename C::OpT;
@@ -1329,12 +1329,12 @@ __global__ __launch_bounds__(512, 1) void chunk_output_ws_kernel(KArgs a) {
         // range check.  Conditional loads would make the compiler merge register copies
         // that wait for the whole prefetch as soon as it is issued.
         load_unit_p<C>(raw, rs, t_begin, pw, lane, dv0, Dv);
-        ws_produce_a<C>(pv, raw, lp, smem, 0, pw, lane, rs.has_li);
+        ws_produce_a<C>(pv, raw, lp, smem, 0, pw, lane, LI);
         load_unit_p<C>(raw, rs, t_begin + kTile, pw, lane, dv0, Dv);
         ws_produce_b<C>(pv, lp, smem, pw, lane);
         lds_barrier();
         for (int kc = 0; kc < nch; ++kc) {
-            ws_produce_a<C>(pv, raw, lp, smem, (kc + 1) & 1, pw, lane, rs.has_li);
+            ws_produce_a<C>(pv, raw, lp, smem, (kc + 1) & 1, pw, lane, LI);
             load_unit_p<C>(raw, rs, t_begin + kTile * (kc + 2), pw, lane, dv0, Dv);
             lds_barrier();  // B1
             ws_produce_b<C>(pv, lp, smem, pw, lane);
@@ -2105,10 +2105,15 @@ static hipError_t launch_cfg(const KArgs &a, hipStream_t st) {
         return hipGetLastError();
     } else if constexpr (!C::MT && C::NSLAB == 1) {
         const LdsPlanWs lw = lds_plan_ws(C::OPB, C::DK);
-        err = hipFuncSetAttribute(reinterpret_cast<const void *>(&chunk_output_ws_kernel<C>),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)lw.total);
+        // the input gate is a compile-time choice: without it the producers carry no gate factor
+        const void *fn = a.li ? reinterpret_cast<const void *>(&chunk_output_ws_kernel<C, true>)
+                              : reinterpret_cast<const void *>(&chunk_output_ws_kernel<C, false>);
+        err = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lw.total);
         if (err != hipSuccess) return err;
-        hipLaunchKernelGGL(chunk_output_ws_kernel<C>, dim3(a3.nwg), dim3(2 * kThreads), lw.total, st, a3);
+        if (a.li)
+            hipLaunchKernelGGL((chunk_output_ws_kernel<C, true>), dim3(a3.nwg), dim3(2 * kThreads), lw.total, st, a3);
+        else
+            hipLaunchKernelGGL((chunk_output_ws_kernel<C, false>), dim3(a3.nwg), dim3(2 * kThreads), lw.total, st, a3);
         return hipGetLastError();
     } else {
         const LdsPlan l3 = lds_plan(C::OPB, C::DK, C::CH, a.nt);
