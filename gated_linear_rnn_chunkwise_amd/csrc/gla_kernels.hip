@@ -1092,7 +1092,7 @@ __device__ __forceinline__ void st_packed(typename C::OpT *row, uint32_t v) {
 
 template <class C>
 struct ProdVals {
-    uint32_t qd[16], ko[16], qi[16];  // packed operands of rows 16g+rr for phase B
+    uint32_t qd[16], ko[16];  // packed operands of rows 16g+rr for phase B
 };
 
 // Exact diagonal-block partial scores of the producer wave's channels in 16-token blocks
@@ -1136,7 +1136,7 @@ __device__ __attribute__((noinline)) void ws_exact_blocks(Raw<C> raw, float *sXa
     }
 }
 
-// Producer phase A: gates of one chunk, key^T and values into buffer nb, q/k/qi values kept
+// Producer phase A: gates of one chunk, key^T and values into buffer nb, q/k values kept
 // for phase B.  Returns nothing; writes LDS only.
 template <class C>
 __device__ __forceinline__ void ws_produce_a(ProdVals<C> &pv, const Raw<C> &raw, const LdsPlanWs &lp,
@@ -1185,21 +1185,19 @@ __device__ __forceinline__ void ws_produce_a(ProdVals<C> &pv, const Raw<C> &raw,
                 run *= al;
             }
         }
-        float pre[C::CPL], post[C::CPL];
+        float post[C::CPL];
         bool hc[C::CPL];
         bool any_h = false;
 #pragma unroll
         for (int c = 0; c < C::CPL; ++c) {
             const float ag = eq[15][c];
-            float p0 = 1.f, p1 = 1.f, all = 1.f;
+            float p1 = 1.f, all = 1.f;
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const float au = __shfl(ag, 16 * u + c16);
                 all *= au;
-                if (u < g) p0 *= au;
                 if (u > g) p1 *= au;
             }
-            pre[c] = p0;
             post[c] = p1;
             hc[c] = !(ag >= C::kMinDiagDecay);
             any_h |= hc[c];
@@ -1214,17 +1212,15 @@ __device__ __forceinline__ void ws_produce_a(ProdVals<C> &pv, const Raw<C> &raw,
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int rr = 4 * g4 + e;
-                float qd[C::CPL], ko[C::CPL], qi[C::CPL];
+                float qd[C::CPL], ko[C::CPL];
 #pragma unroll
                 for (int c = 0; c < C::CPL; ++c) {
                     qd[c] = raw.qf(rr, c) * eq[rr][c];
                     ko[c] = raw.kf(rr, c) * ig[rr] * ek[rr][c];
-                    qi[c] = qd[c] * pre[c];
                     kt4[c][e] = (OpT)(ko[c] * post[c]);
                 }
                 pv.qd[rr] = pack_ops<C>(qd);
                 pv.ko[rr] = pack_ops<C>(ko);
-                pv.qi[rr] = pack_ops<C>(qi);
             }
 #pragma unroll
             for (int c = 0; c < C::CPL; ++c)
@@ -1254,19 +1250,16 @@ __device__ __forceinline__ void ws_produce_a(ProdVals<C> &pv, const Raw<C> &raw,
             for (int e = 0; e < 4; ++e) {
                 const int rr = 4 * g4 + e;
                 const float blr = __shfl(bl, 16 * g + rr);
-                const float eb = fexp2(blr);
                 const float ekr = fexp2(Tt - blr + __shfl(y, 16 * g + rr));
-                float qv[C::CPL], kv[C::CPL], qi[C::CPL];
+                float qv[C::CPL], kv[C::CPL];
 #pragma unroll
                 for (int c = 0; c < C::CPL; ++c) {
                     qv[c] = raw.qf(rr, c);
                     kv[c] = raw.kf(rr, c);
-                    qi[c] = qv[c] * eb;
                     kt4[c][e] = (OpT)(kv[c] * ekr);
                 }
                 pv.qd[rr] = pack_ops<C>(qv);
                 pv.ko[rr] = pack_ops<C>(kv);
-                pv.qi[rr] = pack_ops<C>(qi);
             }
 #pragma unroll
             for (int c = 0; c < C::CPL; ++c)
@@ -1275,7 +1268,7 @@ __device__ __forceinline__ void ws_produce_a(ProdVals<C> &pv, const Raw<C> &raw,
     }
 }
 
-// Producer phase B: q, k, qi of the prepared chunk into the single buffers.
+// Producer phase B: q and k of the prepared chunk into the single buffers.
 template <class C>
 __device__ __forceinline__ void ws_produce_b(const ProdVals<C> &pv, const LdsPlanWs &lp, unsigned char *smem,
                                              int pw, int lane) {
@@ -1284,13 +1277,11 @@ __device__ __forceinline__ void ws_produce_b(const ProdVals<C> &pv, const LdsPla
     const int pc = chperm(C::CPL * (16 * pw + c16));  // rows hold channels in chperm order
     OpT *sQ = reinterpret_cast<OpT *>(smem + lp.q);
     OpT *sK = reinterpret_cast<OpT *>(smem + lp.k);
-    OpT *sQI = reinterpret_cast<OpT *>(smem + lp.qi);
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) {
         const int row = 16 * g + rr;
         st_packed<C>(sQ + row * C::RP + pc, pv.qd[rr]);
         st_packed<C>(sK + row * C::RP + pc, pv.ko[rr]);
-        st_packed<C>(sQI + row * C::RP + pc, pv.qi[rr]);
     }
 }
 
@@ -1348,7 +1339,6 @@ __global__ __launch_bounds__(512, 1) void chunk_output_ws_kernel(KArgs a) {
     const int col = dv0 + 16 * cw + c16;
     const OpT *sQ = reinterpret_cast<const OpT *>(smem + lp.q);
     const OpT *sK = reinterpret_cast<const OpT *>(smem + lp.k);
-    const OpT *sQI = reinterpret_cast<const OpT *>(smem + lp.qi);
     OpT *sP = reinterpret_cast<OpT *>(smem + lp.pbuf);
 
     f32x4 S[C::NBD];
@@ -1456,30 +1446,64 @@ __global__ __launch_bounds__(512, 1) void chunk_output_ws_kernel(KArgs a) {
             const Half z{(OpT)0.f, (OpT)0.f, (OpT)0.f, (OpT)0.f};
             *reinterpret_cast<Half *>(sP + ((cw * 2 + (cw >> 1)) * 64 + lane) * 8 + 4) = z;
         }
-        // inter-chunk term: O = QI . S
+        // inter-chunk term.  Per-channel gate: the queries of block i are referenced to the
+        // block start, so block i multiplies diag(decay across blocks 0..i-1) S, formed here on
+        // the state fragment (the permuted q row holds, at 32m + 8g, channels 32m + 4g + e and
+        // 32m + 16 + 4g + e: the state rows of this lane, and the block decays are stored in
+        // the same order).  Scalar gate: raw q times S, each output row scaled by 2^(b_t).
         f32x4 O[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) O[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-        {
-            Frag sb[C::KSTEP];
 #pragma unroll
-            for (int m = 0; m < C::KSTEP; ++m) {
+        for (int m = 0; m < C::KSTEP; ++m) {
+            float sv[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                sv[e] = S[2 * m][e];
+                sv[e + 4] = S[2 * m + 1][e];
+            }
+            Frag sb;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) sb[e] = (OpT)sv[e];
+            O[0] = mma(ld8<C>(sQ + c16 * C::RP + 32 * m + 8 * g), sb, O[0]);
+            if constexpr (C::CH) {
+                float pre[8];
+                const f32x4 a0 = lds_ld<f32x4>(sAb + 32 * m + 8 * g), a1 = lds_ld<f32x4>(sAb + 32 * m + 8 * g + 4);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    sb[m][e] = (OpT)S[2 * m][e];
-                    sb[m][e + 4] = (OpT)S[2 * m + 1][e];
+                    pre[e] = a0[e];
+                    pre[e + 4] = a1[e];
                 }
-            }
 #pragma unroll
-            for (int m = 0; m < C::KSTEP; ++m) {
-                Frag qa[4];
+                for (int i = 1; i < 4; ++i) {
+                    Frag si;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) qa[i] = ld8<C>(sQI + (16 * i + c16) * C::RP + 32 * m + 8 * g);
+                    for (int e = 0; e < 8; ++e) si[e] = (OpT)(sv[e] * pre[e]);
+                    O[i] = mma(ld8<C>(sQ + (16 * i + c16) * C::RP + 32 * m + 8 * g), si, O[i]);
+                    if (i < 3) {
+                        const float *ab = sAb + i * C::SLAB + 32 * m + 8 * g;
+                        const f32x4 b0 = lds_ld<f32x4>(ab), b1 = lds_ld<f32x4>(ab + 4);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) O[i] = mma(qa[i], sb[m], O[i]);
+                        for (int e = 0; e < 4; ++e) {
+                            pre[e] *= b0[e];
+                            pre[e + 4] *= b1[e];
+                        }
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int i = 1; i < 4; ++i) O[i] = mma(ld8<C>(sQ + (16 * i + c16) * C::RP + 32 * m + 8 * g), sb, O[i]);
             }
         }
-        lds_barrier();  // B1: scores stored; producers may rewrite q, k, qi
+        if constexpr (!C::CH) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const f32x4 bq = lds_ld<f32x4>(sAb + 16 * i + 4 * g);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) O[i][e] *= fexp2(bq[e]);
+            }
+        }
+        lds_barrier();  // B1: scores stored; producers may rewrite q, k
 
         // ---------------- phase B: scores x values, state update, output
         Frag vfr[2];

@@ -115,16 +115,16 @@ GLA_HD inline LdsPlanState lds_plan_state(int opb, int dk) {
 // LDS of the warp-specialised chunk-output kernel (64-token chunks, one slab): four
 // producer waves prepare chunk k+1 while four consumer waves run the matrix products of
 // chunk k.  Arrays read by the consumers only before the mid-iteration barrier are single
-// (q, k, qi); arrays read after it are double-buffered by chunk parity.
+// (q, k); arrays read after it are double-buffered by chunk parity.
 struct LdsPlanWs {
-    uint32_t q, k, qi;  // [64][rp] single buffers
+    uint32_t q, k;  // [64][rp] single buffers, channels in the chperm order
     // double-buffered block: buffer b starts at dbl + b * dstride; offsets inside a buffer:
     uint32_t dbl, dstride;
     uint32_t kst;   // [slab][ktp]
     uint32_t vb;    // [4096] value tile
-    uint32_t ab;    // [4][slab] fp32 decay across each 16-token block (per-channel); [64] log2 running
+    uint32_t ab;    // [4][slab] fp32 decay across each 16-token block, channels in chperm order (per-channel); [64] log2 running
                     //           decay of each row (scalar gates)
-    uint32_t ainv;  // [4][slab] fp32 1/decay of each block, 0 for channels handled exactly (per-channel);
+    uint32_t ainv;  // [4][slab] fp32 1/decay of each block, 0 for channels handled exactly, chperm order (per-channel);
                     //           [64] log2 input gate of each row (scalar gates)
     uint32_t at;    // [slab] fp32 decay across the tile (per-channel)
     uint32_t xact;  // [4 producer waves][4 blocks][136] fp32 exact diagonal-block partial scores
@@ -145,8 +145,6 @@ GLA_HD inline LdsPlanWs lds_plan_ws(int opb, int dk) {
     p.q = off;
     off += al(a64);
     p.k = off;
-    off += al(a64);
-    p.qi = off;
     off += al(a64);
     uint32_t in = 0;
     p.kst = in;
