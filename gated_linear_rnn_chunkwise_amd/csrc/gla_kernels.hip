@@ -38,6 +38,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
 #include <type_traits>
 
 #include "gla.h"
@@ -2088,27 +2089,55 @@ __global__ __launch_bounds__(256) void segment_scan_kernel(KArgs a, int dk) {
     const int nsm = (a.nseg - 1) * a.nsub;
     float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
     if (a.s0) s = *reinterpret_cast<const float4 *>(a.s0 + (size_t)bh * n + idx);
-    for (int j = 0; j < nsm; ++j) {
-        float4 *p = reinterpret_cast<float4 *>(a.ws_state + ((size_t)bh * nsm + j) * n + idx);
-        const float dec = a.ws_decay[((size_t)bh * nsm + j) * dk + d];
-        const float4 x = *p;
-        s.x = s.x * dec + x.x;
-        s.y = s.y * dec + x.y;
-        s.z = s.z * dec + x.z;
-        s.w = s.w * dec + x.w;
-        if ((j + 1) % a.nsub == 0) *p = s;
+    float *ws = a.ws_state + (size_t)bh * nsm * n + idx;
+    const float *wd = a.ws_decay + (size_t)bh * nsm * dk + d;
+    // batches of 8 sub-segments: all loads of a batch are issued before its stores
+    for (int j0 = 0; j0 < nsm; j0 += 8) {
+        float4 x[8];
+        float dec[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int j = min(j0 + u, nsm - 1);
+            x[u] = *reinterpret_cast<const float4 *>(ws + (size_t)j * n);
+            dec[u] = wd[(size_t)j * dk];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int j = j0 + u;
+            if (j < nsm) {
+                s.x = s.x * dec[u] + x[u].x;
+                s.y = s.y * dec[u] + x[u].y;
+                s.z = s.z * dec[u] + x[u].z;
+                s.w = s.w * dec[u] + x[u].w;
+                if ((j + 1) % a.nsub == 0) *reinterpret_cast<float4 *>(ws + (size_t)j * n) = s;
+            }
+        }
     }
 }
 
 // ------------------------------------------------------------------------------------
 // Launchers.
+
+// Raise a kernel's dynamic-LDS limit to the whole 160 KB once per device (the attribute
+// belongs to the function on the current device); `done` holds one bit per device ordinal.
+static hipError_t ensure_lds_limit(const void *fn, std::atomic<uint64_t> &done) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const uint64_t bit = (dev >= 0 && dev < 64) ? (uint64_t(1) << dev) : 0;
+    if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+    e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLds);
+    if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_acq_rel);
+    return e;
+}
+
 template <class C>
 static hipError_t launch_cfg(const KArgs &a, hipStream_t st) {
     hipError_t err;
     if (a.nseg > 1) {
         const LdsPlanState l1 = lds_plan_state(C::OPB, C::DK);
-        err = hipFuncSetAttribute(reinterpret_cast<const void *>(&segment_state_kernel<C>),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)l1.total);
+        static std::atomic<uint64_t> done_state{0};
+        err = ensure_lds_limit(reinterpret_cast<const void *>(&segment_state_kernel<C>), done_state);
         if (err != hipSuccess) return err;
         KArgs a1 = a;
         a1.nwg = (a.B * a.H) * (a.nseg - 1) * a.nsub * a.ndv;
@@ -2122,17 +2151,18 @@ static hipError_t launch_cfg(const KArgs &a, hipStream_t st) {
     a3.nwg = (a.B * a.H) * a.nseg * a.ndv;
     if constexpr (!C::F32 && !C::CH && !C::MT && C::DK == 256) {
         const LdsPlanSg lg = lds_plan_sg(C::DK);
-        err = hipFuncSetAttribute(reinterpret_cast<const void *>(&chunk_output_sg_kernel<C>),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)lg.total);
+        static std::atomic<uint64_t> done_sg{0};
+        err = ensure_lds_limit(reinterpret_cast<const void *>(&chunk_output_sg_kernel<C>), done_sg);
         if (err != hipSuccess) return err;
         hipLaunchKernelGGL(chunk_output_sg_kernel<C>, dim3(a3.nwg), dim3(2 * kThreads), lg.total, st, a3);
         return hipGetLastError();
     } else if constexpr (!C::MT && C::NSLAB == 1) {
         const LdsPlanWs lw = lds_plan_ws(C::OPB, C::DK);
         // the input gate is a compile-time choice: without it the producers carry no gate factor
+        static std::atomic<uint64_t> done_ws[2] = {{0}, {0}};
         const void *fn = a.li ? reinterpret_cast<const void *>(&chunk_output_ws_kernel<C, true>)
                               : reinterpret_cast<const void *>(&chunk_output_ws_kernel<C, false>);
-        err = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lw.total);
+        err = ensure_lds_limit(fn, done_ws[a.li ? 1 : 0]);
         if (err != hipSuccess) return err;
         if (a.li)
             hipLaunchKernelGGL((chunk_output_ws_kernel<C, true>), dim3(a3.nwg), dim3(2 * kThreads), lw.total, st, a3);
@@ -2141,8 +2171,8 @@ static hipError_t launch_cfg(const KArgs &a, hipStream_t st) {
         return hipGetLastError();
     } else {
         const LdsPlan l3 = lds_plan(C::OPB, C::DK, C::CH, a.nt);
-        err = hipFuncSetAttribute(reinterpret_cast<const void *>(&chunk_output_kernel<C>),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)l3.total);
+        static std::atomic<uint64_t> done_out{0};
+        err = ensure_lds_limit(reinterpret_cast<const void *>(&chunk_output_kernel<C>), done_out);
         if (err != hipSuccess) return err;
         hipLaunchKernelGGL(chunk_output_kernel<C>, dim3(a3.nwg), dim3(kThreads), l3.total, st, a3);
         return hipGetLastError();

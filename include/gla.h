@@ -41,8 +41,9 @@
  * call; on a validation error it returns a negative status, launches nothing and writes
  * nothing.  Otherwise it enqueues its kernels on `stream` (a hipStream_t; NULL is the
  * default stream) and returns without synchronising; outputs are valid once the stream
- * has completed the work.  GLA_ERR_HIP reports launch-time errors only.  The library has
- * no mutable global state; calls are re-entrant.  Two calls that share an output, a final
+ * has completed the work.  GLA_ERR_HIP reports launch-time errors only.  The only mutable
+ * global state is a per-device record (atomic bit masks) of which kernels have had their
+ * shared-memory limit raised; calls are re-entrant.  Two calls that share an output, a final
  * state or a caller workspace must not run concurrently.
  */
 #ifndef GLA_H
