@@ -1009,21 +1009,23 @@ __global__ __launch_bounds__(256, 1) void chunk_output_kernel(KArgs a) {
 // products of chunk k; every SIMD holds one producer and one consumer wave, so the
 // vector-ALU gate work and the matrix-core work of neighbouring chunks overlap.  Two
 // barriers per chunk:
-//   phase A  consumers: score blocks of chunk k (q, k single buffers), inter-chunk term (qi)
-//            producers: gates of chunk k+1; key^T, values and decays into buffer (k+1)&1
+//   phase A  consumers: score blocks and inter-chunk term of chunk k (q, k single buffers)
+//            producers: gates of chunk k+1 (block decays, exact partial scores, values and,
+//            for scalar gates, keys^T into buffer (k+1)&1); loads of chunk k+2
 //   B1
 //   phase B  consumers: scores x values, state update (buffer k&1), output store
-//            producers: q, k, qi of chunk k+1 into the single buffers
+//            producers: q, k of chunk k+1 into the single buffers; per-channel gate: keys^T
+//            scaled to the chunk end and the chunk decay into buffer (k+1)&1 (they need the
+//            decays of all four blocks, published before B1)
 //   B2
-// Producer lane mapping: lane = (row block g = lane>>4, channel group c16 = lane&15); wave pw
-// covers channels CPL*(16*pw + c16) .. +CPL-1 for all 64 rows, so the four block decays of a
-// channel meet inside one wave (no barrier for the exchange).
+// Producer lane mapping: producer wave pw owns the 16-row block pw; lane l owns channels
+// CPL*l .. +CPL-1, so every load instruction covers whole rows of q, k and the gates, and a
+// lane walks its block's 16 rows for the running decay products.
 
 template <class C>
 __device__ __forceinline__ void load_unit_p(Raw<C> &r, const Rs &rs, int T0, int pw, int lane, int dv0, int Dv) {
-    const int g = lane >> 4, c16 = lane & 15;
-    const int ch0 = C::CPL * (16 * pw + c16);
-    const uint32_t row0 = (uint32_t)(T0 + 16 * g);
+    const int ch0 = C::CPL * lane;
+    const uint32_t row0 = (uint32_t)(T0 + 16 * pw);
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) {
         const uint32_t off = ((row0 + rr) * C::DK + ch0) * C::IB;
@@ -1045,15 +1047,10 @@ __device__ __forceinline__ void load_unit_p(Raw<C> &r, const Rs &rs, int T0, int
             }
         }
     }
+    // scalar gates: one branch-free load for every kind (per token: stride 4; fixed per head:
+    // stride 0, masked past the sequence end where it is used; none: empty resource)
     const uint32_t t = (uint32_t)(T0 + lane);
-    if constexpr (!C::CH) {
-        if (rs.gate == GLA_GATE_HEAD)
-            r.las = __uint_as_float(bld32(rs.la, t * 4u));
-        else if (rs.gate == GLA_GATE_HEAD_CONST)
-            r.las = (int)t < rs.L ? __uint_as_float(bld32(rs.la, 0)) : 0.f;
-        else
-            r.las = 0.f;
-    }
+    if constexpr (!C::CH) r.las = __uint_as_float(bld32(rs.la, t * rs.gstride));
     r.lis = __uint_as_float(bld32(rs.li, t * 4u));
     const int tp = 64 * pw + lane;
     const uint32_t c0 = dv0 + 4 * (tp & 15);
@@ -1093,18 +1090,19 @@ __device__ __forceinline__ void st_packed(typename C::OpT *row, uint32_t v) {
 
 template <class C>
 struct ProdVals {
-    uint32_t qd[16], ko[16];  // packed operands of rows 16g+rr for phase B
+    uint32_t qd[16];                     // packed q operands of rows 16pw+rr for phase B
+    uint32_t ko[16];                     // packed k operands (block-end reference)
+    float kf[C::CH ? 16 : 1][C::CPL];    // per-channel gate: k at the block end, fp32, for keys^T
+    float ag[C::CPL];                    // per-channel gate: decay across this block
 };
 
-// Exact diagonal-block partial scores of the producer wave's channels in 16-token blocks
-// whose decay is too strong for scaled fp16 operands (rare; kept out of line so the common
-// path keeps its registers).  For every pair s <= t of block gg: the sum over this wave's
-// strongly decayed channels of q_td k_sd 2^(u_td - u_sd) i_s, u the log2 running decay.
+// Exact diagonal-block partial scores of block pw when some of its channels decay too
+// strongly across the block for scaled fp16 operands (rare; kept out of line so the common
+// path keeps its registers).  For every pair s <= t of the block: the sum over the
+// strongly decayed channels of q_td k_sd 2^(u_td - u_sd) i_s, u the log2 running decay,
+// reduced over the wave's lanes (all channels) into dst[t (t + 1) / 2 + s].
 template <class C>
-__device__ __attribute__((noinline)) void ws_exact_blocks(Raw<C> raw, float *sXa, uint64_t hb, int pw, int lane,
-                                                          bool has_li) {
-    const int g = lane >> 4, c16 = lane & 15;
-    if (((hb >> (16 * g)) & 0xffffull) == 0ull) return;
+__device__ __attribute__((noinline)) void ws_exact_block(Raw<C> raw, float *dst, int pw, int lane, bool has_li) {
     float u[16][C::CPL], hcm[C::CPL];
 #pragma unroll
     for (int c = 0; c < C::CPL; ++c) {
@@ -1120,8 +1118,7 @@ __device__ __attribute__((noinline)) void ws_exact_blocks(Raw<C> raw, float *sXa
     const float y = raw.lis * kLog2e;
     float ig[16];
 #pragma unroll
-    for (int rr = 0; rr < 16; ++rr) ig[rr] = has_li ? fexp2(__shfl(y, 16 * g + rr)) : 1.f;
-    float *dst = sXa + (pw * 4 + g) * 136;
+    for (int rr = 0; rr < 16; ++rr) ig[rr] = has_li ? fexp2(__shfl(y, 16 * pw + rr)) : 1.f;
     for (int t = 0; t < 16; ++t) {
         for (int s2 = 0; s2 <= t; ++s2) {
             float part = 0.f;
@@ -1129,28 +1126,26 @@ __device__ __attribute__((noinline)) void ws_exact_blocks(Raw<C> raw, float *sXa
             for (int c = 0; c < C::CPL; ++c)
                 part += hcm[c] * raw.qf(t, c) * raw.kf(s2, c) * fexp2(u[t][c] - u[s2][c]);
             part *= ig[s2];
-#pragma unroll
-            for (int m = 1; m < 16; m <<= 1) part += __shfl_xor(part, m);
-            const int idx = t * (t + 1) / 2 + s2;
-            if (c16 == (idx & 15)) dst[idx] = part;
+            part = wave_sum(part);
+            if (lane == 0) dst[t * (t + 1) / 2 + s2] = part;
         }
     }
 }
 
-// Producer phase A: gates of one chunk, key^T and values into buffer nb, q/k values kept
-// for phase B.  Returns nothing; writes LDS only.
+// Producer phase A: gates of one chunk (block pw), values, block decays and exact partial
+// scores into buffer nb; scalar gates also write keys^T.  q/k operands stay in registers.
 template <class C>
 __device__ __forceinline__ void ws_produce_a(ProdVals<C> &pv, const Raw<C> &raw, const LdsPlanWs &lp,
-                                             unsigned char *smem, int nb, int pw, int lane, bool has_li) {
+                                             unsigned char *smem, int nb, int pw, int lane, bool has_li,
+                                             bool row_valid) {
     using OpT = typename C::OpT;
     using Half = typename C::Half;
-    const int g = lane >> 4, c16 = lane & 15;
-    const int ch0 = C::CPL * (16 * pw + c16);
-    OpT *sKT = reinterpret_cast<OpT *>(smem + (lp.dbl + (nb) * lp.dstride + lp.kst));
-    float *sAb = reinterpret_cast<float *>(smem + (lp.dbl + (nb) * lp.dstride + lp.ab));
-    float *sAi = reinterpret_cast<float *>(smem + (lp.dbl + (nb) * lp.dstride + lp.ainv));
-    float *sAt = reinterpret_cast<float *>(smem + (lp.dbl + (nb) * lp.dstride + lp.at));
-    v_to_lds<C>(raw, reinterpret_cast<OpT *>(smem + (lp.dbl + (nb) * lp.dstride + lp.vb)), 64 * pw + lane);
+    const int ch0 = C::CPL * lane;
+    unsigned char *buf = smem + lp.dbl + (uint32_t)nb * lp.dstride;
+    OpT *sKT = reinterpret_cast<OpT *>(buf + lp.kst);
+    float *sAb = reinterpret_cast<float *>(buf + lp.ab);
+    float *sAi = reinterpret_cast<float *>(buf + lp.ainv);
+    v_to_lds<C>(raw, reinterpret_cast<OpT *>(buf + lp.vb), 64 * pw + lane);
 
     float ig[16];
     {
@@ -1158,7 +1153,7 @@ __device__ __forceinline__ void ws_produce_a(ProdVals<C> &pv, const Raw<C> &raw,
         if constexpr (C::CH) {
             if (has_li) {
 #pragma unroll
-                for (int rr = 0; rr < 16; ++rr) ig[rr] = fexp2(__shfl(y, 16 * g + rr));
+                for (int rr = 0; rr < 16; ++rr) ig[rr] = fexp2(__shfl(y, 16 * pw + rr));
             } else {
 #pragma unroll
                 for (int rr = 0; rr < 16; ++rr) ig[rr] = 1.f;
@@ -1186,57 +1181,40 @@ __device__ __forceinline__ void ws_produce_a(ProdVals<C> &pv, const Raw<C> &raw,
                 run *= al;
             }
         }
-        float post[C::CPL];
-        bool hc[C::CPL];
         bool any_h = false;
 #pragma unroll
         for (int c = 0; c < C::CPL; ++c) {
             const float ag = eq[15][c];
-            float p1 = 1.f, all = 1.f;
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const float au = __shfl(ag, 16 * u + c16);
-                all *= au;
-                if (u > g) p1 *= au;
-            }
-            post[c] = p1;
-            hc[c] = !(ag >= C::kMinDiagDecay);
-            any_h |= hc[c];
+            pv.ag[c] = ag;
+            const bool hc = !(ag >= C::kMinDiagDecay);
+            any_h |= hc;
             // block decays scale q and k fragments: stored in the rows' chperm channel order
-            sAb[g * C::SLAB + chperm(ch0 + c)] = ag;
-            sAi[g * C::SLAB + chperm(ch0 + c)] = hc[c] ? 0.f : frcp(ag);
-            if (g == 0) sAt[ch0 + c] = all;
+            sAb[pw * C::SLAB + chperm(ch0 + c)] = ag;
+            sAi[pw * C::SLAB + chperm(ch0 + c)] = hc ? 0.f : frcp(ag);
         }
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-            Half kt4[C::CPL];
+        for (int rr = 0; rr < 16; ++rr) {
+            float qd[C::CPL], ko[C::CPL];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int rr = 4 * g4 + e;
-                float qd[C::CPL], ko[C::CPL];
-#pragma unroll
-                for (int c = 0; c < C::CPL; ++c) {
-                    qd[c] = raw.qf(rr, c) * eq[rr][c];
-                    ko[c] = raw.kf(rr, c) * ig[rr] * ek[rr][c];
-                    kt4[c][e] = (OpT)(ko[c] * post[c]);
-                }
-                pv.qd[rr] = pack_ops<C>(qd);
-                pv.ko[rr] = pack_ops<C>(ko);
+            for (int c = 0; c < C::CPL; ++c) {
+                qd[c] = raw.qf(rr, c) * eq[rr][c];
+                ko[c] = raw.kf(rr, c) * ig[rr] * ek[rr][c];
+                pv.kf[rr][c] = ko[c];
             }
-#pragma unroll
-            for (int c = 0; c < C::CPL; ++c)
-                *reinterpret_cast<Half *>(sKT + kt_off<C>(ch0 + c, kslot(16 * g + 4 * g4))) = kt4[c];
+            pv.qd[rr] = pack_ops<C>(qd);
+            pv.ko[rr] = pack_ops<C>(ko);
         }
-        // exact diagonal-block partial scores over this wave's channels that are too strongly decayed
-        const uint64_t hb = __ballot(any_h);
-        int *sXf = reinterpret_cast<int *>(smem + (lp.dbl + (nb) * lp.dstride + lp.xflag));
-        if (hb != 0ull) ws_exact_blocks<C>(raw, reinterpret_cast<float *>(smem + (lp.dbl + (nb) * lp.dstride + lp.xact)), hb, pw, lane, has_li);
-        if (lane < 4) sXf[pw * 4 + lane] = ((hb >> (16 * lane)) & 0xffffull) != 0ull ? 1 : 0;
+        // channels of this block whose decay is too strong: exact partial scores (rare)
+        const bool harsh = __ballot(any_h) != 0ull;
+        if (harsh)
+            ws_exact_block<C>(raw, reinterpret_cast<float *>(buf + lp.xact) + pw * 136, pw, lane, has_li);
+        if (lane == 0) reinterpret_cast<int *>(buf + lp.xflag)[pw] = harsh ? 1 : 0;
     } else {
-        // scalar gates: running log2 decay over the tile's rows (lane = row)
+        // scalar gates: running log2 decay over the tile's rows (lane = row); rows past the
+        // sequence end carry no decay (a fixed per-head gate is loaded for them too)
         float *sBr = sAb;  // [64] log2 running decay, row 63 = decay across the tile
         float *sLr = sAi;  // [64] log2 input gate
-        const float x = raw.las * kLog2e;
+        const float x = row_valid ? raw.las * kLog2e : 0.f;
         const float y = raw.lis * kLog2e;
         const float bl = scan_incl(x, lane);
         const float Tt = __shfl(bl, 63);
@@ -1244,14 +1222,14 @@ __device__ __forceinline__ void ws_produce_a(ProdVals<C> &pv, const Raw<C> &raw,
             sBr[lane] = bl;
             sLr[lane] = y;
         }
+        const float wk = fexp2(Tt - bl + y);  // weight of key row `lane` in the state update
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
             Half kt4[C::CPL];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int rr = 4 * g4 + e;
-                const float blr = __shfl(bl, 16 * g + rr);
-                const float ekr = fexp2(Tt - blr + __shfl(y, 16 * g + rr));
+                const float ekr = __shfl(wk, 16 * pw + rr);
                 float qv[C::CPL], kv[C::CPL];
 #pragma unroll
                 for (int c = 0; c < C::CPL; ++c) {
@@ -1264,25 +1242,62 @@ __device__ __forceinline__ void ws_produce_a(ProdVals<C> &pv, const Raw<C> &raw,
             }
 #pragma unroll
             for (int c = 0; c < C::CPL; ++c)
-                *reinterpret_cast<Half *>(sKT + kt_off<C>(ch0 + c, kslot(16 * g + 4 * g4))) = kt4[c];
+                *reinterpret_cast<Half *>(sKT + kt_off<C>(ch0 + c, kslot(16 * pw + 4 * g4))) = kt4[c];
         }
     }
 }
 
-// Producer phase B: q and k of the prepared chunk into the single buffers.
+// Producer phase B: q and k of the prepared chunk into the single buffers; per-channel gate:
+// keys^T scaled to the chunk end (decay of the blocks after this one, from the block decays
+// all producer waves published before B1) and the chunk decay into buffer nb.
 template <class C>
 __device__ __forceinline__ void ws_produce_b(const ProdVals<C> &pv, const LdsPlanWs &lp, unsigned char *smem,
-                                             int pw, int lane) {
+                                             int nb, int pw, int lane) {
     using OpT = typename C::OpT;
-    const int g = lane >> 4, c16 = lane & 15;
-    const int pc = chperm(C::CPL * (16 * pw + c16));  // rows hold channels in chperm order
+    using Half = typename C::Half;
+    const int ch0 = C::CPL * lane;
+    const int pc = chperm(ch0);  // rows hold channels in chperm order
     OpT *sQ = reinterpret_cast<OpT *>(smem + lp.q);
     OpT *sK = reinterpret_cast<OpT *>(smem + lp.k);
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) {
-        const int row = 16 * g + rr;
+        const int row = 16 * pw + rr;
         st_packed<C>(sQ + row * C::RP + pc, pv.qd[rr]);
         st_packed<C>(sK + row * C::RP + pc, pv.ko[rr]);
+    }
+    if constexpr (C::CH) {
+        unsigned char *buf = smem + lp.dbl + (uint32_t)nb * lp.dstride;
+        const float *sAb = reinterpret_cast<const float *>(buf + lp.ab);
+        OpT *sKT = reinterpret_cast<OpT *>(buf + lp.kst);
+        float post[C::CPL], all[C::CPL];
+#pragma unroll
+        for (int c = 0; c < C::CPL; ++c) {
+            float p1 = 1.f, a = 1.f;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const float au = u == pw ? pv.ag[c] : sAb[u * C::SLAB + chperm(ch0 + c)];
+                a *= au;
+                if (u > pw) p1 *= au;
+            }
+            post[c] = p1;
+            all[c] = a;
+        }
+        if (pw == 0) {
+            float *sAt = reinterpret_cast<float *>(buf + lp.at);
+#pragma unroll
+            for (int c = 0; c < C::CPL; ++c) sAt[ch0 + c] = all[c];
+        }
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+            Half kt4[C::CPL];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+#pragma unroll
+                for (int c = 0; c < C::CPL; ++c) kt4[c][e] = (OpT)(pv.kf[4 * g4 + e][c] * post[c]);
+#pragma unroll
+            for (int c = 0; c < C::CPL; ++c)
+                *reinterpret_cast<Half *>(sKT + kt_off<C>(ch0 + c, kslot(16 * pw + 4 * g4))) = kt4[c];
+        }
     }
 }
 
@@ -1321,15 +1336,16 @@ __global__ __launch_bounds__(512, 1) void chunk_output_ws_kernel(KArgs a) {
         // range check.  Conditional loads would make the compiler merge register copies
         // that wait for the whole prefetch as soon as it is issued.
         load_unit_p<C>(raw, rs, t_begin, pw, lane, dv0, Dv);
-        ws_produce_a<C>(pv, raw, lp, smem, 0, pw, lane, LI);
+        ws_produce_a<C>(pv, raw, lp, smem, 0, pw, lane, LI, t_begin + lane < L);
         load_unit_p<C>(raw, rs, t_begin + kTile, pw, lane, dv0, Dv);
-        ws_produce_b<C>(pv, lp, smem, pw, lane);
+        lds_barrier();  // block decays of chunk 0 published
+        ws_produce_b<C>(pv, lp, smem, 0, pw, lane);
         lds_barrier();
         for (int kc = 0; kc < nch; ++kc) {
-            ws_produce_a<C>(pv, raw, lp, smem, (kc + 1) & 1, pw, lane, LI);
+            ws_produce_a<C>(pv, raw, lp, smem, (kc + 1) & 1, pw, lane, LI, t_begin + kTile * (kc + 1) + lane < L);
             load_unit_p<C>(raw, rs, t_begin + kTile * (kc + 2), pw, lane, dv0, Dv);
             lds_barrier();  // B1
-            ws_produce_b<C>(pv, lp, smem, pw, lane);
+            ws_produce_b<C>(pv, lp, smem, (kc + 1) & 1, pw, lane);
             lds_barrier();  // B2
         }
         return;
@@ -1356,6 +1372,7 @@ __global__ __launch_bounds__(512, 1) void chunk_output_ws_kernel(KArgs a) {
             S[n][e] = x;
         }
     }
+    lds_barrier();  // producers: block decays of chunk 0 published
     lds_barrier();  // chunk 0 prepared
 
     // this wave's score blocks: (query block i, key block j); pair 0 is the diagonal (cw, cw)
@@ -1413,15 +1430,12 @@ __global__ __launch_bounds__(512, 1) void chunk_output_ws_kernel(KArgs a) {
             // channels of strongly decayed blocks: exact partial scores from the producers
             const float *sXa = reinterpret_cast<const float *>(smem + (lp.dbl + (b) * lp.dstride + lp.xact));
             const int *sXf = reinterpret_cast<const int *>(smem + (lp.dbl + (b) * lp.dstride + lp.xflag));
-#pragma unroll 1
-            for (int pw = 0; pw < 4; ++pw) {
-                if (sXf[pw * 4 + cw]) {
-                    const float *src = sXa + (pw * 4 + cw) * 136;
+            if (sXf[cw]) {
+                const float *src = sXa + cw * 136;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int s2 = 4 * g + e;
-                        if (s2 <= c16) Pd[0][e] += src[c16 * (c16 + 1) / 2 + s2];
-                    }
+                for (int e = 0; e < 4; ++e) {
+                    const int s2 = 4 * g + e;
+                    if (s2 <= c16) Pd[0][e] += src[c16 * (c16 + 1) / 2 + s2];
                 }
             }
         }

@@ -127,8 +127,8 @@ struct LdsPlanWs {
     uint32_t ainv;  // [4][slab] fp32 1/decay of each block, 0 for channels handled exactly, chperm order (per-channel);
                     //           [64] log2 input gate of each row (scalar gates)
     uint32_t at;    // [slab] fp32 decay across the tile (per-channel)
-    uint32_t xact;  // [4 producer waves][4 blocks][136] fp32 exact diagonal-block partial scores
-    uint32_t xflag; // [4][4] int32: partial present
+    uint32_t xact;  // [4 blocks][136] fp32 exact diagonal-block partial scores
+    uint32_t xflag; // [4] int32: partial present
     uint32_t pbuf;  // [4096] masked score tile
     uint32_t total;
 };
@@ -158,9 +158,9 @@ GLA_HD inline LdsPlanWs lds_plan_ws(int opb, int dk) {
     p.at = in;
     in += al((uint32_t)slab * 4u);
     p.xact = in;
-    in += al(4u * 4u * 136u * 4u);
+    in += al(4u * 136u * 4u);
     p.xflag = in;
-    in += al(16u * 4u);
+    in += al(4u * 4u);
     p.dbl = off;
     p.dstride = in;
     off += 2u * in;
