@@ -1586,9 +1586,9 @@ __global__ __launch_bounds__(512, 1) void chunk_output_ws_kernel(KArgs a) {
 // head) with bf16 inputs, 64-token chunks and Dk = 256.  grid = BH * nseg * ndv
 // workgroups of 512 threads.
 //
-// Producers (waves 4..7): lane (row block g = lane>>4, channel group c16 = lane&15) of
-// wave pw holds channels 4*(16*pw + c16) .. +3 of the 16 rows of block g, so it owns four
-// consecutive tokens of each channel for the transposed key operand.  Consumers (waves
+// Producers (waves 4..7): wave pw owns the 16 rows of block pw and lane l the channels
+// 4l .. 4l+3, so every load covers a whole row and a lane owns consecutive tokens of its
+// channels for the transposed key operand.  Consumers (waves
 // 0..3): 16 value columns each, the Dk x 16 state in registers.  Per tile k:
 //   phase A  consumers: score blocks (q, k), O = diag(2^b) (q . S), state update
 //            S <- 2^T S + (k 2^(T - b + l))^T v    (q, k, k^T: single buffers;
@@ -1606,16 +1606,15 @@ __global__ __launch_bounds__(512, 1) void chunk_output_ws_kernel(KArgs a) {
 
 template <class C>
 struct RawSg {
-    u32x2 q[16], k[16];  // 4 bf16 channels of rows 16g + rr
+    u32x2 q[16], k[16];  // 4 bf16 channels (4 * lane ..) of rows 16 pw + rr
     uint32_t v[4][2];    // 4 values of one row
     float las, lis;      // log gate and log input gate of row (tile start + lane)
 };
 
 template <class C>
 __device__ __forceinline__ void load_unit_sg(RawSg<C> &r, const Rs &rs, int T0, int pw, int lane, int dv0, int Dv) {
-    const int g = lane >> 4, c16 = lane & 15;
-    const int ch0 = 4 * (16 * pw + c16);
-    const uint32_t row0 = (uint32_t)(T0 + 16 * g);
+    const int ch0 = 4 * lane;  // a wave's load covers one whole row
+    const uint32_t row0 = (uint32_t)(T0 + 16 * pw);
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) {
         const uint32_t off = ((row0 + rr) * C::DK + ch0) * 2u;
@@ -1640,7 +1639,7 @@ __device__ __forceinline__ void load_unit_sg(RawSg<C> &r, const Rs &rs, int T0, 
 
 template <class C>
 struct ProdSg {
-    u32x2 qh[16], kh[16];  // fp16 q, k of rows 16g + rr (4 channels)
+    u32x2 qh[16], kh[16];  // fp16 q, k of rows 16 pw + rr (4 channels)
     f16x4 kt[4][4];        // [channel][token group]: scaled keys of 4 consecutive tokens
 };
 
@@ -1648,7 +1647,6 @@ struct ProdSg {
 template <class C>
 __device__ __forceinline__ void sg_produce_a(ProdSg<C> &pv, const RawSg<C> &raw, const LdsPlanSg &lp,
                                              unsigned char *smem, int nb, int pw, int lane, bool row_valid) {
-    const int g = lane >> 4;
     // values in MFMA B-operand order (as v_to_lds)
     {
         f16 *sV = reinterpret_cast<f16 *>(smem + lp.vb) + nb * 4096;
@@ -1677,7 +1675,7 @@ __device__ __forceinline__ void sg_produce_a(ProdSg<C> &pv, const RawSg<C> &raw,
     const float wk = fexp2(T - bl + y);  // weight of key row `lane` in the state update
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) {
-        const float w = __shfl(wk, 16 * g + rr);
+        const float w = __shfl(wk, 16 * pw + rr);
         float qf[4], kf[4];
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
@@ -1699,15 +1697,14 @@ __device__ __forceinline__ void sg_produce_a(ProdSg<C> &pv, const RawSg<C> &raw,
 template <class C>
 __device__ __forceinline__ void sg_produce_b(const ProdSg<C> &pv, const LdsPlanSg &lp, unsigned char *smem, int pw,
                                              int lane) {
-    const int g = lane >> 4, c16 = lane & 15;
-    const int ch0 = 4 * (16 * pw + c16);
+    const int ch0 = 4 * lane;
     const int pc = chperm(ch0);
     f16 *sQ = reinterpret_cast<f16 *>(smem + lp.q);
     f16 *sK = reinterpret_cast<f16 *>(smem + lp.k);
     f16 *sKT = reinterpret_cast<f16 *>(smem + lp.kst);
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) {
-        const int row = 16 * g + rr;
+        const int row = 16 * pw + rr;
         *reinterpret_cast<u32x2 *>(sQ + row * (C::DK + 8) + pc) = pv.qh[rr];
         *reinterpret_cast<u32x2 *>(sK + row * (C::DK + 8) + pc) = pv.kh[rr];
     }
@@ -1715,7 +1712,7 @@ __device__ __forceinline__ void sg_produce_b(const ProdSg<C> &pv, const LdsPlanS
     for (int c = 0; c < 4; ++c)
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4)
-            *reinterpret_cast<f16x4 *>(sKT + kt_off<C>(ch0 + c, kslot(16 * g + 4 * g4))) = pv.kt[c][g4];
+            *reinterpret_cast<f16x4 *>(sKT + kt_off<C>(ch0 + c, kslot(16 * pw + 4 * g4))) = pv.kt[c][g4];
 }
 
 template <class C>
