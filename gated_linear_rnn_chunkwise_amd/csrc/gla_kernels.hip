@@ -184,6 +184,18 @@ __device__ __forceinline__ typename C::Frag scale8(const typename C::Frag &f, co
     }
     return r;
 }
+// 8 fp32 values times per-element factors, rounded once to operands.
+template <class C>
+__device__ __forceinline__ typename C::Frag scale8f(const float *x, const f32x4 &s0, const f32x4 &s1) {
+    using OpT = typename C::OpT;
+    typename C::Frag r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        r[e] = (OpT)(x[e] * s0[e]);
+        r[e + 4] = (OpT)(x[e + 4] * s1[e]);
+    }
+    return r;
+}
 // 8 consecutive operands from global memory through a buffer resource.
 template <class C, int AUX>
 __device__ __forceinline__ typename C::Frag gld8(rsrc_t r, uint32_t off) {
@@ -1395,36 +1407,113 @@ __global__ __launch_bounds__(512, 1) void chunk_output_ws_kernel(KArgs a) {
         const float *sAi = reinterpret_cast<const float *>(smem + (lp.dbl + (b) * lp.dstride + lp.ainv));
         const float *sAt = reinterpret_cast<const float *>(smem + (lp.dbl + (b) * lp.dstride + lp.at));
 
-        // ---------------- phase A: score blocks P^T(j, i) over the key channels
-        f32x4 Pd[3];
+        // ---------------- phase A: score blocks P^T(j, i) over the key channels and the
+        // inter-chunk term, sharing the q fragments.  Per-channel gate: the queries of block i
+        // are referenced to the block start, so block i multiplies diag(decay across blocks
+        // 0..i-1) S, formed on the state fragment (the permuted q row holds, at 32m + 8g,
+        // channels 32m + 4g + e and 32m + 16 + 4g + e: the state rows of this lane, and the
+        // block decays are stored in the same order); key block j of a pair (i, j) with
+        // j + 1 < i meets queries rescaled across the blocks between them, and the diagonal
+        // pair uses keys referenced to the block start (block-end keys times 1/decay).
+        // Scalar gate: raw q times S, each output row scaled by 2^(b_t) afterwards.  Each
+        // wave's score pairs are spelled out per wave (wave-uniform switch).
+        f32x4 Pd[3], O[4];
 #pragma unroll
         for (int kp = 0; kp < 3; ++kp) Pd[kp] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
+        for (int i = 0; i < 4; ++i) O[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
         for (int m = 0; m < C::KSTEP; ++m) {
             const int ch = 32 * m + 8 * g;
-            Frag af[3], bf[3];
+            Frag qf[4];
 #pragma unroll
-            for (int kp = 0; kp < 3; ++kp) {
-                af[kp] = ld8<C>(sK + (16 * pj[kp] + c16) * C::RP + ch);
-                bf[kp] = ld8<C>(sQ + (16 * pi[kp] + c16) * C::RP + ch);
+            for (int i = 0; i < 4; ++i) qf[i] = ld8<C>(sQ + (16 * i + c16) * C::RP + ch);
+            float sv[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                sv[e] = S[2 * m][e];
+                sv[e + 4] = S[2 * m + 1][e];
             }
-            if constexpr (C::CH) {
-                af[0] = scale8<C>(af[0], lds_ld<f32x4>(sAi + cw * C::SLAB + ch), lds_ld<f32x4>(sAi + cw * C::SLAB + ch + 4));
+            Frag sb;
 #pragma unroll
-                for (int kp = 1; kp < 3; ++kp) {
-                    if (pj[kp] + 1 < pi[kp]) {
-                        f32x4 r0 = lds_ld<f32x4>(sAb + (pj[kp] + 1) * C::SLAB + ch);
-                        f32x4 r1 = lds_ld<f32x4>(sAb + (pj[kp] + 1) * C::SLAB + ch + 4);
-                        if (pj[kp] + 2 < pi[kp]) {
-                            r0 *= lds_ld<f32x4>(sAb + (pj[kp] + 2) * C::SLAB + ch);
-                            r1 *= lds_ld<f32x4>(sAb + (pj[kp] + 2) * C::SLAB + ch + 4);
-                        }
-                        bf[kp] = scale8<C>(bf[kp], r0, r1);
+            for (int e = 0; e < 8; ++e) sb[e] = (OpT)sv[e];
+            O[0] = mma(qf[0], sb, O[0]);
+            const auto kf = [&](int j) { return ld8<C>(sK + (16 * j + c16) * C::RP + ch); };
+            if constexpr (C::CH) {
+                const f32x4 a0l = lds_ld<f32x4>(sAb + ch), a0h = lds_ld<f32x4>(sAb + ch + 4);
+                const f32x4 a1l = lds_ld<f32x4>(sAb + C::SLAB + ch), a1h = lds_ld<f32x4>(sAb + C::SLAB + ch + 4);
+                const f32x4 a2l = lds_ld<f32x4>(sAb + 2 * C::SLAB + ch), a2h = lds_ld<f32x4>(sAb + 2 * C::SLAB + ch + 4);
+                {
+                    f32x4 pl = a0l, ph = a0h;
+                    O[1] = mma(qf[1], scale8f<C>(sv, pl, ph), O[1]);
+                    pl *= a1l;
+                    ph *= a1h;
+                    O[2] = mma(qf[2], scale8f<C>(sv, pl, ph), O[2]);
+                    pl *= a2l;
+                    ph *= a2h;
+                    O[3] = mma(qf[3], scale8f<C>(sv, pl, ph), O[3]);
+                }
+                const f32x4 il = lds_ld<f32x4>(sAi + cw * C::SLAB + ch), ih = lds_ld<f32x4>(sAi + cw * C::SLAB + ch + 4);
+                switch (cw) {
+                    case 0: {
+                        const Frag k0 = kf(0), k2 = kf(2);
+                        Pd[0] = mma(scale8<C>(k0, il, ih), qf[0], Pd[0]);
+                        Pd[1] = mma(k0, qf[1], Pd[1]);
+                        Pd[2] = mma(k2, qf[3], Pd[2]);
+                        break;
+                    }
+                    case 1: {
+                        const Frag k1 = kf(1), k0 = kf(0);
+                        Pd[0] = mma(scale8<C>(k1, il, ih), qf[1], Pd[0]);
+                        Pd[1] = mma(k0, scale8<C>(qf[2], a1l, a1h), Pd[1]);
+                        Pd[2] = mma(k1, scale8<C>(qf[3], a2l, a2h), Pd[2]);
+                        break;
+                    }
+                    case 2: {
+                        const Frag k2 = kf(2), k1 = kf(1);
+                        Pd[0] = mma(scale8<C>(k2, il, ih), qf[2], Pd[0]);
+                        Pd[1] = mma(k1, qf[2], Pd[1]);
+                        break;
+                    }
+                    default: {
+                        const Frag k3 = kf(3), k0 = kf(0);
+                        Pd[0] = mma(scale8<C>(k3, il, ih), qf[3], Pd[0]);
+                        Pd[1] = mma(k0, scale8<C>(qf[3], a1l * a2l, a1h * a2h), Pd[1]);
+                        break;
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int i = 1; i < 4; ++i) O[i] = mma(qf[i], sb, O[i]);
+                switch (cw) {
+                    case 0: {
+                        const Frag k0 = kf(0), k2 = kf(2);
+                        Pd[0] = mma(k0, qf[0], Pd[0]);
+                        Pd[1] = mma(k0, qf[1], Pd[1]);
+                        Pd[2] = mma(k2, qf[3], Pd[2]);
+                        break;
+                    }
+                    case 1: {
+                        const Frag k1 = kf(1), k0 = kf(0);
+                        Pd[0] = mma(k1, qf[1], Pd[0]);
+                        Pd[1] = mma(k0, qf[2], Pd[1]);
+                        Pd[2] = mma(k1, qf[3], Pd[2]);
+                        break;
+                    }
+                    case 2: {
+                        const Frag k2 = kf(2), k1 = kf(1);
+                        Pd[0] = mma(k2, qf[2], Pd[0]);
+                        Pd[1] = mma(k1, qf[2], Pd[1]);
+                        break;
+                    }
+                    default: {
+                        const Frag k3 = kf(3), k0 = kf(0);
+                        Pd[0] = mma(k3, qf[3], Pd[0]);
+                        Pd[1] = mma(k0, qf[3], Pd[1]);
+                        break;
                     }
                 }
             }
-#pragma unroll
-            for (int kp = 0; kp < 3; ++kp) Pd[kp] = mma(af[kp], bf[kp], Pd[kp]);
         }
         if constexpr (C::CH) {
             // channels of strongly decayed blocks: exact partial scores from the producers
@@ -1460,55 +1549,6 @@ __global__ __launch_bounds__(512, 1) void chunk_output_ws_kernel(KArgs a) {
         if (cw == 0 || cw == 2) {
             const Half z{(OpT)0.f, (OpT)0.f, (OpT)0.f, (OpT)0.f};
             *reinterpret_cast<Half *>(sP + ((cw * 2 + (cw >> 1)) * 64 + lane) * 8 + 4) = z;
-        }
-        // inter-chunk term.  Per-channel gate: the queries of block i are referenced to the
-        // block start, so block i multiplies diag(decay across blocks 0..i-1) S, formed here on
-        // the state fragment (the permuted q row holds, at 32m + 8g, channels 32m + 4g + e and
-        // 32m + 16 + 4g + e: the state rows of this lane, and the block decays are stored in
-        // the same order).  Scalar gate: raw q times S, each output row scaled by 2^(b_t).
-        f32x4 O[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) O[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int m = 0; m < C::KSTEP; ++m) {
-            float sv[8];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                sv[e] = S[2 * m][e];
-                sv[e + 4] = S[2 * m + 1][e];
-            }
-            Frag sb;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) sb[e] = (OpT)sv[e];
-            O[0] = mma(ld8<C>(sQ + c16 * C::RP + 32 * m + 8 * g), sb, O[0]);
-            if constexpr (C::CH) {
-                float pre[8];
-                const f32x4 a0 = lds_ld<f32x4>(sAb + 32 * m + 8 * g), a1 = lds_ld<f32x4>(sAb + 32 * m + 8 * g + 4);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    pre[e] = a0[e];
-                    pre[e + 4] = a1[e];
-                }
-#pragma unroll
-                for (int i = 1; i < 4; ++i) {
-                    Frag si;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) si[e] = (OpT)(sv[e] * pre[e]);
-                    O[i] = mma(ld8<C>(sQ + (16 * i + c16) * C::RP + 32 * m + 8 * g), si, O[i]);
-                    if (i < 3) {
-                        const float *ab = sAb + i * C::SLAB + 32 * m + 8 * g;
-                        const f32x4 b0 = lds_ld<f32x4>(ab), b1 = lds_ld<f32x4>(ab + 4);
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            pre[e] *= b0[e];
-                            pre[e + 4] *= b1[e];
-                        }
-                    }
-                }
-            } else {
-#pragma unroll
-                for (int i = 1; i < 4; ++i) O[i] = mma(ld8<C>(sQ + (16 * i + c16) * C::RP + 32 * m + 8 * g), sb, O[i]);
-            }
         }
         if constexpr (!C::CH) {
 #pragma unroll
@@ -1816,29 +1856,21 @@ __global__ __launch_bounds__(512, 1) void chunk_output_sg_kernel(KArgs a) {
         const float *sB = reinterpret_cast<const float *>(smem + lp.rows) + b * 128;
         const float *sL = sB + 64;
 
-        // ---------------- phase A: score blocks P^T(j, i)
-        f32x4 Pd[3];
+        // ---------------- phase A: score blocks P^T(j, i) and the inter-chunk term
+        // O = diag(2^b) (q . S), sharing the q fragments: the permuted q row holds, at
+        // 32m + 8g, channels 32m + 4g + e and 32m + 16 + 4g + e, the rows of state blocks 2m
+        // and 2m+1.  Each wave's score pairs are spelled out per wave (wave-uniform switch).
+        f32x4 Pd[3], O[4];
 #pragma unroll
         for (int kp = 0; kp < 3; ++kp) Pd[kp] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int m = 0; m < KSTEP; ++m) {
-            const int ch = 32 * m + 8 * g;
-            f16x8 af[3], bf[3];
-#pragma unroll
-            for (int kp = 0; kp < 3; ++kp) {
-                af[kp] = lds_ld<f16x8>(sK + (16 * pj[kp] + c16) * RP + ch);
-                bf[kp] = lds_ld<f16x8>(sQ + (16 * pi[kp] + c16) * RP + ch);
-            }
-#pragma unroll
-            for (int kp = 0; kp < 3; ++kp) Pd[kp] = mma(af[kp], bf[kp], Pd[kp]);
-        }
-        // inter-chunk term O = diag(2^b) (q . S): the permuted q row holds, at 32m + 8g,
-        // channels 32m + 4g + e and 32m + 16 + 4g + e, the rows of state blocks 2m and 2m+1
-        f32x4 O[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) O[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int m = 0; m < KSTEP; ++m) {
+            const int ch = 32 * m + 8 * g;
+            f16x8 qf[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) qf[i] = lds_ld<f16x8>(sQ + (16 * i + c16) * RP + ch);
             f16x8 sb;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -1846,8 +1878,36 @@ __global__ __launch_bounds__(512, 1) void chunk_output_sg_kernel(KArgs a) {
                 sb[e + 4] = (f16)S[2 * m + 1][e];
             }
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                O[i] = mma(lds_ld<f16x8>(sQ + (16 * i + c16) * RP + 32 * m + 8 * g), sb, O[i]);
+            for (int i = 0; i < 4; ++i) O[i] = mma(qf[i], sb, O[i]);
+            const auto kf = [&](int j) { return lds_ld<f16x8>(sK + (16 * j + c16) * RP + ch); };
+            switch (cw) {
+                case 0: {
+                    const f16x8 k0 = kf(0), k2 = kf(2);
+                    Pd[0] = mma(k0, qf[0], Pd[0]);
+                    Pd[1] = mma(k0, qf[1], Pd[1]);
+                    Pd[2] = mma(k2, qf[3], Pd[2]);
+                    break;
+                }
+                case 1: {
+                    const f16x8 k1 = kf(1), k0 = kf(0);
+                    Pd[0] = mma(k1, qf[1], Pd[0]);
+                    Pd[1] = mma(k0, qf[2], Pd[1]);
+                    Pd[2] = mma(k1, qf[3], Pd[2]);
+                    break;
+                }
+                case 2: {
+                    const f16x8 k2 = kf(2), k1 = kf(1);
+                    Pd[0] = mma(k2, qf[2], Pd[0]);
+                    Pd[1] = mma(k1, qf[2], Pd[1]);
+                    break;
+                }
+                default: {
+                    const f16x8 k3 = kf(3), k0 = kf(0);
+                    Pd[0] = mma(k3, qf[3], Pd[0]);
+                    Pd[1] = mma(k0, qf[3], Pd[1]);
+                    break;
+                }
+            }
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
