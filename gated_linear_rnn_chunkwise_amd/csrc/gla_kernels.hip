@@ -225,6 +225,28 @@ __device__ __forceinline__ typename C::Frag gld8_in(rsrc_t r, uint32_t off) {
     }
 }
 
+// Output tile through LDS: each consumer wave writes its 16 columns of the 64-row tile
+// (accumulator layout: rows 16i + 4g + e, column 16 cw + c16), and after a barrier stores
+// 16 whole rows of 64 columns with 16-byte stores (rows past the sequence end are dropped
+// by the buffer range check).
+__device__ __forceinline__ void stage_out(float *sO, const f32x4 (&O)[4], int cw, int g, int c16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sO[(16 * i + 4 * g + e) * 68 + 16 * cw + c16] = O[i][e];
+}
+__device__ __forceinline__ void store_staged(const float *sO, rsrc_t out, int T0, int Dv, int dv0, int cw,
+                                             int lane) {
+    const int c4 = lane & 15;
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+        const int row = 16 * cw + 4 * rr + (lane >> 4);
+        const f32x4 x = lds_ld<f32x4>(sO + row * 68 + 4 * c4);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), out,
+                                               (int)(((uint32_t)(T0 + row) * Dv + dv0 + 4 * c4) * 4u), 0, 0);
+    }
+}
+
 // ------------------------------------------------------------------------------------
 // Raw input of one unit (64-token tile x one slab of key channels), prefetched into
 // registers.  Thread (wave w, lane) holds rows 16w..16w+15 of the tile for its CPL key
@@ -1601,16 +1623,9 @@ __global__ __launch_bounds__(512, 1) void chunk_output_ws_kernel(KArgs a) {
 #pragma unroll
             for (int n = 0; n < C::NBD; ++n) S[n] = acc[n];
         }
-        {
-            const uint32_t ob = ((uint32_t)(T0 + 4 * g) * Dv + col) * 4u;
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(O[i][e]), rs.out,
-                                                          (int)(ob + (uint32_t)((16 * i + e) * Dv * 4)), 0, 0);
-        }
+        stage_out(reinterpret_cast<float *>(smem + lp.ostage), O, cw, g, c16);
         lds_barrier();  // B2
+        store_staged(reinterpret_cast<const float *>(smem + lp.ostage), rs.out, T0, Dv, dv0, cw, lane);
     }
 
     if (seg == a.nseg - 1 && a.fin) {
@@ -1968,16 +1983,9 @@ __global__ __launch_bounds__(512, 1) void chunk_output_sg_kernel(KArgs a) {
             O[2] = mma(pa[4], vfr[1], O[2]);
             O[3] = mma(pa[5], vfr[1], O[3]);
         }
-        {
-            const uint32_t ob = ((uint32_t)(T0 + 4 * g) * Dv + col) * 4u;
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(O[i][e]), rs.out,
-                                                          (int)(ob + (uint32_t)((16 * i + e) * Dv * 4)), 0, 0);
-        }
+        stage_out(reinterpret_cast<float *>(smem + lp.ostage), O, cw, g, c16);
         lds_barrier();  // B2
+        store_staged(reinterpret_cast<const float *>(smem + lp.ostage), rs.out, T0, Dv, dv0, cw, lane);
     }
 
     if (seg == a.nseg - 1 && a.fin) {

@@ -130,6 +130,7 @@ struct LdsPlanWs {
     uint32_t xact;  // [4 blocks][136] fp32 exact diagonal-block partial scores
     uint32_t xflag; // [4] int32: partial present
     uint32_t pbuf;  // [4096] masked score tile
+    uint32_t ostage;  // [64][68] fp32 output tile, staged for whole-row stores
     uint32_t total;
 };
 
@@ -166,6 +167,8 @@ GLA_HD inline LdsPlanWs lds_plan_ws(int opb, int dk) {
     off += 2u * in;
     p.pbuf = off;
     off += al(4096u * (uint32_t)opb);
+    p.ostage = off;
+    off += al(64u * 68u * 4u);
     p.total = off;
     return p;
 }
@@ -184,6 +187,7 @@ struct LdsPlanSg {
     uint32_t vb;    // [2][4096] fp16 value tiles
     uint32_t rows;  // [2][128] fp32: log2 running decay of each row, then log2 input gate
     uint32_t pbuf;  // [4096] fp16 masked scores
+    uint32_t ostage;  // [64][68] fp32 output tile, staged for whole-row stores
     uint32_t total;
 };
 
@@ -203,6 +207,8 @@ GLA_HD inline LdsPlanSg lds_plan_sg(int dk) {
     off += al(2u * 128u * 4u);
     p.pbuf = off;
     off += al(4096u * 2u);
+    p.ostage = off;
+    off += al(64u * 68u * 4u);
     p.total = off;
     return p;
 }
