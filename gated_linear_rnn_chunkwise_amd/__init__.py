@@ -29,7 +29,8 @@ FLAG_TILE_PAIRS = 1
 GATE_NAMES = {"none": GATE_NONE, "channel": GATE_CHANNEL, "head": GATE_HEAD, "head_const": GATE_HEAD_CONST}
 
 # Entry points declared in include/gla.h.
-EXPORTS = ("gla_fwd", "gla_fwd_ex", "gla_workspace_size", "gla_query_plan", "gla_status_string", "gla_version")
+EXPORTS = ("gla_fwd", "gla_fwd_ex", "gla_workspace_size", "gla_query_plan", "gla_step", "gla_status_string",
+           "gla_version")
 
 
 class GlaDesc(ctypes.Structure):
@@ -50,6 +51,16 @@ class GlaPlan(ctypes.Structure):
         ("seg_chunks", ctypes.c_int32), ("n_seg", ctypes.c_int32), ("dv_tiles", ctypes.c_int32),
         ("tiles_per_chunk", ctypes.c_int32), ("grid_state", ctypes.c_int32), ("grid_scan", ctypes.c_int32),
         ("grid_out", ctypes.c_int32), ("tile_pairs", ctypes.c_int32), ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+class GlaStepDesc(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int32), ("H", ctypes.c_int32), ("Dk", ctypes.c_int32), ("Dv", ctypes.c_int32),
+        ("in_dtype", ctypes.c_int32), ("gate_kind", ctypes.c_int32),
+        ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+        ("log_alpha", ctypes.c_void_p), ("log_ig", ctypes.c_void_p),
+        ("state", ctypes.c_void_p), ("out", ctypes.c_void_p),
     ]
 
 
@@ -82,6 +93,8 @@ def load(path: str = LIB_PATH):
         lib.gla_workspace_size.restype = i32
         lib.gla_query_plan.argtypes = [ctypes.POINTER(GlaDesc), ctypes.POINTER(GlaPlan)]
         lib.gla_query_plan.restype = i32
+        lib.gla_step.argtypes = [ctypes.POINTER(GlaStepDesc), vp]
+        lib.gla_step.restype = i32
         lib.gla_status_string.argtypes = [i32]
         lib.gla_status_string.restype = ctypes.c_char_p
         lib.gla_version.argtypes = []
@@ -194,6 +207,59 @@ def fwd_headline(q, k, v, log_alpha, out, final_state, chunk: int = 64, stream=N
     s = stream if stream is not None else torch.cuda.current_stream(q.device)
     return int(load().gla_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(out), _ptr(final_state), B, H, L,
                               Dk, Dv, int(chunk), ctypes.c_void_p(s.cuda_stream)))
+
+
+def step_gate_kind_of(log_alpha, B: int, H: int, Dk: int) -> int:
+    if log_alpha is None:
+        return GATE_NONE
+    shape = tuple(log_alpha.shape)
+    if shape == (B, H, Dk):
+        return GATE_CHANNEL
+    if shape == (B, H):
+        return GATE_HEAD
+    if shape == (H,):
+        return GATE_HEAD_CONST
+    raise ValueError("log_alpha shape %s matches no gate layout for B=%d H=%d Dk=%d" % (shape, B, H, Dk))
+
+
+def make_step_desc(q, k, v, state, out, log_alpha=None, log_ig=None, gate_kind=None) -> GlaStepDesc:
+    """Fill a :class:`GlaStepDesc` (q, k: [B,H,Dk]; v: [B,H,Dv]; state [B,H,Dk,Dv])."""
+    import torch
+
+    B, H, Dk = q.shape
+    Dv = v.shape[-1]
+    d = GlaStepDesc()
+    d.B, d.H, d.Dk, d.Dv = B, H, Dk, Dv
+    if q.dtype == torch.bfloat16:
+        d.in_dtype = DTYPE_BF16
+    elif q.dtype == torch.float32:
+        d.in_dtype = DTYPE_F32
+    else:
+        raise TypeError("q, k, v must be bf16 or fp32, got %s" % q.dtype)
+    d.gate_kind = step_gate_kind_of(log_alpha, B, H, Dk) if gate_kind is None else int(gate_kind)
+    d.q, d.k, d.v = _ptr(q), _ptr(k), _ptr(v)
+    d.log_alpha, d.log_ig = _ptr(log_alpha), _ptr(log_ig)
+    d.state, d.out = _ptr(state), _ptr(out)
+    return d
+
+
+def step(q, k, v, state, log_alpha=None, *, log_ig=None, out=None, stream=None):
+    """One recurrent step on the current HIP stream: ``state`` [B,H,Dk,Dv] fp32 is updated in
+    place (``S <- diag(alpha) S + i k^T v``) and ``o = q S`` [B,H,Dv] fp32 is returned."""
+    import torch
+
+    lib = load()
+    B, H, Dk = q.shape
+    Dv = v.shape[-1]
+    if out is None:
+        out = torch.empty((B, H, Dv), dtype=torch.float32, device=q.device)
+    _check_tensors(q, k, v, log_alpha, log_ig, state, out)
+    d = make_step_desc(q, k, v, state, out, log_alpha, log_ig)
+    s = stream if stream is not None else torch.cuda.current_stream(q.device)
+    st = lib.gla_step(ctypes.byref(d), ctypes.c_void_p(s.cuda_stream))
+    if st != GLA_OK:
+        raise GlaError(st, "gla_step")
+    return out
 
 
 def plan(desc: GlaDesc) -> GlaPlan:

@@ -19,6 +19,7 @@
 
 namespace gla {
 hipError_t launch_forward(const KArgs &a, bool f32, int dk, hipStream_t st);
+hipError_t launch_step(const gla_step_desc &d, hipStream_t st);
 }
 
 namespace {
@@ -228,6 +229,22 @@ int gla_fwd_ex(const gla_desc *d, void *stream) {
     const hipError_t err = gla::launch_forward(a, d->in_dtype == GLA_DTYPE_F32, d->Dk, s);
     if (owned) (void)hipFreeAsync(ws, s);
     return err == hipSuccess ? GLA_OK : GLA_ERR_HIP;
+}
+
+int gla_step(const gla_step_desc *d, void *stream) {
+    if (!d || !d->q || !d->k || !d->v || !d->state || !d->out) return GLA_ERR_INVALID_ARG;
+    if (d->B <= 0 || d->H <= 0 || d->Dk <= 0 || d->Dv <= 0) return GLA_ERR_INVALID_ARG;
+    if (d->in_dtype != GLA_DTYPE_BF16 && d->in_dtype != GLA_DTYPE_F32) return GLA_ERR_INVALID_ARG;
+    if (d->gate_kind < GLA_GATE_NONE || d->gate_kind > GLA_GATE_HEAD_CONST) return GLA_ERR_INVALID_ARG;
+    if ((d->gate_kind == GLA_GATE_NONE) != (d->log_alpha == nullptr)) return GLA_ERR_INVALID_ARG;
+    const void *ptrs[] = {d->q, d->k, d->v, d->log_alpha, d->log_ig, d->state, d->out};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p)) return GLA_ERR_INVALID_ARG;
+    const int64_t bh = int64_t(d->B) * d->H;
+    if (bh > (int64_t(1) << 24) || bh * int64_t(d->Dk) * d->Dv > (int64_t(1) << 40)) return GLA_ERR_INVALID_ARG;
+    if (d->Dk > 4096 || d->Dv % 64 != 0 || d->Dv > 4096) return GLA_ERR_UNSUPPORTED;
+    if (bh * (d->Dv / 64) > INT32_MAX) return GLA_ERR_UNSUPPORTED;
+    return gla::launch_step(*d, reinterpret_cast<hipStream_t>(stream)) == hipSuccess ? GLA_OK : GLA_ERR_HIP;
 }
 
 int gla_fwd(const void *q, const void *k, const void *v, const float *log_alpha, void *out, float *final_state,

@@ -2268,6 +2268,81 @@ static hipError_t launch_dk(const KArgs &a, bool ch, bool mt, hipStream_t st) {
     return launch_cfg<Cfg<F32, DK, false, false>>(a, st);
 }
 
+// ------------------------------------------------------------------------------------
+// step_kernel: one token of the recurrence.  grid = BH * (Dv / 64) workgroups of 256
+// threads; a workgroup owns one (batch, head) and 64 value columns.  Thread t updates
+// columns 4(t & 15) .. +3 of the state rows d = (t >> 4) + 16 j (float4 loads and stores,
+// 256 contiguous bytes per row), accumulates its part of o = q S_new, and the 16 row groups
+// are summed through LDS.
+template <bool F32>
+__global__ __launch_bounds__(256) void step_kernel(gla_step_desc d) {
+    __shared__ float sq[4096], sk[4096], sa[4096];
+    __shared__ float4 part[16][16];
+    const int ndv = d.Dv / 64;
+    const int bh = (int)blockIdx.x / ndv, dvt = (int)blockIdx.x % ndv;
+    const int h = bh % d.H;
+    const int tid = (int)threadIdx.x;
+    const int Dk = d.Dk, Dv = d.Dv;
+    const auto in = [&](const void *p, size_t i) -> float {
+        if constexpr (F32) return reinterpret_cast<const float *>(p)[i];
+        else return __uint_as_float((uint32_t)reinterpret_cast<const uint16_t *>(p)[i] << 16);
+    };
+    float ig = 1.f;
+    if (d.log_ig) ig = fexp2(d.log_ig[bh] * kLog2e);
+    float ascalar = 1.f;
+    if (d.gate_kind == GLA_GATE_HEAD) ascalar = fexp2(d.log_alpha[bh] * kLog2e);
+    else if (d.gate_kind == GLA_GATE_HEAD_CONST) ascalar = fexp2(d.log_alpha[h] * kLog2e);
+    for (int r = tid; r < Dk; r += 256) {
+        sq[r] = in(d.q, (size_t)bh * Dk + r);
+        sk[r] = in(d.k, (size_t)bh * Dk + r) * ig;
+        sa[r] = d.gate_kind == GLA_GATE_CHANNEL ? fexp2(d.log_alpha[(size_t)bh * Dk + r] * kLog2e) : ascalar;
+    }
+    __syncthreads();
+    const int cq = tid & 15, rg = tid >> 4;
+    const int c0 = dvt * 64 + 4 * cq;
+    float vv[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) vv[j] = in(d.v, (size_t)bh * Dv + c0 + j);
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    float *S = d.state + (size_t)bh * Dk * Dv + c0;
+    for (int r = rg; r < Dk; r += 16) {
+        float4 *p = reinterpret_cast<float4 *>(S + (size_t)r * Dv);
+        float4 x = *p;
+        const float a = sa[r], kr = sk[r], qr = sq[r];
+        x.x = a * x.x + kr * vv[0];
+        x.y = a * x.y + kr * vv[1];
+        x.z = a * x.z + kr * vv[2];
+        x.w = a * x.w + kr * vv[3];
+        *p = x;
+        acc.x += qr * x.x;
+        acc.y += qr * x.y;
+        acc.z += qr * x.z;
+        acc.w += qr * x.w;
+    }
+    part[rg][cq] = acc;
+    __syncthreads();
+    if (tid < 16) {
+        float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int g = 0; g < 16; ++g) {
+            const float4 y = part[g][tid];
+            o.x += y.x;
+            o.y += y.y;
+            o.z += y.z;
+            o.w += y.w;
+        }
+        *reinterpret_cast<float4 *>(d.out + (size_t)bh * Dv + dvt * 64 + 4 * tid) = o;
+    }
+}
+
+hipError_t launch_step(const gla_step_desc &d, hipStream_t st) {
+    const int grid = d.B * d.H * (d.Dv / 64);
+    if (d.in_dtype == GLA_DTYPE_F32)
+        hipLaunchKernelGGL(step_kernel<true>, dim3(grid), dim3(256), 0, st, d);
+    else
+        hipLaunchKernelGGL(step_kernel<false>, dim3(grid), dim3(256), 0, st, d);
+    return hipGetLastError();
+}
+
 hipError_t launch_forward(const KArgs &a, bool f32, int dk, hipStream_t st) {
     const bool ch = a.gate == GLA_GATE_CHANNEL;
     const bool mt = a.nt > 1;

@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define GLA_VERSION 10100 /* major * 10000 + minor * 100 + patch */
+#define GLA_VERSION 10200 /* major * 10000 + minor * 100 + patch */
 
 /* Status codes.  0 is success; errors are negative. */
 enum gla_status {
@@ -151,6 +151,35 @@ int gla_workspace_size(const gla_desc *d, size_t *bytes);
 
 /* Launch plan gla_fwd_ex would use for `d` (no HIP call).  Returns a gla_status. */
 int gla_query_plan(const gla_desc *d, gla_plan *plan);
+
+/* One token of the recurrence for every (batch, head): the recurrent (decoding) form, one
+ * rank-1 write of the state followed by one vector-matrix read [Hardware-Efficient Training
+ * of Linear Attention Models, talk summary, 4:04 and 7:36]:
+ *
+ *     S <- diag(alpha) S + i k^T v ,     o = q S .
+ *
+ * A chunkwise forward pass over L tokens followed by steps for tokens L, L+1, ... gives the
+ * same outputs as one forward pass over all of them (the state is the final state of the
+ * forward pass).  Everything is dense and row-major on the device, 16-byte aligned.  */
+typedef struct gla_step_desc {
+    int32_t B, H, Dk, Dv;    /* batch, heads, key and value head dims */
+    int32_t in_dtype;        /* enum gla_dtype of q, k, v */
+    int32_t gate_kind;       /* enum gla_gate; CHANNEL: [B, H, Dk], HEAD: [B, H], HEAD_CONST: [H] */
+    const void *q;           /* [B, H, Dk] */
+    const void *k;           /* [B, H, Dk] */
+    const void *v;           /* [B, H, Dv] */
+    const float *log_alpha;  /* layout per gate_kind; must be NULL iff gate_kind == NONE */
+    const float *log_ig;     /* [B, H] log input gate, or NULL (i = 1) */
+    float *state;            /* [B, H, Dk, Dv] fp32 state, read and updated in place */
+    float *out;              /* [B, H, Dv] fp32 output */
+} gla_step_desc;
+
+/* Recurrent step.  Support matrix (else GLA_ERR_UNSUPPORTED): Dk in [1, 4096], Dv a
+ * multiple of 64 up to 4096.  Validation as for gla_fwd_ex (GLA_ERR_INVALID_ARG for NULL
+ * required pointers, sizes <= 0, misalignment, a gate pointer inconsistent with its kind).
+ * The state must not alias q, k, v, the gates or the output.  Asynchronous on `stream`;
+ * allocates nothing.  Returns a gla_status. */
+int gla_step(const gla_step_desc *d, void *stream);
 
 /* Static English text for a status code (never NULL). */
 const char *gla_status_string(int status);

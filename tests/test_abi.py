@@ -202,3 +202,29 @@ def test_tile_pair_flag_in_plan(lib):
         # per-channel gate, tile pairs: keys of the earlier tiles of a chunk go to scratch
         assert p1.workspace_bytes == (0 if chunk == 64 else
                                       (p1.grid_out * (chunk // 64 - 1) * 64 * 128 * 2 + 255) // 256 * 256)
+
+
+def step_desc(**kw):
+    d = gla.GlaStepDesc()
+    base = dict(B=2, H=3, Dk=128, Dv=128, in_dtype=gla.DTYPE_BF16, gate_kind=gla.GATE_CHANNEL, q=A, k=A, v=A,
+                log_alpha=A, log_ig=None, state=A, out=A)
+    base.update(kw)
+    for key, val in base.items():
+        setattr(d, key, val)
+    return d
+
+
+@pytest.mark.parametrize("field,bad", [("B", 0), ("H", -1), ("Dk", 0), ("Dv", 0), ("in_dtype", 7), ("gate_kind", 9),
+                                       ("q", None), ("state", None), ("out", None), ("v", A + 8)])
+def test_step_invalid_arguments(lib, field, bad):
+    assert lib.gla_step(ctypes.byref(step_desc(**{field: bad})), None) == gla.GLA_ERR_INVALID_ARG
+
+
+def test_step_gate_pointer_must_match_kind(lib):
+    assert lib.gla_step(ctypes.byref(step_desc(gate_kind=gla.GATE_NONE)), None) == gla.GLA_ERR_INVALID_ARG
+    assert lib.gla_step(ctypes.byref(step_desc(log_alpha=None)), None) == gla.GLA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("kw", [dict(Dv=96), dict(Dv=4160), dict(Dk=4097)])
+def test_step_unsupported(lib, kw):
+    assert lib.gla_step(ctypes.byref(step_desc(**kw)), None) == gla.GLA_ERR_UNSUPPORTED

@@ -271,3 +271,61 @@ def test_full_workload_sampled_heads(gpu_lib, name, heads, tile_pairs):
     gfin = fin.reshape(-1, *fin.shape[2:])[heads][None]
     check(w, got, ref)
     check(w, gfin, rfin, "final_state")
+
+
+# ------------------------------------------------------------------------------ recurrent step
+def _token(d, w, t):
+    """Inputs of token t: q, k [B,H,Dk], v [B,H,Dv], gate in the step layout, input gate [B,H]."""
+    la = d["log_alpha"]
+    if la is not None and w.gate in ("channel", "head"):
+        la = la[:, :, t]
+    li = None if d["log_ig"] is None else d["log_ig"][:, :, t]
+    return d["q"][:, :, t], d["k"][:, :, t], d["v"][:, :, t], la, li
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("gate,ig", [("channel", False), ("head", True), ("head_const", False), ("none", False),
+                                     ("channel", True)])
+@pytest.mark.parametrize("Dk,Dv", [(128, 128), (64, 192), (256, 64), (100, 64)])
+def test_step_sequence_matches_recurrence(gpu_lib, dtype, gate, ig, Dk, Dv):
+    # 9 steps from a random initial state against the fp64 recurrence over the same tokens
+    w = gin.custom(2, 3, 9, Dk, Dv, 64, dtype=dtype, gate=gate, input_gate=ig)
+    d = gin.make_inputs(w, seed=21)
+    s0 = torch.randn(2, 3, Dk, Dv, generator=torch.Generator().manual_seed(5)) * 0.1
+    state = s0.clone().cuda()
+    outs = []
+    for t in range(w.L):
+        q, k, v, la, li = (None if x is None else x.cuda().contiguous() for x in _token(d, w, t))
+        outs.append(gpu_lib.step(q, k, v, state, la, log_ig=li).cpu())
+    torch.cuda.synchronize()
+    got = torch.stack(outs, dim=2).double().numpy()
+    ref, rfin = run_oracle(d, w, initial_state=s0)
+    check(w, got, ref)
+    check(w, state.cpu().double().numpy(), rfin, "final_state")
+
+
+@pytest.mark.parametrize("gate,ig,chunk", [("channel", False, 64), ("head", True, 256), ("head_const", False, 128)])
+def test_step_continues_chunkwise_forward(gpu_lib, gate, ig, chunk):
+    # chunkwise forward over L tokens, then recurrent steps for tokens L.. from its final state
+    L, extra = 300, 5
+    Dk = 256 if gate == "head" else 128
+    w = gin.custom(2, 2, L + extra, Dk, 128, chunk, gate=gate, input_gate=ig)
+    d = gin.make_inputs(w, seed=12)
+    dl = dict(d)
+    for key in ("q", "k", "v"):
+        dl[key] = d[key][:, :, :L].contiguous()
+    if gate in ("channel", "head"):
+        dl["log_alpha"] = d["log_alpha"][:, :, :L].contiguous()
+    if d["log_ig"] is not None:
+        dl["log_ig"] = d["log_ig"][:, :, :L].contiguous()
+    _, fin = run_gpu(gpu_lib, dl, w.with_(L=L))
+    state = torch.from_numpy(fin).float().cuda()
+    outs = []
+    for t in range(L, L + extra):
+        q, k, v, la, li = (None if x is None else x.cuda().contiguous() for x in _token(d, w, t))
+        outs.append(gpu_lib.step(q, k, v, state, la, log_ig=li).cpu())
+    torch.cuda.synchronize()
+    got = torch.stack(outs, dim=2).double().numpy()
+    ref, rfin = run_oracle(d, w)
+    check(w, got, ref[:, :, L:])
+    check(w, state.cpu().double().numpy(), rfin, "final_state")
