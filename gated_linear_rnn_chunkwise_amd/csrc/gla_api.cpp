@@ -94,18 +94,14 @@ int make_plan(const gla_desc *d, Plan *p) {
     p->nseg = (p->nc + sc - 1) / sc;
     p->seg_len = sc * d->chunk;
     // Segment boundary states are sums of sub-segment states, computed by more workgroups
-    // than there are boundaries: nsub is the largest divisor of the tiles per segment that
-    // keeps the state grid near kTargetStateWorkgroups.
+    // than there are boundaries: nsub (sub-segments of a segment, whose tile counts differ
+    // by at most one) brings the state grid nearest to kTargetStateWorkgroups.
     p->nsub = 1;
     if (p->nseg > 1) {
         const int64_t base = bh * (p->nseg - 1) * p->ndv;
         const int tiles = p->seg_len / gla::kTile;
-        const int64_t want = std::max<int64_t>(1, (kTargetStateWorkgroups + base - 1) / base);
-        for (int d = (int)std::min<int64_t>(want, tiles); d >= 1; --d)
-            if (tiles % d == 0) {
-                p->nsub = d;
-                break;
-            }
+        const int64_t want = (kTargetStateWorkgroups + base / 2) / base;
+        p->nsub = (int)std::max<int64_t>(1, std::min<int64_t>(want, tiles));
     }
     const int64_t nss = int64_t(p->nseg - 1) * p->nsub;
     const int64_t g3 = bh * p->nseg * p->ndv;

@@ -1997,8 +1997,8 @@ __global__ __launch_bounds__(512, 1) void chunk_output_sg_kernel(KArgs a) {
 }
 
 // ------------------------------------------------------------------------------------
-// segment_state_kernel: grid = BH * (nseg - 1) * nsub * ndv.  The state sub-segment j (of
-// seg_len / nsub tokens) produces from zero, sum_s diag(decay from s to the sub-segment end)
+// segment_state_kernel: grid = BH * (nseg - 1) * nsub * ndv.  The state sub-segment j (a
+// run of whole tiles; the nsub runs of a segment differ by at most one tile) produces from zero, sum_s diag(decay from s to the sub-segment end)
 // i_s k_s^T v_s, accumulated tile by tile (dS <- diag(tile decay) dS + K~^T V), and the decay
 // across the sub-segment.
 template <class C>
@@ -2015,7 +2015,6 @@ __global__ __launch_bounds__(256, 3) void segment_state_kernel(KArgs a) {
     float *sAs = reinterpret_cast<float *>(smem + lp.aseg);
 
     const int nsm = (a.nseg - 1) * a.nsub;
-    const int sub_len = a.seg_len / a.nsub;
     int id = xcd_remap((int)blockIdx.x, a.nwg);
     const int dvt = id % a.ndv;
     id /= a.ndv;
@@ -2027,8 +2026,11 @@ __global__ __launch_bounds__(256, 3) void segment_state_kernel(KArgs a) {
     const int L = a.L, Dv = a.Dv;
     const int dv0 = dvt * kDvTile;
     const int col = dv0 + 16 * w + c16;
-    const int t_begin = seg * sub_len;
-    const int t_end = min(L, t_begin + sub_len);
+    // sub-segment jj of segment sg: tiles [tiles * jj / nsub, tiles * (jj + 1) / nsub) of it
+    const int tiles = a.seg_len / kTile;
+    const int sg = seg / a.nsub, jj = seg % a.nsub;
+    const int t_begin = sg * a.seg_len + kTile * ((tiles * jj) / a.nsub);
+    const int t_end = min(L, sg * a.seg_len + kTile * ((tiles * (jj + 1)) / a.nsub));
     const int chl = C::CPL * lane;
     const Rs rs = make_rs<C>(a, bh, h);
 
