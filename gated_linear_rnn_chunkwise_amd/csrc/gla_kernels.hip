@@ -1056,36 +1056,10 @@ __global__ __launch_bounds__(256, 1) void chunk_output_kernel(KArgs a) {
 // CPL*l .. +CPL-1, so every load instruction covers whole rows of q, k and the gates, and a
 // lane walks its block's 16 rows for the running decay products.
 
+// The loads of one unit come in three groups, so that the producer can reissue each group
+// for the chunk after next as soon as it has consumed that group's registers.
 template <class C>
-__device__ __forceinline__ void load_unit_p(Raw<C> &r, const Rs &rs, int T0, int pw, int lane, int dv0, int Dv) {
-    const int ch0 = C::CPL * lane;
-    const uint32_t row0 = (uint32_t)(T0 + 16 * pw);
-#pragma unroll
-    for (int rr = 0; rr < 16; ++rr) {
-        const uint32_t off = ((row0 + rr) * C::DK + ch0) * C::IB;
-        if constexpr (C::CPL == 2 || C::F32) {
-            r.q[rr] = bld32(rs.q, off);
-            r.k[rr] = bld32(rs.k, off);
-        } else {
-            r.q[rr] = __builtin_amdgcn_raw_buffer_load_b16(rs.q, (int)off, 0, 0);
-            r.k[rr] = __builtin_amdgcn_raw_buffer_load_b16(rs.k, (int)off, 0, 0);
-        }
-        if constexpr (C::CH) {
-            const uint32_t goff = ((row0 + rr) * C::DK + ch0) * 4u;
-            if constexpr (C::CPL == 2) {
-                const u32x2 g2 = bld64(rs.la, goff);
-                r.la[rr][0] = __uint_as_float(g2[0]);
-                r.la[rr][1] = __uint_as_float(g2[1]);
-            } else {
-                r.la[rr][0] = __uint_as_float(bld32(rs.la, goff));
-            }
-        }
-    }
-    // scalar gates: one branch-free load for every kind (per token: stride 4; fixed per head:
-    // stride 0, masked past the sequence end where it is used; none: empty resource)
-    const uint32_t t = (uint32_t)(T0 + lane);
-    if constexpr (!C::CH) r.las = __uint_as_float(bld32(rs.la, t * rs.gstride));
-    r.lis = __uint_as_float(bld32(rs.li, t * 4u));
+__device__ __forceinline__ void load_p_v(Raw<C> &r, const Rs &rs, int T0, int pw, int lane, int dv0, int Dv) {
     const int tp = 64 * pw + lane;
     const uint32_t c0 = dv0 + 4 * (tp & 15);
 #pragma unroll
@@ -1101,6 +1075,51 @@ __device__ __forceinline__ void load_unit_p(Raw<C> &r, const Rs &rs, int T0, int
             r.v[e][1] = x[1];
         }
     }
+}
+template <class C>
+__device__ __forceinline__ void load_p_gates(Raw<C> &r, const Rs &rs, int T0, int pw, int lane) {
+    if constexpr (C::CH) {
+        const int ch0 = C::CPL * lane;
+        const uint32_t row0 = (uint32_t)(T0 + 16 * pw);
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+            const uint32_t goff = ((row0 + rr) * C::DK + ch0) * 4u;
+            if constexpr (C::CPL == 2) {
+                const u32x2 g2 = bld64(rs.la, goff);
+                r.la[rr][0] = __uint_as_float(g2[0]);
+                r.la[rr][1] = __uint_as_float(g2[1]);
+            } else {
+                r.la[rr][0] = __uint_as_float(bld32(rs.la, goff));
+            }
+        }
+    }
+    // scalar gates: one branch-free load for every kind (per token: stride 4; fixed per head:
+    // stride 0, masked past the sequence end where it is used; none: empty resource)
+    const uint32_t t = (uint32_t)(T0 + lane);
+    if constexpr (!C::CH) r.las = __uint_as_float(bld32(rs.la, t * rs.gstride));
+    r.lis = __uint_as_float(bld32(rs.li, t * 4u));
+}
+template <class C>
+__device__ __forceinline__ void load_p_qk(Raw<C> &r, const Rs &rs, int T0, int pw, int lane) {
+    const int ch0 = C::CPL * lane;
+    const uint32_t row0 = (uint32_t)(T0 + 16 * pw);
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) {
+        const uint32_t off = ((row0 + rr) * C::DK + ch0) * C::IB;
+        if constexpr (C::CPL == 2 || C::F32) {
+            r.q[rr] = bld32(rs.q, off);
+            r.k[rr] = bld32(rs.k, off);
+        } else {
+            r.q[rr] = __builtin_amdgcn_raw_buffer_load_b16(rs.q, (int)off, 0, 0);
+            r.k[rr] = __builtin_amdgcn_raw_buffer_load_b16(rs.k, (int)off, 0, 0);
+        }
+    }
+}
+template <class C>
+__device__ __forceinline__ void load_unit_p(Raw<C> &r, const Rs &rs, int T0, int pw, int lane, int dv0, int Dv) {
+    load_p_qk<C>(r, rs, T0, pw, lane);
+    load_p_gates<C>(r, rs, T0, pw, lane);
+    load_p_v<C>(r, rs, T0, pw, lane, dv0, Dv);
 }
 
 // CPL operands of one row packed into 32 bits (fp16 pair / one fp16 / one fp32).
@@ -1169,9 +1188,9 @@ __device__ __attribute__((noinline)) void ws_exact_block(Raw<C> raw, float *dst,
 // Producer phase A: gates of one chunk (block pw), values, block decays and exact partial
 // scores into buffer nb; scalar gates also write keys^T.  q/k operands stay in registers.
 template <class C>
-__device__ __forceinline__ void ws_produce_a(ProdVals<C> &pv, const Raw<C> &raw, const LdsPlanWs &lp,
+__device__ __forceinline__ void ws_produce_a(ProdVals<C> &pv, Raw<C> &raw, const LdsPlanWs &lp,
                                              unsigned char *smem, int nb, int pw, int lane, bool has_li,
-                                             bool row_valid) {
+                                             bool row_valid, const Rs &rs, int Tn, int dv0, int Dv) {
     using OpT = typename C::OpT;
     using Half = typename C::Half;
     const int ch0 = C::CPL * lane;
@@ -1180,6 +1199,8 @@ __device__ __forceinline__ void ws_produce_a(ProdVals<C> &pv, const Raw<C> &raw,
     float *sAb = reinterpret_cast<float *>(buf + lp.ab);
     float *sAi = reinterpret_cast<float *>(buf + lp.ainv);
     v_to_lds<C>(raw, reinterpret_cast<OpT *>(buf + lp.vb), 64 * pw + lane);
+    load_p_v<C>(raw, rs, Tn, pw, lane, dv0, Dv);
+    __builtin_amdgcn_sched_barrier(0);
 
     float ig[16];
     {
@@ -1216,16 +1237,32 @@ __device__ __forceinline__ void ws_produce_a(ProdVals<C> &pv, const Raw<C> &raw,
             }
         }
         bool any_h = false;
+        float fa[C::CPL], fi[C::CPL];
 #pragma unroll
         for (int c = 0; c < C::CPL; ++c) {
             const float ag = eq[15][c];
             pv.ag[c] = ag;
             const bool hc = !(ag >= C::kMinDiagDecay);
             any_h |= hc;
+            fa[c] = ag;
+            fi[c] = hc ? 0.f : frcp(ag);
             // block decays scale q and k fragments: stored in the rows' chperm channel order
             sAb[pw * C::SLAB + chperm(ch0 + c)] = ag;
-            sAi[pw * C::SLAB + chperm(ch0 + c)] = hc ? 0.f : frcp(ag);
+            sAi[pw * C::SLAB + chperm(ch0 + c)] = fi[c];
         }
+        {
+            OpT *sF = reinterpret_cast<OpT *>(buf + lp.fh);
+            const int pc = chperm(ch0);
+            if (pw < 3) st_packed<C>(sF + (kFhA0 + pw) * C::SLAB + pc, pack_ops<C>(fa));
+            st_packed<C>(sF + (kFhInv + pw) * C::SLAB + pc, pack_ops<C>(fi));
+        }
+        // channels of this block whose decay is too strong: exact partial scores (rare)
+        const bool harsh = __ballot(any_h) != 0ull;
+        if (harsh)
+            ws_exact_block<C>(raw, reinterpret_cast<float *>(buf + lp.xact) + pw * 136, pw, lane, has_li);
+        if (lane == 0) reinterpret_cast<int *>(buf + lp.xflag)[pw] = harsh ? 1 : 0;
+        load_p_gates<C>(raw, rs, Tn, pw, lane);
+        __builtin_amdgcn_sched_barrier(0);  // keep the reload ahead of the work below
 #pragma unroll
         for (int rr = 0; rr < 16; ++rr) {
             float qd[C::CPL], ko[C::CPL];
@@ -1238,11 +1275,7 @@ __device__ __forceinline__ void ws_produce_a(ProdVals<C> &pv, const Raw<C> &raw,
             pv.qd[rr] = pack_ops<C>(qd);
             pv.ko[rr] = pack_ops<C>(ko);
         }
-        // channels of this block whose decay is too strong: exact partial scores (rare)
-        const bool harsh = __ballot(any_h) != 0ull;
-        if (harsh)
-            ws_exact_block<C>(raw, reinterpret_cast<float *>(buf + lp.xact) + pw * 136, pw, lane, has_li);
-        if (lane == 0) reinterpret_cast<int *>(buf + lp.xflag)[pw] = harsh ? 1 : 0;
+        load_p_qk<C>(raw, rs, Tn, pw, lane);
     } else {
         // scalar gates: running log2 decay over the tile's rows (lane = row); rows past the
         // sequence end carry no decay (a fixed per-head gate is loaded for them too)
@@ -1257,6 +1290,8 @@ __device__ __forceinline__ void ws_produce_a(ProdVals<C> &pv, const Raw<C> &raw,
             sLr[lane] = y;
         }
         const float wk = fexp2(Tt - bl + y);  // weight of key row `lane` in the state update
+        load_p_gates<C>(raw, rs, Tn, pw, lane);
+        __builtin_amdgcn_sched_barrier(0);  // keep the reload ahead of the work below
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
             Half kt4[C::CPL];
@@ -1278,6 +1313,7 @@ __device__ __forceinline__ void ws_produce_a(ProdVals<C> &pv, const Raw<C> &raw,
             for (int c = 0; c < C::CPL; ++c)
                 *reinterpret_cast<Half *>(sKT + kt_off<C>(ch0 + c, kslot(16 * pw + 4 * g4))) = kt4[c];
         }
+        load_p_qk<C>(raw, rs, Tn, pw, lane);
     }
 }
 
@@ -1320,6 +1356,20 @@ __device__ __forceinline__ void ws_produce_b(const ProdVals<C> &pv, const LdsPla
             float *sAt = reinterpret_cast<float *>(buf + lp.at);
 #pragma unroll
             for (int c = 0; c < C::CPL; ++c) sAt[ch0 + c] = all[c];
+        } else {
+            // products of block decays for the inter-chunk term and the rescaled queries:
+            // wave 1 a_0 a_1, wave 2 a_0 a_1 a_2, wave 3 a_1 a_2
+            float f[C::CPL];
+#pragma unroll
+            for (int c = 0; c < C::CPL; ++c) {
+                const int cp = chperm(ch0 + c);
+                const float a1 = sAb[C::SLAB + cp];
+                const float a2 = pw == 1 ? 1.f : sAb[2 * C::SLAB + cp];
+                const float a0 = pw == 3 ? 1.f : sAb[cp];
+                f[c] = a0 * a1 * a2;
+            }
+            const int row = pw == 1 ? kFhP2 : pw == 2 ? kFhP3 : kFhA12;
+            st_packed<C>(reinterpret_cast<OpT *>(buf + lp.fh) + row * C::SLAB + pc, pack_ops<C>(f));
         }
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
@@ -1370,14 +1420,14 @@ __global__ __launch_bounds__(512, 1) void chunk_output_ws_kernel(KArgs a) {
         // range check.  Conditional loads would make the compiler merge register copies
         // that wait for the whole prefetch as soon as it is issued.
         load_unit_p<C>(raw, rs, t_begin, pw, lane, dv0, Dv);
-        ws_produce_a<C>(pv, raw, lp, smem, 0, pw, lane, LI, t_begin + lane < L);
-        load_unit_p<C>(raw, rs, t_begin + kTile, pw, lane, dv0, Dv);
+        ws_produce_a<C>(pv, raw, lp, smem, 0, pw, lane, LI, t_begin + lane < L, rs, t_begin + kTile, dv0, Dv);
         lds_barrier();  // block decays of chunk 0 published
         ws_produce_b<C>(pv, lp, smem, 0, pw, lane);
         lds_barrier();
         for (int kc = 0; kc < nch; ++kc) {
-            ws_produce_a<C>(pv, raw, lp, smem, (kc + 1) & 1, pw, lane, LI, t_begin + kTile * (kc + 1) + lane < L);
-            load_unit_p<C>(raw, rs, t_begin + kTile * (kc + 2), pw, lane, dv0, Dv);
+            // prepares chunk kc + 1 and reloads the registers with chunk kc + 2 group by group
+            ws_produce_a<C>(pv, raw, lp, smem, (kc + 1) & 1, pw, lane, LI, t_begin + kTile * (kc + 1) + lane < L,
+                            rs, t_begin + kTile * (kc + 2), dv0, Dv);
             lds_barrier();  // B1
             ws_produce_b<C>(pv, lp, smem, (kc + 1) & 1, pw, lane);
             lds_barrier();  // B2
@@ -1428,6 +1478,7 @@ __global__ __launch_bounds__(512, 1) void chunk_output_ws_kernel(KArgs a) {
         const float *sAb = reinterpret_cast<const float *>(smem + (lp.dbl + (b) * lp.dstride + lp.ab));
         const float *sAi = reinterpret_cast<const float *>(smem + (lp.dbl + (b) * lp.dstride + lp.ainv));
         const float *sAt = reinterpret_cast<const float *>(smem + (lp.dbl + (b) * lp.dstride + lp.at));
+        const OpT *sF = reinterpret_cast<const OpT *>(smem + (lp.dbl + (b) * lp.dstride + lp.fh));
 
         // ---------------- phase A: score blocks P^T(j, i) over the key channels and the
         // inter-chunk term, sharing the q fragments.  Per-channel gate: the queries of block i
@@ -1461,7 +1512,42 @@ __global__ __launch_bounds__(512, 1) void chunk_output_ws_kernel(KArgs a) {
             for (int e = 0; e < 8; ++e) sb[e] = (OpT)sv[e];
             O[0] = mma(qf[0], sb, O[0]);
             const auto kf = [&](int j) { return ld8<C>(sK + (16 * j + c16) * C::RP + ch); };
-            if constexpr (C::CH) {
+            if constexpr (C::CH && !C::F32) {
+                // fp16 operands: the factors are fp16 too, applied with packed multiplies
+                const auto fh = [&](int row) { return ld8<C>(sF + row * C::SLAB + ch); };
+                O[1] = mma(qf[1], sb * fh(kFhA0), O[1]);
+                O[2] = mma(qf[2], sb * fh(kFhP2), O[2]);
+                O[3] = mma(qf[3], sb * fh(kFhP3), O[3]);
+                const Frag fi = fh(kFhInv + cw);
+                switch (cw) {
+                    case 0: {
+                        const Frag k0 = kf(0), k2 = kf(2);
+                        Pd[0] = mma(k0 * fi, qf[0], Pd[0]);
+                        Pd[1] = mma(k0, qf[1], Pd[1]);
+                        Pd[2] = mma(k2, qf[3], Pd[2]);
+                        break;
+                    }
+                    case 1: {
+                        const Frag k1 = kf(1), k0 = kf(0);
+                        Pd[0] = mma(k1 * fi, qf[1], Pd[0]);
+                        Pd[1] = mma(k0, qf[2] * fh(kFhA1), Pd[1]);
+                        Pd[2] = mma(k1, qf[3] * fh(kFhA2), Pd[2]);
+                        break;
+                    }
+                    case 2: {
+                        const Frag k2 = kf(2), k1 = kf(1);
+                        Pd[0] = mma(k2 * fi, qf[2], Pd[0]);
+                        Pd[1] = mma(k1, qf[2], Pd[1]);
+                        break;
+                    }
+                    default: {
+                        const Frag k3 = kf(3), k0 = kf(0);
+                        Pd[0] = mma(k3 * fi, qf[3], Pd[0]);
+                        Pd[1] = mma(k0, qf[3] * fh(kFhA12), Pd[1]);
+                        break;
+                    }
+                }
+            } else if constexpr (C::CH) {
                 const f32x4 a0l = lds_ld<f32x4>(sAb + ch), a0h = lds_ld<f32x4>(sAb + ch + 4);
                 const f32x4 a1l = lds_ld<f32x4>(sAb + C::SLAB + ch), a1h = lds_ld<f32x4>(sAb + C::SLAB + ch + 4);
                 const f32x4 a2l = lds_ld<f32x4>(sAb + 2 * C::SLAB + ch), a2h = lds_ld<f32x4>(sAb + 2 * C::SLAB + ch + 4);

@@ -116,6 +116,19 @@ GLA_HD inline LdsPlanState lds_plan_state(int opb, int dk) {
 // producer waves prepare chunk k+1 while four consumer waves run the matrix products of
 // chunk k.  Arrays read by the consumers only before the mid-iteration barrier are single
 // (q, k); arrays read after it are double-buffered by chunk parity.
+// Rows of the operand-precision gate factors of the warp-specialised kernel (a_u = decay
+// across 16-token block u of the tile, per channel).
+enum : int {
+    kFhA0 = 0,    // a_0
+    kFhA1 = 1,    // a_1
+    kFhA2 = 2,    // a_2
+    kFhA12 = 3,   // a_1 a_2
+    kFhInv = 4,   // rows 4 + u: 1 / a_u, 0 for channels whose block u is handled exactly
+    kFhP2 = 8,    // a_0 a_1
+    kFhP3 = 9,    // a_0 a_1 a_2
+    kFhRows = 10
+};
+
 struct LdsPlanWs {
     uint32_t q, k;  // [64][rp] single buffers, channels in the chperm order
     // double-buffered block: buffer b starts at dbl + b * dstride; offsets inside a buffer:
@@ -129,6 +142,8 @@ struct LdsPlanWs {
     uint32_t at;    // [slab] fp32 decay across the tile (per-channel)
     uint32_t xact;  // [4 blocks][136] fp32 exact diagonal-block partial scores
     uint32_t xflag; // [4] int32: partial present
+    uint32_t fh;    // [10][slab] per-channel gate factors in operand precision, chperm order:
+                    //           rows kFh* below
     uint32_t pbuf;  // [4096] masked score tile
     uint32_t ostage;  // [64][68] fp32 output tile, staged for whole-row stores
     uint32_t total;
@@ -162,6 +177,8 @@ GLA_HD inline LdsPlanWs lds_plan_ws(int opb, int dk) {
     in += al(4u * 136u * 4u);
     p.xflag = in;
     in += al(4u * 4u);
+    p.fh = in;
+    in += al((uint32_t)kFhRows * (uint32_t)slab * (uint32_t)opb);
     p.dbl = off;
     p.dstride = in;
     off += 2u * in;
