@@ -50,6 +50,7 @@ typedef _Float16 f16;
 typedef f16 f16x8 __attribute__((ext_vector_type(8)));
 typedef f16 f16x4 __attribute__((ext_vector_type(4)));
 typedef f16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -184,6 +185,27 @@ __device__ __forceinline__ typename C::Frag scale8(const typename C::Frag &f, co
     }
     return r;
 }
+// Lane n of the calling lane's 16-lane row (DPP row broadcast); n must fold to a constant.
+__device__ __forceinline__ uint32_t row_bcast(uint32_t v, int n) {
+#define GLA_RB(N) \
+    case N: return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x150 + N, 0xf, 0xf, false);
+    switch (n) {
+        GLA_RB(0) GLA_RB(1) GLA_RB(2) GLA_RB(3) GLA_RB(4) GLA_RB(5) GLA_RB(6) GLA_RB(7)
+        GLA_RB(8) GLA_RB(9) GLA_RB(10) GLA_RB(11) GLA_RB(12) GLA_RB(13) GLA_RB(14)
+        default: return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x150 + 15, 0xf, 0xf, false);
+    }
+#undef GLA_RB
+}
+// Eight fp16 per-channel factors of MFMA k-step m for a lane of row g, from one dword per lane
+// that holds factor dword 16 (lane>>2 & 3) + 4 g + (lane & 3) of the row (see fac_dword).
+__device__ __forceinline__ f16x8 fac_frag(uint32_t f, int m) {
+    const u32x4 d{row_bcast(f, 4 * m), row_bcast(f, 4 * m + 1), row_bcast(f, 4 * m + 2), row_bcast(f, 4 * m + 3)};
+    return __builtin_bit_cast(f16x8, d);
+}
+// The factor dword a lane (g, c16) loads once per tile: k-step c16 >> 2, dword c16 & 3 of the
+// eight channels 32 m + 8 g ..; rows of ndw dwords (ndw = 16 x k-steps).
+__device__ __forceinline__ int fac_dword(int g, int c16, int ndw) { return (16 * (c16 >> 2) + 4 * g + (c16 & 3)) & (ndw - 1); }
+
 // 8 fp32 values times per-element factors, rounded once to operands.
 template <class C>
 __device__ __forceinline__ typename C::Frag scale8f(const float *x, const f32x4 &s0, const f32x4 &s1) {
@@ -1495,6 +1517,23 @@ __global__ __launch_bounds__(512, 1) void chunk_output_ws_kernel(KArgs a) {
         for (int kp = 0; kp < 3; ++kp) Pd[kp] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int i = 0; i < 4; ++i) O[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // fp16 per-channel factors: one dword of each needed row per lane for the whole tile
+        uint32_t fw[6] = {0u, 0u, 0u, 0u, 0u, 0u};
+        if constexpr (C::CH && !C::F32) {
+            const uint32_t *sFd = reinterpret_cast<const uint32_t *>(sF);
+            const int fd = fac_dword(g, c16, C::SLAB / 2);
+            constexpr int RW = C::SLAB / 2;  // dwords per factor row
+            fw[0] = sFd[kFhA0 * RW + fd];
+            fw[1] = sFd[kFhP2 * RW + fd];
+            fw[2] = sFd[kFhP3 * RW + fd];
+            fw[3] = sFd[(kFhInv + cw) * RW + fd];
+            if (cw == 1) {
+                fw[4] = sFd[kFhA1 * RW + fd];
+                fw[5] = sFd[kFhA2 * RW + fd];
+            } else if (cw == 3) {
+                fw[4] = sFd[kFhA12 * RW + fd];
+            }
+        }
 #pragma unroll
         for (int m = 0; m < C::KSTEP; ++m) {
             const int ch = 32 * m + 8 * g;
@@ -1514,11 +1553,10 @@ __global__ __launch_bounds__(512, 1) void chunk_output_ws_kernel(KArgs a) {
             const auto kf = [&](int j) { return ld8<C>(sK + (16 * j + c16) * C::RP + ch); };
             if constexpr (C::CH && !C::F32) {
                 // fp16 operands: the factors are fp16 too, applied with packed multiplies
-                const auto fh = [&](int row) { return ld8<C>(sF + row * C::SLAB + ch); };
-                O[1] = mma(qf[1], sb * fh(kFhA0), O[1]);
-                O[2] = mma(qf[2], sb * fh(kFhP2), O[2]);
-                O[3] = mma(qf[3], sb * fh(kFhP3), O[3]);
-                const Frag fi = fh(kFhInv + cw);
+                O[1] = mma(qf[1], sb * fac_frag(fw[0], m), O[1]);
+                O[2] = mma(qf[2], sb * fac_frag(fw[1], m), O[2]);
+                O[3] = mma(qf[3], sb * fac_frag(fw[2], m), O[3]);
+                const Frag fi = fac_frag(fw[3], m);
                 switch (cw) {
                     case 0: {
                         const Frag k0 = kf(0), k2 = kf(2);
@@ -1530,8 +1568,8 @@ __global__ __launch_bounds__(512, 1) void chunk_output_ws_kernel(KArgs a) {
                     case 1: {
                         const Frag k1 = kf(1), k0 = kf(0);
                         Pd[0] = mma(k1 * fi, qf[1], Pd[0]);
-                        Pd[1] = mma(k0, qf[2] * fh(kFhA1), Pd[1]);
-                        Pd[2] = mma(k1, qf[3] * fh(kFhA2), Pd[2]);
+                        Pd[1] = mma(k0, qf[2] * fac_frag(fw[4], m), Pd[1]);
+                        Pd[2] = mma(k1, qf[3] * fac_frag(fw[5], m), Pd[2]);
                         break;
                     }
                     case 2: {
@@ -1543,7 +1581,7 @@ __global__ __launch_bounds__(512, 1) void chunk_output_ws_kernel(KArgs a) {
                     default: {
                         const Frag k3 = kf(3), k0 = kf(0);
                         Pd[0] = mma(k3 * fi, qf[3], Pd[0]);
-                        Pd[1] = mma(k0, qf[3] * fh(kFhA12), Pd[1]);
+                        Pd[1] = mma(k0, qf[3] * fac_frag(fw[4], m), Pd[1]);
                         break;
                     }
                 }
@@ -1687,10 +1725,19 @@ __global__ __launch_bounds__(512, 1) void chunk_output_ws_kernel(KArgs a) {
         }
         {
             f32x4 acc[C::NBD];
+            // fp16 per-channel path: lane (g, c16) loads the tile decays of rows 16 n + 4 g + e,
+            // n = c16 >> 1, e = 2 (c16 & 1) + {0, 1}; row broadcasts hand them to the row's lanes
+            f32x2 atw{0.f, 0.f};
+            if constexpr (C::CH && !C::F32)
+                atw = lds_ld<f32x2>(sAt + 16 * ((c16 >> 1) & (C::NBD - 1)) + 4 * g + 2 * (c16 & 1));
 #pragma unroll
             for (int n = 0; n < C::NBD; ++n) {
                 f32x4 at;
-                if constexpr (C::CH) {
+                if constexpr (C::CH && !C::F32) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        at[e] = __uint_as_float(row_bcast(__float_as_uint(atw[e & 1]), 2 * n + (e >> 1)));
+                } else if constexpr (C::CH) {
                     at = lds_ld<f32x4>(sAt + 16 * n + 4 * g);
                 } else {
                     const float x = fexp2(sAb[63]);
