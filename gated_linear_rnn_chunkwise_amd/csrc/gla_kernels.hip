@@ -1171,6 +1171,19 @@ struct ProdVals {
     float ag[C::CPL];                    // per-channel gate: decay across this block
 };
 
+// q and k rows of block pw into the buffers at sQ, sK.
+template <class C>
+__device__ __forceinline__ void ws_store_qk(const ProdVals<C> &pv, typename C::OpT *sQ, typename C::OpT *sK,
+                                            int pw, int lane) {
+    const int pc = chperm(C::CPL * lane);  // rows hold channels in chperm order
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) {
+        const int row = 16 * pw + rr;
+        st_packed<C>(sQ + row * C::RP + pc, pv.qd[rr]);
+        st_packed<C>(sK + row * C::RP + pc, pv.ko[rr]);
+    }
+}
+
 // Exact diagonal-block partial scores of block pw when some of its channels decay too
 // strongly across the block for scaled fp16 operands (rare; kept out of line so the common
 // path keeps its registers).  For every pair s <= t of the block: the sum over the
@@ -1270,7 +1283,7 @@ __device__ __forceinline__ void ws_produce_a(ProdVals<C> &pv, Raw<C> &raw, const
             fi[c] = hc ? 0.f : frcp(ag);
             // block decays scale q and k fragments: stored in the rows' chperm channel order
             sAb[pw * C::SLAB + chperm(ch0 + c)] = ag;
-            sAi[pw * C::SLAB + chperm(ch0 + c)] = fi[c];
+            if constexpr (C::F32) sAi[pw * C::SLAB + chperm(ch0 + c)] = fi[c];
         }
         {
             OpT *sF = reinterpret_cast<OpT *>(buf + lp.fh);
@@ -1298,6 +1311,7 @@ __device__ __forceinline__ void ws_produce_a(ProdVals<C> &pv, Raw<C> &raw, const
             pv.ko[rr] = pack_ops<C>(ko);
         }
         load_p_qk<C>(raw, rs, Tn, pw, lane);
+        if (lp.qkd) ws_store_qk<C>(pv, reinterpret_cast<OpT *>(buf + lp.q), reinterpret_cast<OpT *>(buf + lp.k), pw, lane);
     } else {
         // scalar gates: running log2 decay over the tile's rows (lane = row); rows past the
         // sequence end carry no decay (a fixed per-head gate is loaded for them too)
@@ -1336,6 +1350,7 @@ __device__ __forceinline__ void ws_produce_a(ProdVals<C> &pv, Raw<C> &raw, const
                 *reinterpret_cast<Half *>(sKT + kt_off<C>(ch0 + c, kslot(16 * pw + 4 * g4))) = kt4[c];
         }
         load_p_qk<C>(raw, rs, Tn, pw, lane);
+        if (lp.qkd) ws_store_qk<C>(pv, reinterpret_cast<OpT *>(buf + lp.q), reinterpret_cast<OpT *>(buf + lp.k), pw, lane);
     }
 }
 
@@ -1349,14 +1364,7 @@ __device__ __forceinline__ void ws_produce_b(const ProdVals<C> &pv, const LdsPla
     using Half = typename C::Half;
     const int ch0 = C::CPL * lane;
     const int pc = chperm(ch0);  // rows hold channels in chperm order
-    OpT *sQ = reinterpret_cast<OpT *>(smem + lp.q);
-    OpT *sK = reinterpret_cast<OpT *>(smem + lp.k);
-#pragma unroll
-    for (int rr = 0; rr < 16; ++rr) {
-        const int row = 16 * pw + rr;
-        st_packed<C>(sQ + row * C::RP + pc, pv.qd[rr]);
-        st_packed<C>(sK + row * C::RP + pc, pv.ko[rr]);
-    }
+    if (!lp.qkd) ws_store_qk<C>(pv, reinterpret_cast<OpT *>(smem + lp.q), reinterpret_cast<OpT *>(smem + lp.k), pw, lane);
     if constexpr (C::CH) {
         unsigned char *buf = smem + lp.dbl + (uint32_t)nb * lp.dstride;
         const float *sAb = reinterpret_cast<const float *>(buf + lp.ab);
@@ -1460,8 +1468,6 @@ __global__ __launch_bounds__(512, 1) void chunk_output_ws_kernel(KArgs a) {
     // ================================ consumers
     const int cw = w;
     const int col = dv0 + 16 * cw + c16;
-    const OpT *sQ = reinterpret_cast<const OpT *>(smem + lp.q);
-    const OpT *sK = reinterpret_cast<const OpT *>(smem + lp.k);
     OpT *sP = reinterpret_cast<OpT *>(smem + lp.pbuf);
 
     f32x4 S[C::NBD];
@@ -1495,6 +1501,9 @@ __global__ __launch_bounds__(512, 1) void chunk_output_ws_kernel(KArgs a) {
     for (int kc = 0; kc < nch; ++kc) {
         const int b = kc & 1;
         const int T0 = t_begin + kTile * kc;
+        const unsigned char *qkbase = lp.qkd ? smem + lp.dbl + b * lp.dstride : smem;
+        const OpT *sQ = reinterpret_cast<const OpT *>(qkbase + lp.q);
+        const OpT *sK = reinterpret_cast<const OpT *>(qkbase + lp.k);
         const OpT *sKT = reinterpret_cast<const OpT *>(smem + (lp.dbl + (b) * lp.dstride + lp.kst));
         const OpT *sV = reinterpret_cast<const OpT *>(smem + (lp.dbl + (b) * lp.dstride + lp.vb));
         const float *sAb = reinterpret_cast<const float *>(smem + (lp.dbl + (b) * lp.dstride + lp.ab));

@@ -130,18 +130,20 @@ enum : int {
 };
 
 struct LdsPlanWs {
-    uint32_t q, k;  // [64][rp] single buffers, channels in the chperm order
+    uint32_t q, k;  // [64][rp], channels in the chperm order: inside each double buffer (fp16
+                    // operands, qkd = 1) or single buffers at the front (fp32 operands)
+    uint32_t qkd;
     // double-buffered block: buffer b starts at dbl + b * dstride; offsets inside a buffer:
     uint32_t dbl, dstride;
     uint32_t kst;   // [slab][ktp]
     uint32_t vb;    // [4096] value tile
     uint32_t ab;    // [4][slab] fp32 decay across each 16-token block, channels in chperm order (per-channel); [64] log2 running
                     //           decay of each row (scalar gates)
-    uint32_t ainv;  // [4][slab] fp32 1/decay of each block, 0 for channels handled exactly, chperm order (per-channel);
-                    //           [64] log2 input gate of each row (scalar gates)
+    uint32_t ainv;  // fp32 operands: [4][slab] 1/decay of each block, 0 for channels handled exactly, chperm order
+                    //           (per-channel); [64] log2 input gate of each row (scalar gates)
     uint32_t at;    // [slab] fp32 decay across the tile (per-channel)
     uint32_t xact;  // [4 blocks][136] fp32 exact diagonal-block partial scores
-    uint32_t xflag; // [4] int32: partial present
+    uint32_t xflag; // [4] int32: partial present (right after xact)
     uint32_t fh;    // [10][slab] per-channel gate factors in operand precision, chperm order:
                     //           rows kFh* below
     uint32_t pbuf;  // [4096] masked score tile
@@ -157,12 +159,15 @@ GLA_HD inline LdsPlanWs lds_plan_ws(int opb, int dk) {
     const uint32_t a64 = 64u * (uint32_t)rp * (uint32_t)opb;
     auto al = [](uint32_t x) { return (x + 255u) & ~255u; };
     LdsPlanWs p{};
-    uint32_t off = 0;
-    p.q = off;
-    off += al(a64);
-    p.k = off;
-    off += al(a64);
-    uint32_t in = 0;
+    // fp16 operands: q and k double-buffered (the producers write a chunk's rows while the
+    // consumers read the previous chunk's), which fills the 160 KB exactly for Dk = 128
+    p.qkd = opb == 2 ? 1u : 0u;
+    uint32_t off = 0, in = 0;
+    uint32_t &qk = p.qkd ? in : off;
+    p.q = qk;
+    qk += al(a64);
+    p.k = qk;
+    qk += al(a64);
     p.kst = in;
     in += al((uint32_t)slab * (uint32_t)ktp * (uint32_t)opb);
     p.vb = in;
@@ -170,13 +175,12 @@ GLA_HD inline LdsPlanWs lds_plan_ws(int opb, int dk) {
     p.ab = in;
     in += al(4u * (uint32_t)slab * 4u);
     p.ainv = in;
-    in += al(4u * (uint32_t)slab * 4u);
+    in += al(p.qkd ? 64u * 4u : 4u * (uint32_t)slab * 4u);
     p.at = in;
     in += al((uint32_t)slab * 4u);
     p.xact = in;
-    in += al(4u * 136u * 4u);
-    p.xflag = in;
-    in += al(4u * 4u);
+    p.xflag = in + 4u * 136u * 4u;
+    in += al(4u * 136u * 4u + 4u * 4u);
     p.fh = in;
     in += al((uint32_t)kFhRows * (uint32_t)slab * (uint32_t)opb);
     p.dbl = off;
