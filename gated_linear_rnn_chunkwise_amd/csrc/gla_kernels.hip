@@ -1233,10 +1233,6 @@ __device__ __forceinline__ void ws_produce_a(ProdVals<C> &pv, Raw<C> &raw, const
     OpT *sKT = reinterpret_cast<OpT *>(buf + lp.kst);
     float *sAb = reinterpret_cast<float *>(buf + lp.ab);
     float *sAi = reinterpret_cast<float *>(buf + lp.ainv);
-    v_to_lds<C>(raw, reinterpret_cast<OpT *>(buf + lp.vb), 64 * pw + lane);
-    load_p_v<C>(raw, rs, Tn, pw, lane, dv0, Dv);
-    __builtin_amdgcn_sched_barrier(0);
-
     float ig[16];
     {
         const float y = raw.lis * kLog2e;
@@ -1449,7 +1445,8 @@ __global__ __launch_bounds__(512, 1) void chunk_output_ws_kernel(KArgs a) {
         // chunks ahead reads rows past the (batch, head) extent as zero through the buffer
         // range check.  Conditional loads would make the compiler merge register copies
         // that wait for the whole prefetch as soon as it is issued.
-        load_unit_p<C>(raw, rs, t_begin, pw, lane, dv0, Dv);
+        load_p_qk<C>(raw, rs, t_begin, pw, lane);
+        load_p_gates<C>(raw, rs, t_begin, pw, lane);
         ws_produce_a<C>(pv, raw, lp, smem, 0, pw, lane, LI, t_begin + lane < L, rs, t_begin + kTile, dv0, Dv);
         lds_barrier();  // block decays of chunk 0 published
         ws_produce_b<C>(pv, lp, smem, 0, pw, lane);
@@ -1484,6 +1481,12 @@ __global__ __launch_bounds__(512, 1) void chunk_output_ws_kernel(KArgs a) {
             S[n][e] = x;
         }
     }
+    // values: the consumers stage them (chunk k + 1 into buffer (k + 1) & 1 while working on
+    // chunk k), one prefetched chunk in registers
+    Raw<C> vraw;
+    load_p_v<C>(vraw, rs, t_begin, cw, lane, dv0, Dv);
+    v_to_lds<C>(vraw, reinterpret_cast<OpT *>(smem + lp.dbl + lp.vb), 64 * cw + lane);
+    load_p_v<C>(vraw, rs, t_begin + kTile, cw, lane, dv0, Dv);
     lds_barrier();  // producers: block decays of chunk 0 published
     lds_barrier();  // chunk 0 prepared
 
@@ -1510,6 +1513,9 @@ __global__ __launch_bounds__(512, 1) void chunk_output_ws_kernel(KArgs a) {
         const float *sAi = reinterpret_cast<const float *>(smem + (lp.dbl + (b) * lp.dstride + lp.ainv));
         const float *sAt = reinterpret_cast<const float *>(smem + (lp.dbl + (b) * lp.dstride + lp.at));
         const OpT *sF = reinterpret_cast<const OpT *>(smem + (lp.dbl + (b) * lp.dstride + lp.fh));
+
+        v_to_lds<C>(vraw, reinterpret_cast<OpT *>(smem + lp.dbl + (b ^ 1) * lp.dstride + lp.vb), 64 * cw + lane);
+        load_p_v<C>(vraw, rs, T0 + 2 * kTile, cw, lane, dv0, Dv);
 
         // ---------------- phase A: score blocks P^T(j, i) over the key channels and the
         // inter-chunk term, sharing the q fragments.  Per-channel gate: the queries of block i
