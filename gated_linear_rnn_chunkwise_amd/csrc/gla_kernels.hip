@@ -1065,15 +1065,18 @@ __global__ __launch_bounds__(256, 1) void chunk_output_kernel(KArgs a) {
 // products of chunk k; every SIMD holds one producer and one consumer wave, so the
 // vector-ALU gate work and the matrix-core work of neighbouring chunks overlap.  Two
 // barriers per chunk:
-//   phase A  consumers: score blocks and inter-chunk term of chunk k (q, k single buffers)
-//            producers: gates of chunk k+1 (block decays, exact partial scores, values and,
-//            for scalar gates, keys^T into buffer (k+1)&1); loads of chunk k+2
+//   phase A  consumers: score blocks and inter-chunk term of chunk k; values of chunk k+1
+//            from registers into buffer (k+1)&1, loads of the values of chunk k+2
+//            producers: gates of chunk k+1 (block decays, factors, exact partial scores
+//            and, for scalar gates, keys^T into buffer (k+1)&1); fp16 operands: q, k of
+//            chunk k+1 into buffer (k+1)&1; loads of chunk k+2
 //   B1
-//   phase B  consumers: scores x values, state update (buffer k&1), output store
-//            producers: q, k of chunk k+1 into the single buffers; per-channel gate: keys^T
-//            scaled to the chunk end and the chunk decay into buffer (k+1)&1 (they need the
-//            decays of all four blocks, published before B1)
-//   B2
+//   phase B  consumers: scores x values, state update (buffer k&1), output staging
+//            producers: fp32 operands: q, k of chunk k+1 into the single buffers;
+//            per-channel gate: keys^T scaled to the chunk end, the chunk decay and the
+//            products of block decays into buffer (k+1)&1 (they need the decays of all
+//            four blocks, published before B1)
+//   B2       consumers: staged output tile to memory
 // Producer lane mapping: producer wave pw owns the 16-row block pw; lane l owns channels
 // CPL*l .. +CPL-1, so every load instruction covers whole rows of q, k and the gates, and a
 // lane walks its block's 16 rows for the running decay products.
