@@ -150,6 +150,75 @@ def copy_probe(torch, steps):
     print(json.dumps({"copy_probe_bytes_per_launch": COPY_PROBE_BYTES, "launches": max(steps, 1)}), flush=True)
 
 
+def decode_bench(args, torch, gla, gin, w, wname):
+    """``--decode``: the recurrent step entry point (one token for every (batch, head), state
+    updated in place) on the workload's head shape.  A step is one ``gla_step`` call; the
+    roofline counts the state read and written once, the token's q, k, v and gates read and
+    its fp32 output written."""
+    import ctypes
+
+    lib = gla.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    B, H, Dk, Dv = w.B, w.H, w.Dk, w.Dv
+    sets = []
+    for i in range(2):
+        # one token of the workload's recipe (its L dimension dropped)
+        d = gin.make_inputs(w.with_(L=1), seed=args.seed + i)
+        sq = lambda t: None if t is None else (t if t.dim() == 1 else t.select(2, 0)).contiguous().to(dev)
+        sets.append((sq(d["q"]), sq(d["k"]), sq(d["v"]), sq(d["log_alpha"]), sq(d["log_ig"])))
+    state = [torch.zeros(B, H, Dk, Dv, dtype=torch.float32, device=dev) for _ in range(2)]
+    out = torch.empty(B, H, Dv, dtype=torch.float32, device=dev)
+    descs = [gla.make_step_desc(q, k, v, state[i], out, la, li) for i, (q, k, v, la, li) in enumerate(sets)]
+    stream = torch.cuda.current_stream(dev)
+    sptr = ctypes.c_void_p(stream.cuda_stream)
+
+    def step(i):
+        st = lib.gla_step(ctypes.byref(descs[i & 1]), sptr)
+        if st != 0:
+            raise gla.GlaError(st, "gla_step")
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    K = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    t0 = time.perf_counter()
+    for i in range(K):
+        ev[i][0].record(stream)
+        step(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / K
+    mean_launch_ms = sum(a.elapsed_time(b) for a, b in ev) / K
+    ib = 4 if w.dtype == "f32" else 2
+    gate = {"channel": 4 * Dk, "head": 4, "head_const": 0, "none": 0}[w.gate] + (4 if w.input_gate else 0)
+    nbytes = float(B * H) * (2.0 * 4 * Dk * Dv + ib * (2 * Dk + Dv) + gate + 4 * Dv)
+    achieved = nbytes / (mean_launch_ms * 1e-3) / 1e9
+    rec = {
+        "metric": "gla_step decode tokens/s (one token per sequence per step)",
+        "value": B / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": wname + "_decode", "B": B, "H": H, "Dk": Dk, "Dv": Dv, "gate": w.gate,
+                   "input_gate": w.input_gate, "in_dtype": w.dtype, "state_dtype": "fp32"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None, "kernel": "step kernel",
+                     "algorithmic_bytes_per_launch": nbytes, "mean_launch_ms": round(mean_launch_ms, 6)},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -163,6 +232,8 @@ def main():
                     help="chunks > 64 tokens in the tile-pair (tiled large-chunk) form")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain device copy of known size (HBM counter calibration)")
+    ap.add_argument("--decode", action="store_true",
+                    help="time the recurrent step entry point (one token per sequence) on the workload's heads")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -181,6 +252,9 @@ def main():
 
     wname = args.workload or gin.HEADLINE
     w = gin.WORKLOADS[wname]
+    if args.decode:
+        decode_bench(args, torch, gla, gin, w, wname)
+        return
     lib = gla.load()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
