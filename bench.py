@@ -144,10 +144,20 @@ def copy_probe(torch, steps):
     n = COPY_PROBE_BYTES // 4
     src = [torch.rand(n, device=dev) for _ in range(2)]
     dst = torch.empty(n, device=dev)
+    ms = []
     for i in range(max(steps, 1)):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
         dst.copy_(src[i & 1])
+        e1.record()
+        ms.append((e0, e1))
     torch.cuda.synchronize()
-    print(json.dumps({"copy_probe_bytes_per_launch": COPY_PROBE_BYTES, "launches": max(steps, 1)}), flush=True)
+    t = sorted(a.elapsed_time(b) for a, b in ms)
+    med = t[len(t) // 2]
+    # a copy reads and writes COPY_PROBE_BYTES: the rate a plain device copy reaches on this HBM
+    print(json.dumps({"copy_probe_bytes_per_launch": COPY_PROBE_BYTES, "launches": max(steps, 1),
+                      "median_launch_ms": round(med, 5),
+                      "copy_gbps_read_plus_write": round(2.0 * COPY_PROBE_BYTES / (med * 1e-3) / 1e9, 1)}), flush=True)
 
 
 def decode_bench(args, torch, gla, gin, w, wname):
