@@ -1081,8 +1081,9 @@ __global__ __launch_bounds__(256, 1) void chunk_output_kernel(KArgs a) {
 // CPL*l .. +CPL-1, so every load instruction covers whole rows of q, k and the gates, and a
 // lane walks its block's 16 rows for the running decay products.
 
-// The loads of one unit come in three groups, so that the producer can reissue each group
-// for the chunk after next as soon as it has consumed that group's registers.
+// The loads of one unit in three groups: the producers reissue the q/k and gate groups for
+// the chunk after next as soon as they have consumed those registers; the consumers load the
+// values (wave index in place of pw).
 template <class C>
 __device__ __forceinline__ void load_p_v(Raw<C> &r, const Rs &rs, int T0, int pw, int lane, int dv0, int Dv) {
     const int tp = 64 * pw + lane;
@@ -1139,12 +1140,6 @@ __device__ __forceinline__ void load_p_qk(Raw<C> &r, const Rs &rs, int T0, int p
             r.k[rr] = __builtin_amdgcn_raw_buffer_load_b16(rs.k, (int)off, 0, 0);
         }
     }
-}
-template <class C>
-__device__ __forceinline__ void load_unit_p(Raw<C> &r, const Rs &rs, int T0, int pw, int lane, int dv0, int Dv) {
-    load_p_qk<C>(r, rs, T0, pw, lane);
-    load_p_gates<C>(r, rs, T0, pw, lane);
-    load_p_v<C>(r, rs, T0, pw, lane, dv0, Dv);
 }
 
 // CPL operands of one row packed into 32 bits (fp16 pair / one fp16 / one fp32).

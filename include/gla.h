@@ -24,7 +24,8 @@
  * Numbers.  q, k, v are bf16 or fp32; gates are fp32 natural logs; the output, the
  * states and all accumulation are fp32.  With bf16 inputs the products that involve a
  * computed operand (gate-rescaled q and k, the masked score matrix, the carried state)
- * take fp16 operands on the matrix cores; with fp32 inputs every operand stays fp32.
+ * take fp16 operands on the matrix cores, and per-channel decay factors are applied to
+ * those operands in fp16; with fp32 inputs every operand stays fp32.
  *
  * Layout and ownership.  Every tensor is dense, row-major and contiguous on the device,
  * with the shapes given below, and 16-byte aligned.  The caller owns all memory; the
