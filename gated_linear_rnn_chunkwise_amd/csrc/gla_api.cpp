@@ -25,7 +25,11 @@ hipError_t launch_step(const gla_step_desc &d, hipStream_t st);
 namespace {
 
 constexpr int kTargetWorkgroups = 256;     // one per compute unit on MI355X
-constexpr int kTargetStateWorkgroups = 768;  // the segment-state kernel fits three per compute unit
+// The segment-state kernel fits three workgroups per compute unit.  Its state grid is aimed at
+// about three per CU for scalar gates and two per CU for per-channel gates, whose gate work
+// per tile is heavier (measured on the RetNet and long-sequence GLA workloads: 3-4% apart).
+constexpr int kTargetStateWorkgroups = 768;
+constexpr int kTargetStateWorkgroupsChannel = 512;
 constexpr int64_t kSmallProblem = 65536;   // head-tokens below which segmenting does not pay
 
 struct Plan {
@@ -95,12 +99,13 @@ int make_plan(const gla_desc *d, Plan *p) {
     p->seg_len = sc * d->chunk;
     // Segment boundary states are sums of sub-segment states, computed by more workgroups
     // than there are boundaries: nsub (sub-segments of a segment, whose tile counts differ
-    // by at most one) brings the state grid nearest to kTargetStateWorkgroups.
+    // by at most one) brings the state grid nearest to its target.
     p->nsub = 1;
     if (p->nseg > 1) {
         const int64_t base = bh * (p->nseg - 1) * p->ndv;
         const int tiles = p->seg_len / gla::kTile;
-        const int64_t want = (kTargetStateWorkgroups + base / 2) / base;
+        const int64_t target = ch ? kTargetStateWorkgroupsChannel : kTargetStateWorkgroups;
+        const int64_t want = (target + base / 2) / base;
         p->nsub = (int)std::max<int64_t>(1, std::min<int64_t>(want, tiles));
     }
     const int64_t nss = int64_t(p->nseg - 1) * p->nsub;

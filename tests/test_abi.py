@@ -143,8 +143,8 @@ def test_caller_workspace_too_small(lib):
 def test_workspace_size_formula(lib):
     # segments: (B*H) * (nseg - 1) local states of Dk*Dv fp32 plus their Dk decays, 256-byte aligned
     # the state of each segment boundary is a sum of sub-segment states: the state grid
-    # (B*H * (nseg-1) * nsub * Dv/64) is brought nearest to 768 workgroups, with nsub at most
-    # the 64-token tiles per segment
+    # (B*H * (nseg-1) * nsub * Dv/64) is brought nearest to 512 workgroups for a per-channel
+    # gate (768 for scalar gates), with nsub at most the 64-token tiles per segment
     d = desc(B=2, H=2, L=4096, Dk=128, Dv=64, chunk=64, seg_chunks=16)
     p = gla.plan(d)
     assert p.n_seg == 4 and p.seg_chunks == 16
@@ -153,7 +153,9 @@ def test_workspace_size_formula(lib):
     al = lambda x: (x + 255) // 256 * 256
     assert p.workspace_bytes == al(4 * nss * 128 * 64 * 4) + al(4 * nss * 128 * 4)
     p2 = gla.plan(desc(B=1, H=16, L=32768, Dk=128, Dv=128, chunk=64))
-    assert p2.n_seg == 8 and p2.grid_state == 16 * 7 * 3 * 2  # 3 sub-segments of 21 or 22 tiles
+    assert p2.n_seg == 8 and p2.grid_state == 16 * 7 * 2 * 2  # 2 sub-segments of 32 tiles
+    p3 = gla.plan(desc(B=4, H=8, L=8192, Dk=128, Dv=128, chunk=128, gate_kind=gla.GATE_HEAD_CONST))
+    assert p3.n_seg == 4 and p3.grid_state == 32 * 3 * 4 * 2  # scalar gate: 4 sub-segments of 8 tiles
     assert gla.plan(desc(B=2, H=2, L=4096, seg_chunks=64)).workspace_bytes == 0
 
 
