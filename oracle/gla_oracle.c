@@ -111,6 +111,141 @@ int gla_oracle_recurrent(const double *q, const double *k, const double *v,
     return failed ? -1 : 0;
 }
 
+/* Gradients of the recurrence (reverse-mode differentiation of each step, in fp64).
+ *
+ * Given the forward inputs and the gradients of a scalar loss with respect to the outputs,
+ *   dO          [B, H, L, Dv]   d loss / d out
+ *   dS_fin      [B, H, Dk, Dv]  d loss / d final_state, or NULL (zero)
+ * it returns
+ *   dq, dk      [B, H, L, Dk]
+ *   dv          [B, H, L, Dv]
+ *   dlog_alpha  [B, H, L, Dk]   with respect to the per-channel log decay (the caller sums
+ *                               it over the broadcast axes of a scalar gate kind)
+ *   dlog_ig     [B, H, L]       or NULL
+ *   dS0         [B, H, Dk, Dv]  with respect to the initial state, or NULL
+ *
+ * Each step t is S_t = diag(a_t) S_{t-1} + i_t k_t^T v_t, o_t = q_t S_t, with
+ * a_t = exp(log_alpha_t), i_t = exp(log_ig_t).  Walking t from L-1 down to 0 with
+ * G = d loss / d S_t (starting from dS_fin):
+ *   G += q_t^T dO_t                       (the read o_t = q_t S_t)
+ *   dq_t = dO_t S_t^T
+ *   dk_t = i_t G v_t^T,   dv_t = i_t k_t G
+ *   dlog_ig_t = i_t k_t G v_t^T
+ *   dlog_alpha_t[d] = a_t[d] sum_c G[d, c] S_{t-1}[d, c]
+ *   G <- diag(a_t) G                      (d loss / d S_{t-1})
+ * and dS0 is the final G.  The states S_{t-1} are recomputed from checkpoints every 64
+ * tokens (the same forward recurrence), so memory stays O((L/64 + 64) Dk Dv) per pair.
+ * Returns 0, or -1 on a bad size, a NULL required pointer or an allocation failure. */
+int gla_oracle_backward(const double *q, const double *k, const double *v, const double *log_alpha,
+                        const double *log_ig, const double *S0, const double *dO, const double *dS_fin,
+                        double *dq, double *dk, double *dv, double *dlog_alpha, double *dlog_ig,
+                        double *dS0, long B, long H, long L, long Dk, long Dv)
+{
+    if (!q || !k || !v || !log_alpha || !dO || !dq || !dk || !dv || !dlog_alpha) return -1;
+    if (B <= 0 || H <= 0 || L <= 0 || Dk <= 0 || Dv <= 0) return -1;
+    const long BH = B * H, M = Dk * Dv, CK = 64;
+    const long ncp = (L + CK - 1) / CK;
+    int failed = 0;
+
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long bh = 0; bh < BH; ++bh) {
+        /* cp[j] = state before token j*CK (j = 0..ncp-1); blk[u] = state after token j*CK+u */
+        double *cp = (double *)malloc(sizeof(double) * (size_t)(ncp * M));
+        double *blk = (double *)malloc(sizeof(double) * (size_t)(CK * M));
+        double *G = (double *)malloc(sizeof(double) * (size_t)M);
+        if (!cp || !blk || !G) {
+            free(cp);
+            free(blk);
+            free(G);
+#pragma omp atomic write
+            failed = 1;
+            continue;
+        }
+        const double *la = log_alpha + bh * L * Dk;
+        const double *li = log_ig ? log_ig + bh * L : NULL;
+        /* one forward step from Sp (state before t) into Sn */
+#define GLA_STEP(Sp, Sn, t)                                                                  \
+        do {                                                                                 \
+            const double *kt_ = k + (bh * L + (t)) * Dk, *vt_ = v + (bh * L + (t)) * Dv;     \
+            const double ig_ = li ? exp(li[(t)]) : 1.0;                                      \
+            for (long d = 0; d < Dk; ++d) {                                                  \
+                const double a_ = exp(la[(t) * Dk + d]), w_ = ig_ * kt_[d];                  \
+                for (long c = 0; c < Dv; ++c) (Sn)[d * Dv + c] = a_ * (Sp)[d * Dv + c] + w_ * vt_[c]; \
+            }                                                                                \
+        } while (0)
+        /* forward: checkpoints */
+        if (S0)
+            memcpy(cp, S0 + bh * M, sizeof(double) * (size_t)M);
+        else
+            memset(cp, 0, sizeof(double) * (size_t)M);
+        for (long j = 0; j < ncp; ++j) {
+            const long t0 = j * CK, t1 = t0 + CK < L ? t0 + CK : L;
+            const double *Sp = cp + j * M;
+            for (long t = t0; t < t1; ++t) {
+                double *Sn = blk + (t - t0) * M;
+                GLA_STEP(Sp, Sn, t);
+                Sp = Sn;
+            }
+            if (j + 1 < ncp) memcpy(cp + (j + 1) * M, Sp, sizeof(double) * (size_t)M);
+        }
+        /* reverse */
+        if (dS_fin)
+            memcpy(G, dS_fin + bh * M, sizeof(double) * (size_t)M);
+        else
+            memset(G, 0, sizeof(double) * (size_t)M);
+        for (long j = ncp - 1; j >= 0; --j) {
+            const long t0 = j * CK, t1 = t0 + CK < L ? t0 + CK : L;
+            {   /* states of this block, recomputed from its checkpoint */
+                const double *Sp = cp + j * M;
+                for (long t = t0; t < t1; ++t) {
+                    double *Sn = blk + (t - t0) * M;
+                    GLA_STEP(Sp, Sn, t);
+                    Sp = Sn;
+                }
+            }
+            for (long t = t1 - 1; t >= t0; --t) {
+                const double *St = blk + (t - t0) * M;
+                const double *Sprev = t > t0 ? blk + (t - 1 - t0) * M : cp + j * M;
+                const double *qt = q + (bh * L + t) * Dk, *kt = k + (bh * L + t) * Dk;
+                const double *vt = v + (bh * L + t) * Dv, *dOt = dO + (bh * L + t) * Dv;
+                const double ig = li ? exp(li[t]) : 1.0;
+                double *dqt = dq + (bh * L + t) * Dk, *dkt = dk + (bh * L + t) * Dk;
+                double *dvt = dv + (bh * L + t) * Dv, *dlat = dlog_alpha + (bh * L + t) * Dk;
+                for (long d = 0; d < Dk; ++d)
+                    for (long c = 0; c < Dv; ++c) G[d * Dv + c] += qt[d] * dOt[c];
+                double dli = 0.0;
+                for (long c = 0; c < Dv; ++c) dvt[c] = 0.0;
+                for (long d = 0; d < Dk; ++d) {
+                    double sq = 0.0, sk = 0.0, sa = 0.0;
+                    for (long c = 0; c < Dv; ++c) {
+                        sq += dOt[c] * St[d * Dv + c];
+                        sk += G[d * Dv + c] * vt[c];
+                        sa += G[d * Dv + c] * Sprev[d * Dv + c];
+                        dvt[c] += kt[d] * G[d * Dv + c];
+                    }
+                    const double a = exp(la[t * Dk + d]);
+                    dqt[d] = sq;
+                    dkt[d] = ig * sk;
+                    dli += kt[d] * sk;
+                    dlat[d] = a * sa;
+                }
+                for (long c = 0; c < Dv; ++c) dvt[c] *= ig;
+                if (dlog_ig) dlog_ig[bh * L + t] = ig * dli;
+                for (long d = 0; d < Dk; ++d) {
+                    const double a = exp(la[t * Dk + d]);
+                    for (long c = 0; c < Dv; ++c) G[d * Dv + c] *= a;
+                }
+            }
+        }
+#undef GLA_STEP
+        if (dS0) memcpy(dS0 + bh * M, G, sizeof(double) * (size_t)M);
+        free(cp);
+        free(blk);
+        free(G);
+    }
+    return failed ? -1 : 0;
+}
+
 /* Number of OpenMP threads the recurrence uses (1 without OpenMP). */
 int gla_oracle_threads(void)
 {

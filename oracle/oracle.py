@@ -21,6 +21,11 @@ Forms (all fp64, computed from the exact input values):
   Attention, abstract, for arbitrary chunk sizes].  Tiny inputs only.
 * :func:`bruteforce_ungated` -- causal sums ``o_t = sum_{s<=t} (q_t . k_s) v_s`` in
   Python loops, the textbook ungated case.  Tiny inputs only.
+* :func:`backward` -- gradients of a scalar loss through the recurrence: reverse-mode
+  differentiation of each step of the definition, in C.  The pages train these models
+  [talk summary, 7:36 "Challenges in Training Linear Attention"] but print no gradient;
+  the derivative of the definition is fixed by the definition itself, and the tests pin it
+  by finite differences.
 
 Gate kinds (how a stored gate broadcasts to the per-channel log decay):
 ``"none"`` (zero), ``"channel"`` ``[B,H,L,Dk]``, ``"head"`` ``[B,H,L]`` (one decay per
@@ -60,6 +65,8 @@ def load_library(path: str):
     dp = ctypes.POINTER(ctypes.c_double)
     lib.gla_oracle_recurrent.argtypes = [dp, dp, dp, dp, dp, dp, dp, dp] + [ctypes.c_long] * 5
     lib.gla_oracle_recurrent.restype = ctypes.c_int
+    lib.gla_oracle_backward.argtypes = [dp] * 14 + [ctypes.c_long] * 5
+    lib.gla_oracle_backward.restype = ctypes.c_int
     lib.gla_oracle_threads.restype = ctypes.c_int
     lib.gla_oracle_threads.argtypes = []
     return lib
@@ -136,6 +143,49 @@ def recurrent(q, k, v, gate_kind="none", log_alpha=None, log_ig=None, initial_st
     if rc != 0:
         raise RuntimeError("gla_oracle_recurrent failed (%d)" % rc)
     return out, fin
+
+
+def reduce_gate_grad(gate_kind: str, g: np.ndarray):
+    """Sum a per-channel log-decay gradient ``[B,H,L,Dk]`` over the axes a stored gate of
+    ``gate_kind`` is broadcast along (the adjoint of :func:`expand_gate`)."""
+    if gate_kind == "none":
+        return None
+    if gate_kind == "channel":
+        return g
+    if gate_kind == "head":
+        return g.sum(axis=3)
+    return g.sum(axis=(0, 2, 3))
+
+
+def backward(q, k, v, dout, gate_kind="none", log_alpha=None, log_ig=None, initial_state=None, dfinal=None,
+             lib=None):
+    """Gradients of a scalar loss through the recurrence, in C (reverse-mode differentiation
+    of each step; ``gla_oracle_backward``).  ``dout`` [B,H,L,Dv] and ``dfinal`` [B,H,Dk,Dv]
+    (or None) are the loss gradients with respect to the outputs.  Returns a dict with
+    ``dq``, ``dk`` [B,H,L,Dk], ``dv`` [B,H,L,Dv], ``dlog_alpha`` (the stored gate's layout,
+    None without a gate), ``dlog_ig`` [B,H,L] (None without an input gate) and
+    ``dinitial_state`` [B,H,Dk,Dv], all fp64."""
+    q64, k64, v64, do64 = _f64(q), _f64(k), _f64(v), _f64(dout)
+    B, H, L, Dk = q64.shape
+    Dv = v64.shape[-1]
+    assert k64.shape == q64.shape and v64.shape == (B, H, L, Dv) and do64.shape == (B, H, L, Dv)
+    la = expand_gate(gate_kind, log_alpha, B, H, L, Dk)
+    li = _f64(log_ig)
+    s0, dsf = _f64(initial_state), _f64(dfinal)
+    dq, dk = np.empty((B, H, L, Dk)), np.empty((B, H, L, Dk))
+    dv, dla = np.empty((B, H, L, Dv)), np.empty((B, H, L, Dk))
+    dli = np.empty((B, H, L)) if li is not None else None
+    ds0 = np.empty((B, H, Dk, Dv))
+    dp = ctypes.POINTER(ctypes.c_double)
+
+    def p(a):
+        return None if a is None else a.ctypes.data_as(dp)
+
+    rc = (lib or _load()).gla_oracle_backward(p(q64), p(k64), p(v64), p(la), p(li), p(s0), p(do64), p(dsf), p(dq),
+                                              p(dk), p(dv), p(dla), p(dli), p(ds0), B, H, L, Dk, Dv)
+    if rc != 0:
+        raise RuntimeError("gla_oracle_backward failed (%d)" % rc)
+    return dict(dq=dq, dk=dk, dv=dv, dlog_alpha=reduce_gate_grad(gate_kind, dla), dlog_ig=dli, dinitial_state=ds0)
 
 
 def parallel_form(q, k, v, gate_kind="none", log_alpha=None, log_ig=None, initial_state=None):
