@@ -29,8 +29,8 @@ FLAG_TILE_PAIRS = 1
 GATE_NAMES = {"none": GATE_NONE, "channel": GATE_CHANNEL, "head": GATE_HEAD, "head_const": GATE_HEAD_CONST}
 
 # Entry points declared in include/gla.h.
-EXPORTS = ("gla_fwd", "gla_fwd_ex", "gla_workspace_size", "gla_query_plan", "gla_step", "gla_status_string",
-           "gla_version")
+EXPORTS = ("gla_fwd", "gla_fwd_ex", "gla_workspace_size", "gla_query_plan", "gla_step", "gla_bwd",
+           "gla_bwd_workspace_size", "gla_status_string", "gla_version")
 
 
 class GlaDesc(ctypes.Structure):
@@ -61,6 +61,19 @@ class GlaStepDesc(ctypes.Structure):
         ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
         ("log_alpha", ctypes.c_void_p), ("log_ig", ctypes.c_void_p),
         ("state", ctypes.c_void_p), ("out", ctypes.c_void_p),
+    ]
+
+
+class GlaBwdDesc(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int32), ("H", ctypes.c_int32), ("L", ctypes.c_int32), ("Dk", ctypes.c_int32),
+        ("Dv", ctypes.c_int32), ("in_dtype", ctypes.c_int32), ("gate_kind", ctypes.c_int32),
+        ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+        ("log_alpha", ctypes.c_void_p), ("log_ig", ctypes.c_void_p), ("initial_state", ctypes.c_void_p),
+        ("dout", ctypes.c_void_p), ("dfinal_state", ctypes.c_void_p),
+        ("dq", ctypes.c_void_p), ("dk", ctypes.c_void_p), ("dv", ctypes.c_void_p),
+        ("dlog_alpha", ctypes.c_void_p), ("dlog_ig", ctypes.c_void_p), ("dinitial_state", ctypes.c_void_p),
+        ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
     ]
 
 
@@ -95,6 +108,10 @@ def load(path: str = LIB_PATH):
         lib.gla_query_plan.restype = i32
         lib.gla_step.argtypes = [ctypes.POINTER(GlaStepDesc), vp]
         lib.gla_step.restype = i32
+        lib.gla_bwd.argtypes = [ctypes.POINTER(GlaBwdDesc), vp]
+        lib.gla_bwd.restype = i32
+        lib.gla_bwd_workspace_size.argtypes = [ctypes.POINTER(GlaBwdDesc), ctypes.POINTER(ctypes.c_size_t)]
+        lib.gla_bwd_workspace_size.restype = i32
         lib.gla_status_string.argtypes = [i32]
         lib.gla_status_string.restype = ctypes.c_char_p
         lib.gla_version.argtypes = []
@@ -196,6 +213,59 @@ def fwd(q, k, v, log_alpha=None, *, log_ig=None, initial_state=None, chunk: int 
     if st != GLA_OK:
         raise GlaError(st, "gla_fwd_ex")
     return out, fin
+
+
+def make_bwd_desc(q, k, v, dout, dq, dk, dv, log_alpha=None, log_ig=None, initial_state=None, dfinal_state=None,
+                  dlog_alpha=None, dlog_ig=None, dinitial_state=None, workspace=None, workspace_bytes=0,
+                  gate_kind=None) -> GlaBwdDesc:
+    """Fill a :class:`GlaBwdDesc` from tensors (shapes read from q and v)."""
+    import torch
+
+    B, H, L, Dk = q.shape
+    Dv = v.shape[-1]
+    d = GlaBwdDesc()
+    d.B, d.H, d.L, d.Dk, d.Dv = B, H, L, Dk, Dv
+    if q.dtype == torch.bfloat16:
+        d.in_dtype = DTYPE_BF16
+    elif q.dtype == torch.float32:
+        d.in_dtype = DTYPE_F32
+    else:
+        raise TypeError("q, k, v must be bf16 or fp32, got %s" % q.dtype)
+    d.gate_kind = gate_kind_of(log_alpha, B, H, L, Dk) if gate_kind is None else int(gate_kind)
+    d.q, d.k, d.v = _ptr(q), _ptr(k), _ptr(v)
+    d.log_alpha, d.log_ig, d.initial_state = _ptr(log_alpha), _ptr(log_ig), _ptr(initial_state)
+    d.dout, d.dfinal_state = _ptr(dout), _ptr(dfinal_state)
+    d.dq, d.dk, d.dv = _ptr(dq), _ptr(dk), _ptr(dv)
+    d.dlog_alpha, d.dlog_ig, d.dinitial_state = _ptr(dlog_alpha), _ptr(dlog_ig), _ptr(dinitial_state)
+    d.workspace = _ptr(workspace) if workspace is not None else None
+    d.workspace_bytes = int(workspace_bytes)
+    return d
+
+
+def bwd(q, k, v, dout, log_alpha=None, *, log_ig=None, initial_state=None, dfinal_state=None, stream=None):
+    """Gradients of the forward pass on the current HIP stream (scalar gate kinds or none).
+
+    ``dout`` [B,H,L,Dv] and ``dfinal_state`` [B,H,Dk,Dv] (or None) are fp32 loss gradients
+    with respect to the outputs.  Returns a dict of fp32 tensors: ``dq``, ``dk``, ``dv``,
+    ``dlog_alpha`` (layout of ``log_alpha``; None without a gate), ``dlog_ig`` (None without
+    an input gate) and ``dinitial_state``."""
+    import torch
+
+    lib = load()
+    B, H, L, Dk = q.shape
+    Dv = v.shape[-1]
+    f = dict(dtype=torch.float32, device=q.device)
+    dq, dk, dv = torch.empty((B, H, L, Dk), **f), torch.empty((B, H, L, Dk), **f), torch.empty((B, H, L, Dv), **f)
+    dla = torch.empty(log_alpha.shape, **f) if log_alpha is not None else None
+    dli = torch.empty((B, H, L), **f) if log_ig is not None else None
+    ds0 = torch.empty((B, H, Dk, Dv), **f)
+    _check_tensors(q, k, v, log_alpha, log_ig, initial_state, dout, dfinal_state, dq, dk, dv, dla, dli, ds0)
+    d = make_bwd_desc(q, k, v, dout, dq, dk, dv, log_alpha, log_ig, initial_state, dfinal_state, dla, dli, ds0)
+    s = stream if stream is not None else torch.cuda.current_stream(q.device)
+    st = lib.gla_bwd(ctypes.byref(d), ctypes.c_void_p(s.cuda_stream))
+    if st != GLA_OK:
+        raise GlaError(st, "gla_bwd")
+    return dict(dq=dq, dk=dk, dv=dv, dlog_alpha=dla, dlog_ig=dli, dinitial_state=ds0)
 
 
 def fwd_headline(q, k, v, log_alpha, out, final_state, chunk: int = 64, stream=None) -> int:

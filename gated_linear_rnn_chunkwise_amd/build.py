@@ -1,8 +1,8 @@
 """Build the HIP library ``libgla.so`` in-tree for gfx950.
 
 Usage: ``python -m gated_linear_rnn_chunkwise_amd.build`` (or call :func:`build`).
-Every call compiles from source: the kernels (``csrc/gla_kernels.hip``) and the C ABI
-(``csrc/gla_api.cpp``) are compiled in parallel and linked into one shared library.
+Every call compiles from source: the kernels (``csrc/gla_kernels.hip``, ``csrc/gla_bwd.hip``) and
+the C ABI (``csrc/gla_api.cpp``) are compiled in parallel and linked into one shared library.
 """
 from __future__ import annotations
 
@@ -26,7 +26,7 @@ COMMON = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", INCLUDE, "-I", CSRC, "-Wall", "-Wno-unused-variable", "-Wno-unused-but-set-variable",
 ]
-SOURCES = ["gla_kernels.hip", "gla_api.cpp"]
+SOURCES = ["gla_kernels.hip", "gla_bwd.hip", "gla_api.cpp"]
 
 
 def _compile(src: str) -> str:

@@ -20,6 +20,12 @@
 namespace gla {
 hipError_t launch_forward(const KArgs &a, bool f32, int dk, hipStream_t st);
 hipError_t launch_step(const gla_step_desc &d, hipStream_t st);
+hipError_t bwd_reverse(const void *src, int dt, float *dst, int BH, int L, int D, hipStream_t st);
+hipError_t bwd_convert(const void *src, int dt, float *dst, size_t total, hipStream_t st);
+hipError_t bwd_gate(const float *la, int kind, float *dst, int BH, int H, int L, hipStream_t st);
+hipError_t bwd_transpose(const float *src, float *dst, int BH, int R, int C, hipStream_t st);
+hipError_t bwd_finish(const gla_bwd_desc &d, const float *oA, const float *oB, float *g, const float *finA,
+                      const float *finC, float *part, hipStream_t st);
 }
 
 namespace {
@@ -269,3 +275,188 @@ int gla_fwd(const void *q, const void *k, const void *v, const float *log_alpha,
 }
 
 }  // extern "C"
+
+// ------------------------------------------------------------------------------------
+// Backward pass: operand preparation, three chunkwise forward passes, and the reductions
+// (gla_bwd.hip has the method).
+
+namespace {
+
+bool bwd_dim_ok(int x) { return x == 64 || x == 128 || x == 256; }
+
+int validate_bwd(const gla_bwd_desc *d) {
+    if (!d || !d->q || !d->k || !d->v || !d->dout || !d->dq || !d->dk || !d->dv) return GLA_ERR_INVALID_ARG;
+    if (d->B <= 0 || d->H <= 0 || d->L <= 0 || d->Dk <= 0 || d->Dv <= 0) return GLA_ERR_INVALID_ARG;
+    if (d->in_dtype != GLA_DTYPE_BF16 && d->in_dtype != GLA_DTYPE_F32) return GLA_ERR_INVALID_ARG;
+    if (d->gate_kind < GLA_GATE_NONE || d->gate_kind > GLA_GATE_HEAD_CONST) return GLA_ERR_INVALID_ARG;
+    if ((d->gate_kind == GLA_GATE_NONE) != (d->log_alpha == nullptr)) return GLA_ERR_INVALID_ARG;
+    if (d->gate_kind == GLA_GATE_NONE && d->dlog_alpha) return GLA_ERR_INVALID_ARG;
+    if (d->dlog_ig && !d->log_ig) return GLA_ERR_INVALID_ARG;
+    const void *ptrs[] = {d->q, d->k, d->v, d->log_alpha, d->log_ig, d->initial_state, d->dout, d->dfinal_state,
+                          d->dq, d->dk, d->dv, d->dlog_alpha, d->dlog_ig, d->dinitial_state, d->workspace};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p)) return GLA_ERR_INVALID_ARG;
+    if (d->workspace && d->workspace_bytes == 0) return GLA_ERR_INVALID_ARG;
+    const int64_t lim = int64_t(1) << 40;
+    const int64_t bh = int64_t(d->B) * d->H;
+    if (bh > (int64_t(1) << 24)) return GLA_ERR_INVALID_ARG;
+    if (bh * d->L > lim / std::max(d->Dk, d->Dv)) return GLA_ERR_INVALID_ARG;
+    if (d->gate_kind == GLA_GATE_CHANNEL) return GLA_ERR_UNSUPPORTED;
+    if (!bwd_dim_ok(d->Dk) || !bwd_dim_ok(d->Dv)) return GLA_ERR_UNSUPPORTED;
+    return GLA_OK;
+}
+
+// The forward pass of one of the three backward passes (fp32 operands, 64-token chunks).
+gla_desc bwd_pass_desc(const gla_bwd_desc *d, int dk, int dv, const void *q, const void *k, const void *v,
+                       int gate_kind, const float *la, const float *li, const float *s0, float *out, float *fin) {
+    gla_desc f{};
+    f.B = d->B;
+    f.H = d->H;
+    f.L = d->L;
+    f.Dk = dk;
+    f.Dv = dv;
+    f.chunk = gla::kTile;
+    f.in_dtype = GLA_DTYPE_F32;
+    f.gate_kind = gate_kind;
+    f.q = q;
+    f.k = k;
+    f.v = v;
+    f.log_alpha = la;
+    f.log_ig = li;
+    f.initial_state = s0;
+    f.out = out;
+    f.final_state = fin;
+    return f;
+}
+
+struct BwdPlan {
+    size_t rq, rk, rv, rdo, kc, vc, lar, oA, oB, finA, finC, s0T, dfT, g, part, fws, total;
+    size_t fws_bytes;
+};
+
+// Scratch layout; offsets are 256-byte aligned.  Returns GLA_OK or the status of a forward
+// pass's own plan.
+int bwd_plan(const gla_bwd_desc *d, BwdPlan *p) {
+    const size_t bh = size_t(d->B) * d->H, L = size_t(d->L), Dk = size_t(d->Dk), Dv = size_t(d->Dv);
+    const bool bf = d->in_dtype == GLA_DTYPE_BF16;
+    const bool gate = d->gate_kind != GLA_GATE_NONE;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t o = off;
+        off += align256(bytes);
+        return o;
+    };
+    p->rq = take(bh * L * Dk * 4);
+    p->rk = take(bh * L * Dk * 4);
+    p->rv = take(bh * L * Dv * 4);
+    p->rdo = take(bh * L * Dv * 4);
+    p->kc = bf ? take(bh * L * Dv * 4) : 0;
+    p->vc = bf ? take(bh * L * Dk * 4) : 0;
+    p->lar = gate ? take(bh * L * 4) : 0;
+    p->oA = take(bh * L * Dv * 4);
+    p->oB = take(bh * L * Dk * 4);
+    p->finA = take(bh * Dk * Dv * 4);
+    p->finC = take(bh * Dk * Dv * 4);
+    p->s0T = d->initial_state ? take(bh * Dk * Dv * 4) : 0;
+    p->dfT = d->dfinal_state ? take(bh * Dk * Dv * 4) : 0;
+    p->g = gate ? take(bh * L * 4) : 0;
+    p->part = take(bh * 4);
+    // the forward passes run one after the other on the stream and share one workspace
+    const void *x = reinterpret_cast<const void *>(uintptr_t(256));
+    float *y = reinterpret_cast<float *>(uintptr_t(256));
+    const int rgate = gate ? GLA_GATE_HEAD : GLA_GATE_NONE;
+    const float *rla = gate ? y : nullptr;
+    gla_desc f[3] = {bwd_pass_desc(d, d->Dk, d->Dv, x, x, x, rgate, rla, nullptr, nullptr, y, y),
+                     bwd_pass_desc(d, d->Dv, d->Dk, x, x, x, rgate, rla, nullptr, nullptr, y, nullptr),
+                     bwd_pass_desc(d, d->Dv, d->Dk, x, x, x, d->gate_kind, d->log_alpha, d->log_ig, nullptr, y, y)};
+    size_t fw = 0;
+    for (const gla_desc &fd : f) {
+        size_t n = 0;
+        const int st = gla_workspace_size(&fd, &n);
+        if (st != GLA_OK) return st;
+        fw = std::max(fw, n);
+    }
+    p->fws_bytes = fw;
+    p->fws = take(fw);
+    p->total = off;
+    return GLA_OK;
+}
+
+}  // namespace
+
+int gla_bwd_workspace_size(const gla_bwd_desc *d, size_t *bytes) {
+    if (!bytes) return GLA_ERR_INVALID_ARG;
+    int st = validate_bwd(d);
+    if (st != GLA_OK) return st;
+    BwdPlan p;
+    if ((st = bwd_plan(d, &p)) != GLA_OK) return st;
+    *bytes = p.total;
+    return GLA_OK;
+}
+
+int gla_bwd(const gla_bwd_desc *d, void *stream) {
+    int st = validate_bwd(d);
+    if (st != GLA_OK) return st;
+    BwdPlan p;
+    if ((st = bwd_plan(d, &p)) != GLA_OK) return st;
+    if (d->workspace && d->workspace_bytes < p.total) return GLA_ERR_WORKSPACE;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    char *ws = reinterpret_cast<char *>(d->workspace);
+    bool owned = false;
+    if (!ws) {
+        void *m = nullptr;
+        if (hipMallocAsync(&m, p.total, s) != hipSuccess || !m) {
+            (void)hipGetLastError();
+            return GLA_ERR_WORKSPACE;
+        }
+        ws = reinterpret_cast<char *>(m);
+        owned = true;
+    }
+    auto F = [&](size_t off) { return reinterpret_cast<float *>(ws + off); };
+    const int BH = d->B * d->H, L = d->L, Dk = d->Dk, Dv = d->Dv, dt = d->in_dtype;
+    const bool gate = d->gate_kind != GLA_GATE_NONE;
+    const bool bf = dt == GLA_DTYPE_BF16;
+    int rc = GLA_OK;
+    auto ok = [&](hipError_t e) {
+        if (e != hipSuccess && rc == GLA_OK) rc = GLA_ERR_HIP;
+        return rc == GLA_OK;
+    };
+    auto fwd = [&](const gla_desc &f0) {
+        if (rc != GLA_OK) return false;
+        gla_desc f = f0;
+        f.workspace = p.fws_bytes ? ws + p.fws : nullptr;
+        f.workspace_bytes = p.fws_bytes;
+        const int r = gla_fwd_ex(&f, stream);
+        if (r != GLA_OK) rc = r;
+        return rc == GLA_OK;
+    };
+    // operands of the three passes
+    ok(gla::bwd_reverse(d->q, dt, F(p.rq), BH, L, Dk, s)) && ok(gla::bwd_reverse(d->k, dt, F(p.rk), BH, L, Dk, s)) &&
+        ok(gla::bwd_reverse(d->v, dt, F(p.rv), BH, L, Dv, s)) &&
+        ok(gla::bwd_reverse(d->dout, GLA_DTYPE_F32, F(p.rdo), BH, L, Dv, s));
+    if (bf) {
+        ok(gla::bwd_convert(d->v, dt, F(p.kc), size_t(BH) * L * Dv, s)) &&
+            ok(gla::bwd_convert(d->k, dt, F(p.vc), size_t(BH) * L * Dk, s));
+    }
+    if (gate) ok(gla::bwd_gate(d->log_alpha, d->gate_kind, F(p.lar), BH, d->H, L, s));
+    if (d->initial_state) ok(gla::bwd_transpose(d->initial_state, F(p.s0T), BH, Dk, Dv, s));
+    if (d->dfinal_state) ok(gla::bwd_transpose(d->dfinal_state, F(p.dfT), BH, Dk, Dv, s));
+    const int rgate = gate ? GLA_GATE_HEAD : GLA_GATE_NONE;
+    const float *rla = gate ? F(p.lar) : nullptr;
+    const void *kc = bf ? static_cast<const void *>(F(p.kc)) : d->v;
+    const void *vc = bf ? static_cast<const void *>(F(p.vc)) : d->k;
+    // dv (reversed; its final state is the gradient of the state after token 0)
+    fwd(bwd_pass_desc(d, Dk, Dv, F(p.rk), F(p.rq), F(p.rdo), rgate, rla, nullptr, d->dfinal_state, F(p.oA),
+                      F(p.finA)));
+    // dk (reversed, keys and values exchanged)
+    fwd(bwd_pass_desc(d, Dv, Dk, F(p.rv), F(p.rdo), F(p.rq), rgate, rla, nullptr,
+                      d->dfinal_state ? F(p.dfT) : nullptr, F(p.oB), nullptr));
+    // dq (keys and values exchanged; its final state is the forward final state, transposed)
+    fwd(bwd_pass_desc(d, Dv, Dk, d->dout, kc, vc, d->gate_kind, d->log_alpha, d->log_ig,
+                      d->initial_state ? F(p.s0T) : nullptr, d->dq, F(p.finC)));
+    if (rc == GLA_OK)
+        ok(gla::bwd_finish(*d, F(p.oA), F(p.oB), (gate && d->dlog_alpha) ? F(p.g) : nullptr, F(p.finA), F(p.finC),
+                           F(p.part), s));
+    if (owned) (void)hipFreeAsync(ws, s);
+    return rc;
+}

@@ -58,6 +58,15 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
 constexpr float kLog2e = 1.4426950408889634f;
+
+// log2 of a per-token decay for running sums in log space, floored at -150: below it the
+// fp32 factor 2^x is zero either way, and the floor keeps the running sums small enough
+// that differences of two of them keep fp32 precision (a gate of log -1e4 would otherwise
+// make them about 1.4e4 and cost two to three significant digits).  NaN passes through.
+__device__ __forceinline__ float log2_decay(float la) {
+    const float x = la * kLog2e;
+    return x < -150.f ? -150.f : x;
+}
 constexpr int kRsrcFlags = 0x00020000;  // raw buffer, 32-bit data format (gfx9 family)
 
 // ------------------------------------------------------------------------------------
@@ -505,7 +514,7 @@ __device__ __attribute__((noinline)) f32x4 ch_diag_exact(f32x4 acc, Raw<C> r, in
         float run = 0.f;
 #pragma unroll
         for (int rr = 0; rr < 16; ++rr) {
-            run += r.la[rr][c] * kLog2e;
+            run += log2_decay(r.la[rr][c]);
             u[rr][c] = run;
         }
     }
@@ -744,7 +753,7 @@ __global__ __launch_bounds__(256, 1) void chunk_output_kernel(KArgs a) {
                     }
                 } else {
                     // scalar gates: running log2 decay over the tile's rows (lane = row)
-                    const float x = raw.las * kLog2e;
+                    const float x = log2_decay(raw.las);
                     const float y = raw.lis * kLog2e;
                     const float bl = scan_incl(x, lane);
                     Tt = __shfl(bl, 63);
@@ -1195,7 +1204,7 @@ __device__ __attribute__((noinline)) void ws_exact_block(Raw<C> raw, float *dst,
         float run = 0.f, prod = 1.f;
 #pragma unroll
         for (int rr = 0; rr < 16; ++rr) {
-            run += raw.la[rr][c] * kLog2e;
+            run += log2_decay(raw.la[rr][c]);
             u[rr][c] = run;
             prod *= fexp2(raw.la[rr][c] * kLog2e);
         }
@@ -1311,7 +1320,7 @@ __device__ __forceinline__ void ws_produce_a(ProdVals<C> &pv, Raw<C> &raw, const
         // sequence end carry no decay (a fixed per-head gate is loaded for them too)
         float *sBr = sAb;  // [64] log2 running decay, row 63 = decay across the tile
         float *sLr = sAi;  // [64] log2 input gate
-        const float x = row_valid ? raw.las * kLog2e : 0.f;
+        const float x = row_valid ? log2_decay(raw.las) : 0.f;
         const float y = raw.lis * kLog2e;
         const float bl = scan_incl(x, lane);
         const float Tt = __shfl(bl, 63);
@@ -1864,7 +1873,7 @@ __device__ __forceinline__ void sg_produce_a(ProdSg<C> &pv, const RawSg<C> &raw,
         }
     }
     // running log2 decay over the tile's rows (lane = row) and the key weights
-    const float x = row_valid ? raw.las * kLog2e : 0.f;
+    const float x = row_valid ? log2_decay(raw.las) : 0.f;
     const float y = raw.lis * kLog2e;
     const float bl = scan_incl(x, lane);
     const float T = __shfl(bl, 63);
@@ -2231,7 +2240,7 @@ __global__ __launch_bounds__(256, 3) void segment_state_kernel(KArgs a) {
                         *reinterpret_cast<Half *>(sKT + kt_off<C>(chl + c, kslot(16 * w + 4 * g4))) = kt4[c];
                 }
             } else {
-                const float x = raw.las * kLog2e;
+                const float x = log2_decay(raw.las);
                 const float y = raw.lis * kLog2e;
                 const float bl = scan_incl(x, lane);
                 Tt = __shfl(bl, 63);

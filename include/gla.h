@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define GLA_VERSION 10200 /* major * 10000 + minor * 100 + patch */
+#define GLA_VERSION 10300 /* major * 10000 + minor * 100 + patch */
 
 /* Status codes.  0 is success; errors are negative. */
 enum gla_status {
@@ -181,6 +181,53 @@ typedef struct gla_step_desc {
  * The state must not alias q, k, v, the gates or the output.  Asynchronous on `stream`;
  * allocates nothing.  Returns a gla_status. */
 int gla_step(const gla_step_desc *d, void *stream);
+
+/* Gradients of the forward pass (the backward pass used in training [Hardware-Efficient
+ * Training of Linear Attention Models, talk summary, 7:36]): for a scalar loss with
+ * gradient dout = d loss / d out and dfinal_state = d loss / d final_state, the gradients
+ * with respect to q, k, v, the log gates and the initial state.  They follow from the
+ * definition by differentiating each step; computed chunkwise on the GPU.
+ *
+ * Method (scalar gate kinds): with G_t = d loss / d S_t, which obeys the same recurrence
+ * run backwards in time (G_t = q_t^T dout_t + diag(alpha_{t+1}) G_{t+1}, G_{L-1} starting
+ * from dfinal_state), dv_t = i_t k_t G_t, dk_t = i_t (G_t v_t^T)^T and dq_t = dout_t S_t^T;
+ * each is a chunkwise forward pass over re-ordered operands (time reversed for dv and dk,
+ * keys and values exchanged for dk and dq).  The log-gate gradients follow from
+ * d loss / d B_t = q_t . dq_t - k_t . dk_t (B_t the running sum of log decays; plus the
+ * final-state term at the last token) summed from t to the end, and dlog_ig_t = k_t . dk_t.
+ * The intermediate passes run with fp32 operands.
+ *
+ * Shapes: q, k [B,H,L,Dk] and v [B,H,L,Dv] in in_dtype; gates as in gla_desc; dout
+ * [B,H,L,Dv] fp32; dfinal_state [B,H,Dk,Dv] fp32 or NULL (zero); outputs fp32: dq, dk
+ * [B,H,L,Dk], dv [B,H,L,Dv], dlog_alpha in the layout of log_alpha (NULL iff gate_kind is
+ * NONE), dlog_ig [B,H,L] (may be non-NULL only with log_ig), dinitial_state [B,H,Dk,Dv] or
+ * NULL.  Outputs must not alias inputs or each other. */
+typedef struct gla_bwd_desc {
+    int32_t B, H, L, Dk, Dv;
+    int32_t in_dtype;             /* enum gla_dtype of q, k, v */
+    int32_t gate_kind;            /* enum gla_gate */
+    const void *q, *k, *v;
+    const float *log_alpha;       /* must be NULL iff gate_kind == NONE */
+    const float *log_ig;          /* [B, H, L] or NULL */
+    const float *initial_state;   /* [B, H, Dk, Dv] or NULL */
+    const float *dout;            /* [B, H, L, Dv] */
+    const float *dfinal_state;    /* [B, H, Dk, Dv] or NULL */
+    float *dq, *dk, *dv;
+    float *dlog_alpha;
+    float *dlog_ig;
+    float *dinitial_state;
+    void *workspace;              /* device scratch or NULL (allocated on the stream) */
+    size_t workspace_bytes;
+} gla_bwd_desc;
+
+/* Backward pass.  Support matrix (else GLA_ERR_UNSUPPORTED): gate_kind NONE, HEAD or
+ * HEAD_CONST (a per-channel gate needs the decay on the value side of two of the passes,
+ * which no kernel here computes); Dk and Dv in {64, 128, 256}; L as for gla_fwd_ex.
+ * Validation and asynchrony as for gla_fwd_ex.  Returns a gla_status. */
+int gla_bwd(const gla_bwd_desc *d, void *stream);
+
+/* Scratch bytes gla_bwd needs for `d` (no HIP call).  Returns a gla_status. */
+int gla_bwd_workspace_size(const gla_bwd_desc *d, size_t *bytes);
 
 /* Static English text for a status code (never NULL). */
 const char *gla_status_string(int status);

@@ -230,3 +230,49 @@ def test_step_gate_pointer_must_match_kind(lib):
 @pytest.mark.parametrize("kw", [dict(Dv=96), dict(Dv=4160), dict(Dk=4097)])
 def test_step_unsupported(lib, kw):
     assert lib.gla_step(ctypes.byref(step_desc(**kw)), None) == gla.GLA_ERR_UNSUPPORTED
+
+
+# ------------------------------------------------------------------------------ backward
+def bdesc(**kw):
+    d = gla.GlaBwdDesc()
+    base = dict(B=2, H=3, L=100, Dk=128, Dv=128, in_dtype=gla.DTYPE_BF16, gate_kind=gla.GATE_HEAD, q=A, k=A, v=A,
+                log_alpha=A, log_ig=None, initial_state=None, dout=A, dfinal_state=None, dq=A, dk=A, dv=A,
+                dlog_alpha=A, dlog_ig=None, dinitial_state=None, workspace=None, workspace_bytes=0)
+    base.update(kw)
+    for key, val in base.items():
+        setattr(d, key, val)
+    return d
+
+
+def bstatus(lib, d):
+    n = ctypes.c_size_t(0)
+    return lib.gla_bwd_workspace_size(ctypes.byref(d), ctypes.byref(n)), n.value
+
+
+def test_bwd_valid_and_workspace_grows_with_length(lib):
+    st, n1 = bstatus(lib, bdesc())
+    assert st == gla.GLA_OK and n1 > 0
+    st, n2 = bstatus(lib, bdesc(L=1000))
+    assert st == gla.GLA_OK and n2 > n1
+    for kind, la in ((gla.GATE_NONE, None), (gla.GATE_HEAD_CONST, A)):
+        st, _ = bstatus(lib, bdesc(gate_kind=kind, log_alpha=la, dlog_alpha=la))
+        assert st == gla.GLA_OK
+
+
+@pytest.mark.parametrize("kw", [dict(dq=None), dict(dout=None), dict(q=None), dict(L=0), dict(dq=A + 4),
+                                dict(gate_kind=gla.GATE_NONE, log_alpha=None),  # dlog_alpha without a gate
+                                dict(dlog_ig=A),                                  # input-gate grad without one
+                                dict(gate_kind=9), dict(in_dtype=7)])
+def test_bwd_invalid_arguments(lib, kw):
+    assert bstatus(lib, bdesc(**kw))[0] == gla.GLA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("kw", [dict(gate_kind=gla.GATE_CHANNEL), dict(Dk=100), dict(Dv=512), dict(Dk=32)])
+def test_bwd_unsupported(lib, kw):
+    assert bstatus(lib, bdesc(**kw))[0] == gla.GLA_ERR_UNSUPPORTED
+
+
+def test_bwd_rejects_small_workspace_before_launching(lib):
+    st, need = bstatus(lib, bdesc())
+    d = bdesc(workspace=A, workspace_bytes=need - 256)
+    assert lib.gla_bwd(ctypes.byref(d), None) == gla.GLA_ERR_WORKSPACE
