@@ -232,6 +232,95 @@ def decode_bench(args, torch, gla, gin, w, wname):
     print(json.dumps(rec), flush=True)
 
 
+def backward_bench(args, torch, gla, gin, w, wname):
+    """``--backward``: the gradients of one forward pass (``gla_bwd``) on the workload.  A
+    step is one call; the roofline counts the bytes a fused backward must move: q, k, v, the
+    gates and the fp32 output gradient read, the fp32 dq, dk, dv and gate gradients written,
+    plus the final-state gradient read and the initial-state gradient written."""
+    import ctypes
+
+    lib = gla.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    sets = []
+    for i in range(2):
+        d = gin.make_inputs(w, seed=args.seed + i)
+        g = torch.Generator().manual_seed(args.seed + 100 + i)
+        dout = torch.randn(w.B, w.H, w.L, w.Dv, generator=g)
+        dfin = torch.randn(w.B, w.H, w.Dk, w.Dv, generator=g) * 0.1
+        sets.append({k: (v.to(dev) if hasattr(v, "to") else v) for k, v in d.items() if v is not None})
+        sets[-1]["dout"], sets[-1]["dfin"] = dout.to(dev), dfin.to(dev)
+    f = dict(dtype=torch.float32, device=dev)
+    B, H, L, Dk, Dv = w.B, w.H, w.L, w.Dk, w.Dv
+    dq, dk, dv = torch.empty(B, H, L, Dk, **f), torch.empty(B, H, L, Dk, **f), torch.empty(B, H, L, Dv, **f)
+    ds0 = torch.empty(B, H, Dk, Dv, **f)
+    descs = []
+    for st in sets:
+        la, li = st.get("log_alpha"), st.get("log_ig")
+        dla = torch.empty(la.shape, **f) if la is not None else None
+        dli = torch.empty(li.shape, **f) if li is not None else None
+        st["dla"], st["dli"] = dla, dli
+        descs.append(gla.make_bwd_desc(st["q"], st["k"], st["v"], st["dout"], dq, dk, dv, la, li, None, st["dfin"],
+                                       dla, dli, ds0))
+    need = ctypes.c_size_t(0)
+    rc = lib.gla_bwd_workspace_size(ctypes.byref(descs[0]), ctypes.byref(need))
+    if rc != 0:
+        raise gla.GlaError(rc, "gla_bwd_workspace_size")
+    ws = torch.empty(need.value, dtype=torch.uint8, device=dev)
+    for dsc in descs:
+        dsc.workspace, dsc.workspace_bytes = ws.data_ptr(), need.value
+    stream = torch.cuda.current_stream(dev)
+    sptr = ctypes.c_void_p(stream.cuda_stream)
+
+    def step(i):
+        st = lib.gla_bwd(ctypes.byref(descs[i & 1]), sptr)
+        if st != 0:
+            raise gla.GlaError(st, "gla_bwd")
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    K = args.steps
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(K):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / K
+    mean_ms = e0.elapsed_time(e1) / K
+    ib = 4 if w.dtype == "f32" else 2
+    gate = {"channel": 4 * Dk, "head": 4, "head_const": 0, "none": 0}[w.gate] + (4 if w.input_gate else 0)
+    per_ht = ib * (2 * Dk + Dv) + gate + 4 * Dv + 4 * (2 * Dk + Dv) + gate
+    nbytes = float(B * H * L) * per_ht + 2.0 * B * H * Dk * Dv * 4
+    achieved = nbytes / (mean_ms * 1e-3) / 1e9
+    rec = {
+        "metric": "GLA backward tokens/s (gradients of one forward pass)",
+        "value": B * L / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": wname + "_backward", "B": B, "H": H, "L": L, "Dk": Dk, "Dv": Dv, "gate": w.gate,
+                   "input_gate": w.input_gate, "in_dtype": w.dtype,
+                   "pass_operands": "fp16 (scaled output gradient) and bf16" if w.dtype == "bf16" else "fp32"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "kernel": "whole backward (K calls between two events)",
+                     "algorithmic_bytes_per_launch": nbytes, "mean_launch_ms": round(mean_ms, 5)},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -245,6 +334,8 @@ def main():
                     help="chunks > 64 tokens in the tile-pair (tiled large-chunk) form")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain device copy of known size (HBM counter calibration)")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the backward pass (gla_bwd) of the workload (scalar gates or none)")
     ap.add_argument("--decode", action="store_true",
                     help="time the recurrent step entry point (one token per sequence) on the workload's heads")
     args = ap.parse_args()
@@ -267,6 +358,9 @@ def main():
     w = gin.WORKLOADS[wname]
     if args.decode:
         decode_bench(args, torch, gla, gin, w, wname)
+        return
+    if args.backward:
+        backward_bench(args, torch, gla, gin, w, wname)
         return
     lib = gla.load()
     dev = torch.device("cuda:0")

@@ -18,14 +18,19 @@
 #include "gla_layout.h"
 
 namespace gla {
-hipError_t launch_forward(const KArgs &a, bool f32, int dk, hipStream_t st);
+hipError_t launch_forward(const KArgs &a, bool f32, int h16, int dk, hipStream_t st);
 hipError_t launch_step(const gla_step_desc &d, hipStream_t st);
 hipError_t bwd_reverse(const void *src, int dt, float *dst, int BH, int L, int D, hipStream_t st);
-hipError_t bwd_convert(const void *src, int dt, float *dst, size_t total, hipStream_t st);
 hipError_t bwd_gate(const float *la, int kind, float *dst, int BH, int H, int L, hipStream_t st);
-hipError_t bwd_transpose(const float *src, float *dst, int BH, int R, int C, hipStream_t st);
+hipError_t bwd_transpose(const float *src, const uint32_t *mx, float *dst, int BH, int R, int C, hipStream_t st);
+size_t bwd_absmax_parts(int L, int Dv, int Dk, bool dfin);
+hipError_t bwd_dout16(const float *dout, const float *dfin, float *part, uint32_t *mx, _Float16 *fwd, _Float16 *rev,
+                      int BH, int L, int Dv, int Dk, hipStream_t st);
+hipError_t bwd_rev16(const void *src, void *dst, int BH, int L, int D, hipStream_t st);
+hipError_t bwd_scale(const float *src, const uint32_t *mx, float *dst, int BH, size_t m, hipStream_t st);
 hipError_t bwd_finish(const gla_bwd_desc &d, const float *oA, const float *oB, float *g, const float *finA,
-                      const float *finC, float *part, hipStream_t st);
+                      const float *finC, const float *dfT, float *part, const uint32_t *mx, hipStream_t st);
+constexpr int kH16Q = 1, kH16K = 2, kH16V = 4;  // fp16 operand bits of launch_forward
 }
 
 namespace {
@@ -187,7 +192,20 @@ int gla_query_plan(const gla_desc *d, gla_plan *out) {
     return GLA_OK;
 }
 
-int gla_fwd_ex(const gla_desc *d, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// Output mapping of a backward pass (KArgs::out_rev, out_li, out_mx).
+struct OutMapArgs {
+    int rev = 0;
+    const float *li = nullptr;
+    const uint32_t *mx = nullptr;
+};
+
+// The forward pass; h16 marks operands given as fp16 instead of bf16 and om maps the output
+// rows (backward passes only).
+int fwd_run(const gla_desc *d, int h16, void *stream, const OutMapArgs &om = OutMapArgs()) {
     Plan p;
     const int st = checked_plan(d, &p);
     if (st != GLA_OK) return st;
@@ -232,11 +250,20 @@ int gla_fwd_ex(const gla_desc *d, void *stream) {
     a.nsub = p.nsub;
     a.ndv = p.ndv;
     a.nwg = p.grid_out;
+    a.out_rev = om.rev;
+    a.out_li = om.li;
+    a.out_mx = om.mx;
 
-    const hipError_t err = gla::launch_forward(a, d->in_dtype == GLA_DTYPE_F32, d->Dk, s);
+    const hipError_t err = gla::launch_forward(a, d->in_dtype == GLA_DTYPE_F32, h16, d->Dk, s);
     if (owned) (void)hipFreeAsync(ws, s);
     return err == hipSuccess ? GLA_OK : GLA_ERR_HIP;
 }
+
+}  // namespace
+
+extern "C" {
+
+int gla_fwd_ex(const gla_desc *d, void *stream) { return fwd_run(d, 0, stream); }
 
 int gla_step(const gla_step_desc *d, void *stream) {
     if (!d || !d->q || !d->k || !d->v || !d->state || !d->out) return GLA_ERR_INVALID_ARG;
@@ -306,7 +333,8 @@ int validate_bwd(const gla_bwd_desc *d) {
     return GLA_OK;
 }
 
-// The forward pass of one of the three backward passes (fp32 operands, 64-token chunks).
+// The forward pass of one of the three backward passes (64-token chunks; fp32 operands for
+// fp32 inputs, else bf16 with the output gradient as fp16).
 gla_desc bwd_pass_desc(const gla_bwd_desc *d, int dk, int dv, const void *q, const void *k, const void *v,
                        int gate_kind, const float *la, const float *li, const float *s0, float *out, float *fin) {
     gla_desc f{};
@@ -316,7 +344,7 @@ gla_desc bwd_pass_desc(const gla_bwd_desc *d, int dk, int dv, const void *q, con
     f.Dk = dk;
     f.Dv = dv;
     f.chunk = gla::kTile;
-    f.in_dtype = GLA_DTYPE_F32;
+    f.in_dtype = d->in_dtype;
     f.gate_kind = gate_kind;
     f.q = q;
     f.k = k;
@@ -330,7 +358,7 @@ gla_desc bwd_pass_desc(const gla_bwd_desc *d, int dk, int dv, const void *q, con
 }
 
 struct BwdPlan {
-    size_t rq, rk, rv, rdo, kc, vc, lar, oA, oB, finA, finC, s0T, dfT, g, part, fws, total;
+    size_t rq, rk, rv, rdo, fdo, mx, mxp, s0A, lar, oA, oB, finA, finC, s0T, dfT, g, part, fws, total;
     size_t fws_bytes;
 };
 
@@ -346,15 +374,19 @@ int bwd_plan(const gla_bwd_desc *d, BwdPlan *p) {
         off += align256(bytes);
         return o;
     };
-    p->rq = take(bh * L * Dk * 4);
-    p->rk = take(bh * L * Dk * 4);
-    p->rv = take(bh * L * Dv * 4);
-    p->rdo = take(bh * L * Dv * 4);
-    p->kc = bf ? take(bh * L * Dv * 4) : 0;
-    p->vc = bf ? take(bh * L * Dk * 4) : 0;
+    // operand copies: fp32 for fp32 inputs; bf16 reversed q, k, v and fp16 output gradients
+    const size_t eb = bf ? 2 : 4;
+    p->rq = take(bh * L * Dk * eb);
+    p->rk = take(bh * L * Dk * eb);
+    p->rv = take(bh * L * Dv * eb);
+    p->rdo = take(bh * L * Dv * eb);
+    p->fdo = bf ? take(bh * L * Dv * 2) : 0;
+    p->mx = bf ? take(bh * 4) : 0;
+    p->mxp = bf ? take(bh * gla::bwd_absmax_parts(d->L, d->Dv, d->Dk, d->dfinal_state != nullptr) * 4) : 0;
+    p->s0A = (bf && d->dfinal_state) ? take(bh * Dk * Dv * 4) : 0;
     p->lar = gate ? take(bh * L * 4) : 0;
-    p->oA = take(bh * L * Dv * 4);
-    p->oB = take(bh * L * Dk * 4);
+    p->oA = bf ? 0 : take(bh * L * Dv * 4);
+    p->oB = bf ? 0 : take(bh * L * Dk * 4);
     p->finA = take(bh * Dk * Dv * 4);
     p->finC = take(bh * Dk * Dv * 4);
     p->s0T = d->initial_state ? take(bh * Dk * Dv * 4) : 0;
@@ -421,42 +453,61 @@ int gla_bwd(const gla_bwd_desc *d, void *stream) {
         if (e != hipSuccess && rc == GLA_OK) rc = GLA_ERR_HIP;
         return rc == GLA_OK;
     };
-    auto fwd = [&](const gla_desc &f0) {
+    auto fwd = [&](const gla_desc &f0, int h16, const OutMapArgs &om) {
         if (rc != GLA_OK) return false;
         gla_desc f = f0;
         f.workspace = p.fws_bytes ? ws + p.fws : nullptr;
         f.workspace_bytes = p.fws_bytes;
-        const int r = gla_fwd_ex(&f, stream);
+        const int r = fwd_run(&f, bf ? h16 : 0, stream, bf ? om : OutMapArgs());
         if (r != GLA_OK) rc = r;
         return rc == GLA_OK;
     };
+    auto V = [&](size_t off) { return static_cast<void *>(ws + off); };
+    uint32_t *mx = bf ? reinterpret_cast<uint32_t *>(ws + p.mx) : nullptr;
     // operands of the three passes
-    ok(gla::bwd_reverse(d->q, dt, F(p.rq), BH, L, Dk, s)) && ok(gla::bwd_reverse(d->k, dt, F(p.rk), BH, L, Dk, s)) &&
-        ok(gla::bwd_reverse(d->v, dt, F(p.rv), BH, L, Dv, s)) &&
-        ok(gla::bwd_reverse(d->dout, GLA_DTYPE_F32, F(p.rdo), BH, L, Dv, s));
     if (bf) {
-        ok(gla::bwd_convert(d->v, dt, F(p.kc), size_t(BH) * L * Dv, s)) &&
-            ok(gla::bwd_convert(d->k, dt, F(p.vc), size_t(BH) * L * Dk, s));
+        // reversed bf16 copies of q, k, v; the scaled output gradient as fp16 (both orders)
+        ok(gla::bwd_dout16(d->dout, d->dfinal_state, F(p.mxp), mx, reinterpret_cast<_Float16 *>(ws + p.fdo),
+                           reinterpret_cast<_Float16 *>(ws + p.rdo), BH, L, Dv, Dk, s)) &&
+            ok(gla::bwd_rev16(d->q, V(p.rq), BH, L, Dk, s)) && ok(gla::bwd_rev16(d->k, V(p.rk), BH, L, Dk, s)) &&
+            ok(gla::bwd_rev16(d->v, V(p.rv), BH, L, Dv, s));
+        if (d->dfinal_state) ok(gla::bwd_scale(d->dfinal_state, mx, F(p.s0A), BH, size_t(Dk) * Dv, s));
+    } else {
+        ok(gla::bwd_reverse(d->q, dt, F(p.rq), BH, L, Dk, s)) &&
+            ok(gla::bwd_reverse(d->k, dt, F(p.rk), BH, L, Dk, s)) &&
+            ok(gla::bwd_reverse(d->v, dt, F(p.rv), BH, L, Dv, s)) &&
+            ok(gla::bwd_reverse(d->dout, GLA_DTYPE_F32, F(p.rdo), BH, L, Dv, s));
     }
     if (gate) ok(gla::bwd_gate(d->log_alpha, d->gate_kind, F(p.lar), BH, d->H, L, s));
-    if (d->initial_state) ok(gla::bwd_transpose(d->initial_state, F(p.s0T), BH, Dk, Dv, s));
-    if (d->dfinal_state) ok(gla::bwd_transpose(d->dfinal_state, F(p.dfT), BH, Dk, Dv, s));
+    if (d->initial_state) ok(gla::bwd_transpose(d->initial_state, nullptr, F(p.s0T), BH, Dk, Dv, s));
+    if (d->dfinal_state) ok(gla::bwd_transpose(d->dfinal_state, mx, F(p.dfT), BH, Dk, Dv, s));
     const int rgate = gate ? GLA_GATE_HEAD : GLA_GATE_NONE;
     const float *rla = gate ? F(p.lar) : nullptr;
-    const void *kc = bf ? static_cast<const void *>(F(p.kc)) : d->v;
-    const void *vc = bf ? static_cast<const void *>(F(p.vc)) : d->k;
+    const float *s0A = d->dfinal_state ? (bf ? F(p.s0A) : d->dfinal_state) : nullptr;
+    const void *fdo = bf ? V(p.fdo) : d->dout;
+    // bf16: the reversed passes store their rows un-reversed, times i_t / s, straight into dv
+    // and dk, and the dq pass its rows times 1/s; fp32: the post kernel does this.
+    OutMapArgs om_rev, om_q;
+    om_rev.rev = 1;
+    om_rev.li = d->log_ig;
+    om_rev.mx = mx;
+    om_q.mx = mx;
     // dv (reversed; its final state is the gradient of the state after token 0)
-    fwd(bwd_pass_desc(d, Dk, Dv, F(p.rk), F(p.rq), F(p.rdo), rgate, rla, nullptr, d->dfinal_state, F(p.oA),
-                      F(p.finA)));
+    fwd(bwd_pass_desc(d, Dk, Dv, V(p.rk), V(p.rq), V(p.rdo), rgate, rla, nullptr, s0A, bf ? d->dv : F(p.oA),
+                      F(p.finA)),
+        gla::kH16V, om_rev);
     // dk (reversed, keys and values exchanged)
-    fwd(bwd_pass_desc(d, Dv, Dk, F(p.rv), F(p.rdo), F(p.rq), rgate, rla, nullptr,
-                      d->dfinal_state ? F(p.dfT) : nullptr, F(p.oB), nullptr));
+    fwd(bwd_pass_desc(d, Dv, Dk, V(p.rv), V(p.rdo), V(p.rq), rgate, rla, nullptr,
+                      d->dfinal_state ? F(p.dfT) : nullptr, bf ? d->dk : F(p.oB), nullptr),
+        gla::kH16K, om_rev);
     // dq (keys and values exchanged; its final state is the forward final state, transposed)
-    fwd(bwd_pass_desc(d, Dv, Dk, d->dout, kc, vc, d->gate_kind, d->log_alpha, d->log_ig,
-                      d->initial_state ? F(p.s0T) : nullptr, d->dq, F(p.finC)));
+    fwd(bwd_pass_desc(d, Dv, Dk, fdo, d->v, d->k, d->gate_kind, d->log_alpha, d->log_ig,
+                      d->initial_state ? F(p.s0T) : nullptr, d->dq, F(p.finC)),
+        gla::kH16Q, om_q);
     if (rc == GLA_OK)
-        ok(gla::bwd_finish(*d, F(p.oA), F(p.oB), (gate && d->dlog_alpha) ? F(p.g) : nullptr, F(p.finA), F(p.finC),
-                           F(p.part), s));
+        ok(gla::bwd_finish(*d, bf ? nullptr : F(p.oA), bf ? nullptr : F(p.oB),
+                           (gate && d->dlog_alpha) ? F(p.g) : nullptr, F(p.finA), F(p.finC),
+                           d->dfinal_state ? F(p.dfT) : nullptr, F(p.part), mx, s));
     if (owned) (void)hipFreeAsync(ws, s);
     return rc;
 }

@@ -14,11 +14,18 @@
 // pass's final state is G_0 and the third's is the forward final state, transposed.  The
 // log-gate gradient is the reverse running sum of q_t . dq_t - k_t . dk_t (plus the
 // final-state term at the last token), and dlog_ig_t = k_t . dk_t.  All scalars fp32.
+//
+// With bf16 inputs the passes run on the fp16 matrix-core path: q, k and v stay bf16 and the
+// output gradient (fp32) enters as fp16, multiplied per (batch, head) by a power of two s
+// that brings its largest magnitude into [4, 8) (the final-state gradient's largest
+// magnitude counts at 1/64, as it enters the passes' fp32 states).  Every pass output is
+// linear in that operand, so the gradients are the outputs times 1/s, exactly.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include "gla.h"
+#include "gla_layout.h"
 
 namespace gla {
 
@@ -37,6 +44,102 @@ __device__ __forceinline__ float wave_sum64(float x) {
     return x;
 }
 
+typedef _Float16 h16x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ float scale_of(uint32_t mbits) { return grad_scale_of(mbits); }
+
+// Largest magnitude per (batch, head) of the output gradient (n4 float4 per slice, blocks
+// j < nb of the slice's nb + nbf) and of the final-state gradient over 64 (nf4 float4 per
+// slice, blocks nb .. nb + nbf - 1), kPerBlock float4 a block, one partial maximum per block
+// into part[bh * (nb + nbf) + j].
+constexpr int kPerThread = 8;
+constexpr int kPerBlock = 256 * kPerThread;
+__global__ __launch_bounds__(256) void bwd_absmax_kernel(const float *dout, const float *dfin, float *part,
+                                                        size_t n4, size_t nf4, int nb, int nbf) {
+    __shared__ float red[4];
+    const size_t bh = blockIdx.x / (unsigned)(nb + nbf);
+    const int j = (int)(blockIdx.x % (unsigned)(nb + nbf));
+    const int tid = (int)threadIdx.x;
+    const bool fin = j >= nb;
+    const float4 *src = fin ? reinterpret_cast<const float4 *>(dfin) + bh * nf4
+                            : reinterpret_cast<const float4 *>(dout) + bh * n4;
+    const size_t n = fin ? nf4 : n4;
+    const size_t i0 = (size_t)(fin ? j - nb : j) * kPerBlock;
+    const size_t i1 = i0 + kPerBlock < n ? i0 + kPerBlock : n;
+    float4 x[kPerThread];
+    if (i1 - i0 == (size_t)kPerBlock) {
+        // a whole block: all loads issued before any is used
+#pragma unroll
+        for (int u = 0; u < kPerThread; ++u) x[u] = src[i0 + (size_t)u * 256 + tid];
+    } else {
+#pragma unroll
+        for (int u = 0; u < kPerThread; ++u) {
+            const size_t i = i0 + (size_t)u * 256 + tid;
+            x[u] = i < i1 ? src[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+    }
+    float m = 0.f;
+#pragma unroll
+    for (int u = 0; u < kPerThread; ++u)
+        m = fmaxf(m, fmaxf(fmaxf(fabsf(x[u].x), fabsf(x[u].y)), fmaxf(fabsf(x[u].z), fabsf(x[u].w))));
+    if (fin) m *= 0.015625f;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+    if ((tid & 63) == 0) red[tid >> 6] = m;
+    __syncthreads();
+    if (tid == 0) part[blockIdx.x] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
+// mx[bh] = bit pattern of the largest of the slice's np partial maxima (one wave per slice).
+__global__ __launch_bounds__(256) void bwd_absmax_final_kernel(const float *part, uint32_t *mx, int np, int BH) {
+    const int bh = (int)(blockIdx.x * 4 + (threadIdx.x >> 6));
+    const int lane = (int)threadIdx.x & 63;
+    if (bh >= BH) return;
+    float m = 0.f;
+    for (int i = lane; i < np; i += 64) m = fmaxf(m, part[(size_t)bh * np + i]);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+    if (lane == 0) mx[bh] = __float_as_uint(m);
+}
+
+// Rows of 16-bit values in reversed token order: dst[bh][u][:] = src[bh][L-1-u][:], 16 bytes
+// a thread (D a multiple of 8).
+__global__ __launch_bounds__(256) void bwd_rev16_kernel(const uint4 *src, uint4 *dst, int L, int d8, size_t total) {
+    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= total) return;
+    const size_t row = i / (size_t)d8;
+    const int c = (int)(i % (size_t)d8);
+    const size_t bh = row / (size_t)L;
+    const int u = (int)(row % (size_t)L);
+    dst[i] = src[(bh * L + (L - 1 - u)) * (size_t)d8 + c];
+}
+
+// The scaled output gradient as fp16, in token order (fwd) and reversed (rev).
+__global__ __launch_bounds__(256) void bwd_dout16_kernel(const float *dout, const uint32_t *mx, h16x8 *fwd,
+                                                        h16x8 *rev, int L, int d8, size_t total) {
+    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= total) return;
+    const size_t row = i / (size_t)d8;
+    const int c = (int)(i % (size_t)d8);
+    const size_t bh = row / (size_t)L;
+    const int t = (int)(row % (size_t)L);
+    const float s = scale_of(mx[bh]);
+    const float4 a = reinterpret_cast<const float4 *>(dout)[2 * i];
+    const float4 b = reinterpret_cast<const float4 *>(dout)[2 * i + 1];
+    const h16x8 h = {(_Float16)(a.x * s), (_Float16)(a.y * s), (_Float16)(a.z * s), (_Float16)(a.w * s),
+                     (_Float16)(b.x * s), (_Float16)(b.y * s), (_Float16)(b.z * s), (_Float16)(b.w * s)};
+    fwd[i] = h;
+    rev[(bh * L + (L - 1 - t)) * (size_t)d8 + c] = h;
+}
+
+// dst = s * src per (batch, head) slice of m elements.
+__global__ __launch_bounds__(256) void bwd_scale_kernel(const float *src, const uint32_t *mx, float *dst, size_t m,
+                                                       size_t total) {
+    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= total) return;
+    dst[i] = src[i] * scale_of(mx[i / m]);
+}
+
 // Reversed, fp32 copies of one [L, D] row set per (b, h): dst[bh][u][:] = src[bh][L-1-u][:].
 __global__ __launch_bounds__(256) void bwd_reverse_kernel(const void *src, int dt, float *dst, int L, int D,
                                                          size_t total) {
@@ -47,13 +150,6 @@ __global__ __launch_bounds__(256) void bwd_reverse_kernel(const void *src, int d
     const size_t bh = row / (size_t)L;
     const int u = (int)(row % (size_t)L);
     dst[i] = in_at(src, dt, (bh * L + (L - 1 - u)) * (size_t)D + c);
-}
-
-// fp32 copy in the same order.
-__global__ __launch_bounds__(256) void bwd_convert_kernel(const void *src, int dt, float *dst, size_t total) {
-    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= total) return;
-    dst[i] = in_at(src, dt, i);
 }
 
 // Log gate of the reversed passes in the per-head-and-token layout [BH, L].
@@ -68,20 +164,21 @@ __global__ __launch_bounds__(256) void bwd_gate_kernel(const float *la, int kind
     dst[i] = x;
 }
 
-// [BH][R][C] -> [BH][C][R]
-__global__ __launch_bounds__(256) void bwd_transpose_kernel(const float *src, float *dst, int R, int C,
-                                                           size_t total) {
+// [BH][R][C] -> [BH][C][R], times the slice's scale when mx is given.
+__global__ __launch_bounds__(256) void bwd_transpose_kernel(const float *src, const uint32_t *mx, float *dst, int R,
+                                                           int C, size_t total) {
     const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= total) return;
     const size_t m = (size_t)R * C;
     const size_t bh = i / m;
     const size_t rc = i % m;
     const int r = (int)(rc / C), c = (int)(rc % C);
-    dst[bh * m + (size_t)c * R + r] = src[i];
+    dst[bh * m + (size_t)c * R + r] = mx ? src[i] * scale_of(mx[bh]) : src[i];
 }
 
 // One wave per token: dk_t = i_t oB[L-1-t], dv_t = i_t oA[L-1-t]; g_t = q_t . dq_t - k_t . dk_t;
-// dlog_ig_t = k_t . dk_t.  Dk and Dv are at most 256 (four values per lane).
+// dlog_ig_t = k_t . dk_t.  Without oA / oB the passes stored dk, dv and dq in place (scaled
+// and un-reversed) and only the dot products are formed.  Dk and Dv are at most 256.
 __global__ __launch_bounds__(256) void bwd_post_kernel(gla_bwd_desc d, const float *oA, const float *oB, float *g,
                                                       size_t ntok) {
     const size_t tok = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -91,15 +188,22 @@ __global__ __launch_bounds__(256) void bwd_post_kernel(gla_bwd_desc d, const flo
     const size_t bh = tok / (size_t)L;
     const int t = (int)(tok % (size_t)L);
     const size_t rtok = bh * L + (L - 1 - t);
-    const float ig = d.log_ig ? exp2f(d.log_ig[tok] * kLog2eB) : 1.f;
     float qdq = 0.f, kdk = 0.f;
-    for (int c = lane; c < Dk; c += 64) {
-        const float dkv = ig * oB[rtok * Dk + c];
-        d.dk[tok * Dk + c] = dkv;
-        kdk += in_at(d.k, d.in_dtype, tok * Dk + c) * dkv;
-        qdq += in_at(d.q, d.in_dtype, tok * Dk + c) * d.dq[tok * Dk + c];
+    if (!oB) {
+        for (int c = lane; c < Dk; c += 64) {
+            kdk += in_at(d.k, d.in_dtype, tok * Dk + c) * d.dk[tok * Dk + c];
+            qdq += in_at(d.q, d.in_dtype, tok * Dk + c) * d.dq[tok * Dk + c];
+        }
+    } else {
+        const float ig = d.log_ig ? exp2f(d.log_ig[tok] * kLog2eB) : 1.f;
+        for (int c = lane; c < Dk; c += 64) {
+            const float dkv = ig * oB[rtok * Dk + c];
+            d.dk[tok * Dk + c] = dkv;
+            kdk += in_at(d.k, d.in_dtype, tok * Dk + c) * dkv;
+            qdq += in_at(d.q, d.in_dtype, tok * Dk + c) * d.dq[tok * Dk + c];
+        }
+        for (int c = lane; c < Dv; c += 64) d.dv[tok * Dv + c] = ig * oA[rtok * Dv + c];
     }
-    for (int c = lane; c < Dv; c += 64) d.dv[tok * Dv + c] = ig * oA[rtok * Dv + c];
     qdq = wave_sum64(qdq);
     kdk = wave_sum64(kdk);
     if (lane == 0) {
@@ -108,72 +212,125 @@ __global__ __launch_bounds__(256) void bwd_post_kernel(gla_bwd_desc d, const flo
     }
 }
 
-// One workgroup per (b, h): adds the final-state term to the last token's g, then the
-// reverse running sum (per head and token gate) or the weighted total sum_u (u+1) g_u (fixed
-// per-head gate, into part[bh]); and dinitial_state = a_0 G_0.
-__global__ __launch_bounds__(256) void bwd_gate_reduce_kernel(gla_bwd_desc d, float *g, const float *finA,
-                                                             const float *finC, float *part) {
+// g_t = q_t . dq_t - k_t . dk_t and dlog_ig_t = k_t . dk_t from the stored gradients: 2^lg =
+// Dk / 4 lanes per token (four channels each, 16-byte gradient loads), 64 / 2^lg tokens per
+// wave.
+__global__ __launch_bounds__(256) void bwd_dot_kernel(gla_bwd_desc d, float *g, size_t ntok, int lg) {
+    const int lane = (int)threadIdx.x & 63;
+    const int G = 1 << lg;
+    const size_t tok = ((size_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * (size_t)(64 >> lg) + (size_t)(lane >> lg);
+    const int c = (lane & (G - 1)) * 4;
+    const size_t Dk = (size_t)d.Dk;
+    float qdq = 0.f, kdk = 0.f;
+    if (tok < ntok) {
+        const size_t o = tok * Dk + c;
+        const float4 dq = *reinterpret_cast<const float4 *>(d.dq + o);
+        const float4 dk = *reinterpret_cast<const float4 *>(d.dk + o);
+        float q[4], k[4];
+        if (d.in_dtype == GLA_DTYPE_F32) {
+            const float4 a = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(d.q) + o);
+            const float4 b = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(d.k) + o);
+            q[0] = a.x, q[1] = a.y, q[2] = a.z, q[3] = a.w;
+            k[0] = b.x, k[1] = b.y, k[2] = b.z, k[3] = b.w;
+        } else {
+            const uint2 a = *reinterpret_cast<const uint2 *>(reinterpret_cast<const uint16_t *>(d.q) + o);
+            const uint2 b = *reinterpret_cast<const uint2 *>(reinterpret_cast<const uint16_t *>(d.k) + o);
+            q[0] = __uint_as_float(a.x << 16), q[1] = __uint_as_float(a.x & 0xffff0000u);
+            q[2] = __uint_as_float(a.y << 16), q[3] = __uint_as_float(a.y & 0xffff0000u);
+            k[0] = __uint_as_float(b.x << 16), k[1] = __uint_as_float(b.x & 0xffff0000u);
+            k[2] = __uint_as_float(b.y << 16), k[3] = __uint_as_float(b.y & 0xffff0000u);
+        }
+        qdq = q[0] * dq.x + q[1] * dq.y + q[2] * dq.z + q[3] * dq.w;
+        kdk = k[0] * dk.x + k[1] * dk.y + k[2] * dk.z + k[3] * dk.w;
+    }
+    for (int o = G >> 1; o > 0; o >>= 1) {
+        qdq += __shfl_xor(qdq, o);
+        kdk += __shfl_xor(kdk, o);
+    }
+    if ((lane & (G - 1)) == 0 && tok < ntok) {
+        if (g) g[tok] = qdq - kdk;
+        if (d.dlog_ig) d.dlog_ig[tok] = kdk;
+    }
+}
+
+// The final-state term of the last token's g: the sum over (j, d) of dfinal^T[j][d] S_fin^T[j][d]
+// (dfT and finC both transposed; times 1/s when dfT carries the scale), kPerBlock float4 per
+// workgroup, added into g atomically.
+__global__ __launch_bounds__(256) void bwd_fin_term_kernel(const float *dfT, const float *finC, const uint32_t *mx,
+                                                          float *g, int L, size_t n4, int nb) {
+    __shared__ float red[4];
+    const size_t bh = blockIdx.x / (unsigned)nb;
+    const size_t i0 = (size_t)(blockIdx.x % (unsigned)nb) * kPerBlock;
+    const size_t i1 = i0 + kPerBlock < n4 ? i0 + kPerBlock : n4;
+    const float4 *a = reinterpret_cast<const float4 *>(dfT) + bh * n4;
+    const float4 *b = reinterpret_cast<const float4 *>(finC) + bh * n4;
+    const int tid = (int)threadIdx.x;
+    float sum = 0.f;
+    for (size_t i = i0 + tid; i < i1; i += 256) {
+        const float4 x = a[i], y = b[i];
+        sum += x.x * y.x + x.y * y.y + x.z * y.z + x.w * y.w;
+    }
+    sum = wave_sum64(sum);
+    if ((tid & 63) == 0) red[tid >> 6] = sum;
+    __syncthreads();
+    if (tid == 0) {
+        const float inv = mx ? 1.f / scale_of(mx[bh]) : 1.f;
+        atomicAdd(g + bh * L + L - 1, (red[0] + red[1] + red[2] + red[3]) * inv);
+    }
+}
+
+// One workgroup per (b, h): the reverse running sum of g into dlog_alpha (per head and token
+// gate), or the weighted total sum_u (u+1) g_u into part[bh] (fixed per-head gate).
+__global__ __launch_bounds__(256) void bwd_gate_reduce_kernel(gla_bwd_desc d, const float *g, float *part) {
     __shared__ float red[256];
     __shared__ float carry;
     const int bh = blockIdx.x, tid = threadIdx.x;
-    const int L = d.L, Dk = d.Dk, Dv = d.Dv;
-    const size_t m = (size_t)Dk * Dv;
-    if (g) {
-        if (d.dfinal_state) {
-            // sum over (d, j) of dfinal[d][j] * S_fin[d][j]; finC holds S_fin transposed [j][d]
-            float s = 0.f;
-            for (size_t i = tid; i < m; i += 256) {
-                const int r = (int)(i / Dv), c = (int)(i % Dv);
-                s += d.dfinal_state[bh * m + i] * finC[bh * m + (size_t)c * Dk + r];
-            }
-            red[tid] = s;
+    const int L = d.L;
+    const float *gb = g + (size_t)bh * L;
+    if (d.gate_kind == GLA_GATE_HEAD) {
+        if (tid == 0) carry = 0.f;
+        __syncthreads();
+        // blocks of 256 tokens from the end; inclusive suffix scan inside a block
+        for (int end = L; end > 0; end -= 256) {
+            const int t = end - 1 - tid;
+            red[tid] = t >= 0 ? gb[t] : 0.f;
             __syncthreads();
-            for (int o = 128; o > 0; o >>= 1) {
-                if (tid < o) red[tid] += red[tid + o];
+            for (int o = 1; o < 256; o <<= 1) {
+                const float y = tid >= o ? red[tid - o] : 0.f;
+                __syncthreads();
+                red[tid] += y;
                 __syncthreads();
             }
-            if (tid == 0) g[(size_t)bh * L + L - 1] += red[0];
+            const float c0 = carry;
+            if (t >= 0) d.dlog_alpha[(size_t)bh * L + t] = red[tid] + c0;
+            __syncthreads();
+            if (tid == 255) carry = c0 + red[255];
             __syncthreads();
         }
-        float *gb = g + (size_t)bh * L;
-        if (d.gate_kind == GLA_GATE_HEAD) {
-            if (tid == 0) carry = 0.f;
+    } else {
+        float s = 0.f;
+        for (int t = tid; t < L; t += 256) s += (float)(t + 1) * gb[t];
+        red[tid] = s;
+        __syncthreads();
+        for (int o = 128; o > 0; o >>= 1) {
+            if (tid < o) red[tid] += red[tid + o];
             __syncthreads();
-            // blocks of 256 tokens from the end; inclusive suffix scan inside a block
-            for (int end = L; end > 0; end -= 256) {
-                const int t = end - 1 - tid;
-                red[tid] = t >= 0 ? gb[t] : 0.f;
-                __syncthreads();
-                for (int o = 1; o < 256; o <<= 1) {
-                    const float y = tid >= o ? red[tid - o] : 0.f;
-                    __syncthreads();
-                    red[tid] += y;
-                    __syncthreads();
-                }
-                const float c0 = carry;
-                if (t >= 0) d.dlog_alpha[(size_t)bh * L + t] = red[tid] + c0;
-                __syncthreads();
-                if (tid == 255) carry = c0 + red[255];
-                __syncthreads();
-            }
-        } else {
-            float s = 0.f;
-            for (int t = tid; t < L; t += 256) s += (float)(t + 1) * gb[t];
-            red[tid] = s;
-            __syncthreads();
-            for (int o = 128; o > 0; o >>= 1) {
-                if (tid < o) red[tid] += red[tid + o];
-                __syncthreads();
-            }
-            if (tid == 0) part[bh] = red[0];
         }
+        if (tid == 0) part[bh] = red[0];
     }
-    if (d.dinitial_state) {
-        float a0 = 1.f;
-        if (d.gate_kind == GLA_GATE_HEAD) a0 = exp2f(d.log_alpha[(size_t)bh * L] * kLog2eB);
-        else if (d.gate_kind == GLA_GATE_HEAD_CONST) a0 = exp2f(d.log_alpha[bh % d.H] * kLog2eB);
-        for (size_t i = tid; i < m; i += 256) d.dinitial_state[bh * m + i] = a0 * finA[bh * m + i];
-    }
+}
+
+// dinitial_state = a_0 G_0: the first pass's final state times the first token's decay (and
+// 1/s when finA carries the scale).
+__global__ __launch_bounds__(256) void bwd_dinit_kernel(gla_bwd_desc d, const float *finA, const uint32_t *mx,
+                                                       size_t m, size_t total) {
+    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= total) return;
+    const size_t bh = i / m;
+    float a0 = mx ? 1.f / scale_of(mx[bh]) : 1.f;
+    if (d.gate_kind == GLA_GATE_HEAD) a0 *= exp2f(d.log_alpha[bh * d.L] * kLog2eB);
+    else if (d.gate_kind == GLA_GATE_HEAD_CONST) a0 *= exp2f(d.log_alpha[bh % d.H] * kLog2eB);
+    d.dinitial_state[i] = a0 * finA[i];
 }
 
 // Fixed per-head gate: dlog_alpha[h] = sum over the batch of the per-(b, h) totals.
@@ -195,32 +352,83 @@ hipError_t bwd_reverse(const void *src, int dt, float *dst, int BH, int L, int D
     return hipGetLastError();
 }
 
-hipError_t bwd_convert(const void *src, int dt, float *dst, size_t total, hipStream_t st) {
-    hipLaunchKernelGGL(bwd_convert_kernel, dim3(nblk(total, 256)), dim3(256), 0, st, src, dt, dst, total);
-    return hipGetLastError();
-}
-
 hipError_t bwd_gate(const float *la, int kind, float *dst, int BH, int H, int L, hipStream_t st) {
     const size_t total = (size_t)BH * L;
     hipLaunchKernelGGL(bwd_gate_kernel, dim3(nblk(total, 256)), dim3(256), 0, st, la, kind, dst, H, L, total);
     return hipGetLastError();
 }
 
-hipError_t bwd_transpose(const float *src, float *dst, int BH, int R, int C, hipStream_t st) {
+hipError_t bwd_transpose(const float *src, const uint32_t *mx, float *dst, int BH, int R, int C, hipStream_t st) {
     const size_t total = (size_t)BH * R * C;
-    hipLaunchKernelGGL(bwd_transpose_kernel, dim3(nblk(total, 256)), dim3(256), 0, st, src, dst, R, C, total);
+    hipLaunchKernelGGL(bwd_transpose_kernel, dim3(nblk(total, 256)), dim3(256), 0, st, src, mx, dst, R, C, total);
+    return hipGetLastError();
+}
+
+size_t bwd_absmax_parts(int L, int Dv, int Dk, bool dfin) {
+    return nblk((size_t)L * Dv / 4, kPerBlock) + (dfin ? nblk((size_t)Dk * Dv / 4, kPerBlock) : 0);
+}
+
+// Per-(batch, head) scale of the output gradient into mx (bit patterns of the largest
+// magnitudes, through bwd_absmax_parts(...) partials per slice in part), then its fp16
+// copies (token order and reversed).
+hipError_t bwd_dout16(const float *dout, const float *dfin, float *part, uint32_t *mx, _Float16 *fwd, _Float16 *rev,
+                      int BH, int L, int Dv, int Dk, hipStream_t st) {
+    const size_t n4 = (size_t)L * Dv / 4, nf4 = dfin ? (size_t)Dk * Dv / 4 : 0;
+    const int nb = (int)nblk(n4, kPerBlock), nbf = (int)nblk(nf4, kPerBlock);
+    hipLaunchKernelGGL(bwd_absmax_kernel, dim3((unsigned)((size_t)(nb + nbf) * BH)), dim3(256), 0, st, dout, dfin,
+                       part, n4, nf4, nb, nbf);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(bwd_absmax_final_kernel, dim3(nblk((size_t)BH, 4)), dim3(256), 0, st, part, mx, nb + nbf, BH);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const size_t total = (size_t)BH * L * (Dv / 8);
+    hipLaunchKernelGGL(bwd_dout16_kernel, dim3(nblk(total, 256)), dim3(256), 0, st, dout, mx,
+                       reinterpret_cast<h16x8 *>(fwd), reinterpret_cast<h16x8 *>(rev), L, Dv / 8, total);
+    return hipGetLastError();
+}
+
+hipError_t bwd_rev16(const void *src, void *dst, int BH, int L, int D, hipStream_t st) {
+    const size_t total = (size_t)BH * L * (D / 8);
+    hipLaunchKernelGGL(bwd_rev16_kernel, dim3(nblk(total, 256)), dim3(256), 0, st, reinterpret_cast<const uint4 *>(src),
+                       reinterpret_cast<uint4 *>(dst), L, D / 8, total);
+    return hipGetLastError();
+}
+
+hipError_t bwd_scale(const float *src, const uint32_t *mx, float *dst, int BH, size_t m, hipStream_t st) {
+    const size_t total = (size_t)BH * m;
+    hipLaunchKernelGGL(bwd_scale_kernel, dim3(nblk(total, 256)), dim3(256), 0, st, src, mx, dst, m, total);
     return hipGetLastError();
 }
 
 hipError_t bwd_finish(const gla_bwd_desc &d, const float *oA, const float *oB, float *g, const float *finA,
-                      const float *finC, float *part, hipStream_t st) {
+                      const float *finC, const float *dfT, float *part, const uint32_t *mx, hipStream_t st) {
     const int BH = d.B * d.H;
     const size_t ntok = (size_t)BH * d.L;
-    hipLaunchKernelGGL(bwd_post_kernel, dim3(nblk(ntok, 4)), dim3(256), 0, st, d, oA, oB, g, ntok);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    if (g || d.dinitial_state) {
-        hipLaunchKernelGGL(bwd_gate_reduce_kernel, dim3(BH), dim3(256), 0, st, d, g, finA, finC, part);
+    hipError_t e = hipSuccess;
+    if (oB) {
+        hipLaunchKernelGGL(bwd_post_kernel, dim3(nblk(ntok, 4)), dim3(256), 0, st, d, oA, oB, g, ntok);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    } else if (g || d.dlog_ig) {
+        const int lg = d.Dk == 64 ? 4 : (d.Dk == 128 ? 5 : 6);  // Dk / 4 lanes per token
+        const size_t per_block = (size_t)4 * (64 >> lg);
+        hipLaunchKernelGGL(bwd_dot_kernel, dim3(nblk(ntok, (unsigned)per_block)), dim3(256), 0, st, d, g, ntok, lg);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    const size_t m = (size_t)d.Dk * d.Dv;
+    if (g && dfT) {
+        const size_t n4 = m / 4;
+        const int nb = (int)nblk(n4, kPerBlock);
+        hipLaunchKernelGGL(bwd_fin_term_kernel, dim3((unsigned)((size_t)nb * BH)), dim3(256), 0, st, dfT, finC, mx, g,
+                           d.L, n4, nb);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    if (g) {
+        hipLaunchKernelGGL(bwd_gate_reduce_kernel, dim3(BH), dim3(256), 0, st, d, g, part);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    if (d.dinitial_state) {
+        const size_t total = (size_t)BH * m;
+        hipLaunchKernelGGL(bwd_dinit_kernel, dim3(nblk(total, 256)), dim3(256), 0, st, d, finA, mx, m, total);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     if (g && d.gate_kind == GLA_GATE_HEAD_CONST) {

@@ -71,9 +71,12 @@ constexpr int kRsrcFlags = 0x00020000;  // raw buffer, 32-bit data format (gfx9 
 
 // ------------------------------------------------------------------------------------
 // Instance configuration.
-template <bool F32_, int DK_, bool CH_, bool MT_>
+template <bool F32_, int DK_, bool CH_, bool MT_, int H16_ = 0>
 struct Cfg {
     static constexpr bool F32 = F32_;  // fp32 inputs and operands (else bf16 inputs, fp16 operands)
+    // Inputs given as fp16 instead of bf16, one bit per operand (kOpQ, kOpK, kOpV): the
+    // backward pass feeds its scaled output gradient this way.
+    static constexpr int H16 = H16_;
     static constexpr int DK = DK_;
     static constexpr bool CH = CH_;    // per-channel gate
     static constexpr bool MT = MT_;    // chunk of several 64-token tiles
@@ -113,6 +116,14 @@ __device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(
 __device__ __forceinline__ float frcp(float x) { return __builtin_amdgcn_rcpf(x); }
 __device__ __forceinline__ float bf_lo(uint32_t x) { return __uint_as_float(x << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
+__device__ __forceinline__ float h_lo(uint32_t x) { return (float)__builtin_bit_cast(f16x2, x)[0]; }
+__device__ __forceinline__ float h_hi(uint32_t x) { return (float)__builtin_bit_cast(f16x2, x)[1]; }
+enum { kOpQ = 0, kOpK = 1, kOpV = 2 };
+// Low / high 16-bit input of a packed pair of operand OP as fp32.
+template <class C, int OP>
+__device__ __forceinline__ float in_lo(uint32_t x) { return ((C::H16 >> OP) & 1) ? h_lo(x) : bf_lo(x); }
+template <class C, int OP>
+__device__ __forceinline__ float in_hi(uint32_t x) { return ((C::H16 >> OP) & 1) ? h_hi(x) : bf_hi(x); }
 
 __device__ __forceinline__ rsrc_t make_rsrc(const void *p, uint64_t bytes) {
     const uint32_t n = bytes > 0xffffffffull ? 0xffffffffu : (uint32_t)bytes;
@@ -240,12 +251,13 @@ __device__ __forceinline__ typename C::Frag gld8(rsrc_t r, uint32_t off) {
     }
 }
 // 8 consecutive raw inputs (bf16 or fp32) from global memory as operands.
-template <class C>
+template <class C, int OP>
 __device__ __forceinline__ typename C::Frag gld8_in(rsrc_t r, uint32_t off) {
     if constexpr (C::F32) {
         return gld8<C, 0>(r, off);
     } else {
         const u32x4 x = bld128(r, off);
+        if constexpr ((C::H16 >> OP) & 1) return __builtin_bit_cast(f16x8, x);
         typename C::Frag f;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -278,6 +290,42 @@ __device__ __forceinline__ void store_staged(const float *sO, rsrc_t out, int T0
     }
 }
 
+// The same for the backward pass's instances: row t goes to row L-1-t when rev, times
+// oinv and (has_li) times exp of the destination row's log input gate; rows past the
+// sequence end are not stored.
+__device__ __forceinline__ void store_staged_map(const float *sO, rsrc_t out, rsrc_t oli, int T0, int L, int Dv,
+                                                 int dv0, int cw, int lane, bool rev, bool has_li, float oinv) {
+    const int c4 = lane & 15;
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+        const int row = 16 * cw + 4 * rr + (lane >> 4);
+        const int t = T0 + row;
+        const int dst = rev ? L - 1 - t : t;
+        float f = oinv;
+        if (has_li) f *= fexp2(__uint_as_float(bld32(oli, (uint32_t)dst * 4u)) * kLog2e);
+        f32x4 x = lds_ld<f32x4>(sO + row * 68 + 4 * c4);
+        x *= f;
+        if (t < L)
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), out,
+                                                   (int)(((uint32_t)dst * Dv + dv0 + 4 * c4) * 4u), 0, 0);
+    }
+}
+
+// Output mapping of a backward-pass instance, set up once per workgroup.
+struct OutMap {
+    rsrc_t li;
+    float inv;
+    bool rev, has_li;
+};
+__device__ __forceinline__ OutMap make_out_map(const KArgs &a, int bh) {
+    OutMap m;
+    m.rev = a.out_rev != 0;
+    m.has_li = a.out_li != nullptr;
+    m.li = m.has_li ? make_rsrc(a.out_li + (size_t)bh * a.L, (uint64_t)a.L * 4) : make_rsrc(a.out, 0);
+    m.inv = a.out_mx ? 1.f / grad_scale_of(a.out_mx[bh]) : 1.f;
+    return m;
+}
+
 // ------------------------------------------------------------------------------------
 // Raw input of one unit (64-token tile x one slab of key channels), prefetched into
 // registers.  Thread (wave w, lane) holds rows 16w..16w+15 of the tile for its CPL key
@@ -288,11 +336,15 @@ struct Raw {
     float la[C::CH ? 16 : 1][C::CPL];   // per-channel log gates
     float las, lis;                     // log gate / log input gate of row (tile start + lane)
     uint32_t v[4][C::F32 ? 4 : 2];      // 4 values of one row
-    __device__ float qf(int r, int c) const { return C::F32 ? __uint_as_float(q[r]) : (c ? bf_hi(q[r]) : bf_lo(q[r])); }
-    __device__ float kf(int r, int c) const { return C::F32 ? __uint_as_float(k[r]) : (c ? bf_hi(k[r]) : bf_lo(k[r])); }
+    __device__ float qf(int r, int c) const {
+        return C::F32 ? __uint_as_float(q[r]) : (c ? in_hi<C, kOpQ>(q[r]) : in_lo<C, kOpQ>(q[r]));
+    }
+    __device__ float kf(int r, int c) const {
+        return C::F32 ? __uint_as_float(k[r]) : (c ? in_hi<C, kOpK>(k[r]) : in_lo<C, kOpK>(k[r]));
+    }
     __device__ float vf(int e, int j) const {
         if constexpr (C::F32) return __uint_as_float(v[e][j]);
-        else return (j & 1) ? bf_hi(v[e][j >> 1]) : bf_lo(v[e][j >> 1]);
+        else return (j & 1) ? in_hi<C, kOpV>(v[e][j >> 1]) : in_lo<C, kOpV>(v[e][j >> 1]);
     }
 };
 
@@ -587,6 +639,7 @@ __device__ __forceinline__ Pairs make_pairs(int w, bool ch) {
 // chunk_output_kernel: grid = BH * nseg * ndv workgroups of 256 threads.
 template <class C>
 __global__ __launch_bounds__(256, 1) void chunk_output_kernel(KArgs a) {
+    static_assert(C::H16 == 0, "the backward pass's instances run the ws and sg kernels");
     using OpT = typename C::OpT;
     using Frag = typename C::Frag;
     using Half = typename C::Half;
@@ -991,7 +1044,7 @@ __global__ __launch_bounds__(256, 1) void chunk_output_kernel(KArgs a) {
                             } else {
 #pragma unroll
                                 for (int j = 0; j < 4; ++j)
-                                    af[j] = gld8_in<C>(rs.k, (uint32_t)(((c0 + kTile * kj + 16 * j + c16) * C::DK +
+                                    af[j] = gld8_in<C, kOpK>(rs.k, (uint32_t)(((c0 + kTile * kj + 16 * j + c16) * C::DK +
                                                                          sl * C::SLAB + ch) * C::IB));
                             }
 #pragma unroll
@@ -1441,6 +1494,7 @@ __global__ __launch_bounds__(512, 1) void chunk_output_ws_kernel(KArgs a) {
     const int t_end = min(L, t_begin + a.seg_len);
     const int nch = (t_end - t_begin + kTile - 1) / kTile;
     const Rs rs = make_rs<C>(a, bh, h);
+    [[maybe_unused]] const OutMap om = C::H16 != 0 ? make_out_map(a, bh) : OutMap{};
 
     if (w >= 4) {
         // ============================ producers
@@ -1780,7 +1834,11 @@ __global__ __launch_bounds__(512, 1) void chunk_output_ws_kernel(KArgs a) {
         }
         stage_out(reinterpret_cast<float *>(smem + lp.ostage), O, cw, g, c16);
         lds_barrier();  // B2
-        store_staged(reinterpret_cast<const float *>(smem + lp.ostage), rs.out, T0, Dv, dv0, cw, lane);
+        if constexpr (C::H16 != 0)
+            store_staged_map(reinterpret_cast<const float *>(smem + lp.ostage), rs.out, om.li, T0, L, Dv, dv0, cw,
+                             lane, om.rev, om.has_li, om.inv);
+        else
+            store_staged(reinterpret_cast<const float *>(smem + lp.ostage), rs.out, T0, Dv, dv0, cw, lane);
     }
 
     if (seg == a.nseg - 1 && a.fin) {
@@ -1868,7 +1926,7 @@ __device__ __forceinline__ void sg_produce_a(ProdSg<C> &pv, const RawSg<C> &raw,
         for (int j = 0; j < 4; ++j) {
             f16x4 h4;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) h4[e] = (f16)((j & 1) ? bf_hi(raw.v[e][j >> 1]) : bf_lo(raw.v[e][j >> 1]));
+            for (int e = 0; e < 4; ++e) h4[e] = (f16)((j & 1) ? in_hi<C, kOpV>(raw.v[e][j >> 1]) : in_lo<C, kOpV>(raw.v[e][j >> 1]));
             *reinterpret_cast<f16x4 *>(sV + ((p * 4 + gq) * 64 + vsw(c0 + j)) * 8 + hh * 4) = h4;
         }
     }
@@ -1889,10 +1947,10 @@ __device__ __forceinline__ void sg_produce_a(ProdSg<C> &pv, const RawSg<C> &raw,
         float qf[4], kf[4];
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
-            qf[2 * c] = bf_lo(raw.q[rr][c]);
-            qf[2 * c + 1] = bf_hi(raw.q[rr][c]);
-            kf[2 * c] = bf_lo(raw.k[rr][c]);
-            kf[2 * c + 1] = bf_hi(raw.k[rr][c]);
+            qf[2 * c] = in_lo<C, kOpQ>(raw.q[rr][c]);
+            qf[2 * c + 1] = in_hi<C, kOpQ>(raw.q[rr][c]);
+            kf[2 * c] = in_lo<C, kOpK>(raw.k[rr][c]);
+            kf[2 * c + 1] = in_hi<C, kOpK>(raw.k[rr][c]);
         }
         pv.qh[rr] = u32x2{__builtin_bit_cast(uint32_t, f16x2{(f16)qf[0], (f16)qf[1]}),
                           __builtin_bit_cast(uint32_t, f16x2{(f16)qf[2], (f16)qf[3]})};
@@ -1949,6 +2007,7 @@ __global__ __launch_bounds__(512, 1) void chunk_output_sg_kernel(KArgs a) {
     const int t_end = min(L, t_begin + a.seg_len);
     const int nch = (t_end - t_begin + kTile - 1) / kTile;
     const Rs rs = make_rs<C>(a, bh, h);
+    [[maybe_unused]] const OutMap om = C::H16 != 0 ? make_out_map(a, bh) : OutMap{};
 
     if (w >= 4) {
         // ============================ producers
@@ -2140,7 +2199,11 @@ __global__ __launch_bounds__(512, 1) void chunk_output_sg_kernel(KArgs a) {
         }
         stage_out(reinterpret_cast<float *>(smem + lp.ostage), O, cw, g, c16);
         lds_barrier();  // B2
-        store_staged(reinterpret_cast<const float *>(smem + lp.ostage), rs.out, T0, Dv, dv0, cw, lane);
+        if constexpr (C::H16 != 0)
+            store_staged_map(reinterpret_cast<const float *>(smem + lp.ostage), rs.out, om.li, T0, L, Dv, dv0, cw,
+                             lane, om.rev, om.has_li, om.inv);
+        else
+            store_staged(reinterpret_cast<const float *>(smem + lp.ostage), rs.out, T0, Dv, dv0, cw, lane);
     }
 
     if (seg == a.nseg - 1 && a.fin) {
@@ -2500,9 +2563,25 @@ hipError_t launch_step(const gla_step_desc &d, hipStream_t st) {
     return hipGetLastError();
 }
 
-hipError_t launch_forward(const KArgs &a, bool f32, int dk, hipStream_t st) {
+template <int M>
+static hipError_t launch_h16(const KArgs &a, int dk, hipStream_t st) {
+    if (dk == 64) return launch_cfg<Cfg<false, 64, false, false, M>>(a, st);
+    if (dk == 128) return launch_cfg<Cfg<false, 128, false, false, M>>(a, st);
+    return launch_cfg<Cfg<false, 256, false, false, M>>(a, st);
+}
+
+// h16: which of q, k, v (bits kOpQ, kOpK, kOpV) are fp16 rather than bf16.  Only one fp16
+// operand, with scalar gates and 64-token chunks: the forms the backward pass runs.
+hipError_t launch_forward(const KArgs &a, bool f32, int h16, int dk, hipStream_t st) {
     const bool ch = a.gate == GLA_GATE_CHANNEL;
     const bool mt = a.nt > 1;
+    if (h16) {
+        if (ch || mt || f32) return hipErrorInvalidValue;
+        if (h16 == 1 << kOpQ) return launch_h16<1 << kOpQ>(a, dk, st);
+        if (h16 == 1 << kOpK) return launch_h16<1 << kOpK>(a, dk, st);
+        if (h16 == 1 << kOpV) return launch_h16<1 << kOpV>(a, dk, st);
+        return hipErrorInvalidValue;
+    }
     if (f32) {
         if (dk == 64) return launch_dk<true, 64>(a, ch, mt, st);
         if (dk == 128) return launch_dk<true, 128>(a, ch, mt, st);

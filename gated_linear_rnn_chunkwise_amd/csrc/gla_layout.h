@@ -262,6 +262,25 @@ struct KArgs {
     int nseg, ndv;    // segments; 64-column value tiles
     int nsub;         // sub-segments per segment in the segment-state kernel
     int nwg;          // workgroups of the launch (for the XCD-aware remap)
+    // Output mapping of the backward pass's instances (fp16 operands; ignored elsewhere):
+    // row t is stored at row L-1-t when out_rev, times 1/s with s the scale of out_mx[bh]
+    // (when non-null) and times exp(out_li[bh][destination row]) (when non-null).
+    int out_rev;
+    const float *out_li;
+    const uint32_t *out_mx;
 };
+
+#if defined(__HIPCC__)
+// Power-of-two scale of the backward pass's output gradient from the bit pattern of its
+// largest magnitude m: s = 2^(2 - e) for m in [2^e, 2^(e+1)), so that m s lies in [4, 8);
+// the exponent of s is kept in [-126, 126] (m zero or subnormal: 2^126; m infinite or NaN:
+// 2^-126).
+__device__ inline float grad_scale_of(uint32_t mbits) {
+    const int e = (int)((mbits >> 23) & 0xffu) - 127;
+    int x = 2 - e;
+    x = x < -126 ? -126 : (x > 126 ? 126 : x);
+    return __uint_as_float((uint32_t)(127 + x) << 23);
+}
+#endif
 
 }  // namespace gla

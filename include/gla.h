@@ -195,13 +195,18 @@ int gla_step(const gla_step_desc *d, void *stream);
  * keys and values exchanged for dk and dq).  The log-gate gradients follow from
  * d loss / d B_t = q_t . dq_t - k_t . dk_t (B_t the running sum of log decays; plus the
  * final-state term at the last token) summed from t to the end, and dlog_ig_t = k_t . dk_t.
- * The intermediate passes run with fp32 operands.
+ * Precision: fp32 inputs run the passes with fp32 operands.  bf16 inputs run them on the
+ * fp16 matrix-core path of the forward pass, with q, k, v as given and dout entering as
+ * fp16 after a per-(batch, head) power-of-two scale that puts its largest magnitude in
+ * [4, 8) (dfinal_state counts at 1/64 of its magnitude); the scale is divided out exactly.
+ * The range limits of bf16 forward inputs apply to q, k, v.
  *
  * Shapes: q, k [B,H,L,Dk] and v [B,H,L,Dv] in in_dtype; gates as in gla_desc; dout
  * [B,H,L,Dv] fp32; dfinal_state [B,H,Dk,Dv] fp32 or NULL (zero); outputs fp32: dq, dk
- * [B,H,L,Dk], dv [B,H,L,Dv], dlog_alpha in the layout of log_alpha (NULL iff gate_kind is
- * NONE), dlog_ig [B,H,L] (may be non-NULL only with log_ig), dinitial_state [B,H,Dk,Dv] or
- * NULL.  Outputs must not alias inputs or each other. */
+ * [B,H,L,Dk], dv [B,H,L,Dv], dlog_alpha in the layout of log_alpha (must be NULL when
+ * gate_kind is NONE; NULL otherwise skips it), dlog_ig [B,H,L] (may be non-NULL only with
+ * log_ig), dinitial_state [B,H,Dk,Dv] or NULL.  Outputs must not alias inputs or each
+ * other. */
 typedef struct gla_bwd_desc {
     int32_t B, H, L, Dk, Dv;
     int32_t in_dtype;             /* enum gla_dtype of q, k, v */

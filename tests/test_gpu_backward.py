@@ -1,9 +1,19 @@
 """GPU parity of the backward pass (gla_bwd through the C ABI) against the fp64 oracle's
 gradients (oracle.backward, itself pinned by finite differences).
 
-Bar: every gradient satisfies max |gpu - oracle| <= 1e-4 * RMS(oracle) over the compared
-tensor.  The backward's passes run with fp32 operands (bf16 inputs convert exactly), so the
-fp32 rule applies to both input dtypes.
+Bar, fp32 inputs (fp32 operands throughout): every gradient satisfies
+max |gpu - oracle| <= 1e-4 * RMS(oracle) over the compared tensor, the forward pass's rule.
+
+Bar, bf16 inputs: the passes take fp16 matrix operands (computed operands, states and the
+output gradient scaled by a power of two, each rounded once to fp16, 2^-12 relative), so an
+element's error scales with the magnitude of the terms that form it rather than with the
+tensor's RMS (the rows of the first tokens, led by a large initial state, reach several
+times the RMS, and an element of such a row may cancel to near zero).  Every element
+satisfies |gpu - oracle| <= 1e-2 * max(RMS(oracle), scale_i), with scale_i the size of its
+terms: for dq, dk, dv and dinitial_state the RMS of the element's row (last axis: one
+state row and one gradient row form all of it); for dlog_ig_t = k_t . dk_t the product of
+the norms; for the log-gate gradients, sums over tokens of q_t . dq_t - k_t . dk_t, the root
+sum of squares of those norm products.
 """
 import numpy as np
 import pytest
@@ -14,7 +24,7 @@ from gated_linear_rnn_chunkwise_amd import inputs as gin
 
 pytestmark = pytest.mark.gpu
 
-TOL = 1e-4
+TOLS = {"f32": 1e-4, "bf16": 1e-2}
 
 
 def rel_err(got, ref):
@@ -41,13 +51,51 @@ def run(gla, w, d, dout, s0, df):
     return {k: None if v is None else v.cpu().double().numpy() for k, v in r.items()}
 
 
-def check_all(got, ref, what):
+def dot_scale(a, b):
+    """|a_t| |b_t| per token: the size of the terms of the dot product a_t . b_t."""
+    a = np.asarray(a.double().numpy() if hasattr(a, "double") else a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    return np.sqrt((a * a).sum(axis=-1) * (b * b).sum(axis=-1))
+
+
+def row_scale(x):
+    x = np.asarray(x, dtype=np.float64)
+    return np.sqrt(np.mean(x * x, axis=-1, keepdims=True))
+
+
+def gate_scale(d, ref, gate):
+    """Root sum of squares of the dot products that each log-gate gradient element sums:
+    per (b, h, t) over s >= t (per-token gate), per head over b and t weighted by t + 1
+    (fixed gate, the sum over t of the per-token sums)."""
+    sq = dot_scale(d["q"], ref["dq"]) ** 2 + dot_scale(d["k"], ref["dk"]) ** 2
+    if gate == "head":
+        return np.sqrt(np.cumsum(sq[..., ::-1], axis=-1)[..., ::-1])
+    w = (np.arange(sq.shape[-1]) + 1.0) ** 2
+    return np.sqrt((sq * w).sum(axis=(0, 2)))
+
+
+def scaled_err(got, ref, scale):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    rms = float(np.sqrt(np.mean(ref * ref)))
+    return float(np.max(np.abs(got - ref) / np.maximum(np.maximum(scale, rms), 1e-300)))
+
+
+def check_all(got, ref, what, dtype, d=None, gate=None):
+    tol = TOLS[dtype]
     for key in ("dq", "dk", "dv", "dlog_alpha", "dlog_ig", "dinitial_state"):
         if ref[key] is None:
             assert got[key] is None, (what, key)
             continue
-        e = rel_err(got[key], ref[key])
-        assert e <= TOL, "%s %s: max|err|/RMS = %.3e" % (what, key, e)
+        if dtype == "f32":
+            e = rel_err(got[key], ref[key])
+        elif key == "dlog_alpha":
+            e = scaled_err(got[key], ref[key], gate_scale(d, ref, gate))
+        elif key == "dlog_ig":
+            e = scaled_err(got[key], ref[key], dot_scale(d["k"], ref["dk"]))
+        else:
+            e = scaled_err(got[key], ref[key], row_scale(ref[key]))
+        assert e <= tol, "%s %s: max|err|/scale = %.3e" % (what, key, e)
 
 
 CASES = []
@@ -65,7 +113,7 @@ def test_backward_small_shapes(gpu_lib, dtype, gate, ig, Dk, Dv, L):
     dout, s0, df = grads_in(w, L, with_s0=(L != 70), with_df=(L != 333))
     got = run(gpu_lib, w, d, dout, s0, df)
     ref = oracle.backward(d["q"], d["k"], d["v"], dout, gate, d["log_alpha"], d["log_ig"], s0, df)
-    check_all(got, ref, w.name)
+    check_all(got, ref, w.name, dtype, d, gate)
 
 
 def test_backward_strong_decay(gpu_lib):
@@ -79,7 +127,7 @@ def test_backward_strong_decay(gpu_lib):
     dout, s0, df = grads_in(w, 5, True, True)
     got = run(gpu_lib, w, d, dout, s0, df)
     ref = oracle.backward(d["q"], d["k"], d["v"], dout, "head", la, d["log_ig"], s0, df)
-    check_all(got, ref, "strong decay")
+    check_all(got, ref, "strong decay", "bf16", d, "head")
 
 
 def test_backward_retnet_workload_sampled_heads(gpu_lib):
@@ -96,12 +144,16 @@ def test_backward_retnet_workload_sampled_heads(gpu_lib):
     sel = lambda x: x.reshape(-1, *x.shape[2:])[rows][None]
     la = d["log_alpha"][hh].reshape(1, 1, 1).expand(1, len(rows), w.L).contiguous()
     ref = oracle.backward(sel(d["q"]), sel(d["k"]), sel(d["v"]), sel(dout), "head", la, None, None, sel(df))
+    tol = TOLS[w.dtype]
     for key in ("dq", "dk", "dv", "dinitial_state"):
-        e = rel_err(got[key].reshape(-1, *got[key].shape[2:])[rows], ref[key][0])
-        assert e <= TOL, "%s: max|err|/RMS = %.3e" % (key, e)
+        g = got[key].reshape(-1, *got[key].shape[2:])[rows]
+        e = scaled_err(g, ref[key][0], row_scale(ref[key][0]))
+        assert e <= tol, "%s: max|err|/scale = %.3e" % (key, e)
+    # the fixed gate's gradient of head 5 sums the sampled slices' per-token gradients
     total = float(ref["dlog_alpha"].sum())
-    scale = max(abs(total), 1e-3 * float(np.abs(ref["dlog_alpha"]).sum()))
-    assert abs(got["dlog_alpha"][hh] - total) <= TOL * scale, (got["dlog_alpha"][hh], total)
+    dsel = {"q": sel(d["q"]), "k": sel(d["k"])}
+    scale = float(np.sqrt(np.sum(gate_scale(dsel, ref, "head_const") ** 2)))  # over the sampled slices
+    assert abs(got["dlog_alpha"][hh] - total) <= tol * max(abs(total), scale), (got["dlog_alpha"][hh], total)
 
 
 def test_backward_rejects_per_channel_gate(gpu_lib):
