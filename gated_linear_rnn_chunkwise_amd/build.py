@@ -26,7 +26,7 @@ COMMON = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", INCLUDE, "-I", CSRC, "-Wall", "-Wno-unused-variable", "-Wno-unused-but-set-variable",
 ]
-SOURCES = ["gla_kernels.hip", "gla_bwd.hip", "gla_api.cpp"]
+SOURCES = ["gla_kernels.hip", "gla_bwd.hip", "gla_bwd_chan.hip", "gla_api.cpp"]
 
 
 def _compile(src: str) -> str:

@@ -31,6 +31,9 @@ hipError_t bwd_scale(const float *src, const uint32_t *mx, float *dst, int BH, s
 hipError_t bwd_finish(const gla_bwd_desc &d, const float *oA, const float *oB, float *g, const float *finA,
                       const float *finC, const float *dfT, float *part, const uint32_t *mx, hipStream_t st);
 constexpr int kH16Q = 1, kH16K = 2, kH16V = 4;  // fp16 operand bits of launch_forward
+size_t chan_scratch_floats(int BH, int L, int Dk);
+hipError_t chan_backward(const gla_bwd_desc &d, const float *s0T, const float *dfT, float *finA, float *finC,
+                         float *scratch, hipStream_t st);
 }
 
 namespace {
@@ -328,7 +331,6 @@ int validate_bwd(const gla_bwd_desc *d) {
     const int64_t bh = int64_t(d->B) * d->H;
     if (bh > (int64_t(1) << 24)) return GLA_ERR_INVALID_ARG;
     if (bh * d->L > lim / std::max(d->Dk, d->Dv)) return GLA_ERR_INVALID_ARG;
-    if (d->gate_kind == GLA_GATE_CHANNEL) return GLA_ERR_UNSUPPORTED;
     if (!bwd_dim_ok(d->Dk) || !bwd_dim_ok(d->Dv)) return GLA_ERR_UNSUPPORTED;
     return GLA_OK;
 }
@@ -358,7 +360,7 @@ gla_desc bwd_pass_desc(const gla_bwd_desc *d, int dk, int dv, const void *q, con
 }
 
 struct BwdPlan {
-    size_t rq, rk, rv, rdo, fdo, mx, mxp, s0A, lar, oA, oB, finA, finC, s0T, dfT, g, part, fws, total;
+    size_t chs, rq, rk, rv, rdo, fdo, mx, mxp, s0A, lar, oA, oB, finA, finC, s0T, dfT, g, part, fws, total;
     size_t fws_bytes;
 };
 
@@ -374,6 +376,19 @@ int bwd_plan(const gla_bwd_desc *d, BwdPlan *p) {
         off += align256(bytes);
         return o;
     };
+    if (d->gate_kind == GLA_GATE_CHANNEL) {
+        // per-channel gate: the passes read the caller's tensors; scratch for the transposed
+        // states, the final states and the log-gate scan
+        *p = BwdPlan{};
+        p->finA = take(bh * Dk * Dv * 4);
+        p->finC = take(bh * Dk * Dv * 4);
+        p->s0T = d->initial_state ? take(bh * Dk * Dv * 4) : 0;
+        p->dfT = d->dfinal_state ? take(bh * Dk * Dv * 4) : 0;
+        p->chs = take(gla::chan_scratch_floats(d->B * d->H, d->L, d->Dk) * 4);
+        p->fws_bytes = 0;
+        p->total = off;
+        return GLA_OK;
+    }
     // operand copies: fp32 for fp32 inputs; bf16 reversed q, k, v and fp16 output gradients
     const size_t eb = bf ? 2 : 4;
     p->rq = take(bh * L * Dk * eb);
@@ -463,6 +478,17 @@ int gla_bwd(const gla_bwd_desc *d, void *stream) {
         return rc == GLA_OK;
     };
     auto V = [&](size_t off) { return static_cast<void *>(ws + off); };
+    if (d->gate_kind == GLA_GATE_CHANNEL) {
+        if (d->initial_state) ok(gla::bwd_transpose(d->initial_state, nullptr, F(p.s0T), BH, Dk, Dv, s));
+        if (d->dfinal_state) ok(gla::bwd_transpose(d->dfinal_state, nullptr, F(p.dfT), BH, Dk, Dv, s));
+        const float *s0T = d->initial_state ? F(p.s0T) : nullptr;
+        const float *dfT = d->dfinal_state ? F(p.dfT) : nullptr;
+        if (rc == GLA_OK) ok(gla::chan_backward(*d, s0T, dfT, F(p.finA), F(p.finC), F(p.chs), s));
+        if (rc == GLA_OK)
+            ok(gla::bwd_finish(*d, nullptr, nullptr, nullptr, F(p.finA), F(p.finC), dfT, nullptr, nullptr, s));
+        if (owned) (void)hipFreeAsync(ws, s);
+        return rc;
+    }
     uint32_t *mx = bf ? reinterpret_cast<uint32_t *>(ws + p.mx) : nullptr;
     // operands of the three passes
     if (bf) {

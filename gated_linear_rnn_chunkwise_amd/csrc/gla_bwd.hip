@@ -320,8 +320,8 @@ __global__ __launch_bounds__(256) void bwd_gate_reduce_kernel(gla_bwd_desc d, co
     }
 }
 
-// dinitial_state = a_0 G_0: the first pass's final state times the first token's decay (and
-// 1/s when finA carries the scale).
+// dinitial_state = diag(alpha_0) G_0: the first pass's final state times the first token's
+// decay (and 1/s when finA carries the scale).
 __global__ __launch_bounds__(256) void bwd_dinit_kernel(gla_bwd_desc d, const float *finA, const uint32_t *mx,
                                                        size_t m, size_t total) {
     const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
@@ -330,6 +330,8 @@ __global__ __launch_bounds__(256) void bwd_dinit_kernel(gla_bwd_desc d, const fl
     float a0 = mx ? 1.f / scale_of(mx[bh]) : 1.f;
     if (d.gate_kind == GLA_GATE_HEAD) a0 *= exp2f(d.log_alpha[bh * d.L] * kLog2eB);
     else if (d.gate_kind == GLA_GATE_HEAD_CONST) a0 *= exp2f(d.log_alpha[bh % d.H] * kLog2eB);
+    else if (d.gate_kind == GLA_GATE_CHANNEL)  // row r of G_0 decays with channel r of token 0
+        a0 *= exp2f(d.log_alpha[bh * d.L * d.Dk + (i % m) / d.Dv] * kLog2eB);
     d.dinitial_state[i] = a0 * finA[i];
 }
 

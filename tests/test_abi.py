@@ -254,9 +254,13 @@ def test_bwd_valid_and_workspace_grows_with_length(lib):
     assert st == gla.GLA_OK and n1 > 0
     st, n2 = bstatus(lib, bdesc(L=1000))
     assert st == gla.GLA_OK and n2 > n1
-    for kind, la in ((gla.GATE_NONE, None), (gla.GATE_HEAD_CONST, A)):
+    for kind, la in ((gla.GATE_NONE, None), (gla.GATE_HEAD_CONST, A), (gla.GATE_CHANNEL, A)):
         st, _ = bstatus(lib, bdesc(gate_kind=kind, log_alpha=la, dlog_alpha=la))
         assert st == gla.GLA_OK
+    # the per-channel path's scratch grows with the length too (the log-gate scan rows)
+    st, c1 = bstatus(lib, bdesc(gate_kind=gla.GATE_CHANNEL))
+    st2, c2 = bstatus(lib, bdesc(gate_kind=gla.GATE_CHANNEL, L=1000))
+    assert st == st2 == gla.GLA_OK and c2 > c1
 
 
 @pytest.mark.parametrize("kw", [dict(dq=None), dict(dout=None), dict(q=None), dict(L=0), dict(dq=A + 4),
@@ -267,7 +271,7 @@ def test_bwd_invalid_arguments(lib, kw):
     assert bstatus(lib, bdesc(**kw))[0] == gla.GLA_ERR_INVALID_ARG
 
 
-@pytest.mark.parametrize("kw", [dict(gate_kind=gla.GATE_CHANNEL), dict(Dk=100), dict(Dv=512), dict(Dk=32)])
+@pytest.mark.parametrize("kw", [dict(Dk=100), dict(Dv=512), dict(Dk=32), dict(gate_kind=gla.GATE_CHANNEL, Dv=96)])
 def test_bwd_unsupported(lib, kw):
     assert bstatus(lib, bdesc(**kw))[0] == gla.GLA_ERR_UNSUPPORTED
 

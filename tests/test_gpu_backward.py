@@ -156,10 +156,35 @@ def test_backward_retnet_workload_sampled_heads(gpu_lib):
     assert abs(got["dlog_alpha"][hh] - total) <= tol * max(abs(total), scale), (got["dlog_alpha"][hh], total)
 
 
-def test_backward_rejects_per_channel_gate(gpu_lib):
-    w = gin.custom(1, 1, 64, 64, 64, 64, gate="channel")
-    d = gin.make_inputs(w, seed=0)
-    dout = torch.randn(1, 1, 64, 64)
-    with pytest.raises(gpu_lib.GlaError) as ei:
-        run(gpu_lib, w, d, dout, None, None)
-    assert ei.value.status == gpu_lib.GLA_ERR_UNSUPPORTED
+CH_CASES = []
+for dtype in ("bf16", "f32"):
+    for ig in (False, True):
+        for Dk, Dv in ((64, 64), (128, 128), (64, 128), (256, 64), (128, 256)):
+            CH_CASES.append((dtype, ig, Dk, Dv))
+
+
+@pytest.mark.parametrize("dtype,ig,Dk,Dv", CH_CASES)
+@pytest.mark.parametrize("L", [1, 70, 333])
+def test_backward_per_channel_gate(gpu_lib, dtype, ig, Dk, Dv, L):
+    # the per-channel path computes in fp32 throughout (exact decay factors), so the fp32 bar
+    # applies to both input dtypes
+    w = gin.custom(2, 2, L, Dk, Dv, 64, dtype=dtype, gate="channel", input_gate=ig)
+    d = gin.make_inputs(w, seed=L + Dk + 3 * Dv)
+    dout, s0, df = grads_in(w, L + 1, with_s0=(L != 70), with_df=(L != 333))
+    got = run(gpu_lib, w, d, dout, s0, df)
+    ref = oracle.backward(d["q"], d["k"], d["v"], dout, "channel", d["log_alpha"], d["log_ig"], s0, df)
+    check_all(got, ref, w.name, "f32")
+
+
+def test_backward_per_channel_strong_decay(gpu_lib):
+    # channels with a near-zero or zero gate on some tokens, in the forward and reversed passes
+    w = gin.custom(1, 2, 150, 64, 64, 64, dtype="bf16", gate="channel", input_gate=True)
+    d = gin.make_inputs(w, seed=4)
+    la = d["log_alpha"].clone()
+    la[:, :, 40, :16] = -30.0
+    la[:, :, 100:103, 8:40] = -1e4
+    d["log_alpha"] = la
+    dout, s0, df = grads_in(w, 6, True, True)
+    got = run(gpu_lib, w, d, dout, s0, df)
+    ref = oracle.backward(d["q"], d["k"], d["v"], dout, "channel", la, d["log_ig"], s0, df)
+    check_all(got, ref, "per-channel strong decay", "f32")
