@@ -22,6 +22,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "gla.h"
 #include "gla_layout.h"
 
@@ -41,6 +43,11 @@ struct ChanPass {
     const float *oli;      // output row weight exp(oli[bh][destination row]), or null
     float *fin;            // [BH][Dq][Dn] or null
     int L, Dn;
+    // Sequence segments run in parallel: segment s covers pass tokens [s seg_len, (s+1) seg_len).
+    // ws_state [BH][nseg-1][Dq][Dn]: a segment's own state (state kernel), then the state
+    // entering segment s+1 (scan); ws_decay [BH][nseg-1][Dg]: the segment's decay.
+    int seg_len, nseg;
+    float *ws_state, *ws_decay;
 };
 
 namespace {
@@ -53,6 +60,18 @@ __device__ __forceinline__ float ld_in(const void *p, int dt, size_t i) {
     return __uint_as_float((uint32_t)reinterpret_cast<const uint16_t *>(p)[i] << 16);
 }
 
+// Raw input bits (fp32, or bf16 in the low half) and their value; the dtype is a template
+// argument so that a load's result is not consumed on the path that issues it.
+template <bool F32>
+__device__ __forceinline__ uint32_t ld_raw(const void *p, size_t i) {
+    if constexpr (F32) return reinterpret_cast<const uint32_t *>(p)[i];
+    else return (uint32_t)reinterpret_cast<const uint16_t *>(p)[i];
+}
+template <bool F32>
+__device__ __forceinline__ float raw_val(uint32_t x) {
+    return F32 ? __uint_as_float(x) : __uint_as_float(x << 16);
+}
+
 __device__ __forceinline__ float fexp2c(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Workgroup barrier over LDS only: global loads in flight (the next block's operands) are
@@ -63,247 +82,343 @@ __device__ __forceinline__ void lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-// Sum over the 8 consecutive lanes of a row group: quad swaps, then the half-row mirror
-// (lane i and 7 - i of each group of eight).
-__device__ __forceinline__ float sum8(float x) {
-    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
-    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
-    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xF, 0xF, false));  // row_half_mirror
-    return x;
-}
-
 __device__ __forceinline__ float log2_gate(float la) {
     const float x = la * kLog2eC;
     return x < -150.f ? -150.f : x;
 }
 
-// grid = BH * (Dn / 64) workgroups of 512 threads.  Thread tid owns value column
-// n = tid >> 3 of the workgroup's 64 and the RD consecutive state rows from r RD, r = tid & 7.
-// The operands of the next block are fetched into registers while the current one is
-// computed.
-constexpr int kThr = 512;
+typedef float f32x4c __attribute__((ext_vector_type(4)));
+
+// LDS plan of a pass (floats): q and k rows padded to DQ + 4, transposed tiles with rows of
+// 16 tokens padded to 20.
 template <bool KG, int DQ>
-__global__ __launch_bounds__(kThr) void chan_pass_kernel(ChanPass a) {
-    constexpr int RD = DQ / 8;
-    constexpr int QP = DQ + 4;            // padded row of q, k and key-side decays (16-byte aligned)
-    constexpr int GW = KG ? DQ : 64;      // gate columns of a block
-    constexpr int GP = GW + 4;
-    constexpr int NQ = kBlk * DQ / kThr;  // q (and k) elements fetched per thread
-    constexpr int NG = kBlk * GW / kThr;  // gate elements fetched per thread
-    constexpr int NV = kBlk * 64 / kThr;  // value elements fetched per thread
-    __shared__ __align__(16) float sQ[kBlk * QP];
-    __shared__ __align__(16) float sK[kBlk * QP];
-    __shared__ __align__(16) float sB[kBlk * GP];
-    __shared__ __align__(16) float sV[kBlk * 64];
-    __shared__ __align__(16) float sVf[kBlk * 64];
-    __shared__ __align__(16) float sP[kBlk * kBlk];
+struct ChanLds {
+    static constexpr int QP = DQ + 4, TP = 20;
+    static constexpr int Q = 0;                           // [16][QP] q, then the decayed q (key gate)
+    static constexpr int KX = Q + kBlk * QP;              // [16][QP] k (value gate) or k 2^(-b_s) (key gate)
+    static constexpr int KT = KX + kBlk * QP;             // [DQ][TP] decayed k, transposed
+    static constexpr int B = KT + DQ * TP;                // key gate [16][QP] / value gate [64][TP]: log2 decays
+    static constexpr int VT = B + (KG ? kBlk * QP : 64 * TP);  // [64][TP] v, transposed
+    static constexpr int VF = VT + 64 * TP;               // [64][TP] decayed v, transposed (value gate)
+    static constexpr int P = VF + (KG ? 0 : 64 * TP);     // [16][TP] scores
+    static constexpr int FLAG = P + kBlk * TP;            // strong-decay flag of the block
+    static constexpr int TOTAL = FLAG + 4;
+};
+
+__device__ __forceinline__ f32x4c mfma4(float a, float b, f32x4c c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// A block whose running log2 decay reaches below this (in any key channel) forms its
+// key-gated scores exactly instead of as a product of q 2^(b_t) and k 2^(-b_s).
+constexpr float kFactorFloor = -60.f;
+
+// grid = BH * (Dn / 64) workgroups of 256 threads.  Wave w owns value columns 16 w .. 16 w + 15
+// of the workgroup's 64; lane l (c16 = l & 15, g = l >> 4) holds the state in matrix-core
+// accumulator layout: rows 16 j + 4 g + e (j < DQ / 16, e < 4) of column 16 w + c16.  Both
+// block products run on the fp32 matrix cores (16x16x4):
+//   output  O[t][n] += sum_d q'[t][d] S[d][n], with the contraction index of step (j, e) and
+//           lane group g being d = 16 j + 4 g + e, so that each lane's own state registers
+//           are its B operand;
+//   state   S[d][n] = dec S[d][n] + sum_s k'[s][d] v'[s][n], token index s = 4 g + m.
+// The operands of the next block are fetched into registers (raw bits) while the current one
+// is computed.  FM: which of q, k, v (bits 0, 1, 2) are fp32; the others are bf16.
+// ST: the state kernel of the segments before the last (no outputs; the segment's own state
+// from zero and its decay into the workspace).
+template <bool KG, int DQ, int FM, bool ST>
+__global__ __launch_bounds__(256, 2) void chan_pass_kernel(ChanPass a) {
+    constexpr bool QF = FM & 1, KF = (FM >> 1) & 1, VF = (FM >> 2) & 1;
+    using Lp = ChanLds<KG, DQ>;
+    constexpr int QP = Lp::QP, TP = Lp::TP, NJ = DQ / 16;
+    constexpr int GW = KG ? DQ : 64;
+    constexpr int NQ = kBlk * DQ / 256;   // q (and k) elements fetched per thread
+    constexpr int NG = kBlk * GW / 256;   // gate elements fetched per thread
+    constexpr int NV = kBlk * 64 / 256;   // value elements fetched per thread
+    extern __shared__ __align__(16) float lds[];
+    float *sQ = lds + Lp::Q, *sKX = lds + Lp::KX, *sKT = lds + Lp::KT, *sB = lds + Lp::B;
+    float *sVT = lds + Lp::VT, *sVF = lds + Lp::VF, *sP = lds + Lp::P;
+    int *sFlag = reinterpret_cast<int *>(lds + Lp::FLAG);
 
     const int ndt = a.Dn / 64;
-    const size_t bh = blockIdx.x / (unsigned)ndt;
-    const int n0 = (int)(blockIdx.x % (unsigned)ndt) * 64;
-    const int tid = (int)threadIdx.x, n = tid >> 3, r = tid & 7;
+    const int nsb = ST ? a.nseg - 1 : a.nseg;
+    size_t id = blockIdx.x;
+    const int seg = (int)(id % (unsigned)nsb);
+    id /= (unsigned)nsb;
+    const int n0 = (int)(id % (unsigned)ndt) * 64;
+    const size_t bh = id / (unsigned)ndt;
+    const int tid = (int)threadIdx.x, lane = tid & 63, w = tid >> 6, c16 = lane & 15, g = lane >> 4;
+    const int ncol = 16 * w + c16;        // this lane's column within the workgroup's 64
     const int L = a.L, Dn = a.Dn;
     const int Dg = KG ? DQ : Dn;
-    const int d0 = r * RD;
+    const int ub = seg * a.seg_len, ue = min(L, ub + a.seg_len);
+    const size_t nsm = (size_t)(a.nseg - 1);
 
-    float S[RD];
+    // the state entering the segment: the initial state, the scanned boundary state, or zero
+    const float *s_in = (ST || seg == 0) ? nullptr : a.ws_state + (bh * nsm + seg - 1) * (size_t)DQ * Dn;
+    f32x4c S[NJ];
 #pragma unroll
-    for (int i = 0; i < RD; ++i) S[i] = a.s0 ? a.s0[(bh * DQ + d0 + i) * Dn + n0 + n] : 0.f;
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            S[j][e] = s_in ? s_in[(size_t)(16 * j + 4 * g + e) * Dn + n0 + ncol] : 0.f;
+    if (!ST && seg == 0 && a.s0) {
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                S[j][e] = a.s0[(bh * DQ + 16 * j + 4 * g + e) * Dn + n0 + ncol];
+    }
+    float gtot = 0.f;  // state kernel: the segment's log2 decay of column tid (tid < GW)
 
-    float fq[NQ], fk[NQ], fg[NG], fv[NV];
-    // operands of the block at u0 (zero past the sequence end) and per-token log2 gates
+    // next block: raw q, k, v bits, value-row and output-row log weights, log gates
+    uint32_t fq[NQ], fk[NQ], fv[NV];
+    float fvl[NV], fg[NG], fol[4], ol[4];
     auto fetch = [&](int u0) {
 #pragma unroll
-        for (int j = 0; j < NQ; ++j) {
-            const int idx = tid + j * kThr, t = idx / DQ, d = idx % DQ, u = u0 + t;
-            fq[j] = fk[j] = 0.f;
-            if (u < L) {
+        for (int i = 0; i < NQ; ++i) {
+            const int idx = tid + i * 256, t = idx / DQ, d = idx % DQ, u = u0 + t;
+            fq[i] = fk[i] = 0u;
+            if (u < ue) {
                 const size_t rq = bh * L + (a.qrev ? L - 1 - u : u), rk = bh * L + (a.krev ? L - 1 - u : u);
-                fq[j] = ld_in(a.q, a.qdt, rq * DQ + d);
-                fk[j] = ld_in(a.k, a.kdt, rk * DQ + d);
+                fq[i] = ld_raw<QF>(a.q, rq * DQ + d);
+                fk[i] = ld_raw<KF>(a.k, rk * DQ + d);
             }
         }
 #pragma unroll
-        for (int j = 0; j < NV; ++j) {
-            const int idx = tid + j * kThr, t = idx >> 6, c = idx & 63, u = u0 + t;
-            fv[j] = 0.f;
-            if (u < L) {
+        for (int i = 0; i < NV; ++i) {
+            const int idx = tid + i * 256, t = idx >> 6, c = idx & 63, u = u0 + t;
+            fv[i] = 0u;
+            fvl[i] = 0.f;
+            if (u < ue) {
                 const size_t rv = bh * L + (a.vrev ? L - 1 - u : u);
-                fv[j] = ld_in(a.v, a.vdt, rv * Dn + n0 + c);
-                if (a.vli) fv[j] *= fexp2c(a.vli[rv] * kLog2eC);
+                fv[i] = ld_raw<VF>(a.v, rv * Dn + n0 + c);
+                if (a.vli) fvl[i] = a.vli[rv];
             }
         }
 #pragma unroll
-        for (int j = 0; j < NG; ++j) {
-            const int idx = tid + j * kThr, t = idx / GW, c = idx % GW, u = u0 + t;
-            fg[j] = 0.f;
-            if (u < L && !(a.grev && u == 0)) {
+        for (int i = 0; i < NG; ++i) {
+            const int idx = tid + i * 256, t = idx / GW, c = idx % GW, u = u0 + t;
+            fg[i] = 0.f;
+            if (u < ue && !(a.grev && u == 0)) {
                 const size_t rg = bh * L + (a.grev ? L - u : u);
-                fg[j] = log2_gate(a.la[rg * Dg + (KG ? c : n0 + c)]);
+                fg[i] = a.la[rg * Dg + (KG ? c : n0 + c)];
             }
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int u = u0 + 4 * g + e;
+            fol[e] = 0.f;
+            if (!ST && a.oli && u < ue) fol[e] = a.oli[bh * L + (a.orev ? L - 1 - u : u)];
         }
     };
-    fetch(0);
+    fetch(ub);
 
-    for (int u0 = 0; u0 < L; u0 += kBlk) {
+    for (int u0 = ub; u0 < ue; u0 += kBlk) {
+        // ---- raw operands into LDS: q, k by rows, v transposed, log2 gates (key gate by
+        // token rows, value gate transposed)
 #pragma unroll
-        for (int j = 0; j < NQ; ++j) {
-            const int idx = tid + j * kThr, t = idx / DQ, d = idx % DQ;
-            sQ[t * QP + d] = fq[j];
-            sK[t * QP + d] = fk[j];
+        for (int i = 0; i < NQ; ++i) {
+            const int idx = tid + i * 256, t = idx / DQ, d = idx % DQ;
+            sQ[t * QP + d] = raw_val<QF>(fq[i]);
+            sKX[t * QP + d] = raw_val<KF>(fk[i]);
         }
 #pragma unroll
-        for (int j = 0; j < NV; ++j) sV[tid + j * kThr] = fv[j];
-#pragma unroll
-        for (int j = 0; j < NG; ++j) {
-            const int idx = tid + j * kThr;
-            sB[(idx / GW) * GP + idx % GW] = fg[j];
+        for (int i = 0; i < NV; ++i) {
+            const int idx = tid + i * 256;
+            float v = raw_val<VF>(fv[i]);
+            if (a.vli) v *= fexp2c(fvl[i] * kLog2eC);
+            sVT[(idx & 63) * TP + (idx >> 6)] = v;
         }
+#pragma unroll
+        for (int i = 0; i < NG; ++i) {
+            const int idx = tid + i * 256, t = idx / GW, c = idx % GW;
+            const float x = fg[i] == 0.f ? 0.f : log2_gate(fg[i]);
+            if constexpr (KG) sB[t * QP + c] = x;
+            else sB[c * TP + t] = x;
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ol[e] = fol[e];
+        if (tid == 0) *sFlag = 0;
         lds_sync();
-        if (u0 + kBlk < L) fetch(u0 + kBlk);
-        // running log2 decay inside the block, inclusive
+        if (u0 + kBlk < ue) fetch(u0 + kBlk);
+        // ---- running log2 decays inside the block, inclusive
         if (tid < GW) {
             float b[kBlk];
 #pragma unroll
-            for (int t = 0; t < kBlk; ++t) b[t] = sB[t * GP + tid];
+            for (int t = 0; t < kBlk; ++t) b[t] = KG ? sB[t * QP + tid] : sB[tid * TP + t];
             float run = 0.f;
 #pragma unroll
             for (int t = 0; t < kBlk; ++t) {
                 run += b[t];
-                sB[t * GP + tid] = run;
+                if constexpr (KG) sB[t * QP + tid] = run;
+                else sB[tid * TP + t] = run;
             }
+            if (KG && run < kFactorFloor) *sFlag = 1;
+            gtot += run;
         }
         lds_sync();
-        // ---- scores P[t][s] (s <= t); the key gate enters them exactly
-        if (tid < kBlk * kBlk) {
+        const bool exact = !ST && KG && *sFlag != 0;
+        if (exact) {
+            // strong decay in this block: key-gated scores with every factor formed exactly
             const int t = tid >> 4, s = tid & 15;
             float p = 0.f;
-            if (s <= t) {
-#pragma unroll 4
-                for (int d = 0; d < DQ; d += 4) {
-                    const float4 x = *reinterpret_cast<const float4 *>(sQ + t * QP + d);
-                    const float4 y = *reinterpret_cast<const float4 *>(sK + s * QP + d);
-                    if constexpr (KG) {
-                        const float4 bt = *reinterpret_cast<const float4 *>(sB + t * GP + d);
-                        const float4 bs = *reinterpret_cast<const float4 *>(sB + s * GP + d);
-                        p += x.x * y.x * fexp2c(bt.x - bs.x) + x.y * y.y * fexp2c(bt.y - bs.y) +
-                             x.z * y.z * fexp2c(bt.z - bs.z) + x.w * y.w * fexp2c(bt.w - bs.w);
-                    } else {
-                        p += x.x * y.x + x.y * y.y + x.z * y.z + x.w * y.w;
-                    }
-                }
-            }
-            sP[t * kBlk + s] = p;
+            if (s <= t)
+                for (int d = 0; d < DQ; ++d)
+                    p += sQ[t * QP + d] * sKX[s * QP + d] * fexp2c(sB[t * QP + d] - sB[s * QP + d]);
+            sP[t * TP + s] = p;
+            lds_sync();
         }
-        lds_sync();
-        // ---- decay-weighted operands: key gate: q_t 2^(b_t), k_s 2^(b_15 - b_s); value gate:
-        // v_s 2^(b_15 - b_s)
+        // ---- decay-weighted operands
         if constexpr (KG) {
-            for (int idx = tid; idx < kBlk * DQ; idx += kThr) {
+            for (int idx = tid; idx < kBlk * DQ; idx += 256) {
                 const int t = idx / DQ, d = idx % DQ;
-                sQ[t * QP + d] *= fexp2c(sB[t * GP + d]);
-                sK[t * QP + d] *= fexp2c(sB[(kBlk - 1) * GP + d] - sB[t * GP + d]);
+                const float bt = sB[t * QP + d], b15 = sB[(kBlk - 1) * QP + d];
+                const float kv = sKX[t * QP + d];
+                sQ[t * QP + d] *= fexp2c(bt);             // q_t 2^(b_t)
+                sKT[d * TP + t] = kv * fexp2c(b15 - bt);  // k_t 2^(b_15 - b_t)
+                sKX[t * QP + d] = kv * fexp2c(-bt);       // k_t 2^(-b_t), for the scores
             }
         } else {
-            for (int idx = tid; idx < kBlk * 64; idx += kThr) {
-                const int t = idx >> 6, c = idx & 63;
-                sVf[idx] = sV[idx] * fexp2c(sB[(kBlk - 1) * GP + c] - sB[t * GP + c]);
+            for (int idx = tid; idx < kBlk * DQ; idx += 256) {
+                const int t = idx / DQ, d = idx % DQ;
+                sKT[d * TP + t] = sKX[t * QP + d];
+            }
+            for (int idx = tid; idx < kBlk * 64; idx += 256) {
+                const int c = idx >> 4, t = idx & 15;
+                sVF[c * TP + t] = sVT[c * TP + t] * fexp2c(sB[c * TP + kBlk - 1] - sB[c * TP + t]);
             }
         }
         lds_sync();
-        // ---- outputs: the entering state's term, reduced over the eight row groups, plus the
-        // block's own tokens
-        float acc[kBlk];
+        // ---- scores P[t][s] = sum_d q[t][d] k[s][d] on the matrix cores (wave 0), s <= t
+        if (!ST && !exact && w == 0) {
+            f32x4c pc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int t = 0; t < kBlk; ++t) {
-            float x = 0.f;
+            for (int j = 0; j < NJ; ++j) {
+                const f32x4c qa = *reinterpret_cast<const f32x4c *>(sQ + c16 * QP + 16 * j + 4 * g);
+                const f32x4c kb = *reinterpret_cast<const f32x4c *>(sKX + c16 * QP + 16 * j + 4 * g);
 #pragma unroll
-            for (int i = 0; i < RD; i += 4) {
-                const float4 q4 = *reinterpret_cast<const float4 *>(sQ + t * QP + d0 + i);
-                x += q4.x * S[i] + q4.y * S[i + 1] + q4.z * S[i + 2] + q4.w * S[i + 3];
+                for (int e = 0; e < 4; ++e) pc = mfma4(qa[e], kb[e], pc);
             }
-            acc[t] = x;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int t = 4 * g + e;
+                sP[t * TP + c16] = c16 <= t ? pc[e] : 0.f;
+            }
+        }
+        if constexpr (!ST) lds_sync();
+        // ---- outputs of the block's 16 tokens for this lane's column
+        if constexpr (!ST) {
+        f32x4c O = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            const f32x4c qa = *reinterpret_cast<const f32x4c *>(sQ + c16 * QP + 16 * j + 4 * g);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) O = mfma4(qa[e], S[j][e], O);
+        }
+        if constexpr (KG) {
+            // the block's own tokens: P (decays included) times v
+            const f32x4c pa = *reinterpret_cast<const f32x4c *>(sP + c16 * TP + 4 * g);
+            const f32x4c vb = *reinterpret_cast<const f32x4c *>(sVT + ncol * TP + 4 * g);
+#pragma unroll
+            for (int m = 0; m < 4; ++m) O = mfma4(pa[m], vb[m], O);
+        } else {
+            // value gate: the entering state's term decays with the column; the block's own
+            // tokens with exact factors 2^(b_t - b_s), s <= t
+            float vc[kBlk], bc[kBlk];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const f32x4c v4 = *reinterpret_cast<const f32x4c *>(sVT + ncol * TP + 4 * m);
+                const f32x4c b4 = *reinterpret_cast<const f32x4c *>(sB + ncol * TP + 4 * m);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) vc[4 * m + e] = v4[e], bc[4 * m + e] = b4[e];
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                float bt = bc[0];
+#pragma unroll
+                for (int m = 1; m < kBlk; ++m) bt = (4 * g + e == m) ? bc[m] : bt;
+                float o = O[e] * fexp2c(bt);
+                const float *prow = sP + (4 * g + e) * TP;
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const f32x4c p4 = *reinterpret_cast<const f32x4c *>(prow + 4 * m);
+#pragma unroll
+                    for (int x = 0; x < 4; ++x) {
+                        const int s2 = 4 * m + x;
+                        const float f = s2 <= 4 * g + e ? fexp2c(bt - bc[s2]) : 0.f;
+                        o += p4[x] * vc[s2] * f;
+                    }
+                }
+                O[e] = o;
+            }
         }
 #pragma unroll
-        for (int t = 0; t < kBlk; ++t) acc[t] = sum8(acc[t]);
-        float vcol[kBlk];
-#pragma unroll
-        for (int s = 0; s < kBlk; ++s) vcol[s] = sV[s * 64 + n];
-        // lane r of the group finishes tokens r and r + 8 (no divergence: selects, and a fixed
-        // loop over the block's tokens with the causal mask as a select)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int t = r + 8 * h;
-            float o = 0.f;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) o = (r == j) ? acc[j + 8 * h] : o;
-            const float4 *prow = reinterpret_cast<const float4 *>(sP + t * kBlk);
-            float pr[kBlk];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const float4 p4 = prow[j];
-                pr[4 * j] = p4.x, pr[4 * j + 1] = p4.y, pr[4 * j + 2] = p4.z, pr[4 * j + 3] = p4.w;
-            }
-            if constexpr (KG) {
-#pragma unroll
-                for (int s2 = 0; s2 < kBlk; ++s2) o += pr[s2] * vcol[s2];  // P is zero above the diagonal
-            } else {
-                const float bt = sB[t * GP + n];
-                o *= fexp2c(bt);
-#pragma unroll
-                for (int s2 = 0; s2 < kBlk; ++s2) {
-                    const float f = s2 <= t ? fexp2c(bt - sB[s2 * GP + n]) : 0.f;
-                    o += pr[s2] * vcol[s2] * f;
-                }
-            }
-            const int u = u0 + t;
-            if (u < L) {
+        for (int e = 0; e < 4; ++e) {
+            const int u = u0 + 4 * g + e;
+            if (u < ue) {
                 const size_t dst = bh * L + (a.orev ? L - 1 - u : u);
-                if (a.oli) o *= fexp2c(a.oli[dst] * kLog2eC);
-                a.out[dst * Dn + n0 + n] = o;
+                float o = O[e];
+                if (a.oli) o *= fexp2c(ol[e] * kLog2eC);
+                a.out[dst * Dn + n0 + ncol] = o;
             }
+        }
         }
         // ---- state to the block end
         if constexpr (KG) {
 #pragma unroll
-            for (int i = 0; i < RD; i += 4) {
-                const float4 dec = *reinterpret_cast<const float4 *>(sB + (kBlk - 1) * GP + d0 + i);
-                float x0 = S[i] * fexp2c(dec.x), x1 = S[i + 1] * fexp2c(dec.y);
-                float x2 = S[i + 2] * fexp2c(dec.z), x3 = S[i + 3] * fexp2c(dec.w);
+            for (int j = 0; j < NJ; ++j) {
+                const f32x4c d4 = *reinterpret_cast<const f32x4c *>(sB + (kBlk - 1) * QP + 16 * j + 4 * g);
 #pragma unroll
-                for (int s = 0; s < kBlk; ++s) {
-                    const float4 k4 = *reinterpret_cast<const float4 *>(sK + s * QP + d0 + i);
-                    x0 += k4.x * vcol[s];
-                    x1 += k4.y * vcol[s];
-                    x2 += k4.z * vcol[s];
-                    x3 += k4.w * vcol[s];
-                }
-                S[i] = x0, S[i + 1] = x1, S[i + 2] = x2, S[i + 3] = x3;
+                for (int e = 0; e < 4; ++e) S[j][e] *= fexp2c(d4[e]);
             }
         } else {
-            const float dec = fexp2c(sB[(kBlk - 1) * GP + n]);
-            float vf[kBlk];
+            const float dec = fexp2c(sB[ncol * TP + kBlk - 1]);
 #pragma unroll
-            for (int s = 0; s < kBlk; ++s) vf[s] = sVf[s * 64 + n];
+            for (int j = 0; j < NJ; ++j) S[j] *= dec;
+        }
+        const float *vsrc = KG ? sVT : sVF;
+        const f32x4c vb = *reinterpret_cast<const f32x4c *>(vsrc + ncol * TP + 4 * g);
 #pragma unroll
-            for (int i = 0; i < RD; i += 4) {
-                float x0 = S[i] * dec, x1 = S[i + 1] * dec, x2 = S[i + 2] * dec, x3 = S[i + 3] * dec;
+        for (int j = 0; j < NJ; ++j) {
+            const f32x4c ka = *reinterpret_cast<const f32x4c *>(sKT + (16 * j + c16) * TP + 4 * g);
 #pragma unroll
-                for (int s = 0; s < kBlk; ++s) {
-                    const float4 k4 = *reinterpret_cast<const float4 *>(sK + s * QP + d0 + i);
-                    x0 += k4.x * vf[s];
-                    x1 += k4.y * vf[s];
-                    x2 += k4.z * vf[s];
-                    x3 += k4.w * vf[s];
-                }
-                S[i] = x0, S[i + 1] = x1, S[i + 2] = x2, S[i + 3] = x3;
-            }
+            for (int m = 0; m < 4; ++m) S[j] = mfma4(ka[m], vb[m], S[j]);
         }
         lds_sync();
     }
-    if (a.fin) {
+    if constexpr (ST) {
+        float *st = a.ws_state + (bh * nsm + seg) * (size_t)DQ * Dn;
 #pragma unroll
-        for (int i = 0; i < RD; ++i) a.fin[(bh * DQ + d0 + i) * Dn + n0 + n] = S[i];
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) st[(size_t)(16 * j + 4 * g + e) * Dn + n0 + ncol] = S[j][e];
+        // the segment's decay: per key channel (written by the first value tile) or per value column
+        if (tid < GW && (!KG || n0 == 0))
+            a.ws_decay[(bh * nsm + seg) * Dg + (KG ? tid : n0 + tid)] = fexp2c(gtot);
+    } else if (a.fin && seg == a.nseg - 1) {
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) a.fin[(bh * DQ + 16 * j + 4 * g + e) * Dn + n0 + ncol] = S[j][e];
+    }
+}
+
+// The states entering segments 1 .. nseg-1: S <- decay_s S + own_s from the initial state
+// (or zero), one thread per state element, written over the segments' own states.
+template <bool KG>
+__global__ __launch_bounds__(256) void chan_seg_scan_kernel(ChanPass a, int Dq, size_t total) {
+    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= total) return;
+    const size_t m = (size_t)Dq * a.Dn;
+    const size_t bh = i / m, e = i % m;
+    const int d = (int)(e / (size_t)a.Dn), n = (int)(e % (size_t)a.Dn);
+    const int Dg = KG ? Dq : a.Dn;
+    const size_t nsm = (size_t)(a.nseg - 1);
+    float x = a.s0 ? a.s0[i] : 0.f;
+    for (size_t s = 0; s < nsm; ++s) {
+        float *st = a.ws_state + (bh * nsm + s) * m + e;
+        x = a.ws_decay[(bh * nsm + s) * Dg + (KG ? d : n)] * x + *st;
+        *st = x;
     }
 }
 
@@ -370,22 +485,91 @@ __global__ __launch_bounds__(64) void chan_scan_kernel(gla_bwd_desc d, const flo
 
 inline unsigned nblkc(size_t n, unsigned per) { return (unsigned)((n + per - 1) / per); }
 
+// Raise the kernel's dynamic-LDS limit once per device (one bit per device ordinal).
+hipError_t lds_limit(const void *fn, std::atomic<uint64_t> &done, int bytes) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const uint64_t bit = (dev >= 0 && dev < 64) ? (uint64_t(1) << dev) : 0;
+    if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+    e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_acq_rel);
+    return e;
+}
+
+template <bool KG, int DQ, int FM>
+hipError_t launch_dq(const ChanPass &p, int BH, hipStream_t st) {
+    static std::atomic<uint64_t> done[2] = {{0}, {0}};
+    const int bytes = ChanLds<KG, DQ>::TOTAL * 4;
+    hipError_t e;
+    if (p.nseg > 1) {
+        const void *fs = reinterpret_cast<const void *>(&chan_pass_kernel<KG, DQ, FM, true>);
+        if ((e = lds_limit(fs, done[1], bytes)) != hipSuccess) return e;
+        const dim3 gs((unsigned)((size_t)BH * (p.Dn / 64) * (p.nseg - 1)));
+        hipLaunchKernelGGL((chan_pass_kernel<KG, DQ, FM, true>), gs, dim3(256), bytes, st, p);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        const size_t total = (size_t)BH * DQ * p.Dn;
+        hipLaunchKernelGGL((chan_seg_scan_kernel<KG>), dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, p,
+                           DQ, total);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    const void *fn = reinterpret_cast<const void *>(&chan_pass_kernel<KG, DQ, FM, false>);
+    if ((e = lds_limit(fn, done[0], bytes)) != hipSuccess) return e;
+    const dim3 grid((unsigned)((size_t)BH * (p.Dn / 64) * p.nseg));
+    hipLaunchKernelGGL((chan_pass_kernel<KG, DQ, FM, false>), grid, dim3(256), bytes, st, p);
+    return hipGetLastError();
+}
+
+template <bool KG, int FM>
+hipError_t launch_fm(const ChanPass &p, int BH, int Dq, hipStream_t st) {
+    if (Dq == 64) return launch_dq<KG, 64, FM>(p, BH, st);
+    if (Dq == 128) return launch_dq<KG, 128, FM>(p, BH, st);
+    return launch_dq<KG, 256, FM>(p, BH, st);
+}
+
+// The operand dtypes the three passes use: every operand fp32 (fp32 inputs), or bf16 inputs
+// with the fp32 output gradient as v (key-gated pass), k or q (value-gated passes).
 template <bool KG>
 hipError_t launch_pass(const ChanPass &p, int BH, int Dq, hipStream_t st) {
-    const dim3 grid((unsigned)((size_t)BH * (p.Dn / 64)));
-    if (Dq == 64) hipLaunchKernelGGL((chan_pass_kernel<KG, 64>), grid, dim3(kThr), 0, st, p);
-    else if (Dq == 128) hipLaunchKernelGGL((chan_pass_kernel<KG, 128>), grid, dim3(kThr), 0, st, p);
-    else hipLaunchKernelGGL((chan_pass_kernel<KG, 256>), grid, dim3(kThr), 0, st, p);
-    return hipGetLastError();
+    const int fm = (p.qdt == GLA_DTYPE_F32 ? 1 : 0) | (p.kdt == GLA_DTYPE_F32 ? 2 : 0) |
+                   (p.vdt == GLA_DTYPE_F32 ? 4 : 0);
+    if (fm == 7) return launch_fm<KG, 7>(p, BH, Dq, st);
+    if constexpr (KG) {
+        if (fm == 4) return launch_fm<KG, 4>(p, BH, Dq, st);
+    } else {
+        if (fm == 2) return launch_fm<KG, 2>(p, BH, Dq, st);
+        if (fm == 1) return launch_fm<KG, 1>(p, BH, Dq, st);
+    }
+    return hipErrorInvalidValue;
 }
 
 }  // namespace
 
+// Sequence segments of the passes: enough workgroups for about four per compute unit
+// (value tiles x segments), segments of at least 64 tokens, lengths a multiple of 16.
+constexpr int kChanTargetWorkgroups = 1024;
+void chan_segments(int BH, int L, int Dn, int *nseg, int *seg_len) {
+    const long long tiles = (long long)BH * (Dn / 64);
+    long long want = (kChanTargetWorkgroups + tiles - 1) / tiles;
+    const long long most = ((long long)L + 63) / 64;
+    if (want > most) want = most;
+    if (want < 1) want = 1;
+    int len = (int)((((long long)L + want - 1) / want + kBlk - 1) / kBlk * kBlk);
+    *seg_len = len;
+    *nseg = (int)(((long long)L + len - 1) / len);
+}
+
 // Scratch floats of the per-channel path beyond the transposed states: the g rows and the
-// segment totals.
-size_t chan_scratch_floats(int BH, int L, int Dk) {
-    const size_t nseg = ((size_t)L + kSeg - 1) / kSeg;
-    return (size_t)BH * L * Dk + (size_t)BH * nseg * Dk + (size_t)BH * Dk;
+// segment totals of the log-gate scan, and the segment states and decays of the passes.
+size_t chan_scratch_floats(int BH, int L, int Dk, int Dv) {
+    const size_t ns = ((size_t)L + kSeg - 1) / kSeg;
+    size_t n = (size_t)BH * L * Dk + (size_t)BH * ns * Dk + (size_t)BH * Dk;
+    int s1, l1, s2, l2;
+    chan_segments(BH, L, Dv, &s1, &l1);  // the key-gated pass (value dimension Dv)
+    chan_segments(BH, L, Dk, &s2, &l2);  // the value-gated passes (value dimension Dk)
+    const size_t nsm = (size_t)((s1 > s2 ? s1 : s2) - 1);
+    n += (size_t)BH * nsm * Dk * Dv + (size_t)BH * nsm * (Dk > Dv ? Dk : Dv);
+    return n;
 }
 
 // The three passes and the per-channel log-gate gradient.  s0T = initial^T and dfT =
@@ -395,8 +579,18 @@ hipError_t chan_backward(const gla_bwd_desc &d, const float *s0T, const float *d
                          float *scratch, hipStream_t st) {
     const int BH = d.B * d.H, L = d.L, Dk = d.Dk, Dv = d.Dv, dt = d.in_dtype;
     hipError_t e;
+    const int nsg = (L + kSeg - 1) / kSeg;
+    float *g_rows = scratch;
+    float *part = g_rows + (size_t)BH * L * Dk;
+    float *fterm = part + (size_t)BH * nsg * Dk;
+    float *seg_ws = fterm + (size_t)BH * Dk;
     ChanPass p{};
     p.L = L;
+    p.ws_state = seg_ws;
+    auto segs = [&](int Dn, int Dq) {
+        chan_segments(BH, L, Dn, &p.nseg, &p.seg_len);
+        p.ws_decay = seg_ws + (size_t)BH * (p.nseg - 1) * Dq * Dn;
+    };
     // dv: key-gated, reversed
     p.q = d.k, p.qdt = dt, p.qrev = 1;
     p.k = d.q, p.kdt = dt, p.krev = 1;
@@ -407,6 +601,7 @@ hipError_t chan_backward(const gla_bwd_desc &d, const float *s0T, const float *d
     p.out = d.dv, p.orev = 1, p.oli = d.log_ig;
     p.fin = finA;
     p.Dn = Dv;
+    segs(Dv, Dk);
     if ((e = launch_pass<true>(p, BH, Dk, st)) != hipSuccess) return e;
     // dk: value-gated, reversed, keys and values exchanged
     p.q = d.v, p.qdt = dt, p.qrev = 1;
@@ -416,6 +611,7 @@ hipError_t chan_backward(const gla_bwd_desc &d, const float *s0T, const float *d
     p.out = d.dk;
     p.fin = nullptr;
     p.Dn = Dk;
+    segs(Dk, Dv);
     if ((e = launch_pass<false>(p, BH, Dv, st)) != hipSuccess) return e;
     // dq: value-gated, keys and values exchanged, input gate on the values
     p.q = d.dout, p.qdt = GLA_DTYPE_F32, p.qrev = 0;
@@ -428,10 +624,8 @@ hipError_t chan_backward(const gla_bwd_desc &d, const float *s0T, const float *d
     p.fin = finC;
     if ((e = launch_pass<false>(p, BH, Dv, st)) != hipSuccess) return e;
     if (d.dlog_alpha) {
-        const int nseg = (L + kSeg - 1) / kSeg;
-        float *g = scratch;
-        float *part = g + (size_t)BH * L * Dk;
-        float *fterm = part + (size_t)BH * nseg * Dk;
+        const int nseg = nsg;
+        float *g = g_rows;
         if (dfT) {
             const size_t total = (size_t)BH * Dk;
             hipLaunchKernelGGL(chan_fterm_kernel, dim3(nblkc(total, 256)), dim3(256), 0, st, dfT, finC, fterm, Dk, Dv,

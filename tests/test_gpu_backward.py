@@ -188,3 +188,20 @@ def test_backward_per_channel_strong_decay(gpu_lib):
     got = run(gpu_lib, w, d, dout, s0, df)
     ref = oracle.backward(d["q"], d["k"], d["v"], dout, "channel", la, d["log_ig"], s0, df)
     check_all(got, ref, "per-channel strong decay", "f32")
+
+
+def test_backward_headline_workload_sampled_heads(gpu_lib):
+    # the per-channel GLA workload at full size (the launch bench.py --backward times); three
+    # sampled (batch, head) slices against the oracle's gradients of those slices
+    w = gin.WORKLOADS["gla_bf16_B8H16L2048"]
+    d = gin.make_inputs(w, seed=0)
+    dout, s0, df = grads_in(w, 0, False, True)
+    got = run(gpu_lib, w, d, dout, s0, df)
+    rows = [0, 37, w.B * w.H - 1]
+    sel = lambda x: x.reshape(-1, *x.shape[2:])[rows][None]
+    ref = oracle.backward(sel(d["q"]), sel(d["k"]), sel(d["v"]), sel(dout), "channel", sel(d["log_alpha"]), None,
+                          None, sel(df))
+    for key in ("dq", "dk", "dv", "dlog_alpha", "dinitial_state"):
+        g = got[key].reshape(-1, *got[key].shape[2:])[rows]
+        e = rel_err(g, ref[key][0])
+        assert e <= TOLS["f32"], "%s: max|err|/RMS = %.3e" % (key, e)
