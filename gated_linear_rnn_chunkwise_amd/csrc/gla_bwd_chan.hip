@@ -60,12 +60,24 @@ __device__ __forceinline__ float ld_in(const void *p, int dt, size_t i) {
     return __uint_as_float((uint32_t)reinterpret_cast<const uint16_t *>(p)[i] << 16);
 }
 
-// Raw input bits (fp32, or bf16 in the low half) and their value; the dtype is a template
+// Buffer resources over one (batch, head) slice: 32-bit element offsets, and an offset past
+// the range (kOff) reads zero, so masked elements need no branch.
+typedef __amdgpu_buffer_rsrc_t rsrc_c;
+constexpr uint32_t kOff = 0xffffffffu;
+__device__ __forceinline__ rsrc_c mk_rsrc(const void *p, uint64_t bytes) {
+    const uint32_t n = bytes > 0xfffffff0ull ? 0xfffffff0u : (uint32_t)bytes;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)n, 0x00020000);
+}
+// Raw input bits (fp32, or bf16 in the low half) of element i; the dtype is a template
 // argument so that a load's result is not consumed on the path that issues it.
 template <bool F32>
-__device__ __forceinline__ uint32_t ld_raw(const void *p, size_t i) {
-    if constexpr (F32) return reinterpret_cast<const uint32_t *>(p)[i];
-    else return (uint32_t)reinterpret_cast<const uint16_t *>(p)[i];
+__device__ __forceinline__ uint32_t ld_raw(rsrc_c r, uint32_t i) {
+    const uint32_t off = i == kOff ? kOff : i * (F32 ? 4u : 2u);
+    if constexpr (F32) return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
+    else return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
+}
+__device__ __forceinline__ float ld_f32(rsrc_c r, uint32_t i) {
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (int)(i == kOff ? kOff : i * 4u), 0, 0));
 }
 template <bool F32>
 __device__ __forceinline__ float raw_val(uint32_t x) {
@@ -100,7 +112,8 @@ struct ChanLds {
     static constexpr int B = KT + DQ * TP;                // key gate [16][QP] / value gate [64][TP]: log2 decays
     static constexpr int VT = B + (KG ? kBlk * QP : 64 * TP);  // [64][TP] v, transposed
     static constexpr int VF = VT + 64 * TP;               // [64][TP] decayed v, transposed (value gate)
-    static constexpr int P = VF + (KG ? 0 : 64 * TP);     // [16][TP] scores
+    static constexpr int VX = VF + (KG ? 0 : 64 * TP);    // [64][TP] v 2^(-b_s), transposed (value gate)
+    static constexpr int P = VX + (KG ? 0 : 64 * TP);     // [16][TP] scores
     static constexpr int FLAG = P + kBlk * TP;            // strong-decay flag of the block
     static constexpr int TOTAL = FLAG + 4;
 };
@@ -136,7 +149,7 @@ __global__ __launch_bounds__(256, 2) void chan_pass_kernel(ChanPass a) {
     constexpr int NV = kBlk * 64 / 256;   // value elements fetched per thread
     extern __shared__ __align__(16) float lds[];
     float *sQ = lds + Lp::Q, *sKX = lds + Lp::KX, *sKT = lds + Lp::KT, *sB = lds + Lp::B;
-    float *sVT = lds + Lp::VT, *sVF = lds + Lp::VF, *sP = lds + Lp::P;
+    float *sVT = lds + Lp::VT, *sVF = lds + Lp::VF, *sVX = lds + Lp::VX, *sP = lds + Lp::P;
     int *sFlag = reinterpret_cast<int *>(lds + Lp::FLAG);
 
     const int ndt = a.Dn / 64;
@@ -171,44 +184,44 @@ __global__ __launch_bounds__(256, 2) void chan_pass_kernel(ChanPass a) {
     float gtot = 0.f;  // state kernel: the segment's log2 decay of column tid (tid < GW)
 
     // next block: raw q, k, v bits, value-row and output-row log weights, log gates
+    const uint64_t Lu = (uint64_t)L;
+    const rsrc_c rq = mk_rsrc(reinterpret_cast<const char *>(a.q) + bh * Lu * DQ * (QF ? 4 : 2), Lu * DQ * (QF ? 4 : 2));
+    const rsrc_c rk = mk_rsrc(reinterpret_cast<const char *>(a.k) + bh * Lu * DQ * (KF ? 4 : 2), Lu * DQ * (KF ? 4 : 2));
+    const rsrc_c rv = mk_rsrc(reinterpret_cast<const char *>(a.v) + bh * Lu * Dn * (VF ? 4 : 2), Lu * Dn * (VF ? 4 : 2));
+    const rsrc_c rg = mk_rsrc(a.la + bh * Lu * Dg, Lu * Dg * 4);
+    const rsrc_c rvl = mk_rsrc(a.vli ? a.vli + bh * Lu : a.la, a.vli ? Lu * 4 : 0);
+    const rsrc_c rol = mk_rsrc(a.oli ? a.oli + bh * Lu : a.la, a.oli ? Lu * 4 : 0);
     uint32_t fq[NQ], fk[NQ], fv[NV];
     float fvl[NV], fg[NG], fol[4], ol[4];
     auto fetch = [&](int u0) {
 #pragma unroll
         for (int i = 0; i < NQ; ++i) {
             const int idx = tid + i * 256, t = idx / DQ, d = idx % DQ, u = u0 + t;
-            fq[i] = fk[i] = 0u;
-            if (u < ue) {
-                const size_t rq = bh * L + (a.qrev ? L - 1 - u : u), rk = bh * L + (a.krev ? L - 1 - u : u);
-                fq[i] = ld_raw<QF>(a.q, rq * DQ + d);
-                fk[i] = ld_raw<KF>(a.k, rk * DQ + d);
-            }
+            const bool ok = u < ue;
+            const uint32_t rowq = (uint32_t)(a.qrev ? L - 1 - u : u), rowk = (uint32_t)(a.krev ? L - 1 - u : u);
+            fq[i] = ld_raw<QF>(rq, ok ? rowq * DQ + d : kOff);
+            fk[i] = ld_raw<KF>(rk, ok ? rowk * DQ + d : kOff);
         }
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
             const int idx = tid + i * 256, t = idx >> 6, c = idx & 63, u = u0 + t;
-            fv[i] = 0u;
-            fvl[i] = 0.f;
-            if (u < ue) {
-                const size_t rv = bh * L + (a.vrev ? L - 1 - u : u);
-                fv[i] = ld_raw<VF>(a.v, rv * Dn + n0 + c);
-                if (a.vli) fvl[i] = a.vli[rv];
-            }
+            const bool ok = u < ue;
+            const uint32_t row = (uint32_t)(a.vrev ? L - 1 - u : u);
+            fv[i] = ld_raw<VF>(rv, ok ? row * (uint32_t)Dn + n0 + c : kOff);
+            fvl[i] = ld_f32(rvl, ok ? row : kOff);
         }
 #pragma unroll
         for (int i = 0; i < NG; ++i) {
             const int idx = tid + i * 256, t = idx / GW, c = idx % GW, u = u0 + t;
-            fg[i] = 0.f;
-            if (u < ue && !(a.grev && u == 0)) {
-                const size_t rg = bh * L + (a.grev ? L - u : u);
-                fg[i] = a.la[rg * Dg + (KG ? c : n0 + c)];
-            }
+            const bool ok = u < ue && !(a.grev && u == 0);
+            const uint32_t row = (uint32_t)(a.grev ? L - u : u);
+            fg[i] = ld_f32(rg, ok ? row * (uint32_t)Dg + (KG ? c : n0 + c) : kOff);
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int u = u0 + 4 * g + e;
-            fol[e] = 0.f;
-            if (!ST && a.oli && u < ue) fol[e] = a.oli[bh * L + (a.orev ? L - 1 - u : u)];
+            const uint32_t row = (uint32_t)(a.orev ? L - 1 - u : u);
+            fol[e] = ld_f32(rol, (!ST && u < ue) ? row : kOff);
         }
     };
     fetch(ub);
@@ -253,11 +266,14 @@ __global__ __launch_bounds__(256, 2) void chan_pass_kernel(ChanPass a) {
                 if constexpr (KG) sB[t * QP + tid] = run;
                 else sB[tid * TP + t] = run;
             }
-            if (KG && run < kFactorFloor) *sFlag = 1;
+            if (run < kFactorFloor) *sFlag = 1;
             gtot += run;
         }
         lds_sync();
-        const bool exact = !ST && KG && *sFlag != 0;
+        // strong decay in this block: key gate: scores with exact factors; value gate: the
+        // block's own tokens with exact factors
+        const bool strong = !ST && *sFlag != 0;
+        const bool exact = KG && strong;
         if (exact) {
             // strong decay in this block: key-gated scores with every factor formed exactly
             const int t = tid >> 4, s = tid & 15;
@@ -285,7 +301,9 @@ __global__ __launch_bounds__(256, 2) void chan_pass_kernel(ChanPass a) {
             }
             for (int idx = tid; idx < kBlk * 64; idx += 256) {
                 const int c = idx >> 4, t = idx & 15;
-                sVF[c * TP + t] = sVT[c * TP + t] * fexp2c(sB[c * TP + kBlk - 1] - sB[c * TP + t]);
+                const float bt = sB[c * TP + t], vv = sVT[c * TP + t];
+                sVF[c * TP + t] = vv * fexp2c(sB[c * TP + kBlk - 1] - bt);
+                if (!ST) sVX[c * TP + t] = vv * fexp2c(-bt);  // bounded by 2^60 unless strong
             }
         }
         lds_sync();
@@ -321,9 +339,18 @@ __global__ __launch_bounds__(256, 2) void chan_pass_kernel(ChanPass a) {
             const f32x4c vb = *reinterpret_cast<const f32x4c *>(sVT + ncol * TP + 4 * g);
 #pragma unroll
             for (int m = 0; m < 4; ++m) O = mfma4(pa[m], vb[m], O);
+        } else if (!strong) {
+            // value gate: (q S + P v 2^(-b_s)) 2^(b_t) per column, all factors bounded
+            const f32x4c pa = *reinterpret_cast<const f32x4c *>(sP + c16 * TP + 4 * g);
+            const f32x4c vb = *reinterpret_cast<const f32x4c *>(sVX + ncol * TP + 4 * g);
+#pragma unroll
+            for (int m = 0; m < 4; ++m) O = mfma4(pa[m], vb[m], O);
+            const f32x4c b4 = *reinterpret_cast<const f32x4c *>(sB + ncol * TP + 4 * g);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) O[e] *= fexp2c(b4[e]);
         } else {
-            // value gate: the entering state's term decays with the column; the block's own
-            // tokens with exact factors 2^(b_t - b_s), s <= t
+            // value gate, strong decay: the entering state's term decays with the column; the
+            // block's own tokens with exact factors 2^(b_t - b_s), s <= t
             float vc[kBlk], bc[kBlk];
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
