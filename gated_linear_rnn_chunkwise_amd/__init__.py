@@ -243,7 +243,7 @@ def make_bwd_desc(q, k, v, dout, dq, dk, dv, log_alpha=None, log_ig=None, initia
 
 
 def bwd(q, k, v, dout, log_alpha=None, *, log_ig=None, initial_state=None, dfinal_state=None, stream=None):
-    """Gradients of the forward pass on the current HIP stream (scalar gate kinds or none).
+    """Gradients of the forward pass on the current HIP stream (every gate kind).
 
     ``dout`` [B,H,L,Dv] and ``dfinal_state`` [B,H,Dk,Dv] (or None) are fp32 loss gradients
     with respect to the outputs.  Returns a dict of fp32 tensors: ``dq``, ``dk``, ``dv``,

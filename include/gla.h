@@ -188,18 +188,21 @@ int gla_step(const gla_step_desc *d, void *stream);
  * with respect to q, k, v, the log gates and the initial state.  They follow from the
  * definition by differentiating each step; computed chunkwise on the GPU.
  *
- * Method (scalar gate kinds): with G_t = d loss / d S_t, which obeys the same recurrence
+ * Method: with G_t = d loss / d S_t, which obeys the same recurrence
  * run backwards in time (G_t = q_t^T dout_t + diag(alpha_{t+1}) G_{t+1}, G_{L-1} starting
  * from dfinal_state), dv_t = i_t k_t G_t, dk_t = i_t (G_t v_t^T)^T and dq_t = dout_t S_t^T;
  * each is a chunkwise forward pass over re-ordered operands (time reversed for dv and dk,
- * keys and values exchanged for dk and dq).  The log-gate gradients follow from
- * d loss / d B_t = q_t . dq_t - k_t . dk_t (B_t the running sum of log decays; plus the
- * final-state term at the last token) summed from t to the end, and dlog_ig_t = k_t . dk_t.
- * Precision: fp32 inputs run the passes with fp32 operands.  bf16 inputs run them on the
- * fp16 matrix-core path of the forward pass, with q, k, v as given and dout entering as
- * fp16 after a per-(batch, head) power-of-two scale that puts its largest magnitude in
- * [4, 8) (dfinal_state counts at 1/64 of its magnitude); the scale is divided out exactly.
- * The range limits of bf16 forward inputs apply to q, k, v.
+ * keys and values exchanged for dk and dq).  With a per-channel gate the dk and dq passes
+ * decay their states on the value side, S_t = S_{t-1} diag(alpha_t) + ..., which their own
+ * kernel computes.  The log-gate gradients follow from d loss / d B_t = q_t * dq_t -
+ * k_t * dk_t (B_t the running sum of log decays, per channel; a dot product over channels
+ * for scalar gates; plus the final-state term at the last token) summed from t to the end,
+ * and dlog_ig_t = k_t . dk_t.
+ * Precision: fp32 inputs, and every per-channel gate, run the passes in fp32.  bf16 inputs
+ * with a scalar gate or none run them on the fp16 matrix-core path of the forward pass, with
+ * q, k, v as given and dout entering as fp16 after a per-(batch, head) power-of-two scale
+ * that puts its largest magnitude in [4, 8) (dfinal_state counts at 1/64 of its magnitude);
+ * the scale is divided out exactly.  The range limits of bf16 forward inputs apply to q, k, v.
  *
  * Shapes: q, k [B,H,L,Dk] and v [B,H,L,Dv] in in_dtype; gates as in gla_desc; dout
  * [B,H,L,Dv] fp32; dfinal_state [B,H,Dk,Dv] fp32 or NULL (zero); outputs fp32: dq, dk
@@ -225,10 +228,9 @@ typedef struct gla_bwd_desc {
     size_t workspace_bytes;
 } gla_bwd_desc;
 
-/* Backward pass.  Support matrix (else GLA_ERR_UNSUPPORTED): gate_kind NONE, HEAD or
- * HEAD_CONST (a per-channel gate needs the decay on the value side of two of the passes,
- * which no kernel here computes); Dk and Dv in {64, 128, 256}; L as for gla_fwd_ex.
- * Validation and asynchrony as for gla_fwd_ex.  Returns a gla_status. */
+/* Backward pass.  Support matrix (else GLA_ERR_UNSUPPORTED): every gate kind; Dk and Dv in
+ * {64, 128, 256}; L as for gla_fwd_ex.  Validation and asynchrony as for gla_fwd_ex.
+ * Returns a gla_status. */
 int gla_bwd(const gla_bwd_desc *d, void *stream);
 
 /* Scratch bytes gla_bwd needs for `d` (no HIP call).  Returns a gla_status. */
