@@ -332,6 +332,9 @@ int validate_bwd(const gla_bwd_desc *d) {
     if (bh > (int64_t(1) << 24)) return GLA_ERR_INVALID_ARG;
     if (bh * d->L > lim / std::max(d->Dk, d->Dv)) return GLA_ERR_INVALID_ARG;
     if (!bwd_dim_ok(d->Dk) || !bwd_dim_ok(d->Dv)) return GLA_ERR_UNSUPPORTED;
+    // one (batch, head) slice is addressed with 32-bit byte offsets, as in the forward pass
+    if ((int64_t(d->L) + 2 * gla::kMaxChunk) * std::max(d->Dk, d->Dv) * 4 >= (int64_t(1) << 32))
+        return GLA_ERR_UNSUPPORTED;
     return GLA_OK;
 }
 

@@ -271,7 +271,9 @@ def test_bwd_invalid_arguments(lib, kw):
     assert bstatus(lib, bdesc(**kw))[0] == gla.GLA_ERR_INVALID_ARG
 
 
-@pytest.mark.parametrize("kw", [dict(Dk=100), dict(Dv=512), dict(Dk=32), dict(gate_kind=gla.GATE_CHANNEL, Dv=96)])
+@pytest.mark.parametrize("kw", [dict(Dk=100), dict(Dv=512), dict(Dk=32), dict(gate_kind=gla.GATE_CHANNEL, Dv=96),
+                                dict(B=1, H=1, L=1 << 22, Dk=256),  # a slice past 32-bit byte offsets
+                                dict(B=1, H=1, L=1 << 22, Dk=256, gate_kind=gla.GATE_CHANNEL)])
 def test_bwd_unsupported(lib, kw):
     assert bstatus(lib, bdesc(**kw))[0] == gla.GLA_ERR_UNSUPPORTED
 
