@@ -193,35 +193,49 @@ __global__ __launch_bounds__(256, 2) void chan_pass_kernel(ChanPass a) {
     const rsrc_c rol = mk_rsrc(a.oli ? a.oli + bh * Lu : a.la, a.oli ? Lu * 4 : 0);
     uint32_t fq[NQ], fk[NQ], fv[NV];
     float fvl[NV], fg[NG], fol[4], ol[4];
+    // Element i of a thread's share sits RS = 256 / DQ rows (q, k, key-side gates) or 4 rows
+    // (v, value-side gates) after element i - 1, so its offset is a fixed step from the first.
+    constexpr int RS = 256 / DQ;
+    const int tq = tid / DQ, dq = tid % DQ, tv = tid >> 6, cv = tid & 63;
+    auto row_of = [&](int rev, int u) { return rev ? L - 1 - u : u; };
     auto fetch = [&](int u0) {
+        const int uq = u0 + tq, uv = u0 + tv;
+        {
+            const int bq = row_of(a.qrev, uq) * DQ + dq, bk = row_of(a.krev, uq) * DQ + dq;
+            const int sq = a.qrev ? -RS * DQ : RS * DQ, sk = a.krev ? -RS * DQ : RS * DQ;
 #pragma unroll
-        for (int i = 0; i < NQ; ++i) {
-            const int idx = tid + i * 256, t = idx / DQ, d = idx % DQ, u = u0 + t;
-            const bool ok = u < ue;
-            const uint32_t rowq = (uint32_t)(a.qrev ? L - 1 - u : u), rowk = (uint32_t)(a.krev ? L - 1 - u : u);
-            fq[i] = ld_raw<QF>(rq, ok ? rowq * DQ + d : kOff);
-            fk[i] = ld_raw<KF>(rk, ok ? rowk * DQ + d : kOff);
+            for (int i = 0; i < NQ; ++i) {
+                const bool ok = uq + i * RS < ue;
+                fq[i] = ld_raw<QF>(rq, ok ? (uint32_t)(bq + i * sq) : kOff);
+                fk[i] = ld_raw<KF>(rk, ok ? (uint32_t)(bk + i * sk) : kOff);
+            }
         }
+        {
+            const int rv0 = row_of(a.vrev, uv), sr = a.vrev ? -4 : 4;
 #pragma unroll
-        for (int i = 0; i < NV; ++i) {
-            const int idx = tid + i * 256, t = idx >> 6, c = idx & 63, u = u0 + t;
-            const bool ok = u < ue;
-            const uint32_t row = (uint32_t)(a.vrev ? L - 1 - u : u);
-            fv[i] = ld_raw<VF>(rv, ok ? row * (uint32_t)Dn + n0 + c : kOff);
-            fvl[i] = ld_f32(rvl, ok ? row : kOff);
+            for (int i = 0; i < NV; ++i) {
+                const bool ok = uv + 4 * i < ue;
+                const int row = rv0 + i * sr;
+                fv[i] = ld_raw<VF>(rv, ok ? (uint32_t)(row * Dn + n0 + cv) : kOff);
+                fvl[i] = ld_f32(rvl, ok ? (uint32_t)row : kOff);
+            }
         }
+        {
+            // gate rows: token u reads row L - u when reversed (zero for u = 0), else row u
+            const int ug = KG ? uq : uv, cg = KG ? dq : n0 + cv, step = KG ? RS : 4;
+            const int r0 = a.grev ? L - ug : ug, sr = a.grev ? -step : step;
 #pragma unroll
-        for (int i = 0; i < NG; ++i) {
-            const int idx = tid + i * 256, t = idx / GW, c = idx % GW, u = u0 + t;
-            const bool ok = u < ue && !(a.grev && u == 0);
-            const uint32_t row = (uint32_t)(a.grev ? L - u : u);
-            fg[i] = ld_f32(rg, ok ? row * (uint32_t)Dg + (KG ? c : n0 + c) : kOff);
+            for (int i = 0; i < NG; ++i) {
+                const int u = ug + i * step;
+                const bool ok = u < ue && !(a.grev && u == 0);
+                fg[i] = ld_f32(rg, ok ? (uint32_t)((r0 + i * sr) * Dg + cg) : kOff);
+            }
         }
+        {
+            const int u = u0 + 4 * g, r0 = row_of(a.orev, u), sr = a.orev ? -1 : 1;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int u = u0 + 4 * g + e;
-            const uint32_t row = (uint32_t)(a.orev ? L - 1 - u : u);
-            fol[e] = ld_f32(rol, (!ST && u < ue) ? row : kOff);
+            for (int e = 0; e < 4; ++e)
+                fol[e] = ld_f32(rol, (!ST && u + e < ue) ? (uint32_t)(r0 + e * sr) : kOff);
         }
     };
     fetch(ub);
@@ -309,14 +323,17 @@ __global__ __launch_bounds__(256, 2) void chan_pass_kernel(ChanPass a) {
         lds_sync();
         // ---- scores P[t][s] = sum_d q[t][d] k[s][d] on the matrix cores (wave 0), s <= t
         if (!ST && !exact && w == 0) {
-            f32x4c pc = {0.f, 0.f, 0.f, 0.f};
+            // four independent accumulators (one per e) so that the products do not wait on
+            // each other
+            f32x4c pe[4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
             for (int j = 0; j < NJ; ++j) {
                 const f32x4c qa = *reinterpret_cast<const f32x4c *>(sQ + c16 * QP + 16 * j + 4 * g);
                 const f32x4c kb = *reinterpret_cast<const f32x4c *>(sKX + c16 * QP + 16 * j + 4 * g);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) pc = mfma4(qa[e], kb[e], pc);
+                for (int e = 0; e < 4; ++e) pe[e] = mfma4(qa[e], kb[e], pe[e]);
             }
+            const f32x4c pc = (pe[0] + pe[1]) + (pe[2] + pe[3]);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int t = 4 * g + e;
@@ -326,13 +343,14 @@ __global__ __launch_bounds__(256, 2) void chan_pass_kernel(ChanPass a) {
         if constexpr (!ST) lds_sync();
         // ---- outputs of the block's 16 tokens for this lane's column
         if constexpr (!ST) {
-        f32x4c O = {0.f, 0.f, 0.f, 0.f};
+        f32x4c Oe[4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
             const f32x4c qa = *reinterpret_cast<const f32x4c *>(sQ + c16 * QP + 16 * j + 4 * g);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) O = mfma4(qa[e], S[j][e], O);
+            for (int e = 0; e < 4; ++e) Oe[e] = mfma4(qa[e], S[j][e], Oe[e]);
         }
+        f32x4c O = (Oe[0] + Oe[1]) + (Oe[2] + Oe[3]);
         if constexpr (KG) {
             // the block's own tokens: P (decays included) times v
             const f32x4c pa = *reinterpret_cast<const f32x4c *>(sP + c16 * TP + 4 * g);
