@@ -10,10 +10,11 @@
 // but with a per-channel gate the last two need the decay on the value dimension of their
 // state: F_val runs S_t = S_{t-1} diag(gamma_t) + k_t^T v_t, o_t = q_t S_t, where F_key is
 // the forward recurrence S_t = diag(gamma_t) S_{t-1} + k_t^T v_t.  chan_pass_kernel computes
-// both in fp32 over 16-token blocks: inside a block every decay factor is formed exactly as
-// 2^(b_t - b_s) <= 1 from running log2 decays, and the state is carried from block to block.
-// Reversal, the input gate of the values and the output row mapping are index arithmetic on
-// the caller's tensors, so the passes need no operand copies.
+// both in fp32 over 16-token blocks from running log2 decays b_t: every decay factor
+// 2^(b_t - b_s) <= 1 is either split into two factors bounded by 2^60 (while the block's
+// decay stays above 2^-60) or formed exactly, and the state is carried from block to block
+// and across sequence segments.  Reversal, the input gate of the values and the output row
+// mapping are index arithmetic on the caller's tensors, so the passes need no operand copies.
 //
 // The per-channel log-gate gradient is the reverse running sum over tokens of
 // q_t,d dq_t,d - k_t,d dk_t,d, plus sum_j dfinal[d][j] S_fin[d][j] at the last token
@@ -126,7 +127,8 @@ __device__ __forceinline__ f32x4c mfma4(float a, float b, f32x4c c) {
 // key-gated scores exactly instead of as a product of q 2^(b_t) and k 2^(-b_s).
 constexpr float kFactorFloor = -60.f;
 
-// grid = BH * (Dn / 64) workgroups of 256 threads.  Wave w owns value columns 16 w .. 16 w + 15
+// grid = BH * (Dn / 64) * segments workgroups of 256 threads (segment index fastest).  Wave w
+// owns value columns 16 w .. 16 w + 15
 // of the workgroup's 64; lane l (c16 = l & 15, g = l >> 4) holds the state in matrix-core
 // accumulator layout: rows 16 j + 4 g + e (j < DQ / 16, e < 4) of column 16 w + c16.  Both
 // block products run on the fp32 matrix cores (16x16x4):
