@@ -56,10 +56,6 @@ namespace {
 constexpr float kLog2eC = 1.4426950408889634f;
 constexpr int kBlk = 16;  // tokens per block
 
-__device__ __forceinline__ float ld_in(const void *p, int dt, size_t i) {
-    if (dt == GLA_DTYPE_F32) return reinterpret_cast<const float *>(p)[i];
-    return __uint_as_float((uint32_t)reinterpret_cast<const uint16_t *>(p)[i] << 16);
-}
 
 // Buffer resources over one (batch, head) slice: 32-bit element offsets, and an offset past
 // the range (kOff) reads zero, so masked elements need no branch.
@@ -470,43 +466,78 @@ __global__ __launch_bounds__(256) void chan_seg_scan_kernel(ChanPass a, int Dq, 
 }
 
 // fterm[bh][d] = sum_j dfT[bh][j][d] finC[bh][j][d] (both [Dv][Dk]): the final-state term
-// of channel d's log-gate gradient.  One thread per (bh, d).
+// of channel d's log-gate gradient.  Workgroup = 64 channels of one (bh); its four waves
+// take every fourth j and are summed through LDS.
 __global__ __launch_bounds__(256) void chan_fterm_kernel(const float *dfT, const float *finC, float *fterm, int Dk,
-                                                        int Dv, size_t total) {
-    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= total) return;
-    const size_t bh = i / (size_t)Dk;
-    const int d = (int)(i % (size_t)Dk);
+                                                        int Dv) {
+    __shared__ float part[4][64];
+    const int ndt = Dk / 64;
+    const size_t bh = blockIdx.x / (unsigned)ndt;
+    const int d = (int)(blockIdx.x % (unsigned)ndt) * 64 + ((int)threadIdx.x & 63);
+    const int w = (int)threadIdx.x >> 6;
     const size_t base = bh * (size_t)Dv * Dk + d;
     float s = 0.f;
-    for (int j = 0; j < Dv; ++j) s += dfT[base + (size_t)j * Dk] * finC[base + (size_t)j * Dk];
-    fterm[i] = s;
+#pragma unroll 4
+    for (int j = w; j < Dv; j += 4) s += dfT[base + (size_t)j * Dk] * finC[base + (size_t)j * Dk];
+    part[w][threadIdx.x & 63] = s;
+    __syncthreads();
+    if (w == 0) fterm[bh * Dk + d] = (part[0][threadIdx.x] + part[1][threadIdx.x]) + (part[2][threadIdx.x] + part[3][threadIdx.x]);
 }
 
 constexpr int kSeg = 64;  // tokens per segment of the log-gate scan
 
+// Four consecutive channels of an input row as fp32 (16-byte fp32 or 8-byte bf16 loads).
+__device__ __forceinline__ float4 ld4_in(const void *p, int dt, size_t i) {
+    if (dt == GLA_DTYPE_F32) return *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(p) + i);
+    const uint2 x = *reinterpret_cast<const uint2 *>(reinterpret_cast<const uint16_t *>(p) + i);
+    return make_float4(__uint_as_float(x.x << 16), __uint_as_float(x.x & 0xffff0000u), __uint_as_float(x.y << 16),
+                       __uint_as_float(x.y & 0xffff0000u));
+}
+
 // g[bh][t][d] = q dq - k dk (+ fterm at the last token) and the segment totals
-// part[bh][seg][d].  Workgroup = 64 channels of one (bh, segment).
-__global__ __launch_bounds__(64) void chan_g_kernel(gla_bwd_desc d, const float *fterm, float *g, float *part,
-                                                   int nseg) {
-    const int ndt = d.Dk / 64;
+// part[bh][seg][d].  Workgroup = 64 channels of one (bh) and four segments: lane l of wave w
+// takes channels 4 (l & 15) .. + 3 and rows t = 4 i + (l >> 4) of segment 4 * block + w.
+__global__ __launch_bounds__(256) void chan_g_kernel(gla_bwd_desc d, const float *fterm, float *g, float *part,
+                                                    int nseg) {
+    __shared__ float4 red[4][4][16];
+    const int ndt = d.Dk / 64, nsb = (nseg + 3) / 4;
     size_t id = blockIdx.x;
-    const int seg = (int)(id % (unsigned)nseg);
-    id /= (unsigned)nseg;
+    const int sb = (int)(id % (unsigned)nsb);
+    id /= (unsigned)nsb;
     const int dt = (int)(id % (unsigned)ndt);
     const size_t bh = id / (unsigned)ndt;
-    const int c = dt * 64 + (int)threadIdx.x;
+    const int w = (int)threadIdx.x >> 6, lane = (int)threadIdx.x & 63, q4 = lane & 15, r4 = lane >> 4;
+    const int seg = sb * 4 + w;
+    const int c = dt * 64 + 4 * q4;
     const int L = d.L, Dk = d.Dk;
     const int t0 = seg * kSeg, t1 = min(L, t0 + kSeg);
-    float sum = 0.f;
-    for (int t = t0; t < t1; ++t) {
-        const size_t i = (bh * L + t) * Dk + c;
-        float x = ld_in(d.q, d.in_dtype, i) * d.dq[i] - ld_in(d.k, d.in_dtype, i) * d.dk[i];
-        if (t == L - 1 && fterm) x += fterm[bh * Dk + c];
-        g[i] = x;
-        sum += x;
+    float4 sum = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (seg < nseg) {
+        for (int t = t0 + r4; t < t1; t += 4) {
+            const size_t i = (bh * L + t) * Dk + c;
+            const float4 q = ld4_in(d.q, d.in_dtype, i), k = ld4_in(d.k, d.in_dtype, i);
+            const float4 dq = *reinterpret_cast<const float4 *>(d.dq + i), dk = *reinterpret_cast<const float4 *>(d.dk + i);
+            float4 x = make_float4(q.x * dq.x - k.x * dk.x, q.y * dq.y - k.y * dk.y, q.z * dq.z - k.z * dk.z,
+                                   q.w * dq.w - k.w * dk.w);
+            if (t == L - 1 && fterm) {
+                const float4 f = *reinterpret_cast<const float4 *>(fterm + bh * Dk + c);
+                x.x += f.x, x.y += f.y, x.z += f.z, x.w += f.w;
+            }
+            *reinterpret_cast<float4 *>(g + i) = x;
+            sum.x += x.x, sum.y += x.y, sum.z += x.z, sum.w += x.w;
+        }
     }
-    part[(bh * nseg + seg) * Dk + c] = sum;
+    red[w][r4][q4] = sum;
+    __syncthreads();
+    if (seg < nseg && r4 == 0) {
+        float4 s = red[w][0][q4];
+#pragma unroll
+        for (int j = 1; j < 4; ++j) {
+            const float4 y = red[w][j][q4];
+            s.x += y.x, s.y += y.y, s.z += y.z, s.w += y.w;
+        }
+        *reinterpret_cast<float4 *>(part + (bh * nseg + seg) * Dk + c) = s;
+    }
 }
 
 // dlog_alpha[bh][t][d] = sum over s >= t of g[bh][s][d]: the carry from the later segments,
@@ -530,7 +561,6 @@ __global__ __launch_bounds__(64) void chan_scan_kernel(gla_bwd_desc d, const flo
     }
 }
 
-inline unsigned nblkc(size_t n, unsigned per) { return (unsigned)((n + per - 1) / per); }
 
 // Raise the kernel's dynamic-LDS limit once per device (one bit per device ordinal).
 hipError_t lds_limit(const void *fn, std::atomic<uint64_t> &done, int bytes) {
@@ -674,14 +704,14 @@ hipError_t chan_backward(const gla_bwd_desc &d, const float *s0T, const float *d
         const int nseg = nsg;
         float *g = g_rows;
         if (dfT) {
-            const size_t total = (size_t)BH * Dk;
-            hipLaunchKernelGGL(chan_fterm_kernel, dim3(nblkc(total, 256)), dim3(256), 0, st, dfT, finC, fterm, Dk, Dv,
-                               total);
+            hipLaunchKernelGGL(chan_fterm_kernel, dim3((unsigned)((size_t)BH * (Dk / 64))), dim3(256), 0, st, dfT, finC,
+                               fterm, Dk, Dv);
             if ((e = hipGetLastError()) != hipSuccess) return e;
         }
-        const dim3 grid((unsigned)((size_t)BH * (Dk / 64) * nseg));
-        hipLaunchKernelGGL(chan_g_kernel, grid, dim3(64), 0, st, d, dfT ? fterm : nullptr, g, part, nseg);
+        const dim3 grid_g((unsigned)((size_t)BH * (Dk / 64) * ((nseg + 3) / 4)));
+        hipLaunchKernelGGL(chan_g_kernel, grid_g, dim3(256), 0, st, d, dfT ? fterm : nullptr, g, part, nseg);
         if ((e = hipGetLastError()) != hipSuccess) return e;
+        const dim3 grid((unsigned)((size_t)BH * (Dk / 64) * nseg));
         hipLaunchKernelGGL(chan_scan_kernel, grid, dim3(64), 0, st, d, g, part, nseg);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
