@@ -26,7 +26,6 @@ hipError_t bwd_transpose(const float *src, const uint32_t *mx, float *dst, int B
 size_t bwd_absmax_parts(int L, int Dv, int Dk, bool dfin);
 hipError_t bwd_dout16(const float *dout, const float *dfin, float *part, uint32_t *mx, _Float16 *fwd, _Float16 *rev,
                       int BH, int L, int Dv, int Dk, hipStream_t st);
-hipError_t bwd_rev16(const void *src, void *dst, int BH, int L, int D, hipStream_t st);
 hipError_t bwd_scale(const float *src, const uint32_t *mx, float *dst, int BH, size_t m, hipStream_t st);
 hipError_t bwd_finish(const gla_bwd_desc &d, const float *oA, const float *oB, float *g, const float *finA,
                       const float *finC, const float *dfT, float *part, const uint32_t *mx, hipStream_t st);
@@ -204,6 +203,7 @@ struct OutMapArgs {
     int rev = 0;
     const float *li = nullptr;
     const uint32_t *mx = nullptr;
+    int in_rev = 0;  // the pass reads q, k, v in reversed token order
 };
 
 // The forward pass; h16 marks operands given as fp16 instead of bf16 and om maps the output
@@ -256,6 +256,7 @@ int fwd_run(const gla_desc *d, int h16, void *stream, const OutMapArgs &om = Out
     a.out_rev = om.rev;
     a.out_li = om.li;
     a.out_mx = om.mx;
+    a.in_rev = om.in_rev;
 
     const hipError_t err = gla::launch_forward(a, d->in_dtype == GLA_DTYPE_F32, h16, d->Dk, s);
     if (owned) (void)hipFreeAsync(ws, s);
@@ -392,12 +393,12 @@ int bwd_plan(const gla_bwd_desc *d, BwdPlan *p) {
         p->total = off;
         return GLA_OK;
     }
-    // operand copies: fp32 for fp32 inputs; bf16 reversed q, k, v and fp16 output gradients
-    const size_t eb = bf ? 2 : 4;
-    p->rq = take(bh * L * Dk * eb);
-    p->rk = take(bh * L * Dk * eb);
-    p->rv = take(bh * L * Dv * eb);
-    p->rdo = take(bh * L * Dv * eb);
+    // operand copies: fp32 reversed q, k, v and output gradient for fp32 inputs; for bf16
+    // inputs the passes read q, k, v reversed in place and the output gradient as fp16
+    p->rq = bf ? 0 : take(bh * L * Dk * 4);
+    p->rk = bf ? 0 : take(bh * L * Dk * 4);
+    p->rv = bf ? 0 : take(bh * L * Dv * 4);
+    p->rdo = bf ? 0 : take(bh * L * Dv * 4);
     p->fdo = bf ? take(bh * L * Dv * 2) : 0;
     p->mx = bf ? take(bh * 4) : 0;
     p->mxp = bf ? take(bh * gla::bwd_absmax_parts(d->L, d->Dv, d->Dk, d->dfinal_state != nullptr) * 4) : 0;
@@ -495,11 +496,10 @@ int gla_bwd(const gla_bwd_desc *d, void *stream) {
     uint32_t *mx = bf ? reinterpret_cast<uint32_t *>(ws + p.mx) : nullptr;
     // operands of the three passes
     if (bf) {
-        // reversed bf16 copies of q, k, v; the scaled output gradient as fp16 (both orders)
-        ok(gla::bwd_dout16(d->dout, d->dfinal_state, F(p.mxp), mx, reinterpret_cast<_Float16 *>(ws + p.fdo),
-                           reinterpret_cast<_Float16 *>(ws + p.rdo), BH, L, Dv, Dk, s)) &&
-            ok(gla::bwd_rev16(d->q, V(p.rq), BH, L, Dk, s)) && ok(gla::bwd_rev16(d->k, V(p.rk), BH, L, Dk, s)) &&
-            ok(gla::bwd_rev16(d->v, V(p.rv), BH, L, Dv, s));
+        // the scaled output gradient as fp16 (the reversed passes read it, and q, k, v, from
+        // the end)
+        ok(gla::bwd_dout16(d->dout, d->dfinal_state, F(p.mxp), mx, reinterpret_cast<_Float16 *>(ws + p.fdo), nullptr,
+                           BH, L, Dv, Dk, s));
         if (d->dfinal_state) ok(gla::bwd_scale(d->dfinal_state, mx, F(p.s0A), BH, size_t(Dk) * Dv, s));
     } else {
         ok(gla::bwd_reverse(d->q, dt, F(p.rq), BH, L, Dk, s)) &&
@@ -520,14 +520,18 @@ int gla_bwd(const gla_bwd_desc *d, void *stream) {
     om_rev.rev = 1;
     om_rev.li = d->log_ig;
     om_rev.mx = mx;
+    om_rev.in_rev = 1;
     om_q.mx = mx;
+    // operands of the reversed passes: the caller's q, k, v and the fp16 output gradient read
+    // from the end (bf16), or the reversed fp32 copies
+    const void *rq = bf ? d->q : V(p.rq), *rk = bf ? d->k : V(p.rk), *rv = bf ? d->v : V(p.rv);
+    const void *rdo = bf ? fdo : V(p.rdo);
     // dv (reversed; its final state is the gradient of the state after token 0)
-    fwd(bwd_pass_desc(d, Dk, Dv, V(p.rk), V(p.rq), V(p.rdo), rgate, rla, nullptr, s0A, bf ? d->dv : F(p.oA),
-                      F(p.finA)),
-        gla::kH16V, om_rev);
+    fwd(bwd_pass_desc(d, Dk, Dv, rk, rq, rdo, rgate, rla, nullptr, s0A, bf ? d->dv : F(p.oA), F(p.finA)), gla::kH16V,
+        om_rev);
     // dk (reversed, keys and values exchanged)
-    fwd(bwd_pass_desc(d, Dv, Dk, V(p.rv), V(p.rdo), V(p.rq), rgate, rla, nullptr,
-                      d->dfinal_state ? F(p.dfT) : nullptr, bf ? d->dk : F(p.oB), nullptr),
+    fwd(bwd_pass_desc(d, Dv, Dk, rv, rdo, rq, rgate, rla, nullptr, d->dfinal_state ? F(p.dfT) : nullptr,
+                      bf ? d->dk : F(p.oB), nullptr),
         gla::kH16K, om_rev);
     // dq (keys and values exchanged; its final state is the forward final state, transposed)
     fwd(bwd_pass_desc(d, Dv, Dk, fdo, d->v, d->k, d->gate_kind, d->log_alpha, d->log_ig,

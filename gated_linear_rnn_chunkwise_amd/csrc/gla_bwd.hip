@@ -102,19 +102,7 @@ __global__ __launch_bounds__(256) void bwd_absmax_final_kernel(const float *part
     if (lane == 0) mx[bh] = __float_as_uint(m);
 }
 
-// Rows of 16-bit values in reversed token order: dst[bh][u][:] = src[bh][L-1-u][:], 16 bytes
-// a thread (D a multiple of 8).
-__global__ __launch_bounds__(256) void bwd_rev16_kernel(const uint4 *src, uint4 *dst, int L, int d8, size_t total) {
-    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= total) return;
-    const size_t row = i / (size_t)d8;
-    const int c = (int)(i % (size_t)d8);
-    const size_t bh = row / (size_t)L;
-    const int u = (int)(row % (size_t)L);
-    dst[i] = src[(bh * L + (L - 1 - u)) * (size_t)d8 + c];
-}
-
-// The scaled output gradient as fp16, in token order (fwd) and reversed (rev).
+// The scaled output gradient as fp16, in token order (fwd) and, when rev is given, reversed.
 __global__ __launch_bounds__(256) void bwd_dout16_kernel(const float *dout, const uint32_t *mx, h16x8 *fwd,
                                                         h16x8 *rev, int L, int d8, size_t total) {
     const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
@@ -129,7 +117,7 @@ __global__ __launch_bounds__(256) void bwd_dout16_kernel(const float *dout, cons
     const h16x8 h = {(_Float16)(a.x * s), (_Float16)(a.y * s), (_Float16)(a.z * s), (_Float16)(a.w * s),
                      (_Float16)(b.x * s), (_Float16)(b.y * s), (_Float16)(b.z * s), (_Float16)(b.w * s)};
     fwd[i] = h;
-    rev[(bh * L + (L - 1 - t)) * (size_t)d8 + c] = h;
+    if (rev) rev[(bh * L + (L - 1 - t)) * (size_t)d8 + c] = h;
 }
 
 // dst = s * src per (batch, head) slice of m elements.
@@ -386,13 +374,6 @@ hipError_t bwd_dout16(const float *dout, const float *dfin, float *part, uint32_
     const size_t total = (size_t)BH * L * (Dv / 8);
     hipLaunchKernelGGL(bwd_dout16_kernel, dim3(nblk(total, 256)), dim3(256), 0, st, dout, mx,
                        reinterpret_cast<h16x8 *>(fwd), reinterpret_cast<h16x8 *>(rev), L, Dv / 8, total);
-    return hipGetLastError();
-}
-
-hipError_t bwd_rev16(const void *src, void *dst, int BH, int L, int D, hipStream_t st) {
-    const size_t total = (size_t)BH * L * (D / 8);
-    hipLaunchKernelGGL(bwd_rev16_kernel, dim3(nblk(total, 256)), dim3(256), 0, st, reinterpret_cast<const uint4 *>(src),
-                       reinterpret_cast<uint4 *>(dst), L, D / 8, total);
     return hipGetLastError();
 }
 

@@ -354,7 +354,16 @@ struct Rs {
     int gate, L;
     uint32_t gstride;  // bytes between the scalar gates of consecutive rows (0: one value or none)
     bool has_li;
+    bool rev;          // backward-pass instances: token t reads q, k, v row L-1-t
 };
+
+// Row of q, k, v that token t reads.  Past the sequence end (t >= L) a reversed row is
+// negative, and its 32-bit byte offset lies past the slice, so it reads zero like t >= L does.
+template <class C>
+__device__ __forceinline__ uint32_t in_row(const Rs &rs, int t) {
+    if constexpr (C::H16 != 0) return (uint32_t)(rs.rev ? rs.L - 1 - t : t);
+    else return (uint32_t)t;
+}
 
 template <class C>
 __device__ __forceinline__ Rs make_rs(const KArgs &a, int bh, int h) {
@@ -378,6 +387,7 @@ __device__ __forceinline__ Rs make_rs(const KArgs &a, int bh, int h) {
     r.L = a.L;
     r.gstride = a.gate == GLA_GATE_HEAD ? 4u : 0u;
     r.has_li = a.li != nullptr;
+    r.rev = a.in_rev != 0;
     return r;
 }
 
@@ -386,10 +396,9 @@ __device__ __forceinline__ void load_unit(Raw<C> &r, const Rs &rs, int T0, int s
                                           int Dv) {
     const int ch0 = sl * C::SLAB + C::CPL * lane;
     const uint32_t row0 = (uint32_t)(T0 + 16 * w);
-    const uint32_t qoff = (row0 * C::DK + ch0) * C::IB;
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) {
-        const uint32_t off = qoff + rr * C::DK * C::IB;
+        const uint32_t off = (in_row<C>(rs, T0 + 16 * w + rr) * C::DK + ch0) * C::IB;
         if constexpr (C::CPL == 2 || C::F32) {
             if constexpr (WQ) r.q[rr] = bld32(rs.q, off);
             r.k[rr] = bld32(rs.k, off);
@@ -423,7 +432,7 @@ __device__ __forceinline__ void load_unit(Raw<C> &r, const Rs &rs, int T0, int s
         const uint32_t c0 = dv0 + 4 * (tid & 15);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const uint32_t off = ((uint32_t)(T0 + 4 * (tid >> 4) + e) * Dv + c0) * C::IB;
+            const uint32_t off = (in_row<C>(rs, T0 + 4 * (tid >> 4) + e) * Dv + c0) * C::IB;
             if constexpr (C::F32) {
                 const u32x4 x = bld128(rs.v, off);
 #pragma unroll
@@ -1152,7 +1161,7 @@ __device__ __forceinline__ void load_p_v(Raw<C> &r, const Rs &rs, int T0, int pw
     const uint32_t c0 = dv0 + 4 * (tp & 15);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-        const uint32_t off = ((uint32_t)(T0 + 4 * (tp >> 4) + e) * Dv + c0) * C::IB;
+        const uint32_t off = (in_row<C>(rs, T0 + 4 * (tp >> 4) + e) * Dv + c0) * C::IB;
         if constexpr (C::F32) {
             const u32x4 x = bld128(rs.v, off);
 #pragma unroll
@@ -1190,10 +1199,9 @@ __device__ __forceinline__ void load_p_gates(Raw<C> &r, const Rs &rs, int T0, in
 template <class C>
 __device__ __forceinline__ void load_p_qk(Raw<C> &r, const Rs &rs, int T0, int pw, int lane) {
     const int ch0 = C::CPL * lane;
-    const uint32_t row0 = (uint32_t)(T0 + 16 * pw);
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) {
-        const uint32_t off = ((row0 + rr) * C::DK + ch0) * C::IB;
+        const uint32_t off = (in_row<C>(rs, T0 + 16 * pw + rr) * C::DK + ch0) * C::IB;
         if constexpr (C::CPL == 2 || C::F32) {
             r.q[rr] = bld32(rs.q, off);
             r.k[rr] = bld32(rs.k, off);
@@ -1882,10 +1890,9 @@ struct RawSg {
 template <class C>
 __device__ __forceinline__ void load_unit_sg(RawSg<C> &r, const Rs &rs, int T0, int pw, int lane, int dv0, int Dv) {
     const int ch0 = 4 * lane;  // a wave's load covers one whole row
-    const uint32_t row0 = (uint32_t)(T0 + 16 * pw);
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) {
-        const uint32_t off = ((row0 + rr) * C::DK + ch0) * 2u;
+        const uint32_t off = (in_row<C>(rs, T0 + 16 * pw + rr) * C::DK + ch0) * 2u;
         r.q[rr] = bld64(rs.q, off);
         r.k[rr] = bld64(rs.k, off);
     }
@@ -1898,7 +1905,7 @@ __device__ __forceinline__ void load_unit_sg(RawSg<C> &r, const Rs &rs, int T0, 
     const uint32_t c0 = dv0 + 4 * (tp & 15);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-        const uint32_t off = ((uint32_t)(T0 + 4 * (tp >> 4) + e) * Dv + c0) * 2u;
+        const uint32_t off = (in_row<C>(rs, T0 + 4 * (tp >> 4) + e) * Dv + c0) * 2u;
         const u32x2 x = bld64(rs.v, off);
         r.v[e][0] = x[0];
         r.v[e][1] = x[1];

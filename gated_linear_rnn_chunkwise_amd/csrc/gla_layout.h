@@ -268,6 +268,7 @@ struct KArgs {
     int out_rev;
     const float *out_li;
     const uint32_t *out_mx;
+    int in_rev;       // token t reads q, k, v row L-1-t (the gates are given in token order)
 };
 
 #if defined(__HIPCC__)
