@@ -242,19 +242,18 @@ __global__ __launch_bounds__(256) void bwd_dot_kernel(gla_bwd_desc d, float *g, 
 }
 
 // The final-state term of the last token's g: the sum over (j, d) of dfinal^T[j][d] S_fin^T[j][d]
-// (dfT and finC both transposed; times 1/s when dfT carries the scale), kPerBlock float4 per
-// workgroup, added into g atomically.
+// (dfT and finC both transposed; times 1/s when dfT carries the scale).  One workgroup per
+// (b, h) in a fixed order, so the result does not depend on scheduling.
 __global__ __launch_bounds__(256) void bwd_fin_term_kernel(const float *dfT, const float *finC, const uint32_t *mx,
-                                                          float *g, int L, size_t n4, int nb) {
+                                                          float *g, int L, size_t n4) {
     __shared__ float red[4];
-    const size_t bh = blockIdx.x / (unsigned)nb;
-    const size_t i0 = (size_t)(blockIdx.x % (unsigned)nb) * kPerBlock;
-    const size_t i1 = i0 + kPerBlock < n4 ? i0 + kPerBlock : n4;
+    const size_t bh = blockIdx.x;
     const float4 *a = reinterpret_cast<const float4 *>(dfT) + bh * n4;
     const float4 *b = reinterpret_cast<const float4 *>(finC) + bh * n4;
     const int tid = (int)threadIdx.x;
     float sum = 0.f;
-    for (size_t i = i0 + tid; i < i1; i += 256) {
+#pragma unroll 4
+    for (size_t i = tid; i < n4; i += 256) {
         const float4 x = a[i], y = b[i];
         sum += x.x * y.x + x.y * y.y + x.z * y.z + x.w * y.w;
     }
@@ -263,7 +262,7 @@ __global__ __launch_bounds__(256) void bwd_fin_term_kernel(const float *dfT, con
     __syncthreads();
     if (tid == 0) {
         const float inv = mx ? 1.f / scale_of(mx[bh]) : 1.f;
-        atomicAdd(g + bh * L + L - 1, (red[0] + red[1] + red[2] + red[3]) * inv);
+        g[bh * L + L - 1] += ((red[0] + red[1]) + (red[2] + red[3])) * inv;
     }
 }
 
@@ -399,10 +398,7 @@ hipError_t bwd_finish(const gla_bwd_desc &d, const float *oA, const float *oB, f
     }
     const size_t m = (size_t)d.Dk * d.Dv;
     if (g && dfT) {
-        const size_t n4 = m / 4;
-        const int nb = (int)nblk(n4, kPerBlock);
-        hipLaunchKernelGGL(bwd_fin_term_kernel, dim3((unsigned)((size_t)nb * BH)), dim3(256), 0, st, dfT, finC, mx, g,
-                           d.L, n4, nb);
+        hipLaunchKernelGGL(bwd_fin_term_kernel, dim3((unsigned)BH), dim3(256), 0, st, dfT, finC, mx, g, d.L, m / 4);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     if (g) {

@@ -205,3 +205,39 @@ def test_backward_headline_workload_sampled_heads(gpu_lib):
         g = got[key].reshape(-1, *got[key].shape[2:])[rows]
         e = rel_err(g, ref[key][0])
         assert e <= TOLS["f32"], "%s: max|err|/RMS = %.3e" % (key, e)
+
+
+@pytest.mark.parametrize("gate,ig", [("head", True), ("head_const", False), ("channel", True)])
+def test_backward_bitwise_deterministic_and_caller_workspace(gpu_lib, gate, ig):
+    # two calls with the library's own scratch and one with a caller workspace give the same
+    # bits (no atomics decide an order anywhere in the backward)
+    import ctypes
+    w = gin.custom(2, 3, 777, 128, 128, 64, dtype="bf16", gate=gate, input_gate=ig)
+    d = gin.make_inputs(w, seed=11)
+    dout, s0, df = grads_in(w, 11, True, True)
+    a = run(gpu_lib, w, d, dout, s0, df)
+    b = run(gpu_lib, w, d, dout, s0, df)
+    cu = lambda t: None if t is None else t.to("cuda").contiguous()
+    # every device tensor the descriptor points to stays referenced until the call has run
+    q, k, v, la, li = cu(d["q"]), cu(d["k"]), cu(d["v"]), cu(d["log_alpha"]), cu(d["log_ig"])
+    do_g, s0_g, df_g = cu(dout), cu(s0), cu(df)
+    f = dict(dtype=torch.float32, device="cuda")
+    out = {"dq": torch.empty(q.shape, **f), "dk": torch.empty(k.shape, **f), "dv": torch.empty(v.shape, **f),
+           "dlog_alpha": torch.empty(la.shape, **f), "dlog_ig": torch.empty(li.shape, **f) if li is not None else None,
+           "dinitial_state": torch.empty(2, 3, 128, 128, **f)}
+    desc = gpu_lib.make_bwd_desc(q, k, v, do_g, out["dq"], out["dk"], out["dv"], la, li, s0_g, df_g,
+                                 out["dlog_alpha"], out["dlog_ig"], out["dinitial_state"])
+    lib = gpu_lib.load()
+    need = ctypes.c_size_t(0)
+    assert lib.gla_bwd_workspace_size(ctypes.byref(desc), ctypes.byref(need)) == gpu_lib.GLA_OK
+    ws = torch.full((need.value,), 0xFF, dtype=torch.uint8, device="cuda")  # stale contents must not matter
+    desc.workspace, desc.workspace_bytes = ws.data_ptr(), need.value
+    st = torch.cuda.current_stream()
+    assert lib.gla_bwd(ctypes.byref(desc), ctypes.c_void_p(st.cuda_stream)) == gpu_lib.GLA_OK
+    torch.cuda.synchronize()
+    c = {kk: None if vv is None else vv.cpu().double().numpy() for kk, vv in out.items()}
+    for key in ("dq", "dk", "dv", "dlog_alpha", "dlog_ig", "dinitial_state"):
+        if a[key] is None:
+            continue
+        assert np.array_equal(a[key], b[key]), key
+        assert np.array_equal(a[key], c[key]), key
