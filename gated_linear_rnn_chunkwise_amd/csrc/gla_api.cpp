@@ -32,7 +32,8 @@ hipError_t bwd_finish(const gla_bwd_desc &d, const float *oA, const float *oB, f
 constexpr int kH16Q = 1, kH16K = 2, kH16V = 4;  // fp16 operand bits of launch_forward
 size_t chan_scratch_floats(int BH, int L, int Dk, int Dv);
 hipError_t chan_backward(const gla_bwd_desc &d, const float *s0T, const float *dfT, float *finA, float *finC,
-                         float *scratch, hipStream_t st);
+                         float *scratch, bool skip_dv, hipStream_t st);
+hipError_t bwd_gate_ch(const float *la, float *dst, int BH, int L, int Dk, hipStream_t st);
 }
 
 namespace {
@@ -363,6 +364,10 @@ gla_desc bwd_pass_desc(const gla_bwd_desc *d, int dk, int dv, const void *q, con
     return f;
 }
 
+// The per-channel backward's dv pass (key-gated) runs on the forward kernel's fp16 path for
+// bf16 inputs with Dk <= 128; otherwise, and for the other two passes, on chan_pass_kernel.
+bool chan_dv_fast(const gla_bwd_desc *d) { return d->in_dtype == GLA_DTYPE_BF16 && d->Dk <= 128; }
+
 struct BwdPlan {
     size_t chs, rq, rk, rv, rdo, fdo, mx, mxp, s0A, lar, oA, oB, finA, finC, s0T, dfT, g, part, fws, total;
     size_t fws_bytes;
@@ -382,7 +387,9 @@ int bwd_plan(const gla_bwd_desc *d, BwdPlan *p) {
     };
     if (d->gate_kind == GLA_GATE_CHANNEL) {
         // per-channel gate: the passes read the caller's tensors; scratch for the transposed
-        // states, the final states and the log-gate scan
+        // states, the final states and the log-gate scan; with the dv pass on the forward
+        // kernel (bf16, Dk <= 128) also the fp16 output gradient, its scales, the scaled
+        // final-state gradient, the reversed gate and that pass's own workspace
         *p = BwdPlan{};
         p->finA = take(bh * Dk * Dv * 4);
         p->finC = take(bh * Dk * Dv * 4);
@@ -390,6 +397,21 @@ int bwd_plan(const gla_bwd_desc *d, BwdPlan *p) {
         p->dfT = d->dfinal_state ? take(bh * Dk * Dv * 4) : 0;
         p->chs = take(gla::chan_scratch_floats(d->B * d->H, d->L, d->Dk, d->Dv) * 4);
         p->fws_bytes = 0;
+        if (chan_dv_fast(d)) {
+            p->fdo = take(bh * L * Dv * 2);
+            p->mx = take(bh * 4);
+            p->mxp = take(bh * gla::bwd_absmax_parts(d->L, d->Dv, d->Dk, d->dfinal_state != nullptr) * 4);
+            p->s0A = d->dfinal_state ? take(bh * Dk * Dv * 4) : 0;
+            p->lar = take(bh * L * Dk * 4);
+            const void *x = reinterpret_cast<const void *>(uintptr_t(256));
+            float *y = reinterpret_cast<float *>(uintptr_t(256));
+            const gla_desc f = bwd_pass_desc(d, d->Dk, d->Dv, x, x, x, GLA_GATE_CHANNEL, y, nullptr, nullptr, y, y);
+            size_t n = 0;
+            const int st = gla_workspace_size(&f, &n);
+            if (st != GLA_OK) return st;
+            p->fws_bytes = n;
+            p->fws = take(n);
+        }
         p->total = off;
         return GLA_OK;
     }
@@ -487,9 +509,27 @@ int gla_bwd(const gla_bwd_desc *d, void *stream) {
         if (d->dfinal_state) ok(gla::bwd_transpose(d->dfinal_state, nullptr, F(p.dfT), BH, Dk, Dv, s));
         const float *s0T = d->initial_state ? F(p.s0T) : nullptr;
         const float *dfT = d->dfinal_state ? F(p.dfT) : nullptr;
-        if (rc == GLA_OK) ok(gla::chan_backward(*d, s0T, dfT, F(p.finA), F(p.finC), F(p.chs), s));
+        const bool fast = chan_dv_fast(d);
+        uint32_t *cmx = fast ? reinterpret_cast<uint32_t *>(ws + p.mx) : nullptr;
+        if (fast) {
+            // dv: key-gated forward pass over the reversed sequence on the fp16 path, as for
+            // scalar gates, with the per-channel gate reversed into scratch
+            ok(gla::bwd_dout16(d->dout, d->dfinal_state, F(p.mxp), cmx, reinterpret_cast<_Float16 *>(ws + p.fdo),
+                               nullptr, BH, L, Dv, Dk, s));
+            if (d->dfinal_state) ok(gla::bwd_scale(d->dfinal_state, cmx, F(p.s0A), BH, size_t(Dk) * Dv, s));
+            ok(gla::bwd_gate_ch(d->log_alpha, F(p.lar), BH, L, Dk, s));
+            OutMapArgs om;
+            om.rev = 1;
+            om.li = d->log_ig;
+            om.mx = cmx;
+            om.in_rev = 1;
+            fwd(bwd_pass_desc(d, Dk, Dv, d->k, d->q, V(p.fdo), GLA_GATE_CHANNEL, F(p.lar), nullptr,
+                              d->dfinal_state ? F(p.s0A) : nullptr, d->dv, F(p.finA)),
+                gla::kH16V, om);
+        }
+        if (rc == GLA_OK) ok(gla::chan_backward(*d, s0T, dfT, F(p.finA), F(p.finC), F(p.chs), fast, s));
         if (rc == GLA_OK)
-            ok(gla::bwd_finish(*d, nullptr, nullptr, nullptr, F(p.finA), F(p.finC), dfT, nullptr, nullptr, s));
+            ok(gla::bwd_finish(*d, nullptr, nullptr, nullptr, F(p.finA), F(p.finC), dfT, nullptr, cmx, s));
         if (owned) (void)hipFreeAsync(ws, s);
         return rc;
     }

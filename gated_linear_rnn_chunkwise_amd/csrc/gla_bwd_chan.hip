@@ -652,8 +652,10 @@ size_t chan_scratch_floats(int BH, int L, int Dk, int Dv) {
 // The three passes and the per-channel log-gate gradient.  s0T = initial^T and dfT =
 // dfinal^T ([Dv][Dk], or null), finA [Dk][Dv] and finC [Dv][Dk] receive the first and third
 // passes' final states, scratch holds chan_scratch_floats(...) floats.
+// skip_dv: the dv pass ran elsewhere (bf16 inputs with Dk <= 128 take it on the forward
+// kernel's fp16 path).
 hipError_t chan_backward(const gla_bwd_desc &d, const float *s0T, const float *dfT, float *finA, float *finC,
-                         float *scratch, hipStream_t st) {
+                         float *scratch, bool skip_dv, hipStream_t st) {
     const int BH = d.B * d.H, L = d.L, Dk = d.Dk, Dv = d.Dv, dt = d.in_dtype;
     hipError_t e;
     const int nsg = (L + kSeg - 1) / kSeg;
@@ -679,7 +681,7 @@ hipError_t chan_backward(const gla_bwd_desc &d, const float *s0T, const float *d
     p.fin = finA;
     p.Dn = Dv;
     segs(Dv, Dk);
-    if ((e = launch_pass<true>(p, BH, Dk, st)) != hipSuccess) return e;
+    if (!skip_dv && (e = launch_pass<true>(p, BH, Dk, st)) != hipSuccess) return e;
     // dk: value-gated, reversed, keys and values exchanged
     p.q = d.v, p.qdt = dt, p.qrev = 1;
     p.k = d.dout, p.kdt = GLA_DTYPE_F32, p.krev = 1;

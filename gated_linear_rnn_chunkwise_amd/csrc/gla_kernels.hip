@@ -2578,12 +2578,19 @@ static hipError_t launch_h16(const KArgs &a, int dk, hipStream_t st) {
 }
 
 // h16: which of q, k, v (bits kOpQ, kOpK, kOpV) are fp16 rather than bf16.  Only one fp16
-// operand, with scalar gates and 64-token chunks: the forms the backward pass runs.
+// operand and 64-token chunks: the forms the backward pass runs (with a per-channel gate only
+// the value operand, Dk <= 128).
 hipError_t launch_forward(const KArgs &a, bool f32, int h16, int dk, hipStream_t st) {
     const bool ch = a.gate == GLA_GATE_CHANNEL;
     const bool mt = a.nt > 1;
+    if (h16 && ch) {
+        if (mt || f32 || h16 != 1 << kOpV) return hipErrorInvalidValue;
+        if (dk == 64) return launch_cfg<Cfg<false, 64, true, false, 1 << kOpV>>(a, st);
+        if (dk == 128) return launch_cfg<Cfg<false, 128, true, false, 1 << kOpV>>(a, st);
+        return hipErrorInvalidValue;
+    }
     if (h16) {
-        if (ch || mt || f32) return hipErrorInvalidValue;
+        if (mt || f32) return hipErrorInvalidValue;
         if (h16 == 1 << kOpQ) return launch_h16<1 << kOpQ>(a, dk, st);
         if (h16 == 1 << kOpK) return launch_h16<1 << kOpK>(a, dk, st);
         if (h16 == 1 << kOpV) return launch_h16<1 << kOpV>(a, dk, st);

@@ -198,11 +198,13 @@ int gla_step(const gla_step_desc *d, void *stream);
  * k_t * dk_t (B_t the running sum of log decays, per channel; a dot product over channels
  * for scalar gates; plus the final-state term at the last token) summed from t to the end,
  * and dlog_ig_t = k_t . dk_t.
- * Precision: fp32 inputs, and every per-channel gate, run the passes in fp32.  bf16 inputs
- * with a scalar gate or none run them on the fp16 matrix-core path of the forward pass, with
- * q, k, v as given and dout entering as fp16 after a per-(batch, head) power-of-two scale
- * that puts its largest magnitude in [4, 8) (dfinal_state counts at 1/64 of its magnitude);
- * the scale is divided out exactly.  The range limits of bf16 forward inputs apply to q, k, v.
+ * Precision: fp32 inputs run the passes in fp32.  bf16 inputs run the passes that the forward
+ * kernels compute (all three for a scalar gate or none; the dv pass for a per-channel gate
+ * with Dk <= 128) on their fp16 matrix-core path, with q, k, v as given and dout entering as
+ * fp16 after a per-(batch, head) power-of-two scale that puts its largest magnitude in [4, 8)
+ * (dfinal_state counts at 1/64 of its magnitude); the scale is divided out exactly.  The
+ * other per-channel passes run in fp32.  The range limits of bf16 forward inputs apply to
+ * q, k, v.
  *
  * Shapes: q, k [B,H,L,Dk] and v [B,H,L,Dv] in in_dtype; gates as in gla_desc; dout
  * [B,H,L,Dv] fp32; dfinal_state [B,H,Dk,Dv] fp32 or NULL (zero); outputs fp32: dq, dk
