@@ -33,7 +33,6 @@ constexpr int kH16Q = 1, kH16K = 2, kH16V = 4;  // fp16 operand bits of launch_f
 size_t chan_scratch_floats(int BH, int L, int Dk, int Dv);
 hipError_t chan_backward(const gla_bwd_desc &d, const float *s0T, const float *dfT, float *finA, float *finC,
                          float *scratch, bool skip_dv, hipStream_t st);
-hipError_t bwd_gate_ch(const float *la, float *dst, int BH, int L, int Dk, hipStream_t st);
 }
 
 namespace {
@@ -389,7 +388,7 @@ int bwd_plan(const gla_bwd_desc *d, BwdPlan *p) {
         // per-channel gate: the passes read the caller's tensors; scratch for the transposed
         // states, the final states and the log-gate scan; with the dv pass on the forward
         // kernel (bf16, Dk <= 128) also the fp16 output gradient, its scales, the scaled
-        // final-state gradient, the reversed gate and that pass's own workspace
+        // final-state gradient and that pass's own workspace
         *p = BwdPlan{};
         p->finA = take(bh * Dk * Dv * 4);
         p->finC = take(bh * Dk * Dv * 4);
@@ -402,7 +401,6 @@ int bwd_plan(const gla_bwd_desc *d, BwdPlan *p) {
             p->mx = take(bh * 4);
             p->mxp = take(bh * gla::bwd_absmax_parts(d->L, d->Dv, d->Dk, d->dfinal_state != nullptr) * 4);
             p->s0A = d->dfinal_state ? take(bh * Dk * Dv * 4) : 0;
-            p->lar = take(bh * L * Dk * 4);
             const void *x = reinterpret_cast<const void *>(uintptr_t(256));
             float *y = reinterpret_cast<float *>(uintptr_t(256));
             const gla_desc f = bwd_pass_desc(d, d->Dk, d->Dv, x, x, x, GLA_GATE_CHANNEL, y, nullptr, nullptr, y, y);
@@ -513,17 +511,16 @@ int gla_bwd(const gla_bwd_desc *d, void *stream) {
         uint32_t *cmx = fast ? reinterpret_cast<uint32_t *>(ws + p.mx) : nullptr;
         if (fast) {
             // dv: key-gated forward pass over the reversed sequence on the fp16 path, as for
-            // scalar gates, with the per-channel gate reversed into scratch
+            // scalar gates; the kernel reads the per-channel gate reversed and shifted in place
             ok(gla::bwd_dout16(d->dout, d->dfinal_state, F(p.mxp), cmx, reinterpret_cast<_Float16 *>(ws + p.fdo),
                                nullptr, BH, L, Dv, Dk, s));
             if (d->dfinal_state) ok(gla::bwd_scale(d->dfinal_state, cmx, F(p.s0A), BH, size_t(Dk) * Dv, s));
-            ok(gla::bwd_gate_ch(d->log_alpha, F(p.lar), BH, L, Dk, s));
             OutMapArgs om;
             om.rev = 1;
             om.li = d->log_ig;
             om.mx = cmx;
             om.in_rev = 1;
-            fwd(bwd_pass_desc(d, Dk, Dv, d->k, d->q, V(p.fdo), GLA_GATE_CHANNEL, F(p.lar), nullptr,
+            fwd(bwd_pass_desc(d, Dk, Dv, d->k, d->q, V(p.fdo), GLA_GATE_CHANNEL, d->log_alpha, nullptr,
                               d->dfinal_state ? F(p.s0A) : nullptr, d->dv, F(p.finA)),
                 gla::kH16V, om);
         }

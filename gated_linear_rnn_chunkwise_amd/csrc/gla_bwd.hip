@@ -152,18 +152,6 @@ __global__ __launch_bounds__(256) void bwd_gate_kernel(const float *la, int kind
     dst[i] = x;
 }
 
-// Per-channel log gate of the reversed passes: dst[bh][u][:] = la[bh][L-u][:] (u >= 1), zero for
-// u = 0; four channels a thread.
-__global__ __launch_bounds__(256) void bwd_gate_ch_kernel(const float4 *la, float4 *dst, int L, int d4, size_t total) {
-    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= total) return;
-    const size_t row = i / (size_t)d4;
-    const int c = (int)(i % (size_t)d4);
-    const size_t bh = row / (size_t)L;
-    const int u = (int)(row % (size_t)L);
-    dst[i] = u == 0 ? make_float4(0.f, 0.f, 0.f, 0.f) : la[(bh * L + (L - u)) * (size_t)d4 + c];
-}
-
 // [BH][R][C] -> [BH][C][R], times the slice's scale when mx is given.
 __global__ __launch_bounds__(256) void bwd_transpose_kernel(const float *src, const uint32_t *mx, float *dst, int R,
                                                            int C, size_t total) {
@@ -385,13 +373,6 @@ hipError_t bwd_dout16(const float *dout, const float *dfin, float *part, uint32_
     const size_t total = (size_t)BH * L * (Dv / 8);
     hipLaunchKernelGGL(bwd_dout16_kernel, dim3(nblk(total, 256)), dim3(256), 0, st, dout, mx,
                        reinterpret_cast<h16x8 *>(fwd), reinterpret_cast<h16x8 *>(rev), L, Dv / 8, total);
-    return hipGetLastError();
-}
-
-hipError_t bwd_gate_ch(const float *la, float *dst, int BH, int L, int Dk, hipStream_t st) {
-    const size_t total = (size_t)BH * L * (Dk / 4);
-    hipLaunchKernelGGL(bwd_gate_ch_kernel, dim3(nblk(total, 256)), dim3(256), 0, st, reinterpret_cast<const float4 *>(la),
-                       reinterpret_cast<float4 *>(dst), L, Dk / 4, total);
     return hipGetLastError();
 }
 

@@ -364,6 +364,14 @@ __device__ __forceinline__ uint32_t in_row(const Rs &rs, int t) {
     if constexpr (C::H16 != 0) return (uint32_t)(rs.rev ? rs.L - 1 - t : t);
     else return (uint32_t)t;
 }
+// Row of a per-channel gate that token t reads: reversed passes take the gate of the token
+// after (row L - t); token 0 and the rows past the sequence end read row L, past the slice:
+// zero, no decay (a padding row must not decay the final state).
+template <class C>
+__device__ __forceinline__ uint32_t gate_row(const Rs &rs, int t) {
+    if constexpr (C::H16 != 0) return (uint32_t)(rs.rev ? (t < rs.L ? rs.L - t : rs.L) : t);
+    else return (uint32_t)t;
+}
 
 template <class C>
 __device__ __forceinline__ Rs make_rs(const KArgs &a, int bh, int h) {
@@ -395,7 +403,6 @@ template <class C, bool WQ>
 __device__ __forceinline__ void load_unit(Raw<C> &r, const Rs &rs, int T0, int sl, int w, int lane, int tid, int dv0,
                                           int Dv) {
     const int ch0 = sl * C::SLAB + C::CPL * lane;
-    const uint32_t row0 = (uint32_t)(T0 + 16 * w);
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) {
         const uint32_t off = (in_row<C>(rs, T0 + 16 * w + rr) * C::DK + ch0) * C::IB;
@@ -407,7 +414,7 @@ __device__ __forceinline__ void load_unit(Raw<C> &r, const Rs &rs, int T0, int s
             r.k[rr] = __builtin_amdgcn_raw_buffer_load_b16(rs.k, (int)off, 0, 0);
         }
         if constexpr (C::CH) {
-            const uint32_t goff = (row0 * C::DK + ch0 + rr * C::DK) * 4u;
+            const uint32_t goff = (gate_row<C>(rs, T0 + 16 * w + rr) * C::DK + ch0) * 4u;
             if constexpr (C::CPL == 2) {
                 const u32x2 g2 = bld64(rs.la, goff);
                 r.la[rr][0] = __uint_as_float(g2[0]);
@@ -1177,10 +1184,9 @@ template <class C>
 __device__ __forceinline__ void load_p_gates(Raw<C> &r, const Rs &rs, int T0, int pw, int lane) {
     if constexpr (C::CH) {
         const int ch0 = C::CPL * lane;
-        const uint32_t row0 = (uint32_t)(T0 + 16 * pw);
 #pragma unroll
         for (int rr = 0; rr < 16; ++rr) {
-            const uint32_t goff = ((row0 + rr) * C::DK + ch0) * 4u;
+            const uint32_t goff = (gate_row<C>(rs, T0 + 16 * pw + rr) * C::DK + ch0) * 4u;
             if constexpr (C::CPL == 2) {
                 const u32x2 g2 = bld64(rs.la, goff);
                 r.la[rr][0] = __uint_as_float(g2[0]);

@@ -268,7 +268,8 @@ struct KArgs {
     int out_rev;
     const float *out_li;
     const uint32_t *out_mx;
-    int in_rev;       // token t reads q, k, v row L-1-t (the gates are given in token order)
+    int in_rev;       // token t reads q, k, v row L-1-t and a per-channel gate's row L-t (zero
+                      // for t = 0); scalar gates are given in the pass's token order
 };
 
 #if defined(__HIPCC__)
