@@ -312,7 +312,7 @@ def backward_bench(args, torch, gla, gin, w, wname):
         "config": {"workload": wname + "_backward", "B": B, "H": H, "L": L, "Dk": Dk, "Dv": Dv, "gate": w.gate,
                    "input_gate": w.input_gate, "in_dtype": w.dtype,
                    "pass_operands": ("fp32" if w.dtype != "bf16" else
-                                     "dv pass fp16 (scaled output gradient) and bf16; dk, dq passes fp32"
+                                     "fp16 (scaled output gradient) and bf16; dv pass fp32 when Dk = 256"
                                      if w.gate == "channel" else "fp16 (scaled output gradient) and bf16")},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,

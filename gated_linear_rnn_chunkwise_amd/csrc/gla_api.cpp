@@ -32,7 +32,7 @@ hipError_t bwd_finish(const gla_bwd_desc &d, const float *oA, const float *oB, f
 constexpr int kH16Q = 1, kH16K = 2, kH16V = 4;  // fp16 operand bits of launch_forward
 size_t chan_scratch_floats(int BH, int L, int Dk, int Dv);
 hipError_t chan_backward(const gla_bwd_desc &d, const float *s0T, const float *dfT, float *finA, float *finC,
-                         float *scratch, bool skip_dv, hipStream_t st);
+                         float *scratch, bool skip_dv, const _Float16 *fdo, const uint32_t *mx, hipStream_t st);
 }
 
 namespace {
@@ -364,7 +364,8 @@ gla_desc bwd_pass_desc(const gla_bwd_desc *d, int dk, int dv, const void *q, con
 }
 
 // The per-channel backward's dv pass (key-gated) runs on the forward kernel's fp16 path for
-// bf16 inputs with Dk <= 128; otherwise, and for the other two passes, on chan_pass_kernel.
+// bf16 inputs with Dk <= 128, otherwise on chan_pass_kernel; the other two passes run on
+// chan_vg16_kernel (fp16 operands) for bf16 inputs and on chan_pass_kernel for fp32.
 bool chan_dv_fast(const gla_bwd_desc *d) { return d->in_dtype == GLA_DTYPE_BF16 && d->Dk <= 128; }
 
 struct BwdPlan {
@@ -386,9 +387,9 @@ int bwd_plan(const gla_bwd_desc *d, BwdPlan *p) {
     };
     if (d->gate_kind == GLA_GATE_CHANNEL) {
         // per-channel gate: the passes read the caller's tensors; scratch for the transposed
-        // states, the final states and the log-gate scan; with the dv pass on the forward
-        // kernel (bf16, Dk <= 128) also the fp16 output gradient, its scales, the scaled
-        // final-state gradient and that pass's own workspace
+        // states, the final states and the log-gate scan; for bf16 inputs also the fp16 output
+        // gradient and its scales; with the dv pass on the forward kernel (bf16, Dk <= 128)
+        // also the scaled final-state gradient and that pass's own workspace
         *p = BwdPlan{};
         p->finA = take(bh * Dk * Dv * 4);
         p->finC = take(bh * Dk * Dv * 4);
@@ -396,10 +397,12 @@ int bwd_plan(const gla_bwd_desc *d, BwdPlan *p) {
         p->dfT = d->dfinal_state ? take(bh * Dk * Dv * 4) : 0;
         p->chs = take(gla::chan_scratch_floats(d->B * d->H, d->L, d->Dk, d->Dv) * 4);
         p->fws_bytes = 0;
-        if (chan_dv_fast(d)) {
+        if (bf) {
             p->fdo = take(bh * L * Dv * 2);
             p->mx = take(bh * 4);
             p->mxp = take(bh * gla::bwd_absmax_parts(d->L, d->Dv, d->Dk, d->dfinal_state != nullptr) * 4);
+        }
+        if (chan_dv_fast(d)) {
             p->s0A = d->dfinal_state ? take(bh * Dk * Dv * 4) : 0;
             const void *x = reinterpret_cast<const void *>(uintptr_t(256));
             float *y = reinterpret_cast<float *>(uintptr_t(256));
@@ -508,12 +511,15 @@ int gla_bwd(const gla_bwd_desc *d, void *stream) {
         const float *s0T = d->initial_state ? F(p.s0T) : nullptr;
         const float *dfT = d->dfinal_state ? F(p.dfT) : nullptr;
         const bool fast = chan_dv_fast(d);
-        uint32_t *cmx = fast ? reinterpret_cast<uint32_t *>(ws + p.mx) : nullptr;
+        uint32_t *cmx = bf ? reinterpret_cast<uint32_t *>(ws + p.mx) : nullptr;
+        const _Float16 *cfdo = bf ? reinterpret_cast<const _Float16 *>(ws + p.fdo) : nullptr;
+        // the output gradient times a power-of-two scale s per (batch, head), as fp16
+        if (bf)
+            ok(gla::bwd_dout16(d->dout, d->dfinal_state, F(p.mxp), cmx, reinterpret_cast<_Float16 *>(ws + p.fdo),
+                               nullptr, BH, L, Dv, Dk, s));
         if (fast) {
             // dv: key-gated forward pass over the reversed sequence on the fp16 path, as for
             // scalar gates; the kernel reads the per-channel gate reversed and shifted in place
-            ok(gla::bwd_dout16(d->dout, d->dfinal_state, F(p.mxp), cmx, reinterpret_cast<_Float16 *>(ws + p.fdo),
-                               nullptr, BH, L, Dv, Dk, s));
             if (d->dfinal_state) ok(gla::bwd_scale(d->dfinal_state, cmx, F(p.s0A), BH, size_t(Dk) * Dv, s));
             OutMapArgs om;
             om.rev = 1;
@@ -524,9 +530,12 @@ int gla_bwd(const gla_bwd_desc *d, void *stream) {
                               d->dfinal_state ? F(p.s0A) : nullptr, d->dv, F(p.finA)),
                 gla::kH16V, om);
         }
-        if (rc == GLA_OK) ok(gla::chan_backward(*d, s0T, dfT, F(p.finA), F(p.finC), F(p.chs), fast, s));
         if (rc == GLA_OK)
-            ok(gla::bwd_finish(*d, nullptr, nullptr, nullptr, F(p.finA), F(p.finC), dfT, nullptr, cmx, s));
+            ok(gla::chan_backward(*d, s0T, dfT, F(p.finA), F(p.finC), F(p.chs), fast, cfdo, cmx, s));
+        // the dv pass's final state is scaled by s only on the forward kernel's path
+        if (rc == GLA_OK)
+            ok(gla::bwd_finish(*d, nullptr, nullptr, nullptr, F(p.finA), F(p.finC), dfT, nullptr, fast ? cmx : nullptr,
+                               s));
         if (owned) (void)hipFreeAsync(ws, s);
         return rc;
     }

@@ -49,6 +49,10 @@ struct ChanPass {
     // entering segment s+1 (scan); ws_decay [BH][nseg-1][Dg]: the segment's decay.
     int seg_len, nseg;
     float *ws_state, *ws_decay;
+    // fp16 passes (chan_vg16_kernel): per (batch, head) output-gradient scale bits; outputs are
+    // divided by the scale s, and the initial state multiplied by s when s0_scaled
+    const uint32_t *mx;
+    int s0_scaled;
 };
 
 namespace {
@@ -110,8 +114,10 @@ struct ChanLds {
     static constexpr int VT = B + (KG ? kBlk * QP : 64 * TP);  // [64][TP] v, transposed
     static constexpr int VF = VT + 64 * TP;               // [64][TP] decayed v, transposed (value gate)
     static constexpr int VX = VF + (KG ? 0 : 64 * TP);    // [64][TP] v 2^(-b_s), transposed (value gate)
-    static constexpr int P = VX + (KG ? 0 : 64 * TP);     // [16][TP] scores
-    static constexpr int FLAG = P + kBlk * TP;            // strong-decay flag of the block
+    static constexpr int P = VX + (KG ? 0 : 64 * TP);     // [16][TP] scores; value gate: [4][16][TP], one
+                                                          // partial sum per wave
+    static constexpr int TOT = P + (KG ? 1 : 4) * kBlk * TP;  // [4][64] value gate: each wave's log2 decay
+    static constexpr int FLAG = TOT + (KG ? 0 : 4 * 64);  // strong-decay flag of the block
     static constexpr int TOTAL = FLAG + 4;
 };
 
@@ -147,7 +153,7 @@ __global__ __launch_bounds__(256, 2) void chan_pass_kernel(ChanPass a) {
     constexpr int NV = kBlk * 64 / 256;   // value elements fetched per thread
     extern __shared__ __align__(16) float lds[];
     float *sQ = lds + Lp::Q, *sKX = lds + Lp::KX, *sKT = lds + Lp::KT, *sB = lds + Lp::B;
-    float *sVT = lds + Lp::VT, *sVF = lds + Lp::VF, *sVX = lds + Lp::VX, *sP = lds + Lp::P;
+    float *sVT = lds + Lp::VT, *sVF = lds + Lp::VF, *sVX = lds + Lp::VX, *sP = lds + Lp::P, *sTot = lds + Lp::TOT;
     int *sFlag = reinterpret_cast<int *>(lds + Lp::FLAG);
 
     const int ndt = a.Dn / 64;
@@ -191,13 +197,14 @@ __global__ __launch_bounds__(256, 2) void chan_pass_kernel(ChanPass a) {
     const rsrc_c rol = mk_rsrc(a.oli ? a.oli + bh * Lu : a.la, a.oli ? Lu * 4 : 0);
     uint32_t fq[NQ], fk[NQ], fv[NV];
     float fvl[NV], fg[NG], fol[4], ol[4];
-    // Element i of a thread's share sits RS = 256 / DQ rows (q, k, key-side gates) or 4 rows
-    // (v, value-side gates) after element i - 1, so its offset is a fixed step from the first.
+    // Element i of a thread's share sits RS = 256 / DQ rows (q, k, key-side gates) or one row
+    // (v, value-side gates: tokens 4 tv .. 4 tv + 3 of column cv) after element i - 1, so its
+    // offset is a fixed step from the first.
     constexpr int RS = 256 / DQ;
     const int tq = tid / DQ, dq = tid % DQ, tv = tid >> 6, cv = tid & 63;
     auto row_of = [&](int rev, int u) { return rev ? L - 1 - u : u; };
     auto fetch = [&](int u0) {
-        const int uq = u0 + tq, uv = u0 + tv;
+        const int uq = u0 + tq, uv = u0 + 4 * tv;
         {
             const int bq = row_of(a.qrev, uq) * DQ + dq, bk = row_of(a.krev, uq) * DQ + dq;
             const int sq = a.qrev ? -RS * DQ : RS * DQ, sk = a.krev ? -RS * DQ : RS * DQ;
@@ -209,10 +216,10 @@ __global__ __launch_bounds__(256, 2) void chan_pass_kernel(ChanPass a) {
             }
         }
         {
-            const int rv0 = row_of(a.vrev, uv), sr = a.vrev ? -4 : 4;
+            const int rv0 = row_of(a.vrev, uv), sr = a.vrev ? -1 : 1;
 #pragma unroll
             for (int i = 0; i < NV; ++i) {
-                const bool ok = uv + 4 * i < ue;
+                const bool ok = uv + i < ue;
                 const int row = rv0 + i * sr;
                 fv[i] = ld_raw<VF>(rv, ok ? (uint32_t)(row * Dn + n0 + cv) : kOff);
                 fvl[i] = ld_f32(rvl, ok ? (uint32_t)row : kOff);
@@ -220,7 +227,7 @@ __global__ __launch_bounds__(256, 2) void chan_pass_kernel(ChanPass a) {
         }
         {
             // gate rows: token u reads row L - u when reversed (zero for u = 0), else row u
-            const int ug = KG ? uq : uv, cg = KG ? dq : n0 + cv, step = KG ? RS : 4;
+            const int ug = KG ? uq : uv, cg = KG ? dq : n0 + cv, step = KG ? RS : 1;
             const int r0 = a.grev ? L - ug : ug, sr = a.grev ? -step : step;
 #pragma unroll
             for (int i = 0; i < NG; ++i) {
@@ -239,65 +246,74 @@ __global__ __launch_bounds__(256, 2) void chan_pass_kernel(ChanPass a) {
     fetch(ub);
 
     for (int u0 = ub; u0 < ue; u0 += kBlk) {
-        // ---- raw operands into LDS: q, k by rows, v transposed, log2 gates (key gate by
-        // token rows, value gate transposed)
+        // ---- raw operands into LDS: q, k by rows (value gate: k also transposed), v
+        // transposed, key-gate logs by token rows; the value gate's running log2 decays over
+        // each thread's four tokens stay in registers, with the wave's total in LDS
 #pragma unroll
         for (int i = 0; i < NQ; ++i) {
             const int idx = tid + i * 256, t = idx / DQ, d = idx % DQ;
             sQ[t * QP + d] = raw_val<QF>(fq[i]);
-            sKX[t * QP + d] = raw_val<KF>(fk[i]);
+            const float kv = raw_val<KF>(fk[i]);
+            sKX[t * QP + d] = kv;
+            if constexpr (!KG) sKT[d * TP + t] = kv;
         }
+        f32x4c vr;
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
-            const int idx = tid + i * 256;
             float v = raw_val<VF>(fv[i]);
             if (a.vli) v *= fexp2c(fvl[i] * kLog2eC);
-            sVT[(idx & 63) * TP + (idx >> 6)] = v;
+            vr[i] = v;
         }
+        f32x4c loc;
+        if constexpr (KG) {
+            *reinterpret_cast<f32x4c *>(sVT + cv * TP + 4 * tv) = vr;
 #pragma unroll
-        for (int i = 0; i < NG; ++i) {
-            const int idx = tid + i * 256, t = idx / GW, c = idx % GW;
-            const float x = fg[i] == 0.f ? 0.f : log2_gate(fg[i]);
-            if constexpr (KG) sB[t * QP + c] = x;
-            else sB[c * TP + t] = x;
+            for (int i = 0; i < NG; ++i) {
+                const int idx = tid + i * 256, t = idx / GW, c = idx % GW;
+                sB[t * QP + c] = fg[i] == 0.f ? 0.f : log2_gate(fg[i]);
+            }
+        } else {
+            float run = 0.f;
+#pragma unroll
+            for (int i = 0; i < NG; ++i) {
+                run += fg[i] == 0.f ? 0.f : log2_gate(fg[i]);
+                loc[i] = run;
+            }
+            sTot[tv * 64 + cv] = run;
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) ol[e] = fol[e];
         if (tid == 0) *sFlag = 0;
         lds_sync();
         if (u0 + kBlk < ue) fetch(u0 + kBlk);
-        // ---- running log2 decays inside the block, inclusive
-        if (tid < GW) {
-            float b[kBlk];
-#pragma unroll
-            for (int t = 0; t < kBlk; ++t) b[t] = KG ? sB[t * QP + tid] : sB[tid * TP + t];
-            float run = 0.f;
-#pragma unroll
-            for (int t = 0; t < kBlk; ++t) {
-                run += b[t];
-                if constexpr (KG) sB[t * QP + tid] = run;
-                else sB[tid * TP + t] = run;
-            }
-            if (run < kFactorFloor) *sFlag = 1;
-            gtot += run;
-        }
-        lds_sync();
-        // strong decay in this block: key gate: scores with exact factors; value gate: the
-        // block's own tokens with exact factors
-        const bool strong = !ST && *sFlag != 0;
-        const bool exact = KG && strong;
-        if (exact) {
-            // strong decay in this block: key-gated scores with every factor formed exactly
-            const int t = tid >> 4, s = tid & 15;
-            float p = 0.f;
-            if (s <= t)
-                for (int d = 0; d < DQ; ++d)
-                    p += sQ[t * QP + d] * sKX[s * QP + d] * fexp2c(sB[t * QP + d] - sB[s * QP + d]);
-            sP[t * TP + s] = p;
-            lds_sync();
-        }
-        // ---- decay-weighted operands
         if constexpr (KG) {
+            // ---- running log2 decays inside the block, inclusive
+            if (tid < GW) {
+                float b[kBlk];
+#pragma unroll
+                for (int t = 0; t < kBlk; ++t) b[t] = sB[t * QP + tid];
+                float run = 0.f;
+#pragma unroll
+                for (int t = 0; t < kBlk; ++t) {
+                    run += b[t];
+                    sB[t * QP + tid] = run;
+                }
+                if (run < kFactorFloor) *sFlag = 1;
+                gtot += run;
+            }
+            lds_sync();
+            const bool exact = !ST && *sFlag != 0;
+            if (exact) {
+                // strong decay in this block: key-gated scores with every factor formed exactly
+                const int t = tid >> 4, s = tid & 15;
+                float p = 0.f;
+                if (s <= t)
+                    for (int d = 0; d < DQ; ++d)
+                        p += sQ[t * QP + d] * sKX[s * QP + d] * fexp2c(sB[t * QP + d] - sB[s * QP + d]);
+                sP[t * TP + s] = p;
+                lds_sync();
+            }
+            // ---- decay-weighted operands
             for (int idx = tid; idx < kBlk * DQ; idx += 256) {
                 const int t = idx / DQ, d = idx % DQ;
                 const float bt = sB[t * QP + d], b15 = sB[(kBlk - 1) * QP + d];
@@ -306,39 +322,85 @@ __global__ __launch_bounds__(256, 2) void chan_pass_kernel(ChanPass a) {
                 sKT[d * TP + t] = kv * fexp2c(b15 - bt);  // k_t 2^(b_15 - b_t)
                 sKX[t * QP + d] = kv * fexp2c(-bt);       // k_t 2^(-b_t), for the scores
             }
+            lds_sync();
+            // ---- scores P[t][s] = sum_d q[t][d] k[s][d] on the matrix cores (wave 0), s <= t
+            if (!ST && !exact && w == 0) {
+                // four independent accumulators (one per e) so that the products do not wait on
+                // each other
+                f32x4c pe[4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) {
+                    const f32x4c qa = *reinterpret_cast<const f32x4c *>(sQ + c16 * QP + 16 * j + 4 * g);
+                    const f32x4c kb = *reinterpret_cast<const f32x4c *>(sKX + c16 * QP + 16 * j + 4 * g);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) pe[e] = mfma4(qa[e], kb[e], pe[e]);
+                }
+                const f32x4c pc = (pe[0] + pe[1]) + (pe[2] + pe[3]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int t = 4 * g + e;
+                    sP[t * TP + c16] = c16 <= t ? pc[e] : 0.f;
+                }
+            }
+            if constexpr (!ST) lds_sync();
         } else {
-            for (int idx = tid; idx < kBlk * DQ; idx += 256) {
-                const int t = idx / DQ, d = idx % DQ;
-                sKT[d * TP + t] = sKX[t * QP + d];
+            // ---- value gate: the running log2 decays of column cv, tokens 4 tv .. 4 tv + 3,
+            // from the waves' totals; the decay-weighted values
+            float pre = 0.f, tot = 0.f;
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                const float y = sTot[x * 64 + cv];
+                tot += y;
+                pre += x < tv ? y : 0.f;
             }
-            for (int idx = tid; idx < kBlk * 64; idx += 256) {
-                const int c = idx >> 4, t = idx & 15;
-                const float bt = sB[c * TP + t], vv = sVT[c * TP + t];
-                sVF[c * TP + t] = vv * fexp2c(sB[c * TP + kBlk - 1] - bt);
-                if (!ST) sVX[c * TP + t] = vv * fexp2c(-bt);  // bounded by 2^60 unless strong
+            f32x4c b4, vf4, vx4;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                b4[i] = pre + loc[i];
+                vf4[i] = vr[i] * fexp2c(tot - b4[i]);
+                vx4[i] = vr[i] * fexp2c(-b4[i]);  // bounded by 2^60 unless strong
             }
+            *reinterpret_cast<f32x4c *>(sB + cv * TP + 4 * tv) = b4;
+            *reinterpret_cast<f32x4c *>(sVF + cv * TP + 4 * tv) = vf4;
+            if constexpr (!ST) {
+                *reinterpret_cast<f32x4c *>(sVT + cv * TP + 4 * tv) = vr;
+                *reinterpret_cast<f32x4c *>(sVX + cv * TP + 4 * tv) = vx4;
+                if (tot < kFactorFloor) *sFlag = 1;
+                // ---- scores P[t][s] = sum_d q[t][d] k[s][d] on the matrix cores, the
+                // contraction split over the four waves (wave w: channels of steps j in its
+                // quarter), one partial per wave
+                constexpr int JW = NJ / 4;
+                f32x4c pe[4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+                for (int jj = 0; jj < JW; ++jj) {
+                    const int j = w * JW + jj;
+                    const f32x4c qa = *reinterpret_cast<const f32x4c *>(sQ + c16 * QP + 16 * j + 4 * g);
+                    const f32x4c kb = *reinterpret_cast<const f32x4c *>(sKX + c16 * QP + 16 * j + 4 * g);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) pe[e] = mfma4(qa[e], kb[e], pe[e]);
+                }
+                const f32x4c pc = (pe[0] + pe[1]) + (pe[2] + pe[3]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int t = 4 * g + e;
+                    sP[(w * kBlk + t) * TP + c16] = c16 <= t ? pc[e] : 0.f;
+                }
+            }
+            if (tid < 64) gtot += tot;
+            lds_sync();
         }
-        lds_sync();
-        // ---- scores P[t][s] = sum_d q[t][d] k[s][d] on the matrix cores (wave 0), s <= t
-        if (!ST && !exact && w == 0) {
-            // four independent accumulators (one per e) so that the products do not wait on
-            // each other
-            f32x4c pe[4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+        // scores, 4 consecutive columns of row t (value gate: the sum of the waves' partials)
+        auto p4 = [&](int t, int s0) {
+            f32x4c r = *reinterpret_cast<const f32x4c *>(sP + t * TP + s0);
+            if constexpr (!KG) {
 #pragma unroll
-            for (int j = 0; j < NJ; ++j) {
-                const f32x4c qa = *reinterpret_cast<const f32x4c *>(sQ + c16 * QP + 16 * j + 4 * g);
-                const f32x4c kb = *reinterpret_cast<const f32x4c *>(sKX + c16 * QP + 16 * j + 4 * g);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) pe[e] = mfma4(qa[e], kb[e], pe[e]);
+                for (int x = 1; x < 4; ++x) r += *reinterpret_cast<const f32x4c *>(sP + (x * kBlk + t) * TP + s0);
             }
-            const f32x4c pc = (pe[0] + pe[1]) + (pe[2] + pe[3]);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int t = 4 * g + e;
-                sP[t * TP + c16] = c16 <= t ? pc[e] : 0.f;
-            }
-        }
-        if constexpr (!ST) lds_sync();
+            return r;
+        };
+        // strong decay in this block: key gate: scores with exact factors (above); value gate:
+        // the block's own tokens with exact factors
+        const bool strong = !ST && *sFlag != 0;
         // ---- outputs of the block's 16 tokens for this lane's column
         if constexpr (!ST) {
         f32x4c Oe[4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
@@ -357,7 +419,7 @@ __global__ __launch_bounds__(256, 2) void chan_pass_kernel(ChanPass a) {
             for (int m = 0; m < 4; ++m) O = mfma4(pa[m], vb[m], O);
         } else if (!strong) {
             // value gate: (q S + P v 2^(-b_s)) 2^(b_t) per column, all factors bounded
-            const f32x4c pa = *reinterpret_cast<const f32x4c *>(sP + c16 * TP + 4 * g);
+            const f32x4c pa = p4(c16, 4 * g);
             const f32x4c vb = *reinterpret_cast<const f32x4c *>(sVX + ncol * TP + 4 * g);
 #pragma unroll
             for (int m = 0; m < 4; ++m) O = mfma4(pa[m], vb[m], O);
@@ -381,15 +443,14 @@ __global__ __launch_bounds__(256, 2) void chan_pass_kernel(ChanPass a) {
 #pragma unroll
                 for (int m = 1; m < kBlk; ++m) bt = (4 * g + e == m) ? bc[m] : bt;
                 float o = O[e] * fexp2c(bt);
-                const float *prow = sP + (4 * g + e) * TP;
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
-                    const f32x4c p4 = *reinterpret_cast<const f32x4c *>(prow + 4 * m);
+                    const f32x4c pr = p4(4 * g + e, 4 * m);
 #pragma unroll
                     for (int x = 0; x < 4; ++x) {
                         const int s2 = 4 * m + x;
                         const float f = s2 <= 4 * g + e ? fexp2c(bt - bc[s2]) : 0.f;
-                        o += p4[x] * vc[s2] * f;
+                        o += pr[x] * vc[s2] * f;
                     }
                 }
                 O[e] = o;
@@ -446,6 +507,340 @@ __global__ __launch_bounds__(256, 2) void chan_pass_kernel(ChanPass a) {
     }
 }
 
+// ---------------------------------------------------------------------------------------
+// Value-gated pass with fp16 operands (bf16 inputs; the scaled fp16 output gradient as one
+// operand).  The same blocks, decays and state layout as chan_pass_kernel<false, ...>, with
+// the products on the fp16 matrix cores: scores and q S as 16x16x32 steps whose 32-slot
+// contraction of lane group g holds channels 32 m + 4 g + x and 32 m + 16 + 4 g + x (x < 4),
+// the lane's own state rows of blocks 2 m and 2 m + 1; the block's own tokens and the state
+// update as 16x16x16 steps over the 16 tokens.  Factors applied to fp16 operands are bounded
+// by 2^8: a block whose decay reaches below 2^-8 forms its own tokens' factors exactly.
+// Accumulation, decays and the state are fp32; the state is rounded to fp16 as the B operand
+// of q S, as in the forward kernel.  Outputs are scaled by 1/s (mx) and, when s0_scaled, the
+// initial state by s.
+typedef _Float16 h16c;
+typedef h16c h16x4c __attribute__((ext_vector_type(4)));
+typedef h16c h16x8c __attribute__((ext_vector_type(8)));
+typedef h16c h16x2c __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2c __attribute__((ext_vector_type(2)));
+
+constexpr float kFactorFloor16 = -8.f;
+
+// LDS plan (bytes): fp16 q and k rows padded by 16 B, fp16 transposed rows of 16 tokens
+// padded to 20 halves, fp32 transposed rows padded to 20 floats.
+template <int DQ>
+struct VgLds {
+    static constexpr int QH = DQ + 8, TH = 20, TP = 20;
+    static constexpr int Q = 0;                       // [16][QH] h  q
+    static constexpr int K = Q + kBlk * QH * 2;       // [16][QH] h  k
+    static constexpr int KT = K + kBlk * QH * 2;      // [DQ][TH] h  k, transposed
+    static constexpr int VF = KT + DQ * TH * 2;       // [64][TH] h  v 2^(b_15 - b_s), transposed
+    static constexpr int VX = VF + 64 * TH * 2;       // [64][TH] h  v 2^(-b_s), transposed
+    static constexpr int B = VX + 64 * TH * 2;        // [64][TP] f  running log2 decays
+    static constexpr int VT = B + 64 * TP * 4;        // [64][TP] f  v (strong blocks)
+    static constexpr int P = VT + 64 * TP * 4;        // [4][16][TP] f  score partials, one per wave
+    static constexpr int TOT = P + 4 * kBlk * TP * 4; // [4][64] f  each wave's log2 decay
+    static constexpr int FLAG = TOT + 4 * 64 * 4;
+    static constexpr int BYTES = FLAG + 16;
+};
+
+__device__ __forceinline__ f32x4c mfma16x16(h16x4c a, h16x4c b, f32x4c c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4c mfma16x32(h16x8c a, h16x8c b, f32x4c c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+// Four operands (two dwords) as fp16: fp16 bits as they are, bf16 converted.
+template <bool H16>
+__device__ __forceinline__ h16x4c to_h4(u32x2c r) {
+    if constexpr (H16) {
+        return __builtin_bit_cast(h16x4c, r);
+    } else {
+        const f32x4c f = {__uint_as_float(r.x << 16), __uint_as_float(r.x & 0xffff0000u),
+                          __uint_as_float(r.y << 16), __uint_as_float(r.y & 0xffff0000u)};
+        return __builtin_convertvector(f, h16x4c);
+    }
+}
+template <bool H16>
+__device__ __forceinline__ float h_val(uint32_t x) {
+    if constexpr (H16) return (float)__builtin_bit_cast(h16c, (uint16_t)x);
+    else return __uint_as_float(x << 16);
+}
+// Eight fp16 operands of a 16x16x32 step: channels c .. c + 3 and c + 16 .. c + 19.
+__device__ __forceinline__ h16x8c frag8(const h16c *row, int c) {
+    const h16x4c lo = *reinterpret_cast<const h16x4c *>(row + c);
+    const h16x4c hi = *reinterpret_cast<const h16x4c *>(row + c + 16);
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// grid and work split as chan_pass_kernel.  FH: which of q, k, v (bits 0, 1, 2) are fp16;
+// the others are bf16.
+template <int DQ, int FH, bool ST>
+__global__ __launch_bounds__(256, 2) void chan_vg16_kernel(ChanPass a) {
+    constexpr bool QH16 = FH & 1, KH16 = (FH >> 1) & 1, VH16 = (FH >> 2) & 1;
+    using Lp = VgLds<DQ>;
+    constexpr int QH = Lp::QH, TH = Lp::TH, TP = Lp::TP, NJ = DQ / 16, NM = DQ / 32;
+    constexpr int GR = DQ / 4;   // four-channel groups per row
+    constexpr int NR = DQ / 64;  // q and k rows per thread
+    constexpr int NV = 4;        // v: tokens 4 tv .. 4 tv + 3 of column cv
+    extern __shared__ __align__(16) char smem[];
+    h16c *sQ = reinterpret_cast<h16c *>(smem + Lp::Q), *sK = reinterpret_cast<h16c *>(smem + Lp::K);
+    h16c *sKT = reinterpret_cast<h16c *>(smem + Lp::KT), *sVF = reinterpret_cast<h16c *>(smem + Lp::VF);
+    h16c *sVX = reinterpret_cast<h16c *>(smem + Lp::VX);
+    float *sB = reinterpret_cast<float *>(smem + Lp::B), *sVT = reinterpret_cast<float *>(smem + Lp::VT);
+    float *sP = reinterpret_cast<float *>(smem + Lp::P), *sTot = reinterpret_cast<float *>(smem + Lp::TOT);
+    int *sFlag = reinterpret_cast<int *>(smem + Lp::FLAG);
+
+    const int ndt = a.Dn / 64;
+    const int nsb = ST ? a.nseg - 1 : a.nseg;
+    size_t id = blockIdx.x;
+    const int seg = (int)(id % (unsigned)nsb);
+    id /= (unsigned)nsb;
+    const int n0 = (int)(id % (unsigned)ndt) * 64;
+    const size_t bh = id / (unsigned)ndt;
+    const int tid = (int)threadIdx.x, lane = tid & 63, w = tid >> 6, c16 = lane & 15, g = lane >> 4;
+    const int ncol = 16 * w + c16;
+    const int L = a.L, Dn = a.Dn;
+    const int ub = seg * a.seg_len, ue = min(L, ub + a.seg_len);
+    const size_t nsm = (size_t)(a.nseg - 1);
+    const float sc = grad_scale_of(a.mx[bh]);
+    const float osc = 1.f / sc;
+
+    const float *s_in = (ST || seg == 0) ? nullptr : a.ws_state + (bh * nsm + seg - 1) * (size_t)DQ * Dn;
+    f32x4c S[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            S[j][e] = s_in ? s_in[(size_t)(16 * j + 4 * g + e) * Dn + n0 + ncol] : 0.f;
+    if (!ST && seg == 0 && a.s0) {
+        const float is = a.s0_scaled ? sc : 1.f;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                S[j][e] = a.s0[(bh * DQ + 16 * j + 4 * g + e) * Dn + n0 + ncol] * is;
+    }
+    float gtot = 0.f;
+
+    const uint64_t Lu = (uint64_t)L;
+    const rsrc_c rq = mk_rsrc(reinterpret_cast<const char *>(a.q) + bh * Lu * DQ * 2, Lu * DQ * 2);
+    const rsrc_c rk = mk_rsrc(reinterpret_cast<const char *>(a.k) + bh * Lu * DQ * 2, Lu * DQ * 2);
+    const rsrc_c rv = mk_rsrc(reinterpret_cast<const char *>(a.v) + bh * Lu * Dn * 2, Lu * Dn * 2);
+    const rsrc_c rg = mk_rsrc(a.la + bh * Lu * Dn, Lu * Dn * 4);
+    const rsrc_c rvl = mk_rsrc(a.vli ? a.vli + bh * Lu : a.la, a.vli ? Lu * 4 : 0);
+    const rsrc_c rol = mk_rsrc(a.oli ? a.oli + bh * Lu : a.la, a.oli ? Lu * 4 : 0);
+    u32x2c fq[NR], fk[NR];
+    uint32_t fv[NV];
+    float fvl[NV], fg[NV], fol[4], ol[4];
+    // q, k: thread (rq0, gq) holds rows NR rq0 + i, channels 4 gq .. 4 gq + 3
+    const int rq0 = tid / GR, gq = tid % GR, tv = tid >> 6, cv = tid & 63;
+    auto row_of = [&](int rev, int u) { return rev ? L - 1 - u : u; };
+    auto fetch = [&](int u0) {
+#pragma unroll
+        for (int i = 0; i < NR; ++i) {
+            const int u = u0 + NR * rq0 + i;
+            const bool ok = u < ue;
+            const uint32_t oq = (uint32_t)((row_of(a.qrev, u) * DQ + 4 * gq) * 2);
+            const uint32_t ok_ = (uint32_t)((row_of(a.krev, u) * DQ + 4 * gq) * 2);
+            fq[i] = __builtin_amdgcn_raw_buffer_load_b64(rq, (int)(ok ? oq : kOff), 0, 0);
+            fk[i] = __builtin_amdgcn_raw_buffer_load_b64(rk, (int)(ok ? ok_ : kOff), 0, 0);
+        }
+        const int uv = u0 + 4 * tv;
+        const int rv0 = row_of(a.vrev, uv), sr = a.vrev ? -1 : 1;
+        const int r0 = a.grev ? L - uv : uv, sg = a.grev ? -1 : 1;
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int u = uv + i;
+            const bool ok = u < ue;
+            const int row = rv0 + i * sr;
+            fv[i] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rv, (int)(ok ? (uint32_t)((row * Dn + n0 + cv) * 2) : kOff), 0, 0);
+            fvl[i] = ld_f32(rvl, ok ? (uint32_t)row : kOff);
+            // gate rows: token u reads row L - u when reversed (zero for u = 0), else row u
+            const bool okg = ok && !(a.grev && u == 0);
+            fg[i] = ld_f32(rg, okg ? (uint32_t)((r0 + i * sg) * Dn + n0 + cv) : kOff);
+        }
+        const int u = u0 + 4 * g, ro = row_of(a.orev, u), so = a.orev ? -1 : 1;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) fol[e] = ld_f32(rol, (!ST && u + e < ue) ? (uint32_t)(ro + e * so) : kOff);
+    };
+    fetch(ub);
+
+    for (int u0 = ub; u0 < ue; u0 += kBlk) {
+        // ---- q, k rows and k transposed as fp16; v and the running log2 decays of its four
+        // tokens in registers, the wave's decay total in LDS
+        h16x4c kh[NR];
+#pragma unroll
+        for (int i = 0; i < NR; ++i) {
+            const int t = NR * rq0 + i;
+            *reinterpret_cast<h16x4c *>(sQ + t * QH + 4 * gq) = to_h4<QH16>(fq[i]);
+            kh[i] = to_h4<KH16>(fk[i]);
+            *reinterpret_cast<h16x4c *>(sK + t * QH + 4 * gq) = kh[i];
+        }
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            h16c *dst = sKT + (4 * gq + x) * TH + NR * rq0;
+            if constexpr (NR == 1) {
+                dst[0] = kh[0][x];
+            } else if constexpr (NR == 2) {
+                *reinterpret_cast<h16x2c *>(dst) = h16x2c{kh[0][x], kh[1][x]};
+            } else {
+                *reinterpret_cast<h16x4c *>(dst) = h16x4c{kh[0][x], kh[1][x], kh[2][x], kh[3][x]};
+            }
+        }
+        f32x4c vr, loc;
+        float run = 0.f;
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            float v = h_val<VH16>(fv[i]);
+            if (a.vli) v *= fexp2c(fvl[i] * kLog2eC);
+            vr[i] = v;
+            run += fg[i] == 0.f ? 0.f : log2_gate(fg[i]);
+            loc[i] = run;
+        }
+        sTot[tv * 64 + cv] = run;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ol[e] = fol[e];
+        if (tid == 0) *sFlag = 0;
+        lds_sync();
+        if (u0 + kBlk < ue) fetch(u0 + kBlk);
+        // ---- running log2 decays of column cv, tokens 4 tv .. 4 tv + 3; decay-weighted values
+        {
+            float pre = 0.f, tot = 0.f;
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                const float y = sTot[x * 64 + cv];
+                tot += y;
+                pre += x < tv ? y : 0.f;
+            }
+            f32x4c b4, vf4, vx4;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                b4[i] = pre + loc[i];
+                vf4[i] = vr[i] * fexp2c(tot - b4[i]);
+                vx4[i] = vr[i] * fexp2c(-b4[i]);  // bounded by 2^8 unless strong
+            }
+            *reinterpret_cast<f32x4c *>(sB + cv * TP + 4 * tv) = b4;
+            *reinterpret_cast<h16x4c *>(sVF + cv * TH + 4 * tv) = __builtin_convertvector(vf4, h16x4c);
+            if constexpr (!ST) {
+                *reinterpret_cast<f32x4c *>(sVT + cv * TP + 4 * tv) = vr;
+                *reinterpret_cast<h16x4c *>(sVX + cv * TH + 4 * tv) = __builtin_convertvector(vx4, h16x4c);
+                if (tot < kFactorFloor16) *sFlag = 1;
+            }
+            if (tid < 64) gtot += tot;
+        }
+        if constexpr (!ST) {
+            // ---- scores P[t][s] = q_t . k_s, the 32-channel steps split over the waves, one
+            // partial per wave (zero for a wave without steps)
+            constexpr int MW = NM >= 4 ? NM / 4 : 1;
+            f32x4c pc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int mm = 0; mm < MW; ++mm) {
+                const int m = w * MW + mm;
+                if (m < NM) {
+                    const h16x8c qa = frag8(sQ + c16 * QH, 32 * m + 4 * g);
+                    const h16x8c kb = frag8(sK + c16 * QH, 32 * m + 4 * g);
+                    pc = mfma16x32(qa, kb, pc);
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int t = 4 * g + e;
+                sP[(w * kBlk + t) * TP + c16] = c16 <= t ? pc[e] : 0.f;
+            }
+        }
+        lds_sync();
+        if constexpr (!ST) {
+            const bool strong = *sFlag != 0;
+            auto p4 = [&](int t, int s0) {
+                f32x4c r = *reinterpret_cast<const f32x4c *>(sP + t * TP + s0);
+#pragma unroll
+                for (int x = 1; x < 4; ++x) r += *reinterpret_cast<const f32x4c *>(sP + (x * kBlk + t) * TP + s0);
+                return r;
+            };
+            // ---- outputs of the block's 16 tokens for this lane's column: q S
+            f32x4c O = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int m = 0; m < NM; ++m) {
+                const h16x8c qa = frag8(sQ + c16 * QH, 32 * m + 4 * g);
+                const h16x4c s0 = __builtin_convertvector(S[2 * m], h16x4c);
+                const h16x4c s1 = __builtin_convertvector(S[2 * m + 1], h16x4c);
+                O = mfma16x32(qa, __builtin_shufflevector(s0, s1, 0, 1, 2, 3, 4, 5, 6, 7), O);
+            }
+            if (!strong) {
+                // (q S + P v 2^(-b_s)) 2^(b_t)
+                const h16x4c pa = __builtin_convertvector(p4(c16, 4 * g), h16x4c);
+                const h16x4c vb = *reinterpret_cast<const h16x4c *>(sVX + ncol * TH + 4 * g);
+                O = mfma16x16(pa, vb, O);
+                const f32x4c b4 = *reinterpret_cast<const f32x4c *>(sB + ncol * TP + 4 * g);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) O[e] *= fexp2c(b4[e]);
+            } else {
+                // strong decay: the entering state's term decays with the column; the block's
+                // own tokens with exact factors 2^(b_t - b_s), s <= t, in fp32
+                float vc[kBlk], bc[kBlk];
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const f32x4c v4 = *reinterpret_cast<const f32x4c *>(sVT + ncol * TP + 4 * m);
+                    const f32x4c b4 = *reinterpret_cast<const f32x4c *>(sB + ncol * TP + 4 * m);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) vc[4 * m + e] = v4[e], bc[4 * m + e] = b4[e];
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    float bt = bc[0];
+#pragma unroll
+                    for (int m = 1; m < kBlk; ++m) bt = (4 * g + e == m) ? bc[m] : bt;
+                    float o = O[e] * fexp2c(bt);
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) {
+                        const f32x4c pr = p4(4 * g + e, 4 * m);
+#pragma unroll
+                        for (int x = 0; x < 4; ++x) {
+                            const int s2 = 4 * m + x;
+                            const float f = s2 <= 4 * g + e ? fexp2c(bt - bc[s2]) : 0.f;
+                            o += pr[x] * vc[s2] * f;
+                        }
+                    }
+                    O[e] = o;
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int u = u0 + 4 * g + e;
+                if (u < ue) {
+                    const size_t dst = bh * L + (a.orev ? L - 1 - u : u);
+                    float o = O[e] * osc;
+                    if (a.oli) o *= fexp2c(ol[e] * kLog2eC);
+                    a.out[dst * Dn + n0 + ncol] = o;
+                }
+            }
+        }
+        // ---- state to the block end: S diag(2^(b_15)) + k^T (v 2^(b_15 - b_s))
+        const float dec = fexp2c(sB[ncol * TP + kBlk - 1]);
+        const h16x4c vb = *reinterpret_cast<const h16x4c *>(sVF + ncol * TH + 4 * g);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            const h16x4c ka = *reinterpret_cast<const h16x4c *>(sKT + (16 * j + c16) * TH + 4 * g);
+            S[j] = mfma16x16(ka, vb, S[j] * dec);
+        }
+        lds_sync();
+    }
+    if constexpr (ST) {
+        float *st = a.ws_state + (bh * nsm + seg) * (size_t)DQ * Dn;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) st[(size_t)(16 * j + 4 * g + e) * Dn + n0 + ncol] = S[j][e];
+        if (tid < 64) a.ws_decay[(bh * nsm + seg) * Dn + n0 + tid] = fexp2c(gtot);
+    } else if (a.fin && seg == a.nseg - 1) {
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) a.fin[(bh * DQ + 16 * j + 4 * g + e) * Dn + n0 + ncol] = S[j][e];
+    }
+}
+
 // The states entering segments 1 .. nseg-1: S <- decay_s S + own_s from the initial state
 // (or zero), one thread per state element, written over the segments' own states.
 template <bool KG>
@@ -457,7 +852,7 @@ __global__ __launch_bounds__(256) void chan_seg_scan_kernel(ChanPass a, int Dq, 
     const int d = (int)(e / (size_t)a.Dn), n = (int)(e % (size_t)a.Dn);
     const int Dg = KG ? Dq : a.Dn;
     const size_t nsm = (size_t)(a.nseg - 1);
-    float x = a.s0 ? a.s0[i] : 0.f;
+    float x = a.s0 ? a.s0[i] * (a.s0_scaled ? grad_scale_of(a.mx[bh]) : 1.f) : 0.f;
     for (size_t s = 0; s < nsm; ++s) {
         float *st = a.ws_state + (bh * nsm + s) * m + e;
         x = a.ws_decay[(bh * nsm + s) * Dg + (KG ? d : n)] * x + *st;
@@ -597,6 +992,37 @@ hipError_t launch_dq(const ChanPass &p, int BH, hipStream_t st) {
     return hipGetLastError();
 }
 
+template <int DQ, int FH>
+hipError_t launch_vg16_dq(const ChanPass &p, int BH, hipStream_t st) {
+    static std::atomic<uint64_t> done[2] = {{0}, {0}};
+    const int bytes = VgLds<DQ>::BYTES;
+    hipError_t e;
+    if (p.nseg > 1) {
+        const void *fs = reinterpret_cast<const void *>(&chan_vg16_kernel<DQ, FH, true>);
+        if ((e = lds_limit(fs, done[1], bytes)) != hipSuccess) return e;
+        const dim3 gs((unsigned)((size_t)BH * (p.Dn / 64) * (p.nseg - 1)));
+        hipLaunchKernelGGL((chan_vg16_kernel<DQ, FH, true>), gs, dim3(256), bytes, st, p);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        const size_t total = (size_t)BH * DQ * p.Dn;
+        hipLaunchKernelGGL((chan_seg_scan_kernel<false>), dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, p,
+                           DQ, total);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    const void *fn = reinterpret_cast<const void *>(&chan_vg16_kernel<DQ, FH, false>);
+    if ((e = lds_limit(fn, done[0], bytes)) != hipSuccess) return e;
+    const dim3 grid((unsigned)((size_t)BH * (p.Dn / 64) * p.nseg));
+    hipLaunchKernelGGL((chan_vg16_kernel<DQ, FH, false>), grid, dim3(256), bytes, st, p);
+    return hipGetLastError();
+}
+
+// A value-gated pass on fp16 operands: FH = 2 (k is the fp16 output gradient) or 1 (q is).
+template <int FH>
+hipError_t launch_vg16(const ChanPass &p, int BH, int Dq, hipStream_t st) {
+    if (Dq == 64) return launch_vg16_dq<64, FH>(p, BH, st);
+    if (Dq == 128) return launch_vg16_dq<128, FH>(p, BH, st);
+    return launch_vg16_dq<256, FH>(p, BH, st);
+}
+
 template <bool KG, int FM>
 hipError_t launch_fm(const ChanPass &p, int BH, int Dq, hipStream_t st) {
     if (Dq == 64) return launch_dq<KG, 64, FM>(p, BH, st);
@@ -653,9 +1079,11 @@ size_t chan_scratch_floats(int BH, int L, int Dk, int Dv) {
 // dfinal^T ([Dv][Dk], or null), finA [Dk][Dv] and finC [Dv][Dk] receive the first and third
 // passes' final states, scratch holds chan_scratch_floats(...) floats.
 // skip_dv: the dv pass ran elsewhere (bf16 inputs with Dk <= 128 take it on the forward
-// kernel's fp16 path).
+// kernel's fp16 path).  fdo, mx (bf16 inputs, else null): the output gradient times s as fp16
+// ([BH][L][Dv]) and the scale bits of s per (batch, head); with them the dk and dq passes run
+// on fp16 operands (chan_vg16_kernel).
 hipError_t chan_backward(const gla_bwd_desc &d, const float *s0T, const float *dfT, float *finA, float *finC,
-                         float *scratch, bool skip_dv, hipStream_t st) {
+                         float *scratch, bool skip_dv, const _Float16 *fdo, const uint32_t *mx, hipStream_t st) {
     const int BH = d.B * d.H, L = d.L, Dk = d.Dk, Dv = d.Dv, dt = d.in_dtype;
     hipError_t e;
     const int nsg = (L + kSeg - 1) / kSeg;
@@ -683,25 +1111,27 @@ hipError_t chan_backward(const gla_bwd_desc &d, const float *s0T, const float *d
     segs(Dv, Dk);
     if (!skip_dv && (e = launch_pass<true>(p, BH, Dk, st)) != hipSuccess) return e;
     // dk: value-gated, reversed, keys and values exchanged
+    const bool h16 = mx != nullptr;
+    p.mx = mx;
     p.q = d.v, p.qdt = dt, p.qrev = 1;
-    p.k = d.dout, p.kdt = GLA_DTYPE_F32, p.krev = 1;
+    p.k = h16 ? static_cast<const void *>(fdo) : d.dout, p.kdt = GLA_DTYPE_F32, p.krev = 1;
     p.v = d.q, p.vdt = dt, p.vrev = 1;
-    p.s0 = dfT;
+    p.s0 = dfT, p.s0_scaled = h16 ? 1 : 0;
     p.out = d.dk;
     p.fin = nullptr;
     p.Dn = Dk;
     segs(Dk, Dv);
-    if ((e = launch_pass<false>(p, BH, Dv, st)) != hipSuccess) return e;
+    if ((e = h16 ? launch_vg16<2>(p, BH, Dv, st) : launch_pass<false>(p, BH, Dv, st)) != hipSuccess) return e;
     // dq: value-gated, keys and values exchanged, input gate on the values
-    p.q = d.dout, p.qdt = GLA_DTYPE_F32, p.qrev = 0;
+    p.q = h16 ? static_cast<const void *>(fdo) : d.dout, p.qdt = GLA_DTYPE_F32, p.qrev = 0;
     p.k = d.v, p.kdt = dt, p.krev = 0;
     p.v = d.k, p.vdt = dt, p.vrev = 0;
     p.vli = d.log_ig;
     p.grev = 0;
-    p.s0 = s0T;
+    p.s0 = s0T, p.s0_scaled = 0;
     p.out = d.dq, p.orev = 0, p.oli = nullptr;
     p.fin = finC;
-    if ((e = launch_pass<false>(p, BH, Dv, st)) != hipSuccess) return e;
+    if ((e = h16 ? launch_vg16<1>(p, BH, Dv, st) : launch_pass<false>(p, BH, Dv, st)) != hipSuccess) return e;
     if (d.dlog_alpha) {
         const int nseg = nsg;
         float *g = g_rows;

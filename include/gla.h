@@ -25,7 +25,9 @@
  * states and all accumulation are fp32.  With bf16 inputs the products that involve a
  * computed operand (gate-rescaled q and k, the masked score matrix, the carried state)
  * take fp16 operands on the matrix cores, and per-channel decay factors are applied to
- * those operands in fp16; with fp32 inputs every operand stays fp32.
+ * those operands in fp16; with fp32 inputs every operand stays fp32.  fp16 holds
+ * magnitudes up to 65504 with 11 significant bits, so with bf16 inputs q, k, v and the
+ * entries of the carried state must stay below that (larger data needs fp32 inputs).
  *
  * Layout and ownership.  Every tensor is dense, row-major and contiguous on the device,
  * with the shapes given below, and 16-byte aligned.  The caller owns all memory; the
@@ -198,13 +200,13 @@ int gla_step(const gla_step_desc *d, void *stream);
  * k_t * dk_t (B_t the running sum of log decays, per channel; a dot product over channels
  * for scalar gates; plus the final-state term at the last token) summed from t to the end,
  * and dlog_ig_t = k_t . dk_t.
- * Precision: fp32 inputs run the passes in fp32.  bf16 inputs run the passes that the forward
- * kernels compute (all three for a scalar gate or none; the dv pass for a per-channel gate
- * with Dk <= 128) on their fp16 matrix-core path, with q, k, v as given and dout entering as
- * fp16 after a per-(batch, head) power-of-two scale that puts its largest magnitude in [4, 8)
- * (dfinal_state counts at 1/64 of its magnitude); the scale is divided out exactly.  The
- * other per-channel passes run in fp32.  The range limits of bf16 forward inputs apply to
- * q, k, v.
+ * Precision: fp32 inputs run the passes in fp32.  bf16 inputs run every pass on fp16
+ * matrix-core operands (the forward kernels' fp16 path for the passes they compute, a
+ * value-gated kernel of the same numerics for the per-channel dk and dq passes), with q, k,
+ * v as given and dout entering as fp16 after a per-(batch, head) power-of-two scale that
+ * puts its largest magnitude in [4, 8) (dfinal_state counts at 1/64 of its magnitude); the
+ * scale is divided out exactly.  Only the per-channel dv pass with Dk = 256 runs in fp32.
+ * The fp16 range of the forward pass applies to q, k, v and to the passes' states.
  *
  * Shapes: q, k [B,H,L,Dk] and v [B,H,L,Dv] in in_dtype; gates as in gla_desc; dout
  * [B,H,L,Dv] fp32; dfinal_state [B,H,Dk,Dv] fp32 or NULL (zero); outputs fp32: dq, dk
