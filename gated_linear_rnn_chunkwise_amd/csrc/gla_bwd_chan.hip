@@ -1048,12 +1048,15 @@ hipError_t launch_pass(const ChanPass &p, int BH, int Dq, hipStream_t st) {
 
 }  // namespace
 
-// Sequence segments of the passes: enough workgroups for about four per compute unit
-// (value tiles x segments), segments of at least 64 tokens, lengths a multiple of 16.
+// Sequence segments of the passes: about `target` workgroups (value tiles x segments),
+// segments of at least 64 tokens, lengths a multiple of 16.  On 256 compute units: the fp32
+// pass kernel holds two workgroups per unit (two rounds of 512), the fp16 value-gated kernel
+// three (one round of 768; 512, 1024, 1536 and 2048 measured slower).
 constexpr int kChanTargetWorkgroups = 1024;
-void chan_segments(int BH, int L, int Dn, int *nseg, int *seg_len) {
+constexpr int kVg16TargetWorkgroups = 768;
+void chan_segments(int BH, int L, int Dn, int target, int *nseg, int *seg_len) {
     const long long tiles = (long long)BH * (Dn / 64);
-    long long want = (kChanTargetWorkgroups + tiles - 1) / tiles;
+    long long want = (target + tiles - 1) / tiles;
     const long long most = ((long long)L + 63) / 64;
     if (want > most) want = most;
     if (want < 1) want = 1;
@@ -1068,8 +1071,11 @@ size_t chan_scratch_floats(int BH, int L, int Dk, int Dv) {
     const size_t ns = ((size_t)L + kSeg - 1) / kSeg;
     size_t n = (size_t)BH * L * Dk + (size_t)BH * ns * Dk + (size_t)BH * Dk;
     int s1, l1, s2, l2;
-    chan_segments(BH, L, Dv, &s1, &l1);  // the key-gated pass (value dimension Dv)
-    chan_segments(BH, L, Dk, &s2, &l2);  // the value-gated passes (value dimension Dk)
+    chan_segments(BH, L, Dv, kChanTargetWorkgroups, &s1, &l1);  // the key-gated pass (value dimension Dv)
+    chan_segments(BH, L, Dk, kChanTargetWorkgroups, &s2, &l2);  // the value-gated passes (value dimension Dk)
+    int s3 = 0;
+    chan_segments(BH, L, Dk, kVg16TargetWorkgroups, &s3, &l2);  // the same on fp16 operands
+    s2 = s2 > s3 ? s2 : s3;
     const size_t nsm = (size_t)((s1 > s2 ? s1 : s2) - 1);
     n += (size_t)BH * nsm * Dk * Dv + (size_t)BH * nsm * (Dk > Dv ? Dk : Dv);
     return n;
@@ -1094,8 +1100,8 @@ hipError_t chan_backward(const gla_bwd_desc &d, const float *s0T, const float *d
     ChanPass p{};
     p.L = L;
     p.ws_state = seg_ws;
-    auto segs = [&](int Dn, int Dq) {
-        chan_segments(BH, L, Dn, &p.nseg, &p.seg_len);
+    auto segs = [&](int Dn, int Dq, int target) {
+        chan_segments(BH, L, Dn, target, &p.nseg, &p.seg_len);
         p.ws_decay = seg_ws + (size_t)BH * (p.nseg - 1) * Dq * Dn;
     };
     // dv: key-gated, reversed
@@ -1108,7 +1114,7 @@ hipError_t chan_backward(const gla_bwd_desc &d, const float *s0T, const float *d
     p.out = d.dv, p.orev = 1, p.oli = d.log_ig;
     p.fin = finA;
     p.Dn = Dv;
-    segs(Dv, Dk);
+    segs(Dv, Dk, kChanTargetWorkgroups);
     if (!skip_dv && (e = launch_pass<true>(p, BH, Dk, st)) != hipSuccess) return e;
     // dk: value-gated, reversed, keys and values exchanged
     const bool h16 = mx != nullptr;
@@ -1120,7 +1126,7 @@ hipError_t chan_backward(const gla_bwd_desc &d, const float *s0T, const float *d
     p.out = d.dk;
     p.fin = nullptr;
     p.Dn = Dk;
-    segs(Dk, Dv);
+    segs(Dk, Dv, h16 ? kVg16TargetWorkgroups : kChanTargetWorkgroups);
     if ((e = h16 ? launch_vg16<2>(p, BH, Dv, st) : launch_pass<false>(p, BH, Dv, st)) != hipSuccess) return e;
     // dq: value-gated, keys and values exchanged, input gate on the values
     p.q = h16 ? static_cast<const void *>(fdo) : d.dout, p.qdt = GLA_DTYPE_F32, p.qrev = 0;
