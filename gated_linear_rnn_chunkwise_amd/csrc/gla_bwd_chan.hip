@@ -526,11 +526,12 @@ typedef uint32_t u32x2c __attribute__((ext_vector_type(2)));
 
 constexpr float kFactorFloor16 = -8.f;
 
-// LDS plan (bytes): fp16 q and k rows padded by 16 B, fp16 transposed rows of 16 tokens
+// LDS plan (bytes): fp16 q and k rows padded by 48 B (the fragment reads of a half-wave then
+// fall on distinct banks), fp16 transposed rows of 16 tokens
 // padded to 20 halves, fp32 transposed rows padded to 20 floats.
 template <int DQ>
 struct VgLds {
-    static constexpr int QH = DQ + 8, TH = 20, TP = 20;
+    static constexpr int QH = DQ + 24, TH = 20, TP = 20;
     static constexpr int Q = 0;                       // [16][QH] h  q
     static constexpr int K = Q + kBlk * QH * 2;       // [16][QH] h  k
     static constexpr int KT = K + kBlk * QH * 2;      // [DQ][TH] h  k, transposed
@@ -627,7 +628,10 @@ __global__ __launch_bounds__(256, 2) void chan_vg16_kernel(ChanPass a) {
     const rsrc_c rq = mk_rsrc(reinterpret_cast<const char *>(a.q) + bh * Lu * DQ * 2, Lu * DQ * 2);
     const rsrc_c rk = mk_rsrc(reinterpret_cast<const char *>(a.k) + bh * Lu * DQ * 2, Lu * DQ * 2);
     const rsrc_c rv = mk_rsrc(reinterpret_cast<const char *>(a.v) + bh * Lu * Dn * 2, Lu * Dn * 2);
-    const rsrc_c rg = mk_rsrc(a.la + bh * Lu * Dn, Lu * Dn * 4);
+    // The gate of a reversed pass is token u's row L - u: row L - 1 - u of a view that starts
+    // one row later.
+    const uint64_t g1 = a.grev ? 1 : 0;
+    const rsrc_c rg = mk_rsrc(a.la + (bh * Lu + g1) * Dn, (Lu - g1) * Dn * 4);
     const rsrc_c rvl = mk_rsrc(a.vli ? a.vli + bh * Lu : a.la, a.vli ? Lu * 4 : 0);
     const rsrc_c rol = mk_rsrc(a.oli ? a.oli + bh * Lu : a.la, a.oli ? Lu * 4 : 0);
     u32x2c fq[NR], fk[NR];
@@ -635,34 +639,33 @@ __global__ __launch_bounds__(256, 2) void chan_vg16_kernel(ChanPass a) {
     float fvl[NV], fg[NV], fol[4], ol[4];
     // q, k: thread (rq0, gq) holds rows NR rq0 + i, channels 4 gq .. 4 gq + 3
     const int rq0 = tid / GR, gq = tid % GR, tv = tid >> 6, cv = tid & 63;
-    auto row_of = [&](int rev, int u) { return rev ? L - 1 - u : u; };
+    // Token u reads row L - 1 - u of a reversed operand, else row u, with no masks: segments
+    // end on block boundaries, so only the sequence end cuts a block, and rows past either end
+    // lie outside the slice (a negative row wraps to a 32-bit offset past it) and read zero.
+    auto row_of = [&](int rev, int u) { return (uint32_t)(rev ? L - 1 - u : u); };
     auto fetch = [&](int u0) {
 #pragma unroll
         for (int i = 0; i < NR; ++i) {
             const int u = u0 + NR * rq0 + i;
-            const bool ok = u < ue;
-            const uint32_t oq = (uint32_t)((row_of(a.qrev, u) * DQ + 4 * gq) * 2);
-            const uint32_t ok_ = (uint32_t)((row_of(a.krev, u) * DQ + 4 * gq) * 2);
-            fq[i] = __builtin_amdgcn_raw_buffer_load_b64(rq, (int)(ok ? oq : kOff), 0, 0);
-            fk[i] = __builtin_amdgcn_raw_buffer_load_b64(rk, (int)(ok ? ok_ : kOff), 0, 0);
+            const uint32_t oq = (row_of(a.qrev, u) * (uint32_t)DQ + 4u * gq) * 2u;
+            const uint32_t ok_ = (row_of(a.krev, u) * (uint32_t)DQ + 4u * gq) * 2u;
+            fq[i] = __builtin_amdgcn_raw_buffer_load_b64(rq, (int)oq, 0, 0);
+            fk[i] = __builtin_amdgcn_raw_buffer_load_b64(rk, (int)ok_, 0, 0);
         }
-        const int uv = u0 + 4 * tv;
-        const int rv0 = row_of(a.vrev, uv), sr = a.vrev ? -1 : 1;
-        const int r0 = a.grev ? L - uv : uv, sg = a.grev ? -1 : 1;
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
-            const int u = uv + i;
-            const bool ok = u < ue;
-            const int row = rv0 + i * sr;
-            fv[i] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rv, (int)(ok ? (uint32_t)((row * Dn + n0 + cv) * 2) : kOff), 0, 0);
-            fvl[i] = ld_f32(rvl, ok ? (uint32_t)row : kOff);
-            // gate rows: token u reads row L - u when reversed (zero for u = 0), else row u
-            const bool okg = ok && !(a.grev && u == 0);
-            fg[i] = ld_f32(rg, okg ? (uint32_t)((r0 + i * sg) * Dn + n0 + cv) : kOff);
+            const int u = u0 + 4 * tv + i;
+            const uint32_t rv_ = row_of(a.vrev, u), rg_ = row_of(a.grev, u);
+            fv[i] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rv, (int)((rv_ * (uint32_t)Dn + n0 + cv) * 2u), 0, 0);
+            fvl[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rvl, (int)(rv_ * 4u), 0, 0));
+            fg[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rg, (int)((rg_ * (uint32_t)Dn + n0 + cv) * 4u), 0, 0));
         }
-        const int u = u0 + 4 * g, ro = row_of(a.orev, u), so = a.orev ? -1 : 1;
+        if constexpr (!ST) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) fol[e] = ld_f32(rol, (!ST && u + e < ue) ? (uint32_t)(ro + e * so) : kOff);
+            for (int e = 0; e < 4; ++e)
+                fol[e] = __uint_as_float(
+                    __builtin_amdgcn_raw_buffer_load_b32(rol, (int)(row_of(a.orev, u0 + 4 * g + e) * 4u), 0, 0));
+        }
     };
     fetch(ub);
 
@@ -695,12 +698,14 @@ __global__ __launch_bounds__(256, 2) void chan_vg16_kernel(ChanPass a) {
             float v = h_val<VH16>(fv[i]);
             if (a.vli) v *= fexp2c(fvl[i] * kLog2eC);
             vr[i] = v;
-            run += fg[i] == 0.f ? 0.f : log2_gate(fg[i]);
+            run += log2_gate(fg[i]);
             loc[i] = run;
         }
         sTot[tv * 64 + cv] = run;
+        if constexpr (!ST) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) ol[e] = fol[e];
+            for (int e = 0; e < 4; ++e) ol[e] = fol[e];
+        }
         if (tid == 0) *sFlag = 0;
         lds_sync();
         if (u0 + kBlk < ue) fetch(u0 + kBlk);
