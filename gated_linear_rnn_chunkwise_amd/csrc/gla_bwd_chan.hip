@@ -53,6 +53,17 @@ struct ChanPass {
     // divided by the scale s, and the initial state multiplied by s when s0_scaled
     const uint32_t *mx;
     int s0_scaled;
+    // The per-channel log-gate gradient, formed by the reversed dk pass on fp16 operands
+    // (chan_vg16_kernel, g_out non-null): pass token u is sequence row t = L-1-u, so the
+    // running sum over the pass of g_t = q_t dq_t - k_t dk_t (the pass's v operand is q) is the
+    // sum over s >= t.  g_dq: dq [BH][L][Dn] fp32 (from the dq pass), g_k: k [BH][L][Dn] bf16;
+    // g_out: dlog_alpha, complete in the first segment (which starts from g_fterm, the
+    // final-state term, or zero), the segment's own sum elsewhere; g_part [BH][nseg][Dn]: the
+    // segments' totals, for chan_gfix_kernel.
+    const float *g_dq;
+    const void *g_k;
+    float *g_out, *g_part;
+    const float *g_fterm;
 };
 
 namespace {
@@ -575,8 +586,8 @@ __device__ __forceinline__ h16x8c frag8(const h16c *row, int c) {
 }
 
 // grid and work split as chan_pass_kernel.  FH: which of q, k, v (bits 0, 1, 2) are fp16;
-// the others are bf16.
-template <int DQ, int FH, bool ST>
+// the others are bf16.  GG: the pass forms the log-gate gradient (g_out).
+template <int DQ, int FH, bool ST, bool GG = false>
 __global__ __launch_bounds__(256, 2) void chan_vg16_kernel(ChanPass a) {
     constexpr bool QH16 = FH & 1, KH16 = (FH >> 1) & 1, VH16 = (FH >> 2) & 1;
     using Lp = VgLds<DQ>;
@@ -623,6 +634,10 @@ __global__ __launch_bounds__(256, 2) void chan_vg16_kernel(ChanPass a) {
                 S[j][e] = a.s0[(bh * DQ + 16 * j + 4 * g + e) * Dn + n0 + ncol] * is;
     }
     float gtot = 0.f;
+    // gate gradient: running sum of the segment's terms before the current block (every lane
+    // group g of a column holds it), and the final-state term that the first segment starts from
+    float grun = 0.f;
+    const float gf = (GG && !ST && seg == 0 && a.g_fterm) ? a.g_fterm[bh * Dn + n0 + ncol] : 0.f;
 
     const uint64_t Lu = (uint64_t)L;
     const rsrc_c rq = mk_rsrc(reinterpret_cast<const char *>(a.q) + bh * Lu * DQ * 2, Lu * DQ * 2);
@@ -634,6 +649,9 @@ __global__ __launch_bounds__(256, 2) void chan_vg16_kernel(ChanPass a) {
     const rsrc_c rg = mk_rsrc(a.la + (bh * Lu + g1) * Dn, (Lu - g1) * Dn * 4);
     const rsrc_c rvl = mk_rsrc(a.vli ? a.vli + bh * Lu : a.la, a.vli ? Lu * 4 : 0);
     const rsrc_c rol = mk_rsrc(a.oli ? a.oli + bh * Lu : a.la, a.oli ? Lu * 4 : 0);
+    constexpr bool gg = GG && !ST;
+    const rsrc_c rgd = mk_rsrc(gg ? a.g_dq + bh * Lu * Dn : a.la, gg ? Lu * Dn * 4 : 0);
+    const rsrc_c rgk = mk_rsrc(gg ? reinterpret_cast<const char *>(a.g_k) + bh * Lu * Dn * 2 : nullptr, gg ? Lu * Dn * 2 : 0);
     u32x2c fq[NR], fk[NR];
     uint32_t fv[NV];
     float fvl[NV], fg[NV], fol[4], ol[4];
@@ -709,6 +727,17 @@ __global__ __launch_bounds__(256, 2) void chan_vg16_kernel(ChanPass a) {
         if (tid == 0) *sFlag = 0;
         lds_sync();
         if (u0 + kBlk < ue) fetch(u0 + kBlk);
+        // gate gradient: dq and k of this lane's output elements, needed after the block's
+        // products (loaded here rather than a block ahead, to keep registers for occupancy)
+        float gd[4], gk[4];
+        if constexpr (gg) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t oe = row_of(a.orev, u0 + 4 * g + e) * (uint32_t)Dn + n0 + ncol;
+                gd[e] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rgd, (int)(oe * 4u), 0, 0));
+                gk[e] = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rgk, (int)(oe * 2u), 0, 0) << 16);
+            }
+        }
         // ---- running log2 decays of column cv, tokens 4 tv .. 4 tv + 3; decay-weighted values
         {
             float pre = 0.f, tot = 0.f;
@@ -810,15 +839,32 @@ __global__ __launch_bounds__(256, 2) void chan_vg16_kernel(ChanPass a) {
                     O[e] = o;
                 }
             }
+            f32x4c gt;  // gate-gradient terms q dq - k dk of this lane's four tokens
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int u = u0 + 4 * g + e;
-                if (u < ue) {
-                    const size_t dst = bh * L + (a.orev ? L - 1 - u : u);
-                    float o = O[e] * osc;
-                    if (a.oli) o *= fexp2c(ol[e] * kLog2eC);
-                    a.out[dst * Dn + n0 + ncol] = o;
+                float o = O[e] * osc;
+                if (a.oli) o *= fexp2c(ol[e] * kLog2eC);
+                if constexpr (gg) gt[e] = sVT[ncol * TP + 4 * g + e] * gd[e] - gk[e] * o;
+                if (u < ue) a.out[(bh * L + (a.orev ? L - 1 - u : u)) * Dn + n0 + ncol] = o;
+            }
+            if constexpr (gg) {
+                // running sum over the block's 16 tokens (token 4 g + e): within the lane, then
+                // over the lane groups g of the column (lanes c16 + 16 g)
+                const float c1 = gt[0] + gt[1], c2 = c1 + gt[2], c3 = c2 + gt[3];
+                float inc = c3;
+                float y = __shfl_up(inc, 16);
+                inc += g >= 1 ? y : 0.f;
+                y = __shfl_up(inc, 32);
+                inc += g >= 2 ? y : 0.f;
+                const float base = gf + grun + (inc - c3);
+                const float cs[4] = {gt[0], c1, c2, c3};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int u = u0 + 4 * g + e;
+                    if (u < ue) a.g_out[(bh * L + (a.orev ? L - 1 - u : u)) * Dn + n0 + ncol] = base + cs[e];
                 }
+                grun += __shfl(inc, 48 + c16);
             }
         }
         // ---- state to the block end: S diag(2^(b_15)) + k^T (v 2^(b_15 - b_s))
@@ -843,6 +889,33 @@ __global__ __launch_bounds__(256, 2) void chan_vg16_kernel(ChanPass a) {
         for (int j = 0; j < NJ; ++j)
 #pragma unroll
             for (int e = 0; e < 4; ++e) a.fin[(bh * DQ + 16 * j + 4 * g + e) * Dn + n0 + ncol] = S[j][e];
+    }
+    if (gg && g == 0) a.g_part[(bh * a.nseg + seg) * Dn + n0 + ncol] = grun;
+}
+
+// dlog_alpha rows of segments 1 .. nseg-1 of the reversed dk pass: add the final-state term
+// and the totals of the segments before (later rows of the sequence).  Workgroup = up to 64
+// pass tokens of one segment of one (batch, head); thread = 4 channels of a row.
+__global__ __launch_bounds__(256) void chan_gfix_kernel(float *gout, const float *part, const float *fterm, int L,
+                                                        int Dk, int seg_len, int nseg, int chunks) {
+    size_t id = blockIdx.x;
+    const int ch = (int)(id % (unsigned)chunks);
+    id /= (unsigned)chunks;
+    const int seg = 1 + (int)(id % (unsigned)(nseg - 1));
+    const size_t bh = id / (unsigned)(nseg - 1);
+    const int G = Dk / 4, R = 256 / G;  // channel groups per row, rows in flight
+    const int c = 4 * ((int)threadIdx.x % G), r = (int)threadIdx.x / G;
+    float4 add = fterm ? *reinterpret_cast<const float4 *>(fterm + bh * Dk + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int s2 = 0; s2 < seg; ++s2) {
+        const float4 p = *reinterpret_cast<const float4 *>(part + (bh * nseg + s2) * Dk + c);
+        add.x += p.x, add.y += p.y, add.z += p.z, add.w += p.w;
+    }
+    const int u0 = seg * seg_len + ch * 64, u1 = min(min(L, (seg + 1) * seg_len), u0 + 64);
+    for (int u = u0 + r; u < u1; u += R) {
+        float4 *x = reinterpret_cast<float4 *>(gout + (bh * L + (L - 1 - u)) * Dk + c);
+        float4 v = *x;
+        v.x += add.x, v.y += add.y, v.z += add.z, v.w += add.w;
+        *x = v;
     }
 }
 
@@ -997,7 +1070,7 @@ hipError_t launch_dq(const ChanPass &p, int BH, hipStream_t st) {
     return hipGetLastError();
 }
 
-template <int DQ, int FH>
+template <int DQ, int FH, bool GG>
 hipError_t launch_vg16_dq(const ChanPass &p, int BH, hipStream_t st) {
     static std::atomic<uint64_t> done[2] = {{0}, {0}};
     const int bytes = VgLds<DQ>::BYTES;
@@ -1013,19 +1086,20 @@ hipError_t launch_vg16_dq(const ChanPass &p, int BH, hipStream_t st) {
                            DQ, total);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    const void *fn = reinterpret_cast<const void *>(&chan_vg16_kernel<DQ, FH, false>);
+    const void *fn = reinterpret_cast<const void *>(&chan_vg16_kernel<DQ, FH, false, GG>);
     if ((e = lds_limit(fn, done[0], bytes)) != hipSuccess) return e;
     const dim3 grid((unsigned)((size_t)BH * (p.Dn / 64) * p.nseg));
-    hipLaunchKernelGGL((chan_vg16_kernel<DQ, FH, false>), grid, dim3(256), bytes, st, p);
+    hipLaunchKernelGGL((chan_vg16_kernel<DQ, FH, false, GG>), grid, dim3(256), bytes, st, p);
     return hipGetLastError();
 }
 
-// A value-gated pass on fp16 operands: FH = 2 (k is the fp16 output gradient) or 1 (q is).
-template <int FH>
+// A value-gated pass on fp16 operands: FH = 2 (k is the fp16 output gradient) or 1 (q is);
+// GG: the pass also forms the log-gate gradient (p.g_out).
+template <int FH, bool GG>
 hipError_t launch_vg16(const ChanPass &p, int BH, int Dq, hipStream_t st) {
-    if (Dq == 64) return launch_vg16_dq<64, FH>(p, BH, st);
-    if (Dq == 128) return launch_vg16_dq<128, FH>(p, BH, st);
-    return launch_vg16_dq<256, FH>(p, BH, st);
+    if (Dq == 64) return launch_vg16_dq<64, FH, GG>(p, BH, st);
+    if (Dq == 128) return launch_vg16_dq<128, FH, GG>(p, BH, st);
+    return launch_vg16_dq<256, FH, GG>(p, BH, st);
 }
 
 template <bool KG, int FM>
@@ -1121,36 +1195,67 @@ hipError_t chan_backward(const gla_bwd_desc &d, const float *s0T, const float *d
     p.Dn = Dv;
     segs(Dv, Dk, kChanTargetWorkgroups);
     if (!skip_dv && (e = launch_pass<true>(p, BH, Dk, st)) != hipSuccess) return e;
-    // dk: value-gated, reversed, keys and values exchanged
     const bool h16 = mx != nullptr;
     p.mx = mx;
-    p.q = d.v, p.qdt = dt, p.qrev = 1;
-    p.k = h16 ? static_cast<const void *>(fdo) : d.dout, p.kdt = GLA_DTYPE_F32, p.krev = 1;
-    p.v = d.q, p.vdt = dt, p.vrev = 1;
-    p.s0 = dfT, p.s0_scaled = h16 ? 1 : 0;
-    p.out = d.dk;
-    p.fin = nullptr;
+    p.la = d.log_alpha;
     p.Dn = Dk;
     segs(Dk, Dv, h16 ? kVg16TargetWorkgroups : kChanTargetWorkgroups);
-    if ((e = h16 ? launch_vg16<2>(p, BH, Dv, st) : launch_pass<false>(p, BH, Dv, st)) != hipSuccess) return e;
+    // dk: value-gated, reversed, keys and values exchanged
+    auto dk_pass = [&](bool with_g) {
+        p.q = d.v, p.qdt = dt, p.qrev = 1;
+        p.k = h16 ? static_cast<const void *>(fdo) : d.dout, p.kdt = GLA_DTYPE_F32, p.krev = 1;
+        p.v = d.q, p.vdt = dt, p.vrev = 1;
+        p.vli = nullptr;
+        p.grev = 1;
+        p.s0 = dfT, p.s0_scaled = h16 ? 1 : 0;
+        p.out = d.dk, p.orev = 1, p.oli = d.log_ig;
+        p.fin = nullptr;
+        p.g_dq = with_g ? d.dq : nullptr;
+        p.g_k = with_g ? d.k : nullptr;
+        p.g_out = with_g ? d.dlog_alpha : nullptr;
+        p.g_part = with_g ? part : nullptr;
+        p.g_fterm = with_g && dfT ? fterm : nullptr;
+        if (!h16) return launch_pass<false>(p, BH, Dv, st);
+        return with_g ? launch_vg16<2, true>(p, BH, Dv, st) : launch_vg16<2, false>(p, BH, Dv, st);
+    };
     // dq: value-gated, keys and values exchanged, input gate on the values
-    p.q = h16 ? static_cast<const void *>(fdo) : d.dout, p.qdt = GLA_DTYPE_F32, p.qrev = 0;
-    p.k = d.v, p.kdt = dt, p.krev = 0;
-    p.v = d.k, p.vdt = dt, p.vrev = 0;
-    p.vli = d.log_ig;
-    p.grev = 0;
-    p.s0 = s0T, p.s0_scaled = 0;
-    p.out = d.dq, p.orev = 0, p.oli = nullptr;
-    p.fin = finC;
-    if ((e = h16 ? launch_vg16<1>(p, BH, Dv, st) : launch_pass<false>(p, BH, Dv, st)) != hipSuccess) return e;
+    auto dq_pass = [&]() {
+        p.q = h16 ? static_cast<const void *>(fdo) : d.dout, p.qdt = GLA_DTYPE_F32, p.qrev = 0;
+        p.k = d.v, p.kdt = dt, p.krev = 0;
+        p.v = d.k, p.vdt = dt, p.vrev = 0;
+        p.vli = d.log_ig;
+        p.grev = 0;
+        p.s0 = s0T, p.s0_scaled = 0;
+        p.out = d.dq, p.orev = 0, p.oli = nullptr;
+        p.fin = finC;
+        p.g_dq = nullptr, p.g_k = nullptr, p.g_out = nullptr, p.g_part = nullptr, p.g_fterm = nullptr;
+        return h16 ? launch_vg16<1, false>(p, BH, Dv, st) : launch_pass<false>(p, BH, Dv, st);
+    };
+    auto fterm_of = [&]() {
+        hipLaunchKernelGGL(chan_fterm_kernel, dim3((unsigned)((size_t)BH * (Dk / 64))), dim3(256), 0, st, dfT, finC,
+                           fterm, Dk, Dv);
+        return hipGetLastError();
+    };
+    if (h16 && d.dlog_alpha) {
+        // the reversed dk pass forms the log-gate gradient: dq and the final-state term first
+        if ((e = dq_pass()) != hipSuccess) return e;
+        if (dfT && (e = fterm_of()) != hipSuccess) return e;
+        if ((e = dk_pass(true)) != hipSuccess) return e;
+        if (p.nseg > 1) {
+            const int chunks = (p.seg_len + 63) / 64;
+            const dim3 grid((unsigned)((size_t)BH * (p.nseg - 1) * chunks));
+            hipLaunchKernelGGL(chan_gfix_kernel, grid, dim3(256), 0, st, d.dlog_alpha, part, dfT ? fterm : nullptr, L,
+                               Dk, p.seg_len, p.nseg, chunks);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+        }
+        return hipSuccess;
+    }
+    if ((e = dk_pass(false)) != hipSuccess) return e;
+    if ((e = dq_pass()) != hipSuccess) return e;
     if (d.dlog_alpha) {
         const int nseg = nsg;
         float *g = g_rows;
-        if (dfT) {
-            hipLaunchKernelGGL(chan_fterm_kernel, dim3((unsigned)((size_t)BH * (Dk / 64))), dim3(256), 0, st, dfT, finC,
-                               fterm, Dk, Dv);
-            if ((e = hipGetLastError()) != hipSuccess) return e;
-        }
+        if (dfT && (e = fterm_of()) != hipSuccess) return e;
         const dim3 grid_g((unsigned)((size_t)BH * (Dk / 64) * ((nseg + 3) / 4)));
         hipLaunchKernelGGL(chan_g_kernel, grid_g, dim3(256), 0, st, d, dfT ? fterm : nullptr, g, part, nseg);
         if ((e = hipGetLastError()) != hipSuccess) return e;
