@@ -1133,6 +1133,9 @@ hipError_t launch_pass(const ChanPass &p, int BH, int Dq, hipStream_t st) {
 // three (one round of 768; 512, 1024, 1536 and 2048 measured slower).
 constexpr int kChanTargetWorkgroups = 1024;
 constexpr int kVg16TargetWorkgroups = 768;
+// The dk pass that also forms the log-gate gradient holds two workgroups per unit (its
+// registers): one round of 512 (768 and 1,024 measured slower).
+constexpr int kVg16GateTargetWorkgroups = 512;
 void chan_segments(int BH, int L, int Dn, int target, int *nseg, int *seg_len) {
     const long long tiles = (long long)BH * (Dn / 64);
     long long want = (target + tiles - 1) / tiles;
@@ -1240,6 +1243,7 @@ hipError_t chan_backward(const gla_bwd_desc &d, const float *s0T, const float *d
         // the reversed dk pass forms the log-gate gradient: dq and the final-state term first
         if ((e = dq_pass()) != hipSuccess) return e;
         if (dfT && (e = fterm_of()) != hipSuccess) return e;
+        segs(Dk, Dv, kVg16GateTargetWorkgroups);
         if ((e = dk_pass(true)) != hipSuccess) return e;
         if (p.nseg > 1) {
             const int chunks = (p.seg_len + 63) / 64;
