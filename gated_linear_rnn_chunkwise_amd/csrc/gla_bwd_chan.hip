@@ -16,9 +16,14 @@
 // and across sequence segments.  Reversal, the input gate of the values and the output row
 // mapping are index arithmetic on the caller's tensors, so the passes need no operand copies.
 //
+// With bf16 inputs the value-gated passes run on fp16 operands (chan_vg16_kernel), and fp32
+// inputs keep them in chan_pass_kernel.
+//
 // The per-channel log-gate gradient is the reverse running sum over tokens of
-// q_t,d dq_t,d - k_t,d dk_t,d, plus sum_j dfinal[d][j] S_fin[d][j] at the last token
-// (chan_g_kernel and chan_scan_kernel: 64-token segments, then carries).
+// q_t,d dq_t,d - k_t,d dk_t,d, plus sum_j dfinal[d][j] S_fin[d][j] at the last token.  On the
+// fp16 path the reversed dk pass forms it in pass order (after the dq pass), and
+// chan_gfix_kernel adds the earlier segments' totals; on the fp32 path chan_g_kernel and
+// chan_scan_kernel form it afterwards (64-token segments, then carries).
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
