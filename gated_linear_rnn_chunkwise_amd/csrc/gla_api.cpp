@@ -30,7 +30,7 @@ hipError_t bwd_scale(const float *src, const uint32_t *mx, float *dst, int BH, s
 hipError_t bwd_finish(const gla_bwd_desc &d, const float *oA, const float *oB, float *g, const float *finA,
                       const float *finC, const float *dfT, float *part, const uint32_t *mx, hipStream_t st);
 constexpr int kH16Q = 1, kH16K = 2, kH16V = 4;  // fp16 operand bits of launch_forward
-size_t chan_scratch_floats(int BH, int L, int Dk, int Dv);
+size_t chan_scratch_floats(int BH, int L, int Dk, int Dv, bool g_rows);
 hipError_t chan_backward(const gla_bwd_desc &d, const float *s0T, const float *dfT, float *finA, float *finC,
                          float *scratch, bool skip_dv, const _Float16 *fdo, const uint32_t *mx, hipStream_t st);
 }
@@ -395,7 +395,7 @@ int bwd_plan(const gla_bwd_desc *d, BwdPlan *p) {
         p->finC = take(bh * Dk * Dv * 4);
         p->s0T = d->initial_state ? take(bh * Dk * Dv * 4) : 0;
         p->dfT = d->dfinal_state ? take(bh * Dk * Dv * 4) : 0;
-        p->chs = take(gla::chan_scratch_floats(d->B * d->H, d->L, d->Dk, d->Dv) * 4);
+        p->chs = take(gla::chan_scratch_floats(d->B * d->H, d->L, d->Dk, d->Dv, !bf) * 4);
         p->fws_bytes = 0;
         if (bf) {
             p->fdo = take(bh * L * Dv * 2);

@@ -1152,11 +1152,12 @@ void chan_segments(int BH, int L, int Dn, int target, int *nseg, int *seg_len) {
     *nseg = (int)(((long long)L + len - 1) / len);
 }
 
-// Scratch floats of the per-channel path beyond the transposed states: the g rows and the
-// segment totals of the log-gate scan, and the segment states and decays of the passes.
-size_t chan_scratch_floats(int BH, int L, int Dk, int Dv) {
+// Scratch floats of the per-channel path beyond the transposed states: the g rows (g_rows:
+// fp32 inputs) and the segment totals of the log-gate gradient, the final-state term, and the
+// segment states and decays of the passes.
+size_t chan_scratch_floats(int BH, int L, int Dk, int Dv, bool g_rows) {
     const size_t ns = ((size_t)L + kSeg - 1) / kSeg;
-    size_t n = (size_t)BH * L * Dk + (size_t)BH * ns * Dk + (size_t)BH * Dk;
+    size_t n = (g_rows ? (size_t)BH * L * Dk : 0) + (size_t)BH * ns * Dk + (size_t)BH * Dk;
     int s1, l1, s2, l2;
     chan_segments(BH, L, Dv, kChanTargetWorkgroups, &s1, &l1);  // the key-gated pass (value dimension Dv)
     chan_segments(BH, L, Dk, kChanTargetWorkgroups, &s2, &l2);  // the value-gated passes (value dimension Dk)
@@ -1180,8 +1181,9 @@ hipError_t chan_backward(const gla_bwd_desc &d, const float *s0T, const float *d
     const int BH = d.B * d.H, L = d.L, Dk = d.Dk, Dv = d.Dv, dt = d.in_dtype;
     hipError_t e;
     const int nsg = (L + kSeg - 1) / kSeg;
+    // the log-gate rows exist only where chan_g_kernel forms them (fp32 inputs)
     float *g_rows = scratch;
-    float *part = g_rows + (size_t)BH * L * Dk;
+    float *part = g_rows + (mx ? 0 : (size_t)BH * L * Dk);
     float *fterm = part + (size_t)BH * nsg * Dk;
     float *seg_ws = fterm + (size_t)BH * Dk;
     ChanPass p{};
