@@ -227,7 +227,7 @@ __global__ __launch_bounds__(256, 2) void chan_pass_kernel(ChanPass a) {
 #pragma unroll
             for (int i = 0; i < NQ; ++i) {
                 const bool ok = uq + i * RS < ue;
-                fq[i] = ld_raw<QF>(rq, ok ? (uint32_t)(bq + i * sq) : kOff);
+                if constexpr (!ST) fq[i] = ld_raw<QF>(rq, ok ? (uint32_t)(bq + i * sq) : kOff);  // no q: states only
                 fk[i] = ld_raw<KF>(rk, ok ? (uint32_t)(bk + i * sk) : kOff);
             }
         }
@@ -268,7 +268,7 @@ __global__ __launch_bounds__(256, 2) void chan_pass_kernel(ChanPass a) {
 #pragma unroll
         for (int i = 0; i < NQ; ++i) {
             const int idx = tid + i * 256, t = idx / DQ, d = idx % DQ;
-            sQ[t * QP + d] = raw_val<QF>(fq[i]);
+            if constexpr (!ST) sQ[t * QP + d] = raw_val<QF>(fq[i]);
             const float kv = raw_val<KF>(fk[i]);
             sKX[t * QP + d] = kv;
             if constexpr (!KG) sKT[d * TP + t] = kv;
@@ -334,7 +334,7 @@ __global__ __launch_bounds__(256, 2) void chan_pass_kernel(ChanPass a) {
                 const int t = idx / DQ, d = idx % DQ;
                 const float bt = sB[t * QP + d], b15 = sB[(kBlk - 1) * QP + d];
                 const float kv = sKX[t * QP + d];
-                sQ[t * QP + d] *= fexp2c(bt);             // q_t 2^(b_t)
+                if constexpr (!ST) sQ[t * QP + d] *= fexp2c(bt);  // q_t 2^(b_t)
                 sKT[d * TP + t] = kv * fexp2c(b15 - bt);  // k_t 2^(b_15 - b_t)
                 sKX[t * QP + d] = kv * fexp2c(-bt);       // k_t 2^(-b_t), for the scores
             }
@@ -672,7 +672,7 @@ __global__ __launch_bounds__(256, 2) void chan_vg16_kernel(ChanPass a) {
             const int u = u0 + NR * rq0 + i;
             const uint32_t oq = (row_of(a.qrev, u) * (uint32_t)DQ + 4u * gq) * 2u;
             const uint32_t ok_ = (row_of(a.krev, u) * (uint32_t)DQ + 4u * gq) * 2u;
-            fq[i] = __builtin_amdgcn_raw_buffer_load_b64(rq, (int)oq, 0, 0);
+            if constexpr (!ST) fq[i] = __builtin_amdgcn_raw_buffer_load_b64(rq, (int)oq, 0, 0);  // no q: states only
             fk[i] = __builtin_amdgcn_raw_buffer_load_b64(rk, (int)ok_, 0, 0);
         }
 #pragma unroll
@@ -699,7 +699,7 @@ __global__ __launch_bounds__(256, 2) void chan_vg16_kernel(ChanPass a) {
 #pragma unroll
         for (int i = 0; i < NR; ++i) {
             const int t = NR * rq0 + i;
-            *reinterpret_cast<h16x4c *>(sQ + t * QH + 4 * gq) = to_h4<QH16>(fq[i]);
+            if constexpr (!ST) *reinterpret_cast<h16x4c *>(sQ + t * QH + 4 * gq) = to_h4<QH16>(fq[i]);
             kh[i] = to_h4<KH16>(fk[i]);
             *reinterpret_cast<h16x4c *>(sK + t * QH + 4 * gq) = kh[i];
         }
