@@ -213,6 +213,19 @@ def test_backward_per_channel_strong_decay(gpu_lib):
     check_all(got, ref, "per-channel strong decay", "bf16", d, "channel")
 
 
+@pytest.mark.parametrize("ig", [False, True])
+def test_backward_per_channel_many_segments(gpu_lib, ig):
+    # few (batch, head) slices at length 2048: the value-gated passes split the sequence into
+    # dozens of 64-token segments (state kernels, segment scans, and the log-gate gradient's
+    # segment totals joined afterwards); initial state and final-state gradient given
+    w = gin.custom(2, 2, 2048, 128, 128, 64, dtype="bf16", gate="channel", input_gate=ig)
+    d = gin.make_inputs(w, seed=21 + ig)
+    dout, s0, df = grads_in(w, 22, True, True)
+    got = run(gpu_lib, w, d, dout, s0, df)
+    ref = oracle.backward(d["q"], d["k"], d["v"], dout, "channel", d["log_alpha"], d["log_ig"], s0, df)
+    check_all(got, ref, "per-channel, many segments", "bf16", d, "channel")
+
+
 def test_backward_headline_workload_sampled_heads(gpu_lib):
     # the per-channel GLA workload at full size (the launch bench.py --backward times); three
     # sampled (batch, head) slices against the oracle's gradients of those slices
