@@ -270,7 +270,7 @@ __global__ __launch_bounds__(256, 2) void chan_pass_kernel(ChanPass a) {
             const int idx = tid + i * 256, t = idx / DQ, d = idx % DQ;
             if constexpr (!ST) sQ[t * QP + d] = raw_val<QF>(fq[i]);
             const float kv = raw_val<KF>(fk[i]);
-            sKX[t * QP + d] = kv;
+            if constexpr (KG || !ST) sKX[t * QP + d] = kv;  // value-gate states use k^T only
             if constexpr (!KG) sKT[d * TP + t] = kv;
         }
         f32x4c vr;
@@ -701,7 +701,7 @@ __global__ __launch_bounds__(256, 2) void chan_vg16_kernel(ChanPass a) {
             const int t = NR * rq0 + i;
             if constexpr (!ST) *reinterpret_cast<h16x4c *>(sQ + t * QH + 4 * gq) = to_h4<QH16>(fq[i]);
             kh[i] = to_h4<KH16>(fk[i]);
-            *reinterpret_cast<h16x4c *>(sK + t * QH + 4 * gq) = kh[i];
+            if constexpr (!ST) *reinterpret_cast<h16x4c *>(sK + t * QH + 4 * gq) = kh[i];  // states use k^T only
         }
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
