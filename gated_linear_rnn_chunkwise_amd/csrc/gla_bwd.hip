@@ -153,15 +153,25 @@ __global__ __launch_bounds__(256) void bwd_gate_kernel(const float *la, int kind
 }
 
 // [BH][R][C] -> [BH][C][R], times the slice's scale when mx is given.
+// One 64 x 64 tile per workgroup through LDS (rows read and written whole); R and C are
+// multiples of 64.
 __global__ __launch_bounds__(256) void bwd_transpose_kernel(const float *src, const uint32_t *mx, float *dst, int R,
-                                                           int C, size_t total) {
-    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= total) return;
+                                                           int C) {
+    __shared__ float tile[64][65];
+    const int tr = R / 64, tc = C / 64;
+    size_t id = blockIdx.x;
+    const int bc = (int)(id % (unsigned)tc);
+    id /= (unsigned)tc;
+    const int br = (int)(id % (unsigned)tr);
+    const size_t bh = id / (unsigned)tr;
+    const float sc = mx ? scale_of(mx[bh]) : 1.f;
     const size_t m = (size_t)R * C;
-    const size_t bh = i / m;
-    const size_t rc = i % m;
-    const int r = (int)(rc / C), c = (int)(rc % C);
-    dst[bh * m + (size_t)c * R + r] = mx ? src[i] * scale_of(mx[bh]) : src[i];
+    const float *s = src + bh * m;
+    float *o = dst + bh * m;
+    const int x = (int)threadIdx.x & 63, y0 = (int)threadIdx.x >> 6;
+    for (int y = y0; y < 64; y += 4) tile[y][x] = s[(size_t)(br * 64 + y) * C + bc * 64 + x] * sc;
+    __syncthreads();
+    for (int y = y0; y < 64; y += 4) o[(size_t)(bc * 64 + y) * R + br * 64 + x] = tile[x][y];
 }
 
 // One wave per token: dk_t = i_t oB[L-1-t], dv_t = i_t oA[L-1-t]; g_t = q_t . dq_t - k_t . dk_t;
@@ -348,8 +358,8 @@ hipError_t bwd_gate(const float *la, int kind, float *dst, int BH, int H, int L,
 }
 
 hipError_t bwd_transpose(const float *src, const uint32_t *mx, float *dst, int BH, int R, int C, hipStream_t st) {
-    const size_t total = (size_t)BH * R * C;
-    hipLaunchKernelGGL(bwd_transpose_kernel, dim3(nblk(total, 256)), dim3(256), 0, st, src, mx, dst, R, C, total);
+    const size_t tiles = (size_t)BH * (R / 64) * (C / 64);
+    hipLaunchKernelGGL(bwd_transpose_kernel, dim3((unsigned)tiles), dim3(256), 0, st, src, mx, dst, R, C);
     return hipGetLastError();
 }
 
