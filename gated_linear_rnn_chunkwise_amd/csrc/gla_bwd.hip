@@ -319,17 +319,22 @@ __global__ __launch_bounds__(256) void bwd_gate_reduce_kernel(gla_bwd_desc d, co
 
 // dinitial_state = diag(alpha_0) G_0: the first pass's final state times the first token's
 // decay (and 1/s when finA carries the scale).
+// Workgroup = 1,024 consecutive elements (four per thread) of one (batch, head) slice of
+// m = Dk * Dv elements, a multiple of 4,096.
 __global__ __launch_bounds__(256) void bwd_dinit_kernel(gla_bwd_desc d, const float *finA, const uint32_t *mx,
-                                                       size_t m, size_t total) {
-    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= total) return;
-    const size_t bh = i / m;
+                                                       int m) {
+    const unsigned nb = (unsigned)m / 1024u;
+    const size_t bh = blockIdx.x / nb;
+    const int e = (int)(blockIdx.x % nb) * 1024 + 4 * (int)threadIdx.x;  // element within the slice
     float a0 = mx ? 1.f / scale_of(mx[bh]) : 1.f;
     if (d.gate_kind == GLA_GATE_HEAD) a0 *= exp2f(d.log_alpha[bh * d.L] * kLog2eB);
     else if (d.gate_kind == GLA_GATE_HEAD_CONST) a0 *= exp2f(d.log_alpha[bh % d.H] * kLog2eB);
     else if (d.gate_kind == GLA_GATE_CHANNEL)  // row r of G_0 decays with channel r of token 0
-        a0 *= exp2f(d.log_alpha[bh * d.L * d.Dk + (i % m) / d.Dv] * kLog2eB);
-    d.dinitial_state[i] = a0 * finA[i];
+        a0 *= exp2f(d.log_alpha[bh * d.L * d.Dk + e / d.Dv] * kLog2eB);
+    const size_t i = bh * (size_t)m + e;
+    float4 x = *reinterpret_cast<const float4 *>(finA + i);
+    x.x *= a0, x.y *= a0, x.z *= a0, x.w *= a0;
+    *reinterpret_cast<float4 *>(d.dinitial_state + i) = x;
 }
 
 // Fixed per-head gate: dlog_alpha[h] = sum over the batch of the per-(b, h) totals.
@@ -416,8 +421,8 @@ hipError_t bwd_finish(const gla_bwd_desc &d, const float *oA, const float *oB, f
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     if (d.dinitial_state) {
-        const size_t total = (size_t)BH * m;
-        hipLaunchKernelGGL(bwd_dinit_kernel, dim3(nblk(total, 256)), dim3(256), 0, st, d, finA, mx, m, total);
+        hipLaunchKernelGGL(bwd_dinit_kernel, dim3((unsigned)((size_t)BH * (m / 1024))), dim3(256), 0, st, d, finA, mx,
+                           (int)m);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     if (g && d.gate_kind == GLA_GATE_HEAD_CONST) {
