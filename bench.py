@@ -10,10 +10,14 @@ synchronisations.  Two input sets alternate between steps so successive steps do
 re-read the same bytes from the 256 MB last-level cache.  Prints one JSON line.
 
 Reported beside the throughput:
-* ``roofline`` of the dominant kernel: algorithmic bytes per launch over the mean launch
-  duration (HIP events recorded on the stream the kernels run on), against the 8 TB/s
-  HBM peak; ``traffic`` is the measured HBM traffic of that kernel from rocprofv3
+* ``roofline`` of the dominant kernel: the I/O floor (inputs and gates read once, fp32
+  output and final state written once) over the mean launch duration (HIP events recorded
+  on the stream the kernels run on; the median and the minimum beside it), against the
+  8 TB/s HBM peak.  Bytes moved beyond the floor (segment states, second reads) are ``extra_bytes``
+  and not credited.  ``traffic`` is the measured HBM traffic of that kernel from rocprofv3
   counters (profiles/), or null when the counters were taken on other kernel source.
+* ``tflops`` counts the flops as executed (a chunk of more than 64 tokens runs as 64-token
+  chunks unless the tile-pair form is selected).
 * ``cpu_baseline``: the fp64 oracle (the plain token recurrence) timed on this host's
   cores on the same workload, converted to the same unit.
 """
@@ -41,10 +45,30 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def algorithmic_flops(w) -> float:
+def algorithmic_flops(w, chunk=None) -> float:
     """Inter-chunk products (K^T V and Q S: 4 Dk Dv per head-token) plus the causal
-    intra-chunk score and value products ((C+1)(Dk+Dv) per head-token on average)."""
-    return float(w.B * w.H * w.L) * (4.0 * w.Dk * w.Dv + (w.chunk + 1) * (w.Dk + w.Dv))
+    intra-chunk score and value products ((C+1)(Dk+Dv) per head-token on average) for chunks
+    of ``chunk`` tokens (default: the workload's)."""
+    c = w.chunk if chunk is None else chunk
+    return float(w.B * w.H * w.L) * (4.0 * w.Dk * w.Dv + (c + 1) * (w.Dk + w.Dv))
+
+
+def host_cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+
+    return platform.processor() or "unknown"
+
+
+def quantiles(xs):
+    xs = sorted(xs)
+    return xs[len(xs) // 2], xs[0]
 
 
 def io_floor_bytes(w) -> float:
@@ -121,6 +145,8 @@ def cpu_baseline(w, d, budget_s: float = 20.0) -> dict:
         "value": tokens_per_s,
         "unit": "tokens/s",
         "cores": threads,
+        "host_cpu": host_cpu_model(),
+        "host_logical_cpus": os.cpu_count(),
         "kind": "oracle",
         "sample": "%d of %d (batch, head) pairs at full length %d, %d repetition(s), fp64 token recurrence, "
                   "%.2f s" % (nheads, BH, w.L, reps, t),
@@ -412,32 +438,45 @@ def main():
     launch_ms = [a.elapsed_time(b) for a, b in ev]
     mean_launch_ms = sum(launch_ms) / K
 
+    med_launch_ms, min_launch_ms = quantiles(launch_ms)
+
     tokens = w.B * w.L
     value = tokens / (ms_per_step * 1e-3)
-    flops = algorithmic_flops(w)
+    # flops as executed: without tile pairs a chunk of more than 64 tokens is computed as
+    # 64-token chunks (the state advances per tile), so its intra-chunk work is that of C = 64
+    exec_chunk = w.chunk if plan.tile_pairs else min(w.chunk, 64)
+    flops = algorithmic_flops(w, exec_chunk)
     io = io_floor_bytes(w)
     tflops = flops / (ms_per_step * 1e-3) / 1e12
 
-    # Dominant kernel: the chunk-output kernel.  With one segment it is the only launch of
-    # a step, so the events around the call time exactly that kernel.  With several
-    # segments the step also runs the segment-state kernel (k, v and gates of all but the
-    # last segment in, one fp32 state and decay per segment boundary out) and the scan
-    # (boundary states in and out); the roofline then covers the whole step.
+    # Roofline against the I/O floor: q, k, v and the gates read once, the fp32 output and
+    # final state written once.  With one segment the chunk-output kernel is the only launch
+    # of a step, so the events around the call time exactly that kernel.  With several
+    # segments the events time the whole step (segment-state, segment-scan and chunk-output
+    # kernels); the bytes those extra kernels move beyond the floor (the segment-state
+    # kernel's second read of k, v and gates, the boundary states written and read) are
+    # reported as ``extra_bytes`` and not credited.
+    ib = 4 if w.dtype == "f32" else 2
+    gate = {"channel": 4 * w.Dk, "head": 4, "head_const": 0, "none": 0}[w.gate] + (4 if w.input_gate else 0)
     if plan.n_seg == 1:
-        kbytes = io
+        extra = 0.0
         scope = "chunk-output kernel (the only launch of a step)"
     else:
-        ib = 4 if w.dtype == "f32" else 2
-        gate = {"channel": 4 * w.Dk, "head": 4, "head_const": 0, "none": 0}[w.gate] + (4 if w.input_gate else 0)
-        bnd = w.B * w.H * (plan.n_seg - 1)
-        kbytes = io + 4.0 * bnd * (w.Dk * w.Dv + w.Dk) * 4 \
-            + float(w.B * w.H * w.L) * (plan.n_seg - 1) / plan.n_seg * (ib * (w.Dk + w.Dv) + gate)
-        scope = "step (segment-state, segment-scan and chunk-output kernels)"
-    achieved = kbytes / (mean_launch_ms * 1e-3) / 1e9
+        # sub-segment states per slice: written by the state kernel and read by the scan, which
+        # writes one state per segment boundary that the chunk-output kernel reads
+        nss = plan.grid_state // max(1, w.B * w.H * plan.dv_tiles)
+        extra = float(w.B * w.H * w.L) * (plan.n_seg - 1) / plan.n_seg * (ib * (w.Dk + w.Dv) + gate) \
+            + float(w.B * w.H) * (2 * nss + 2 * (plan.n_seg - 1)) * (w.Dk * w.Dv + w.Dk) * 4
+        scope = "whole step (segment-state, segment-scan and chunk-output kernels)"
+    achieved = io / (mean_launch_ms * 1e-3) / 1e9
     traffic = measured_traffic(wname) if plan.n_seg == 1 else None
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic, "kernel": scope,
-            "algorithmic_bytes_per_launch": kbytes, "mean_launch_ms": round(mean_launch_ms, 5)}
+            "algorithmic_bytes_per_launch": io, "extra_bytes": extra,
+            "median_launch_ms": round(med_launch_ms, 5), "min_launch_ms": round(min_launch_ms, 5),
+            "mean_launch_ms": round(mean_launch_ms, 5),
+            "frac_at_median_launch": round(io / (med_launch_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "frac_at_min_launch": round(io / (min_launch_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -465,6 +504,8 @@ def main():
                    "workgroups": plan.grid_out},
         "head_tokens_per_s": value * w.H,
         "tflops": round(tflops, 2),
+        "tflops_counts": "flops executed: chunk %d%s" % (exec_chunk, "" if exec_chunk == w.chunk else
+                                                       " (chunk %d runs as 64-token chunks)" % w.chunk),
         "pct_bf16_mfma_peak": round(100.0 * tflops / BF16_MFMA_PEAK_TFLOPS, 2),
         "io_floor_gbps": round(io / (ms_per_step * 1e-3) / 1e9, 1),
         "pct_hbm_peak_io_floor": round(100.0 * io / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),

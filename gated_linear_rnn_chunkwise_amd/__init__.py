@@ -175,6 +175,30 @@ def make_desc(q, k, v, log_alpha=None, log_ig=None, initial_state=None, out=None
     return d
 
 
+def _check_shape(t, shape, name):
+    """Raise ValueError unless tensor ``t`` (or None) has exactly ``shape``."""
+    if t is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+
+
+def _check_fwd_shapes(q, k, v, log_alpha, log_ig, initial_state, out, fin):
+    """Every tensor of a forward call against the sizes taken from q and v.  The kernels size
+    their memory ranges from these sizes, so a shorter tensor would be read or written past
+    its end."""
+    if q.dim() != 4 or v.dim() != 4:
+        raise ValueError("q and v must be [B, H, L, D]")
+    B, H, L, Dk = q.shape
+    Dv = v.shape[-1]
+    _check_shape(k, (B, H, L, Dk), "k")
+    _check_shape(v, (B, H, L, Dv), "v")
+    if log_alpha is not None:
+        gate_kind_of(log_alpha, B, H, L, Dk)  # raises when no gate layout matches
+    _check_shape(log_ig, (B, H, L), "log_ig")
+    _check_shape(initial_state, (B, H, Dk, Dv), "initial_state")
+    _check_shape(out, (B, H, L, Dv), "out")
+    _check_shape(fin, (B, H, Dk, Dv), "final_state")
+
+
 def _check_tensors(q, k, v, *others):
     import torch
 
@@ -201,6 +225,7 @@ def fwd(q, k, v, log_alpha=None, *, log_ig=None, initial_state=None, chunk: int 
     lib = load()
     B, H, L, Dk = q.shape
     Dv = v.shape[-1]
+    _check_fwd_shapes(q, k, v, log_alpha, log_ig, initial_state, out, None)
     if out is None:
         out = torch.empty((B, H, L, Dv), dtype=torch.float32, device=q.device)
     fin = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=q.device) if final_state else None
@@ -252,8 +277,11 @@ def bwd(q, k, v, dout, log_alpha=None, *, log_ig=None, initial_state=None, dfina
     import torch
 
     lib = load()
+    _check_fwd_shapes(q, k, v, log_alpha, log_ig, initial_state, None, None)
     B, H, L, Dk = q.shape
     Dv = v.shape[-1]
+    _check_shape(dout, (B, H, L, Dv), "dout")
+    _check_shape(dfinal_state, (B, H, Dk, Dv), "dfinal_state")
     f = dict(dtype=torch.float32, device=q.device)
     dq, dk, dv = torch.empty((B, H, L, Dk), **f), torch.empty((B, H, L, Dk), **f), torch.empty((B, H, L, Dv), **f)
     dla = torch.empty(log_alpha.shape, **f) if log_alpha is not None else None
@@ -272,6 +300,12 @@ def fwd_headline(q, k, v, log_alpha, out, final_state, chunk: int = 64, stream=N
     """The 13-argument entry point ``gla_fwd`` (bf16 inputs, per-channel gate or None); returns the status."""
     import torch
 
+    if log_alpha is not None and log_alpha.dim() != 4:
+        raise ValueError("gla_fwd takes a per-channel log_alpha [B, H, L, Dk] or None")
+    _check_fwd_shapes(q, k, v, log_alpha, None, None, out, final_state)
+    _check_tensors(q, k, v, log_alpha, out, final_state)
+    if q.dtype != torch.bfloat16:
+        raise TypeError("gla_fwd takes bf16 q, k, v")
     B, H, L, Dk = q.shape
     Dv = v.shape[-1]
     s = stream if stream is not None else torch.cuda.current_stream(q.device)
@@ -319,8 +353,16 @@ def step(q, k, v, state, log_alpha=None, *, log_ig=None, out=None, stream=None):
     import torch
 
     lib = load()
+    if q.dim() != 3 or v.dim() != 3:
+        raise ValueError("q and v must be [B, H, D]")
     B, H, Dk = q.shape
     Dv = v.shape[-1]
+    _check_shape(k, (B, H, Dk), "k")
+    if log_alpha is not None:
+        step_gate_kind_of(log_alpha, B, H, Dk)
+    _check_shape(log_ig, (B, H), "log_ig")
+    _check_shape(state, (B, H, Dk, Dv), "state")
+    _check_shape(out, (B, H, Dv), "out")
     if out is None:
         out = torch.empty((B, H, Dv), dtype=torch.float32, device=q.device)
     _check_tensors(q, k, v, log_alpha, log_ig, state, out)

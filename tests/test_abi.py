@@ -282,3 +282,66 @@ def test_bwd_rejects_small_workspace_before_launching(lib):
     st, need = bstatus(lib, bdesc())
     d = bdesc(workspace=A, workspace_bytes=need - 256)
     assert lib.gla_bwd(ctypes.byref(d), None) == gla.GLA_ERR_WORKSPACE
+
+
+# ------------------------------------------------------------------------------ binding shape checks
+def _cpu_fwd_args(B=2, H=3, L=10, Dk=64, Dv=64):
+    import torch
+
+    f = torch.float32
+    return dict(q=torch.zeros(B, H, L, Dk, dtype=torch.bfloat16), k=torch.zeros(B, H, L, Dk, dtype=torch.bfloat16),
+                v=torch.zeros(B, H, L, Dv, dtype=torch.bfloat16), log_alpha=torch.zeros(B, H, L, Dk, dtype=f),
+                log_ig=torch.zeros(B, H, L, dtype=f), initial_state=torch.zeros(B, H, Dk, Dv, dtype=f),
+                out=torch.zeros(B, H, L, Dv, dtype=f))
+
+
+@pytest.mark.parametrize("name,shape", [("k", (2, 3, 9, 64)), ("k", (2, 3, 10, 32)), ("v", (2, 3, 9, 64)),
+                                        ("log_alpha", (2, 3, 10, 32)), ("log_alpha", (2, 3, 9)),
+                                        ("log_ig", (2, 3, 9)), ("initial_state", (2, 3, 64, 32)),
+                                        ("out", (2, 3, 10, 32))])
+def test_fwd_rejects_mismatched_shapes_before_device_work(lib, name, shape):
+    # the kernels size their memory ranges from q and v: any other tensor of the wrong shape
+    # is refused on the host (these CPU tensors would otherwise fail the device check later)
+    import torch
+
+    a = _cpu_fwd_args()
+    a[name] = torch.zeros(shape, dtype=a[name].dtype)
+    with pytest.raises(ValueError, match=name if name != "log_alpha" else "log_alpha"):
+        gla.fwd(a["q"], a["k"], a["v"], a["log_alpha"], log_ig=a["log_ig"], initial_state=a["initial_state"],
+                out=a["out"])
+
+
+@pytest.mark.parametrize("name,shape", [("dout", (2, 3, 9, 64)), ("dfinal_state", (2, 3, 64, 63)),
+                                        ("k", (1, 3, 10, 64)), ("log_ig", (2, 3, 11))])
+def test_bwd_rejects_mismatched_shapes_before_device_work(lib, name, shape):
+    import torch
+
+    a = _cpu_fwd_args()
+    a["dout"] = torch.zeros(2, 3, 10, 64)
+    a["dfinal_state"] = torch.zeros(2, 3, 64, 64)
+    a[name] = torch.zeros(shape, dtype=a[name].dtype)
+    with pytest.raises(ValueError, match=name):
+        gla.bwd(a["q"], a["k"], a["v"], a["dout"], a["log_alpha"], log_ig=a["log_ig"],
+                initial_state=a["initial_state"], dfinal_state=a["dfinal_state"])
+
+
+@pytest.mark.parametrize("name,shape", [("k", (2, 3, 32)), ("state", (2, 3, 64, 32)), ("out", (2, 3, 32)),
+                                        ("log_ig", (2, 2)), ("log_alpha", (2, 3, 63))])
+def test_step_rejects_mismatched_shapes_before_device_work(lib, name, shape):
+    import torch
+
+    f = torch.float32
+    a = dict(q=torch.zeros(2, 3, 64), k=torch.zeros(2, 3, 64), v=torch.zeros(2, 3, 64),
+             state=torch.zeros(2, 3, 64, 64), out=torch.zeros(2, 3, 64), log_ig=torch.zeros(2, 3),
+             log_alpha=torch.zeros(2, 3, 64, dtype=f))
+    a[name] = torch.zeros(shape, dtype=f)
+    with pytest.raises(ValueError, match=name if name != "log_alpha" else "log_alpha"):
+        gla.step(a["q"], a["k"], a["v"], a["state"], a["log_alpha"], log_ig=a["log_ig"], out=a["out"])
+
+
+def test_headline_binding_rejects_mismatched_shapes(lib):
+    import torch
+
+    a = _cpu_fwd_args()
+    with pytest.raises(ValueError, match="out"):
+        gla.fwd_headline(a["q"], a["k"], a["v"], a["log_alpha"], torch.zeros(2, 3, 10, 32), None)
