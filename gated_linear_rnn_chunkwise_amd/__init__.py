@@ -29,8 +29,9 @@ FLAG_TILE_PAIRS = 1
 GATE_NAMES = {"none": GATE_NONE, "channel": GATE_CHANNEL, "head": GATE_HEAD, "head_const": GATE_HEAD_CONST}
 
 # Entry points declared in include/gla.h.
-EXPORTS = ("gla_fwd", "gla_fwd_ex", "gla_workspace_size", "gla_query_plan", "gla_step", "gla_bwd",
-           "gla_bwd_workspace_size", "gla_status_string", "gla_version")
+EXPORTS = ("gla_fwd", "gla_fwd_ex", "gla_fwd_noalloc", "gla_workspace_size", "gla_query_plan", "gla_step",
+           "gla_bwd", "gla_bwd_workspace_size", "gla_status_string", "gla_version")
+NOALLOC_SCRATCH_BYTES = 32 << 20  # GLA_NOALLOC_SCRATCH_BYTES
 
 
 class GlaDesc(ctypes.Structure):
@@ -102,6 +103,8 @@ def load(path: str = LIB_PATH):
         lib.gla_fwd.restype = i32
         lib.gla_fwd_ex.argtypes = [ctypes.POINTER(GlaDesc), vp]
         lib.gla_fwd_ex.restype = i32
+        lib.gla_fwd_noalloc.argtypes = [ctypes.POINTER(GlaDesc), vp]
+        lib.gla_fwd_noalloc.restype = i32
         lib.gla_workspace_size.argtypes = [ctypes.POINTER(GlaDesc), ctypes.POINTER(ctypes.c_size_t)]
         lib.gla_workspace_size.restype = i32
         lib.gla_query_plan.argtypes = [ctypes.POINTER(GlaDesc), ctypes.POINTER(GlaPlan)]
@@ -238,6 +241,30 @@ def fwd(q, k, v, log_alpha=None, *, log_ig=None, initial_state=None, chunk: int 
     if st != GLA_OK:
         raise GlaError(st, "gla_fwd_ex")
     return out, fin
+
+
+def fwd_noalloc(q, k, v, log_alpha=None, *, log_ig=None, initial_state=None, chunk: int = 64, out=None,
+                final_state=None, seg_chunks: int = 0, stream=None, tile_pairs: bool = False):
+    """The forward pass through ``gla_fwd_noalloc``: no device memory is allocated by the
+    library (its scratch is a fixed per-GPU array).  ``out`` and ``final_state`` (or None)
+    are caller tensors, so nothing at all is allocated when both are given.  Returns
+    ``(out, final_state)``."""
+    import torch
+
+    lib = load()
+    _check_fwd_shapes(q, k, v, log_alpha, log_ig, initial_state, out, final_state)
+    B, H, L, Dk = q.shape
+    Dv = v.shape[-1]
+    if out is None:
+        out = torch.empty((B, H, L, Dv), dtype=torch.float32, device=q.device)
+    _check_tensors(q, k, v, log_alpha, log_ig, initial_state, out, final_state)
+    d = make_desc(q, k, v, log_alpha, log_ig, initial_state, out, final_state, chunk, seg_chunks, None, 0,
+                  tile_pairs=tile_pairs)
+    s = stream if stream is not None else torch.cuda.current_stream(q.device)
+    st = lib.gla_fwd_noalloc(ctypes.byref(d), ctypes.c_void_p(s.cuda_stream))
+    if st != GLA_OK:
+        raise GlaError(st, "gla_fwd_noalloc")
+    return out, final_state
 
 
 def make_bwd_desc(q, k, v, dout, dq, dk, dv, log_alpha=None, log_ig=None, initial_state=None, dfinal_state=None,

@@ -13,6 +13,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "gla.h"
 #include "gla_layout.h"
@@ -265,9 +266,62 @@ int fwd_run(const gla_desc *d, int h16, void *stream, const OutMapArgs &om = Out
 
 }  // namespace
 
+// ------------------------------------------------------------------------------------
+// Scratch of gla_fwd_noalloc: a device array built into the library.  Each GPU holds its own
+// copy at its own address, resolved once per device with that device current.  In host code
+// `scratch` names a host-side stand-in, never the device memory: only the resolved address
+// is ever passed to a kernel.
+namespace {
+
+static __device__ __align__(256) unsigned char scratch[GLA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_addr[kMaxDevices];  // per device; nullptr until resolved (guarded by g_scratch_mu)
+
+// Address of the current device's copy of `scratch`.
+int scratch_address(void **out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return GLA_ERR_HIP;
+    }
+    if (dev < 0 || dev >= kMaxDevices) return GLA_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_addr[dev]) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+            (void)hipGetLastError();
+            return GLA_ERR_HIP;
+        }
+        g_scratch_addr[dev] = ptr;
+    }
+    *out = g_scratch_addr[dev];
+    return GLA_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 int gla_fwd_ex(const gla_desc *d, void *stream) { return fwd_run(d, 0, stream); }
+
+int gla_fwd_noalloc(const gla_desc *d, void *stream) {
+    Plan p;
+    int st = checked_plan(d, &p);
+    if (st != GLA_OK) return st;
+    if (d->workspace != nullptr || d->workspace_bytes != 0) return GLA_ERR_INVALID_ARG;
+    if (p.ws_bytes > size_t(GLA_NOALLOC_SCRATCH_BYTES)) return GLA_ERR_WORKSPACE;
+    gla_desc f = *d;
+    if (p.ws_bytes > 0) {
+        void *ptr = nullptr;
+        if ((st = scratch_address(&ptr)) != GLA_OK) return st;
+        f.workspace = ptr;
+        f.workspace_bytes = GLA_NOALLOC_SCRATCH_BYTES;
+    }
+    // with the workspace given, the forward pass allocates nothing
+    return fwd_run(&f, 0, stream);
+}
 
 int gla_step(const gla_step_desc *d, void *stream) {
     if (!d || !d->q || !d->k || !d->v || !d->state || !d->out) return GLA_ERR_INVALID_ARG;

@@ -46,8 +46,10 @@
  * default stream) and returns without synchronising; outputs are valid once the stream
  * has completed the work.  GLA_ERR_HIP reports launch-time errors only.  The only mutable
  * global state is a per-device record (atomic bit masks) of which kernels have had their
- * shared-memory limit raised; calls are re-entrant.  Two calls that share an output, a final
- * state or a caller workspace must not run concurrently.
+ * shared-memory limit raised, and the per-device scratch of gla_fwd_noalloc with its
+ * address cache (mutex-guarded); calls other than gla_fwd_noalloc are re-entrant.  Two
+ * calls that share an output, a final state or a caller workspace must not run
+ * concurrently.
  */
 #ifndef GLA_H
 #define GLA_H
@@ -59,7 +61,7 @@
 extern "C" {
 #endif
 
-#define GLA_VERSION 10300 /* major * 10000 + minor * 100 + patch */
+#define GLA_VERSION 10400 /* major * 10000 + minor * 100 + patch */
 
 /* Status codes.  0 is success; errors are negative. */
 enum gla_status {
@@ -148,6 +150,24 @@ int gla_fwd(const void *q, const void *k, const void *v, const float *log_alpha,
  * with GLA_FLAG_TILE_PAIRS and fp32 inputs: chunk > 64 is then unsupported for Dk = 256,
  * and for Dk = 128 under a per-channel gate.  Returns a gla_status. */
 int gla_fwd_ex(const gla_desc *d, void *stream);
+
+/* Device scratch available to gla_fwd_noalloc on each GPU: 32 MiB. */
+#define GLA_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+/* Forward pass that allocates no memory, for callers that cannot allocate: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation.  Same operation,
+ * arguments, support matrix and kernels as gla_fwd_ex, except the scratch: d->workspace must
+ * be NULL and d->workspace_bytes 0 (else GLA_ERR_INVALID_ARG); the scratch the call needs
+ * (gla_workspace_size; only sequence-segmented calls and the tile-pair form need any) comes
+ * from a device array of GLA_NOALLOC_SCRATCH_BYTES built into the library, one per GPU,
+ * held from the first call on that GPU until the process ends.  A call that needs more
+ * returns GLA_ERR_WORKSPACE and launches nothing.  The first call on a GPU resolves the
+ * array's address with that GPU current (a HIP runtime query, no allocation).
+ * Every call on one GPU shares that GPU's array and leaves its contents behind (nothing in
+ * it is read before this call writes it): calls that overlap in time on one GPU, on
+ * different streams or from different host threads, race on it and must be serialised by
+ * the caller.  Returns a gla_status. */
+int gla_fwd_noalloc(const gla_desc *d, void *stream);
 
 /* Scratch bytes gla_fwd_ex needs for `d` (no HIP call).  Returns a gla_status. */
 int gla_workspace_size(const gla_desc *d, size_t *bytes);

@@ -345,3 +345,25 @@ def test_headline_binding_rejects_mismatched_shapes(lib):
     a = _cpu_fwd_args()
     with pytest.raises(ValueError, match="out"):
         gla.fwd_headline(a["q"], a["k"], a["v"], a["log_alpha"], torch.zeros(2, 3, 10, 32), None)
+
+
+def test_noalloc_rejects_caller_workspace_and_oversized_scratch(lib):
+    # gla_fwd_noalloc takes its scratch from the library's fixed per-GPU array: a caller
+    # workspace is an invalid argument, and a call whose scratch exceeds the array is refused
+    # before any HIP call
+    d = desc(workspace=A, workspace_bytes=1 << 20)
+    assert lib.gla_fwd_noalloc(ctypes.byref(d), None) == gla.GLA_ERR_INVALID_ARG
+    big = desc(B=1, H=16, L=1 << 18, seg_chunks=1)  # one boundary state per 64-token chunk
+    need = gla.workspace_size(big)
+    assert need > gla.NOALLOC_SCRATCH_BYTES
+    assert lib.gla_fwd_noalloc(ctypes.byref(big), None) == gla.GLA_ERR_WORKSPACE
+    # validation errors come first, as for gla_fwd_ex
+    assert lib.gla_fwd_noalloc(ctypes.byref(desc(q=None)), None) == gla.GLA_ERR_INVALID_ARG
+    assert lib.gla_fwd_noalloc(ctypes.byref(desc(Dk=96)), None) == gla.GLA_ERR_UNSUPPORTED
+    assert lib.gla_fwd_noalloc(None, None) == gla.GLA_ERR_INVALID_ARG
+
+
+def test_noalloc_scratch_limit_matches_header():
+    hdr = open(HEADER).read()
+    m = re.search(r"#define GLA_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", hdr)
+    assert m and int(m.group(1)) << int(m.group(2)) == gla.NOALLOC_SCRATCH_BYTES
