@@ -16,6 +16,12 @@ then draw the gate pre-activations.  Gates are stored as fp32 logs:
   gate ``log_ig = logsigmoid(b)``, ``b ~ N(0, 1)``, ``[B, H, L]`` (sigmoid forget and
   input gates of the mLSTM variant).
 * ``none``: no gate.
+
+Delta-rule workloads (``rule == "delta"``) draw ``q`` and ``k`` uniformly on the unit sphere
+(fp32 N(0, 1) rows divided by their L2 norm in fp32, then rounded to the input dtype), ``v``
+as above, then the writing strength ``beta = sigmoid(x)``, ``x ~ N(0, 1)``, ``[B, H, L]``
+fp32, then the gate (``head``: ``log_alpha = logsigmoid(a)``, ``a ~ N(3, 1)``; Gated
+DeltaNet) or none (DeltaNet).
 """
 from __future__ import annotations
 
@@ -43,6 +49,8 @@ class Workload:
     final_state: bool = True
     gate_shift: float = 3.0      # mean of the forget pre-activation for gate == "head"
     channel_gate_div: float = 16.0
+    rule: str = "linear"         # "linear": S_t = diag(alpha_t) S_{t-1} + i_t k_t^T v_t;
+                                 # "delta": the delta rule with writing strength beta_t
 
     def with_(self, **kw) -> "Workload":
         return replace(self, **kw)
@@ -66,6 +74,14 @@ WORKLOADS = {
 }
 HEADLINE = "gla_bf16_B8H16L2048"
 
+# Delta-rule workloads (DeltaNet and Gated DeltaNet) at the headline shape.
+DELTA_WORKLOADS = {
+    "deltanet_bf16_B8H16L2048": Workload("deltanet_bf16_B8H16L2048", 8, 16, 2048, 128, 128, 64, gate="none",
+                                         rule="delta"),
+    "gated_deltanet_bf16_B8H16L2048": Workload("gated_deltanet_bf16_B8H16L2048", 8, 16, 2048, 128, 128, 64,
+                                               gate="head", rule="delta"),
+}
+
 
 def _dt(name: str):
     return {"bf16": torch.bfloat16, "f32": torch.float32}[name]
@@ -80,6 +96,8 @@ def make_inputs(w: Workload, seed: int = 0, device="cpu") -> dict:
     sd = float(w.scale_dim or Dk)
     div = torch.tensor(math.sqrt(sd), dtype=torch.float32)
     dt = _dt(w.dtype)
+    if w.rule == "delta":
+        return _make_delta_inputs(w, g, div, dt, device)
     q = (torch.randn(B, H, L, Dk, generator=g, dtype=torch.float32) / div).to(dt)
     k = (torch.randn(B, H, L, Dk, generator=g, dtype=torch.float32) / div).to(dt)
     v = (torch.randn(B, H, L, Dv, generator=g, dtype=torch.float32) / div).to(dt)
@@ -111,7 +129,39 @@ def make_inputs(w: Workload, seed: int = 0, device="cpu") -> dict:
     return out
 
 
+def _unit_rows(x):
+    return x / torch.sqrt((x * x).sum(dim=-1, keepdim=True))
+
+
+def _make_delta_inputs(w: Workload, g, div, dt, device) -> dict:
+    B, H, L, Dk, Dv = w.B, w.H, w.L, w.Dk, w.Dv
+    q = _unit_rows(torch.randn(B, H, L, Dk, generator=g, dtype=torch.float32)).to(dt)
+    k = _unit_rows(torch.randn(B, H, L, Dk, generator=g, dtype=torch.float32)).to(dt)
+    v = (torch.randn(B, H, L, Dv, generator=g, dtype=torch.float32) / div).to(dt)
+    beta = torch.sigmoid(torch.randn(B, H, L, generator=g, dtype=torch.float32))
+    la = None
+    if w.gate == "head":
+        la = torch.nn.functional.logsigmoid(torch.randn(B, H, L, generator=g, dtype=torch.float32) + w.gate_shift)
+    elif w.gate == "head_const":
+        la = torch.tensor([math.log1p(-(2.0 ** (-5 - h))) for h in range(H)], dtype=torch.float64).float()
+    elif w.gate != "none":
+        raise ValueError("delta-rule workloads take a scalar gate, not %r" % w.gate)
+    h = hashlib.sha256()
+    for t in (q, k, v, beta, la):
+        if t is not None:
+            h.update(t.contiguous().view(torch.uint8).numpy().tobytes() if t.dtype != torch.bfloat16
+                     else t.contiguous().view(torch.int16).numpy().tobytes())
+    out = dict(q=q, k=k, v=v, beta=beta, log_alpha=la, log_ig=None, sha256=h.hexdigest())
+    if device != "cpu":
+        for key in ("q", "k", "v", "beta", "log_alpha"):
+            if out[key] is not None:
+                out[key] = out[key].to(device)
+    return out
+
+
 def custom(B, H, L, Dk, Dv, chunk, dtype="bf16", gate="channel", input_gate=False, **kw) -> Workload:
     """A workload of arbitrary shape with the same value distributions."""
-    return Workload("custom_B%dH%dL%dDk%dDv%dC%d_%s_%s" % (B, H, L, Dk, Dv, chunk, dtype, gate), B, H, L, Dk,
-                    Dv, chunk, dtype=dtype, gate=gate, input_gate=input_gate, **kw)
+    rule = kw.get("rule", "linear")
+    return Workload("custom_B%dH%dL%dDk%dDv%dC%d_%s_%s%s" % (B, H, L, Dk, Dv, chunk, dtype, gate,
+                                                           "_delta" if rule == "delta" else ""),
+                    B, H, L, Dk, Dv, chunk, dtype=dtype, gate=gate, input_gate=input_gate, **kw)

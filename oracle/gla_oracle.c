@@ -246,6 +246,95 @@ int gla_oracle_backward(const double *q, const double *k, const double *v, const
     return failed ? -1 : 0;
 }
 
+/* The delta rule (DeltaNet) and its gated form, token by token, for every (b, h) pair.
+ *
+ * DeltaNet gives each token a writing strength beta_t that decides how much of the value
+ * the state already associates with k_t is replaced by v_t [Hardware-Efficient Training of
+ * Linear Attention Models, talk summary, 22:36].  Its update is one step of stochastic
+ * gradient descent, with step size beta_t, on the squared error of predicting v_t from
+ * k_t with the state as a fast weight [same talk, 31:16]: with the loss
+ * 1/2 |k_t S - v_t|^2, whose gradient in S is k_t^T (k_t S - v_t),
+ *
+ *     S_t = S' - beta_t k_t^T (k_t S' - v_t) = (I - beta_t k_t^T k_t) S' + beta_t k_t^T v_t ,
+ *
+ * an identity-plus-rank-one transition [same talk, 31:16].  Gated DeltaNet adds a scalar
+ * per-token decay alpha_t in the manner of Mamba-2 [same talk, 31:16]; read plainly, as
+ * for the gated linear recurrence above, the decay applies to the previous state before
+ * the token is written: S' = alpha_t S_{t-1} (alpha_t = 1 for DeltaNet).  The read is
+ * o_t = q_t S_t, as in linear attention [same talk, 4:04].
+ *
+ *   q, k        [B, H, L, Dk]
+ *   v           [B, H, L, Dv]
+ *   beta        [B, H, L]      writing strength, used as given
+ *   log_alpha   [B, H, L]      natural log of the decay, or NULL (alpha = 1)
+ *   S0          [B, H, Dk, Dv] or NULL (zero initial state)
+ *   out         [B, H, L, Dv]
+ *   final_state [B, H, Dk, Dv] or NULL
+ *
+ * Returns 0, or -1 when a size is not positive, a required pointer is NULL or an
+ * allocation fails. */
+int gla_oracle_delta(const double *q, const double *k, const double *v, const double *beta,
+                     const double *log_alpha, const double *S0, double *out, double *final_state,
+                     long B, long H, long L, long Dk, long Dv)
+{
+    if (!q || !k || !v || !beta || !out) return -1;
+    if (B <= 0 || H <= 0 || L <= 0 || Dk <= 0 || Dv <= 0) return -1;
+    const long BH = B * H;
+    int failed = 0;
+
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long bh = 0; bh < BH; ++bh) {
+        double *S = (double *)malloc(sizeof(double) * (size_t)(Dk * Dv));
+        double *pred = (double *)malloc(sizeof(double) * (size_t)Dv);
+        if (!S || !pred) {
+            free(S);
+            free(pred);
+#pragma omp atomic write
+            failed = 1;
+            continue;
+        }
+        if (S0)
+            memcpy(S, S0 + bh * Dk * Dv, sizeof(double) * (size_t)(Dk * Dv));
+        else
+            memset(S, 0, sizeof(double) * (size_t)(Dk * Dv));
+
+        for (long t = 0; t < L; ++t) {
+            const double *qt = q + (bh * L + t) * Dk;
+            const double *kt = k + (bh * L + t) * Dk;
+            const double *vt = v + (bh * L + t) * Dv;
+            const double bt = beta[bh * L + t];
+            const double at = log_alpha ? exp(log_alpha[bh * L + t]) : 1.0;
+            double *ot = out + (bh * L + t) * Dv;
+
+            /* decay: S' = alpha_t S_{t-1} */
+            for (long i = 0; i < Dk * Dv; ++i) S[i] *= at;
+            /* prediction of v_t from the decayed state: k_t S' */
+            for (long c = 0; c < Dv; ++c) pred[c] = 0.0;
+            for (long d = 0; d < Dk; ++d) {
+                const double *Sd = S + d * Dv;
+                for (long c = 0; c < Dv; ++c) pred[c] += kt[d] * Sd[c];
+            }
+            /* gradient step: S_t = S' + beta_t k_t^T (v_t - k_t S') */
+            for (long d = 0; d < Dk; ++d) {
+                double *Sd = S + d * Dv;
+                const double w = bt * kt[d];
+                for (long c = 0; c < Dv; ++c) Sd[c] += w * (vt[c] - pred[c]);
+            }
+            /* read: o_t = q_t S_t */
+            for (long c = 0; c < Dv; ++c) ot[c] = 0.0;
+            for (long d = 0; d < Dk; ++d) {
+                const double *Sd = S + d * Dv;
+                for (long c = 0; c < Dv; ++c) ot[c] += qt[d] * Sd[c];
+            }
+        }
+        if (final_state)
+            memcpy(final_state + bh * Dk * Dv, S, sizeof(double) * (size_t)(Dk * Dv));
+        free(S);
+        free(pred);
+    }
+    return failed ? -1 : 0;
+}
+
 /* Number of OpenMP threads the recurrence uses (1 without OpenMP). */
 int gla_oracle_threads(void)
 {

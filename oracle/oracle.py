@@ -1,4 +1,4 @@
-"""fp64 oracle for the gated linear attention forward pass.
+"""fp64 oracle for the gated linear attention forward pass and the delta rule.
 
 TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
 ``cpu_baseline`` leg of ``bench.py`` may import this module.  The GPU library never
@@ -26,6 +26,14 @@ Forms (all fp64, computed from the exact input values):
   [talk summary, 7:36 "Challenges in Training Linear Attention"] but print no gradient;
   the derivative of the definition is fixed by the definition itself, and the tests pin it
   by finite differences.
+
+* :func:`delta_recurrent` -- the delta rule (DeltaNet, and Gated DeltaNet with a scalar
+  per-token decay), token by token in C (``gla_oracle_delta``): each token takes one
+  gradient step of size ``beta_t`` on ``1/2 |k_t S - v_t|^2`` [talk summary, 22:36 and
+  31:16].
+* :func:`delta_chunkwise_form` -- the same map chunkwise, with the lower-triangular (WY)
+  system that turns the product of identity-plus-rank-one transitions into sums
+  [talk summary, 31:16].  Tiny inputs only.
 
 Gate kinds (how a stored gate broadcasts to the per-channel log decay):
 ``"none"`` (zero), ``"channel"`` ``[B,H,L,Dk]``, ``"head"`` ``[B,H,L]`` (one decay per
@@ -67,6 +75,8 @@ def load_library(path: str):
     lib.gla_oracle_recurrent.restype = ctypes.c_int
     lib.gla_oracle_backward.argtypes = [dp] * 14 + [ctypes.c_long] * 5
     lib.gla_oracle_backward.restype = ctypes.c_int
+    lib.gla_oracle_delta.argtypes = [dp] * 8 + [ctypes.c_long] * 5
+    lib.gla_oracle_delta.restype = ctypes.c_int
     lib.gla_oracle_threads.restype = ctypes.c_int
     lib.gla_oracle_threads.argtypes = []
     return lib
@@ -284,3 +294,102 @@ def final_state_closed_form(k, v, gate_kind="none", log_alpha=None, log_ig=None)
     G = np.cumsum(la, axis=2)
     w = np.exp(G[:, :, -1:, :] - G) * ig[..., None]  # [B,H,L,Dk]
     return np.einsum("bhtd,bhtc->bhdc", k64 * w, v64)
+
+
+# ---------------------------------------------------------------------------------------
+# The delta rule (DeltaNet) and its gated form.
+
+def delta_gate(log_alpha, B: int, H: int, L: int):
+    """Broadcast a per-token ``[B,H,L]`` or fixed per-head ``[H]`` log decay to ``[B,H,L]``
+    (fp64), or None."""
+    if log_alpha is None:
+        return None
+    a = _f64(log_alpha)
+    if a.shape == (H,) and (B, H, L) != (H,):
+        return np.ascontiguousarray(np.broadcast_to(a[None, :, None], (B, H, L)))
+    assert a.shape == (B, H, L), a.shape
+    return a
+
+
+def delta_recurrent(q, k, v, beta, log_alpha=None, initial_state=None, lib=None):
+    """The delta rule, token by token in C (``gla_oracle_delta``): with
+    ``S' = alpha_t S_{t-1}``, ``S_t = S' + beta_t k_t^T (v_t - k_t S')`` and
+    ``o_t = q_t S_t`` -- one gradient step of size beta_t on ``1/2 |k_t S - v_t|^2``
+    [Hardware-Efficient Training of Linear Attention Models, talk summary, 22:36 and 31:16].
+    ``beta`` is ``[B,H,L]``; ``log_alpha`` ``[B,H,L]``, ``[H]`` or None (DeltaNet).
+    Returns ``(out [B,H,L,Dv], final_state [B,H,Dk,Dv])`` in fp64."""
+    q64, k64, v64 = _f64(q), _f64(k), _f64(v)
+    B, H, L, Dk = q64.shape
+    Dv = v64.shape[-1]
+    assert k64.shape == q64.shape and v64.shape == (B, H, L, Dv)
+    b64 = _f64(beta)
+    assert b64.shape == (B, H, L), b64.shape
+    la = delta_gate(log_alpha, B, H, L)
+    s0 = _f64(initial_state)
+    if s0 is not None:
+        assert s0.shape == (B, H, Dk, Dv)
+    out = np.empty((B, H, L, Dv))
+    fin = np.empty((B, H, Dk, Dv))
+    dp = ctypes.POINTER(ctypes.c_double)
+
+    def p(a):
+        return None if a is None else a.ctypes.data_as(dp)
+
+    rc = (lib or _load()).gla_oracle_delta(p(q64), p(k64), p(v64), p(b64), p(la), p(s0), p(out), p(fin),
+                                           B, H, L, Dk, Dv)
+    if rc != 0:
+        raise RuntimeError("gla_oracle_delta failed (%d)" % rc)
+    return out, fin
+
+
+def delta_chunkwise_form(q, k, v, beta, chunk: int, log_alpha=None, initial_state=None):
+    """The delta rule computed chunkwise with the WY representation, plainly (fp64).
+
+    The talk (31:16) names the obstacle -- the cumulative product of identity-plus-rank-one
+    transitions -- and the remedy: the WY representation turns that product into a sum,
+    so the chunkwise algorithm (11:58) applies.  Written out for one chunk of n tokens
+    entering with state ``S0``: with ``b`` the inclusive running sum of the log decay
+    inside the chunk and ``g = exp(b)``, every token's update is
+    ``S_t = alpha_t S_{t-1} + k_t^T u_t`` with ``u_t = beta_t (v_t - alpha_t k_t S_{t-1})``;
+    unrolling, ``S_t = g_t S0 + sum_{i<=t} (g_t / g_i) k_i^T u_i``, so the u_t satisfy the
+    unit lower-triangular system
+
+        u_t + beta_t sum_{i<t} (g_t / g_i) (k_t . k_i) u_i = beta_t (v_t - g_t k_t S0),
+
+    i.e. ``(I + A) U = diag(beta) (V - diag(g) K S0)``.  With ``T = (I + A)^-1 diag(beta)``
+    (the WY factor): ``U = T V - (T diag(g) K) S0``, and
+
+        O     = diag(g) Q S0 + ((Q K^T) * [g_t / g_i]_{i<=t}) U
+        S_out = g_n S0 + (diag(g_n / g) K)^T U .
+
+    Tiny inputs only.  Returns ``(out, final_state)``."""
+    q64, k64, v64 = _f64(q), _f64(k), _f64(v)
+    B, H, L, Dk = q64.shape
+    Dv = v64.shape[-1]
+    b64 = _f64(beta)
+    la = delta_gate(log_alpha, B, H, L)
+    if la is None:
+        la = np.zeros((B, H, L))
+    s0 = None if initial_state is None else _f64(initial_state)
+    out = np.zeros((B, H, L, Dv))
+    fin = np.zeros((B, H, Dk, Dv))
+    for bb in range(B):
+        for h in range(H):
+            S = np.zeros((Dk, Dv)) if s0 is None else s0[bb, h].copy()
+            for c0 in range(0, L, chunk):
+                c1 = min(L, c0 + chunk)
+                n = c1 - c0
+                Q, K, V = q64[bb, h, c0:c1], k64[bb, h, c0:c1], v64[bb, h, c0:c1]
+                be = b64[bb, h, c0:c1]
+                bcum = np.cumsum(la[bb, h, c0:c1])
+                g = np.exp(bcum)
+                ratio = np.exp(bcum[:, None] - bcum[None, :])  # g_t / g_i, used where i <= t
+                strict = np.tril(np.ones((n, n)), -1)
+                incl = np.tril(np.ones((n, n)))
+                A = be[:, None] * ratio * (K @ K.T) * strict
+                T = np.linalg.solve(np.eye(n) + A, np.diag(be))
+                U = T @ V - (T @ (g[:, None] * K)) @ S
+                out[bb, h, c0:c1] = (g[:, None] * Q) @ S + ((Q @ K.T) * ratio * incl) @ U
+                S = g[-1] * S + ((g[-1] / g)[:, None] * K).T @ U
+            fin[bb, h] = S
+    return out, fin
