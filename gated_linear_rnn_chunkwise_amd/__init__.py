@@ -30,7 +30,7 @@ GATE_NAMES = {"none": GATE_NONE, "channel": GATE_CHANNEL, "head": GATE_HEAD, "he
 
 # Entry points declared in include/gla.h.
 EXPORTS = ("gla_fwd", "gla_fwd_ex", "gla_fwd_noalloc", "gla_workspace_size", "gla_query_plan", "gla_step",
-           "gla_bwd", "gla_bwd_workspace_size", "gla_status_string", "gla_version")
+           "gla_bwd", "gla_bwd_workspace_size", "gla_delta_fwd", "gla_status_string", "gla_version")
 NOALLOC_SCRATCH_BYTES = 32 << 20  # GLA_NOALLOC_SCRATCH_BYTES
 
 
@@ -78,6 +78,17 @@ class GlaBwdDesc(ctypes.Structure):
     ]
 
 
+class GlaDeltaDesc(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int32), ("H", ctypes.c_int32), ("L", ctypes.c_int32), ("Dk", ctypes.c_int32),
+        ("Dv", ctypes.c_int32), ("chunk", ctypes.c_int32), ("in_dtype", ctypes.c_int32),
+        ("gate_kind", ctypes.c_int32),
+        ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("beta", ctypes.c_void_p),
+        ("log_alpha", ctypes.c_void_p), ("initial_state", ctypes.c_void_p),
+        ("out", ctypes.c_void_p), ("final_state", ctypes.c_void_p),
+    ]
+
+
 class GlaError(RuntimeError):
     def __init__(self, status: int, what: str = ""):
         self.status = status
@@ -115,6 +126,8 @@ def load(path: str = LIB_PATH):
         lib.gla_bwd.restype = i32
         lib.gla_bwd_workspace_size.argtypes = [ctypes.POINTER(GlaBwdDesc), ctypes.POINTER(ctypes.c_size_t)]
         lib.gla_bwd_workspace_size.restype = i32
+        lib.gla_delta_fwd.argtypes = [ctypes.POINTER(GlaDeltaDesc), vp]
+        lib.gla_delta_fwd.restype = i32
         lib.gla_status_string.argtypes = [i32]
         lib.gla_status_string.restype = ctypes.c_char_p
         lib.gla_version.argtypes = []
@@ -415,3 +428,71 @@ def workspace_size(desc: GlaDesc) -> int:
     if st != GLA_OK:
         raise GlaError(st, "gla_workspace_size")
     return int(n.value)
+
+
+# ---------------------------------------------------------------------------------------
+# Delta rule (DeltaNet, Gated DeltaNet).
+
+def delta_gate_kind_of(log_alpha, B: int, H: int, L: int) -> int:
+    if log_alpha is None:
+        return GATE_NONE
+    shape = tuple(log_alpha.shape)
+    if shape == (B, H, L):
+        return GATE_HEAD
+    if shape == (H,):
+        return GATE_HEAD_CONST
+    raise ValueError("log_alpha shape %s matches no delta-rule gate layout for B=%d H=%d L=%d" % (shape, B, H, L))
+
+
+def make_delta_desc(q, k, v, beta, log_alpha=None, initial_state=None, out=None, final_state=None,
+                    chunk=64, gate_kind=None) -> GlaDeltaDesc:
+    """Fill a :class:`GlaDeltaDesc` from tensors (shapes read from q and v)."""
+    import torch
+
+    B, H, L, Dk = q.shape
+    Dv = v.shape[-1]
+    d = GlaDeltaDesc()
+    d.B, d.H, d.L, d.Dk, d.Dv, d.chunk = B, H, L, Dk, Dv, int(chunk)
+    if q.dtype == torch.bfloat16:
+        d.in_dtype = DTYPE_BF16
+    elif q.dtype == torch.float32:
+        d.in_dtype = DTYPE_F32
+    else:
+        raise TypeError("q, k, v must be bf16 or fp32, got %s" % q.dtype)
+    d.gate_kind = delta_gate_kind_of(log_alpha, B, H, L) if gate_kind is None else int(gate_kind)
+    d.q, d.k, d.v, d.beta = _ptr(q), _ptr(k), _ptr(v), _ptr(beta)
+    d.log_alpha, d.initial_state = _ptr(log_alpha), _ptr(initial_state)
+    d.out, d.final_state = _ptr(out), _ptr(final_state)
+    return d
+
+
+def delta_fwd(q, k, v, beta, log_alpha=None, *, initial_state=None, chunk: int = 64, final_state: bool = True,
+              out=None, stream=None):
+    """Delta-rule forward (``gla_delta_fwd``) on the current HIP stream: DeltaNet without
+    ``log_alpha``, Gated DeltaNet with a ``[B,H,L]`` (or fixed ``[H]``) log decay.  ``beta``
+    is the ``[B,H,L]`` fp32 writing strength.  Returns ``(out [B,H,L,Dv] fp32,
+    final_state [B,H,Dk,Dv] fp32 or None)``."""
+    import torch
+
+    lib = load()
+    if q.dim() != 4 or v.dim() != 4:
+        raise ValueError("q and v must be [B, H, L, D]")
+    B, H, L, Dk = q.shape
+    Dv = v.shape[-1]
+    _check_shape(k, (B, H, L, Dk), "k")
+    _check_shape(v, (B, H, L, Dv), "v")
+    _check_shape(beta, (B, H, L), "beta")
+    if log_alpha is not None:
+        delta_gate_kind_of(log_alpha, B, H, L)
+    _check_shape(initial_state, (B, H, Dk, Dv), "initial_state")
+    _check_shape(out, (B, H, L, Dv), "out")
+    if out is None:
+        out = torch.empty((B, H, L, Dv), dtype=torch.float32, device=q.device)
+    fin = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=q.device) if final_state else None
+    _check_tensors(q, k, v, beta, log_alpha, initial_state, out, fin)
+    d = make_delta_desc(q, k, v, beta, log_alpha, initial_state, out, fin, chunk)
+    s = stream if stream is not None else torch.cuda.current_stream(q.device)
+    st = lib.gla_delta_fwd(ctypes.byref(d), ctypes.c_void_p(s.cuda_stream))
+    if st != GLA_OK:
+        raise GlaError(st, "gla_delta_fwd")
+    return out, fin

@@ -1,0 +1,621 @@
+// delta_kernels.hip -- gfx950 kernel of the chunkwise delta rule (DeltaNet and Gated DeltaNet).
+//
+// The update.  Each token takes one gradient step of size beta_t on the squared error of
+// predicting v_t from k_t, with the state as a fast weight, after the previous state is
+// decayed by a scalar gate alpha_t (1 for DeltaNet) [Hardware-Efficient Training of Linear
+// Attention Models, talk summary, 22:36 and 31:16]:
+//
+//     S_t = alpha_t (I - beta_t k_t^T k_t) S_{t-1} + beta_t k_t^T v_t ,     o_t = q_t S_t .
+//
+// Chunkwise form.  The transition is identity plus rank one; its product over a chunk is
+// carried by the WY representation, which turns it into sums so that the chunkwise
+// algorithm runs on matrix products [same talk, 31:16 and 11:58].  For a chunk of 64 tokens
+// entering with state S0, with b the running log decay inside the chunk and g = 2^b:
+//
+//     A   = strictly lower part of  diag(beta) [g_t / g_s] (K K^T)
+//     N   = (I + A)^-1                                   (unit lower triangular)
+//     U   = N diag(beta) V  -  N diag(beta g) K S0       (the tokens' corrections u_t)
+//     O   = diag(g) Q S0  +  ((Q K^T) * [g_t / g_s]_{s<=t}) U
+//     S1  = g_63 S0  +  K^T diag(g_63 / g) U .
+//
+// u_t = beta_t (v_t - alpha_t k_t S_{t-1}) is the step each token takes; unrolled over the
+// chunk the u_t satisfy (I + A) U = diag(beta) (V - diag(g) K S0), which is where the
+// triangular system comes from.  Every decay ratio that appears is g_t / g_s with s <= t,
+// at most 1.
+//
+// Work split.  One workgroup (4 waves) owns one (batch, head) and one 64-column slice of
+// the value dimension, and walks the sequence chunk by chunk with its Dk x 64 slice of the
+// state in registers (wave w: columns 16w..16w+15, in matrix-core accumulator layout).  Per
+// chunk:
+//   1. the chunk's q, k (rows, and k transposed), v (transposed), beta and gates into LDS;
+//   2. K K^T -> A and Q K^T -> P (masked, decayed), and Q S0 (the state's share of O);
+//   3. the diagonal 16x16 blocks of I + A inverted by forward substitution (fp32, vector
+//      ALU), then the blocks below them by block forward substitution on the matrix cores;
+//      N diag(beta) and N diag(beta g) stored as operands;
+//   4. W = N diag(beta g) K (all Dk columns, shared by the waves) and N diag(beta) V;
+//   5. U = N diag(beta) V - W S0, O += P U, S1 = g S0 + K^T diag(g_63 / g) U.
+// The accumulator layout of the state (lane (g, c) holds rows 4g+e of each 16-row block,
+// column c) doubles as the B operand of the products that contract over the state's rows,
+// once the contraction index is ordered so that k-slot 8g+j of a 32-deep step is row
+// 4g+j (j < 4) or 16+4g+j-4 (j >= 4) of the step's 32 rows; the same order is used for
+// tokens, so U feeds P U and K^T U straight from registers.  Channel rows (q, k, W) and
+// token rows (P, N, K^T, V^T) are stored in LDS in that order.
+//
+// Numbers.  bf16 inputs: matrix operands fp16 (q, k, v converted; computed operands rounded
+// once), fp32 accumulation; the triangular solve of the diagonal blocks is fp32.  fp32
+// inputs: fp32 operands throughout.  States, decays and outputs are fp32.
+//
+// Rows past the sequence end read as zero through buffer resources (k = v = beta = 0 and
+// no decay: such a token changes nothing) and their output stores are dropped.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <atomic>
+#include <type_traits>
+
+#include "gla.h"
+#include "gla_delta.h"
+
+namespace gla_delta {
+
+typedef _Float16 f16;
+typedef f16 f16x8 __attribute__((ext_vector_type(8)));
+typedef f16 f16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kRsrcFlags = 0x00020000;  // raw buffer, 32-bit data format
+constexpr int kC = 64;                   // tokens per chunk
+constexpr int kAR = 68;                  // fp32 row stride of the A / N matrix in LDS
+
+template <bool F32_, int DK_>
+struct Cfg {
+    static constexpr bool F32 = F32_;
+    static constexpr int DK = DK_;
+    using OpT = typename std::conditional<F32, float, f16>::type;
+    using Frag = typename std::conditional<F32, f32x8, f16x8>::type;  // one 32-deep operand
+    using Quad = typename std::conditional<F32, f32x4, f16x4>::type;  // 4 consecutive operands
+    static constexpr int OB = F32 ? 4 : 2;
+    static constexpr int IB = F32 ? 4 : 2;
+    static constexpr int RQ = DK + 16 / OB;  // row stride of channel rows (q, k, W)
+    static constexpr int RT = kC + 16 / OB;  // row stride of token rows (P, N, K^T, V^T)
+    static constexpr int NB = DK / 16;       // 16-row blocks of the state
+    static constexpr int NM = DK / 32;       // 32-deep steps over the channels
+    static constexpr int NP = DK / 4;        // 4-element pieces of a channel row
+    static constexpr int QSTEP = 256 / NP;   // token quads apart of a thread's pieces
+    static constexpr int QPT = 16 / QSTEP;   // token quads per thread (16 quads per chunk)
+    using Piece = typename std::conditional<F32, u32x4, u32x2>::type;  // 4 raw inputs
+};
+
+// LDS layout (bytes).  sQ is reused for W once q is no longer read.
+struct Plan {
+    uint32_t q, k, kt, vt, p, tv, tk, a, b, be, total;
+};
+__host__ __device__ inline Plan make_plan(bool f32, int dk) {
+    const uint32_t ob = f32 ? 4u : 2u;
+    const uint32_t rq = (uint32_t)dk + 16u / ob, rt = (uint32_t)kC + 16u / ob;
+    auto al = [](uint32_t x) { return (x + 255u) & ~255u; };
+    Plan p{};
+    uint32_t off = 0;
+    p.q = off;
+    off += al(kC * rq * ob);
+    p.k = off;
+    off += al(kC * rq * ob);
+    p.kt = off;
+    off += al((uint32_t)dk * rt * ob);
+    p.vt = off;
+    off += al(64u * rt * ob);
+    p.p = off;
+    off += al(kC * rt * ob);
+    p.tv = off;
+    off += al(kC * rt * ob);
+    p.tk = off;
+    off += al(kC * rt * ob);
+    p.a = off;
+    off += al(kC * kAR * 4u);
+    p.b = off;
+    off += al(kC * 4u);
+    p.be = off;
+    off += al(kC * 4u);
+    p.total = off;
+    return p;
+}
+
+uint32_t lds_bytes(bool f32, int dk) { return make_plan(f32, dk).total; }
+
+// ------------------------------------------------------------------------------------
+__device__ __forceinline__ void barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+__device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float bf_lo(uint32_t x) { return __uint_as_float(x << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
+__device__ __forceinline__ rsrc_t make_rsrc(const void *p, uint64_t bytes) {
+    const uint32_t n = bytes > 0xffffffffull ? 0xffffffffu : (uint32_t)bytes;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)n, kRsrcFlags);
+}
+__device__ __forceinline__ u32x4 bld128(rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+}
+__device__ __forceinline__ float bld_f32(rsrc_t r, uint32_t off) {
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
+}
+__device__ __forceinline__ void bst_f32(float x, rsrc_t r, uint32_t off) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), r, (int)off, 0, 0);
+}
+// log2 of a per-token decay, floored at -150 (the factor is zero either way; the floor
+// keeps running sums small enough for their differences to keep fp32 precision).
+__device__ __forceinline__ float log2_decay(float la) {
+    const float x = la * kLog2e;
+    return x < -150.f ? -150.f : x;
+}
+__device__ __forceinline__ float scan_incl(float x, int lane) {
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const float y = __shfl_up(x, off);
+        if (lane >= off) x += y;
+    }
+    return x;
+}
+// Workgroups i and i+8, ... go to the same XCD; consecutive logical workgroups (the value
+// slices of one head, which read the same q and k) are placed on one XCD to share its L2.
+__device__ __forceinline__ int xcd_remap(int i, int n) {
+    if ((n & 7) != 0) return i;
+    return (i & 7) * (n >> 3) + (i >> 3);
+}
+
+// Position of index x (0..31) inside its 32-group: slot 8g+j holds 4g+j (j < 4) and
+// 16+4g+j-4 (j >= 4).
+__device__ __forceinline__ int pos32(int x) { return x < 16 ? 8 * (x >> 2) + (x & 3) : 8 * ((x - 16) >> 2) + 4 + (x & 3); }
+__device__ __forceinline__ int perm(int x) { return (x & ~31) + pos32(x & 31); }
+
+// 32-deep product with fp16 operands, or the same contraction as eight fp32 4-deep steps
+// (element e of every lane's eight values forms step e).
+__device__ __forceinline__ f32x4 mma(const f16x8 &a, const f16x8 &b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma(const f32x8 &a, const f32x8 &b, f32x4 c) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[e], b[e], c, 0, 0, 0);
+    return c;
+}
+// 16-deep product: lane (g, c) gives A[c][4g+e] and B[4g+e][c] (e < 4), so a 16x16
+// accumulator is directly a B operand.
+template <bool F32>
+__device__ __forceinline__ f32x4 mma16(const f32x4 &a, const f32x4 &b, f32x4 c) {
+    if constexpr (F32) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[e], b[e], c, 0, 0, 0);
+        return c;
+    } else {
+        const f16x4 ah{(f16)a[0], (f16)a[1], (f16)a[2], (f16)a[3]};
+        const f16x4 bh{(f16)b[0], (f16)b[1], (f16)b[2], (f16)b[3]};
+        return __builtin_amdgcn_mfma_f32_16x16x16f16(ah, bh, c, 0, 0, 0);
+    }
+}
+
+template <class C>
+__device__ __forceinline__ typename C::Frag ld_frag(const typename C::OpT *p) {
+    if constexpr (C::F32) {
+        const f32x4 a = *reinterpret_cast<const f32x4 *>(p), b = *reinterpret_cast<const f32x4 *>(p + 4);
+        return f32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    } else {
+        return *reinterpret_cast<const f16x8 *>(p);
+    }
+}
+// Operand from two 16x16 accumulators (rows 4g+e of blocks 2m and 2m+1), times s.
+template <class C>
+__device__ __forceinline__ typename C::Frag acc_frag(const f32x4 &lo, const f32x4 &hi, float s = 1.f) {
+    using OpT = typename C::OpT;
+    typename C::Frag f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        f[e] = (OpT)(lo[e] * s);
+        f[e + 4] = (OpT)(hi[e] * s);
+    }
+    return f;
+}
+// The same with a per-row factor.
+template <class C>
+__device__ __forceinline__ typename C::Frag acc_frag_rows(const f32x4 &lo, const f32x4 &hi, const f32x4 &slo,
+                                                          const f32x4 &shi) {
+    using OpT = typename C::OpT;
+    typename C::Frag f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        f[e] = (OpT)(lo[e] * slo[e]);
+        f[e + 4] = (OpT)(hi[e] * shi[e]);
+    }
+    return f;
+}
+
+// Raw 4-element pieces of the next chunk, held in registers while the current one runs:
+// thread tid holds piece tid % NP of the channel rows of token quads tid / NP + j QSTEP (q
+// and k), columns 4 (tid & 15).. of token quad tid >> 4 (v), and the beta and gate of
+// token tid & 63.
+template <class C>
+struct Pref {
+    typename C::Piece q[C::QPT][4], k[C::QPT][4], v[4];
+    float beta, la;
+};
+
+template <class C>
+__device__ __forceinline__ typename C::Piece ld_piece(rsrc_t r, uint32_t off) {
+    if constexpr (C::F32) return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+    else return __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0);
+}
+
+template <class C>
+__device__ __forceinline__ void prefetch(Pref<C> &pf, rsrc_t rq, rsrc_t rk, rsrc_t rv, rsrc_t rb, rsrc_t rla,
+                                         uint32_t gstride, int T0, int tid, int dv0, int Dv) {
+    const int c = tid % C::NP;
+#pragma unroll
+    for (int j = 0; j < C::QPT; ++j) {
+        const int a = tid / C::NP + j * C::QSTEP;
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+            const uint32_t off = ((uint32_t)(T0 + 4 * a + tt) * C::DK + 4 * c) * C::IB;
+            pf.q[j][tt] = ld_piece<C>(rq, off);
+            pf.k[j][tt] = ld_piece<C>(rk, off);
+        }
+    }
+    {
+        const int a = tid >> 4, cv = tid & 15;
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt)
+            pf.v[tt] = ld_piece<C>(rv, ((uint32_t)(T0 + 4 * a + tt) * Dv + dv0 + 4 * cv) * C::IB);
+    }
+    pf.beta = bld_f32(rb, (uint32_t)(T0 + (tid & 63)) * 4u);
+    pf.la = bld_f32(rla, (uint32_t)(T0 + (tid & 63)) * gstride);
+}
+
+// Element e (0..3) of a raw piece as fp32.
+template <class C>
+__device__ __forceinline__ float el(const typename C::Piece &x, int e) {
+    if constexpr (C::F32) return __uint_as_float(x[e]);
+    else return (e & 1) ? bf_hi(x[e >> 1]) : bf_lo(x[e >> 1]);
+}
+
+template <class C>
+__device__ __forceinline__ void store_quad(typename C::OpT *p, float a, float b, float c, float d) {
+    using Q = typename C::Quad;
+    using OpT = typename C::OpT;
+    *reinterpret_cast<Q *>(p) = Q{(OpT)a, (OpT)b, (OpT)c, (OpT)d};
+}
+
+// The prefetched chunk into LDS: q and k rows (channels in slot order), k^T and v^T (tokens
+// in slot order), beta, and the running log2 decay (wave 0).  Four consecutive channels or
+// tokens starting at a multiple of 4 occupy four consecutive slots.
+template <class C>
+__device__ __forceinline__ void stage(const Pref<C> &pf, unsigned char *smem, const Plan &lp, int tid, int lane,
+                                      int w, bool row_valid_lane) {
+    using OpT = typename C::OpT;
+    OpT *sQ = reinterpret_cast<OpT *>(smem + lp.q);
+    OpT *sK = reinterpret_cast<OpT *>(smem + lp.k);
+    OpT *sKt = reinterpret_cast<OpT *>(smem + lp.kt);
+    OpT *sVt = reinterpret_cast<OpT *>(smem + lp.vt);
+    const int c = tid % C::NP;
+    const int pc = perm(4 * c);
+#pragma unroll
+    for (int j = 0; j < C::QPT; ++j) {
+        const int a = tid / C::NP + j * C::QSTEP;
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+            const int t = 4 * a + tt;
+            store_quad<C>(sQ + t * C::RQ + pc, el<C>(pf.q[j][tt], 0), el<C>(pf.q[j][tt], 1), el<C>(pf.q[j][tt], 2),
+                          el<C>(pf.q[j][tt], 3));
+            store_quad<C>(sK + t * C::RQ + pc, el<C>(pf.k[j][tt], 0), el<C>(pf.k[j][tt], 1), el<C>(pf.k[j][tt], 2),
+                          el<C>(pf.k[j][tt], 3));
+        }
+        const int tp = perm(4 * a);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            store_quad<C>(sKt + (4 * c + e) * C::RT + tp, el<C>(pf.k[j][0], e), el<C>(pf.k[j][1], e),
+                          el<C>(pf.k[j][2], e), el<C>(pf.k[j][3], e));
+    }
+    {
+        const int a = tid >> 4, cv = tid & 15;
+        const int tp = perm(4 * a);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            store_quad<C>(sVt + (4 * cv + e) * C::RT + tp, el<C>(pf.v[0], e), el<C>(pf.v[1], e), el<C>(pf.v[2], e),
+                          el<C>(pf.v[3], e));
+    }
+    if (w == 0) {
+        float *sB = reinterpret_cast<float *>(smem + lp.b);
+        float *sBe = reinterpret_cast<float *>(smem + lp.be);
+        const float x = row_valid_lane ? log2_decay(pf.la) : 0.f;
+        sB[lane] = scan_incl(x, lane);
+        sBe[lane] = row_valid_lane ? pf.beta : 0.f;
+    }
+}
+
+template <class C>
+__global__ __launch_bounds__(256, 1) void delta_chunk_kernel(DeltaArgs a) {
+    using OpT = typename C::OpT;
+    using Frag = typename C::Frag;
+    extern __shared__ __align__(256) unsigned char smem[];
+    const Plan lp = make_plan(C::F32, C::DK);
+    OpT *sQ = reinterpret_cast<OpT *>(smem + lp.q);
+    OpT *sW = sQ;  // W replaces q once q is no longer read
+    const OpT *sK = reinterpret_cast<const OpT *>(smem + lp.k);
+    const OpT *sKt = reinterpret_cast<const OpT *>(smem + lp.kt);
+    const OpT *sVt = reinterpret_cast<const OpT *>(smem + lp.vt);
+    OpT *sP = reinterpret_cast<OpT *>(smem + lp.p);
+    OpT *sTv = reinterpret_cast<OpT *>(smem + lp.tv);
+    OpT *sTk = reinterpret_cast<OpT *>(smem + lp.tk);
+    float *sA = reinterpret_cast<float *>(smem + lp.a);
+    const float *sB = reinterpret_cast<const float *>(smem + lp.b);
+    const float *sBe = reinterpret_cast<const float *>(smem + lp.be);
+
+    const int id = xcd_remap((int)blockIdx.x, (int)gridDim.x);
+    const int dvt = id % a.ndv;
+    const int bh = id / a.ndv;
+    const int h = bh % a.H;
+    const int dv0 = dvt * 64;
+    const int tid = (int)threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
+    const int L = a.L, Dv = a.Dv;
+    const size_t bhL = (size_t)bh * L;
+
+    const rsrc_t rq = make_rsrc(reinterpret_cast<const char *>(a.q) + bhL * C::DK * C::IB, (uint64_t)L * C::DK * C::IB);
+    const rsrc_t rk = make_rsrc(reinterpret_cast<const char *>(a.k) + bhL * C::DK * C::IB, (uint64_t)L * C::DK * C::IB);
+    const rsrc_t rv = make_rsrc(reinterpret_cast<const char *>(a.v) + bhL * Dv * C::IB, (uint64_t)L * Dv * C::IB);
+    const rsrc_t rb = make_rsrc(a.beta + bhL, (uint64_t)L * 4);
+    rsrc_t rla;
+    uint32_t gstride = 4u;
+    if (a.gate == GLA_GATE_HEAD) {
+        rla = make_rsrc(a.la + bhL, (uint64_t)L * 4);
+    } else if (a.gate == GLA_GATE_HEAD_CONST) {
+        rla = make_rsrc(a.la + h, 4);
+        gstride = 0u;
+    } else {
+        rla = make_rsrc(a.out, 0);  // reads return zero: no decay
+    }
+    const rsrc_t rout = make_rsrc(a.out + bhL * Dv, (uint64_t)L * Dv * 4);
+
+    // this wave's slice of the state: rows 16r+4g+e, column dv0 + 16w + c16
+    f32x4 S[C::NB];
+    const int col = dv0 + 16 * w + c16;
+#pragma unroll
+    for (int r = 0; r < C::NB; ++r) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            S[r][e] = a.s0 ? a.s0[((size_t)bh * C::DK + 16 * r + 4 * g + e) * Dv + col] : 0.f;
+    }
+
+    Pref<C> pf;
+    prefetch<C>(pf, rq, rk, rv, rb, rla, gstride, 0, tid, dv0, Dv);
+    const int nc = (L + kC - 1) / kC;
+    for (int ci = 0; ci < nc; ++ci) {
+        const int T0 = ci * kC;
+        stage<C>(pf, smem, lp, tid, lane, w, T0 + lane < L);
+        barrier();  // B1: chunk staged
+        prefetch<C>(pf, rq, rk, rv, rb, rla, gstride, T0 + kC, tid, dv0, Dv);
+
+        // ---- products that do not depend on the state's update
+        // (a) K K^T, row block w -> A (strictly lower, decayed, times beta of the row)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if (j <= w) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int m = 0; m < C::NM; ++m)
+                    acc = mma(ld_frag<C>(sK + (16 * w + c16) * C::RQ + 32 * m + 8 * g),
+                              ld_frag<C>(sK + (16 * j + c16) * C::RQ + 32 * m + 8 * g), acc);
+                const int s = 16 * j + c16;
+                const float bs = sB[s];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int t = 16 * w + 4 * g + e;
+                    sA[t * kAR + s] = s < t ? sBe[t] * fexp2(sB[t] - bs) * acc[e] : 0.f;
+                }
+            }
+        }
+        // (b) Q K^T, row block 3-w -> P (causal, decayed; zero above the diagonal)
+        {
+            const int i = 3 - w;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                if (j <= i) {
+#pragma unroll
+                    for (int m = 0; m < C::NM; ++m)
+                        acc = mma(ld_frag<C>(sQ + (16 * i + c16) * C::RQ + 32 * m + 8 * g),
+                                  ld_frag<C>(sK + (16 * j + c16) * C::RQ + 32 * m + 8 * g), acc);
+                }
+                const int s = 16 * j + c16;
+                const float bs = sB[s];
+                const int ps = perm(s);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int t = 16 * i + 4 * g + e;
+                    sP[t * C::RT + ps] = (OpT)(s <= t ? fexp2(sB[t] - bs) * acc[e] : 0.f);
+                }
+            }
+        }
+        // (c) the state's share of the output: diag(g) Q S0
+        f32x4 O[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int m = 0; m < C::NM; ++m)
+                acc = mma(ld_frag<C>(sQ + (16 * i + c16) * C::RQ + 32 * m + 8 * g), acc_frag<C>(S[2 * m], S[2 * m + 1]),
+                          acc);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[e] *= fexp2(sB[16 * i + 4 * g + e]);
+            O[i] = acc;
+        }
+        barrier();  // B2: A and P complete
+
+        // ---- (I + A)^-1: diagonal blocks by forward substitution (wave w: block w, lane
+        // column c16; every lane group computes it, group 0 writes it over A's block)
+        {
+            float x[16];
+            float *blk = sA + (16 * w) * kAR + 16 * w;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float acc = r == c16 ? 1.f : 0.f;
+#pragma unroll
+                for (int i = 0; i < r; ++i) acc -= blk[r * kAR + i] * x[i];
+                x[r] = acc;
+            }
+            if (g == 0) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) blk[r * kAR + c16] = x[r];
+            }
+        }
+        barrier();  // B3: diagonal inverses D_i in place
+        // blocks below the diagonal, column block j = w: N_ij = -D_i sum_{j<=k<i} A_ik N_kj;
+        // every block of the column is kept in accumulator layout (a B operand as it is)
+        {
+            const int j = w;
+            f32x4 Nb[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                Nb[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+                if (i == j) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) Nb[i][e] = sA[(16 * i + 4 * g + e) * kAR + 16 * i + c16];
+                } else if (i > j) {
+                    f32x4 R = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int k = 0; k < i; ++k)
+                        if (k >= j)
+                            R = mma16<C::F32>(*reinterpret_cast<const f32x4 *>(sA + (16 * i + c16) * kAR + 16 * k + 4 * g),
+                                              Nb[k], R);
+                    const f32x4 d = *reinterpret_cast<const f32x4 *>(sA + (16 * i + c16) * kAR + 16 * i + 4 * g);
+                    Nb[i] = -mma16<C::F32>(d, R, f32x4{0.f, 0.f, 0.f, 0.f});
+                }
+            }
+            // column block j of N diag(beta) and N diag(beta g), as operands
+            const int s = 16 * j + c16;
+            const float be = sBe[s];
+            const float bg = be * fexp2(sB[s]);
+            const int ps = perm(s);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int t = 16 * i + 4 * g + e;
+                    sTv[t * C::RT + ps] = (OpT)(Nb[i][e] * be);
+                    sTk[t * C::RT + ps] = (OpT)(Nb[i][e] * bg);
+                }
+            }
+        }
+        barrier();  // B4: N diag(beta), N diag(beta g) complete
+
+        // ---- W = N diag(beta g) K (wave w: channel blocks of its quarter), U' = N diag(beta) V
+#pragma unroll
+        for (int jb = 0; jb < C::NB / 4; ++jb) {
+            const int jt = w * (C::NB / 4) + jb;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int m = 0; m < 2; ++m)
+                    acc = mma(ld_frag<C>(sTk + (16 * i + c16) * C::RT + 32 * m + 8 * g),
+                              ld_frag<C>(sKt + (16 * jt + c16) * C::RT + 32 * m + 8 * g), acc);
+                const int pd = perm(16 * jt + c16);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) sW[(16 * i + 4 * g + e) * C::RQ + pd] = (OpT)acc[e];
+            }
+        }
+        f32x4 U[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int m = 0; m < 2; ++m)
+                acc = mma(ld_frag<C>(sTv + (16 * i + c16) * C::RT + 32 * m + 8 * g),
+                          ld_frag<C>(sVt + (16 * w + c16) * C::RT + 32 * m + 8 * g), acc);
+            U[i] = acc;
+        }
+        barrier();  // B5: W complete
+
+        // ---- U = U' - W S0
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+            for (int m = 0; m < C::NM; ++m)
+                U[i] = mma(ld_frag<C>(sW + (16 * i + c16) * C::RQ + 32 * m + 8 * g),
+                           acc_frag<C>(S[2 * m], S[2 * m + 1], -1.f), U[i]);
+        }
+        // ---- O += P U, stored
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+            for (int m = 0; m < 2; ++m)
+                O[i] = mma(ld_frag<C>(sP + (16 * i + c16) * C::RT + 32 * m + 8 * g), acc_frag<C>(U[2 * m], U[2 * m + 1]),
+                           O[i]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                bst_f32(O[i][e], rout, ((uint32_t)(T0 + 16 * i + 4 * g + e) * Dv + col) * 4u);
+        }
+        // ---- S1 = g_63 S0 + K^T diag(g_63 / g) U
+        {
+            const float bC = sB[kC - 1];
+            const float gC = fexp2(bC);
+            f32x4 f[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) f[i][e] = fexp2(bC - sB[16 * i + 4 * g + e]);
+            Frag ub[2];
+#pragma unroll
+            for (int m = 0; m < 2; ++m) ub[m] = acc_frag_rows<C>(U[2 * m], U[2 * m + 1], f[2 * m], f[2 * m + 1]);
+#pragma unroll
+            for (int r = 0; r < C::NB; ++r) {
+                f32x4 acc = S[r] * gC;
+#pragma unroll
+                for (int m = 0; m < 2; ++m) acc = mma(ld_frag<C>(sKt + (16 * r + c16) * C::RT + 32 * m + 8 * g), ub[m], acc);
+                S[r] = acc;
+            }
+        }
+        barrier();  // B6: the chunk's LDS may be overwritten
+    }
+
+    if (a.fin) {
+#pragma unroll
+        for (int r = 0; r < C::NB; ++r)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) a.fin[((size_t)bh * C::DK + 16 * r + 4 * g + e) * Dv + col] = S[r][e];
+    }
+}
+
+template <class C>
+static hipError_t launch_cfg(const DeltaArgs &a, hipStream_t st) {
+    static std::atomic<uint64_t> done{0};
+    const uint32_t lds = lds_bytes(C::F32, C::DK);
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const uint64_t bit = 1ull << (dev & 63);
+    if (!(done.load(std::memory_order_acquire) & bit)) {
+        e = hipFuncSetAttribute(reinterpret_cast<const void *>(&delta_chunk_kernel<C>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+        done.fetch_or(bit, std::memory_order_acq_rel);
+    }
+    hipLaunchKernelGGL(delta_chunk_kernel<C>, dim3((unsigned)a.nwg), dim3(256), lds, st, a);
+    return hipGetLastError();
+}
+
+hipError_t launch(const DeltaArgs &a, bool f32, int dk, hipStream_t st) {
+    if (f32) {
+        if (dk == 64) return launch_cfg<Cfg<true, 64>>(a, st);
+        return hipErrorInvalidValue;
+    }
+    if (dk == 64) return launch_cfg<Cfg<false, 64>>(a, st);
+    if (dk == 128) return launch_cfg<Cfg<false, 128>>(a, st);
+    if (dk == 256) return launch_cfg<Cfg<false, 256>>(a, st);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace gla_delta

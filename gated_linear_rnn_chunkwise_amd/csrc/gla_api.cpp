@@ -16,6 +16,7 @@
 #include <mutex>
 
 #include "gla.h"
+#include "gla_delta.h"
 #include "gla_layout.h"
 
 namespace gla {
@@ -643,4 +644,52 @@ int gla_bwd(const gla_bwd_desc *d, void *stream) {
                            d->dfinal_state ? F(p.dfT) : nullptr, F(p.part), mx, s));
     if (owned) (void)hipFreeAsync(ws, s);
     return rc;
+}
+
+// ------------------------------------------------------------------------------------
+// Delta rule (delta_kernels.hip).
+
+extern "C" int gla_delta_fwd(const gla_delta_desc *d, void *stream) {
+    if (!d || !d->q || !d->k || !d->v || !d->beta || !d->out) return GLA_ERR_INVALID_ARG;
+    if (d->B <= 0 || d->H <= 0 || d->L <= 0 || d->Dk <= 0 || d->Dv <= 0 || d->chunk <= 0) return GLA_ERR_INVALID_ARG;
+    if (d->in_dtype != GLA_DTYPE_BF16 && d->in_dtype != GLA_DTYPE_F32) return GLA_ERR_INVALID_ARG;
+    if (d->gate_kind != GLA_GATE_NONE && d->gate_kind != GLA_GATE_HEAD && d->gate_kind != GLA_GATE_HEAD_CONST)
+        return d->gate_kind == GLA_GATE_CHANNEL ? GLA_ERR_UNSUPPORTED : GLA_ERR_INVALID_ARG;
+    if ((d->gate_kind == GLA_GATE_NONE) != (d->log_alpha == nullptr)) return GLA_ERR_INVALID_ARG;
+    const void *ptrs[] = {d->q, d->k, d->v, d->beta, d->log_alpha, d->initial_state, d->out, d->final_state};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p)) return GLA_ERR_INVALID_ARG;
+    const int64_t lim = int64_t(1) << 40;
+    const int64_t bh = int64_t(d->B) * d->H;
+    if (bh > (int64_t(1) << 24)) return GLA_ERR_INVALID_ARG;
+    if (bh * d->L > lim / std::max(d->Dk, d->Dv)) return GLA_ERR_INVALID_ARG;
+    if (bh * int64_t(d->Dk) * d->Dv > lim) return GLA_ERR_INVALID_ARG;
+    const bool f32 = d->in_dtype == GLA_DTYPE_F32;
+    if (d->chunk != 64) return GLA_ERR_UNSUPPORTED;
+    if (f32 ? d->Dk != 64 : (d->Dk != 64 && d->Dk != 128 && d->Dk != 256)) return GLA_ERR_UNSUPPORTED;
+    if (d->Dv % 64 != 0 || d->Dv > 4096) return GLA_ERR_UNSUPPORTED;
+    // one (batch, head) slice is addressed with 32-bit byte offsets, one chunk past the end
+    // read by the prefetch
+    if ((int64_t(d->L) + 128) * std::max(d->Dk, d->Dv) * 4 >= (int64_t(1) << 32)) return GLA_ERR_UNSUPPORTED;
+    if (gla_delta::lds_bytes(f32, d->Dk) > gla::kMaxLds) return GLA_ERR_UNSUPPORTED;
+    const int64_t nwg = bh * (d->Dv / 64);
+    if (nwg > INT32_MAX) return GLA_ERR_UNSUPPORTED;
+    gla_delta::DeltaArgs a{};
+    a.q = d->q;
+    a.k = d->k;
+    a.v = d->v;
+    a.beta = d->beta;
+    a.la = d->log_alpha;
+    a.s0 = d->initial_state;
+    a.out = d->out;
+    a.fin = d->final_state;
+    a.B = d->B;
+    a.H = d->H;
+    a.L = d->L;
+    a.Dv = d->Dv;
+    a.gate = d->gate_kind;
+    a.ndv = d->Dv / 64;
+    a.nwg = (int)nwg;
+    return gla_delta::launch(a, f32, d->Dk, reinterpret_cast<hipStream_t>(stream)) == hipSuccess ? GLA_OK
+                                                                                               : GLA_ERR_HIP;
 }

@@ -260,6 +260,49 @@ int gla_bwd(const gla_bwd_desc *d, void *stream);
 /* Scratch bytes gla_bwd needs for `d` (no HIP call).  Returns a gla_status. */
 int gla_bwd_workspace_size(const gla_bwd_desc *d, size_t *bytes);
 
+/* The delta rule: DeltaNet and Gated DeltaNet, computed chunkwise.  For every (batch, head),
+ * with a Dk x Dv fp32 state S (zero, or the given initial state, before the first token):
+ *
+ *     S_t = alpha_t (I - beta_t k_t^T k_t) S_{t-1} + beta_t k_t^T v_t ,     o_t = q_t S_t .
+ *
+ * beta_t is the writing strength of token t [Hardware-Efficient Training of Linear Attention
+ * Models, talk summary, 22:36]; the update is one gradient step of size beta_t on
+ * 1/2 |k_t S - v_t|^2, the state acting as a fast weight, and Gated DeltaNet adds a scalar
+ * decay alpha_t in the manner of Mamba-2 [same talk, 31:16], here applied to the previous
+ * state before the token is written (alpha_t = 1 for DeltaNet).  The transition is identity
+ * plus rank one; the chunkwise form carries its product over a chunk with the WY
+ * representation (a unit lower-triangular solve per chunk) [same talk, 31:16], and gives the
+ * same map as the recurrence up to rounding.  beta and keys are used as given: the step is a
+ * contraction of the state along k_t only while 0 <= beta_t |k_t|^2 <= 2 (unit-norm keys and
+ * beta in [0, 1] keep every state bounded; other values are computed as given).
+ *
+ * Numbers: bf16 inputs run the matrix products on fp16 operands (q, k, v converted, computed
+ * operands rounded once) with fp32 accumulation, and the triangular solve's diagonal blocks
+ * in fp32; fp32 inputs keep fp32 operands throughout.  States and outputs are fp32. */
+typedef struct gla_delta_desc {
+    int32_t B, H, L, Dk, Dv;     /* batch, heads, sequence length, key and value head dims */
+    int32_t chunk;               /* chunk size; 64 (the kernel's chunk) */
+    int32_t in_dtype;            /* enum gla_dtype of q, k, v */
+    int32_t gate_kind;           /* GLA_GATE_NONE (DeltaNet), GLA_GATE_HEAD (Gated DeltaNet,
+                                    [B, H, L]) or GLA_GATE_HEAD_CONST ([H]) */
+    const void *q;               /* [B, H, L, Dk] in_dtype */
+    const void *k;               /* [B, H, L, Dk] in_dtype */
+    const void *v;               /* [B, H, L, Dv] in_dtype */
+    const float *beta;           /* [B, H, L] fp32 writing strength */
+    const float *log_alpha;      /* natural log of alpha_t per gate_kind; NULL iff NONE */
+    const float *initial_state;  /* [B, H, Dk, Dv] or NULL (zero) */
+    float *out;                  /* [B, H, L, Dv] */
+    float *final_state;          /* [B, H, Dk, Dv] or NULL */
+} gla_delta_desc;
+
+/* Delta-rule forward pass.  Support matrix (else GLA_ERR_UNSUPPORTED): chunk 64; bf16 inputs
+ * with Dk in {64, 128, 256}, fp32 inputs with Dk = 64; Dv a multiple of 64 up to 4096; L as
+ * for gla_fwd_ex.  One workgroup per (batch, head, 64 value columns) walks the whole
+ * sequence (no sequence segments: the state transition of a segment is a full Dk x Dk
+ * matrix, not a decay).  log_alpha must be finite (as for gla_fwd_ex).  Validation,
+ * ownership and asynchrony as for gla_fwd_ex; allocates nothing.  Returns a gla_status. */
+int gla_delta_fwd(const gla_delta_desc *d, void *stream);
+
 /* Static English text for a status code (never NULL). */
 const char *gla_status_string(int status);
 

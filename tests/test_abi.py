@@ -367,3 +367,40 @@ def test_noalloc_scratch_limit_matches_header():
     hdr = open(HEADER).read()
     m = re.search(r"#define GLA_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", hdr)
     assert m and int(m.group(1)) << int(m.group(2)) == gla.NOALLOC_SCRATCH_BYTES
+
+
+def delta_desc(**kw):
+    d = gla.GlaDeltaDesc()
+    base = dict(B=2, H=3, L=100, Dk=128, Dv=128, chunk=64, in_dtype=gla.DTYPE_BF16, gate_kind=gla.GATE_HEAD,
+                q=A, k=A, v=A, beta=A, log_alpha=A, initial_state=None, out=A, final_state=None)
+    base.update(kw)
+    for key, val in base.items():
+        setattr(d, key, val)
+    return d
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), gla.GLA_ERR_INVALID_ARG), (dict(beta=None), gla.GLA_ERR_INVALID_ARG),
+    (dict(out=None), gla.GLA_ERR_INVALID_ARG), (dict(L=0), gla.GLA_ERR_INVALID_ARG),
+    (dict(gate_kind=gla.GATE_NONE), gla.GLA_ERR_INVALID_ARG),  # gate pointer given without a gate
+    (dict(log_alpha=None), gla.GLA_ERR_INVALID_ARG),  # gate kind without a pointer
+    (dict(beta=A + 4), gla.GLA_ERR_INVALID_ARG), (dict(in_dtype=7), gla.GLA_ERR_INVALID_ARG),
+    (dict(gate_kind=gla.GATE_CHANNEL), gla.GLA_ERR_UNSUPPORTED), (dict(chunk=128), gla.GLA_ERR_UNSUPPORTED),
+    (dict(Dk=96), gla.GLA_ERR_UNSUPPORTED), (dict(Dv=96), gla.GLA_ERR_UNSUPPORTED),
+    (dict(in_dtype=gla.DTYPE_F32, Dk=128), gla.GLA_ERR_UNSUPPORTED),
+])
+def test_delta_validation_before_any_hip_call(lib, kw, status):
+    assert lib.gla_delta_fwd(ctypes.byref(delta_desc(**kw)), None) == status
+    assert lib.gla_delta_fwd(None, None) == gla.GLA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("name,shape", [("k", (2, 3, 9, 64)), ("beta", (2, 3, 9)), ("log_alpha", (2, 3, 10, 64)),
+                                        ("initial_state", (2, 3, 64, 32))])
+def test_delta_binding_rejects_mismatched_shapes(lib, name, shape):
+    import torch
+
+    a = dict(q=torch.zeros(2, 3, 10, 64), k=torch.zeros(2, 3, 10, 64), v=torch.zeros(2, 3, 10, 64),
+             beta=torch.zeros(2, 3, 10), log_alpha=torch.zeros(2, 3, 10), initial_state=torch.zeros(2, 3, 64, 64))
+    a[name] = torch.zeros(shape)
+    with pytest.raises(ValueError, match=name):
+        gla.delta_fwd(a["q"], a["k"], a["v"], a["beta"], a["log_alpha"], initial_state=a["initial_state"])
