@@ -349,6 +349,136 @@ def backward_bench(args, torch, gla, gin, w, wname):
     print(json.dumps(rec), flush=True)
 
 
+def delta_flops(w) -> float:
+    """Flops of the chunkwise delta rule per step (C = 64 as executed): per head-token,
+    6 Dk Dv for the products with the state (Q S, W S, K^T U), (C+1)(2 Dk + 2 Dv) for the
+    causal products inside a chunk (Q K^T, N K, N V, P U), (C-1) Dk for K K^T below the
+    diagonal, and C^2 / 3 for the triangular inverse."""
+    C = 64
+    per = 6.0 * w.Dk * w.Dv + (C + 1) * (2 * w.Dk + 2 * w.Dv) + (C - 1) * w.Dk + C * C / 3.0
+    return float(w.B * w.H * w.L) * per
+
+
+def delta_io_floor_bytes(w) -> float:
+    """q, k, v, beta and the gate read once, the fp32 output and final state written once."""
+    ib = 4 if w.dtype == "f32" else 2
+    gate = {"head": 4, "head_const": 0, "none": 0}[w.gate]
+    per_ht = ib * (2 * w.Dk + w.Dv) + 4 + gate + 4 * w.Dv
+    return float(w.B * w.H * w.L) * per_ht + (w.B * w.H * w.Dk * w.Dv * 4 if w.final_state else 0)
+
+
+def delta_cpu_baseline(w, d, budget_s: float = 20.0) -> dict:
+    """The fp64 delta-rule oracle on a bounded sample of whole (batch, head) slices."""
+    import oracle
+
+    BH = w.B * w.H
+    threads = oracle.threads()
+    sel = lambda t, n: None if t is None else t.reshape(-1, *t.shape[2:])[:n][None]
+
+    def run(n, min_time=0.0):
+        q, k, v, be = (oracle.oracle._f64(sel(d[x], n)) for x in ("q", "k", "v", "beta"))
+        la = oracle.oracle._f64(sel(d["log_alpha"], n)) if w.gate == "head" else None
+        reps, t = 0, 0.0
+        while True:
+            t0 = time.perf_counter()
+            oracle.delta_recurrent(q, k, v, be, la)
+            t += time.perf_counter() - t0
+            reps += 1
+            if t >= min_time or reps >= 200:
+                return t, reps
+
+    probe = min(BH, threads)
+    t_probe, _ = run(probe)
+    rounds = max(1, min(int(budget_s / max(t_probe, 1e-6)), math.ceil(BH / threads)))
+    n = min(BH, rounds * threads)
+    t, reps = run(n, min_time=0.5 * budget_s)
+    return {"value": reps * n * w.L / t / w.H, "unit": "tokens/s", "cores": threads, "host_cpu": host_cpu_model(),
+            "host_logical_cpus": os.cpu_count(), "kind": "oracle",
+            "sample": "%d of %d (batch, head) pairs at full length %d, %d repetition(s), fp64 delta-rule "
+                      "recurrence, %.2f s" % (n, BH, w.L, reps, t)}
+
+
+def delta_bench(args, torch, gla, gin, w, wname):
+    """A delta-rule workload (DeltaNet or Gated DeltaNet): a step is one ``gla_delta_fwd``
+    call (one kernel launch) on resident inputs; roofline against the I/O floor."""
+    import ctypes
+
+    lib = gla.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log("bench: generating inputs for", wname)
+    host = [gin.make_inputs(w, seed=args.seed + i) for i in range(2)]
+    sets = [{k: (v.to(dev) if hasattr(v, "to") else v) for k, v in h.items() if v is not None} for h in host]
+    out = torch.empty((w.B, w.H, w.L, w.Dv), dtype=torch.float32, device=dev)
+    fin = torch.empty((w.B, w.H, w.Dk, w.Dv), dtype=torch.float32, device=dev)
+    descs = [gla.make_delta_desc(s["q"], s["k"], s["v"], s["beta"], s.get("log_alpha"), None, out, fin, w.chunk)
+             for s in sets]
+    stream = torch.cuda.current_stream(dev)
+    sptr = ctypes.c_void_p(stream.cuda_stream)
+
+    def step(i):
+        st = lib.gla_delta_fwd(ctypes.byref(descs[i & 1]), sptr)
+        if st != 0:
+            raise gla.GlaError(st, "gla_delta_fwd")
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    K = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        ev[i][0].record(stream)
+        step(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / K
+    launch_ms = [a.elapsed_time(b) for a, b in ev]
+    mean_ms = sum(launch_ms) / K
+    med_ms, min_ms = quantiles(launch_ms)
+    io = delta_io_floor_bytes(w)
+    flops = delta_flops(w)
+    achieved = io / (mean_ms * 1e-3) / 1e9
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("bench: timing the fp64 oracle on host cores")
+        cpu = delta_cpu_baseline(w, host[0])
+    rec = {
+        "metric": "delta-rule fwd tokens/s (%s)" % ("Gated DeltaNet" if w.gate != "none" else "DeltaNet"),
+        "value": w.B * w.L / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": wname, "B": w.B, "H": w.H, "L": w.L, "Dk": w.Dk, "Dv": w.Dv, "chunk": w.chunk,
+                   "rule": "delta", "gate": w.gate, "in_dtype": w.dtype,
+                   "matrix_operands": "fp16 from bf16" if w.dtype == "bf16" else "fp32", "accumulate": "fp32",
+                   "out_dtype": "fp32", "workgroups": w.B * w.H * (w.Dv // 64)},
+        "head_tokens_per_s": w.B * w.H * w.L / (ms_per_step * 1e-3),
+        "tflops": round(flops / (mean_ms * 1e-3) / 1e12, 2),
+        "tflops_counts": "flops of the chunkwise WY form as executed (C = 64)",
+        "pct_bf16_mfma_peak": round(100.0 * flops / (mean_ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 2),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "kernel": "delta chunk kernel (the only launch of a step)",
+                     "algorithmic_bytes_per_launch": io, "extra_bytes": 0.0,
+                     "median_launch_ms": round(med_ms, 5), "min_launch_ms": round(min_ms, 5),
+                     "mean_launch_ms": round(mean_ms, 5),
+                     "frac_at_median_launch": round(io / (med_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                     "frac_at_min_launch": round(io / (min_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -383,6 +513,9 @@ def main():
     from gated_linear_rnn_chunkwise_amd import inputs as gin
 
     wname = args.workload or gin.HEADLINE
+    if wname in gin.DELTA_WORKLOADS:
+        delta_bench(args, torch, gla, gin, gin.DELTA_WORKLOADS[wname], wname)
+        return
     w = gin.WORKLOADS[wname]
     if args.decode:
         decode_bench(args, torch, gla, gin, w, wname)
