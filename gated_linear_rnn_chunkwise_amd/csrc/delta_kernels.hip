@@ -13,8 +13,7 @@
 // entering with state S0, with b the running log decay inside the chunk and g = 2^b:
 //
 //     A   = strictly lower part of  diag(beta) [g_t / g_s] (K K^T)
-//     N   = (I + A)^-1                                   (unit lower triangular)
-//     U   = N diag(beta) V  -  N diag(beta g) K S0       (the tokens' corrections u_t)
+//     U   = (I + A)^-1 diag(beta) (V - diag(g) K S0)     (the tokens' corrections u_t)
 //     O   = diag(g) Q S0  +  ((Q K^T) * [g_t / g_s]_{s<=t}) U
 //     S1  = g_63 S0  +  K^T diag(g_63 / g) U .
 //
@@ -29,11 +28,11 @@
 // chunk:
 //   1. the chunk's q, k (rows, and k transposed), v (transposed), beta and gates into LDS;
 //   2. K K^T -> A and Q K^T -> P (masked, decayed), and Q S0 (the state's share of O);
-//   3. the diagonal 16x16 blocks of I + A inverted by forward substitution (fp32, vector
-//      ALU), then the blocks below them by block forward substitution on the matrix cores;
-//      N diag(beta) and N diag(beta g) stored as operands;
-//   4. W = N diag(beta g) K (all Dk columns, shared by the waves) and N diag(beta) V;
-//   5. U = N diag(beta) V - W S0, O += P U, S1 = g S0 + K^T diag(g_63 / g) U.
+//   3. the diagonal 16x16 blocks D_i of I + A inverted (fp32, vector ALU);
+//   4. U = (I + A)^-1 R with R = diag(beta) (V - diag(g) K S0), by block forward
+//      substitution over the four 16-token blocks, U_i = D_i (R_i - sum_{k<i} A_ik U_k), on
+//      the matrix cores for the wave's own 16 columns (N is never formed);
+//   5. O += P U, S1 = g_63 S0 + K^T diag(g_63 / g) U.
 // The accumulator layout of the state (lane (g, c) holds rows 4g+e of each 16-row block,
 // column c) doubles as the B operand of the products that contract over the state's rows,
 // once the contraction index is ordered so that k-slot 8g+j of a 32-deep step is row
@@ -91,9 +90,9 @@ struct Cfg {
     using Piece = typename std::conditional<F32, u32x4, u32x2>::type;  // 4 raw inputs
 };
 
-// LDS layout (bytes).  sQ is reused for W once q is no longer read.
+// LDS layout (bytes).
 struct Plan {
-    uint32_t q, k, kt, vt, p, tv, tk, a, b, be, total;
+    uint32_t q, k, kt, vt, p, a, b, be, total;
 };
 __host__ __device__ inline Plan make_plan(bool f32, int dk) {
     const uint32_t ob = f32 ? 4u : 2u;
@@ -110,10 +109,6 @@ __host__ __device__ inline Plan make_plan(bool f32, int dk) {
     p.vt = off;
     off += al(64u * rt * ob);
     p.p = off;
-    off += al(kC * rt * ob);
-    p.tv = off;
-    off += al(kC * rt * ob);
-    p.tk = off;
     off += al(kC * rt * ob);
     p.a = off;
     off += al(kC * kAR * 4u);
@@ -340,16 +335,14 @@ template <class C>
 __global__ __launch_bounds__(256, 1) void delta_chunk_kernel(DeltaArgs a) {
     using OpT = typename C::OpT;
     using Frag = typename C::Frag;
+    using Quad = typename C::Quad;
     extern __shared__ __align__(256) unsigned char smem[];
     const Plan lp = make_plan(C::F32, C::DK);
-    OpT *sQ = reinterpret_cast<OpT *>(smem + lp.q);
-    OpT *sW = sQ;  // W replaces q once q is no longer read
+    const OpT *sQ = reinterpret_cast<const OpT *>(smem + lp.q);
     const OpT *sK = reinterpret_cast<const OpT *>(smem + lp.k);
     const OpT *sKt = reinterpret_cast<const OpT *>(smem + lp.kt);
     const OpT *sVt = reinterpret_cast<const OpT *>(smem + lp.vt);
     OpT *sP = reinterpret_cast<OpT *>(smem + lp.p);
-    OpT *sTv = reinterpret_cast<OpT *>(smem + lp.tv);
-    OpT *sTk = reinterpret_cast<OpT *>(smem + lp.tk);
     float *sA = reinterpret_cast<float *>(smem + lp.a);
     const float *sB = reinterpret_cast<const float *>(smem + lp.b);
     const float *sBe = reinterpret_cast<const float *>(smem + lp.be);
@@ -398,165 +391,153 @@ __global__ __launch_bounds__(256, 1) void delta_chunk_kernel(DeltaArgs a) {
         barrier();  // B1: chunk staged
         prefetch<C>(pf, rq, rk, rv, rb, rla, gstride, T0 + kC, tid, dv0, Dv);
 
-        // ---- products that do not depend on the state's update
-        // (a) K K^T, row block w -> A (strictly lower, decayed, times beta of the row)
+        // ---- products that do not need the triangular solve: K K^T of row block w (-> A,
+        // strictly lower, decayed, times beta of the row) and Q K^T of row block 3-w (-> P,
+        // causal, decayed), all four column blocks each as independent accumulator chains
+        {
+            f32x4 kk[4], qk[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            if (j <= w) {
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            for (int j = 0; j < 4; ++j) kk[j] = qk[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+            const int iq = 3 - w;
 #pragma unroll
-                for (int m = 0; m < C::NM; ++m)
-                    acc = mma(ld_frag<C>(sK + (16 * w + c16) * C::RQ + 32 * m + 8 * g),
-                              ld_frag<C>(sK + (16 * j + c16) * C::RQ + 32 * m + 8 * g), acc);
-                const int s = 16 * j + c16;
-                const float bs = sB[s];
+            for (int m = 0; m < C::NM; ++m) {
+                const Frag ak = ld_frag<C>(sK + (16 * w + c16) * C::RQ + 32 * m + 8 * g);
+                const Frag aq = ld_frag<C>(sQ + (16 * iq + c16) * C::RQ + 32 * m + 8 * g);
+                Frag bk[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int t = 16 * w + 4 * g + e;
-                    sA[t * kAR + s] = s < t ? sBe[t] * fexp2(sB[t] - bs) * acc[e] : 0.f;
+                for (int j = 0; j < 4; ++j) bk[j] = ld_frag<C>(sK + (16 * j + c16) * C::RQ + 32 * m + 8 * g);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    kk[j] = mma(ak, bk[j], kk[j]);
+                    qk[j] = mma(aq, bk[j], qk[j]);
                 }
             }
-        }
-        // (b) Q K^T, row block 3-w -> P (causal, decayed; zero above the diagonal)
-        {
-            const int i = 3 - w;
+            const f32x4 bt_k = *reinterpret_cast<const f32x4 *>(sB + 16 * w + 4 * g);
+            const f32x4 be_k = *reinterpret_cast<const f32x4 *>(sBe + 16 * w + 4 * g);
+            const f32x4 bt_q = *reinterpret_cast<const f32x4 *>(sB + 16 * iq + 4 * g);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-                if (j <= i) {
-#pragma unroll
-                    for (int m = 0; m < C::NM; ++m)
-                        acc = mma(ld_frag<C>(sQ + (16 * i + c16) * C::RQ + 32 * m + 8 * g),
-                                  ld_frag<C>(sK + (16 * j + c16) * C::RQ + 32 * m + 8 * g), acc);
-                }
                 const int s = 16 * j + c16;
                 const float bs = sB[s];
+                if (j <= w) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int t = 16 * w + 4 * g + e;
+                        sA[t * kAR + s] = s < t ? be_k[e] * fexp2(bt_k[e] - bs) * kk[j][e] : 0.f;
+                    }
+                }
                 const int ps = perm(s);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int t = 16 * i + 4 * g + e;
-                    sP[t * C::RT + ps] = (OpT)(s <= t ? fexp2(sB[t] - bs) * acc[e] : 0.f);
+                    const int t = 16 * iq + 4 * g + e;
+                    sP[t * C::RT + ps] = (OpT)(s <= t ? fexp2(bt_q[e] - bs) * qk[j][e] : 0.f);
                 }
             }
         }
-        // (c) the state's share of the output: diag(g) Q S0
-        f32x4 O[4];
+        // the state's share of the output, diag(g) Q S0, and the right-hand side of the
+        // triangular system, R = diag(beta) (V - diag(g) K S0), for this wave's 16 columns
+        f32x4 O[4], R[4];
+        {
+            Frag sf[C::NM];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            for (int m = 0; m < C::NM; ++m) sf[m] = acc_frag<C>(S[2 * m], S[2 * m + 1]);
+            f32x4 ks[4];
 #pragma unroll
-            for (int m = 0; m < C::NM; ++m)
-                acc = mma(ld_frag<C>(sQ + (16 * i + c16) * C::RQ + 32 * m + 8 * g), acc_frag<C>(S[2 * m], S[2 * m + 1]),
-                          acc);
+            for (int i = 0; i < 4; ++i) O[i] = ks[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int e = 0; e < 4; ++e) acc[e] *= fexp2(sB[16 * i + 4 * g + e]);
-            O[i] = acc;
+            for (int m = 0; m < C::NM; ++m) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    O[i] = mma(ld_frag<C>(sQ + (16 * i + c16) * C::RQ + 32 * m + 8 * g), sf[m], O[i]);
+                    ks[i] = mma(ld_frag<C>(sK + (16 * i + c16) * C::RQ + 32 * m + 8 * g), sf[m], ks[i]);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const Quad vq = *reinterpret_cast<const Quad *>(sVt + (16 * w + c16) * C::RT + perm(16 * i + 4 * g));
+                const f32x4 bt = *reinterpret_cast<const f32x4 *>(sB + 16 * i + 4 * g);
+                const f32x4 be = *reinterpret_cast<const f32x4 *>(sBe + 16 * i + 4 * g);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float gt = fexp2(bt[e]);
+                    O[i][e] *= gt;
+                    R[i][e] = be[e] * ((float)vq[e] - gt * ks[i][e]);
+                }
+            }
         }
         barrier();  // B2: A and P complete
 
-        // ---- (I + A)^-1: diagonal blocks by forward substitution (wave w: block w, lane
-        // column c16; every lane group computes it, group 0 writes it over A's block)
+        // ---- diagonal blocks of I + A inverted (wave w: block w), right-looking over four
+        // 4-row groups: lane (g, c16) holds rows 4g..4g+3 of column c16; group bg solves its
+        // 4x4 diagonal piece, hands its rows to the groups below (cross-lane reads) and they
+        // subtract their A entries times those rows.
         {
-            float x[16];
             float *blk = sA + (16 * w) * kAR + 16 * w;
+            f32x4 ar[4][4];  // ar[bg][e] = A[4g+e][4bg..4bg+3] of this block
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float acc = r == c16 ? 1.f : 0.f;
+            for (int bg = 0; bg < 4; ++bg)
 #pragma unroll
-                for (int i = 0; i < r; ++i) acc -= blk[r * kAR + i] * x[i];
-                x[r] = acc;
+                for (int e = 0; e < 4; ++e) ar[bg][e] = *reinterpret_cast<const f32x4 *>(blk + (4 * g + e) * kAR + 4 * bg);
+            float x[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[e] = (4 * g + e == c16) ? 1.f : 0.f;
+#pragma unroll
+            for (int bg = 0; bg < 4; ++bg) {
+                if (g == bg) {
+#pragma unroll
+                    for (int e = 1; e < 4; ++e)
+#pragma unroll
+                        for (int j = 0; j < e; ++j) x[e] -= ar[bg][e][j] * x[j];
+                }
+                float xb[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) xb[j] = __shfl(x[j], 16 * bg + c16);
+                if (g > bg) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) x[e] -= ar[bg][e][j] * xb[j];
+                }
             }
-            if (g == 0) {
 #pragma unroll
-                for (int r = 0; r < 16; ++r) blk[r * kAR + c16] = x[r];
-            }
+            for (int e = 0; e < 4; ++e) blk[(4 * g + e) * kAR + c16] = x[e];
         }
         barrier();  // B3: diagonal inverses D_i in place
-        // blocks below the diagonal, column block j = w: N_ij = -D_i sum_{j<=k<i} A_ik N_kj;
-        // every block of the column is kept in accumulator layout (a B operand as it is)
-        {
-            const int j = w;
-            f32x4 Nb[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                Nb[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-                if (i == j) {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) Nb[i][e] = sA[(16 * i + 4 * g + e) * kAR + 16 * i + c16];
-                } else if (i > j) {
-                    f32x4 R = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int k = 0; k < i; ++k)
-                        if (k >= j)
-                            R = mma16<C::F32>(*reinterpret_cast<const f32x4 *>(sA + (16 * i + c16) * kAR + 16 * k + 4 * g),
-                                              Nb[k], R);
-                    const f32x4 d = *reinterpret_cast<const f32x4 *>(sA + (16 * i + c16) * kAR + 16 * i + 4 * g);
-                    Nb[i] = -mma16<C::F32>(d, R, f32x4{0.f, 0.f, 0.f, 0.f});
-                }
-            }
-            // column block j of N diag(beta) and N diag(beta g), as operands
-            const int s = 16 * j + c16;
-            const float be = sBe[s];
-            const float bg = be * fexp2(sB[s]);
-            const int ps = perm(s);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int t = 16 * i + 4 * g + e;
-                    sTv[t * C::RT + ps] = (OpT)(Nb[i][e] * be);
-                    sTk[t * C::RT + ps] = (OpT)(Nb[i][e] * bg);
-                }
-            }
-        }
-        barrier();  // B4: N diag(beta), N diag(beta g) complete
 
-        // ---- W = N diag(beta g) K (wave w: channel blocks of its quarter), U' = N diag(beta) V
-#pragma unroll
-        for (int jb = 0; jb < C::NB / 4; ++jb) {
-            const int jt = w * (C::NB / 4) + jb;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int m = 0; m < 2; ++m)
-                    acc = mma(ld_frag<C>(sTk + (16 * i + c16) * C::RT + 32 * m + 8 * g),
-                              ld_frag<C>(sKt + (16 * jt + c16) * C::RT + 32 * m + 8 * g), acc);
-                const int pd = perm(16 * jt + c16);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) sW[(16 * i + 4 * g + e) * C::RQ + pd] = (OpT)acc[e];
-            }
-        }
+        // ---- U = (I + A)^-1 R by block forward substitution over the four 16-token blocks:
+        // U_i = D_i (R_i - sum_{k<i} A_ik U_k); accumulators serve as B operands directly
         f32x4 U[4];
+        {
+            f32x4 ab[4][4];  // ab[i][k] = row c16 of block (i, k), columns 4g..4g+3 (k < i: -A_ik; k = i: D_i)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int m = 0; m < 2; ++m)
-                acc = mma(ld_frag<C>(sTv + (16 * i + c16) * C::RT + 32 * m + 8 * g),
-                          ld_frag<C>(sVt + (16 * w + c16) * C::RT + 32 * m + 8 * g), acc);
-            U[i] = acc;
-        }
-        barrier();  // B5: W complete
-
-        // ---- U = U' - W S0
+                for (int k = 0; k <= i; ++k) {
+                    const f32x4 x = *reinterpret_cast<const f32x4 *>(sA + (16 * i + c16) * kAR + 16 * k + 4 * g);
+                    ab[i][k] = k < i ? -x : x;
+                }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+            for (int i = 0; i < 4; ++i) {
+                f32x4 acc = R[i];
 #pragma unroll
-            for (int m = 0; m < C::NM; ++m)
-                U[i] = mma(ld_frag<C>(sW + (16 * i + c16) * C::RQ + 32 * m + 8 * g),
-                           acc_frag<C>(S[2 * m], S[2 * m + 1], -1.f), U[i]);
+                for (int k = 0; k < i; ++k) acc = mma16<C::F32>(ab[i][k], U[k], acc);
+                U[i] = mma16<C::F32>(ab[i][i], acc, f32x4{0.f, 0.f, 0.f, 0.f});
+            }
         }
         // ---- O += P U, stored
+        {
+            Frag uf[2];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+            for (int m = 0; m < 2; ++m) uf[m] = acc_frag<C>(U[2 * m], U[2 * m + 1]);
 #pragma unroll
             for (int m = 0; m < 2; ++m)
-                O[i] = mma(ld_frag<C>(sP + (16 * i + c16) * C::RT + 32 * m + 8 * g), acc_frag<C>(U[2 * m], U[2 * m + 1]),
-                           O[i]);
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                bst_f32(O[i][e], rout, ((uint32_t)(T0 + 16 * i + 4 * g + e) * Dv + col) * 4u);
+                for (int i = 0; i < 4; ++i) O[i] = mma(ld_frag<C>(sP + (16 * i + c16) * C::RT + 32 * m + 8 * g), uf[m], O[i]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    bst_f32(O[i][e], rout, ((uint32_t)(T0 + 16 * i + 4 * g + e) * Dv + col) * 4u);
         }
         // ---- S1 = g_63 S0 + K^T diag(g_63 / g) U
         {
@@ -571,14 +552,13 @@ __global__ __launch_bounds__(256, 1) void delta_chunk_kernel(DeltaArgs a) {
 #pragma unroll
             for (int m = 0; m < 2; ++m) ub[m] = acc_frag_rows<C>(U[2 * m], U[2 * m + 1], f[2 * m], f[2 * m + 1]);
 #pragma unroll
-            for (int r = 0; r < C::NB; ++r) {
-                f32x4 acc = S[r] * gC;
+            for (int r = 0; r < C::NB; ++r) S[r] *= gC;
 #pragma unroll
-                for (int m = 0; m < 2; ++m) acc = mma(ld_frag<C>(sKt + (16 * r + c16) * C::RT + 32 * m + 8 * g), ub[m], acc);
-                S[r] = acc;
-            }
+            for (int m = 0; m < 2; ++m)
+#pragma unroll
+                for (int r = 0; r < C::NB; ++r) S[r] = mma(ld_frag<C>(sKt + (16 * r + c16) * C::RT + 32 * m + 8 * g), ub[m], S[r]);
         }
-        barrier();  // B6: the chunk's LDS may be overwritten
+        barrier();  // B4: the chunk's LDS may be overwritten
     }
 
     if (a.fin) {
