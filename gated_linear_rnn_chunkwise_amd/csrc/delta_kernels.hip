@@ -41,8 +41,11 @@
 // token rows (P, N, K^T, V^T) are stored in LDS in that order.
 //
 // Numbers.  bf16 inputs: matrix operands fp16 (q, k, v converted; computed operands rounded
-// once), fp32 accumulation; the triangular solve of the diagonal blocks is fp32.  fp32
-// inputs: fp32 operands throughout.  States, decays and outputs are fp32.
+// once), fp32 accumulation; the triangular solve of the diagonal blocks is fp32.  The
+// corrections U (and the right-hand side of each substitution step) enter their products as
+// an fp16 value plus an fp16 rounding residual: the output is a small difference of terms of
+// the size of U, so one rounding of U would dominate its error.  fp32 inputs: fp32 operands
+// throughout.  States, decays and outputs are fp32.
 //
 // Rows past the sequence end read as zero through buffer resources (k = v = beta = 0 and
 // no decay: such a token changes nothing) and their output stores are dropped.
@@ -228,6 +231,21 @@ __device__ __forceinline__ typename C::Frag acc_frag_rows(const f32x4 &lo, const
         f[e + 4] = (OpT)(hi[e] * shi[e]);
     }
     return f;
+}
+
+// The rounding residual of an operand, as a second operand: x = hi + lo to about 2^-22 of x
+// (fp16 operands); zero with fp32 operands, where no split is needed.
+template <class C>
+__device__ __forceinline__ typename C::Frag residual(const f32x4 &lo, const f32x4 &hi, const typename C::Frag &f,
+                                                     const f32x4 &slo, const f32x4 &shi) {
+    using OpT = typename C::OpT;
+    typename C::Frag r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        r[e] = (OpT)(lo[e] * slo[e] - (float)f[e]);
+        r[e + 4] = (OpT)(hi[e] * shi[e] - (float)f[e + 4]);
+    }
+    return r;
 }
 
 // Raw 4-element pieces of the next chunk, held in registers while the current one runs:
@@ -522,17 +540,34 @@ __global__ __launch_bounds__(256, 1) void delta_chunk_kernel(DeltaArgs a) {
 #pragma unroll
                 for (int k = 0; k < i; ++k) acc = mma16<C::F32>(ab[i][k], U[k], acc);
                 U[i] = mma16<C::F32>(ab[i][i], acc, f32x4{0.f, 0.f, 0.f, 0.f});
+                if constexpr (!C::F32) {
+                    // the right-hand side enters as fp16 twice: its value and its rounding residual
+                    f32x4 res;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) res[e] = acc[e] - (float)(f16)acc[e];
+                    U[i] = mma16<C::F32>(ab[i][i], res, U[i]);
+                }
             }
         }
         // ---- O += P U, stored
         {
-            Frag uf[2];
+            // U enters as its fp16 value plus the rounding residual (the output is a small
+            // difference of terms of the size of U)
+            const f32x4 one = {1.f, 1.f, 1.f, 1.f};
+            Frag uf[2], ur[2];
 #pragma unroll
-            for (int m = 0; m < 2; ++m) uf[m] = acc_frag<C>(U[2 * m], U[2 * m + 1]);
+            for (int m = 0; m < 2; ++m) {
+                uf[m] = acc_frag<C>(U[2 * m], U[2 * m + 1]);
+                ur[m] = residual<C>(U[2 * m], U[2 * m + 1], uf[m], one, one);
+            }
 #pragma unroll
             for (int m = 0; m < 2; ++m)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) O[i] = mma(ld_frag<C>(sP + (16 * i + c16) * C::RT + 32 * m + 8 * g), uf[m], O[i]);
+                for (int i = 0; i < 4; ++i) {
+                    const Frag pa = ld_frag<C>(sP + (16 * i + c16) * C::RT + 32 * m + 8 * g);
+                    O[i] = mma(pa, uf[m], O[i]);
+                    if constexpr (!C::F32) O[i] = mma(pa, ur[m], O[i]);
+                }
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -548,15 +583,22 @@ __global__ __launch_bounds__(256, 1) void delta_chunk_kernel(DeltaArgs a) {
             for (int i = 0; i < 4; ++i)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) f[i][e] = fexp2(bC - sB[16 * i + 4 * g + e]);
-            Frag ub[2];
+            Frag ub[2], ubr[2];
 #pragma unroll
-            for (int m = 0; m < 2; ++m) ub[m] = acc_frag_rows<C>(U[2 * m], U[2 * m + 1], f[2 * m], f[2 * m + 1]);
+            for (int m = 0; m < 2; ++m) {
+                ub[m] = acc_frag_rows<C>(U[2 * m], U[2 * m + 1], f[2 * m], f[2 * m + 1]);
+                ubr[m] = residual<C>(U[2 * m], U[2 * m + 1], ub[m], f[2 * m], f[2 * m + 1]);
+            }
 #pragma unroll
             for (int r = 0; r < C::NB; ++r) S[r] *= gC;
 #pragma unroll
             for (int m = 0; m < 2; ++m)
 #pragma unroll
-                for (int r = 0; r < C::NB; ++r) S[r] = mma(ld_frag<C>(sKt + (16 * r + c16) * C::RT + 32 * m + 8 * g), ub[m], S[r]);
+                for (int r = 0; r < C::NB; ++r) {
+                    const Frag ka = ld_frag<C>(sKt + (16 * r + c16) * C::RT + 32 * m + 8 * g);
+                    S[r] = mma(ka, ub[m], S[r]);
+                    if constexpr (!C::F32) S[r] = mma(ka, ubr[m], S[r]);
+                }
         }
         barrier();  // B4: the chunk's LDS may be overwritten
     }

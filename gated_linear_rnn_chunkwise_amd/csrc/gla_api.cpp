@@ -85,17 +85,21 @@ int validate(const gla_desc *d) {
 int make_plan(const gla_desc *d, Plan *p) {
     if (d->Dk != 64 && d->Dk != 128 && d->Dk != 256) return GLA_ERR_UNSUPPORTED;
     if (d->Dv % gla::kDvTile != 0 || d->Dv > 4096) return GLA_ERR_UNSUPPORTED;
-    if (d->chunk % gla::kTile != 0 || d->chunk > gla::kMaxChunk) return GLA_ERR_UNSUPPORTED;
+    // Chunks of 16 and 32 tokens run as 64-token tiles: the state is carried per tile, which
+    // is the same map (the chunkwise form is exact for every chunk size).
+    if (d->chunk != 16 && d->chunk != 32 && (d->chunk % gla::kTile != 0 || d->chunk > gla::kMaxChunk))
+        return GLA_ERR_UNSUPPORTED;
+    const int chunk = d->chunk < gla::kTile ? gla::kTile : d->chunk;
     // Kernels address one (batch, head) slice through a buffer resource with 32-bit byte
     // offsets, and prefetch up to two chunks past the segment end.
     if ((int64_t(d->L) + 2 * gla::kMaxChunk) * std::max(d->Dk, d->Dv) * 4 >= (int64_t(1) << 32))
         return GLA_ERR_UNSUPPORTED;
     const bool f32 = d->in_dtype == GLA_DTYPE_F32;
     const bool ch = d->gate_kind == GLA_GATE_CHANNEL;
-    p->nt = d->chunk / gla::kTile;
+    p->nt = chunk / gla::kTile;
     // Without tile pairs the state is advanced tile by tile: the kernels walk 64-token chunks.
     p->knt = (d->flags & GLA_FLAG_TILE_PAIRS) ? p->nt : 1;
-    p->nc = (d->L + d->chunk - 1) / d->chunk;
+    p->nc = (d->L + chunk - 1) / chunk;
     p->ndv = d->Dv / gla::kDvTile;
     const int64_t bh = int64_t(d->B) * d->H;
     const int64_t wg1 = bh * p->ndv;
@@ -111,7 +115,7 @@ int make_plan(const gla_desc *d, Plan *p) {
     }
     p->seg_chunks = sc;
     p->nseg = (p->nc + sc - 1) / sc;
-    p->seg_len = sc * d->chunk;
+    p->seg_len = sc * chunk;
     // Segment boundary states are sums of sub-segment states, computed by more workgroups
     // than there are boundaries: nsub (sub-segments of a segment, whose tile counts differ
     // by at most one) brings the state grid nearest to its target.

@@ -98,7 +98,7 @@ enum gla_flag {
 /* Full description of one forward call. */
 typedef struct gla_desc {
     int32_t B, H, L, Dk, Dv; /* batch, heads, sequence length, key and value head dims */
-    int32_t chunk;           /* chunk size C of the chunkwise algorithm */
+    int32_t chunk;           /* chunk size C of the chunkwise algorithm (16, 32 or k * 64) */
     int32_t in_dtype;        /* enum gla_dtype of q, k, v */
     int32_t gate_kind;       /* enum gla_gate */
     const void *q;           /* [B, H, L, Dk] in_dtype */
@@ -142,8 +142,9 @@ int gla_fwd(const void *q, const void *k, const void *v, const float *log_alpha,
  * length and caller workspace.  When d->workspace is NULL and scratch is needed it is
  * allocated and freed stream-ordered on `stream`; otherwise d->workspace_bytes must be at
  * least what gla_workspace_size reports, else GLA_ERR_WORKSPACE.
- * Support matrix (else GLA_ERR_UNSUPPORTED): chunk a multiple of 64 in [64, 512];
- * Dk in {64, 128, 256}; Dv a multiple of 64 up to 4096; L >= 1 with
+ * Support matrix (else GLA_ERR_UNSUPPORTED): chunk 16, 32, or a multiple of 64 in
+ * [64, 512] (chunks of 16 and 32 tokens run as 64-token tiles, the same map, and seg_chunks
+ * then counts 64-token tiles); Dk in {64, 128, 256}; Dv a multiple of 64 up to 4096; L >= 1 with
  * (L + 1024) * max(Dk, Dv) * 4 < 2^32 (one (batch, head) slice is addressed with 32-bit
  * byte offsets, which allows L up to about 1M for Dv = 1024); and the operand tiles of
  * one workgroup must fit the 160 KB of LDS of a compute unit.  That last rule only bites

@@ -116,7 +116,7 @@ def test_headline_entry_point_validates(lib):
     assert lib.gla_fwd(A, A, A, A, A, None, 1, 1, 64, 96, 128, 64, None) == gla.GLA_ERR_UNSUPPORTED
 
 
-@pytest.mark.parametrize("kw", [dict(Dk=96), dict(Dk=32), dict(Dv=96), dict(Dv=32), dict(chunk=32), dict(chunk=96),
+@pytest.mark.parametrize("kw", [dict(Dk=96), dict(Dk=32), dict(Dv=96), dict(Dv=32), dict(chunk=48), dict(chunk=96),
                                 dict(chunk=1024), dict(Dv=4160), dict(B=1, H=1, L=(1 << 23) - 1024)])
 def test_unsupported_shapes(lib, kw):
     d = desc(**kw)
@@ -404,3 +404,12 @@ def test_delta_binding_rejects_mismatched_shapes(lib, name, shape):
     a[name] = torch.zeros(shape)
     with pytest.raises(ValueError, match=name):
         gla.delta_fwd(a["q"], a["k"], a["v"], a["beta"], a["log_alpha"], initial_state=a["initial_state"])
+
+
+@pytest.mark.parametrize("chunk", [16, 32])
+def test_small_chunks_run_as_64_token_tiles(lib, chunk):
+    # chunks of 16 and 32 tokens are accepted and planned as 64-token tiles (the same map)
+    p = gla.plan(desc(chunk=chunk, L=1000))
+    q = gla.plan(desc(chunk=64, L=1000))
+    assert (p.tiles_per_chunk, p.n_seg, p.grid_out) == (1, q.n_seg, q.grid_out)
+    assert p.tiles_per_chunk == 1

@@ -88,6 +88,19 @@ def test_small_shapes(gpu_lib, dtype, gate, ig, Dk, Dv, chunk, L):
     check(w, fin, rfin, "final_state")
 
 
+@pytest.mark.parametrize("dtype,gate,ig", [("bf16", "channel", False), ("bf16", "head", True), ("f32", "none", False),
+                                          ("f32", "channel", True)])
+@pytest.mark.parametrize("chunk", [16, 32])
+def test_small_chunk_sizes(gpu_lib, dtype, gate, ig, chunk):
+    # chunks of 16 and 32 tokens (run as 64-token tiles) against the oracle, ragged tail
+    w = gin.custom(2, 2, 333, 128 if dtype == "bf16" else 64, 128, chunk, dtype=dtype, gate=gate, input_gate=ig)
+    d = gin.make_inputs(w, seed=chunk)
+    out, fin = run_gpu(gpu_lib, d, w)
+    ref, rfin = run_oracle(d, w)
+    check(w, out, ref)
+    check(w, fin, rfin, "final_state")
+
+
 @pytest.mark.parametrize("dtype,gate,ig,Dk,Dv,chunk", [c for c in SMALL if c[5] > 64])
 @pytest.mark.parametrize("L", [100, 333])
 def test_small_shapes_tile_pairs(gpu_lib, dtype, gate, ig, Dk, Dv, chunk, L):
