@@ -633,7 +633,7 @@ def main():
                    "gate": w.gate, "input_gate": w.input_gate, "in_dtype": w.dtype,
                    "matrix_operands": "fp16 from bf16" if w.dtype == "bf16" else "fp32",
                    "accumulate": "fp32", "out_dtype": "fp32", "n_seg": plan.n_seg,
-                   "tile_pairs": bool(plan.tile_pairs),
+                   "tile_pairs": bool(plan.tile_pairs), "executed_chunk": exec_chunk,
                    "workgroups": plan.grid_out},
         "head_tokens_per_s": value * w.H,
         "tflops": round(tflops, 2),
