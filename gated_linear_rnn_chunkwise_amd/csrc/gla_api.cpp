@@ -29,6 +29,8 @@ size_t bwd_absmax_parts(int L, int Dv, int Dk, bool dfin);
 hipError_t bwd_dout16(const float *dout, const float *dfin, float *part, uint32_t *mx, _Float16 *fwd, _Float16 *rev,
                       int BH, int L, int Dv, int Dk, hipStream_t st);
 hipError_t bwd_scale(const float *src, const uint32_t *mx, float *dst, int BH, size_t m, hipStream_t st);
+hipError_t bwd_copy2d(const void *src, size_t src_stride, void *dst, size_t dst_stride, size_t rows, size_t row_bytes,
+                      hipStream_t st);
 hipError_t bwd_finish(const gla_bwd_desc &d, const float *oA, const float *oB, float *g, const float *finA,
                       const float *finC, const float *dfT, float *part, const uint32_t *mx, hipStream_t st);
 constexpr int kH16Q = 1, kH16K = 2, kH16V = 4;  // fp16 operand bits of launch_forward
@@ -210,6 +212,7 @@ struct OutMapArgs {
     const float *li = nullptr;
     const uint32_t *mx = nullptr;
     int in_rev = 0;  // the pass reads q, k, v in reversed token order
+    int acc = 0;     // add to the output instead of storing
 };
 
 // The forward pass; h16 marks operands given as fp16 instead of bf16 and om maps the output
@@ -263,6 +266,7 @@ int fwd_run(const gla_desc *d, int h16, void *stream, const OutMapArgs &om = Out
     a.out_li = om.li;
     a.out_mx = om.mx;
     a.in_rev = om.in_rev;
+    a.out_acc = om.acc;
 
     const hipError_t err = gla::launch_forward(a, d->in_dtype == GLA_DTYPE_F32, h16, d->Dk, s);
     if (owned) (void)hipFreeAsync(ws, s);
@@ -374,6 +378,14 @@ namespace {
 
 bool bwd_dim_ok(int x) { return x == 64 || x == 128 || x == 256; }
 
+// Dv = 512 with bf16 inputs and a scalar gate (or none): the dk and dq passes, whose key
+// dimension is Dv, run over the two 256-column halves of the values (the gradient of the
+// state splits by value columns) and their outputs add.
+constexpr int kDvHalf = 256;
+bool bwd_split_dv(const gla_bwd_desc *d) {
+    return d->Dv == 2 * kDvHalf && d->in_dtype == GLA_DTYPE_BF16 && d->gate_kind != GLA_GATE_CHANNEL;
+}
+
 int validate_bwd(const gla_bwd_desc *d) {
     if (!d || !d->q || !d->k || !d->v || !d->dout || !d->dq || !d->dk || !d->dv) return GLA_ERR_INVALID_ARG;
     if (d->B <= 0 || d->H <= 0 || d->L <= 0 || d->Dk <= 0 || d->Dv <= 0) return GLA_ERR_INVALID_ARG;
@@ -391,7 +403,7 @@ int validate_bwd(const gla_bwd_desc *d) {
     const int64_t bh = int64_t(d->B) * d->H;
     if (bh > (int64_t(1) << 24)) return GLA_ERR_INVALID_ARG;
     if (bh * d->L > lim / std::max(d->Dk, d->Dv)) return GLA_ERR_INVALID_ARG;
-    if (!bwd_dim_ok(d->Dk) || !bwd_dim_ok(d->Dv)) return GLA_ERR_UNSUPPORTED;
+    if (!bwd_dim_ok(d->Dk) || !(bwd_dim_ok(d->Dv) || bwd_split_dv(d))) return GLA_ERR_UNSUPPORTED;
     // one (batch, head) slice is addressed with 32-bit byte offsets, as in the forward pass
     if ((int64_t(d->L) + 2 * gla::kMaxChunk) * std::max(d->Dk, d->Dv) * 4 >= (int64_t(1) << 32))
         return GLA_ERR_UNSUPPORTED;
@@ -429,6 +441,7 @@ bool chan_dv_fast(const gla_bwd_desc *d) { return d->in_dtype == GLA_DTYPE_BF16 
 
 struct BwdPlan {
     size_t chs, rq, rk, rv, rdo, fdo, mx, mxp, s0A, lar, oA, oB, finA, finC, s0T, dfT, g, part, fws, total;
+    size_t vsl, dsl, s0h, finH;  // Dv split: value and output-gradient halves, a state half, a final-state half
     size_t fws_bytes;
 };
 
@@ -494,14 +507,20 @@ int bwd_plan(const gla_bwd_desc *d, BwdPlan *p) {
     p->dfT = d->dfinal_state ? take(bh * Dk * Dv * 4) : 0;
     p->g = gate ? take(bh * L * 4) : 0;
     p->part = take(bh * 4);
+    const bool split = bwd_split_dv(d);
+    const int kd = split ? kDvHalf : d->Dv;  // key dimension of the dk and dq passes
+    p->vsl = split ? take(bh * L * kDvHalf * 2) : 0;
+    p->dsl = split ? take(bh * L * kDvHalf * 2) : 0;
+    p->s0h = split ? take(bh * kDvHalf * Dk * 4) : 0;
+    p->finH = split ? take(bh * kDvHalf * Dk * 4) : 0;
     // the forward passes run one after the other on the stream and share one workspace
     const void *x = reinterpret_cast<const void *>(uintptr_t(256));
     float *y = reinterpret_cast<float *>(uintptr_t(256));
     const int rgate = gate ? GLA_GATE_HEAD : GLA_GATE_NONE;
     const float *rla = gate ? y : nullptr;
     gla_desc f[3] = {bwd_pass_desc(d, d->Dk, d->Dv, x, x, x, rgate, rla, nullptr, nullptr, y, y),
-                     bwd_pass_desc(d, d->Dv, d->Dk, x, x, x, rgate, rla, nullptr, nullptr, y, nullptr),
-                     bwd_pass_desc(d, d->Dv, d->Dk, x, x, x, d->gate_kind, d->log_alpha, d->log_ig, nullptr, y, y)};
+                     bwd_pass_desc(d, kd, d->Dk, x, x, x, rgate, rla, nullptr, nullptr, y, nullptr),
+                     bwd_pass_desc(d, kd, d->Dk, x, x, x, d->gate_kind, d->log_alpha, d->log_ig, nullptr, y, y)};
     size_t fw = 0;
     for (const gla_desc &fd : f) {
         size_t n = 0;
@@ -634,14 +653,43 @@ int gla_bwd(const gla_bwd_desc *d, void *stream) {
     // dv (reversed; its final state is the gradient of the state after token 0)
     fwd(bwd_pass_desc(d, Dk, Dv, rk, rq, rdo, rgate, rla, nullptr, s0A, bf ? d->dv : F(p.oA), F(p.finA)), gla::kH16V,
         om_rev);
-    // dk (reversed, keys and values exchanged)
-    fwd(bwd_pass_desc(d, Dv, Dk, rv, rdo, rq, rgate, rla, nullptr, d->dfinal_state ? F(p.dfT) : nullptr,
-                      bf ? d->dk : F(p.oB), nullptr),
-        gla::kH16K, om_rev);
-    // dq (keys and values exchanged; its final state is the forward final state, transposed)
-    fwd(bwd_pass_desc(d, Dv, Dk, fdo, d->v, d->k, d->gate_kind, d->log_alpha, d->log_ig,
-                      d->initial_state ? F(p.s0T) : nullptr, d->dq, F(p.finC)),
-        gla::kH16Q, om_q);
+    if (!bwd_split_dv(d)) {
+        // dk (reversed, keys and values exchanged)
+        fwd(bwd_pass_desc(d, Dv, Dk, rv, rdo, rq, rgate, rla, nullptr, d->dfinal_state ? F(p.dfT) : nullptr,
+                          bf ? d->dk : F(p.oB), nullptr),
+            gla::kH16K, om_rev);
+        // dq (keys and values exchanged; its final state is the forward final state, transposed)
+        fwd(bwd_pass_desc(d, Dv, Dk, fdo, d->v, d->k, d->gate_kind, d->log_alpha, d->log_ig,
+                          d->initial_state ? F(p.s0T) : nullptr, d->dq, F(p.finC)),
+            gla::kH16Q, om_q);
+    } else {
+        // the same two passes over each 256-column half of the values (and of the output
+        // gradient): G splits by value columns, so dk and dq are the sums of the halves'
+        // outputs, and the dq pass's final state is the half's rows of the transposed final state
+        const size_t rows = size_t(BH) * L, half_bytes = size_t(kDvHalf) * 2, st_half = size_t(kDvHalf) * Dk * 4;
+        for (int hh = 0; hh < 2 && rc == GLA_OK; ++hh) {
+            ok(gla::bwd_copy2d(static_cast<const char *>(d->v) + hh * half_bytes, size_t(Dv) * 2, V(p.vsl), half_bytes,
+                               rows, half_bytes, s));
+            ok(gla::bwd_copy2d(static_cast<const char *>(fdo) + hh * half_bytes, size_t(Dv) * 2, V(p.dsl), half_bytes,
+                               rows, half_bytes, s));
+            if (d->dfinal_state)
+                ok(gla::bwd_copy2d(reinterpret_cast<const char *>(F(p.dfT)) + hh * st_half, size_t(Dv) * Dk * 4,
+                                   V(p.s0h), st_half, size_t(BH), st_half, s));
+            OutMapArgs om_k = om_rev, om_d = om_q;
+            om_k.acc = om_d.acc = hh;
+            fwd(bwd_pass_desc(d, kDvHalf, Dk, V(p.vsl), V(p.dsl), rq, rgate, rla, nullptr,
+                              d->dfinal_state ? F(p.s0h) : nullptr, d->dk, nullptr),
+                gla::kH16K, om_k);
+            if (d->initial_state)
+                ok(gla::bwd_copy2d(reinterpret_cast<const char *>(F(p.s0T)) + hh * st_half, size_t(Dv) * Dk * 4,
+                                   V(p.s0h), st_half, size_t(BH), st_half, s));
+            fwd(bwd_pass_desc(d, kDvHalf, Dk, V(p.dsl), V(p.vsl), d->k, d->gate_kind, d->log_alpha, d->log_ig,
+                              d->initial_state ? F(p.s0h) : nullptr, d->dq, F(p.finH)),
+                gla::kH16Q, om_d);
+            ok(gla::bwd_copy2d(V(p.finH), st_half, reinterpret_cast<char *>(F(p.finC)) + hh * st_half,
+                               size_t(Dv) * Dk * 4, size_t(BH), st_half, s));
+        }
+    }
     if (rc == GLA_OK)
         ok(gla::bwd_finish(*d, bf ? nullptr : F(p.oA), bf ? nullptr : F(p.oB),
                            (gate && d->dlog_alpha) ? F(p.g) : nullptr, F(p.finA), F(p.finC),

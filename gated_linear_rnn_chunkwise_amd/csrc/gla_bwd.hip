@@ -346,9 +346,32 @@ __global__ __launch_bounds__(256) void bwd_head_sum_kernel(const float *part, fl
     dla[h] = s;
 }
 
+// Strided 2-D copy of 16-byte units: row r of n16 units from src + r * ss to dst + r * ds
+// (strides in 16-byte units).  Splits a pass over value columns into halves and places the
+// halves' states.
+__global__ __launch_bounds__(256) void bwd_copy2d_kernel(const uint4 *src, size_t ss, uint4 *dst, size_t ds, size_t n16,
+                                                        size_t total) {
+    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= total) return;
+    const size_t r = i / n16, c = i % n16;
+    dst[r * ds + c] = src[r * ss + c];
+}
+
 inline unsigned nblk(size_t n, unsigned per) { return (unsigned)((n + per - 1) / per); }
 
 }  // namespace
+
+hipError_t bwd_copy2d(const void *src, size_t src_stride, void *dst, size_t dst_stride, size_t rows, size_t row_bytes,
+                      hipStream_t st) {
+    if ((src_stride | dst_stride | row_bytes) % 16 != 0 || (reinterpret_cast<uintptr_t>(src) & 15) != 0 ||
+        (reinterpret_cast<uintptr_t>(dst) & 15) != 0)
+        return hipErrorInvalidValue;
+    const size_t n16 = row_bytes / 16, total = rows * n16;
+    if (total == 0) return hipSuccess;
+    hipLaunchKernelGGL(bwd_copy2d_kernel, dim3(nblk(total, 256)), dim3(256), 0, st, reinterpret_cast<const uint4 *>(src),
+                       src_stride / 16, reinterpret_cast<uint4 *>(dst), dst_stride / 16, n16, total);
+    return hipGetLastError();
+}
 
 hipError_t bwd_reverse(const void *src, int dt, float *dst, int BH, int L, int D, hipStream_t st) {
     const size_t total = (size_t)BH * L * D;

@@ -291,10 +291,11 @@ __device__ __forceinline__ void store_staged(const float *sO, rsrc_t out, int T0
 }
 
 // The same for the backward pass's instances: row t goes to row L-1-t when rev, times
-// oinv and (has_li) times exp of the destination row's log input gate; rows past the
-// sequence end are not stored.
+// oinv and (has_li) times exp of the destination row's log input gate, added to what the
+// output holds when acc; rows past the sequence end are not stored.
 __device__ __forceinline__ void store_staged_map(const float *sO, rsrc_t out, rsrc_t oli, int T0, int L, int Dv,
-                                                 int dv0, int cw, int lane, bool rev, bool has_li, float oinv) {
+                                                 int dv0, int cw, int lane, bool rev, bool has_li, float oinv,
+                                                 bool acc) {
     const int c4 = lane & 15;
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
@@ -305,9 +306,9 @@ __device__ __forceinline__ void store_staged_map(const float *sO, rsrc_t out, rs
         if (has_li) f *= fexp2(__uint_as_float(bld32(oli, (uint32_t)dst * 4u)) * kLog2e);
         f32x4 x = lds_ld<f32x4>(sO + row * 68 + 4 * c4);
         x *= f;
-        if (t < L)
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), out,
-                                                   (int)(((uint32_t)dst * Dv + dv0 + 4 * c4) * 4u), 0, 0);
+        const uint32_t off = ((uint32_t)dst * Dv + dv0 + 4 * c4) * 4u;
+        if (acc && t < L) x += __builtin_bit_cast(f32x4, bld128(out, off));
+        if (t < L) __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), out, (int)off, 0, 0);
     }
 }
 
@@ -315,7 +316,7 @@ __device__ __forceinline__ void store_staged_map(const float *sO, rsrc_t out, rs
 struct OutMap {
     rsrc_t li;
     float inv;
-    bool rev, has_li;
+    bool rev, has_li, acc;
 };
 __device__ __forceinline__ OutMap make_out_map(const KArgs &a, int bh) {
     OutMap m;
@@ -323,6 +324,7 @@ __device__ __forceinline__ OutMap make_out_map(const KArgs &a, int bh) {
     m.has_li = a.out_li != nullptr;
     m.li = m.has_li ? make_rsrc(a.out_li + (size_t)bh * a.L, (uint64_t)a.L * 4) : make_rsrc(a.out, 0);
     m.inv = a.out_mx ? 1.f / grad_scale_of(a.out_mx[bh]) : 1.f;
+    m.acc = a.out_acc != 0;
     return m;
 }
 
@@ -1850,7 +1852,7 @@ __global__ __launch_bounds__(512, 1) void chunk_output_ws_kernel(KArgs a) {
         lds_barrier();  // B2
         if constexpr (C::H16 != 0)
             store_staged_map(reinterpret_cast<const float *>(smem + lp.ostage), rs.out, om.li, T0, L, Dv, dv0, cw,
-                             lane, om.rev, om.has_li, om.inv);
+                             lane, om.rev, om.has_li, om.inv, om.acc);
         else
             store_staged(reinterpret_cast<const float *>(smem + lp.ostage), rs.out, T0, Dv, dv0, cw, lane);
     }
@@ -2214,7 +2216,7 @@ __global__ __launch_bounds__(512, 1) void chunk_output_sg_kernel(KArgs a) {
         lds_barrier();  // B2
         if constexpr (C::H16 != 0)
             store_staged_map(reinterpret_cast<const float *>(smem + lp.ostage), rs.out, om.li, T0, L, Dv, dv0, cw,
-                             lane, om.rev, om.has_li, om.inv);
+                             lane, om.rev, om.has_li, om.inv, om.acc);
         else
             store_staged(reinterpret_cast<const float *>(smem + lp.ostage), rs.out, T0, Dv, dv0, cw, lane);
     }

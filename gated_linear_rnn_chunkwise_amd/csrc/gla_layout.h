@@ -270,6 +270,8 @@ struct KArgs {
     const uint32_t *out_mx;
     int in_rev;       // token t reads q, k, v row L-1-t and a per-channel gate's row L-t (zero
                       // for t = 0); scalar gates are given in the pass's token order
+    int out_acc;      // backward-pass instances: add the mapped rows to the output instead of
+                      // storing them (a pass split over value columns sums its halves)
 };
 
 #if defined(__HIPCC__)

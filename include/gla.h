@@ -254,8 +254,10 @@ typedef struct gla_bwd_desc {
 } gla_bwd_desc;
 
 /* Backward pass.  Support matrix (else GLA_ERR_UNSUPPORTED): every gate kind; Dk and Dv in
- * {64, 128, 256}; L as for gla_fwd_ex.  Validation and asynchrony as for gla_fwd_ex.
- * Returns a gla_status. */
+ * {64, 128, 256}; also Dv = 512 with bf16 inputs and a gate other than per-channel (the dk
+ * and dq passes, whose key dimension is Dv, then run over the two 256-column halves of v and
+ * dout and add: the state gradient splits by value columns); L as for gla_fwd_ex.
+ * Validation and asynchrony as for gla_fwd_ex.  Returns a gla_status. */
 int gla_bwd(const gla_bwd_desc *d, void *stream);
 
 /* Scratch bytes gla_bwd needs for `d` (no HIP call).  Returns a gla_status. */

@@ -271,7 +271,8 @@ def test_bwd_invalid_arguments(lib, kw):
     assert bstatus(lib, bdesc(**kw))[0] == gla.GLA_ERR_INVALID_ARG
 
 
-@pytest.mark.parametrize("kw", [dict(Dk=100), dict(Dv=512), dict(Dk=32), dict(gate_kind=gla.GATE_CHANNEL, Dv=96),
+@pytest.mark.parametrize("kw", [dict(Dk=100), dict(Dv=1024), dict(Dv=512, in_dtype=gla.DTYPE_F32), dict(Dk=32),
+                                dict(gate_kind=gla.GATE_CHANNEL, Dv=96),
                                 dict(B=1, H=1, L=1 << 22, Dk=256),  # a slice past 32-bit byte offsets
                                 dict(B=1, H=1, L=1 << 22, Dk=256, gate_kind=gla.GATE_CHANNEL)])
 def test_bwd_unsupported(lib, kw):
@@ -413,3 +414,28 @@ def test_small_chunks_run_as_64_token_tiles(lib, chunk):
     q = gla.plan(desc(chunk=64, L=1000))
     assert (p.tiles_per_chunk, p.n_seg, p.grid_out) == (1, q.n_seg, q.grid_out)
     assert p.tiles_per_chunk == 1
+
+
+def bwd_desc(**kw):
+    d = gla.GlaBwdDesc()
+    base = dict(B=2, H=3, L=100, Dk=256, Dv=512, in_dtype=gla.DTYPE_BF16, gate_kind=gla.GATE_HEAD, q=A, k=A, v=A,
+                log_alpha=A, log_ig=A, initial_state=None, dout=A, dfinal_state=A, dq=A, dk=A, dv=A,
+                dlog_alpha=A, dlog_ig=A, dinitial_state=A, workspace=None, workspace_bytes=0)
+    base.update(kw)
+    for key, val in base.items():
+        setattr(d, key, val)
+    return d
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(), gla.GLA_OK), (dict(gate_kind=gla.GATE_NONE, log_alpha=None, dlog_alpha=None), gla.GLA_OK),
+    (dict(gate_kind=gla.GATE_HEAD_CONST), gla.GLA_OK), (dict(Dk=64), gla.GLA_OK),
+    (dict(in_dtype=gla.DTYPE_F32), gla.GLA_ERR_UNSUPPORTED), (dict(gate_kind=gla.GATE_CHANNEL), gla.GLA_ERR_UNSUPPORTED),
+    (dict(Dv=1024), gla.GLA_ERR_UNSUPPORTED), (dict(Dv=384), gla.GLA_ERR_UNSUPPORTED),
+])
+def test_backward_dv512_support(lib, kw, status):
+    # Dv = 512 is supported for bf16 inputs with a scalar gate or none (value-column halves)
+    n = ctypes.c_size_t(0)
+    assert lib.gla_bwd_workspace_size(ctypes.byref(bwd_desc(**kw)), ctypes.byref(n)) == status
+    if status == gla.GLA_OK:
+        assert n.value > 0

@@ -125,6 +125,36 @@ def test_backward_small_shapes(gpu_lib, dtype, gate, ig, Dk, Dv, L):
     check_all(got, ref, w.name, dtype, d, gate)
 
 
+SPLIT_CASES = []
+for gate, ig in (("none", False), ("head", True), ("head", False), ("head_const", False)):
+    for Dk in (64, 128, 256):
+        SPLIT_CASES.append((gate, ig, Dk))
+
+
+@pytest.mark.parametrize("gate,ig,Dk", SPLIT_CASES)
+@pytest.mark.parametrize("L", [1, 70, 333])
+def test_backward_dv512(gpu_lib, gate, ig, Dk, L):
+    # Dv = 512 (the mLSTM head shape has Dk = 256): the dk and dq passes run over the two
+    # 256-column halves of v and dout and add their outputs
+    w = gin.custom(2, 2, L, Dk, 512, 64, dtype="bf16", gate=gate, input_gate=ig, scale_dim=256)
+    d = gin.make_inputs(w, seed=L + Dk + 7)
+    dout, s0, df = grads_in(w, L + 2, with_s0=(L != 70), with_df=(L != 333))
+    got = run(gpu_lib, w, d, dout, s0, df)
+    ref = oracle.backward(d["q"], d["k"], d["v"], dout, gate, d["log_alpha"], d["log_ig"], s0, df)
+    check_all(got, ref, w.name, "bf16", d, gate)
+
+
+def test_backward_mlstm_head_shape_long(gpu_lib):
+    # the mLSTM workload's head shape and gates (Dk 256, Dv 512, per-token forget gate and
+    # input gate) at length 4096 on four (batch, head) slices, every gradient compared whole
+    w = gin.WORKLOADS["mlstm_sig_bf16_B8H8L8192"].with_(B=2, H=2, L=4096)
+    d = gin.make_inputs(w, seed=3)
+    dout, s0, df = grads_in(w, 3, True, True)
+    got = run(gpu_lib, w, d, dout, s0, df)
+    ref = oracle.backward(d["q"], d["k"], d["v"], dout, "head", d["log_alpha"], d["log_ig"], s0, df)
+    check_all(got, ref, "mlstm head shape L4096", "bf16", d, "head")
+
+
 def test_backward_strong_decay(gpu_lib):
     # per head and token gate near zero on some tokens: the reversed passes see the same decays
     w = gin.custom(1, 2, 150, 64, 64, 64, dtype="bf16", gate="head", input_gate=True)
