@@ -464,10 +464,16 @@ __global__ __launch_bounds__(256, 1) void delta_chunk_kernel(DeltaArgs a) {
             for (int i = 0; i < 4; ++i) O[i] = ks[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int m = 0; m < C::NM; ++m) {
+                Frag qa[4], ka[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    O[i] = mma(ld_frag<C>(sQ + (16 * i + c16) * C::RQ + 32 * m + 8 * g), sf[m], O[i]);
-                    ks[i] = mma(ld_frag<C>(sK + (16 * i + c16) * C::RQ + 32 * m + 8 * g), sf[m], ks[i]);
+                    qa[i] = ld_frag<C>(sQ + (16 * i + c16) * C::RQ + 32 * m + 8 * g);
+                    ka[i] = ld_frag<C>(sK + (16 * i + c16) * C::RQ + 32 * m + 8 * g);
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    O[i] = mma(qa[i], sf[m], O[i]);
+                    ks[i] = mma(ka[i], sf[m], ks[i]);
                 }
             }
 #pragma unroll
@@ -541,11 +547,12 @@ __global__ __launch_bounds__(256, 1) void delta_chunk_kernel(DeltaArgs a) {
                 for (int k = 0; k < i; ++k) acc = mma16<C::F32>(ab[i][k], U[k], acc);
                 U[i] = mma16<C::F32>(ab[i][i], acc, f32x4{0.f, 0.f, 0.f, 0.f});
                 if constexpr (!C::F32) {
-                    // the right-hand side enters as fp16 twice: its value and its rounding residual
+                    // the right-hand side enters as fp16 twice: its value and its rounding
+                    // residual (an independent product, added after)
                     f32x4 res;
 #pragma unroll
                     for (int e = 0; e < 4; ++e) res[e] = acc[e] - (float)(f16)acc[e];
-                    U[i] = mma16<C::F32>(ab[i][i], res, U[i]);
+                    U[i] += mma16<C::F32>(ab[i][i], res, f32x4{0.f, 0.f, 0.f, 0.f});
                 }
             }
         }
@@ -560,14 +567,21 @@ __global__ __launch_bounds__(256, 1) void delta_chunk_kernel(DeltaArgs a) {
                 uf[m] = acc_frag<C>(U[2 * m], U[2 * m + 1]);
                 ur[m] = residual<C>(U[2 * m], U[2 * m + 1], uf[m], one, one);
             }
+            Frag pa[4][2];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int m = 0; m < 2; ++m) pa[i][m] = ld_frag<C>(sP + (16 * i + c16) * C::RT + 32 * m + 8 * g);
 #pragma unroll
             for (int m = 0; m < 2; ++m)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const Frag pa = ld_frag<C>(sP + (16 * i + c16) * C::RT + 32 * m + 8 * g);
-                    O[i] = mma(pa, uf[m], O[i]);
-                    if constexpr (!C::F32) O[i] = mma(pa, ur[m], O[i]);
-                }
+                for (int i = 0; i < 4; ++i) O[i] = mma(pa[i][m], uf[m], O[i]);
+            if constexpr (!C::F32) {
+#pragma unroll
+                for (int m = 0; m < 2; ++m)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) O[i] = mma(pa[i][m], ur[m], O[i]);
+            }
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -592,13 +606,17 @@ __global__ __launch_bounds__(256, 1) void delta_chunk_kernel(DeltaArgs a) {
 #pragma unroll
             for (int r = 0; r < C::NB; ++r) S[r] *= gC;
 #pragma unroll
-            for (int m = 0; m < 2; ++m)
+            for (int m = 0; m < 2; ++m) {
+                Frag ka[C::NB];
 #pragma unroll
-                for (int r = 0; r < C::NB; ++r) {
-                    const Frag ka = ld_frag<C>(sKt + (16 * r + c16) * C::RT + 32 * m + 8 * g);
-                    S[r] = mma(ka, ub[m], S[r]);
-                    if constexpr (!C::F32) S[r] = mma(ka, ubr[m], S[r]);
+                for (int r = 0; r < C::NB; ++r) ka[r] = ld_frag<C>(sKt + (16 * r + c16) * C::RT + 32 * m + 8 * g);
+#pragma unroll
+                for (int r = 0; r < C::NB; ++r) S[r] = mma(ka[r], ub[m], S[r]);
+                if constexpr (!C::F32) {
+#pragma unroll
+                    for (int r = 0; r < C::NB; ++r) S[r] = mma(ka[r], ubr[m], S[r]);
                 }
+            }
         }
         barrier();  // B4: the chunk's LDS may be overwritten
     }
