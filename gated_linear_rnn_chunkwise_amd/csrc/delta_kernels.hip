@@ -264,26 +264,27 @@ __device__ __forceinline__ typename C::Piece ld_piece(rsrc_t r, uint32_t off) {
     else return __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0);
 }
 
+// The next chunk's loads are issued in three groups (q rows, k rows, then v, beta and the
+// gate) at different points of the current chunk, so that their issue overlaps the work in
+// between instead of stalling the waves in one block.
 template <class C>
-__device__ __forceinline__ void prefetch(Pref<C> &pf, rsrc_t rq, rsrc_t rk, rsrc_t rv, rsrc_t rb, rsrc_t rla,
-                                         uint32_t gstride, int T0, int tid, int dv0, int Dv) {
+__device__ __forceinline__ void prefetch_rows(typename C::Piece (&dst)[C::QPT][4], rsrc_t r, int T0, int tid) {
     const int c = tid % C::NP;
 #pragma unroll
     for (int j = 0; j < C::QPT; ++j) {
         const int a = tid / C::NP + j * C::QSTEP;
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
-            const uint32_t off = ((uint32_t)(T0 + 4 * a + tt) * C::DK + 4 * c) * C::IB;
-            pf.q[j][tt] = ld_piece<C>(rq, off);
-            pf.k[j][tt] = ld_piece<C>(rk, off);
-        }
-    }
-    {
-        const int a = tid >> 4, cv = tid & 15;
-#pragma unroll
         for (int tt = 0; tt < 4; ++tt)
-            pf.v[tt] = ld_piece<C>(rv, ((uint32_t)(T0 + 4 * a + tt) * Dv + dv0 + 4 * cv) * C::IB);
+            dst[j][tt] = ld_piece<C>(r, ((uint32_t)(T0 + 4 * a + tt) * C::DK + 4 * c) * C::IB);
     }
+}
+template <class C>
+__device__ __forceinline__ void prefetch_rest(Pref<C> &pf, rsrc_t rv, rsrc_t rb, rsrc_t rla, uint32_t gstride,
+                                              int T0, int tid, int dv0, int Dv) {
+    const int a = tid >> 4, cv = tid & 15;
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+        pf.v[tt] = ld_piece<C>(rv, ((uint32_t)(T0 + 4 * a + tt) * Dv + dv0 + 4 * cv) * C::IB);
     pf.beta = bld_f32(rb, (uint32_t)(T0 + (tid & 63)) * 4u);
     pf.la = bld_f32(rla, (uint32_t)(T0 + (tid & 63)) * gstride);
 }
@@ -401,13 +402,15 @@ __global__ __launch_bounds__(256, 1) void delta_chunk_kernel(DeltaArgs a) {
     }
 
     Pref<C> pf;
-    prefetch<C>(pf, rq, rk, rv, rb, rla, gstride, 0, tid, dv0, Dv);
+    prefetch_rows<C>(pf.q, rq, 0, tid);
+    prefetch_rows<C>(pf.k, rk, 0, tid);
+    prefetch_rest<C>(pf, rv, rb, rla, gstride, 0, tid, dv0, Dv);
     const int nc = (L + kC - 1) / kC;
     for (int ci = 0; ci < nc; ++ci) {
         const int T0 = ci * kC;
         stage<C>(pf, smem, lp, tid, lane, w, T0 + lane < L);
         barrier();  // B1: chunk staged
-        prefetch<C>(pf, rq, rk, rv, rb, rla, gstride, T0 + kC, tid, dv0, Dv);
+        prefetch_rows<C>(pf.q, rq, T0 + kC, tid);
 
         // ---- products that do not need the triangular solve: K K^T of row block w (-> A,
         // strictly lower, decayed, times beta of the row) and Q K^T of row block 3-w (-> P,
@@ -452,6 +455,7 @@ __global__ __launch_bounds__(256, 1) void delta_chunk_kernel(DeltaArgs a) {
                 }
             }
         }
+        prefetch_rows<C>(pf.k, rk, T0 + kC, tid);
         // the state's share of the output, diag(g) Q S0, and the right-hand side of the
         // triangular system, R = diag(beta) (V - diag(g) K S0), for this wave's 16 columns
         f32x4 O[4], R[4];
@@ -527,6 +531,7 @@ __global__ __launch_bounds__(256, 1) void delta_chunk_kernel(DeltaArgs a) {
             for (int e = 0; e < 4; ++e) blk[(4 * g + e) * kAR + c16] = x[e];
         }
         barrier();  // B3: diagonal inverses D_i in place
+        prefetch_rest<C>(pf, rv, rb, rla, gstride, T0 + kC, tid, dv0, Dv);
 
         // ---- U = (I + A)^-1 R by block forward substitution over the four 16-token blocks:
         // U_i = D_i (R_i - sum_{k<i} A_ik U_k); accumulators serve as B operands directly
