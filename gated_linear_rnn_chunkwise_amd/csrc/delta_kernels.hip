@@ -172,6 +172,10 @@ __device__ __forceinline__ int xcd_remap(int i, int n) {
 // 16+4g+j-4 (j >= 4).
 __device__ __forceinline__ int pos32(int x) { return x < 16 ? 8 * (x >> 2) + (x & 3) : 8 * ((x - 16) >> 2) + 4 + (x & 3); }
 __device__ __forceinline__ int perm(int x) { return (x & ~31) + pos32(x & 31); }
+// Column of token slot x in row `row` of k^T: the eight 8-slot groups of a row are permuted
+// by an XOR with bits 4..6 of the row, so that the transposed stores of the staging step
+// (four consecutive rows per thread, 4 rows apart across threads) spread over the banks.
+__device__ __forceinline__ int kt_col(int row, int x) { return (((x >> 3) ^ (row >> 4)) & 7) * 8 + (x & 7); }
 
 // 32-deep product with fp16 operands, or the same contraction as eight fp32 4-deep steps
 // (element e of every lane's eight values forms step e).
@@ -330,7 +334,7 @@ __device__ __forceinline__ void stage(const Pref<C> &pf, unsigned char *smem, co
         const int tp = perm(4 * a);
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-            store_quad<C>(sKt + (4 * c + e) * C::RT + tp, el<C>(pf.k[j][0], e), el<C>(pf.k[j][1], e),
+            store_quad<C>(sKt + (4 * c + e) * C::RT + kt_col(4 * c + e, tp), el<C>(pf.k[j][0], e), el<C>(pf.k[j][1], e),
                           el<C>(pf.k[j][2], e), el<C>(pf.k[j][3], e));
     }
     {
@@ -347,6 +351,66 @@ __device__ __forceinline__ void stage(const Pref<C> &pf, unsigned char *smem, co
         const float x = row_valid_lane ? log2_decay(pf.la) : 0.f;
         sB[lane] = scan_incl(x, lane);
         sBe[lane] = row_valid_lane ? pf.beta : 0.f;
+    }
+}
+
+// Score blocks of wave W: row block W of A and row block 3-W of P, blocks on or below the
+// diagonal only.  Each product has a key block as its A operand and the row block (keys for
+// A, queries for P) as its B operand, so the accumulator of lane (g, c) holds four
+// consecutive key positions s = 16j + 4g + e of one row t = 16 W' + c: a row segment of A
+// or P, written with one vector store.  A: t = 16 W + c, A[t][s] = beta_t 2^(b_t - b_s)
+// (K K^T)[t][s] for s < t.  P: t = 16 (3 - W) + c, P[t][s] = 2^(b_t - b_s) (Q K^T)[t][s] for
+// s <= t, with the key positions in slot order; the zero blocks of P that the output
+// product reads (P[0][1] and P[2][3]) are written too.
+template <class C, int W>
+__device__ __forceinline__ void scores(const typename C::OpT *sQ, const typename C::OpT *sK, typename C::OpT *sP,
+                                       float *sA, const float *sB, const float *sBe, int g, int c16) {
+    using Frag = typename C::Frag;
+    using OpT = typename C::OpT;
+    constexpr int IQ = 3 - W;
+    constexpr int NK = W + 1, NQ = IQ + 1;
+    constexpr int NJ = NK > NQ ? NK : NQ;
+    f32x4 kk[NK], qk[NQ];
+#pragma unroll
+    for (int j = 0; j < NK; ++j) kk[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) qk[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int m = 0; m < C::NM; ++m) {
+        Frag ka[NJ];
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) ka[j] = ld_frag<C>(sK + (16 * j + c16) * C::RQ + 32 * m + 8 * g);
+        const Frag bq = ld_frag<C>(sQ + (16 * IQ + c16) * C::RQ + 32 * m + 8 * g);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            if (j < NK) kk[j] = mma(ka[j], ka[W], kk[j]);
+            if (j < NQ) qk[j] = mma(ka[j], bq, qk[j]);
+        }
+    }
+    {
+        const int t = 16 * W + c16;
+        const float bt = sB[t], bet = sBe[t];
+#pragma unroll
+        for (int j = 0; j < NK; ++j) {
+            const f32x4 bs = *reinterpret_cast<const f32x4 *>(sB + 16 * j + 4 * g);
+            f32x4 x;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[e] = 16 * j + 4 * g + e < t ? bet * fexp2(bt - bs[e]) * kk[j][e] : 0.f;
+            *reinterpret_cast<f32x4 *>(sA + t * kAR + 16 * j + 4 * g) = x;
+        }
+    }
+    {
+        const int t = 16 * IQ + c16;
+        const float bt = sB[t];
+#pragma unroll
+        for (int j = 0; j < NQ; ++j) {
+            const f32x4 bs = *reinterpret_cast<const f32x4 *>(sB + 16 * j + 4 * g);
+            float x[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[e] = 16 * j + 4 * g + e <= t ? fexp2(bt - bs[e]) * qk[j][e] : 0.f;
+            store_quad<C>(sP + t * C::RT + perm(16 * j + 4 * g), x[0], x[1], x[2], x[3]);
+        }
+        if constexpr (IQ == 0 || IQ == 2) store_quad<C>(sP + t * C::RT + perm(16 * (IQ + 1) + 4 * g), 0.f, 0.f, 0.f, 0.f);
     }
 }
 
@@ -412,48 +476,13 @@ __global__ __launch_bounds__(256, 1) void delta_chunk_kernel(DeltaArgs a) {
         barrier();  // B1: chunk staged
         prefetch_rows<C>(pf.q, rq, T0 + kC, tid);
 
-        // ---- products that do not need the triangular solve: K K^T of row block w (-> A,
-        // strictly lower, decayed, times beta of the row) and Q K^T of row block 3-w (-> P,
-        // causal, decayed), all four column blocks each as independent accumulator chains
-        {
-            f32x4 kk[4], qk[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) kk[j] = qk[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-            const int iq = 3 - w;
-#pragma unroll
-            for (int m = 0; m < C::NM; ++m) {
-                const Frag ak = ld_frag<C>(sK + (16 * w + c16) * C::RQ + 32 * m + 8 * g);
-                const Frag aq = ld_frag<C>(sQ + (16 * iq + c16) * C::RQ + 32 * m + 8 * g);
-                Frag bk[4];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) bk[j] = ld_frag<C>(sK + (16 * j + c16) * C::RQ + 32 * m + 8 * g);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    kk[j] = mma(ak, bk[j], kk[j]);
-                    qk[j] = mma(aq, bk[j], qk[j]);
-                }
-            }
-            const f32x4 bt_k = *reinterpret_cast<const f32x4 *>(sB + 16 * w + 4 * g);
-            const f32x4 be_k = *reinterpret_cast<const f32x4 *>(sBe + 16 * w + 4 * g);
-            const f32x4 bt_q = *reinterpret_cast<const f32x4 *>(sB + 16 * iq + 4 * g);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int s = 16 * j + c16;
-                const float bs = sB[s];
-                if (j <= w) {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int t = 16 * w + 4 * g + e;
-                        sA[t * kAR + s] = s < t ? be_k[e] * fexp2(bt_k[e] - bs) * kk[j][e] : 0.f;
-                    }
-                }
-                const int ps = perm(s);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int t = 16 * iq + 4 * g + e;
-                    sP[t * C::RT + ps] = (OpT)(s <= t ? fexp2(bt_q[e] - bs) * qk[j][e] : 0.f);
-                }
-            }
+        // ---- products that do not need the triangular solve: A (row block w) and P (row
+        // block 3-w), only their blocks on or below the diagonal (five per wave)
+        switch (w) {
+            case 0: scores<C, 0>(sQ, sK, sP, sA, sB, sBe, g, c16); break;
+            case 1: scores<C, 1>(sQ, sK, sP, sA, sB, sBe, g, c16); break;
+            case 2: scores<C, 2>(sQ, sK, sP, sA, sB, sBe, g, c16); break;
+            default: scores<C, 3>(sQ, sK, sP, sA, sB, sBe, g, c16); break;
         }
         prefetch_rows<C>(pf.k, rk, T0 + kC, tid);
         // the state's share of the output, diag(g) Q S0, and the right-hand side of the
@@ -576,16 +605,18 @@ __global__ __launch_bounds__(256, 1) void delta_chunk_kernel(DeltaArgs a) {
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int m = 0; m < 2; ++m) pa[i][m] = ld_frag<C>(sP + (16 * i + c16) * C::RT + 32 * m + 8 * g);
+                for (int m = 0; m < 2; ++m)
+                    if (i >= 2 * m) pa[i][m] = ld_frag<C>(sP + (16 * i + c16) * C::RT + 32 * m + 8 * g);
+            // token blocks 2 and 3 (m = 1) do not reach query blocks 0 and 1
 #pragma unroll
             for (int m = 0; m < 2; ++m)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) O[i] = mma(pa[i][m], uf[m], O[i]);
+                for (int i = 2 * m; i < 4; ++i) O[i] = mma(pa[i][m], uf[m], O[i]);
             if constexpr (!C::F32) {
 #pragma unroll
                 for (int m = 0; m < 2; ++m)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) O[i] = mma(pa[i][m], ur[m], O[i]);
+                    for (int i = 2 * m; i < 4; ++i) O[i] = mma(pa[i][m], ur[m], O[i]);
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i)
@@ -614,7 +645,8 @@ __global__ __launch_bounds__(256, 1) void delta_chunk_kernel(DeltaArgs a) {
             for (int m = 0; m < 2; ++m) {
                 Frag ka[C::NB];
 #pragma unroll
-                for (int r = 0; r < C::NB; ++r) ka[r] = ld_frag<C>(sKt + (16 * r + c16) * C::RT + 32 * m + 8 * g);
+                for (int r = 0; r < C::NB; ++r)
+                    ka[r] = ld_frag<C>(sKt + (16 * r + c16) * C::RT + kt_col(16 * r + c16, 32 * m + 8 * g));
 #pragma unroll
                 for (int r = 0; r < C::NB; ++r) S[r] = mma(ka[r], ub[m], S[r]);
                 if constexpr (!C::F32) {
