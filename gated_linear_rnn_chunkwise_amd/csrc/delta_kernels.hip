@@ -42,9 +42,10 @@
 //
 // Numbers.  bf16 inputs: matrix operands fp16 (q, k, v converted; computed operands rounded
 // once), fp32 accumulation; the triangular solve of the diagonal blocks is fp32.  The
-// corrections U (and the right-hand side of each substitution step) enter their products as
-// an fp16 value plus an fp16 rounding residual: the output is a small difference of terms of
-// the size of U, so one rounding of U would dominate its error.  fp32 inputs: fp32 operands
+// corrections U enter the output product (and the right-hand side of each substitution step
+// its product) as an fp16 value plus an fp16 rounding residual: the output is a small
+// difference of terms of the size of U, so one rounding of U would dominate its error.  The
+// state update takes U rounded once.  fp32 inputs: fp32 operands
 // throughout.  States, decays and outputs are fp32.
 //
 // Rows past the sequence end read as zero through buffer resources (k = v = beta = 0 and
@@ -633,12 +634,11 @@ __global__ __launch_bounds__(256, 1) void delta_chunk_kernel(DeltaArgs a) {
             for (int i = 0; i < 4; ++i)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) f[i][e] = fexp2(bC - sB[16 * i + 4 * g + e]);
-            Frag ub[2], ubr[2];
+            // the state's increment takes U rounded once: unlike the output, it is not a
+            // small difference of larger terms
+            Frag ub[2];
 #pragma unroll
-            for (int m = 0; m < 2; ++m) {
-                ub[m] = acc_frag_rows<C>(U[2 * m], U[2 * m + 1], f[2 * m], f[2 * m + 1]);
-                ubr[m] = residual<C>(U[2 * m], U[2 * m + 1], ub[m], f[2 * m], f[2 * m + 1]);
-            }
+            for (int m = 0; m < 2; ++m) ub[m] = acc_frag_rows<C>(U[2 * m], U[2 * m + 1], f[2 * m], f[2 * m + 1]);
 #pragma unroll
             for (int r = 0; r < C::NB; ++r) S[r] *= gC;
 #pragma unroll
@@ -649,10 +649,6 @@ __global__ __launch_bounds__(256, 1) void delta_chunk_kernel(DeltaArgs a) {
                     ka[r] = ld_frag<C>(sKt + (16 * r + c16) * C::RT + kt_col(16 * r + c16, 32 * m + 8 * g));
 #pragma unroll
                 for (int r = 0; r < C::NB; ++r) S[r] = mma(ka[r], ub[m], S[r]);
-                if constexpr (!C::F32) {
-#pragma unroll
-                    for (int r = 0; r < C::NB; ++r) S[r] = mma(ka[r], ubr[m], S[r]);
-                }
             }
         }
         barrier();  // B4: the chunk's LDS may be overwritten
