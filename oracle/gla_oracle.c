@@ -335,6 +335,78 @@ int gla_oracle_delta(const double *q, const double *k, const double *v, const do
     return failed ? -1 : 0;
 }
 
+/* The mLSTM cell (the xLSTM's matrix memory), token by token in fp64: the memory and its
+ * normaliser decay by the forget gate f_t = exp(log_f_t) and take the token's write with the
+ * exponential input gate i_t = exp(log_i_t),
+ *     C_t = f_t C_{t-1} + i_t k_t^T v_t ,    n_t = f_t n_{t-1} + i_t k_t ,
+ * and the token reads h_t = q_t C_t / max(|q_t . n_t|, 1)
+ * [Tiled Flash Linear Attention, abstract: the mLSTM of Beck et al. (2024), with its
+ * exponential input gate and normaliser; the sigmoid-gated variant drops both].
+ * C is Dk x Dv (row d, column c), n has Dk entries.  An initial state (C0, n0) is taken in
+ * the unstabilised scale; NULL starts from zero.  final_C / final_n may be NULL. */
+int gla_oracle_mlstm(const double *q, const double *k, const double *v, const double *log_f,
+                     const double *log_i, const double *C0, const double *n0, double *out, double *final_C,
+                     double *final_n, long B, long H, long L, long Dk, long Dv)
+{
+    if (!q || !k || !v || !log_f || !log_i || !out) return -1;
+    if (B <= 0 || H <= 0 || L <= 0 || Dk <= 0 || Dv <= 0) return -1;
+    const long BH = B * H;
+    int failed = 0;
+
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long bh = 0; bh < BH; ++bh) {
+        double *C = (double *)malloc(sizeof(double) * (size_t)(Dk * Dv));
+        double *n = (double *)malloc(sizeof(double) * (size_t)Dk);
+        if (!C || !n) {
+            free(C);
+            free(n);
+#pragma omp atomic write
+            failed = 1;
+            continue;
+        }
+        if (C0)
+            memcpy(C, C0 + bh * Dk * Dv, sizeof(double) * (size_t)(Dk * Dv));
+        else
+            memset(C, 0, sizeof(double) * (size_t)(Dk * Dv));
+        if (n0)
+            memcpy(n, n0 + bh * Dk, sizeof(double) * (size_t)Dk);
+        else
+            memset(n, 0, sizeof(double) * (size_t)Dk);
+
+        for (long t = 0; t < L; ++t) {
+            const double *qt = q + (bh * L + t) * Dk;
+            const double *kt = k + (bh * L + t) * Dk;
+            const double *vt = v + (bh * L + t) * Dv;
+            const double ft = exp(log_f[bh * L + t]);
+            const double it = exp(log_i[bh * L + t]);
+            double *ht = out + (bh * L + t) * Dv;
+
+            /* memory and normaliser: decay, then the token's write */
+            for (long d = 0; d < Dk; ++d) {
+                double *Cd = C + d * Dv;
+                const double w = it * kt[d];
+                for (long c = 0; c < Dv; ++c) Cd[c] = ft * Cd[c] + w * vt[c];
+                n[d] = ft * n[d] + w;
+            }
+            /* read: q_t C_t over max(|q_t . n_t|, 1) */
+            double qn = 0.0;
+            for (long d = 0; d < Dk; ++d) qn += qt[d] * n[d];
+            const double den = fabs(qn) > 1.0 ? fabs(qn) : 1.0;
+            for (long c = 0; c < Dv; ++c) ht[c] = 0.0;
+            for (long d = 0; d < Dk; ++d) {
+                const double *Cd = C + d * Dv;
+                for (long c = 0; c < Dv; ++c) ht[c] += qt[d] * Cd[c];
+            }
+            for (long c = 0; c < Dv; ++c) ht[c] /= den;
+        }
+        if (final_C) memcpy(final_C + bh * Dk * Dv, C, sizeof(double) * (size_t)(Dk * Dv));
+        if (final_n) memcpy(final_n + bh * Dk, n, sizeof(double) * (size_t)Dk);
+        free(C);
+        free(n);
+    }
+    return failed ? -1 : 0;
+}
+
 /* Number of OpenMP threads the recurrence uses (1 without OpenMP). */
 int gla_oracle_threads(void)
 {

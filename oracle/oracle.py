@@ -35,6 +35,18 @@ Forms (all fp64, computed from the exact input values):
   system that turns the product of identity-plus-rank-one transitions into sums
   [talk summary, 31:16].  Tiny inputs only.
 
+* :func:`mlstm_recurrent` -- the mLSTM (the xLSTM's matrix memory) with exponential input
+  gate and normaliser, token by token in C (``gla_oracle_mlstm``): ``C_t = f_t C_{t-1} +
+  i_t k_t^T v_t``, ``n_t = f_t n_{t-1} + i_t k_t``, ``h_t = q_t C_t / max(|q_t . n_t|, 1)``
+  with ``f_t = exp(log_f_t)`` and ``i_t = exp(log_i_t)`` [Tiled Flash Linear Attention,
+  abstract: the mLSTM of Beck et al. (2024); its sigmoid-gated variant drops the normaliser].
+  The pages print neither the exponential gate nor the normaliser; the form used is the one
+  of the cited mLSTM.
+* :func:`mlstm_parallel_form`, :func:`mlstm_stabilized_recurrent` and
+  :func:`mlstm_chunkwise_form` -- the same map as causal pairwise weights, as the
+  max-stabilised token recurrence, and chunkwise with a running maximum of the log
+  weights.  Tiny inputs only.
+
 Gate kinds (how a stored gate broadcasts to the per-channel log decay):
 ``"none"`` (zero), ``"channel"`` ``[B,H,L,Dk]``, ``"head"`` ``[B,H,L]`` (one decay per
 head and token), ``"head_const"`` ``[H]`` (one fixed decay per head).  The optional input
@@ -77,6 +89,8 @@ def load_library(path: str):
     lib.gla_oracle_backward.restype = ctypes.c_int
     lib.gla_oracle_delta.argtypes = [dp] * 8 + [ctypes.c_long] * 5
     lib.gla_oracle_delta.restype = ctypes.c_int
+    lib.gla_oracle_mlstm.argtypes = [dp] * 10 + [ctypes.c_long] * 5
+    lib.gla_oracle_mlstm.restype = ctypes.c_int
     lib.gla_oracle_threads.restype = ctypes.c_int
     lib.gla_oracle_threads.argtypes = []
     return lib
@@ -393,3 +407,167 @@ def delta_chunkwise_form(q, k, v, beta, chunk: int, log_alpha=None, initial_stat
                 S = g[-1] * S + ((g[-1] / g)[:, None] * K).T @ U
             fin[bb, h] = S
     return out, fin
+
+
+# ---------------------------------------------------------------------------------------
+# The mLSTM with exponential input gate and normaliser.
+
+def _mlstm_gates(log_f, log_i, B: int, H: int, L: int):
+    lf, li = _f64(log_f), _f64(log_i)
+    assert lf.shape == (B, H, L) and li.shape == (B, H, L), (lf.shape, li.shape)
+    return lf, li
+
+
+def mlstm_recurrent(q, k, v, log_f, log_i, initial_state=None, lib=None):
+    """The mLSTM token recurrence in C (``gla_oracle_mlstm``), unstabilised fp64:
+    ``C_t = f_t C_{t-1} + i_t k_t^T v_t``, ``n_t = f_t n_{t-1} + i_t k_t``,
+    ``h_t = q_t C_t / max(|q_t . n_t|, 1)``, ``f_t = exp(log_f_t)``, ``i_t = exp(log_i_t)``
+    [Tiled Flash Linear Attention, abstract, citing the mLSTM of Beck et al. (2024)].
+    ``log_f``, ``log_i``: ``[B,H,L]``.  ``initial_state``: ``(C0 [B,H,Dk,Dv], n0 [B,H,Dk])`` in
+    the unstabilised scale, or None.  Returns ``(h [B,H,L,Dv], C_L, n_L)``."""
+    q64, k64, v64 = _f64(q), _f64(k), _f64(v)
+    B, H, L, Dk = q64.shape
+    Dv = v64.shape[-1]
+    assert k64.shape == q64.shape and v64.shape == (B, H, L, Dv)
+    lf, li = _mlstm_gates(log_f, log_i, B, H, L)
+    C0 = n0 = None
+    if initial_state is not None:
+        C0, n0 = _f64(initial_state[0]), _f64(initial_state[1])
+        assert C0.shape == (B, H, Dk, Dv) and n0.shape == (B, H, Dk)
+    out = np.empty((B, H, L, Dv))
+    finC = np.empty((B, H, Dk, Dv))
+    finN = np.empty((B, H, Dk))
+    dp = ctypes.POINTER(ctypes.c_double)
+
+    def p(a):
+        return None if a is None else a.ctypes.data_as(dp)
+
+    rc = (lib or _load()).gla_oracle_mlstm(p(q64), p(k64), p(v64), p(lf), p(li), p(C0), p(n0), p(out), p(finC),
+                                           p(finN), B, H, L, Dk, Dv)
+    if rc != 0:
+        raise RuntimeError("gla_oracle_mlstm failed (%d)" % rc)
+    return out, finC, finN
+
+
+def mlstm_parallel_form(q, k, v, log_f, log_i, initial_state=None):
+    """The mLSTM as causal pairwise weights (fp64, tiny inputs): with ``F`` the running sum
+    of ``log_f`` from the sequence start, token s reaches token t >= s with weight
+    ``D_ts = exp(F_t - F_s + log_i_s)``; ``W = (Q K^T) * D`` (causal), and
+    ``h = (W V + e^F Q C0) / max(|W 1 + e^F Q n0|, 1)`` row by row.  Returns ``h``."""
+    q64, k64, v64 = _f64(q), _f64(k), _f64(v)
+    B, H, L, Dk = q64.shape
+    Dv = v64.shape[-1]
+    lf, li = _mlstm_gates(log_f, log_i, B, H, L)
+    out = np.zeros((B, H, L, Dv))
+    causal = np.tril(np.ones((L, L), dtype=bool))
+    for bb in range(B):
+        for h in range(H):
+            F = np.cumsum(lf[bb, h])
+            logD = F[:, None] - F[None, :] + li[bb, h][None, :]
+            D = np.where(causal, np.exp(np.where(causal, logD, 0.0)), 0.0)
+            Q, K, V = q64[bb, h], k64[bb, h], v64[bb, h]
+            W = (Q @ K.T) * D
+            num = W @ V
+            den = W.sum(axis=1)
+            if initial_state is not None:
+                C0, n0 = _f64(initial_state[0])[bb, h], _f64(initial_state[1])[bb, h]
+                eF = np.exp(F)
+                num = num + eF[:, None] * (Q @ C0)
+                den = den + eF * (Q @ n0)
+            out[bb, h] = num / np.maximum(np.abs(den), 1.0)[:, None]
+    return out
+
+
+def mlstm_stabilized_recurrent(q, k, v, log_f, log_i, initial_state=None):
+    """The max-stabilised mLSTM recurrence (fp64, tiny inputs): the running maximum
+    ``m_t = max(log_f_t + m_{t-1}, log_i_t)`` rescales memory and normaliser to
+    ``C'_t = C_t e^{-m_t}``, ``n'_t = n_t e^{-m_t}``, whose updates take the gates
+    ``exp(log_f_t + m_{t-1} - m_t)`` and ``exp(log_i_t - m_t)`` (both at most 1); the read is
+    ``q_t C'_t / max(|q_t . n'_t|, e^{-m_t})``, the same value as the unstabilised read.
+    ``initial_state``: ``(C0', n0', m0)`` stabilised, or None (``m`` starts at -inf).
+    Returns ``(h, C'_L, n'_L, m_L)``."""
+    q64, k64, v64 = _f64(q), _f64(k), _f64(v)
+    B, H, L, Dk = q64.shape
+    Dv = v64.shape[-1]
+    lf, li = _mlstm_gates(log_f, log_i, B, H, L)
+    out = np.zeros((B, H, L, Dv))
+    finC = np.zeros((B, H, Dk, Dv))
+    finN = np.zeros((B, H, Dk))
+    finM = np.zeros((B, H))
+    for bb in range(B):
+        for h in range(H):
+            if initial_state is None:
+                C, n, m = np.zeros((Dk, Dv)), np.zeros(Dk), -np.inf
+            else:
+                C = _f64(initial_state[0])[bb, h].copy()
+                n = _f64(initial_state[1])[bb, h].copy()
+                m = float(_f64(initial_state[2])[bb, h])
+            for t in range(L):
+                m_new = max(lf[bb, h, t] + m, li[bb, h, t])
+                fp = np.exp(lf[bb, h, t] + m - m_new)
+                ip = np.exp(li[bb, h, t] - m_new)
+                kt, vt, qt = k64[bb, h, t], v64[bb, h, t], q64[bb, h, t]
+                C = fp * C + ip * np.outer(kt, vt)
+                n = fp * n + ip * kt
+                m = m_new
+                out[bb, h, t] = (qt @ C) / max(abs(qt @ n), np.exp(-m))
+            finC[bb, h], finN[bb, h], finM[bb, h] = C, n, m
+    return out, finC, finN, finM
+
+
+def mlstm_chunkwise_form(q, k, v, log_f, log_i, chunk: int, initial_state=None):
+    """The stabilised mLSTM computed chunkwise, plainly (fp64, tiny inputs).
+
+    A chunk enters with the stabilised state ``(C', n', m)``.  Inside it, with ``b`` the
+    inclusive running sum of ``log_f`` and ``a_s = log_i_s - b_s``, token s reaches row t >= s
+    with log weight ``b_t + a_s`` and the entering state reaches it with ``b_t + m``; the row's
+    stabiliser is ``m_t = b_t + M_t`` with ``M_t = max(m, max_{s<=t} a_s)``, so every factor
+    below is at most 1:
+
+        num_t = e^{m - M_t} q_t C' + sum_{s<=t} e^{a_s - M_t} (q_t . k_s) v_s
+        den_t = e^{m - M_t} q_t . n' + sum_{s<=t} e^{a_s - M_t} (q_t . k_s)
+        h_t   = num_t / max(|den_t|, e^{-m_t})
+
+    and at the chunk end (``M_e`` the last row's maximum)
+    ``C' <- e^{m - M_e} C' + K^T diag(e^{a - M_e}) V``, ``n' <- e^{m - M_e} n' + K^T e^{a - M_e}``,
+    ``m <- b_last + M_e``.  This is the chunkwise algorithm [Hardware-Efficient Training of
+    Linear Attention Models, talk summary, 11:58] with the mLSTM's running maximum carried
+    across chunks.  ``initial_state`` as in :func:`mlstm_stabilized_recurrent`.
+    Returns ``(h, C'_L, n'_L, m_L)``."""
+    q64, k64, v64 = _f64(q), _f64(k), _f64(v)
+    B, H, L, Dk = q64.shape
+    Dv = v64.shape[-1]
+    lf, li = _mlstm_gates(log_f, log_i, B, H, L)
+    out = np.zeros((B, H, L, Dv))
+    finC = np.zeros((B, H, Dk, Dv))
+    finN = np.zeros((B, H, Dk))
+    finM = np.zeros((B, H))
+    for bb in range(B):
+        for h in range(H):
+            if initial_state is None:
+                C, n, m = np.zeros((Dk, Dv)), np.zeros(Dk), -np.inf
+            else:
+                C = _f64(initial_state[0])[bb, h].copy()
+                n = _f64(initial_state[1])[bb, h].copy()
+                m = float(_f64(initial_state[2])[bb, h])
+            for c0 in range(0, L, chunk):
+                c1 = min(L, c0 + chunk)
+                Q, K, V = q64[bb, h, c0:c1], k64[bb, h, c0:c1], v64[bb, h, c0:c1]
+                b = np.cumsum(lf[bb, h, c0:c1])
+                a = li[bb, h, c0:c1] - b
+                M = np.maximum(np.maximum.accumulate(a), m)
+                inter = np.exp(m - M)
+                causal = np.tril(np.ones((c1 - c0, c1 - c0), dtype=bool))
+                Wt = np.where(causal, np.exp(np.where(causal, a[None, :] - M[:, None], 0.0)), 0.0)
+                P = (Q @ K.T) * Wt
+                num = inter[:, None] * (Q @ C) + P @ V
+                den = inter * (Q @ n) + P.sum(axis=1)
+                out[bb, h, c0:c1] = num / np.maximum(np.abs(den), np.exp(-(b + M)))[:, None]
+                Me = M[-1]
+                w = np.exp(a - Me)
+                e = np.exp(m - Me)
+                C = e * C + K.T @ (w[:, None] * V)
+                n = e * n + K.T @ w
+                m = b[-1] + Me
+            finC[bb, h], finN[bb, h], finM[bb, h] = C, n, m
+    return out, finC, finN, finM

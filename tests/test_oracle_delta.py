@@ -231,7 +231,7 @@ def _delta_pins_pass(lib) -> bool:
 def _delta_source():
     src = open(os.path.join(os.path.dirname(HERE), "oracle", "gla_oracle.c")).read()
     i0 = src.index("int gla_oracle_delta(")
-    i1 = src.index("/* Number of OpenMP threads")
+    i1 = src.index("/* The mLSTM cell")
     return src, i0, i1
 
 
