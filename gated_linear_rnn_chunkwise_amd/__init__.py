@@ -30,7 +30,8 @@ GATE_NAMES = {"none": GATE_NONE, "channel": GATE_CHANNEL, "head": GATE_HEAD, "he
 
 # Entry points declared in include/gla.h.
 EXPORTS = ("gla_fwd", "gla_fwd_ex", "gla_fwd_noalloc", "gla_workspace_size", "gla_query_plan", "gla_step",
-           "gla_bwd", "gla_bwd_workspace_size", "gla_delta_fwd", "gla_status_string", "gla_version")
+           "gla_bwd", "gla_bwd_workspace_size", "gla_delta_fwd", "gla_mlstm_fwd", "gla_status_string",
+           "gla_version")
 NOALLOC_SCRATCH_BYTES = 32 << 20  # GLA_NOALLOC_SCRATCH_BYTES
 
 
@@ -89,6 +90,18 @@ class GlaDeltaDesc(ctypes.Structure):
     ]
 
 
+class GlaMlstmDesc(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int32), ("H", ctypes.c_int32), ("L", ctypes.c_int32), ("Dk", ctypes.c_int32),
+        ("Dv", ctypes.c_int32), ("chunk", ctypes.c_int32), ("in_dtype", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+        ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("log_f", ctypes.c_void_p),
+        ("log_i", ctypes.c_void_p), ("initial_C", ctypes.c_void_p), ("initial_n", ctypes.c_void_p),
+        ("initial_m", ctypes.c_void_p), ("out", ctypes.c_void_p), ("final_C", ctypes.c_void_p),
+        ("final_n", ctypes.c_void_p), ("final_m", ctypes.c_void_p),
+    ]
+
+
 class GlaError(RuntimeError):
     def __init__(self, status: int, what: str = ""):
         self.status = status
@@ -128,6 +141,8 @@ def load(path: str = LIB_PATH):
         lib.gla_bwd_workspace_size.restype = i32
         lib.gla_delta_fwd.argtypes = [ctypes.POINTER(GlaDeltaDesc), vp]
         lib.gla_delta_fwd.restype = i32
+        lib.gla_mlstm_fwd.argtypes = [ctypes.POINTER(GlaMlstmDesc), vp]
+        lib.gla_mlstm_fwd.restype = i32
         lib.gla_status_string.argtypes = [i32]
         lib.gla_status_string.restype = ctypes.c_char_p
         lib.gla_version.argtypes = []
@@ -495,4 +510,73 @@ def delta_fwd(q, k, v, beta, log_alpha=None, *, initial_state=None, chunk: int =
     st = lib.gla_delta_fwd(ctypes.byref(d), ctypes.c_void_p(s.cuda_stream))
     if st != GLA_OK:
         raise GlaError(st, "gla_delta_fwd")
+    return out, fin
+
+
+def make_mlstm_desc(q, k, v, log_f, log_i, initial_state=None, out=None, final_state=None,
+                    chunk=64) -> GlaMlstmDesc:
+    """Fill a :class:`GlaMlstmDesc` from tensors (shapes read from q and v).  ``initial_state``
+    and ``final_state`` are ``(C' [B,H,Dk,Dv], n' [B,H,Dk], m [B,H])`` triples or None."""
+    import torch
+
+    B, H, L, Dk = q.shape
+    Dv = v.shape[-1]
+    d = GlaMlstmDesc()
+    d.B, d.H, d.L, d.Dk, d.Dv, d.chunk = B, H, L, Dk, Dv, int(chunk)
+    if q.dtype == torch.bfloat16:
+        d.in_dtype = DTYPE_BF16
+    elif q.dtype == torch.float32:
+        d.in_dtype = DTYPE_F32
+    else:
+        raise TypeError("q, k, v must be bf16 or fp32, got %s" % q.dtype)
+    d.reserved = 0
+    d.q, d.k, d.v, d.log_f, d.log_i = _ptr(q), _ptr(k), _ptr(v), _ptr(log_f), _ptr(log_i)
+    if initial_state is not None:
+        d.initial_C, d.initial_n, d.initial_m = (_ptr(t) for t in initial_state)
+    d.out = _ptr(out)
+    if final_state is not None:
+        d.final_C, d.final_n, d.final_m = (_ptr(t) for t in final_state)
+    return d
+
+
+def mlstm_fwd(q, k, v, log_f, log_i, *, initial_state=None, chunk: int = 64, final_state: bool = True, out=None,
+              stream=None):
+    """mLSTM forward with exponential input gate and normaliser (``gla_mlstm_fwd``) on the
+    current HIP stream.  ``log_f``, ``log_i``: ``[B,H,L]`` fp32 natural logs of the forget and
+    input gates.  ``initial_state``: stabilised ``(C', n', m)`` or None.  Returns
+    ``(out [B,H,L,Dv] fp32, (C', n', m) or None)`` with ``C = exp(m) C'``, ``n = exp(m) n'``."""
+    import torch
+
+    lib = load()
+    if q.dim() != 4 or v.dim() != 4:
+        raise ValueError("q and v must be [B, H, L, D]")
+    B, H, L, Dk = q.shape
+    Dv = v.shape[-1]
+    _check_shape(k, (B, H, L, Dk), "k")
+    _check_shape(v, (B, H, L, Dv), "v")
+    _check_shape(log_f, (B, H, L), "log_f")
+    _check_shape(log_i, (B, H, L), "log_i")
+    init = ()
+    if initial_state is not None:
+        if len(initial_state) != 3:
+            raise ValueError("initial_state is a (C', n', m) triple")
+        for t, shape, name in zip(initial_state, ((B, H, Dk, Dv), (B, H, Dk), (B, H)), ("C'", "n'", "m")):
+            if t is None:
+                raise ValueError("initial_state: %s missing" % name)
+            _check_shape(t, shape, "initial " + name)
+        init = tuple(initial_state)
+    _check_shape(out, (B, H, L, Dv), "out")
+    if out is None:
+        out = torch.empty((B, H, L, Dv), dtype=torch.float32, device=q.device)
+    fin = None
+    if final_state:
+        fin = (torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=q.device),
+               torch.empty((B, H, Dk), dtype=torch.float32, device=q.device),
+               torch.empty((B, H), dtype=torch.float32, device=q.device))
+    _check_tensors(q, k, v, log_f, log_i, out, *init, *(fin or ()))
+    d = make_mlstm_desc(q, k, v, log_f, log_i, initial_state, out, fin, chunk)
+    s = stream if stream is not None else torch.cuda.current_stream(q.device)
+    st = lib.gla_mlstm_fwd(ctypes.byref(d), ctypes.c_void_p(s.cuda_stream))
+    if st != GLA_OK:
+        raise GlaError(st, "gla_mlstm_fwd")
     return out, fin

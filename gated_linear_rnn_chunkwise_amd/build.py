@@ -2,8 +2,8 @@
 
 Usage: ``python -m gated_linear_rnn_chunkwise_amd.build`` (or call :func:`build`).
 Every call compiles from source: the kernels (``csrc/gla_kernels.hip``, ``csrc/gla_bwd.hip``,
-``csrc/gla_bwd_chan.hip``, ``csrc/delta_kernels.hip``) and the C ABI (``csrc/gla_api.cpp``) are
-compiled in parallel and linked into one shared library.
+``csrc/gla_bwd_chan.hip``, ``csrc/delta_kernels.hip``, ``csrc/mlstm_kernels.hip``) and the C ABI
+(``csrc/gla_api.cpp``) are compiled in parallel and linked into one shared library.
 """
 from __future__ import annotations
 
@@ -27,7 +27,8 @@ COMMON = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", INCLUDE, "-I", CSRC, "-Wall", "-Wno-unused-variable", "-Wno-unused-but-set-variable",
 ]
-SOURCES = ["gla_kernels.hip", "gla_bwd.hip", "gla_bwd_chan.hip", "delta_kernels.hip", "gla_api.cpp"]
+SOURCES = ["gla_kernels.hip", "gla_bwd.hip", "gla_bwd_chan.hip", "delta_kernels.hip", "mlstm_kernels.hip",
+           "gla_api.cpp"]
 
 
 def _compile(src: str) -> str:

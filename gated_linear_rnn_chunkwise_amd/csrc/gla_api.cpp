@@ -17,6 +17,7 @@
 
 #include "gla.h"
 #include "gla_delta.h"
+#include "gla_mlstm.h"
 #include "gla_layout.h"
 
 namespace gla {
@@ -743,5 +744,57 @@ extern "C" int gla_delta_fwd(const gla_delta_desc *d, void *stream) {
     a.ndv = d->Dv / 64;
     a.nwg = (int)nwg;
     return gla_delta::launch(a, f32, d->Dk, reinterpret_cast<hipStream_t>(stream)) == hipSuccess ? GLA_OK
+                                                                                               : GLA_ERR_HIP;
+}
+
+// ------------------------------------------------------------------------------------
+// mLSTM with exponential input gate and normaliser (mlstm_kernels.hip).
+
+extern "C" int gla_mlstm_fwd(const gla_mlstm_desc *d, void *stream) {
+    if (!d || !d->q || !d->k || !d->v || !d->log_f || !d->log_i || !d->out) return GLA_ERR_INVALID_ARG;
+    if (d->B <= 0 || d->H <= 0 || d->L <= 0 || d->Dk <= 0 || d->Dv <= 0 || d->chunk <= 0) return GLA_ERR_INVALID_ARG;
+    if (d->reserved != 0) return GLA_ERR_INVALID_ARG;
+    if (d->in_dtype != GLA_DTYPE_BF16 && d->in_dtype != GLA_DTYPE_F32) return GLA_ERR_INVALID_ARG;
+    const int given = (d->initial_C != nullptr) + (d->initial_n != nullptr) + (d->initial_m != nullptr);
+    if (given != 0 && given != 3) return GLA_ERR_INVALID_ARG;
+    const void *ptrs[] = {d->q,         d->k,         d->v,         d->log_f,   d->log_i,   d->initial_C, d->initial_n,
+                          d->initial_m, d->out,       d->final_C,   d->final_n, d->final_m};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p)) return GLA_ERR_INVALID_ARG;
+    const int64_t lim = int64_t(1) << 40;
+    const int64_t bh = int64_t(d->B) * d->H;
+    if (bh > (int64_t(1) << 24)) return GLA_ERR_INVALID_ARG;
+    if (bh * d->L > lim / std::max(d->Dk, d->Dv)) return GLA_ERR_INVALID_ARG;
+    if (bh * int64_t(d->Dk) * d->Dv > lim) return GLA_ERR_INVALID_ARG;
+    const bool f32 = d->in_dtype == GLA_DTYPE_F32;
+    if (d->chunk != 64) return GLA_ERR_UNSUPPORTED;
+    if (f32 ? d->Dk != 64 : (d->Dk != 64 && d->Dk != 128 && d->Dk != 256)) return GLA_ERR_UNSUPPORTED;
+    if (d->Dv % 64 != 0 || d->Dv > 4096) return GLA_ERR_UNSUPPORTED;
+    // one (batch, head) slice is addressed with 32-bit byte offsets, one chunk past the end
+    // read by the prefetch
+    if ((int64_t(d->L) + 128) * std::max(d->Dk, d->Dv) * 4 >= (int64_t(1) << 32)) return GLA_ERR_UNSUPPORTED;
+    if (gla_mlstm::lds_bytes(f32, d->Dk) > gla::kMaxLds) return GLA_ERR_UNSUPPORTED;
+    const int64_t nwg = bh * (d->Dv / 64);
+    if (nwg > INT32_MAX) return GLA_ERR_UNSUPPORTED;
+    gla_mlstm::MlstmArgs a{};
+    a.q = d->q;
+    a.k = d->k;
+    a.v = d->v;
+    a.lf = d->log_f;
+    a.li = d->log_i;
+    a.c0 = d->initial_C;
+    a.n0 = d->initial_n;
+    a.m0 = d->initial_m;
+    a.out = d->out;
+    a.fin_c = d->final_C;
+    a.fin_n = d->final_n;
+    a.fin_m = d->final_m;
+    a.B = d->B;
+    a.H = d->H;
+    a.L = d->L;
+    a.Dv = d->Dv;
+    a.ndv = d->Dv / 64;
+    a.nwg = (int)nwg;
+    return gla_mlstm::launch(a, f32, d->Dk, reinterpret_cast<hipStream_t>(stream)) == hipSuccess ? GLA_OK
                                                                                                : GLA_ERR_HIP;
 }

@@ -1,0 +1,25 @@
+// gla_mlstm.h -- arguments of the mLSTM kernel (exponential input gate and normaliser),
+// shared by the host entry point and the gfx950 kernel.
+#pragma once
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+namespace gla_mlstm {
+
+struct MlstmArgs {
+    const void *q, *k, *v;              // [B,H,L,Dk], [B,H,L,Dk], [B,H,L,Dv] in the input dtype
+    const float *lf, *li;               // [B,H,L] log forget gate, log input gate
+    const float *c0, *n0, *m0;          // stabilised initial state [B,H,Dk,Dv], [B,H,Dk], [B,H]; all or none
+    float *out;                         // [B,H,L,Dv]
+    float *fin_c, *fin_n, *fin_m;       // stabilised final state, each optional
+    int B, H, L, Dv;
+    int ndv;                            // 64-column value slices
+    int nwg;                            // workgroups = B * H * ndv
+};
+
+// LDS bytes of one workgroup (fp32 or fp16 operands, Dk).
+uint32_t lds_bytes(bool f32, int dk);
+hipError_t launch(const MlstmArgs &a, bool f32, int dk, hipStream_t st);
+
+}  // namespace gla_mlstm

@@ -17,6 +17,12 @@ then draw the gate pre-activations.  Gates are stored as fp32 logs:
   input gates of the mLSTM variant).
 * ``none``: no gate.
 
+mLSTM workloads with exponential input gate and normaliser (``rule == "mlstm"``) draw ``q``
+and ``v`` as fp32 N(0, 1) and ``k`` as N(0, 1) / sqrt(Dk) (the cell's key scaling), rounded to
+the input dtype, then ``log_f = logsigmoid(a)``, ``a ~ N(3, 1)`` (sigmoid forget gate) and
+``log_i ~ N(0, ig_std^2)`` (the exponential input gate's pre-activation), both ``[B, H, L]``
+fp32.
+
 Delta-rule workloads (``rule == "delta"``) draw ``q`` and ``k`` uniformly on the unit sphere
 (fp32 N(0, 1) rows divided by their L2 norm in fp32, then rounded to the input dtype), ``v``
 as above, then the writing strength ``beta = sigmoid(x)``, ``x ~ N(0, 1)``, ``[B, H, L]``
@@ -50,7 +56,9 @@ class Workload:
     gate_shift: float = 3.0      # mean of the forget pre-activation for gate == "head"
     channel_gate_div: float = 16.0
     rule: str = "linear"         # "linear": S_t = diag(alpha_t) S_{t-1} + i_t k_t^T v_t;
-                                 # "delta": the delta rule with writing strength beta_t
+                                 # "delta": the delta rule with writing strength beta_t;
+                                 # "mlstm": exponential input gate and normaliser
+    ig_std: float = 1.0          # std of the mLSTM log input gate
 
     def with_(self, **kw) -> "Workload":
         return replace(self, **kw)
@@ -82,6 +90,12 @@ DELTA_WORKLOADS = {
                                                gate="head", rule="delta"),
 }
 
+# The mLSTM with exponential input gate and normaliser at the sigmoid-gated mLSTM's head shape.
+MLSTM_WORKLOADS = {
+    "mlstm_exp_bf16_B8H8L8192": Workload("mlstm_exp_bf16_B8H8L8192", 8, 8, 8192, 256, 512, 64, gate="head",
+                                         rule="mlstm"),
+}
+
 
 def _dt(name: str):
     return {"bf16": torch.bfloat16, "f32": torch.float32}[name]
@@ -98,6 +112,8 @@ def make_inputs(w: Workload, seed: int = 0, device="cpu") -> dict:
     dt = _dt(w.dtype)
     if w.rule == "delta":
         return _make_delta_inputs(w, g, div, dt, device)
+    if w.rule == "mlstm":
+        return _make_mlstm_inputs(w, g, dt, device)
     q = (torch.randn(B, H, L, Dk, generator=g, dtype=torch.float32) / div).to(dt)
     k = (torch.randn(B, H, L, Dk, generator=g, dtype=torch.float32) / div).to(dt)
     v = (torch.randn(B, H, L, Dv, generator=g, dtype=torch.float32) / div).to(dt)
@@ -159,9 +175,28 @@ def _make_delta_inputs(w: Workload, g, div, dt, device) -> dict:
     return out
 
 
+def _make_mlstm_inputs(w: Workload, g, dt, device) -> dict:
+    B, H, L, Dk, Dv = w.B, w.H, w.L, w.Dk, w.Dv
+    kdiv = torch.tensor(math.sqrt(Dk), dtype=torch.float32)
+    q = torch.randn(B, H, L, Dk, generator=g, dtype=torch.float32).to(dt)
+    k = (torch.randn(B, H, L, Dk, generator=g, dtype=torch.float32) / kdiv).to(dt)
+    v = torch.randn(B, H, L, Dv, generator=g, dtype=torch.float32).to(dt)
+    lf = torch.nn.functional.logsigmoid(torch.randn(B, H, L, generator=g, dtype=torch.float32) + w.gate_shift)
+    li = torch.randn(B, H, L, generator=g, dtype=torch.float32) * w.ig_std
+    h = hashlib.sha256()
+    for t in (q, k, v, lf, li):
+        h.update(t.contiguous().view(torch.uint8).numpy().tobytes() if t.dtype != torch.bfloat16
+                 else t.contiguous().view(torch.int16).numpy().tobytes())
+    out = dict(q=q, k=k, v=v, log_f=lf, log_i=li, log_alpha=None, log_ig=None, sha256=h.hexdigest())
+    if device != "cpu":
+        for key in ("q", "k", "v", "log_f", "log_i"):
+            out[key] = out[key].to(device)
+    return out
+
+
 def custom(B, H, L, Dk, Dv, chunk, dtype="bf16", gate="channel", input_gate=False, **kw) -> Workload:
     """A workload of arbitrary shape with the same value distributions."""
     rule = kw.get("rule", "linear")
     return Workload("custom_B%dH%dL%dDk%dDv%dC%d_%s_%s%s" % (B, H, L, Dk, Dv, chunk, dtype, gate,
-                                                           "_delta" if rule == "delta" else ""),
+                                                           "" if rule == "linear" else "_" + rule),
                     B, H, L, Dk, Dv, chunk, dtype=dtype, gate=gate, input_gate=input_gate, **kw)

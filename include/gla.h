@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define GLA_VERSION 10400 /* major * 10000 + minor * 100 + patch */
+#define GLA_VERSION 10500 /* major * 10000 + minor * 100 + patch */
 
 /* Status codes.  0 is success; errors are negative. */
 enum gla_status {
@@ -305,6 +305,52 @@ typedef struct gla_delta_desc {
  * matrix, not a decay).  log_alpha must be finite (as for gla_fwd_ex).  Validation,
  * ownership and asynchrony as for gla_fwd_ex; allocates nothing.  Returns a gla_status. */
 int gla_delta_fwd(const gla_delta_desc *d, void *stream);
+
+/* The mLSTM with exponential input gate and normaliser (the xLSTM's matrix memory, the
+ * mLSTM of Beck et al. (2024) to which the Tiled Flash Linear Attention abstract applies its
+ * kernels; the abstract's sigmoid-input-gate variant, gla_fwd_ex with GLA_GATE_HEAD and
+ * log_ig, drops the normaliser).  For every (batch, head), with f_t = exp(log_f_t) and
+ * i_t = exp(log_i_t):
+ *
+ *     C_t = f_t C_{t-1} + i_t k_t^T v_t ,   n_t = f_t n_{t-1} + i_t k_t ,
+ *     out_t = q_t C_t / max(|q_t . n_t|, 1) ,
+ *
+ * C Dk x Dv and n of Dk entries, zero before the first token unless an initial state is
+ * given.  The pages print neither the exponential gate nor the normaliser; this is the cell
+ * as its source defines it.  The input gate is unbounded, so states cross the ABI stabilised:
+ * (C', n', m) with C = exp(m) C' and n = exp(m) n' (m a natural log).  The kernel walks
+ * 64-token chunks carrying (C', n', m) with m the running maximum of the log weights, so
+ * every factor it applies is at most 1; the output equals the recurrence's up to rounding.
+ *
+ * Numbers: bf16 inputs run the matrix products on fp16 operands (q, k, v converted, scores
+ * and weighted values rounded once) with fp32 accumulation; the normaliser and all gate
+ * arithmetic are fp32.  fp32 inputs keep fp32 operands.  Outputs and states are fp32. */
+typedef struct gla_mlstm_desc {
+    int32_t B, H, L, Dk, Dv;     /* batch, heads, sequence length, key and value head dims */
+    int32_t chunk;               /* chunk size; 64 (the kernel's chunk) */
+    int32_t in_dtype;            /* enum gla_dtype of q, k, v */
+    int32_t reserved;            /* 0 */
+    const void *q;               /* [B, H, L, Dk] in_dtype */
+    const void *k;               /* [B, H, L, Dk] in_dtype (any key scaling is the caller's) */
+    const void *v;               /* [B, H, L, Dv] in_dtype */
+    const float *log_f;          /* [B, H, L] fp32 natural log of the forget gate, finite */
+    const float *log_i;          /* [B, H, L] fp32 natural log of the input gate, finite */
+    const float *initial_C;      /* [B, H, Dk, Dv] stabilised C', or NULL: the three initial  */
+    const float *initial_n;      /* [B, H, Dk] stabilised n'          fields are all given or */
+    const float *initial_m;      /* [B, H] m                          all NULL (zero state)  */
+    float *out;                  /* [B, H, L, Dv] */
+    float *final_C;              /* [B, H, Dk, Dv] stabilised C' after the last token, or NULL */
+    float *final_n;              /* [B, H, Dk] or NULL */
+    float *final_m;              /* [B, H] or NULL */
+} gla_mlstm_desc;
+
+/* mLSTM forward pass.  Support matrix (else GLA_ERR_UNSUPPORTED): chunk 64; bf16 inputs with
+ * Dk in {64, 128, 256}, fp32 inputs with Dk = 64; Dv a multiple of 64 up to 4096; L as for
+ * gla_fwd_ex.  One workgroup per (batch, head, 64 value columns) walks the whole sequence.
+ * GLA_ERR_INVALID_ARG: a NULL required pointer, non-positive sizes, a misaligned pointer
+ * (16 bytes), reserved != 0, or an initial state given in part.  Ownership and asynchrony as
+ * for gla_fwd_ex; allocates nothing.  Returns a gla_status. */
+int gla_mlstm_fwd(const gla_mlstm_desc *d, void *stream);
 
 /* Static English text for a status code (never NULL). */
 const char *gla_status_string(int status);

@@ -407,6 +407,63 @@ def test_delta_binding_rejects_mismatched_shapes(lib, name, shape):
         gla.delta_fwd(a["q"], a["k"], a["v"], a["beta"], a["log_alpha"], initial_state=a["initial_state"])
 
 
+def mlstm_desc(**kw):
+    d = gla.GlaMlstmDesc()
+    base = dict(B=2, H=3, L=100, Dk=128, Dv=128, chunk=64, in_dtype=gla.DTYPE_BF16, reserved=0,
+                q=A, k=A, v=A, log_f=A, log_i=A, initial_C=None, initial_n=None, initial_m=None, out=A,
+                final_C=None, final_n=None, final_m=None)
+    base.update(kw)
+    for key, val in base.items():
+        setattr(d, key, val)
+    return d
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), gla.GLA_ERR_INVALID_ARG), (dict(log_f=None), gla.GLA_ERR_INVALID_ARG),
+    (dict(log_i=None), gla.GLA_ERR_INVALID_ARG), (dict(out=None), gla.GLA_ERR_INVALID_ARG),
+    (dict(L=0), gla.GLA_ERR_INVALID_ARG), (dict(Dv=-64), gla.GLA_ERR_INVALID_ARG),
+    (dict(reserved=1), gla.GLA_ERR_INVALID_ARG), (dict(in_dtype=7), gla.GLA_ERR_INVALID_ARG),
+    (dict(initial_C=A), gla.GLA_ERR_INVALID_ARG),  # an initial state given in part
+    (dict(initial_C=A, initial_n=A), gla.GLA_ERR_INVALID_ARG),
+    (dict(log_i=A + 4), gla.GLA_ERR_INVALID_ARG), (dict(final_m=A + 8), gla.GLA_ERR_INVALID_ARG),
+    (dict(chunk=128), gla.GLA_ERR_UNSUPPORTED), (dict(chunk=32), gla.GLA_ERR_UNSUPPORTED),
+    (dict(Dk=96), gla.GLA_ERR_UNSUPPORTED), (dict(Dv=96), gla.GLA_ERR_UNSUPPORTED),
+    (dict(Dv=8192), gla.GLA_ERR_UNSUPPORTED), (dict(in_dtype=gla.DTYPE_F32, Dk=128), gla.GLA_ERR_UNSUPPORTED),
+])
+def test_mlstm_validation_before_any_hip_call(lib, kw, status):
+    assert lib.gla_mlstm_fwd(ctypes.byref(mlstm_desc(**kw)), None) == status
+    assert lib.gla_mlstm_fwd(None, None) == gla.GLA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("name,shape", [("k", (2, 3, 9, 64)), ("log_f", (2, 3, 9)), ("log_i", (2, 3, 10, 1)),
+                                        ("out", (2, 3, 10, 32))])
+def test_mlstm_binding_rejects_mismatched_shapes(lib, name, shape):
+    import torch
+
+    a = dict(q=torch.zeros(2, 3, 10, 64), k=torch.zeros(2, 3, 10, 64), v=torch.zeros(2, 3, 10, 64),
+             log_f=torch.zeros(2, 3, 10), log_i=torch.zeros(2, 3, 10), out=None)
+    a[name] = torch.zeros(shape)
+    with pytest.raises(ValueError, match=name):
+        gla.mlstm_fwd(a["q"], a["k"], a["v"], a["log_f"], a["log_i"], out=a["out"])
+
+
+@pytest.mark.parametrize("which,shape", [(0, (2, 3, 64, 32)), (1, (2, 3, 32)), (2, (2, 3, 1))])
+def test_mlstm_binding_rejects_mismatched_initial_state(lib, which, shape):
+    import torch
+
+    init = [torch.zeros(2, 3, 64, 64), torch.zeros(2, 3, 64), torch.zeros(2, 3)]
+    init[which] = torch.zeros(shape)
+    z = torch.zeros(2, 3, 10, 64)
+    with pytest.raises(ValueError, match="initial"):
+        gla.mlstm_fwd(z, z, z, torch.zeros(2, 3, 10), torch.zeros(2, 3, 10), initial_state=tuple(init))
+
+
+def test_mlstm_desc_layout_matches_header():
+    # the ctypes mirror of gla_mlstm_desc: eight int32 fields, then twelve pointers
+    assert ctypes.sizeof(gla.GlaMlstmDesc) == 8 * 4 + 12 * 8
+    assert gla.GlaMlstmDesc.q.offset == 32
+
+
 @pytest.mark.parametrize("chunk", [16, 32])
 def test_small_chunks_run_as_64_token_tiles(lib, chunk):
     # chunks of 16 and 32 tokens are accepted and planned as 64-token tiles (the same map)
