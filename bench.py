@@ -20,6 +20,11 @@ Reported beside the throughput:
   chunks unless the tile-pair form is selected).
 * ``cpu_baseline``: the fp64 oracle (the plain token recurrence) timed on this host's
   cores on the same workload, converted to the same unit.
+
+``--workload`` takes the gated linear attention workloads (default: the B8 H16 L2048 D128
+per-channel GLA), the delta-rule workloads (DeltaNet, Gated DeltaNet) and the mLSTM with
+exponential input gate and normaliser; ``--backward`` and ``--decode`` time the backward pass
+and the one-token step of a gated linear attention workload.
 """
 from __future__ import annotations
 
@@ -367,21 +372,37 @@ def delta_io_floor_bytes(w) -> float:
     return float(w.B * w.H * w.L) * per_ht + (w.B * w.H * w.Dk * w.Dv * 4 if w.final_state else 0)
 
 
-def delta_cpu_baseline(w, d, budget_s: float = 20.0) -> dict:
-    """The fp64 delta-rule oracle on a bounded sample of whole (batch, head) slices."""
+def mlstm_flops(w) -> float:
+    """Algorithmic flops of the chunkwise mLSTM with normaliser per step (C = 64 as executed):
+    per head-token 4 Dk Dv for the products with the state (q C', K^T V), (C+1)(Dk + Dv) for
+    the causal products inside a chunk (Q K^T, P V) and 4 Dk for the normaliser (q . n',
+    K^T weights).  The fp16 residual products the kernel adds for accuracy are not counted."""
+    C = 64
+    per = 4.0 * w.Dk * w.Dv + (C + 1) * (w.Dk + w.Dv) + 4.0 * w.Dk
+    return float(w.B * w.H * w.L) * per
+
+
+def mlstm_io_floor_bytes(w) -> float:
+    """q, k, v and both gates read once, the fp32 output and the stabilised final state
+    (C', n', m) written once."""
+    ib = 4 if w.dtype == "f32" else 2
+    per_ht = ib * (2 * w.Dk + w.Dv) + 8 + 4 * w.Dv
+    return float(w.B * w.H * w.L) * per_ht + w.B * w.H * (w.Dk * w.Dv + w.Dk + 1) * 4
+
+
+def rows_cpu_baseline(w, d, fn, what, budget_s: float = 20.0) -> dict:
+    """An fp64 oracle on a bounded sample of whole (batch, head) slices: ``fn(d, n)`` runs it on
+    the first ``n`` slices."""
     import oracle
 
     BH = w.B * w.H
     threads = oracle.threads()
-    sel = lambda t, n: None if t is None else t.reshape(-1, *t.shape[2:])[:n][None]
 
     def run(n, min_time=0.0):
-        q, k, v, be = (oracle.oracle._f64(sel(d[x], n)) for x in ("q", "k", "v", "beta"))
-        la = oracle.oracle._f64(sel(d["log_alpha"], n)) if w.gate == "head" else None
         reps, t = 0, 0.0
         while True:
             t0 = time.perf_counter()
-            oracle.delta_recurrent(q, k, v, be, la)
+            fn(d, n)
             t += time.perf_counter() - t0
             reps += 1
             if t >= min_time or reps >= 200:
@@ -394,13 +415,33 @@ def delta_cpu_baseline(w, d, budget_s: float = 20.0) -> dict:
     t, reps = run(n, min_time=0.5 * budget_s)
     return {"value": reps * n * w.L / t / w.H, "unit": "tokens/s", "cores": threads, "host_cpu": host_cpu_model(),
             "host_logical_cpus": os.cpu_count(), "kind": "oracle",
-            "sample": "%d of %d (batch, head) pairs at full length %d, %d repetition(s), fp64 delta-rule "
-                      "recurrence, %.2f s" % (n, BH, w.L, reps, t)}
+            "sample": "%d of %d (batch, head) pairs at full length %d, %d repetition(s), fp64 %s, %.2f s"
+                      % (n, BH, w.L, reps, what, t)}
 
 
-def delta_bench(args, torch, gla, gin, w, wname):
-    """A delta-rule workload (DeltaNet or Gated DeltaNet): a step is one ``gla_delta_fwd``
-    call (one kernel launch) on resident inputs; roofline against the I/O floor."""
+def _first_slices(t, n):
+    import oracle
+
+    return None if t is None else oracle.oracle._f64(t.reshape(-1, *t.shape[2:])[:n][None])
+
+
+def delta_oracle_sample(d, n):
+    import oracle
+
+    f = lambda key: _first_slices(d[key], n)
+    oracle.delta_recurrent(f("q"), f("k"), f("v"), f("beta"), f("log_alpha"))
+
+
+def mlstm_oracle_sample(d, n):
+    import oracle
+
+    f = lambda key: _first_slices(d[key], n)
+    oracle.mlstm_recurrent(f("q"), f("k"), f("v"), f("log_f"), f("log_i"))
+
+
+def rows_bench(args, torch, gla, gin, w, wname, rule):
+    """A delta-rule or mLSTM workload: a step is one call of its entry point (one kernel
+    launch) on resident inputs; roofline against the I/O floor."""
     import ctypes
 
     lib = gla.load()
@@ -411,15 +452,33 @@ def delta_bench(args, torch, gla, gin, w, wname):
     sets = [{k: (v.to(dev) if hasattr(v, "to") else v) for k, v in h.items() if v is not None} for h in host]
     out = torch.empty((w.B, w.H, w.L, w.Dv), dtype=torch.float32, device=dev)
     fin = torch.empty((w.B, w.H, w.Dk, w.Dv), dtype=torch.float32, device=dev)
-    descs = [gla.make_delta_desc(s["q"], s["k"], s["v"], s["beta"], s.get("log_alpha"), None, out, fin, w.chunk)
-             for s in sets]
+    if rule == "delta":
+        descs = [gla.make_delta_desc(s["q"], s["k"], s["v"], s["beta"], s.get("log_alpha"), None, out, fin, w.chunk)
+                 for s in sets]
+        entry, call = "gla_delta_fwd", lib.gla_delta_fwd
+        io, flops = delta_io_floor_bytes(w), delta_flops(w)
+        metric = "delta-rule fwd tokens/s (%s)" % ("Gated DeltaNet" if w.gate != "none" else "DeltaNet")
+        flops_note = "flops of the chunkwise WY form as executed (C = 64)"
+        kernel = "delta chunk kernel (the only launch of a step)"
+        oracle_fn, oracle_what = delta_oracle_sample, "delta-rule recurrence"
+    else:
+        fin3 = (fin, torch.empty((w.B, w.H, w.Dk), dtype=torch.float32, device=dev),
+                torch.empty((w.B, w.H), dtype=torch.float32, device=dev))
+        descs = [gla.make_mlstm_desc(s["q"], s["k"], s["v"], s["log_f"], s["log_i"], None, out, fin3, w.chunk)
+                 for s in sets]
+        entry, call = "gla_mlstm_fwd", lib.gla_mlstm_fwd
+        io, flops = mlstm_io_floor_bytes(w), mlstm_flops(w)
+        metric = "mLSTM (exponential input gate, normaliser) fwd tokens/s"
+        flops_note = "algorithmic flops of the chunkwise form (C = 64), residual products not counted"
+        kernel = "mLSTM chunk kernel (the only launch of a step)"
+        oracle_fn, oracle_what = mlstm_oracle_sample, "mLSTM recurrence"
     stream = torch.cuda.current_stream(dev)
     sptr = ctypes.c_void_p(stream.cuda_stream)
 
     def step(i):
-        st = lib.gla_delta_fwd(ctypes.byref(descs[i & 1]), sptr)
+        st = call(ctypes.byref(descs[i & 1]), sptr)
         if st != 0:
-            raise gla.GlaError(st, "gla_delta_fwd")
+            raise gla.GlaError(st, entry)
 
     for i in range(args.warmup):
         step(i)
@@ -438,15 +497,13 @@ def delta_bench(args, torch, gla, gin, w, wname):
     launch_ms = [a.elapsed_time(b) for a, b in ev]
     mean_ms = sum(launch_ms) / K
     med_ms, min_ms = quantiles(launch_ms)
-    io = delta_io_floor_bytes(w)
-    flops = delta_flops(w)
     achieved = io / (mean_ms * 1e-3) / 1e9
     cpu = None
     if not args.no_cpu_baseline:
         log("bench: timing the fp64 oracle on host cores")
-        cpu = delta_cpu_baseline(w, host[0])
+        cpu = rows_cpu_baseline(w, host[0], oracle_fn, oracle_what)
     rec = {
-        "metric": "delta-rule fwd tokens/s (%s)" % ("Gated DeltaNet" if w.gate != "none" else "DeltaNet"),
+        "metric": metric,
         "value": w.B * w.L / (ms_per_step * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -459,16 +516,15 @@ def delta_bench(args, torch, gla, gin, w, wname):
         "dtype": "bf16" if w.dtype == "bf16" else "f32",
         "data": "synthetic",
         "config": {"workload": wname, "B": w.B, "H": w.H, "L": w.L, "Dk": w.Dk, "Dv": w.Dv, "chunk": w.chunk,
-                   "rule": "delta", "gate": w.gate, "in_dtype": w.dtype,
+                   "rule": rule, "gate": w.gate, "in_dtype": w.dtype,
                    "matrix_operands": "fp16 from bf16" if w.dtype == "bf16" else "fp32", "accumulate": "fp32",
                    "out_dtype": "fp32", "workgroups": w.B * w.H * (w.Dv // 64)},
         "head_tokens_per_s": w.B * w.H * w.L / (ms_per_step * 1e-3),
         "tflops": round(flops / (mean_ms * 1e-3) / 1e12, 2),
-        "tflops_counts": "flops of the chunkwise WY form as executed (C = 64)",
+        "tflops_counts": flops_note,
         "pct_bf16_mfma_peak": round(100.0 * flops / (mean_ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
-                     "kernel": "delta chunk kernel (the only launch of a step)",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None, "kernel": kernel,
                      "algorithmic_bytes_per_launch": io, "extra_bytes": 0.0,
                      "median_launch_ms": round(med_ms, 5), "min_launch_ms": round(min_ms, 5),
                      "mean_launch_ms": round(mean_ms, 5),
@@ -514,7 +570,10 @@ def main():
 
     wname = args.workload or gin.HEADLINE
     if wname in gin.DELTA_WORKLOADS:
-        delta_bench(args, torch, gla, gin, gin.DELTA_WORKLOADS[wname], wname)
+        rows_bench(args, torch, gla, gin, gin.DELTA_WORKLOADS[wname], wname, "delta")
+        return
+    if wname in gin.MLSTM_WORKLOADS:
+        rows_bench(args, torch, gla, gin, gin.MLSTM_WORKLOADS[wname], wname, "mlstm")
         return
     w = gin.WORKLOADS[wname]
     if args.decode:
