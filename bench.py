@@ -85,12 +85,23 @@ def io_floor_bytes(w) -> float:
     return float(w.B * w.H * w.L) * per_ht + (w.B * w.H * w.Dk * w.Dv * 4 if w.final_state else 0)
 
 
-def kernel_source_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+# Source files of each kernel family; the committed counters are valid while they hash the same.
+KERNEL_SOURCES = {
+    "gla": ("gla_kernels.hip", "gla_layout.h"),
+    "delta": ("delta_kernels.hip", "gla_rows.h", "gla_delta.h"),
+    "mlstm": ("mlstm_kernels.hip", "gla_rows.h", "gla_mlstm.h"),
+}
 
 
-def measured_traffic(workload: str):
+def kernel_source_hash(family: str = "gla") -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[family]:
+        with open(os.path.join(os.path.dirname(KERNEL_SRC), name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str, family: str = "gla"):
     """HBM bytes per launch of the dominant kernel from committed rocprofv3 counters, if
     they were taken on the current kernel source."""
     try:
@@ -99,7 +110,7 @@ def measured_traffic(workload: str):
     except (OSError, ValueError):
         return None
     ent = rec.get(workload)
-    if not ent or ent.get("kernel_source_sha256_16") != kernel_source_hash():
+    if not ent or ent.get("kernel_source_sha256_16") != kernel_source_hash(family):
         return None
     return ent.get("bytes_per_launch")
 
@@ -524,7 +535,8 @@ def rows_bench(args, torch, gla, gin, w, wname, rule):
         "tflops_counts": flops_note,
         "pct_bf16_mfma_peak": round(100.0 * flops / (mean_ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None, "kernel": kernel,
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": measured_traffic(wname, rule),
+                     "kernel": kernel,
                      "algorithmic_bytes_per_launch": io, "extra_bytes": 0.0,
                      "median_launch_ms": round(med_ms, 5), "min_launch_ms": round(min_ms, 5),
                      "mean_launch_ms": round(mean_ms, 5),
