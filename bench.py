@@ -558,6 +558,9 @@ def main():
     ap.add_argument("--seg-chunks", type=int, default=0)
     ap.add_argument("--tile-pairs", action="store_true",
                     help="chunks > 64 tokens in the tile-pair (tiled large-chunk) form")
+    ap.add_argument("--query-tiles", action="store_true",
+                    help="the tile-pair form with one workgroup per query tile of a chunk against "
+                         "materialised chunk-start states")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain device copy of known size (HBM counter calibration)")
     ap.add_argument("--backward", action="store_true",
@@ -608,7 +611,8 @@ def main():
     descs = []
     for s in sets:
         descs.append(gla.make_desc(s["q"], s["k"], s["v"], s.get("log_alpha"), s.get("log_ig"), None, out, fin,
-                                   w.chunk, args.seg_chunks, tile_pairs=args.tile_pairs))
+                                   w.chunk, args.seg_chunks, tile_pairs=args.tile_pairs,
+                                   query_tiles=args.query_tiles))
     plan = gla.plan(descs[0])
     ws = None
     if plan.workspace_bytes:
@@ -667,10 +671,12 @@ def main():
         scope = "chunk-output kernel (the only launch of a step)"
     else:
         # sub-segment states per slice: written by the state kernel and read by the scan, which
-        # writes one state per segment boundary that the chunk-output kernel reads
+        # writes one state per segment boundary that the chunk-output kernel reads (once per
+        # query tile with --query-tiles; the re-reads of earlier tiles are not counted)
         nss = plan.grid_state // max(1, w.B * w.H * plan.dv_tiles)
+        qs = plan.tiles_per_chunk if plan.query_tiles else 1
         extra = float(w.B * w.H * w.L) * (plan.n_seg - 1) / plan.n_seg * (ib * (w.Dk + w.Dv) + gate) \
-            + float(w.B * w.H) * (2 * nss + 2 * (plan.n_seg - 1)) * (w.Dk * w.Dv + w.Dk) * 4
+            + float(w.B * w.H) * (2 * nss + (1 + qs) * (plan.n_seg - 1)) * (w.Dk * w.Dv + w.Dk) * 4
         scope = "whole step (segment-state, segment-scan and chunk-output kernels)"
     achieved = io / (mean_launch_ms * 1e-3) / 1e9
     traffic = measured_traffic(wname) if plan.n_seg == 1 else None
@@ -704,7 +710,8 @@ def main():
                    "gate": w.gate, "input_gate": w.input_gate, "in_dtype": w.dtype,
                    "matrix_operands": "fp16 from bf16" if w.dtype == "bf16" else "fp32",
                    "accumulate": "fp32", "out_dtype": "fp32", "n_seg": plan.n_seg,
-                   "tile_pairs": bool(plan.tile_pairs), "executed_chunk": exec_chunk,
+                   "tile_pairs": bool(plan.tile_pairs), "query_tiles": bool(plan.query_tiles),
+                   "executed_chunk": exec_chunk,
                    "workgroups": plan.grid_out},
         "head_tokens_per_s": value * w.H,
         "tflops": round(tflops, 2),

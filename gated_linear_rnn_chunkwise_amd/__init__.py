@@ -26,6 +26,7 @@ GLA_OK, GLA_ERR_INVALID_ARG, GLA_ERR_UNSUPPORTED, GLA_ERR_WORKSPACE, GLA_ERR_HIP
 DTYPE_BF16, DTYPE_F32 = 0, 1
 GATE_NONE, GATE_CHANNEL, GATE_HEAD, GATE_HEAD_CONST = 0, 1, 2, 3
 FLAG_TILE_PAIRS = 1
+FLAG_QUERY_TILES = 2
 GATE_NAMES = {"none": GATE_NONE, "channel": GATE_CHANNEL, "head": GATE_HEAD, "head_const": GATE_HEAD_CONST}
 
 # Entry points declared in include/gla.h.
@@ -52,7 +53,8 @@ class GlaPlan(ctypes.Structure):
     _fields_ = [
         ("seg_chunks", ctypes.c_int32), ("n_seg", ctypes.c_int32), ("dv_tiles", ctypes.c_int32),
         ("tiles_per_chunk", ctypes.c_int32), ("grid_state", ctypes.c_int32), ("grid_scan", ctypes.c_int32),
-        ("grid_out", ctypes.c_int32), ("tile_pairs", ctypes.c_int32), ("workspace_bytes", ctypes.c_size_t),
+        ("grid_out", ctypes.c_int32), ("tile_pairs", ctypes.c_int32), ("query_tiles", ctypes.c_int32),
+        ("workspace_bytes", ctypes.c_size_t),
     ]
 
 
@@ -181,7 +183,8 @@ def gate_kind_of(log_alpha, B: int, H: int, L: int, Dk: int) -> int:
 
 
 def make_desc(q, k, v, log_alpha=None, log_ig=None, initial_state=None, out=None, final_state=None, chunk=64,
-              seg_chunks=0, workspace=None, workspace_bytes=0, gate_kind=None, tile_pairs=False) -> GlaDesc:
+              seg_chunks=0, workspace=None, workspace_bytes=0, gate_kind=None, tile_pairs=False,
+              query_tiles=False) -> GlaDesc:
     """Fill a :class:`GlaDesc` from tensors (shapes read from q and v)."""
     import torch
 
@@ -200,7 +203,7 @@ def make_desc(q, k, v, log_alpha=None, log_ig=None, initial_state=None, out=None
     d.log_alpha, d.log_ig, d.initial_state = _ptr(log_alpha), _ptr(log_ig), _ptr(initial_state)
     d.out, d.final_state = _ptr(out), _ptr(final_state)
     d.seg_chunks = int(seg_chunks)
-    d.flags = FLAG_TILE_PAIRS if tile_pairs else 0
+    d.flags = (FLAG_TILE_PAIRS if tile_pairs else 0) | (FLAG_QUERY_TILES if query_tiles else 0)
     d.workspace = _ptr(workspace)
     d.workspace_bytes = int(workspace_bytes)
     return d
@@ -246,11 +249,13 @@ def _check_tensors(q, k, v, *others):
 
 
 def fwd(q, k, v, log_alpha=None, *, log_ig=None, initial_state=None, chunk: int = 64, final_state: bool = True,
-        seg_chunks: int = 0, out=None, workspace=None, stream=None, tile_pairs: bool = False):
+        seg_chunks: int = 0, out=None, workspace=None, stream=None, tile_pairs: bool = False,
+        query_tiles: bool = False):
     """Gated linear attention forward on the current HIP stream.
 
     ``tile_pairs`` selects the tiled large-chunk form for chunks of more than 64 tokens
-    (``GLA_FLAG_TILE_PAIRS``).  Returns ``(out [B,H,L,Dv] fp32, final_state [B,H,Dk,Dv] fp32 or None)``."""
+    (``GLA_FLAG_TILE_PAIRS``); ``query_tiles`` the same form with one workgroup per query
+    tile against materialised chunk-start states (``GLA_FLAG_QUERY_TILES``).  Returns ``(out [B,H,L,Dv] fp32, final_state [B,H,Dk,Dv] fp32 or None)``."""
     import torch
 
     lib = load()
@@ -263,7 +268,7 @@ def fwd(q, k, v, log_alpha=None, *, log_ig=None, initial_state=None, chunk: int 
     _check_tensors(q, k, v, log_alpha, log_ig, initial_state, out, fin)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     d = make_desc(q, k, v, log_alpha, log_ig, initial_state, out, fin, chunk, seg_chunks, workspace, ws_bytes,
-                  tile_pairs=tile_pairs)
+                  tile_pairs=tile_pairs, query_tiles=query_tiles)
     s = stream if stream is not None else torch.cuda.current_stream(q.device)
     st = lib.gla_fwd_ex(ctypes.byref(d), ctypes.c_void_p(s.cuda_stream))
     if st != GLA_OK:
@@ -272,7 +277,8 @@ def fwd(q, k, v, log_alpha=None, *, log_ig=None, initial_state=None, chunk: int 
 
 
 def fwd_noalloc(q, k, v, log_alpha=None, *, log_ig=None, initial_state=None, chunk: int = 64, out=None,
-                final_state=None, seg_chunks: int = 0, stream=None, tile_pairs: bool = False):
+                final_state=None, seg_chunks: int = 0, stream=None, tile_pairs: bool = False,
+                query_tiles: bool = False):
     """The forward pass through ``gla_fwd_noalloc``: no device memory is allocated by the
     library (its scratch is a fixed per-GPU array).  ``out`` and ``final_state`` (or None)
     are caller tensors, so nothing at all is allocated when both are given.  Returns
@@ -287,7 +293,7 @@ def fwd_noalloc(q, k, v, log_alpha=None, *, log_ig=None, initial_state=None, chu
         out = torch.empty((B, H, L, Dv), dtype=torch.float32, device=q.device)
     _check_tensors(q, k, v, log_alpha, log_ig, initial_state, out, final_state)
     d = make_desc(q, k, v, log_alpha, log_ig, initial_state, out, final_state, chunk, seg_chunks, None, 0,
-                  tile_pairs=tile_pairs)
+                  tile_pairs=tile_pairs, query_tiles=query_tiles)
     s = stream if stream is not None else torch.cuda.current_stream(q.device)
     st = lib.gla_fwd_noalloc(ctypes.byref(d), ctypes.c_void_p(s.cuda_stream))
     if st != GLA_OK:

@@ -53,6 +53,7 @@ constexpr int64_t kSmallProblem = 65536;   // head-tokens below which segmenting
 struct Plan {
     int nt, nc, ndv, seg_chunks, nseg, seg_len, nsub;
     int knt;  // 64-token tiles per chunk as the kernels run it: nt with tile pairs, else 1
+    int qsplit;  // workgroups per chunk and value tile: knt with query tiles, else 1
     int grid_state, grid_scan, grid_out;
     size_t ws_state_bytes, ws_decay_bytes, ws_ke_bytes, ws_bytes;
     uint32_t lds_out, lds_state;
@@ -66,7 +67,10 @@ int validate(const gla_desc *d) {
     if (!d) return GLA_ERR_INVALID_ARG;
     if (!d->q || !d->k || !d->v || !d->out) return GLA_ERR_INVALID_ARG;
     if (d->B <= 0 || d->H <= 0 || d->L <= 0 || d->Dk <= 0 || d->Dv <= 0 || d->chunk <= 0) return GLA_ERR_INVALID_ARG;
-    if (d->seg_chunks < 0 || (d->flags & ~int32_t(GLA_FLAG_TILE_PAIRS)) != 0) return GLA_ERR_INVALID_ARG;
+    if (d->seg_chunks < 0 || (d->flags & ~int32_t(GLA_FLAG_TILE_PAIRS | GLA_FLAG_QUERY_TILES)) != 0)
+        return GLA_ERR_INVALID_ARG;
+    // query tiles make every chunk its own segment
+    if ((d->flags & GLA_FLAG_QUERY_TILES) && d->seg_chunks > 1) return GLA_ERR_INVALID_ARG;
     if (d->in_dtype != GLA_DTYPE_BF16 && d->in_dtype != GLA_DTYPE_F32) return GLA_ERR_INVALID_ARG;
     if (d->gate_kind < GLA_GATE_NONE || d->gate_kind > GLA_GATE_HEAD_CONST) return GLA_ERR_INVALID_ARG;
     if ((d->gate_kind == GLA_GATE_NONE) != (d->log_alpha == nullptr)) return GLA_ERR_INVALID_ARG;
@@ -101,13 +105,17 @@ int make_plan(const gla_desc *d, Plan *p) {
     const bool ch = d->gate_kind == GLA_GATE_CHANNEL;
     p->nt = chunk / gla::kTile;
     // Without tile pairs the state is advanced tile by tile: the kernels walk 64-token chunks.
-    p->knt = (d->flags & GLA_FLAG_TILE_PAIRS) ? p->nt : 1;
+    const bool qtiles = (d->flags & GLA_FLAG_QUERY_TILES) != 0;
+    p->knt = (d->flags & (GLA_FLAG_TILE_PAIRS | GLA_FLAG_QUERY_TILES)) ? p->nt : 1;
+    p->qsplit = qtiles ? p->knt : 1;
     p->nc = (d->L + chunk - 1) / chunk;
     p->ndv = d->Dv / gla::kDvTile;
     const int64_t bh = int64_t(d->B) * d->H;
     const int64_t wg1 = bh * p->ndv;
     int sc;
-    if (d->seg_chunks > 0) {
+    if (qtiles) {
+        sc = 1;  // the chunk-start states are materialised by the segment-state kernel and scan
+    } else if (d->seg_chunks > 0) {
         sc = std::min(d->seg_chunks, p->nc);
     } else if (wg1 >= kTargetWorkgroups || bh * d->L <= kSmallProblem) {
         sc = p->nc;
@@ -131,7 +139,7 @@ int make_plan(const gla_desc *d, Plan *p) {
         p->nsub = (int)std::max<int64_t>(1, std::min<int64_t>(want, tiles));
     }
     const int64_t nss = int64_t(p->nseg - 1) * p->nsub;
-    const int64_t g3 = bh * p->nseg * p->ndv;
+    const int64_t g3 = bh * p->nseg * p->ndv * p->qsplit;
     const int64_t g1 = p->nseg > 1 ? bh * nss * p->ndv : 0;
     if (g3 > INT32_MAX || g1 > INT32_MAX) return GLA_ERR_UNSUPPORTED;
     p->grid_out = (int)g3;
@@ -149,7 +157,9 @@ int make_plan(const gla_desc *d, Plan *p) {
     p->ws_state_bytes = align256(size_t(bh) * size_t(nss) * size_t(d->Dk) * size_t(d->Dv) * 4u);
     p->ws_decay_bytes = align256(size_t(bh) * size_t(nss) * size_t(d->Dk) * 4u);
     if (p->nseg <= 1) p->ws_state_bytes = p->ws_decay_bytes = 0;
-    p->ws_ke_bytes = align256(size_t(g3) * (size_t)gla::ke_scratch_bytes(opb, d->Dk, ch, p->knt));
+    // key scratch: one slot per output workgroup, or per (batch, head, chunk) with query tiles
+    const int64_t ke_slots = p->qsplit > 1 ? bh * p->nseg : g3;
+    p->ws_ke_bytes = align256(size_t(ke_slots) * (size_t)gla::ke_scratch_bytes(opb, d->Dk, ch, p->knt));
     p->ws_bytes = p->ws_state_bytes + p->ws_decay_bytes + p->ws_ke_bytes;
     return GLA_OK;
 }
@@ -199,6 +209,7 @@ int gla_query_plan(const gla_desc *d, gla_plan *out) {
     out->grid_scan = p.grid_scan;
     out->grid_out = p.grid_out;
     out->tile_pairs = p.knt > 1 ? 1 : 0;
+    out->query_tiles = p.qsplit > 1 ? 1 : 0;
     out->workspace_bytes = p.ws_bytes;
     return GLA_OK;
 }
@@ -257,6 +268,7 @@ int fwd_run(const gla_desc *d, int h16, void *stream, const OutMapArgs &om = Out
     a.Dv = d->Dv;
     a.chunk = gla::kTile * p.knt;
     a.nt = p.knt;
+    a.qsplit = p.qsplit;
     a.gate = d->gate_kind;
     a.seg_len = p.seg_len;
     a.nseg = p.nseg;

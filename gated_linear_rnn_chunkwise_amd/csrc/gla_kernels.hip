@@ -654,7 +654,14 @@ __device__ __forceinline__ Pairs make_pairs(int w, bool ch) {
 }
 
 // ------------------------------------------------------------------------------------
-// chunk_output_kernel: grid = BH * nseg * ndv workgroups of 256 threads.
+// chunk_output_kernel: grid = BH * nseg * ndv (* qsplit) workgroups of 256 threads.
+// With a.qsplit > 1 (large chunks, every chunk its own segment) the workgroups of one chunk
+// each output one query tile qi against the chunk-start state from the scan: the second level
+// of sequence parallelism of the tiled large-chunk form.  Workgroup qi prepares tiles
+// 0 .. qi (their decays, and for a per-channel gate their scaled keys, which every workgroup
+// of the chunk writes to the same scratch slot with the same bytes) and runs the products of
+// tile qi only; the workgroup of the last tile of the last chunk also advances the state to
+// the final state.
 template <class C>
 __global__ __launch_bounds__(256, 1) void chunk_output_kernel(KArgs a) {
     static_assert(C::H16 == 0, "the backward pass's instances run the ws and sg kernels");
@@ -682,6 +689,12 @@ __global__ __launch_bounds__(256, 1) void chunk_output_kernel(KArgs a) {
     int id = xcd_remap(wg, a.nwg);
     const int dvt = id % a.ndv;
     id /= a.ndv;
+    const bool qs = C::MT && a.qsplit > 1;
+    int qi = 0;  // with qs: the query tile this workgroup outputs
+    if (qs) {
+        qi = id % a.qsplit;
+        id /= a.qsplit;
+    }
     const int seg = id % a.nseg;
     const int bh = id / a.nseg;
     const int h = bh % a.H;
@@ -692,12 +705,18 @@ __global__ __launch_bounds__(256, 1) void chunk_output_kernel(KArgs a) {
     const int col = dv0 + 16 * w + c16;  // value column of this lane's accumulators
     const int t_begin = seg * a.seg_len;
     const int t_end = min(L, t_begin + a.seg_len);
+    // with qs the segment is one chunk; a tile past the sequence end has nothing to output
+    if (qs && t_begin + kTile * qi >= t_end) return;
+    const bool last_seg = seg == a.nseg - 1;
+    // with qs, the workgroup of the last tile of the last chunk also advances the state
+    const bool fin_wg = !qs || (last_seg && t_begin + kTile * (qi + 1) >= t_end);
     const int chl = C::CPL * lane;
     const Rs rs = make_rs<C>(a, bh, h);
     rsrc_t rke = make_rsrc(a.out, 0);
     if constexpr (C::CH && C::MT) {
         const uint64_t kb = ke_scratch_bytes(C::OPB, C::DK, true, a.nt);
-        rke = make_rsrc(reinterpret_cast<char *>(a.ws_ke) + (uint64_t)wg * kb, kb);
+        const uint64_t slot = qs ? (uint64_t)bh * a.nseg + seg : (uint64_t)wg;
+        rke = make_rsrc(reinterpret_cast<char *>(a.ws_ke) + slot * kb, kb);
     }
 
     // State S[d][col], d = 16n + 4g + e, held across chunks in registers.
@@ -732,9 +751,12 @@ __global__ __launch_bounds__(256, 1) void chunk_output_kernel(KArgs a) {
             for (int n = 0; n < C::NBD; ++n) dS[n] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
         const int ntile = min(a.nt, (t_end - c0 + kTile - 1) / kTile);
+        const int tau_end = qs ? qi + 1 : ntile;
 
-        for (int tau = 0; tau < ntile; ++tau) {
+        for (int tau = 0; tau < tau_end; ++tau) {
             const int T0 = c0 + kTile * tau;
+            // with qs only tile qi is output; the tiles before it are prepared for its pairs
+            const bool out_tile = !qs || tau == qi;
             f32x4 O[4];
             f32x4 Pd[3];
 #pragma unroll
@@ -885,7 +907,7 @@ __global__ __launch_bounds__(256, 1) void chunk_output_kernel(KArgs a) {
                 }
 
                 // ---------------- diagonal-tile score blocks (transposed): P^T(j,i) over this slab
-                {
+                if (out_tile) {
                     const Pairs pr = make_pairs(w, C::CH);
                     const OpT *pa[3], *pb[3];
 #pragma unroll
@@ -910,7 +932,7 @@ __global__ __launch_bounds__(256, 1) void chunk_output_kernel(KArgs a) {
                 }
 
                 // ---------------- inter-chunk term: O += QI . S (rows of this slab)
-                {
+                if (out_tile) {
                     Frag sb[C::KSTEP];
 #pragma unroll
                     for (int m = 0; m < C::KSTEP; ++m) {
@@ -935,7 +957,7 @@ __global__ __launch_bounds__(256, 1) void chunk_output_kernel(KArgs a) {
                 }
 
                 // ---------------- chunk-state contribution of this tile (rows of this slab)
-                {
+                if (fin_wg) {
                     f32x4 acc[C::NBS];
 #pragma unroll
                     for (int n = 0; n < C::NBS; ++n) {
@@ -970,7 +992,7 @@ __global__ __launch_bounds__(256, 1) void chunk_output_kernel(KArgs a) {
             }  // slabs
 
             // ---------------- diagonal tile: mask, store scores, multiply by values
-            {
+            if (out_tile) {
                 const Pairs pr = make_pairs(w, C::CH);
 #pragma unroll
                 for (int kp = 0; kp < 3; ++kp) {
@@ -998,7 +1020,7 @@ __global__ __launch_bounds__(256, 1) void chunk_output_kernel(KArgs a) {
                 }
             }
             lds_barrier();
-            {
+            if (out_tile) {
                 Frag pa[6];
                 pa[0] = ld8<C>(sP + ((0 * 2 + 0) * 64 + lane) * 8);
                 pa[1] = ld8<C>(sP + ((1 * 2 + 0) * 64 + lane) * 8);
@@ -1013,7 +1035,7 @@ __global__ __launch_bounds__(256, 1) void chunk_output_kernel(KArgs a) {
             }
 
             // ---------------- earlier tiles of the same chunk (large chunks)
-            if constexpr (C::MT) {
+            if (C::MT && out_tile) {
 #pragma unroll 1
                 for (int kj = 0; kj < tau; ++kj) {
                     lds_barrier();  // previous readers of sP / sVo are done
@@ -1099,7 +1121,7 @@ __global__ __launch_bounds__(256, 1) void chunk_output_kernel(KArgs a) {
             }
 
             // ---------------- store the tile's outputs (rows past the sequence end are dropped)
-            {
+            if (out_tile) {
                 const uint32_t ob = ((uint32_t)(T0 + 4 * g) * Dv + col) * 4u;
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
@@ -1112,7 +1134,7 @@ __global__ __launch_bounds__(256, 1) void chunk_output_kernel(KArgs a) {
             lds_barrier();  // LDS tile arrays are rewritten by the next unit
         }  // tiles
 
-        if constexpr (C::MT) {
+        if (C::MT && fin_wg) {
             // end of a multi-tile chunk: S <- diag(decay across the chunk) S + dS
 #pragma unroll
             for (int n = 0; n < C::NBD; ++n) {
@@ -1130,7 +1152,7 @@ __global__ __launch_bounds__(256, 1) void chunk_output_kernel(KArgs a) {
         }
     }  // chunks
 
-    if (seg == a.nseg - 1 && a.fin) {
+    if (last_seg && fin_wg && a.fin) {
 #pragma unroll
         for (int n = 0; n < C::NBD; ++n)
 #pragma unroll
@@ -2462,7 +2484,7 @@ static hipError_t launch_cfg(const KArgs &a, hipStream_t st) {
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
     KArgs a3 = a;
-    a3.nwg = (a.B * a.H) * a.nseg * a.ndv;
+    a3.nwg = (a.B * a.H) * a.nseg * a.ndv * (a.qsplit > 1 ? a.qsplit : 1);
     if constexpr (!C::F32 && !C::CH && !C::MT && C::DK == 256) {
         const LdsPlanSg lg = lds_plan_sg(C::DK);
         static std::atomic<uint64_t> done_sg{0};

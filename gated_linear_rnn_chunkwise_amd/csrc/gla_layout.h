@@ -254,9 +254,11 @@ struct KArgs {
     float *ws_state;  // [BH][(nseg-1)*nsub][Dk][Dv]: local sub-segment states; the scan writes the
                       // state entering segment s over entry s*nsub-1
     float *ws_decay;  // [BH][(nseg-1)*nsub][Dk]: decay across each sub-segment
-    void *ws_ke;      // [nwg][nt-1][64][Dk] operand scratch (per-channel gate, several tiles per chunk)
+    void *ws_ke;      // [slots][nt-1][64][Dk] operand scratch (per-channel gate, several tiles per
+                      // chunk): one slot per workgroup, or per (batch, head, chunk) with qsplit
     int B, H, L, Dv;
     int chunk, nt;    // chunk size as the kernels run it and its 64-token tiles
+    int qsplit;       // > 1: one workgroup per query tile of a chunk (each chunk its own segment)
     int gate;         // enum gla_gate
     int seg_len;      // tokens per segment (a multiple of the chunk size)
     int nseg, ndv;    // segments; 64-column value tiles

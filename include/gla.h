@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define GLA_VERSION 10500 /* major * 10000 + minor * 100 + patch */
+#define GLA_VERSION 10600 /* major * 10000 + minor * 100 + patch */
 
 /* Status codes.  0 is success; errors are negative. */
 enum gla_status {
@@ -92,7 +92,16 @@ enum gla_flag {
      * 64-token tile and those terms come through it; both forms give the same result up to
      * rounding, and without the flag fewer operations are needed because the state never
      * leaves the registers. */
-    GLA_FLAG_TILE_PAIRS = 1
+    GLA_FLAG_TILE_PAIRS = 1,
+    /* The tile-pair form with its second level of sequence parallelism [Tiled Flash Linear
+     * Attention, abstract: parallelism inside each chunk]: every chunk is its own segment
+     * (its start state is materialised by the segment-state pass and scan; seg_chunks must
+     * be 0 or 1, else GLA_ERR_INVALID_ARG), and each 64-token query tile of a chunk is
+     * computed by a workgroup of its own against that state, with tile pairs for the earlier
+     * tiles of the chunk.  Implies GLA_FLAG_TILE_PAIRS.  Same result up to rounding; it moves
+     * more bytes than either form above (the chunk states are written, scanned and read once
+     * per query tile, and each query tile re-reads the earlier tiles of its chunk). */
+    GLA_FLAG_QUERY_TILES = 2
 };
 
 /* Full description of one forward call. */
@@ -127,6 +136,7 @@ typedef struct gla_plan {
     int32_t grid_scan;       /* workgroups of the segment-scan kernel (0 if not launched) */
     int32_t grid_out;        /* workgroups of the chunk-output kernel */
     int32_t tile_pairs;      /* 1 if the tile-pair form runs (GLA_FLAG_TILE_PAIRS and chunk > 64) */
+    int32_t query_tiles;     /* 1 if each query tile has a workgroup (GLA_FLAG_QUERY_TILES, chunk > 64) */
     size_t workspace_bytes;  /* device scratch the call needs (0 = none) */
 } gla_plan;
 
@@ -148,7 +158,7 @@ int gla_fwd(const void *q, const void *k, const void *v, const float *log_alpha,
  * (L + 1024) * max(Dk, Dv) * 4 < 2^32 (one (batch, head) slice is addressed with 32-bit
  * byte offsets, which allows L up to about 1M for Dv = 1024); and the operand tiles of
  * one workgroup must fit the 160 KB of LDS of a compute unit.  That last rule only bites
- * with GLA_FLAG_TILE_PAIRS and fp32 inputs: chunk > 64 is then unsupported for Dk = 256,
+ * with GLA_FLAG_TILE_PAIRS or GLA_FLAG_QUERY_TILES and fp32 inputs: chunk > 64 is then unsupported for Dk = 256,
  * and for Dk = 128 under a per-channel gate.  Returns a gla_status. */
 int gla_fwd_ex(const gla_desc *d, void *stream);
 

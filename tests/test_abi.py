@@ -81,7 +81,7 @@ def test_valid_descriptor_plans(lib):
 
 @pytest.mark.parametrize("field,value", [
     ("q", None), ("k", None), ("v", None), ("out", None),
-    ("B", 0), ("H", -1), ("L", 0), ("Dk", 0), ("Dv", 0), ("chunk", 0), ("seg_chunks", -1), ("flags", 2), ("flags", -1),
+    ("B", 0), ("H", -1), ("L", 0), ("Dk", 0), ("Dv", 0), ("chunk", 0), ("seg_chunks", -1), ("flags", 4), ("flags", -1),
     ("in_dtype", 7), ("gate_kind", 9), ("log_alpha", None),
     ("q", A + 2), ("v", A + 8), ("out", A + 4), ("log_alpha", A + 4), ("final_state", A + 12),
     ("initial_state", A + 1), ("log_ig", A + 2),
@@ -204,6 +204,32 @@ def test_tile_pair_flag_in_plan(lib):
         # per-channel gate, tile pairs: keys of the earlier tiles of a chunk go to scratch
         assert p1.workspace_bytes == (0 if chunk == 64 else
                                       (p1.grid_out * (chunk // 64 - 1) * 64 * 128 * 2 + 255) // 256 * 256)
+
+
+def test_query_tile_flag_in_plan(lib):
+    # one workgroup per (batch, head, chunk, query tile, value tile); every chunk is its own
+    # segment, whose start state the segment-state kernel and scan materialise
+    QT = gla.FLAG_QUERY_TILES
+    B, H, L, Dk, Dv = 2, 3, 4096 + 100, 128, 128
+    for chunk in (64, 128, 256, 512):
+        nc = -(-L // chunk)
+        nt = chunk // 64
+        for gate in (gla.GATE_CHANNEL, gla.GATE_HEAD):
+            p = gla.plan(desc(B=B, H=H, L=L, Dk=Dk, Dv=Dv, chunk=chunk, gate_kind=gate, flags=QT))
+            assert p.seg_chunks == 1 and p.n_seg == nc and p.tiles_per_chunk == nt
+            assert p.tile_pairs == (1 if nt > 1 else 0) and p.query_tiles == (1 if nt > 1 else 0)
+            assert p.grid_out == B * H * nc * (Dv // 64) * nt
+            # chunk states: (nc - 1) boundaries, one sub-segment each at this size
+            nss = p.grid_state // (B * H * (Dv // 64))
+            al = lambda x: (x + 255) // 256 * 256
+            ke = al(B * H * nc * (nt - 1) * 64 * Dk * 2) if gate == gla.GATE_CHANNEL else 0
+            assert p.workspace_bytes == al(B * H * nss * Dk * Dv * 4) + al(B * H * nss * Dk * 4) + ke
+    # seg_chunks other than 0 or 1 contradicts one chunk per segment
+    assert status(lib, desc(chunk=128, flags=QT, seg_chunks=2))[0] == gla.GLA_ERR_INVALID_ARG
+    assert status(lib, desc(chunk=128, flags=QT, seg_chunks=1))[0] == gla.GLA_OK
+    assert status(lib, desc(chunk=128, flags=QT | gla.FLAG_TILE_PAIRS))[0] == gla.GLA_OK
+    # the tile-pair LDS limit applies unchanged
+    assert status(lib, desc(Dk=128, chunk=128, in_dtype=gla.DTYPE_F32, flags=QT))[0] == gla.GLA_ERR_UNSUPPORTED
 
 
 def step_desc(**kw):

@@ -30,14 +30,16 @@ def gate_name(w):
     return w.gate
 
 
-def run_gpu(gla, d, w, chunk=None, seg_chunks=0, initial_state=None, final_state=True, tile_pairs=False):
+def run_gpu(gla, d, w, chunk=None, seg_chunks=0, initial_state=None, final_state=True, tile_pairs=False,
+            query_tiles=False):
     dev = "cuda"
     q, k, v = (d[x].to(dev) for x in "qkv")
     la = None if d["log_alpha"] is None else d["log_alpha"].to(dev)
     li = None if d["log_ig"] is None else d["log_ig"].to(dev)
     s0 = None if initial_state is None else initial_state.to(dev)
     out, fin = gla.fwd(q, k, v, la, log_ig=li, initial_state=s0, chunk=chunk or w.chunk,
-                       final_state=final_state, seg_chunks=seg_chunks, tile_pairs=tile_pairs)
+                       final_state=final_state, seg_chunks=seg_chunks, tile_pairs=tile_pairs,
+                       query_tiles=query_tiles)
     torch.cuda.synchronize()
     return out.cpu().double().numpy(), None if fin is None else fin.cpu().double().numpy()
 
@@ -61,13 +63,13 @@ for dtype in ("bf16", "f32"):
                 SMALL.append((dtype, gate, ig, Dk, Dv, chunk))
 
 
-def supported(gla, w, tile_pairs=False):
+def supported(gla, w, tile_pairs=False, query_tiles=False):
     """Status of the library's own support check for a workload (no GPU work)."""
     d = gin.make_inputs(w.with_(L=1), seed=0)
     t = {k: v for k, v in d.items()}
     out = torch.empty(w.B, w.H, 1, w.Dv)
     desc = gla.make_desc(t["q"], t["k"], t["v"], t["log_alpha"], t["log_ig"], None, out, None, w.chunk,
-                         tile_pairs=tile_pairs)
+                         tile_pairs=tile_pairs, query_tiles=query_tiles)
     try:
         gla.workspace_size(desc)
         return True
@@ -113,6 +115,37 @@ def test_small_shapes_tile_pairs(gpu_lib, dtype, gate, ig, Dk, Dv, chunk, L):
     d = gin.make_inputs(w, seed=L)
     out, fin = run_gpu(gpu_lib, d, w, tile_pairs=True)
     ref, rfin = run_oracle(d, w)
+    check(w, out, ref)
+    check(w, fin, rfin, "final_state")
+
+
+@pytest.mark.parametrize("dtype,gate,ig,Dk,Dv,chunk", SMALL)
+@pytest.mark.parametrize("L", [100, 333])
+def test_small_shapes_query_tiles(gpu_lib, dtype, gate, ig, Dk, Dv, chunk, L):
+    # the tiled large-chunk form with one workgroup per query tile of a chunk, every chunk its
+    # own segment (chunk-start states from the segment-state kernel and scan); ragged tails
+    # leave the last chunk with fewer tiles than the others
+    w = gin.custom(2, 2, L, Dk, Dv, chunk, dtype=dtype, gate=gate, input_gate=ig)
+    if not supported(gpu_lib, w, query_tiles=True):
+        assert dtype == "f32" and chunk > 64
+        pytest.skip("configuration reported unsupported (LDS budget)")
+    d = gin.make_inputs(w, seed=L + 1)
+    out, fin = run_gpu(gpu_lib, d, w, query_tiles=True)
+    ref, rfin = run_oracle(d, w)
+    check(w, out, ref)
+    check(w, fin, rfin, "final_state")
+
+
+@pytest.mark.parametrize("gate,ig,chunk,L", [("channel", True, 256, 1000), ("head", True, 512, 1200),
+                                             ("head_const", False, 128, 777), ("none", False, 256, 64 * 12)])
+def test_query_tiles_initial_state(gpu_lib, gate, ig, chunk, L):
+    # chunk-start states built on a given initial state; the final state comes from the
+    # workgroup of the last tile of the last chunk
+    w = gin.custom(1, 3, L, 128, 128, chunk, gate=gate, input_gate=ig)
+    d = gin.make_inputs(w, seed=11)
+    s0 = torch.randn(1, 3, 128, 128, generator=torch.Generator().manual_seed(5)) * 0.1
+    out, fin = run_gpu(gpu_lib, d, w, initial_state=s0, query_tiles=True)
+    ref, rfin = run_oracle(d, w, initial_state=s0)
     check(w, out, ref)
     check(w, fin, rfin, "final_state")
 
@@ -248,15 +281,18 @@ def test_caller_workspace(gpu_lib):
 # Every full-size workload in the launch configuration bench.py times, compared whole: every
 # (batch, head) slice of the output and of the final state, with RMS over the whole tensor.
 FULL = [
-    ("ungated_f32_L256", False),
-    ("gla_bf16_B8H16L2048", False),
-    ("retnet_bf16_B4H8L8192", False),
-    ("retnet_bf16_B4H8L8192", True),
-    ("long_gla_bf16_H16L32768_C64", False),
-    ("long_gla_bf16_H16L32768_C256", False),
-    ("long_gla_bf16_H16L32768_C256", True),
-    ("mlstm_sig_bf16_B8H8L8192", False),
-    ("mlstm_sig_bf16_B8H8L8192", True),
+    ("ungated_f32_L256", ""),
+    ("gla_bf16_B8H16L2048", ""),
+    ("retnet_bf16_B4H8L8192", ""),
+    ("retnet_bf16_B4H8L8192", "tile_pairs"),
+    ("retnet_bf16_B4H8L8192", "query_tiles"),
+    ("long_gla_bf16_H16L32768_C64", ""),
+    ("long_gla_bf16_H16L32768_C256", ""),
+    ("long_gla_bf16_H16L32768_C256", "tile_pairs"),
+    ("long_gla_bf16_H16L32768_C256", "query_tiles"),
+    ("mlstm_sig_bf16_B8H8L8192", ""),
+    ("mlstm_sig_bf16_B8H8L8192", "tile_pairs"),
+    ("mlstm_sig_bf16_B8H8L8192", "query_tiles"),
 ]
 _FULL_REF = {}
 
@@ -271,12 +307,12 @@ def full_reference(w, d):
     return _FULL_REF[key]
 
 
-@pytest.mark.parametrize("name,tile_pairs", FULL, ids=[f[0] + ("_tile_pairs" if f[1] else "") for f in FULL])
-def test_full_workload_whole_tensor(gpu_lib, name, tile_pairs):
+@pytest.mark.parametrize("name,form", FULL, ids=[f[0] + ("_" + f[1] if f[1] else "") for f in FULL])
+def test_full_workload_whole_tensor(gpu_lib, name, form):
     w = gin.WORKLOADS[name]
     d = gin.make_inputs(w, seed=0)
-    print("full workload %s tile_pairs=%s" % (name, tile_pairs), flush=True)
-    out, fin = run_gpu(gpu_lib, d, w, tile_pairs=tile_pairs)
+    print("full workload %s %s" % (name, form or "default"), flush=True)
+    out, fin = run_gpu(gpu_lib, d, w, tile_pairs=form == "tile_pairs", query_tiles=form == "query_tiles")
     ref, rfin = full_reference(w, d)
     e = check(w, out, ref)
     ef = check(w, fin, rfin, "final_state")
