@@ -177,6 +177,15 @@ __device__ __forceinline__ T lds_ld(const void *p) {
     return *reinterpret_cast<const T *>(p);
 }
 
+// Transposing LDS read of 16-bit operands (gfx950): within each group of 16 lanes, lane
+// 4e + q supplies the address of 4 consecutive elements and lane j receives element j & 3 of
+// the vectors of lanes (j >> 2), 4 + (j >> 2), 8 + (j >> 2), 12 + (j >> 2), in that order.
+__device__ __forceinline__ f16x4 lds_tr16(const f16 *p) {
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    const auto lp = (__attribute__((address_space(3))) s16x4 *)(p);
+    return __builtin_bit_cast(f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(lp));
+}
+
 // 8 consecutive operands (16 B fp16, 32 B fp32) from LDS.
 template <class C>
 __device__ __forceinline__ typename C::Frag ld8(const typename C::OpT *p) {
@@ -1894,21 +1903,28 @@ __global__ __launch_bounds__(512, 1) void chunk_output_ws_kernel(KArgs a) {
 //
 // Producers (waves 4..7): wave pw owns the 16 rows of block pw and lane l the channels
 // 4l .. 4l+3, so every load covers a whole row and a lane owns consecutive tokens of its
-// channels for the transposed key operand.  Consumers (waves
-// 0..3): 16 value columns each, the Dk x 16 state in registers.  Per tile k:
-//   phase A  consumers: score blocks (q, k), O = diag(2^b) (q . S), state update
-//            S <- 2^T S + (k 2^(T - b + l))^T v    (q, k, k^T: single buffers;
-//            values and row decays: buffer k&1)
-//            producers: decay scan, values and row decays of tile k+1 into buffer (k+1)&1,
-//            fp16 q, k and scaled k^T of tile k+1 into registers; loads of tile k+2
+// channels for the transposed keys.  Consumers (waves 0..3): 16 value columns each, the
+// Dk x 16 state in registers.  Per tile k:
+//   phase A  consumers: score blocks (q, and the keys read transposed from k^T), O =
+//            diag(2^b) (q . S), state update S <- 2^T S + k^T (diag(w) v) with the key
+//            weights w = 2^(T - b + l) on the value operand (q, values and rows: buffer
+//            k&1; k^T: single buffer)
+//            producers: decay scan, values, rows and fp16 q of tile k+1 into buffer
+//            (k+1)&1, fp16 keys of tile k+1 into registers; loads of tile k+2
 //   B1
 //   phase B  consumers: masked scores x values, output stores
-//            producers: q, k, k^T of tile k+1 into the single buffers
+//            producers: k^T of tile k+1 into the single buffer
 //   B2
 // With a scalar gate the queries need no scaling to the tile start: the inter-chunk
 // product takes raw q and its output rows are scaled by 2^(b_t) in fp32.
-// q and k rows hold their channels in the chperm order, k^T and the value tile use the
-// kt_off and vsw swizzles.
+// q rows hold their channels in the chperm order; k^T rows (one per channel) hold their
+// tokens in k-slot order, with the 16-byte units of a row XOR-swizzled by bits 2-4 of the
+// row and a row pitch of 96 halves: the state update's 16-byte reads (16 consecutive rows,
+// one unit each) and the transposed 8-byte reads of the score products (4 consecutive rows
+// times 4 consecutive units) then both fall on distinct LDS banks.  The value tile uses the
+// vsw swizzle.
+
+__device__ __forceinline__ int kt_off_sg(int r, int s) { return r * 96 + ((((s >> 3) ^ (r >> 2)) & 7) << 3) + (s & 7); }
 
 template <class C>
 struct RawSg {
@@ -1944,11 +1960,10 @@ __device__ __forceinline__ void load_unit_sg(RawSg<C> &r, const Rs &rs, int T0, 
 
 template <class C>
 struct ProdSg {
-    u32x2 qh[16], kh[16];  // fp16 q, k of rows 16 pw + rr (4 channels)
-    f16x4 kt[4][4];        // [channel][token group]: scaled keys of 4 consecutive tokens
+    f16x4 kt[4][4];  // [channel][token group]: fp16 keys of 4 consecutive tokens
 };
 
-// Phase A: values and row decays into buffer nb, operands of the tile into registers.
+// Phase A: values, row data and q rows into buffer nb, the keys of the tile into registers.
 template <class C>
 __device__ __forceinline__ void sg_produce_a(ProdSg<C> &pv, const RawSg<C> &raw, const LdsPlanSg &lp,
                                              unsigned char *smem, int nb, int pw, int lane, bool row_valid) {
@@ -1971,16 +1986,17 @@ __device__ __forceinline__ void sg_produce_a(ProdSg<C> &pv, const RawSg<C> &raw,
     const float x = row_valid ? log2_decay(raw.las) : 0.f;
     const float y = raw.lis * kLog2e;
     const float bl = scan_incl(x, lane);
-    const float T = __shfl(bl, 63);
     if (pw == 0) {
-        float *sR = reinterpret_cast<float *>(smem + lp.rows) + nb * 128;
+        const float T = __shfl(bl, 63);
+        float *sR = reinterpret_cast<float *>(smem + lp.rows) + nb * 192;
         sR[lane] = bl;
         sR[64 + lane] = y;
+        sR[128 + lane] = fexp2(T - bl + y);  // weight of key row `lane` in the state update
     }
-    const float wk = fexp2(T - bl + y);  // weight of key row `lane` in the state update
+    f16 *sQ = reinterpret_cast<f16 *>(smem + lp.q) + nb * 64 * (C::DK + 8);
+    const int pc = chperm(4 * lane);
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) {
-        const float w = __shfl(wk, 16 * pw + rr);
         float qf[4], kf[4];
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
@@ -1989,35 +2005,25 @@ __device__ __forceinline__ void sg_produce_a(ProdSg<C> &pv, const RawSg<C> &raw,
             kf[2 * c] = in_lo<C, kOpK>(raw.k[rr][c]);
             kf[2 * c + 1] = in_hi<C, kOpK>(raw.k[rr][c]);
         }
-        pv.qh[rr] = u32x2{__builtin_bit_cast(uint32_t, f16x2{(f16)qf[0], (f16)qf[1]}),
-                          __builtin_bit_cast(uint32_t, f16x2{(f16)qf[2], (f16)qf[3]})};
-        pv.kh[rr] = u32x2{__builtin_bit_cast(uint32_t, f16x2{(f16)kf[0], (f16)kf[1]}),
-                          __builtin_bit_cast(uint32_t, f16x2{(f16)kf[2], (f16)kf[3]})};
+        *reinterpret_cast<u32x2 *>(sQ + (16 * pw + rr) * (C::DK + 8) + pc) =
+            u32x2{__builtin_bit_cast(uint32_t, f16x2{(f16)qf[0], (f16)qf[1]}),
+                  __builtin_bit_cast(uint32_t, f16x2{(f16)qf[2], (f16)qf[3]})};
 #pragma unroll
-        for (int c = 0; c < 4; ++c) pv.kt[c][rr >> 2][rr & 3] = (f16)(kf[c] * w);
+        for (int c = 0; c < 4; ++c) pv.kt[c][rr >> 2][rr & 3] = (f16)kf[c];
     }
 }
 
-// Phase B: q, k and the scaled keys^T of the prepared tile into the single buffers.
+// Phase B: the keys^T of the prepared tile into the single buffer.
 template <class C>
 __device__ __forceinline__ void sg_produce_b(const ProdSg<C> &pv, const LdsPlanSg &lp, unsigned char *smem, int pw,
                                              int lane) {
     const int ch0 = 4 * lane;
-    const int pc = chperm(ch0);
-    f16 *sQ = reinterpret_cast<f16 *>(smem + lp.q);
-    f16 *sK = reinterpret_cast<f16 *>(smem + lp.k);
     f16 *sKT = reinterpret_cast<f16 *>(smem + lp.kst);
-#pragma unroll
-    for (int rr = 0; rr < 16; ++rr) {
-        const int row = 16 * pw + rr;
-        *reinterpret_cast<u32x2 *>(sQ + row * (C::DK + 8) + pc) = pv.qh[rr];
-        *reinterpret_cast<u32x2 *>(sK + row * (C::DK + 8) + pc) = pv.kh[rr];
-    }
 #pragma unroll
     for (int c = 0; c < 4; ++c)
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4)
-            *reinterpret_cast<f16x4 *>(sKT + kt_off<C>(ch0 + c, kslot(16 * pw + 4 * g4))) = pv.kt[c][g4];
+            *reinterpret_cast<f16x4 *>(sKT + kt_off_sg(ch0 + c, kslot(16 * pw + 4 * g4))) = pv.kt[c][g4];
 }
 
 template <class C>
@@ -2083,8 +2089,6 @@ __global__ __launch_bounds__(512, 1) void chunk_output_sg_kernel(KArgs a) {
     // ================================ consumers
     const int cw = w;
     const int col = dv0 + 16 * cw + c16;
-    const f16 *sQ = reinterpret_cast<const f16 *>(smem + lp.q);
-    const f16 *sK = reinterpret_cast<const f16 *>(smem + lp.k);
     const f16 *sKT = reinterpret_cast<const f16 *>(smem + lp.kst);
     f16 *sP = reinterpret_cast<f16 *>(smem + lp.pbuf);
 
@@ -2118,9 +2122,11 @@ __global__ __launch_bounds__(512, 1) void chunk_output_sg_kernel(KArgs a) {
     for (int kc = 0; kc < nch; ++kc) {
         const int b = kc & 1;
         const int T0 = t_begin + kTile * kc;
+        const f16 *sQ = reinterpret_cast<const f16 *>(smem + lp.q) + b * 64 * RP;
         const f16 *sV = reinterpret_cast<const f16 *>(smem + lp.vb) + b * 4096;
-        const float *sB = reinterpret_cast<const float *>(smem + lp.rows) + b * 128;
+        const float *sB = reinterpret_cast<const float *>(smem + lp.rows) + b * 192;
         const float *sL = sB + 64;
+        const float *sW = sB + 128;
 
         // ---------------- phase A: score blocks P^T(j, i) and the inter-chunk term
         // O = diag(2^b) (q . S), sharing the q fragments: the permuted q row holds, at
@@ -2145,7 +2151,15 @@ __global__ __launch_bounds__(512, 1) void chunk_output_sg_kernel(KArgs a) {
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i) O[i] = mma(qf[i], sb, O[i]);
-            const auto kf = [&](int j) { return lds_ld<f16x8>(sK + (16 * j + c16) * RP + ch); };
+            // key rows 16j + c16 over the channels of this step, read transposed from k^T:
+            // source lane 4e + qq of a 16-lane group supplies tokens 16j + 4qq .. +3 of channel
+            // 32m + 4g + e (and 32m + 16 + 4g + e), the slot order of the permuted q rows
+            const int s_tr = kslot(4 * (c16 & 3)), r_tr = 32 * m + 4 * g + (c16 >> 2);
+            const auto kf = [&](int j) {
+                const f16x4 lo = lds_tr16(sKT + kt_off_sg(r_tr, s_tr + kslot(16 * j)));
+                const f16x4 hi = lds_tr16(sKT + kt_off_sg(r_tr + 16, s_tr + kslot(16 * j)));
+                return f16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            };
             switch (cw) {
                 case 0: {
                     const f16x8 k0 = kf(0), k2 = kf(2);
@@ -2201,7 +2215,8 @@ __global__ __launch_bounds__(512, 1) void chunk_output_sg_kernel(KArgs a) {
             const f16x4 z{(f16)0.f, (f16)0.f, (f16)0.f, (f16)0.f};
             *reinterpret_cast<f16x4 *>(sP + ((cw * 2 + (cw >> 1)) * 64 + lane) * 8 + 4) = z;
         }
-        // state update S <- 2^T S + K~^T V
+        // state update S <- 2^T S + K^T diag(w) V, the key weights on the value operand: slot
+        // 8g + e of step p is token 32p + 4g + e, slot 8g + 4 + e token 32p + 16 + 4g + e
         f16x8 vfr[2];
 #pragma unroll
         for (int p = 0; p < 2; ++p) vfr[p] = lds_ld<f16x8>(sV + ((p * 4 + g) * 64 + vsw(16 * cw + c16)) * 8);
@@ -2211,14 +2226,21 @@ __global__ __launch_bounds__(512, 1) void chunk_output_sg_kernel(KArgs a) {
             for (int n = 0; n < NBD; ++n) S[n] *= at;
 #pragma unroll
             for (int p = 0; p < 2; ++p) {
+                const f32x4 w0 = lds_ld<f32x4>(sW + 32 * p + 4 * g), w1 = lds_ld<f32x4>(sW + 32 * p + 16 + 4 * g);
+                f16x8 vw;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    vw[e] = (f16)((float)vfr[p][e] * w0[e]);
+                    vw[e + 4] = (f16)((float)vfr[p][e + 4] * w1[e]);
+                }
 #pragma unroll
                 for (int n = 0; n < NBD; ++n) {
                     const int r = 16 * n + c16;
-                    S[n] = mma(lds_ld<f16x8>(sKT + kt_off<C>(r, (p * 4 + g) * 8)), vfr[p], S[n]);
+                    S[n] = mma(lds_ld<f16x8>(sKT + kt_off_sg(r, (p * 4 + g) * 8)), vw, S[n]);
                 }
             }
         }
-        lds_barrier();  // B1: scores stored; q, k, k^T free for the next tile
+        lds_barrier();  // B1: scores stored; k^T free for the next tile
 
         // ---------------- phase B: scores x values, output
         {

@@ -202,11 +202,10 @@ GLA_HD inline bool use_ws_kernel(int opb, int dk, int nt) { return nt == 1 && dk
 // q, k and the scaled keys^T are single buffers (consumers read them before the mid-tile
 // barrier); values and row decays are double-buffered by tile parity.
 struct LdsPlanSg {
-    uint32_t q;     // [64][dk + 8] fp16 q, channels permuted inside 32-channel groups
-    uint32_t k;     // [64][dk + 8] fp16 k, same permutation
-    uint32_t kst;   // [dk][72] fp16 keys scaled to the tile end, transposed, k-slot order, swizzled
+    uint32_t q;     // [2][64][dk + 8] fp16 q, channels permuted inside 32-channel groups
+    uint32_t kst;   // [dk][96] fp16 keys, transposed, k-slot order, 16-byte units swizzled by row
     uint32_t vb;    // [2][4096] fp16 value tiles
-    uint32_t rows;  // [2][128] fp32: log2 running decay of each row, then log2 input gate
+    uint32_t rows;  // [2][192] fp32: log2 running decay of each row, log2 input gate, key weight
     uint32_t pbuf;  // [4096] fp16 masked scores
     uint32_t ostage;  // [64][68] fp32 output tile, staged for whole-row stores
     uint32_t total;
@@ -217,15 +216,13 @@ GLA_HD inline LdsPlanSg lds_plan_sg(int dk) {
     LdsPlanSg p{};
     uint32_t off = 0;
     p.q = off;
-    off += al(64u * (uint32_t)(dk + 8) * 2u);
-    p.k = off;
-    off += al(64u * (uint32_t)(dk + 8) * 2u);
+    off += al(2u * 64u * (uint32_t)(dk + 8) * 2u);
     p.kst = off;
-    off += al((uint32_t)dk * 72u * 2u);
+    off += al((uint32_t)dk * 96u * 2u);
     p.vb = off;
     off += al(2u * 4096u * 2u);
     p.rows = off;
-    off += al(2u * 128u * 4u);
+    off += al(2u * 192u * 4u);
     p.pbuf = off;
     off += al(4096u * 2u);
     p.ostage = off;
