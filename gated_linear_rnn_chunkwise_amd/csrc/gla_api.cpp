@@ -785,8 +785,9 @@ extern "C" int gla_mlstm_fwd(const gla_mlstm_desc *d, void *stream) {
     // one (batch, head) slice is addressed with 32-bit byte offsets, one chunk past the end
     // read by the prefetch
     if ((int64_t(d->L) + 128) * std::max(d->Dk, d->Dv) * 4 >= (int64_t(1) << 32)) return GLA_ERR_UNSUPPORTED;
-    if (gla_mlstm::lds_bytes(f32, d->Dk) > gla::kMaxLds) return GLA_ERR_UNSUPPORTED;
-    const int64_t nwg = bh * (d->Dv / 64);
+    const int cols = gla_mlstm::wg_cols(f32, d->Dk, d->Dv);
+    if (gla_mlstm::lds_bytes(f32, d->Dk, cols) > gla::kMaxLds) return GLA_ERR_UNSUPPORTED;
+    const int64_t nwg = bh * (d->Dv / cols);
     if (nwg > INT32_MAX) return GLA_ERR_UNSUPPORTED;
     gla_mlstm::MlstmArgs a{};
     a.q = d->q;
@@ -805,7 +806,7 @@ extern "C" int gla_mlstm_fwd(const gla_mlstm_desc *d, void *stream) {
     a.H = d->H;
     a.L = d->L;
     a.Dv = d->Dv;
-    a.ndv = d->Dv / 64;
+    a.ndv = d->Dv / cols;
     a.nwg = (int)nwg;
     return gla_mlstm::launch(a, f32, d->Dk, reinterpret_cast<hipStream_t>(stream)) == hipSuccess ? GLA_OK
                                                                                                : GLA_ERR_HIP;

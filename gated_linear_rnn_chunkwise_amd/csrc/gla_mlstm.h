@@ -14,12 +14,15 @@ struct MlstmArgs {
     float *out;                         // [B,H,L,Dv]
     float *fin_c, *fin_n, *fin_m;       // stabilised final state, each optional
     int B, H, L, Dv;
-    int ndv;                            // 64-column value slices
+    int ndv;                            // value slices of wg_cols columns
     int nwg;                            // workgroups = B * H * ndv
 };
 
-// LDS bytes of one workgroup (fp32 or fp16 operands, Dk).
-uint32_t lds_bytes(bool f32, int dk);
+// Value columns per workgroup: 128 (eight waves, two per SIMD) for fp16 operands with Dk = 256
+// when Dv is a multiple of 128, else 64 (four waves).
+int wg_cols(bool f32, int dk, int dv);
+// LDS bytes of one workgroup (fp32 or fp16 operands, Dk, value columns).
+uint32_t lds_bytes(bool f32, int dk, int cols);
 hipError_t launch(const MlstmArgs &a, bool f32, int dk, hipStream_t st);
 
 }  // namespace gla_mlstm

@@ -28,11 +28,14 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kRsrcFlags = 0x00020000;  // raw buffer, 32-bit data format
 constexpr int kC = 64;                   // tokens per chunk
 
-// Configuration of a kernel instance: operand type (fp32 or fp16 from bf16) and Dk.
-template <bool F32_, int DK_>
+// Configuration of a kernel instance: operand type (fp32 or fp16 from bf16), Dk and the
+// threads of a workgroup (which share the staging of a chunk; the value tile has NT / 4
+// columns).
+template <bool F32_, int DK_, int NT_ = 256>
 struct Cfg {
     static constexpr bool F32 = F32_;
     static constexpr int DK = DK_;
+    static constexpr int NT = NT_;
     using OpT = typename std::conditional<F32, float, f16>::type;
     using Frag = typename std::conditional<F32, f32x8, f16x8>::type;  // one 32-deep operand
     using Quad = typename std::conditional<F32, f32x4, f16x4>::type;  // 4 consecutive operands
@@ -43,9 +46,11 @@ struct Cfg {
     static constexpr int NB = DK / 16;       // 16-row blocks of the state
     static constexpr int NM = DK / 32;       // 32-deep steps over the channels
     static constexpr int NP = DK / 4;        // 4-element pieces of a channel row
-    static constexpr int QSTEP = 256 / NP;   // token quads apart of a thread's pieces
+    static constexpr int QSTEP = NT / NP;    // token quads apart of a thread's pieces
     static constexpr int QPT = 16 / QSTEP;   // token quads per thread (16 quads per chunk)
+    static constexpr int NVQ = NT / 16;      // 4-column quads of the value tile
     using Piece = typename std::conditional<F32, u32x4, u32x2>::type;  // 4 raw inputs
+    static_assert(QSTEP >= 1 && QPT >= 1 && QSTEP * QPT == 16, "threads must tile a chunk's rows");
 };
 
 // ------------------------------------------------------------------------------------
@@ -177,7 +182,7 @@ __device__ __forceinline__ typename C::Frag residual(const f32x4 &lo, const f32x
 
 // Raw 4-element pieces of the next chunk, held in registers while the current one runs:
 // thread tid holds piece tid % NP of the channel rows of token quads tid / NP + j QSTEP (q
-// and k) and columns 4 (tid & 15).. of token quad tid >> 4 (v).
+// and k) and columns 4 (tid % NVQ).. of token quad tid / NVQ (v).
 template <class C>
 struct Pieces {
     typename C::Piece q[C::QPT][4], k[C::QPT][4], v[4];
@@ -204,7 +209,7 @@ __device__ __forceinline__ void prefetch_rows(typename C::Piece (&dst)[C::QPT][4
 }
 template <class C>
 __device__ __forceinline__ void prefetch_v(typename C::Piece (&dst)[4], rsrc_t rv, int T0, int tid, int dv0, int Dv) {
-    const int a = tid >> 4, cv = tid & 15;
+    const int a = tid / C::NVQ, cv = tid % C::NVQ;
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt)
         dst[tt] = ld_piece<C>(rv, ((uint32_t)(T0 + 4 * a + tt) * Dv + dv0 + 4 * cv) * C::IB);
@@ -251,7 +256,7 @@ __device__ __forceinline__ void stage_rows(const Pieces<C> &pf, typename C::OpT 
                           el<C>(pf.k[j][2], e), el<C>(pf.k[j][3], e));
     }
     {
-        const int a = tid >> 4, cv = tid & 15;
+        const int a = tid / C::NVQ, cv = tid % C::NVQ;
         const int tp = perm(4 * a);
 #pragma unroll
         for (int e = 0; e < 4; ++e)

@@ -65,7 +65,7 @@ constexpr float kLn2 = 0.6931471805599453f;
 struct Plan {
     uint32_t q, k, kt, vt, p, pl, a, mx, mt, wp, den, n, total;
 };
-__host__ __device__ inline Plan make_plan(bool f32, int dk) {
+__host__ __device__ inline Plan make_plan(bool f32, int dk, int cols) {
     const uint32_t ob = f32 ? 4u : 2u;
     const uint32_t rq = (uint32_t)dk + 16u / ob, rt = (uint32_t)kC + 16u / ob;
     auto al = [](uint32_t x) { return (x + 255u) & ~255u; };
@@ -78,7 +78,7 @@ __host__ __device__ inline Plan make_plan(bool f32, int dk) {
     p.kt = off;
     off += al((uint32_t)dk * rt * ob);
     p.vt = off;
-    off += al(64u * rt * ob);
+    off += al((uint32_t)cols * rt * ob);
     p.p = off;  // scores (fp16 value)
     off += al(kC * rt * ob);
     p.pl = off;  // their fp16 rounding residual (fp16 operands only)
@@ -99,7 +99,8 @@ __host__ __device__ inline Plan make_plan(bool f32, int dk) {
     return p;
 }
 
-uint32_t lds_bytes(bool f32, int dk) { return make_plan(f32, dk).total; }
+int wg_cols(bool f32, int dk, int dv) { return !f32 && dk == 256 && dv % 128 == 0 ? 128 : 64; }
+uint32_t lds_bytes(bool f32, int dk, int cols) { return make_plan(f32, dk, cols).total; }
 
 __device__ __forceinline__ float scan_max(float x, int lane) {
 #pragma unroll
@@ -211,11 +212,12 @@ __device__ __forceinline__ void scores(const typename C::OpT *sQ, const typename
 }
 
 template <class C>
-__global__ __launch_bounds__(256, 1) void mlstm_chunk_kernel(MlstmArgs a) {
+__global__ __launch_bounds__(C::NT, 1) void mlstm_chunk_kernel(MlstmArgs a) {
     using OpT = typename C::OpT;
     using Frag = typename C::Frag;
     extern __shared__ __align__(256) unsigned char smem[];
-    const Plan lp = make_plan(C::F32, C::DK);
+    constexpr int NCOL = C::NT / 4;  // value columns of the workgroup, 16 per wave
+    const Plan lp = make_plan(C::F32, C::DK, NCOL);
     const OpT *sQ = reinterpret_cast<const OpT *>(smem + lp.q);
     const OpT *sK = reinterpret_cast<const OpT *>(smem + lp.k);
     const OpT *sKt = reinterpret_cast<const OpT *>(smem + lp.kt);
@@ -232,8 +234,11 @@ __global__ __launch_bounds__(256, 1) void mlstm_chunk_kernel(MlstmArgs a) {
     const int id = xcd_remap((int)blockIdx.x, (int)gridDim.x);
     const int dvt = id % a.ndv;
     const int bh = id / a.ndv;
-    const int dv0 = dvt * 64;
-    const int tid = (int)threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
+    const int dv0 = dvt * NCOL;
+    // the wave index in a scalar register: the score products below run on some waves only,
+    // and a matrix-core instruction does not look at the execution mask
+    const int tid = (int)threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, g = lane >> 4,
+              c16 = lane & 15;
     const int L = a.L, Dv = a.Dv;
     const size_t bhL = (size_t)bh * L;
 
@@ -271,7 +276,8 @@ __global__ __launch_bounds__(256, 1) void mlstm_chunk_kernel(MlstmArgs a) {
             case 0: scores<C, 0>(sQ, sK, sP, sPl, sA, sMx, sN, sDen, m_in, g, c16); break;
             case 1: scores<C, 1>(sQ, sK, sP, sPl, sA, sMx, sN, sDen, m_in, g, c16); break;
             case 2: scores<C, 2>(sQ, sK, sP, sPl, sA, sMx, sN, sDen, m_in, g, c16); break;
-            default: scores<C, 3>(sQ, sK, sP, sPl, sA, sMx, sN, sDen, m_in, g, c16); break;
+            case 3: scores<C, 3>(sQ, sK, sP, sPl, sA, sMx, sN, sDen, m_in, g, c16); break;
+            default: break;  // waves 4..7 of an eight-wave workgroup
         }
         prefetch_rows<C>(pf.k, rk, T0 + kC, tid);
 
@@ -353,15 +359,19 @@ __global__ __launch_bounds__(256, 1) void mlstm_chunk_kernel(MlstmArgs a) {
                     wr[e] = (OpT)(x0 - (float)wv[e]);
                     wr[e + 4] = (OpT)(x1 - (float)wv[e + 4]);
                 }
-                Frag ka[C::NB];
+                // k^T fragments four state blocks at a time (bounds the live registers)
 #pragma unroll
-                for (int r = 0; r < C::NB; ++r)
-                    ka[r] = ld_frag<C>(sKt + (16 * r + c16) * C::RT + kt_col(16 * r + c16, 32 * m + 8 * g));
+                for (int r0 = 0; r0 < C::NB; r0 += 4) {
+                    Frag ka[4];
 #pragma unroll
-                for (int r = 0; r < C::NB; ++r) S[r] = mma(ka[r], wv, S[r]);
-                if constexpr (!C::F32) {
+                    for (int r = 0; r < 4; ++r)
+                        ka[r] = ld_frag<C>(sKt + (16 * (r0 + r) + c16) * C::RT + kt_col(16 * (r0 + r) + c16, 32 * m + 8 * g));
 #pragma unroll
-                    for (int r = 0; r < C::NB; ++r) S[r] = mma(ka[r], wr, S[r]);
+                    for (int r = 0; r < 4; ++r) S[r0 + r] = mma(ka[r], wv, S[r0 + r]);
+                    if constexpr (!C::F32) {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) S[r0 + r] = mma(ka[r], wr, S[r0 + r]);
+                    }
                 }
             }
         }
@@ -397,7 +407,7 @@ __global__ __launch_bounds__(256, 1) void mlstm_chunk_kernel(MlstmArgs a) {
 template <class C>
 static hipError_t launch_cfg(const MlstmArgs &a, hipStream_t st) {
     static std::atomic<uint64_t> done{0};
-    const uint32_t lds = lds_bytes(C::F32, C::DK);
+    const uint32_t lds = lds_bytes(C::F32, C::DK, C::NT / 4);
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
@@ -408,7 +418,7 @@ static hipError_t launch_cfg(const MlstmArgs &a, hipStream_t st) {
         if (e != hipSuccess) return e;
         done.fetch_or(bit, std::memory_order_acq_rel);
     }
-    hipLaunchKernelGGL(mlstm_chunk_kernel<C>, dim3((unsigned)a.nwg), dim3(256), lds, st, a);
+    hipLaunchKernelGGL(mlstm_chunk_kernel<C>, dim3((unsigned)a.nwg), dim3(C::NT), lds, st, a);
     return hipGetLastError();
 }
 
@@ -419,7 +429,8 @@ hipError_t launch(const MlstmArgs &a, bool f32, int dk, hipStream_t st) {
     }
     if (dk == 64) return launch_cfg<Cfg<false, 64>>(a, st);
     if (dk == 128) return launch_cfg<Cfg<false, 128>>(a, st);
-    if (dk == 256) return launch_cfg<Cfg<false, 256>>(a, st);
+    if (dk == 256)
+        return a.Dv / a.ndv == 128 ? launch_cfg<Cfg<false, 256, 512>>(a, st) : launch_cfg<Cfg<false, 256>>(a, st);
     return hipErrorInvalidValue;
 }
 

@@ -69,7 +69,10 @@ def rand_state(B, H, Dk, Dv, seed):
             torch.randn(B, H, generator=g))
 
 
-SMALL = [("bf16", Dk, Dv) for Dk, Dv in ((64, 64), (128, 128), (64, 128), (256, 64), (128, 192), (256, 512))]
+# bf16 with Dk = 256 and Dv a multiple of 128 runs the eight-wave kernel (128 value columns
+# per workgroup), every other shape the four-wave one
+SMALL = [("bf16", Dk, Dv) for Dk, Dv in ((64, 64), (128, 128), (64, 128), (256, 64), (128, 192), (256, 512),
+                                          (256, 128), (256, 384))]
 SMALL += [("f32", 64, Dv) for Dv in (64, 128)]
 
 
@@ -95,12 +98,12 @@ def _nonnegative_qk(d):
     return d
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("dtype,Dk,Dv", [("bf16", 64, 64), ("f32", 64, 64), ("bf16", 256, 128)])
 @pytest.mark.parametrize("ig_std,offset", [(4.0, 0.0), (12.0, 0.0), (1.0, 100.0), (1.0, -60.0)])
-def test_mlstm_extreme_input_gates(gpu_lib, dtype, ig_std, offset):
+def test_mlstm_extreme_input_gates(gpu_lib, dtype, Dk, Dv, ig_std, offset):
     # input gates spread over e^(+-3 ig_std), or all near e^100 (whose products overflow fp32
     # without the running maximum) or e^-60: every factor the kernel applies stays <= 1
-    w = gin.custom(1, 2, 300, 64, 64, 64, dtype=dtype, gate="head", rule="mlstm", ig_std=ig_std)
+    w = gin.custom(1, 2, 300, Dk, Dv, 64, dtype=dtype, gate="head", rule="mlstm", ig_std=ig_std)
     d = _nonnegative_qk(gin.make_inputs(w, seed=7))
     d["log_i"] = d["log_i"] + offset
     out, fin = run_gpu(gpu_lib, d)
@@ -156,8 +159,9 @@ def _running_n(d):
     return res
 
 
-def test_mlstm_deterministic(gpu_lib):
-    w = gin.custom(2, 3, 500, 128, 128, 64, gate="head", rule="mlstm")
+@pytest.mark.parametrize("Dk,Dv", [(128, 128), (256, 256)])
+def test_mlstm_deterministic(gpu_lib, Dk, Dv):
+    w = gin.custom(2, 3, 500, Dk, Dv, 64, gate="head", rule="mlstm")
     d = gin.make_inputs(w, seed=1)
     a, fa = run_gpu(gpu_lib, d)
     b, fb = run_gpu(gpu_lib, d)
