@@ -301,8 +301,26 @@ __device__ __forceinline__ void store_staged(const float *sO, rsrc_t out, int T0
 
 // The same for the backward pass's instances: row t goes to row L-1-t when rev, times
 // oinv and (has_li) times exp of the destination row's log input gate, added to what the
-// output holds when acc; rows past the sequence end are not stored.
-__device__ __forceinline__ void store_staged_map(const float *sO, rsrc_t out, rsrc_t oli, int T0, int L, int Dv,
+// output holds when acc; rows past the sequence end are not stored.  The global loads this
+// needs (the log input gates, the output rows to add to) are issued a phase earlier by
+// load_map_pre, so that the stores do not wait a memory round trip.
+struct MapPre {
+    f32x4 x[4];   // output rows to add to (acc)
+    float li[4];  // log input gates of the destination rows (has_li)
+};
+__device__ __forceinline__ void load_map_pre(MapPre &p, rsrc_t out, rsrc_t oli, int T0, int L, int Dv, int dv0,
+                                             int cw, int lane, bool rev, bool has_li, bool acc) {
+    const int c4 = lane & 15;
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+        const int t = T0 + 16 * cw + 4 * rr + (lane >> 4);
+        // rows past the sequence end read row 0 (in range) and are not stored
+        const uint32_t dst = t < L ? (uint32_t)(rev ? L - 1 - t : t) : 0u;
+        p.li[rr] = has_li ? __uint_as_float(bld32(oli, dst * 4u)) : 0.f;
+        p.x[rr] = acc ? __builtin_bit_cast(f32x4, bld128(out, (dst * Dv + dv0 + 4 * c4) * 4u)) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+}
+__device__ __forceinline__ void store_staged_map(const float *sO, rsrc_t out, const MapPre &p, int T0, int L, int Dv,
                                                  int dv0, int cw, int lane, bool rev, bool has_li, float oinv,
                                                  bool acc) {
     const int c4 = lane & 15;
@@ -312,11 +330,11 @@ __device__ __forceinline__ void store_staged_map(const float *sO, rsrc_t out, rs
         const int t = T0 + row;
         const int dst = rev ? L - 1 - t : t;
         float f = oinv;
-        if (has_li) f *= fexp2(__uint_as_float(bld32(oli, (uint32_t)dst * 4u)) * kLog2e);
+        if (has_li) f *= fexp2(p.li[rr] * kLog2e);
         f32x4 x = lds_ld<f32x4>(sO + row * 68 + 4 * c4);
         x *= f;
+        if (acc) x += p.x[rr];
         const uint32_t off = ((uint32_t)dst * Dv + dv0 + 4 * c4) * 4u;
-        if (acc && t < L) x += __builtin_bit_cast(f32x4, bld128(out, off));
         if (t < L) __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), out, (int)off, 0, 0);
     }
 }
@@ -1828,6 +1846,8 @@ __global__ __launch_bounds__(512, 1) void chunk_output_ws_kernel(KArgs a) {
             }
         }
         lds_barrier();  // B1: scores stored; producers may rewrite q, k
+        [[maybe_unused]] MapPre mp;
+        if constexpr (C::H16 != 0) load_map_pre(mp, rs.out, om.li, T0, L, Dv, dv0, cw, lane, om.rev, om.has_li, om.acc);
 
         // ---------------- phase B: scores x values, state update, output
         Frag vfr[2];
@@ -1882,8 +1902,8 @@ __global__ __launch_bounds__(512, 1) void chunk_output_ws_kernel(KArgs a) {
         stage_out(reinterpret_cast<float *>(smem + lp.ostage), O, cw, g, c16);
         lds_barrier();  // B2
         if constexpr (C::H16 != 0)
-            store_staged_map(reinterpret_cast<const float *>(smem + lp.ostage), rs.out, om.li, T0, L, Dv, dv0, cw,
-                             lane, om.rev, om.has_li, om.inv, om.acc);
+            store_staged_map(reinterpret_cast<const float *>(smem + lp.ostage), rs.out, mp, T0, L, Dv, dv0, cw, lane,
+                             om.rev, om.has_li, om.inv, om.acc);
         else
             store_staged(reinterpret_cast<const float *>(smem + lp.ostage), rs.out, T0, Dv, dv0, cw, lane);
     }
@@ -2241,6 +2261,8 @@ __global__ __launch_bounds__(512, 1) void chunk_output_sg_kernel(KArgs a) {
             }
         }
         lds_barrier();  // B1: scores stored; k^T free for the next tile
+        [[maybe_unused]] MapPre mp;
+        if constexpr (C::H16 != 0) load_map_pre(mp, rs.out, om.li, T0, L, Dv, dv0, cw, lane, om.rev, om.has_li, om.acc);
 
         // ---------------- phase B: scores x values, output
         {
@@ -2259,8 +2281,8 @@ __global__ __launch_bounds__(512, 1) void chunk_output_sg_kernel(KArgs a) {
         stage_out(reinterpret_cast<float *>(smem + lp.ostage), O, cw, g, c16);
         lds_barrier();  // B2
         if constexpr (C::H16 != 0)
-            store_staged_map(reinterpret_cast<const float *>(smem + lp.ostage), rs.out, om.li, T0, L, Dv, dv0, cw,
-                             lane, om.rev, om.has_li, om.inv, om.acc);
+            store_staged_map(reinterpret_cast<const float *>(smem + lp.ostage), rs.out, mp, T0, L, Dv, dv0, cw, lane,
+                             om.rev, om.has_li, om.inv, om.acc);
         else
             store_staged(reinterpret_cast<const float *>(smem + lp.ostage), rs.out, T0, Dv, dv0, cw, lane);
     }
