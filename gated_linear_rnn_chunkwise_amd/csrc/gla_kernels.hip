@@ -287,6 +287,11 @@ __device__ __forceinline__ void stage_out(float *sO, const f32x4 (&O)[4], int cw
 #pragma unroll
         for (int e = 0; e < 4; ++e) sO[(16 * i + 4 * g + e) * 68 + 16 * cw + c16] = O[i][e];
 }
+// Whole-row stores of the output tile with the non-temporal cache policy (gfx950 `nt`): the
+// output is written once and not read back, and streaming it past the caches keeps the
+// inputs the column-slice workgroups of a head share (and the segment states) resident:
+// 1.5-4% on the scalar-gate and segmented workloads.
+constexpr int kStoreNT = 2;
 __device__ __forceinline__ void store_staged(const float *sO, rsrc_t out, int T0, int Dv, int dv0, int cw,
                                              int lane) {
     const int c4 = lane & 15;
@@ -295,15 +300,36 @@ __device__ __forceinline__ void store_staged(const float *sO, rsrc_t out, int T0
         const int row = 16 * cw + 4 * rr + (lane >> 4);
         const f32x4 x = lds_ld<f32x4>(sO + row * 68 + 4 * c4);
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), out,
-                                               (int)(((uint32_t)(T0 + row) * Dv + dv0 + 4 * c4) * 4u), 0, 0);
+                                               (int)(((uint32_t)(T0 + row) * Dv + dv0 + 4 * c4) * 4u), 0, kStoreNT);
     }
 }
 
 // The same for the backward pass's instances: row t goes to row L-1-t when rev, times
 // oinv and (has_li) times exp of the destination row's log input gate, added to what the
-// output holds when acc; rows past the sequence end are not stored.  The global loads this
-// needs (the log input gates, the output rows to add to) are issued a phase earlier by
-// load_map_pre, so that the stores do not wait a memory round trip.
+// output holds when acc; rows past the sequence end are not stored.
+__device__ __forceinline__ void store_staged_map(const float *sO, rsrc_t out, rsrc_t oli, int T0, int L, int Dv,
+                                                 int dv0, int cw, int lane, bool rev, bool has_li, float oinv,
+                                                 bool acc) {
+    const int c4 = lane & 15;
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+        const int row = 16 * cw + 4 * rr + (lane >> 4);
+        const int t = T0 + row;
+        const int dst = rev ? L - 1 - t : t;
+        float f = oinv;
+        if (has_li) f *= fexp2(__uint_as_float(bld32(oli, (uint32_t)dst * 4u)) * kLog2e);
+        f32x4 x = lds_ld<f32x4>(sO + row * 68 + 4 * c4);
+        x *= f;
+        const uint32_t off = ((uint32_t)dst * Dv + dv0 + 4 * c4) * 4u;
+        if (acc && t < L) x += __builtin_bit_cast(f32x4, bld128(out, off));
+        if (t < L) __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), out, (int)off, 0, 0);
+    }
+}
+// The same with the global loads (the log input gates, the output rows to add to) issued a
+// phase earlier by load_map_pre, so that the stores do not wait a memory round trip (used by
+// the scalar-gate kernel, whose consumers issue no other global loads; in the per-channel
+// kernel the consumers' value prefetch is in flight, and the wait for loads that a run-time
+// flag may have skipped then waits for the prefetch).
 struct MapPre {
     f32x4 x[4];   // output rows to add to (acc)
     float li[4];  // log input gates of the destination rows (has_li)
@@ -1846,8 +1872,6 @@ __global__ __launch_bounds__(512, 1) void chunk_output_ws_kernel(KArgs a) {
             }
         }
         lds_barrier();  // B1: scores stored; producers may rewrite q, k
-        [[maybe_unused]] MapPre mp;
-        if constexpr (C::H16 != 0) load_map_pre(mp, rs.out, om.li, T0, L, Dv, dv0, cw, lane, om.rev, om.has_li, om.acc);
 
         // ---------------- phase B: scores x values, state update, output
         Frag vfr[2];
@@ -1902,8 +1926,8 @@ __global__ __launch_bounds__(512, 1) void chunk_output_ws_kernel(KArgs a) {
         stage_out(reinterpret_cast<float *>(smem + lp.ostage), O, cw, g, c16);
         lds_barrier();  // B2
         if constexpr (C::H16 != 0)
-            store_staged_map(reinterpret_cast<const float *>(smem + lp.ostage), rs.out, mp, T0, L, Dv, dv0, cw, lane,
-                             om.rev, om.has_li, om.inv, om.acc);
+            store_staged_map(reinterpret_cast<const float *>(smem + lp.ostage), rs.out, om.li, T0, L, Dv, dv0, cw,
+                             lane, om.rev, om.has_li, om.inv, om.acc);
         else
             store_staged(reinterpret_cast<const float *>(smem + lp.ostage), rs.out, T0, Dv, dv0, cw, lane);
     }
@@ -2261,6 +2285,8 @@ __global__ __launch_bounds__(512, 1) void chunk_output_sg_kernel(KArgs a) {
             }
         }
         lds_barrier();  // B1: scores stored; k^T free for the next tile
+        // the mapped output stage's loads for this tile, a phase ahead of the stores (the
+        // consumers issue no other global loads, so waiting for them waits for nothing else)
         [[maybe_unused]] MapPre mp;
         if constexpr (C::H16 != 0) load_map_pre(mp, rs.out, om.li, T0, L, Dv, dv0, cw, lane, om.rev, om.has_li, om.acc);
 
