@@ -170,6 +170,55 @@ int checked_plan(const gla_desc *d, Plan *p) {
     return make_plan(d, p);
 }
 
+// The kernels take Dk in {64, 128, 256} and Dv a multiple of 64.  The forward entry points
+// also take any other Dk that is a multiple of 16 up to 256 and any other Dv that is a
+// multiple of 16 up to 4096, through zero-padded copies in the workspace: the padded key and
+// query channels are zero (their state rows stay zero and add nothing to the outputs, and a
+// per-channel gate is padded with log decay 0), and the padded value columns are dropped.
+bool native_shape(const gla_desc *d) {
+    return (d->Dk == 64 || d->Dk == 128 || d->Dk == 256) && d->Dv % gla::kDvTile == 0;
+}
+constexpr size_t kNotPadded = ~size_t(0);
+struct PadPlan {
+    gla_desc inner;  // the padded call (pointers are set when it runs)
+    Plan plan;       // its launch plan
+    size_t q, k, v, la, s0, out, fin, ws;  // workspace offsets, or kNotPadded
+    size_t total;    // workspace bytes: padded copies plus the padded call's own workspace
+};
+int pad_plan(const gla_desc *d, PadPlan *pp) {
+    if (d->Dk % 16 != 0 || d->Dk > 256 || d->Dv % 16 != 0 || d->Dv > 4096) return GLA_ERR_UNSUPPORTED;
+    const size_t eb = d->in_dtype == GLA_DTYPE_F32 ? 4 : 2;
+    const int dkp = d->Dk <= 64 ? 64 : (d->Dk <= 128 ? 128 : 256);
+    const int dvp = (d->Dv + gla::kDvTile - 1) / gla::kDvTile * gla::kDvTile;
+    gla_desc in = *d;
+    in.Dk = dkp;
+    in.Dv = dvp;
+    in.workspace = nullptr;
+    in.workspace_bytes = 0;
+    const int st = checked_plan(&in, &pp->plan);
+    if (st != GLA_OK) return st;
+    pp->inner = in;
+    const size_t bh = size_t(d->B) * d->H, bhl = bh * size_t(d->L);
+    const bool pk = dkp != d->Dk, pv = dvp != d->Dv;
+    size_t off = 0;
+    const auto take = [&](bool need, size_t bytes) {
+        if (!need) return kNotPadded;
+        const size_t o = off;
+        off += align256(bytes);
+        return o;
+    };
+    pp->q = take(pk, bhl * dkp * eb);
+    pp->k = take(pk, bhl * dkp * eb);
+    pp->v = take(pv, bhl * dvp * eb);
+    pp->la = take(pk && d->gate_kind == GLA_GATE_CHANNEL, bhl * dkp * 4);
+    pp->s0 = take(d->initial_state != nullptr, bh * dkp * dvp * 4);
+    pp->out = take(pv, bhl * dvp * 4);
+    pp->fin = take(d->final_state != nullptr, bh * dkp * dvp * 4);
+    pp->ws = take(pp->plan.ws_bytes > 0, pp->plan.ws_bytes);
+    pp->total = off;
+    return GLA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -189,18 +238,35 @@ const char *gla_status_string(int status) {
 
 int gla_workspace_size(const gla_desc *d, size_t *bytes) {
     if (!bytes) return GLA_ERR_INVALID_ARG;
-    Plan p;
-    const int st = checked_plan(d, &p);
+    int st = validate(d);
     if (st != GLA_OK) return st;
+    if (!native_shape(d)) {
+        PadPlan pp;
+        if ((st = pad_plan(d, &pp)) != GLA_OK) return st;
+        *bytes = pp.total;
+        return GLA_OK;
+    }
+    Plan p;
+    if ((st = make_plan(d, &p)) != GLA_OK) return st;
     *bytes = p.ws_bytes;
     return GLA_OK;
 }
 
 int gla_query_plan(const gla_desc *d, gla_plan *out) {
     if (!out) return GLA_ERR_INVALID_ARG;
-    Plan p;
-    const int st = checked_plan(d, &p);
+    int st = validate(d);
     if (st != GLA_OK) return st;
+    Plan p;
+    size_t ws_total = 0;
+    if (!native_shape(d)) {
+        PadPlan pp;
+        if ((st = pad_plan(d, &pp)) != GLA_OK) return st;
+        p = pp.plan;
+        ws_total = pp.total;
+    } else {
+        if ((st = make_plan(d, &p)) != GLA_OK) return st;
+        ws_total = p.ws_bytes;
+    }
     out->seg_chunks = p.seg_chunks;
     out->n_seg = p.nseg;
     out->dv_tiles = p.ndv;
@@ -210,7 +276,7 @@ int gla_query_plan(const gla_desc *d, gla_plan *out) {
     out->grid_out = p.grid_out;
     out->tile_pairs = p.knt > 1 ? 1 : 0;
     out->query_tiles = p.qsplit > 1 ? 1 : 0;
-    out->workspace_bytes = p.ws_bytes;
+    out->workspace_bytes = ws_total;
     return GLA_OK;
 }
 
@@ -286,6 +352,98 @@ int fwd_run(const gla_desc *d, int h16, void *stream, const OutMapArgs &om = Out
     return err == hipSuccess ? GLA_OK : GLA_ERR_HIP;
 }
 
+// Zero-filling copy in 16-byte units: dst[g][r][u] = src[g][r][u] for r < s_rows and
+// u < s_units, else 0, for groups g of d_rows rows of d_units units (the destination may be
+// wider or narrower than the source in either dimension).
+__global__ __launch_bounds__(256) void pad_copy_kernel(const uint4 *src, uint32_t s_units, uint32_t s_rows, uint4 *dst,
+                                                       uint32_t d_units, uint32_t d_rows, uint64_t n) {
+    for (uint64_t i = (uint64_t)blockIdx.x * 256u + threadIdx.x; i < n; i += (uint64_t)gridDim.x * 256u) {
+        const uint32_t u = (uint32_t)(i % d_units);
+        const uint64_t rg = i / d_units;
+        const uint32_t r = (uint32_t)(rg % d_rows);
+        const uint64_t g = rg / d_rows;
+        uint4 x = make_uint4(0u, 0u, 0u, 0u);
+        if (u < s_units && r < s_rows) x = src[(g * s_rows + r) * s_units + u];
+        dst[i] = x;
+    }
+}
+bool pad_copy(const void *src, size_t s_row_bytes, size_t s_rows, void *dst, size_t d_row_bytes, size_t d_rows,
+              size_t groups, hipStream_t st) {
+    const uint64_t n = (uint64_t)groups * d_rows * (d_row_bytes / 16);
+    if (n == 0) return true;
+    const uint64_t blocks = std::min<uint64_t>((n + 255) / 256, 1u << 16);
+    hipLaunchKernelGGL(pad_copy_kernel, dim3((unsigned)blocks), dim3(256), 0, st, static_cast<const uint4 *>(src),
+                       (uint32_t)(s_row_bytes / 16), (uint32_t)s_rows, static_cast<uint4 *>(dst),
+                       (uint32_t)(d_row_bytes / 16), (uint32_t)d_rows, n);
+    return hipGetLastError() == hipSuccess;
+}
+
+// The forward pass of a shape the kernels do not take directly, on zero-padded copies (see
+// pad_plan).  ws: workspace of at least pp.total bytes.
+int fwd_padded(const gla_desc *d, const PadPlan &pp, char *ws, void *stream) {
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    const size_t eb = d->in_dtype == GLA_DTYPE_F32 ? 4 : 2;
+    const size_t bh = size_t(d->B) * d->H, bhl = bh * size_t(d->L);
+    const int dkp = pp.inner.Dk, dvp = pp.inner.Dv;
+    gla_desc in = pp.inner;
+    const auto at = [&](size_t o) { return ws + o; };
+    bool ok = true;
+    if (pp.q != kNotPadded) {
+        ok = ok && pad_copy(d->q, d->Dk * eb, 1, at(pp.q), dkp * eb, 1, bhl, s);
+        ok = ok && pad_copy(d->k, d->Dk * eb, 1, at(pp.k), dkp * eb, 1, bhl, s);
+        in.q = at(pp.q);
+        in.k = at(pp.k);
+    }
+    if (pp.v != kNotPadded) {
+        ok = ok && pad_copy(d->v, d->Dv * eb, 1, at(pp.v), dvp * eb, 1, bhl, s);
+        in.v = at(pp.v);
+    }
+    if (pp.la != kNotPadded) {
+        ok = ok && pad_copy(d->log_alpha, d->Dk * 4, 1, at(pp.la), dkp * 4, 1, bhl, s);
+        in.log_alpha = reinterpret_cast<const float *>(at(pp.la));
+    }
+    if (pp.s0 != kNotPadded) {
+        ok = ok && pad_copy(d->initial_state, d->Dv * 4, d->Dk, at(pp.s0), dvp * 4, dkp, bh, s);
+        in.initial_state = reinterpret_cast<const float *>(at(pp.s0));
+    }
+    if (pp.out != kNotPadded) in.out = reinterpret_cast<float *>(at(pp.out));
+    if (pp.fin != kNotPadded) in.final_state = reinterpret_cast<float *>(at(pp.fin));
+    if (pp.ws != kNotPadded) {
+        in.workspace = at(pp.ws);
+        in.workspace_bytes = pp.plan.ws_bytes;
+    }
+    if (!ok) return GLA_ERR_HIP;
+    int st = fwd_run(&in, 0, stream);
+    if (st != GLA_OK) return st;
+    if (pp.out != kNotPadded) ok = ok && pad_copy(at(pp.out), dvp * 4, 1, d->out, d->Dv * 4, 1, bhl, s);
+    if (pp.fin != kNotPadded) ok = ok && pad_copy(at(pp.fin), dvp * 4, dkp, d->final_state, d->Dv * 4, d->Dk, bh, s);
+    return ok ? GLA_OK : GLA_ERR_HIP;
+}
+
+// gla_fwd_ex for every shape: native shapes run directly, others on padded copies in a
+// workspace that is the caller's or allocated stream-ordered here.
+int fwd_entry(const gla_desc *d, void *stream) {
+    int st = validate(d);
+    if (st != GLA_OK) return st;
+    if (native_shape(d)) return fwd_run(d, 0, stream);
+    PadPlan pp;
+    if ((st = pad_plan(d, &pp)) != GLA_OK) return st;
+    if (d->workspace && d->workspace_bytes < pp.total) return GLA_ERR_WORKSPACE;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    void *ws = d->workspace;
+    bool owned = false;
+    if (!ws && pp.total > 0) {
+        if (hipMallocAsync(&ws, pp.total, s) != hipSuccess || !ws) {
+            (void)hipGetLastError();
+            return GLA_ERR_WORKSPACE;
+        }
+        owned = true;
+    }
+    st = fwd_padded(d, pp, static_cast<char *>(ws), stream);
+    if (owned) (void)hipFreeAsync(ws, s);
+    return st;
+}
+
 }  // namespace
 
 // ------------------------------------------------------------------------------------
@@ -326,13 +484,22 @@ int scratch_address(void **out) {
 
 extern "C" {
 
-int gla_fwd_ex(const gla_desc *d, void *stream) { return fwd_run(d, 0, stream); }
+int gla_fwd_ex(const gla_desc *d, void *stream) { return fwd_entry(d, stream); }
 
 int gla_fwd_noalloc(const gla_desc *d, void *stream) {
-    Plan p;
-    int st = checked_plan(d, &p);
+    int st = validate(d);
     if (st != GLA_OK) return st;
     if (d->workspace != nullptr || d->workspace_bytes != 0) return GLA_ERR_INVALID_ARG;
+    if (!native_shape(d)) {
+        PadPlan pp;
+        if ((st = pad_plan(d, &pp)) != GLA_OK) return st;
+        if (pp.total > size_t(GLA_NOALLOC_SCRATCH_BYTES)) return GLA_ERR_WORKSPACE;
+        void *ptr = nullptr;
+        if ((st = scratch_address(&ptr)) != GLA_OK) return st;
+        return fwd_padded(d, pp, static_cast<char *>(ptr), stream);
+    }
+    Plan p;
+    if ((st = make_plan(d, &p)) != GLA_OK) return st;
     if (p.ws_bytes > size_t(GLA_NOALLOC_SCRATCH_BYTES)) return GLA_ERR_WORKSPACE;
     gla_desc f = *d;
     if (p.ws_bytes > 0) {

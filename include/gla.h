@@ -154,7 +154,11 @@ int gla_fwd(const void *q, const void *k, const void *v, const float *log_alpha,
  * least what gla_workspace_size reports, else GLA_ERR_WORKSPACE.
  * Support matrix (else GLA_ERR_UNSUPPORTED): chunk 16, 32, or a multiple of 64 in
  * [64, 512] (chunks of 16 and 32 tokens run as 64-token tiles, the same map, and seg_chunks
- * then counts 64-token tiles); Dk in {64, 128, 256}; Dv a multiple of 64 up to 4096; L >= 1 with
+ * then counts 64-token tiles); Dk a multiple of 16 up to 256 and Dv a multiple of 16 up to
+ * 4096.  Dk in {64, 128, 256} with Dv a multiple of 64 runs directly; other shapes run on
+ * zero-padded copies in the workspace (q, k and a per-channel gate padded to the next Dk of
+ * 64, 128, 256 with zero channels, v and the output to the next multiple of 64 columns, the
+ * states to both; the same result, plus the copies' bytes and workspace); L >= 1 with
  * (L + 1024) * max(Dk, Dv) * 4 < 2^32 (one (batch, head) slice is addressed with 32-bit
  * byte offsets, which allows L up to about 1M for Dv = 1024); and the operand tiles of
  * one workgroup must fit the 160 KB of LDS of a compute unit.  That last rule only bites
@@ -169,7 +173,8 @@ int gla_fwd_ex(const gla_desc *d, void *stream);
  * graph capture, tight serving loops, harnesses that forbid allocation.  Same operation,
  * arguments, support matrix and kernels as gla_fwd_ex, except the scratch: d->workspace must
  * be NULL and d->workspace_bytes 0 (else GLA_ERR_INVALID_ARG); the scratch the call needs
- * (gla_workspace_size; only sequence-segmented calls and the tile-pair form need any) comes
+ * (gla_workspace_size; only sequence-segmented calls, the tile-pair and query-tile forms and
+ * shapes run on padded copies need any) comes
  * from a device array of GLA_NOALLOC_SCRATCH_BYTES built into the library, one per GPU,
  * held from the first call on that GPU until the process ends.  A call that needs more
  * returns GLA_ERR_WORKSPACE and launches nothing.  The first call on a GPU resolves the

@@ -113,15 +113,47 @@ def test_headline_entry_point_validates(lib):
     assert lib.gla_fwd(None, A, A, A, A, None, 1, 1, 64, 128, 128, 64, None) == gla.GLA_ERR_INVALID_ARG
     assert lib.gla_fwd(A, A, A, A, A, None, 1, 1, 0, 128, 128, 64, None) == gla.GLA_ERR_INVALID_ARG
     assert lib.gla_fwd(A, A, A, A, A + 4, None, 1, 1, 64, 128, 128, 64, None) == gla.GLA_ERR_INVALID_ARG
-    assert lib.gla_fwd(A, A, A, A, A, None, 1, 1, 64, 96, 128, 64, None) == gla.GLA_ERR_UNSUPPORTED
+    assert lib.gla_fwd(A, A, A, A, A, None, 1, 1, 64, 24, 128, 64, None) == gla.GLA_ERR_UNSUPPORTED
+    assert lib.gla_fwd(A, A, A, A, A, None, 1, 1, 64, 272, 128, 64, None) == gla.GLA_ERR_UNSUPPORTED
 
 
-@pytest.mark.parametrize("kw", [dict(Dk=96), dict(Dk=32), dict(Dv=96), dict(Dv=32), dict(chunk=48), dict(chunk=96),
-                                dict(chunk=1024), dict(Dv=4160), dict(B=1, H=1, L=(1 << 23) - 1024)])
+@pytest.mark.parametrize("kw", [dict(Dk=24), dict(Dk=272), dict(Dk=8), dict(Dv=40), dict(Dv=8), dict(chunk=48),
+                                dict(chunk=96), dict(chunk=1024), dict(Dv=4160), dict(Dv=4112),
+                                dict(B=1, H=1, L=(1 << 23) - 1024)])
 def test_unsupported_shapes(lib, kw):
     d = desc(**kw)
     assert status(lib, d)[0] == gla.GLA_ERR_UNSUPPORTED
     assert fwd_status(lib, d) == gla.GLA_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("Dk,Dv,gate,s0,fin", [(96, 128, gla.GATE_CHANNEL, False, False), (128, 96, gla.GATE_CHANNEL, True, True),
+                                             (16, 48, gla.GATE_HEAD, True, False), (240, 272, gla.GATE_NONE, False, True),
+                                             (160, 64, gla.GATE_HEAD_CONST, False, False)])
+def test_padded_shapes_plan(lib, Dk, Dv, gate, s0, fin):
+    # Dk a multiple of 16 up to 256 and Dv a multiple of 16 run on zero-padded copies: q and
+    # k (and a per-channel gate) to the next Dk in {64, 128, 256}, v and the output to the
+    # next multiple of 64, the states to both; the workspace holds the copies (256-byte
+    # aligned) followed by the padded call's own workspace
+    B, H, L = 2, 3, 100
+    kw = dict(B=B, H=H, L=L, Dk=Dk, Dv=Dv, gate_kind=gate, log_alpha=None if gate == gla.GATE_NONE else A,
+              initial_state=A if s0 else None, final_state=A if fin else None)
+    st, n = status(lib, desc(**kw))
+    assert st == gla.GLA_OK
+    dkp = 64 if Dk <= 64 else (128 if Dk <= 128 else 256)
+    dvp = -(-Dv // 64) * 64
+    al = lambda x: (x + 255) // 256 * 256
+    bhl, bh = B * H * L, B * H
+    inner = gla.workspace_size(desc(**dict(kw, Dk=dkp, Dv=dvp)))
+    want = 0
+    if dkp != Dk:
+        want += 2 * al(bhl * dkp * 2) + (al(bhl * dkp * 4) if gate == gla.GATE_CHANNEL else 0)
+    if dvp != Dv:
+        want += al(bhl * dvp * 2)
+    want += (al(bh * dkp * dvp * 4) if s0 else 0) + (al(bhl * dvp * 4) if dvp != Dv else 0)
+    want += (al(bh * dkp * dvp * 4) if fin else 0) + al(inner)
+    assert n == want
+    p = gla.plan(desc(**kw))
+    assert p.dv_tiles == dvp // 64 and p.workspace_bytes == n
 
 
 def test_longest_sequence_of_a_slice(lib):
@@ -386,7 +418,9 @@ def test_noalloc_rejects_caller_workspace_and_oversized_scratch(lib):
     assert lib.gla_fwd_noalloc(ctypes.byref(big), None) == gla.GLA_ERR_WORKSPACE
     # validation errors come first, as for gla_fwd_ex
     assert lib.gla_fwd_noalloc(ctypes.byref(desc(q=None)), None) == gla.GLA_ERR_INVALID_ARG
-    assert lib.gla_fwd_noalloc(ctypes.byref(desc(Dk=96)), None) == gla.GLA_ERR_UNSUPPORTED
+    assert lib.gla_fwd_noalloc(ctypes.byref(desc(Dk=24)), None) == gla.GLA_ERR_UNSUPPORTED
+    # a shape run on padded copies whose copies exceed the scratch
+    assert lib.gla_fwd_noalloc(ctypes.byref(desc(B=8, H=16, L=2048, Dk=96)), None) == gla.GLA_ERR_WORKSPACE
     assert lib.gla_fwd_noalloc(None, None) == gla.GLA_ERR_INVALID_ARG
 
 

@@ -277,6 +277,44 @@ def test_caller_workspace(gpu_lib):
     assert ei.value.status == gpu_lib.GLA_ERR_WORKSPACE
 
 
+# ------------------------------------------------------------------------------ padded shapes
+# Dk and Dv multiples of 16 that the kernels do not take directly run on zero-padded copies
+# (Dk to 64, 128 or 256; Dv to the next multiple of 64)
+PADDED = [("bf16", "channel", False, 96, 128), ("bf16", "channel", True, 32, 48), ("bf16", "head", True, 160, 80),
+          ("bf16", "head_const", False, 208, 144), ("bf16", "none", False, 16, 16), ("f32", "channel", True, 48, 112),
+          ("f32", "head", False, 96, 64), ("bf16", "channel", False, 240, 272)]
+
+
+@pytest.mark.parametrize("dtype,gate,ig,Dk,Dv", PADDED)
+@pytest.mark.parametrize("chunk", [64, 128])
+def test_padded_shapes(gpu_lib, dtype, gate, ig, Dk, Dv, chunk):
+    w = gin.custom(2, 2, 333, Dk, Dv, chunk, dtype=dtype, gate=gate, input_gate=ig)
+    d = gin.make_inputs(w, seed=Dk + Dv)
+    s0 = torch.randn(2, 2, Dk, Dv, generator=torch.Generator().manual_seed(Dk)) * 0.1
+    out, fin = run_gpu(gpu_lib, d, w, initial_state=s0)
+    ref, rfin = run_oracle(d, w, initial_state=s0)
+    check(w, out, ref)
+    check(w, fin, rfin, "final_state")
+
+
+def test_padded_shape_entry_points(gpu_lib):
+    # the 13-argument entry point and the allocation-free one take the padded shapes too
+    w = gin.custom(1, 2, 200, 96, 80, 64, gate="channel")
+    d = gin.make_inputs(w, seed=5)
+    ref, rfin = run_oracle(d, w)
+    dev = "cuda"
+    q, k, v, la = (d[x].to(dev) for x in ("q", "k", "v", "log_alpha"))
+    out = torch.empty(1, 2, 200, 80, device=dev)
+    fin = torch.empty(1, 2, 96, 80, device=dev)
+    assert gpu_lib.fwd_headline(q, k, v, la, out, fin, chunk=64) == gpu_lib.GLA_OK
+    torch.cuda.synchronize()
+    check(w, out.cpu().double().numpy(), ref)
+    check(w, fin.cpu().double().numpy(), rfin, "final_state")
+    out2, fin2 = gpu_lib.fwd_noalloc(q, k, v, la, chunk=64, final_state=torch.empty_like(fin))
+    torch.cuda.synchronize()
+    assert torch.equal(out2, out) and torch.equal(fin2, fin)
+
+
 # ------------------------------------------------------------------------------ full-size workloads
 # Every full-size workload in the launch configuration bench.py times, compared whole: every
 # (batch, head) slice of the output and of the final state, with RMS over the whole tensor.
