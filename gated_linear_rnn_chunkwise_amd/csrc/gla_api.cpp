@@ -523,8 +523,8 @@ int gla_step(const gla_step_desc *d, void *stream) {
         if (p && !aligned16(p)) return GLA_ERR_INVALID_ARG;
     const int64_t bh = int64_t(d->B) * d->H;
     if (bh > (int64_t(1) << 24) || bh * int64_t(d->Dk) * d->Dv > (int64_t(1) << 40)) return GLA_ERR_INVALID_ARG;
-    if (d->Dk > 4096 || d->Dv % 64 != 0 || d->Dv > 4096) return GLA_ERR_UNSUPPORTED;
-    if (bh * (d->Dv / 64) > INT32_MAX) return GLA_ERR_UNSUPPORTED;
+    if (d->Dk > 4096 || d->Dv % 16 != 0 || d->Dv > 4096) return GLA_ERR_UNSUPPORTED;
+    if (bh * ((d->Dv + 63) / 64) > INT32_MAX) return GLA_ERR_UNSUPPORTED;
     return gla::launch_step(*d, reinterpret_cast<hipStream_t>(stream)) == hipSuccess ? GLA_OK : GLA_ERR_HIP;
 }
 

@@ -2605,7 +2605,7 @@ template <bool F32>
 __global__ __launch_bounds__(256) void step_kernel(gla_step_desc d) {
     __shared__ float sq[4096], sk[4096], sa[4096];
     __shared__ float4 part[16][16];
-    const int ndv = d.Dv / 64;
+    const int ndv = (d.Dv + 63) / 64;  // the last tile of a Dv that is not a multiple of 64 is partial
     const int bh = (int)blockIdx.x / ndv, dvt = (int)blockIdx.x % ndv;
     const int h = bh % d.H;
     const int tid = (int)threadIdx.x;
@@ -2627,12 +2627,15 @@ __global__ __launch_bounds__(256) void step_kernel(gla_step_desc d) {
     __syncthreads();
     const int cq = tid & 15, rg = tid >> 4;
     const int c0 = dvt * 64 + 4 * cq;
-    float vv[4];
+    const bool cval = c0 < Dv;  // Dv is a multiple of 4: a column quad is in range or past it
+    float vv[4] = {0.f, 0.f, 0.f, 0.f};
+    if (cval) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) vv[j] = in(d.v, (size_t)bh * Dv + c0 + j);
+        for (int j = 0; j < 4; ++j) vv[j] = in(d.v, (size_t)bh * Dv + c0 + j);
+    }
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     float *S = d.state + (size_t)bh * Dk * Dv + c0;
-    for (int r = rg; r < Dk; r += 16) {
+    for (int r = rg; cval && r < Dk; r += 16) {
         float4 *p = reinterpret_cast<float4 *>(S + (size_t)r * Dv);
         float4 x = *p;
         const float a = sa[r], kr = sk[r], qr = sq[r];
@@ -2648,7 +2651,7 @@ __global__ __launch_bounds__(256) void step_kernel(gla_step_desc d) {
     }
     part[rg][cq] = acc;
     __syncthreads();
-    if (tid < 16) {
+    if (tid < 16 && dvt * 64 + 4 * tid < Dv) {
         float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
         for (int g = 0; g < 16; ++g) {
             const float4 y = part[g][tid];
@@ -2662,7 +2665,7 @@ __global__ __launch_bounds__(256) void step_kernel(gla_step_desc d) {
 }
 
 hipError_t launch_step(const gla_step_desc &d, hipStream_t st) {
-    const int grid = d.B * d.H * (d.Dv / 64);
+    const int grid = d.B * d.H * ((d.Dv + 63) / 64);
     if (d.in_dtype == GLA_DTYPE_F32)
         hipLaunchKernelGGL(step_kernel<true>, dim3(grid), dim3(256), 0, st, d);
     else

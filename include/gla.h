@@ -214,7 +214,7 @@ typedef struct gla_step_desc {
 } gla_step_desc;
 
 /* Recurrent step.  Support matrix (else GLA_ERR_UNSUPPORTED): Dk in [1, 4096], Dv a
- * multiple of 64 up to 4096.  Validation as for gla_fwd_ex (GLA_ERR_INVALID_ARG for NULL
+ * multiple of 16 up to 4096.  Validation as for gla_fwd_ex (GLA_ERR_INVALID_ARG for NULL
  * required pointers, sizes <= 0, misalignment, a gate pointer inconsistent with its kind).
  * The state must not alias q, k, v, the gates or the output.  Asynchronous on `stream`;
  * allocates nothing.  Returns a gla_status. */

@@ -285,7 +285,7 @@ def test_step_gate_pointer_must_match_kind(lib):
     assert lib.gla_step(ctypes.byref(step_desc(log_alpha=None)), None) == gla.GLA_ERR_INVALID_ARG
 
 
-@pytest.mark.parametrize("kw", [dict(Dv=96), dict(Dv=4160), dict(Dk=4097)])
+@pytest.mark.parametrize("kw", [dict(Dv=40), dict(Dv=4160), dict(Dk=4097)])
 def test_step_unsupported(lib, kw):
     assert lib.gla_step(ctypes.byref(step_desc(**kw)), None) == gla.GLA_ERR_UNSUPPORTED
 

@@ -370,7 +370,7 @@ def _token(d, w, t):
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("gate,ig", [("channel", False), ("head", True), ("head_const", False), ("none", False),
                                      ("channel", True)])
-@pytest.mark.parametrize("Dk,Dv", [(128, 128), (64, 192), (256, 64), (100, 64)])
+@pytest.mark.parametrize("Dk,Dv", [(128, 128), (64, 192), (256, 64), (100, 64), (96, 80), (48, 16)])
 def test_step_sequence_matches_recurrence(gpu_lib, dtype, gate, ig, Dk, Dv):
     # 9 steps from a random initial state against the fp64 recurrence over the same tokens
     w = gin.custom(2, 3, 9, Dk, Dv, 64, dtype=dtype, gate=gate, input_gate=ig)
