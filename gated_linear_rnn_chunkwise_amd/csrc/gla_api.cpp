@@ -33,7 +33,8 @@ hipError_t bwd_scale(const float *src, const uint32_t *mx, float *dst, int BH, s
 hipError_t bwd_copy2d(const void *src, size_t src_stride, void *dst, size_t dst_stride, size_t rows, size_t row_bytes,
                       hipStream_t st);
 hipError_t bwd_finish(const gla_bwd_desc &d, const float *oA, const float *oB, float *g, const float *finA,
-                      const float *finC, const float *dfT, float *part, const uint32_t *mx, hipStream_t st);
+                      const float *finC, const float *dfT, float *part, const uint32_t *mx, const float *dqp,
+                      const float *dkp, hipStream_t st);
 constexpr int kH16Q = 1, kH16K = 2, kH16V = 4;  // fp16 operand bits of launch_forward
 size_t chan_scratch_floats(int BH, int L, int Dk, int Dv, bool g_rows);
 hipError_t chan_backward(const gla_bwd_desc &d, const float *s0T, const float *dfT, float *finA, float *finC,
@@ -291,6 +292,8 @@ struct OutMapArgs {
     const uint32_t *mx = nullptr;
     int in_rev = 0;  // the pass reads q, k, v in reversed token order
     int acc = 0;     // add to the output instead of storing
+    const void *dot_src = nullptr;  // dq and dk passes: rows to dot with the stored rows
+    float *dot_out = nullptr;       // [Dv/64][BH][L] dot products per 64-column tile
 };
 
 // The forward pass; h16 marks operands given as fp16 instead of bf16 and om maps the output
@@ -346,6 +349,8 @@ int fwd_run(const gla_desc *d, int h16, void *stream, const OutMapArgs &om = Out
     a.out_mx = om.mx;
     a.in_rev = om.in_rev;
     a.out_acc = om.acc;
+    a.dot_src = om.dot_src;
+    a.dot_out = om.dot_out;
 
     const hipError_t err = gla::launch_forward(a, d->in_dtype == GLA_DTYPE_F32, h16, d->Dk, s);
     if (owned) (void)hipFreeAsync(ws, s);
@@ -621,6 +626,7 @@ bool chan_dv_fast(const gla_bwd_desc *d) { return d->in_dtype == GLA_DTYPE_BF16 
 
 struct BwdPlan {
     size_t chs, rq, rk, rv, rdo, fdo, mx, mxp, s0A, lar, oA, oB, finA, finC, s0T, dfT, g, part, fws, total;
+    size_t dqp, dkp;  // bf16: the dq and dk passes' dot products q . dq, k . dk per 64-column tile
     size_t vsl, dsl, s0h, finH;  // Dv split: value and output-gradient halves, a state half, a final-state half
     size_t fws_bytes;
 };
@@ -688,6 +694,12 @@ int bwd_plan(const gla_bwd_desc *d, BwdPlan *p) {
     p->g = gate ? take(bh * L * 4) : 0;
     p->part = take(bh * 4);
     const bool split = bwd_split_dv(d);
+    // bf16 without the value split: the dq and dk passes form q . dq and k . dk as they store
+    // (offset 0 means none: fdo is taken first for bf16)
+    const bool need_g = gate && d->dlog_alpha;
+    const bool dots = bf && !split && (need_g || d->dlog_ig);
+    p->dqp = (dots && need_g) ? take((Dk / 64) * bh * L * 4) : 0;
+    p->dkp = dots ? take((Dk / 64) * bh * L * 4) : 0;
     const int kd = split ? kDvHalf : d->Dv;  // key dimension of the dk and dq passes
     p->vsl = split ? take(bh * L * kDvHalf * 2) : 0;
     p->dsl = split ? take(bh * L * kDvHalf * 2) : 0;
@@ -793,7 +805,7 @@ int gla_bwd(const gla_bwd_desc *d, void *stream) {
         // the dv pass's final state is scaled by s only on the forward kernel's path
         if (rc == GLA_OK)
             ok(gla::bwd_finish(*d, nullptr, nullptr, nullptr, F(p.finA), F(p.finC), dfT, nullptr, fast ? cmx : nullptr,
-                               s));
+                               nullptr, nullptr, s));
         if (owned) (void)hipFreeAsync(ws, s);
         return rc;
     }
@@ -834,14 +846,24 @@ int gla_bwd(const gla_bwd_desc *d, void *stream) {
     fwd(bwd_pass_desc(d, Dk, Dv, rk, rq, rdo, rgate, rla, nullptr, s0A, bf ? d->dv : F(p.oA), F(p.finA)), gla::kH16V,
         om_rev);
     if (!bwd_split_dv(d)) {
-        // dk (reversed, keys and values exchanged)
+        // dk (reversed, keys and values exchanged), with k . dk per stored row (bf16)
+        OutMapArgs om_k = om_rev, om_dq = om_q;
+        if (p.dkp) {
+            om_k.dot_src = d->k;
+            om_k.dot_out = F(p.dkp);
+        }
         fwd(bwd_pass_desc(d, Dv, Dk, rv, rdo, rq, rgate, rla, nullptr, d->dfinal_state ? F(p.dfT) : nullptr,
                           bf ? d->dk : F(p.oB), nullptr),
-            gla::kH16K, om_rev);
-        // dq (keys and values exchanged; its final state is the forward final state, transposed)
+            gla::kH16K, om_k);
+        // dq (keys and values exchanged; its final state is the forward final state, transposed),
+        // with q . dq per stored row (bf16, when the log-gate gradient is wanted)
+        if (p.dqp) {
+            om_dq.dot_src = d->q;
+            om_dq.dot_out = F(p.dqp);
+        }
         fwd(bwd_pass_desc(d, Dv, Dk, fdo, d->v, d->k, d->gate_kind, d->log_alpha, d->log_ig,
                           d->initial_state ? F(p.s0T) : nullptr, d->dq, F(p.finC)),
-            gla::kH16Q, om_q);
+            gla::kH16Q, om_dq);
     } else {
         // the same two passes over each 256-column half of the values (and of the output
         // gradient): G splits by value columns, so dk and dq are the sums of the halves'
@@ -873,7 +895,8 @@ int gla_bwd(const gla_bwd_desc *d, void *stream) {
     if (rc == GLA_OK)
         ok(gla::bwd_finish(*d, bf ? nullptr : F(p.oA), bf ? nullptr : F(p.oB),
                            (gate && d->dlog_alpha) ? F(p.g) : nullptr, F(p.finA), F(p.finC),
-                           d->dfinal_state ? F(p.dfT) : nullptr, F(p.part), mx, s));
+                           d->dfinal_state ? F(p.dfT) : nullptr, F(p.part), mx, p.dqp ? F(p.dqp) : nullptr,
+                           p.dkp ? F(p.dkp) : nullptr, s));
     if (owned) (void)hipFreeAsync(ws, s);
     return rc;
 }

@@ -251,6 +251,22 @@ __global__ __launch_bounds__(256) void bwd_dot_kernel(gla_bwd_desc d, float *g, 
     }
 }
 
+// The same from the dot products the bf16 dq and dk passes formed as they stored their rows:
+// qp and kp hold, per 64-column tile j < nj, q_t . dq_t and k_t . dk_t over the tile's
+// channels ([nj][ntok]; qp null when g is not wanted), summed here in tile order.
+__global__ __launch_bounds__(256) void bwd_dot_sum_kernel(const float *qp, const float *kp, int nj, size_t ntok,
+                                                          float *g, float *dli) {
+    const size_t tok = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (tok >= ntok) return;
+    float qdq = 0.f, kdk = 0.f;
+    for (int j = 0; j < nj; ++j) {
+        if (qp) qdq += qp[(size_t)j * ntok + tok];
+        kdk += kp[(size_t)j * ntok + tok];
+    }
+    if (g) g[tok] = qdq - kdk;
+    if (dli) dli[tok] = kdk;
+}
+
 // The final-state term of the last token's g: the sum over (j, d) of dfinal^T[j][d] S_fin^T[j][d]
 // (dfT and finC both transposed; times 1/s when dfT carries the scale).  One workgroup per
 // (b, h) in a fixed order, so the result does not depend on scheduling.
@@ -421,12 +437,17 @@ hipError_t bwd_scale(const float *src, const uint32_t *mx, float *dst, int BH, s
 }
 
 hipError_t bwd_finish(const gla_bwd_desc &d, const float *oA, const float *oB, float *g, const float *finA,
-                      const float *finC, const float *dfT, float *part, const uint32_t *mx, hipStream_t st) {
+                      const float *finC, const float *dfT, float *part, const uint32_t *mx, const float *dqp,
+                      const float *dkp, hipStream_t st) {
     const int BH = d.B * d.H;
     const size_t ntok = (size_t)BH * d.L;
     hipError_t e = hipSuccess;
     if (oB) {
         hipLaunchKernelGGL(bwd_post_kernel, dim3(nblk(ntok, 4)), dim3(256), 0, st, d, oA, oB, g, ntok);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    } else if (dkp && (g || d.dlog_ig)) {
+        hipLaunchKernelGGL(bwd_dot_sum_kernel, dim3(nblk(ntok, 256)), dim3(256), 0, st, dqp, dkp, d.Dk / 64, ntok, g,
+                           d.dlog_ig);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     } else if (g || d.dlog_ig) {
         const int lg = d.Dk == 64 ? 4 : (d.Dk == 128 ? 5 : 6);  // Dk / 4 lanes per token

@@ -304,12 +304,46 @@ __device__ __forceinline__ void store_staged(const float *sO, rsrc_t out, int T0
     }
 }
 
+// Rows of a backward pass's dot-product source (KArgs::dot_src) for the lane's four output
+// rows, at the destination rows the stores use (four bf16 each), loaded ahead of the stores.
+struct DotPre {
+    u32x2 s[4];
+};
+__device__ __forceinline__ void load_dot_pre(DotPre &p, rsrc_t src, int T0, int L, int Dv, int dv0, int cw, int lane,
+                                             bool rev) {
+    const int c4 = lane & 15;
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+        const int t = T0 + 16 * cw + 4 * rr + (lane >> 4);
+        // rows past the sequence end read row 0 (in range) and store nothing
+        const uint32_t dst = t < L ? (uint32_t)(rev ? L - 1 - t : t) : 0u;
+        p.s[rr] = bld64(src, (dst * (uint32_t)Dv + (uint32_t)(dv0 + 4 * c4)) * 2u);
+    }
+}
+// Sum over the calling lane's 16-lane row, in every lane of it: DPP row rotations by 8, 4, 2
+// and 1 (vector ALU only, no LDS crossbar).
+__device__ __forceinline__ float row_sum16(float x) {
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xf, 0xf, false));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x124, 0xf, 0xf, false));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x122, 0xf, 0xf, false));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x121, 0xf, 0xf, false));
+    return x;
+}
+// The dot product of a stored row segment x with its source row segment, summed over the 16
+// lanes that hold the row's 64 columns; the first of them writes it to drow[dst].
+__device__ __forceinline__ void store_dot(const u32x2 &s, const f32x4 &x, float *drow, int dst, bool valid, int c4) {
+    const float part = row_sum16(bf_lo(s[0]) * x[0] + bf_hi(s[0]) * x[1] + bf_lo(s[1]) * x[2] + bf_hi(s[1]) * x[3]);
+    if (c4 == 0 && valid) drow[dst] = part;
+}
+
 // The same for the backward pass's instances: row t goes to row L-1-t when rev, times
 // oinv and (has_li) times exp of the destination row's log input gate, added to what the
-// output holds when acc; rows past the sequence end are not stored.
+// output holds when acc; rows past the sequence end are not stored.  With DOT, each stored
+// row's dot product with its preloaded source row goes to drow (when non-null).
+template <bool DOT>
 __device__ __forceinline__ void store_staged_map(const float *sO, rsrc_t out, rsrc_t oli, int T0, int L, int Dv,
                                                  int dv0, int cw, int lane, bool rev, bool has_li, float oinv,
-                                                 bool acc) {
+                                                 bool acc, const DotPre &dp, float *drow) {
     const int c4 = lane & 15;
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
@@ -323,6 +357,7 @@ __device__ __forceinline__ void store_staged_map(const float *sO, rsrc_t out, rs
         const uint32_t off = ((uint32_t)dst * Dv + dv0 + 4 * c4) * 4u;
         if (acc && t < L) x += __builtin_bit_cast(f32x4, bld128(out, off));
         if (t < L) __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), out, (int)off, 0, 0);
+        if constexpr (DOT) store_dot(dp.s[rr], x, drow, dst, t < L && drow != nullptr, c4);
     }
 }
 // The same with the global loads (the log input gates, the output rows to add to) issued a
@@ -346,9 +381,10 @@ __device__ __forceinline__ void load_map_pre(MapPre &p, rsrc_t out, rsrc_t oli, 
         p.x[rr] = acc ? __builtin_bit_cast(f32x4, bld128(out, (dst * Dv + dv0 + 4 * c4) * 4u)) : f32x4{0.f, 0.f, 0.f, 0.f};
     }
 }
+template <bool DOT>
 __device__ __forceinline__ void store_staged_map(const float *sO, rsrc_t out, const MapPre &p, int T0, int L, int Dv,
                                                  int dv0, int cw, int lane, bool rev, bool has_li, float oinv,
-                                                 bool acc) {
+                                                 bool acc, const DotPre &dp, float *drow) {
     const int c4 = lane & 15;
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
@@ -362,17 +398,30 @@ __device__ __forceinline__ void store_staged_map(const float *sO, rsrc_t out, co
         if (acc) x += p.x[rr];
         const uint32_t off = ((uint32_t)dst * Dv + dv0 + 4 * c4) * 4u;
         if (t < L) __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), out, (int)off, 0, 0);
+        if constexpr (DOT) store_dot(dp.s[rr], x, drow, dst, t < L && drow != nullptr, c4);
     }
 }
 
-// Output mapping of a backward-pass instance, set up once per workgroup.
+// Output mapping of a backward-pass instance, set up once per workgroup; dsrc and drow are
+// the dot-product source of the workgroup's (batch, head) (a zero-size range when there is
+// none: its loads return zero) and its row of dot_out for value tile dvt (or null).
 struct OutMap {
-    rsrc_t li;
+    rsrc_t li, dsrc;
+    float *drow;
     float inv;
     bool rev, has_li, acc;
 };
-__device__ __forceinline__ OutMap make_out_map(const KArgs &a, int bh) {
+// dq and dk passes of the backward (a scalar gate and an fp16 q or k operand) form the dot
+// products of their stored rows with q or k
+template <class C>
+constexpr bool kDotPass = !C::CH && (C::H16 == (1 << kOpQ) || C::H16 == (1 << kOpK));
+__device__ __forceinline__ OutMap make_out_map(const KArgs &a, int bh, int dvt) {
     OutMap m;
+    const bool dot = a.dot_out != nullptr && a.dot_src != nullptr;
+    m.dsrc = dot ? make_rsrc(reinterpret_cast<const char *>(a.dot_src) + (size_t)bh * a.L * a.Dv * 2,
+                             (uint64_t)a.L * a.Dv * 2)
+                 : make_rsrc(a.out, 0);
+    m.drow = dot ? a.dot_out + ((size_t)dvt * a.B * a.H + bh) * a.L : nullptr;
     m.rev = a.out_rev != 0;
     m.has_li = a.out_li != nullptr;
     m.li = m.has_li ? make_rsrc(a.out_li + (size_t)bh * a.L, (uint64_t)a.L * 4) : make_rsrc(a.out, 0);
@@ -1585,7 +1634,7 @@ __global__ __launch_bounds__(512, 1) void chunk_output_ws_kernel(KArgs a) {
     const int t_end = min(L, t_begin + a.seg_len);
     const int nch = (t_end - t_begin + kTile - 1) / kTile;
     const Rs rs = make_rs<C>(a, bh, h);
-    [[maybe_unused]] const OutMap om = C::H16 != 0 ? make_out_map(a, bh) : OutMap{};
+    [[maybe_unused]] const OutMap om = C::H16 != 0 ? make_out_map(a, bh, dvt) : OutMap{};
 
     if (w >= 4) {
         // ============================ producers
@@ -1667,6 +1716,13 @@ __global__ __launch_bounds__(512, 1) void chunk_output_ws_kernel(KArgs a) {
         const OpT *sF = reinterpret_cast<const OpT *>(smem + (lp.dbl + (b) * lp.dstride + lp.fh));
 
         v_to_lds<C>(vraw, reinterpret_cast<OpT *>(smem + lp.dbl + (b ^ 1) * lp.dstride + lp.vb), 64 * cw + lane);
+        // the dot-product source rows of this tile's stores, issued before the value prefetch so
+        // that the stores' wait for them does not wait for it
+        [[maybe_unused]] DotPre dp{};
+        if constexpr (kDotPass<C>) {
+            load_dot_pre(dp, om.dsrc, T0, L, Dv, dv0, cw, lane, om.rev);
+            __builtin_amdgcn_sched_barrier(0);  // keep them ahead of the prefetch
+        }
         load_p_v<C>(vraw, rs, T0 + 2 * kTile, cw, lane, dv0, Dv);
 
         // ---------------- phase A: score blocks P^T(j, i) over the key channels and the
@@ -1926,8 +1982,8 @@ __global__ __launch_bounds__(512, 1) void chunk_output_ws_kernel(KArgs a) {
         stage_out(reinterpret_cast<float *>(smem + lp.ostage), O, cw, g, c16);
         lds_barrier();  // B2
         if constexpr (C::H16 != 0)
-            store_staged_map(reinterpret_cast<const float *>(smem + lp.ostage), rs.out, om.li, T0, L, Dv, dv0, cw,
-                             lane, om.rev, om.has_li, om.inv, om.acc);
+            store_staged_map<kDotPass<C>>(reinterpret_cast<const float *>(smem + lp.ostage), rs.out, om.li, T0, L, Dv,
+                                          dv0, cw, lane, om.rev, om.has_li, om.inv, om.acc, dp, om.drow);
         else
             store_staged(reinterpret_cast<const float *>(smem + lp.ostage), rs.out, T0, Dv, dv0, cw, lane);
     }
@@ -2094,7 +2150,7 @@ __global__ __launch_bounds__(512, 1) void chunk_output_sg_kernel(KArgs a) {
     const int t_end = min(L, t_begin + a.seg_len);
     const int nch = (t_end - t_begin + kTile - 1) / kTile;
     const Rs rs = make_rs<C>(a, bh, h);
-    [[maybe_unused]] const OutMap om = C::H16 != 0 ? make_out_map(a, bh) : OutMap{};
+    [[maybe_unused]] const OutMap om = C::H16 != 0 ? make_out_map(a, bh, dvt) : OutMap{};
 
     if (w >= 4) {
         // ============================ producers
@@ -2289,6 +2345,8 @@ __global__ __launch_bounds__(512, 1) void chunk_output_sg_kernel(KArgs a) {
         // consumers issue no other global loads, so waiting for them waits for nothing else)
         [[maybe_unused]] MapPre mp;
         if constexpr (C::H16 != 0) load_map_pre(mp, rs.out, om.li, T0, L, Dv, dv0, cw, lane, om.rev, om.has_li, om.acc);
+        [[maybe_unused]] DotPre dp{};
+        if constexpr (kDotPass<C>) load_dot_pre(dp, om.dsrc, T0, L, Dv, dv0, cw, lane, om.rev);
 
         // ---------------- phase B: scores x values, output
         {
@@ -2307,8 +2365,8 @@ __global__ __launch_bounds__(512, 1) void chunk_output_sg_kernel(KArgs a) {
         stage_out(reinterpret_cast<float *>(smem + lp.ostage), O, cw, g, c16);
         lds_barrier();  // B2
         if constexpr (C::H16 != 0)
-            store_staged_map(reinterpret_cast<const float *>(smem + lp.ostage), rs.out, mp, T0, L, Dv, dv0, cw, lane,
-                             om.rev, om.has_li, om.inv, om.acc);
+            store_staged_map<kDotPass<C>>(reinterpret_cast<const float *>(smem + lp.ostage), rs.out, mp, T0, L, Dv,
+                                          dv0, cw, lane, om.rev, om.has_li, om.inv, om.acc, dp, om.drow);
         else
             store_staged(reinterpret_cast<const float *>(smem + lp.ostage), rs.out, T0, Dv, dv0, cw, lane);
     }

@@ -271,6 +271,12 @@ struct KArgs {
                       // for t = 0); scalar gates are given in the pass's token order
     int out_acc;      // backward-pass instances: add the mapped rows to the output instead of
                       // storing them (a pass split over value columns sums its halves)
+    // Backward dq and dk passes (instances with a scalar gate and an fp16 q or k operand):
+    // for each stored row, its dot product with the same row of dot_src (bf16 [BH][L][Dv] in
+    // sequence order: q for the dq pass, k for the dk pass) over the workgroup's 64 columns,
+    // into dot_out[dvt][bh][row] (dot_out null: none).
+    const void *dot_src;
+    float *dot_out;
 };
 
 #if defined(__HIPCC__)
