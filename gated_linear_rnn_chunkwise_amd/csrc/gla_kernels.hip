@@ -140,17 +140,40 @@ __device__ __forceinline__ u32x4 bld128(rsrc_t r, uint32_t off) {
     return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, AUX);
 }
 
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m);
+// Cross-lane steps on the vector ALU (DPP) and the scalar unit (readlane) rather than through
+// the LDS crossbar (ds_bpermute), whose round trips sit on the producers' critical path.
+template <int CTRL, int ROWS = 0xf>
+__device__ __forceinline__ float dpp(float x) {
+    // lanes without a source in range, and rows outside ROWS, read 0
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROWS, 0xf, false));
+}
+// x of lane n (wave-uniform n), through a scalar register.
+__device__ __forceinline__ float lane_bcast(float x, int n) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), n));
+}
+// Sum over the calling lane's 16-lane row, in every lane of it (row rotations by 8, 4, 2, 1).
+__device__ __forceinline__ float row_sum16(float x) {
+    x += dpp<0x128>(x);
+    x += dpp<0x124>(x);
+    x += dpp<0x122>(x);
+    x += dpp<0x121>(x);
     return x;
 }
-__device__ __forceinline__ float scan_incl(float x, int lane) {
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const float y = __shfl_up(x, off);
-        if (lane >= off) x += y;
-    }
+// Sum over the wave (the four row sums added in row order), the same in every lane.
+__device__ __forceinline__ float wave_sum(float x) {
+    x = row_sum16(x);
+    return (lane_bcast(x, 0) + lane_bcast(x, 16)) + (lane_bcast(x, 32) + lane_bcast(x, 48));
+}
+// Inclusive prefix sum over the wave's lanes: row shifts by 1, 2, 4, 8 within each 16-lane
+// row, then the end of row 0 (row broadcast 15) into rows 1 and 3 and the end of row 1 (row
+// broadcast 31) into rows 2 and 3.
+__device__ __forceinline__ float scan_incl(float x, [[maybe_unused]] int lane) {
+    x += dpp<0x111>(x);
+    x += dpp<0x112>(x);
+    x += dpp<0x114>(x);
+    x += dpp<0x118>(x);
+    x += dpp<0x142, 0xa>(x);
+    x += dpp<0x143, 0xc>(x);
     return x;
 }
 
@@ -319,15 +342,6 @@ __device__ __forceinline__ void load_dot_pre(DotPre &p, rsrc_t src, int T0, int 
         const uint32_t dst = t < L ? (uint32_t)(rev ? L - 1 - t : t) : 0u;
         p.s[rr] = bld64(src, (dst * (uint32_t)Dv + (uint32_t)(dv0 + 4 * c4)) * 2u);
     }
-}
-// Sum over the calling lane's 16-lane row, in every lane of it: DPP row rotations by 8, 4, 2
-// and 1 (vector ALU only, no LDS crossbar).
-__device__ __forceinline__ float row_sum16(float x) {
-    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xf, 0xf, false));
-    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x124, 0xf, 0xf, false));
-    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x122, 0xf, 0xf, false));
-    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x121, 0xf, 0xf, false));
-    return x;
 }
 // The dot product of a stored row segment x with its source row segment, summed over the 16
 // lanes that hold the row's 64 columns; the first of them writes it to drow[dst].
@@ -697,7 +711,7 @@ __device__ __attribute__((noinline)) f32x4 ch_diag_exact(f32x4 acc, Raw<C> r, in
     const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     float ig[16];
 #pragma unroll
-    for (int rr = 0; rr < 16; ++rr) ig[rr] = has_li ? fexp2(__shfl(y, 16 * wv + rr)) : 1.f;
+    for (int rr = 0; rr < 16; ++rr) ig[rr] = has_li ? fexp2(lane_bcast(y, 16 * wv + rr)) : 1.f;
     for (int s = 0; s < 16; ++s) {
         for (int t = s; t < 16; ++t) {
             float part = 0.f;
@@ -882,7 +896,7 @@ __global__ __launch_bounds__(256, 1) void chunk_output_kernel(KArgs a) {
                     if (rs.has_li) {
                         const float y = raw.lis * kLog2e;
 #pragma unroll
-                        for (int rr = 0; rr < 16; ++rr) ig[rr] = fexp2(__shfl(y, 16 * w + rr));
+                        for (int rr = 0; rr < 16; ++rr) ig[rr] = fexp2(lane_bcast(y, 16 * w + rr));
                     } else {
 #pragma unroll
                         for (int rr = 0; rr < 16; ++rr) ig[rr] = 1.f;
@@ -951,7 +965,7 @@ __global__ __launch_bounds__(256, 1) void chunk_output_kernel(KArgs a) {
                     const float x = log2_decay(raw.las);
                     const float y = raw.lis * kLog2e;
                     const float bl = scan_incl(x, lane);
-                    Tt = __shfl(bl, 63);
+                    Tt = lane_bcast(bl, 63);
                     if (w == 0 && sl == 0) {
                         sBr[kTile * tau + lane] = Bc + bl;
                         sLr[kTile * tau + lane] = y;
@@ -963,9 +977,9 @@ __global__ __launch_bounds__(256, 1) void chunk_output_kernel(KArgs a) {
                         for (int e = 0; e < 4; ++e) {
                             const int rr = 4 * g4 + e;
                             const int row = 16 * w + rr;
-                            const float blr = __shfl(bl, 16 * w + rr);
+                            const float blr = lane_bcast(bl, 16 * w + rr);
                             const float eb = fexp2(Bc + blr);
-                            const float ekr = fexp2(Tt - blr + __shfl(y, 16 * w + rr));
+                            const float ekr = fexp2(Tt - blr + lane_bcast(y, 16 * w + rr));
                             float qv[C::CPL], kv[C::CPL], qi[C::CPL];
 #pragma unroll
                             for (int c = 0; c < C::CPL; ++c) {
@@ -1406,7 +1420,7 @@ __device__ __attribute__((noinline)) void ws_exact_block(Raw<C> raw, float *dst,
     const float y = raw.lis * kLog2e;
     float ig[16];
 #pragma unroll
-    for (int rr = 0; rr < 16; ++rr) ig[rr] = has_li ? fexp2(__shfl(y, 16 * pw + rr)) : 1.f;
+    for (int rr = 0; rr < 16; ++rr) ig[rr] = has_li ? fexp2(lane_bcast(y, 16 * pw + rr)) : 1.f;
     for (int t = 0; t < 16; ++t) {
         for (int s2 = 0; s2 <= t; ++s2) {
             float part = 0.f;
@@ -1439,7 +1453,7 @@ __device__ __forceinline__ void ws_produce_a(ProdVals<C> &pv, Raw<C> &raw, const
         if constexpr (C::CH) {
             if (has_li) {
 #pragma unroll
-                for (int rr = 0; rr < 16; ++rr) ig[rr] = fexp2(__shfl(y, 16 * pw + rr));
+                for (int rr = 0; rr < 16; ++rr) ig[rr] = fexp2(lane_bcast(y, 16 * pw + rr));
             } else {
 #pragma unroll
                 for (int rr = 0; rr < 16; ++rr) ig[rr] = 1.f;
@@ -1516,7 +1530,7 @@ __device__ __forceinline__ void ws_produce_a(ProdVals<C> &pv, Raw<C> &raw, const
         const float x = row_valid ? log2_decay(raw.las) : 0.f;
         const float y = raw.lis * kLog2e;
         const float bl = scan_incl(x, lane);
-        const float Tt = __shfl(bl, 63);
+        const float Tt = lane_bcast(bl, 63);
         if (pw == 0) {
             sBr[lane] = bl;
             sLr[lane] = y;
@@ -1530,7 +1544,7 @@ __device__ __forceinline__ void ws_produce_a(ProdVals<C> &pv, Raw<C> &raw, const
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int rr = 4 * g4 + e;
-                const float ekr = __shfl(wk, 16 * pw + rr);
+                const float ekr = lane_bcast(wk, 16 * pw + rr);
                 float qv[C::CPL], kv[C::CPL];
 #pragma unroll
                 for (int c = 0; c < C::CPL; ++c) {
@@ -2087,7 +2101,7 @@ __device__ __forceinline__ void sg_produce_a(ProdSg<C> &pv, const RawSg<C> &raw,
     const float y = raw.lis * kLog2e;
     const float bl = scan_incl(x, lane);
     if (pw == 0) {
-        const float T = __shfl(bl, 63);
+        const float T = lane_bcast(bl, 63);
         float *sR = reinterpret_cast<float *>(smem + lp.rows) + nb * 192;
         sR[lane] = bl;
         sR[64 + lane] = y;
@@ -2440,7 +2454,7 @@ __global__ __launch_bounds__(256, 3) void segment_state_kernel(KArgs a) {
                 if (rs.has_li) {
                     const float y = raw.lis * kLog2e;
 #pragma unroll
-                    for (int rr = 0; rr < 16; ++rr) ig[rr] = fexp2(__shfl(y, 16 * w + rr));
+                    for (int rr = 0; rr < 16; ++rr) ig[rr] = fexp2(lane_bcast(y, 16 * w + rr));
                 } else {
 #pragma unroll
                     for (int rr = 0; rr < 16; ++rr) ig[rr] = 1.f;
@@ -2471,14 +2485,14 @@ __global__ __launch_bounds__(256, 3) void segment_state_kernel(KArgs a) {
                 const float x = log2_decay(raw.las);
                 const float y = raw.lis * kLog2e;
                 const float bl = scan_incl(x, lane);
-                Tt = __shfl(bl, 63);
+                Tt = lane_bcast(bl, 63);
 #pragma unroll
                 for (int g4 = 0; g4 < 4; ++g4) {
                     Half kt4[C::CPL];
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int rr = 4 * g4 + e;
-                        const float f = fexp2(Tt - __shfl(bl, 16 * w + rr) + __shfl(y, 16 * w + rr));
+                        const float f = fexp2(Tt - lane_bcast(bl, 16 * w + rr) + lane_bcast(y, 16 * w + rr));
 #pragma unroll
                         for (int c = 0; c < C::CPL; ++c) kt4[c][e] = (OpT)(raw.kf(rr, c) * f);
                     }
