@@ -51,6 +51,7 @@
 // Rows past the sequence end read as zero through buffer resources (k = v = beta = 0 and
 // no decay: such a token changes nothing) and their output stores are dropped.
 #include <hip/hip_runtime.h>
+#include <type_traits>
 #include <stdint.h>
 
 #include <atomic>
@@ -315,8 +316,8 @@ __global__ __launch_bounds__(256, 1) void delta_chunk_kernel(DeltaArgs a) {
             float x[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) x[e] = (4 * g + e == c16) ? 1.f : 0.f;
-#pragma unroll
-            for (int bg = 0; bg < 4; ++bg) {
+            const auto step = [&](auto bgc) {
+                constexpr int bg = decltype(bgc)::value;
                 if (g == bg) {
 #pragma unroll
                     for (int e = 1; e < 4; ++e)
@@ -325,14 +326,18 @@ __global__ __launch_bounds__(256, 1) void delta_chunk_kernel(DeltaArgs a) {
                 }
                 float xb[4];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) xb[j] = __shfl(x[j], 16 * bg + c16);
+                for (int j = 0; j < 4; ++j) xb[j] = row_to_all<bg>(x[j]);
                 if (g > bg) {
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
 #pragma unroll
                         for (int j = 0; j < 4; ++j) x[e] -= ar[bg][e][j] * xb[j];
                 }
-            }
+            };
+            step(std::integral_constant<int, 0>{});
+            step(std::integral_constant<int, 1>{});
+            step(std::integral_constant<int, 2>{});
+            step(std::integral_constant<int, 3>{});
 #pragma unroll
             for (int e = 0; e < 4; ++e) blk[(4 * g + e) * kAR + c16] = x[e];
         }

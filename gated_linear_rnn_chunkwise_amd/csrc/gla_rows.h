@@ -81,13 +81,50 @@ __device__ __forceinline__ float log2_decay(float la) {
     const float x = la * kLog2e;
     return x < -150.f ? -150.f : x;
 }
-__device__ __forceinline__ float scan_incl(float x, int lane) {
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const float y = __shfl_up(x, off);
-        if (lane >= off) x += y;
-    }
+// One DPP step: x of the lane CTRL selects (rows outside ROWS, and lanes whose source lies
+// outside their row, read `none`).
+template <int CTRL, int ROWS = 0xf>
+__device__ __forceinline__ float dpp_or(float x, float none) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(none), __float_as_int(x), CTRL, ROWS, 0xf, false));
+}
+// Inclusive prefix of op over the wave's lanes on the vector ALU (no LDS crossbar): row
+// shifts by 1, 2, 4, 8 within each 16-lane row, then the end of row 0 (row broadcast 15) into
+// rows 1 and 3 and the end of row 1 (row broadcast 31) into rows 2 and 3; id is op's identity.
+template <class Op>
+__device__ __forceinline__ float scan_dpp(float x, float id, Op op) {
+    x = op(x, dpp_or<0x111>(x, id));
+    x = op(x, dpp_or<0x112>(x, id));
+    x = op(x, dpp_or<0x114>(x, id));
+    x = op(x, dpp_or<0x118>(x, id));
+    x = op(x, dpp_or<0x142, 0xa>(x, id));
+    x = op(x, dpp_or<0x143, 0xc>(x, id));
     return x;
+}
+__device__ __forceinline__ float scan_incl(float x, [[maybe_unused]] int lane) {
+    return scan_dpp(x, 0.f, [](float u, float v) { return u + v; });
+}
+// x of lane n (wave-uniform n), through a scalar register.
+__device__ __forceinline__ float lane_bcast(float x, int n) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), n));
+}
+// gfx950 lane-swap moves (v_permlane16_swap / v_permlane32_swap) of x with itself: the first
+// result holds rows (0, 0, 2, 2) / halves (0, 0) of x, the second rows (1, 1, 3, 3) / halves
+// (1, 1), rows being 16 lanes and halves 32.
+__device__ __forceinline__ float add_xor16(float x) {  // x + x of lane (l ^ 16)
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float add_xor32(float x) {  // x + x of lane (l ^ 32)
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// Row R (0..3) of x in every row: x of lane 16 R + (l & 15).
+template <int R>
+__device__ __forceinline__ float row_to_all(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    const uint32_t y = a[R & 1];  // rows (R&1, R&1, 2+(R&1), 2+(R&1))
+    const auto b = __builtin_amdgcn_permlane32_swap(y, y, false, false);
+    return __uint_as_float(b[R >> 1]);
 }
 // Workgroups i and i+8, ... go to the same XCD; consecutive logical workgroups (the value
 // slices of one head, which read the same q and k) are placed on one XCD to share its L2.

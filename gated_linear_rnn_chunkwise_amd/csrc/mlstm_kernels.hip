@@ -102,13 +102,8 @@ __host__ __device__ inline Plan make_plan(bool f32, int dk, int cols) {
 int wg_cols(bool f32, int dk, int dv) { return !f32 && dk == 256 && dv % 128 == 0 ? 128 : 64; }
 uint32_t lds_bytes(bool f32, int dk, int cols) { return make_plan(f32, dk, cols).total; }
 
-__device__ __forceinline__ float scan_max(float x, int lane) {
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const float y = __shfl_up(x, off);
-        if (lane >= off) x = fmaxf(x, y);
-    }
-    return x;
+__device__ __forceinline__ float scan_max(float x, [[maybe_unused]] int lane) {
+    return scan_dpp(x, -__builtin_inff(), [](float u, float v) { return fmaxf(u, v); });
 }
 
 // The next chunk's raw pieces plus the two gates of token tid & 63.
@@ -137,7 +132,7 @@ __device__ __forceinline__ void stage(const Pref<C> &pf, unsigned char *smem, co
         const float b = scan_incl(x, lane);
         const float a = row_valid_lane ? pf.li * kLog2e - b : kNone;
         const float M = fmaxf(scan_max(a, lane), m_in);
-        const float Me = __shfl(M, 63);
+        const float Me = lane_bcast(M, 63);
         reinterpret_cast<float *>(smem + lp.a)[lane] = a;
         reinterpret_cast<float *>(smem + lp.mx)[lane] = M;
         reinterpret_cast<float *>(smem + lp.mt)[lane] = b + M;
@@ -204,10 +199,8 @@ __device__ __forceinline__ void scores(const typename C::OpT *sQ, const typename
 #pragma unroll
         for (int e = 0; e < 4; ++e) qn += (float)qf[e] * n0[e] + (float)qf[e + 4] * n1[e];
     }
-    rs += __shfl_xor(rs, 16);
-    rs += __shfl_xor(rs, 32);
-    qn += __shfl_xor(qn, 16);
-    qn += __shfl_xor(qn, 32);
+    rs = add_xor32(add_xor16(rs));
+    qn = add_xor32(add_xor16(qn));
     if (g == 0) sDen[t] = fexp2(m_in - Mt) * qn + rs;
 }
 
