@@ -856,12 +856,14 @@ __global__ __launch_bounds__(256, 2) void chan_vg16_kernel(ChanPass a) {
             if constexpr (gg) {
                 // running sum over the block's 16 tokens (token 4 g + e): within the lane, then
                 // over the lane groups g of the column (lanes c16 + 16 g)
+                // by gfx950 lane-swap moves: p0 / p1 hold rows (0, 0, 2, 2) / (1, 1, 3, 3) of c3,
+                // their sum the pair sums; h0 / h1 the pair sums of rows 0-1 / 2-3 in every row
                 const float c1 = gt[0] + gt[1], c2 = c1 + gt[2], c3 = c2 + gt[3];
-                float inc = c3;
-                float y = __shfl_up(inc, 16);
-                inc += g >= 1 ? y : 0.f;
-                y = __shfl_up(inc, 32);
-                inc += g >= 2 ? y : 0.f;
+                const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(c3), __float_as_uint(c3), false, false);
+                const float pair = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+                const auto hq = __builtin_amdgcn_permlane32_swap(__float_as_uint(pair), __float_as_uint(pair), false, false);
+                const float h0 = __uint_as_float(hq[0]), h1 = __uint_as_float(hq[1]);
+                const float inc = g == 0 ? c3 : (g == 1 ? pair : (g == 2 ? h0 + c3 : h0 + pair));
                 const float base = gf + grun + (inc - c3);
                 const float cs[4] = {gt[0], c1, c2, c3};
 #pragma unroll
@@ -869,7 +871,7 @@ __global__ __launch_bounds__(256, 2) void chan_vg16_kernel(ChanPass a) {
                     const int u = u0 + 4 * g + e;
                     if (u < ue) a.g_out[(bh * L + (a.orev ? L - 1 - u : u)) * Dn + n0 + ncol] = base + cs[e];
                 }
-                grun += __shfl(inc, 48 + c16);
+                grun += h0 + h1;  // the column's total over the block (row 3's inc)
             }
         }
         // ---- state to the block end: S diag(2^(b_15)) + k^T (v 2^(b_15 - b_s))
