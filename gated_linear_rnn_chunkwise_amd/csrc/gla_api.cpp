@@ -26,6 +26,7 @@ hipError_t launch_step(const gla_step_desc &d, hipStream_t st);
 hipError_t bwd_reverse(const void *src, int dt, float *dst, int BH, int L, int D, hipStream_t st);
 hipError_t bwd_gate(const float *la, int kind, float *dst, int BH, int H, int L, hipStream_t st);
 hipError_t bwd_transpose(const float *src, const uint32_t *mx, float *dst, int BH, int R, int C, hipStream_t st);
+hipError_t bwd_transpose_entries(float *ws, int BH, int N, int nseg, int nsub, hipStream_t st);
 size_t bwd_absmax_parts(int L, int Dv, int Dk, bool dfin);
 hipError_t bwd_dout16(const float *dout, const float *dfin, float *part, uint32_t *mx, _Float16 *fwd, _Float16 *rev,
                       int BH, int L, int Dv, int Dk, hipStream_t st);
@@ -294,6 +295,7 @@ struct OutMapArgs {
     int acc = 0;     // add to the output instead of storing
     const void *dot_src = nullptr;  // dq and dk passes: rows to dot with the stored rows
     float *dot_out = nullptr;       // [Dv/64][BH][L] dot products per 64-column tile
+    int state_t = 0;  // the workspace already holds the segment-entry states, transposed
 };
 
 // The forward pass; h16 marks operands given as fp16 instead of bf16 and om maps the output
@@ -351,6 +353,8 @@ int fwd_run(const gla_desc *d, int h16, void *stream, const OutMapArgs &om = Out
     a.out_acc = om.acc;
     a.dot_src = om.dot_src;
     a.dot_out = om.dot_out;
+    a.state_t = om.state_t;
+    if (om.state_t && (!d->workspace || p.nseg < 2)) return GLA_ERR_INVALID_ARG;
 
     const hipError_t err = gla::launch_forward(a, d->in_dtype == GLA_DTYPE_F32, h16, d->Dk, s);
     if (owned) (void)hipFreeAsync(ws, s);
@@ -843,8 +847,8 @@ int gla_bwd(const gla_bwd_desc *d, void *stream) {
     const void *rq = bf ? d->q : V(p.rq), *rk = bf ? d->k : V(p.rk), *rv = bf ? d->v : V(p.rv);
     const void *rdo = bf ? fdo : V(p.rdo);
     // dv (reversed; its final state is the gradient of the state after token 0)
-    fwd(bwd_pass_desc(d, Dk, Dv, rk, rq, rdo, rgate, rla, nullptr, s0A, bf ? d->dv : F(p.oA), F(p.finA)), gla::kH16V,
-        om_rev);
+    const gla_desc fA = bwd_pass_desc(d, Dk, Dv, rk, rq, rdo, rgate, rla, nullptr, s0A, bf ? d->dv : F(p.oA), F(p.finA));
+    fwd(fA, gla::kH16V, om_rev);
     if (!bwd_split_dv(d)) {
         // dk (reversed, keys and values exchanged), with k . dk per stored row (bf16)
         OutMapArgs om_k = om_rev, om_dq = om_q;
@@ -852,9 +856,20 @@ int gla_bwd(const gla_bwd_desc *d, void *stream) {
             om_k.dot_src = d->k;
             om_k.dot_out = F(p.dkp);
         }
-        fwd(bwd_pass_desc(d, Dv, Dk, rv, rdo, rq, rgate, rla, nullptr, d->dfinal_state ? F(p.dfT) : nullptr,
-                          bf ? d->dk : F(p.oB), nullptr),
-            gla::kH16K, om_k);
+        const gla_desc fB = bwd_pass_desc(d, Dv, Dk, rv, rdo, rq, rgate, rla, nullptr,
+                                          d->dfinal_state ? F(p.dfT) : nullptr, bf ? d->dk : F(p.oB), nullptr);
+        // Its state is the dv pass's transposed: the same gate, keys and values exchanged, and
+        // the initial state transposed.  With Dk = Dv both passes plan the same segments, and
+        // (bf16: the passes share the workspace) the dk pass starts its segments from the dv
+        // pass's segment-entry states, still in the workspace and transposed there in place,
+        // instead of forming its own.
+        Plan pA, pB;
+        if (bf && Dk == Dv && checked_plan(&fA, &pA) == GLA_OK && checked_plan(&fB, &pB) == GLA_OK &&
+            pA.nseg > 1 && pA.nseg == pB.nseg && pA.nsub == pB.nsub && pA.seg_len == pB.seg_len &&
+            pA.knt == 1 && pB.knt == 1 && rc == GLA_OK) {
+            om_k.state_t = ok(gla::bwd_transpose_entries(F(p.fws), BH, Dk, pA.nseg, pA.nsub, s)) ? 1 : 0;
+        }
+        fwd(fB, gla::kH16K, om_k);
         // dq (keys and values exchanged; its final state is the forward final state, transposed),
         // with q . dq per stored row (bf16, when the log-gate gradient is wanted)
         if (p.dqp) {

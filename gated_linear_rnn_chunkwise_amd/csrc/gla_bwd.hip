@@ -174,6 +174,38 @@ __global__ __launch_bounds__(256) void bwd_transpose_kernel(const float *src, co
     for (int y = y0; y < 64; y += 4) o[(size_t)(bc * 64 + y) * R + br * 64 + x] = tile[x][y];
 }
 
+// In place, the transpose of the square N x N segment-entry states of a pass's workspace:
+// entry j*nsub-1 (j = 1 .. nseg-1) of each slice's (nseg-1)*nsub state entries.  The dk pass
+// state is the dv pass's transposed, so these turn the dv pass's entry states into the dk
+// pass's.  One workgroup per pair of 64 x 64 tiles (bi <= bj) of a matrix; both tiles are read
+// into LDS (whole rows) before either is written back, each in the other's place.
+__global__ __launch_bounds__(256) void bwd_transpose_entries_kernel(float *ws, int N, int nseg, int nsub) {
+    __shared__ float ta[64][65], tb[64][65];
+    const int T = N / 64, npair = T * (T + 1) / 2;
+    size_t id = blockIdx.x;
+    int pr = (int)(id % (unsigned)npair);
+    id /= (unsigned)npair;
+    const int j = (int)(id % (unsigned)(nseg - 1)) + 1;
+    const size_t bh = id / (unsigned)(nseg - 1);
+    int bi = 0;
+    while (pr >= T - bi) {
+        pr -= T - bi;
+        ++bi;
+    }
+    const int bj = bi + pr;
+    float *m = ws + (bh * (size_t)(nseg - 1) * nsub + (size_t)j * nsub - 1) * N * N;
+    const int x = (int)threadIdx.x & 63, y0 = (int)threadIdx.x >> 6;
+    for (int y = y0; y < 64; y += 4) {
+        ta[y][x] = m[(size_t)(bi * 64 + y) * N + bj * 64 + x];
+        tb[y][x] = m[(size_t)(bj * 64 + y) * N + bi * 64 + x];
+    }
+    __syncthreads();
+    for (int y = y0; y < 64; y += 4) {
+        m[(size_t)(bi * 64 + y) * N + bj * 64 + x] = tb[x][y];
+        m[(size_t)(bj * 64 + y) * N + bi * 64 + x] = ta[x][y];
+    }
+}
+
 // One wave per token: dk_t = i_t oB[L-1-t], dv_t = i_t oA[L-1-t]; g_t = q_t . dq_t - k_t . dk_t;
 // dlog_ig_t = k_t . dk_t.  Without oA / oB the passes stored dk, dv and dq in place (scaled
 // and un-reversed) and only the dot products are formed.  Dk and Dv are at most 256.
@@ -404,6 +436,14 @@ hipError_t bwd_gate(const float *la, int kind, float *dst, int BH, int H, int L,
 hipError_t bwd_transpose(const float *src, const uint32_t *mx, float *dst, int BH, int R, int C, hipStream_t st) {
     const size_t tiles = (size_t)BH * (R / 64) * (C / 64);
     hipLaunchKernelGGL(bwd_transpose_kernel, dim3((unsigned)tiles), dim3(256), 0, st, src, mx, dst, R, C);
+    return hipGetLastError();
+}
+
+hipError_t bwd_transpose_entries(float *ws, int BH, int N, int nseg, int nsub, hipStream_t st) {
+    if (nseg < 2) return hipSuccess;
+    const int T = N / 64;
+    const size_t blocks = (size_t)BH * (size_t)(nseg - 1) * (size_t)(T * (T + 1) / 2);
+    hipLaunchKernelGGL(bwd_transpose_entries_kernel, dim3((unsigned)blocks), dim3(256), 0, st, ws, N, nseg, nsub);
     return hipGetLastError();
 }
 

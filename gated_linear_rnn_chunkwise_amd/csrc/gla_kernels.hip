@@ -2612,7 +2612,8 @@ static hipError_t ensure_lds_limit(const void *fn, std::atomic<uint64_t> &done) 
 template <class C>
 static hipError_t launch_cfg(const KArgs &a, hipStream_t st) {
     hipError_t err;
-    if (a.nseg > 1) {
+    // entry states given (state_t): only the chunk-output kernel runs
+    if (a.nseg > 1 && !a.state_t) {
         const LdsPlanState l1 = lds_plan_state(C::OPB, C::DK);
         static std::atomic<uint64_t> done_state{0};
         err = ensure_lds_limit(reinterpret_cast<const void *>(&segment_state_kernel<C>), done_state);

@@ -277,6 +277,9 @@ struct KArgs {
     // into dot_out[dvt][bh][row] (dot_out null: none).
     const void *dot_src;
     float *dot_out;
+    // Segment-entry states given: entry s*nsub-1 of ws_state already holds the state entering
+    // segment s (prepared by the caller); the segment-state kernel and the scan do not run.
+    int state_t;
 };
 
 #if defined(__HIPCC__)

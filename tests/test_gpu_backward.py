@@ -155,6 +155,29 @@ def test_backward_mlstm_head_shape_long(gpu_lib):
     check_all(got, ref, "mlstm head shape L4096", "bf16", d, "head")
 
 
+@pytest.mark.parametrize("gate,ig,Dk,Dv", [("head", True, 128, 128), ("head_const", False, 128, 128),
+                                            ("none", False, 64, 128), ("head", False, 256, 256)])
+def test_backward_segmented_scalar_gate(gpu_lib, gate, ig, Dk, Dv):
+    # two (batch, head) slices at length 34001: the passes split the sequence into dozens of
+    # segments (segment-state kernels, scans, chunk-output workgroups starting from entry
+    # states), ragged tail.  With Dk = Dv the dk pass takes the dv pass's segment-entry states,
+    # read transposed; with Dk != Dv the two passes plan different segments and each forms its
+    # own.  Initial state and final-state gradient given.
+    w = gin.custom(1, 2, 34001, Dk, Dv, 64, dtype="bf16", gate=gate, input_gate=ig)
+    for a, b in ((Dk, Dv), (Dv, Dk)):
+        # the forward plan of each pass shape (planning only; the pointers are never used)
+        pd = gpu_lib.GlaDesc()
+        for key, val in dict(B=1, H=2, L=34001, Dk=a, Dv=b, chunk=64, in_dtype=gpu_lib.DTYPE_BF16,
+                             gate_kind=gpu_lib.GATE_HEAD, q=256, k=256, v=256, log_alpha=256, out=256).items():
+            setattr(pd, key, val)
+        assert gpu_lib.plan(pd).n_seg > 8
+    d = gin.make_inputs(w, seed=40 + Dk)
+    dout, s0, df = grads_in(w, 41, True, True)
+    got = run(gpu_lib, w, d, dout, s0, df)
+    ref = oracle.backward(d["q"], d["k"], d["v"], dout, gate, d["log_alpha"], d["log_ig"], s0, df)
+    check_all(got, ref, "segmented %s Dk%d Dv%d" % (gate, Dk, Dv), "bf16", d, gate)
+
+
 def test_backward_strong_decay(gpu_lib):
     # per head and token gate near zero on some tokens: the reversed passes see the same decays
     w = gin.custom(1, 2, 150, 64, 64, 64, dtype="bf16", gate="head", input_gate=True)
