@@ -5,8 +5,10 @@
 
 A step is one forward pass of the whole hot path (every kernel the library launches for
 the workload) over one batch of synthetic, seeded inputs that are already resident in HBM.
-W untimed steps run first; then exactly K steps are timed between two device
-synchronisations.  Two input sets alternate between steps so successive steps do not
+The step first runs untimed for a fixed SETTLE_S seconds of wall clock (the GPU's clocks
+and the inputs' page-table entries reach their steady state: short runs otherwise time the
+first launches about 10% slower), then W untimed warmup steps run; then exactly K steps are
+timed between two device synchronisations.  Two input sets alternate between steps so successive steps do not
 re-read the same bytes from the 256 MB last-level cache.  Prints one JSON line.
 
 Reported beside the throughput:
@@ -48,6 +50,23 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+SETTLE_S = 0.25
+
+
+def settle(torch, step, seconds: float = SETTLE_S) -> int:
+    """Run ``step`` untimed, in batches of 16 launches, until ``seconds`` of wall clock have
+    passed; returns the number of launches.  Nothing it runs is part of the timed region."""
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    n = 0
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(16):
+            step(n)
+            n += 1
+        torch.cuda.synchronize()
+    return n
 
 
 def algorithmic_flops(w, chunk=None) -> float:
@@ -230,6 +249,7 @@ def decode_bench(args, torch, gla, gin, w, wname):
         if st != 0:
             raise gla.GlaError(st, "gla_step")
 
+    settle(torch, step)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -257,6 +277,7 @@ def decode_bench(args, torch, gla, gin, w, wname):
         "n_gpus": 1,
         "steps": K,
         "warmup": args.warmup,
+        "settle_s": SETTLE_S,
         "ms_per_step": round(ms_per_step, 6),
         "higher_is_better": True,
         "scaling": "weak",
@@ -319,6 +340,7 @@ def backward_bench(args, torch, gla, gin, w, wname):
         if st != 0:
             raise gla.GlaError(st, "gla_bwd")
 
+    settle(torch, step)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -345,6 +367,7 @@ def backward_bench(args, torch, gla, gin, w, wname):
         "n_gpus": 1,
         "steps": K,
         "warmup": args.warmup,
+        "settle_s": SETTLE_S,
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -491,6 +514,7 @@ def rows_bench(args, torch, gla, gin, w, wname, rule):
         if st != 0:
             raise gla.GlaError(st, entry)
 
+    settle(torch, step)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -520,6 +544,7 @@ def rows_bench(args, torch, gla, gin, w, wname, rule):
         "n_gpus": 1,
         "steps": K,
         "warmup": args.warmup,
+        "settle_s": SETTLE_S,
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -628,6 +653,7 @@ def main():
         if st != 0:
             raise gla.GlaError(st, "gla_fwd_ex")
 
+    settle(torch, step)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -700,6 +726,7 @@ def main():
         "n_gpus": 1,
         "steps": K,
         "warmup": args.warmup,
+        "settle_s": SETTLE_S,
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
