@@ -357,6 +357,109 @@ def test_full_workload_whole_tensor(gpu_lib, name, form):
     print("  out max|err|/RMS = %.3e, final_state %.3e" % (e, ef), flush=True)
 
 
+# ------------------------------------------------------------------------------ longest slices
+# The longest sequence a (batch, head) slice may have: one slice is addressed with 32-bit byte
+# offsets, (L + 1024) * max(Dk, Dv) * 4 < 2^32.  Too long for the oracle's whole recurrence,
+# so the comparison uses a property that holds at any length: a token whose log gate is -1e4 on
+# every channel (a decay of exactly zero in fp32) starts the state afresh, S_t = i_t k_t^T v_t,
+# so the outputs from that token on, and the final state after the last such token, equal the
+# recurrence run from zero over the tokens from it alone.  Several such tokens are planted (one
+# at the start, one in the middle, one near the end) and the window after each is compared
+# whole with the oracle.  Two slices, so the second slice's fp32 gate and output rows start
+# past 4 GiB (slice bases are 64-bit addresses).  Inputs are seeded draws made on the device.
+LONGEST = [
+    # dtype, gate, input gate, Dk, Dv
+    ("bf16", "channel", False, 128, 128),
+    ("bf16", "head", True, 256, 512),
+]
+
+
+@pytest.mark.parametrize("dtype,gate,ig,Dk,Dv", LONGEST)
+def test_longest_slice_windows(gpu_lib, dtype, gate, ig, Dk, Dv):
+    B, H = 1, 2
+    L = (1 << 32) // (max(Dk, Dv) * 4) - 1025
+    assert (L + 1024) * max(Dk, Dv) * 4 < (1 << 32) <= (L + 1025) * max(Dk, Dv) * 4
+    dev = "cuda"
+    print("longest slice %s %s Dk%d Dv%d L=%d" % (dtype, gate, Dk, Dv, L), flush=True)
+    g = torch.Generator(device=dev)
+    g.manual_seed(77 + Dk)
+    wdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    q = (torch.randn(B, H, L, Dk, generator=g, device=dev) / Dk ** 0.5).to(wdt)
+    k = (torch.randn(B, H, L, Dk, generator=g, device=dev) / Dk ** 0.5).to(wdt)
+    v = (torch.randn(B, H, L, Dv, generator=g, device=dev) / Dk ** 0.5).to(wdt)
+    shape = (B, H, L, Dk) if gate == "channel" else (B, H, L)
+    la = torch.nn.functional.logsigmoid(torch.randn(*shape, generator=g, device=dev)) / 16
+    li = torch.nn.functional.logsigmoid(torch.randn(B, H, L, generator=g, device=dev)) if ig else None
+    W = 1000
+    starts = [0, L // 3 + 17, L - 1500]
+    for t in starts:
+        la[:, :, t] = -1e4
+    out, fin = gpu_lib.fwd(q, k, v, la, log_ig=li, chunk=64)
+    torch.cuda.synchronize()
+    cpu = lambda x, a, b: None if x is None else x[:, :, a:b].cpu()
+    for t in starts:
+        e = min(L, t + W) if t != starts[-1] else L
+        ref, rfin = oracle.recurrent(cpu(q, t, e), cpu(k, t, e), cpu(v, t, e), gate, cpu(la, t, e), cpu(li, t, e))
+        got = out[:, :, t:e].cpu().double().numpy()
+        err = rel_err(got, ref)
+        print("  window [%d, %d): out max|err|/RMS = %.3e" % (t, e, err), flush=True)
+        assert err <= TOL[dtype], "window at %d: %.3e" % (t, err)
+        if e == L:
+            ef = rel_err(fin.cpu().double().numpy(), rfin)
+            print("  final_state max|err|/RMS = %.3e" % ef, flush=True)
+            assert ef <= TOL[dtype]
+    del q, k, v, la, li, out, fin
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("dtype,gate,ig,Dk,Dv", LONGEST)
+def test_longest_slice_state_across_segments(gpu_lib, dtype, gate, ig, Dk, Dv):
+    # The state carried across the whole longest slice (dozens of sequence segments, the
+    # segment-state kernel and the scan): every log gate is 0 (no decay) and every key is zero
+    # except at 64 planted tokens spread over the sequence, so the state at token t is the
+    # input-gated sum of the planted tokens' k^T v up to t, exactly the recurrence over the
+    # planted tokens alone.  A window's outputs are compared with the recurrence run over the
+    # planted tokens before it followed by the window's own tokens; the last window also
+    # compares the final state.
+    B, H = 1, 2
+    L = (1 << 32) // (max(Dk, Dv) * 4) - 1025
+    dev = "cuda"
+    print("longest slice, state across segments: %s %s Dk%d Dv%d L=%d" % (dtype, gate, Dk, Dv, L), flush=True)
+    g = torch.Generator(device=dev)
+    g.manual_seed(91 + Dk)
+    wdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    q = (torch.randn(B, H, L, Dk, generator=g, device=dev) / Dk ** 0.5).to(wdt)
+    v = (torch.randn(B, H, L, Dv, generator=g, device=dev) / Dk ** 0.5).to(wdt)
+    rng = np.random.default_rng(5 + Dk)
+    planted = np.sort(rng.choice(L - 2000, size=64, replace=False))
+    k = torch.zeros(B, H, L, Dk, dtype=wdt, device=dev)
+    kp = torch.randn(B, H, len(planted), Dk, generator=g, device=dev) / Dk ** 0.5
+    k[:, :, torch.from_numpy(planted).to(dev)] = kp.to(wdt)
+    shape = (B, H, L, Dk) if gate == "channel" else (B, H, L)
+    la = torch.zeros(*shape, device=dev)
+    li = torch.nn.functional.logsigmoid(torch.randn(B, H, L, generator=g, device=dev)) if ig else None
+    out, fin = gpu_lib.fwd(q, k, v, la, log_ig=li, chunk=64)
+    torch.cuda.synchronize()
+    W = 1000
+    for a in (L // 2 + 5, L - 1200):
+        b = min(L, a + W) if a != L - 1200 else L
+        idx = torch.from_numpy(np.concatenate([planted[planted < a], np.arange(a, b)])).to(dev)
+        sel = lambda x: None if x is None else x[:, :, idx].cpu()
+        ref, rfin = oracle.recurrent(sel(q), sel(k), sel(v), gate, sel(la), sel(li))
+        n = b - a
+        got = out[:, :, a:b].cpu().double().numpy()
+        err = rel_err(got, ref[:, :, -n:])
+        print("  window [%d, %d) after %d planted tokens: out max|err|/RMS = %.3e"
+              % (a, b, int((planted < a).sum()), err), flush=True)
+        assert err <= TOL[dtype], "window at %d: %.3e" % (a, err)
+        if b == L:
+            ef = rel_err(fin.cpu().double().numpy(), rfin)
+            print("  final_state max|err|/RMS = %.3e" % ef, flush=True)
+            assert ef <= TOL[dtype]
+    del q, k, v, la, li, out, fin
+    torch.cuda.empty_cache()
+
+
 # ------------------------------------------------------------------------------ recurrent step
 def _token(d, w, t):
     """Inputs of token t: q, k [B,H,Dk], v [B,H,Dv], gate in the step layout, input gate [B,H]."""
