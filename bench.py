@@ -705,7 +705,9 @@ def main():
             + float(w.B * w.H) * (2 * nss + (1 + qs) * (plan.n_seg - 1)) * (w.Dk * w.Dv + w.Dk) * 4
         scope = "whole step (segment-state, segment-scan and chunk-output kernels)"
     achieved = io / (mean_launch_ms * 1e-3) / 1e9
-    traffic = measured_traffic(wname) if plan.n_seg == 1 else None
+    # the committed counters are those of the default form's single kernel
+    default_form = plan.n_seg == 1 and not plan.tile_pairs and not plan.query_tiles
+    traffic = measured_traffic(wname) if default_form else None
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic, "kernel": scope,
             "algorithmic_bytes_per_launch": io, "extra_bytes": extra,
