@@ -50,7 +50,11 @@ constexpr int kTargetWorkgroups = 256;     // one per compute unit on MI355X
 // per tile is heavier (measured on the RetNet and long-sequence GLA workloads: 3-4% apart).
 constexpr int kTargetStateWorkgroups = 768;
 constexpr int kTargetStateWorkgroupsChannel = 512;
-constexpr int64_t kSmallProblem = 65536;   // head-tokens below which segmenting does not pay
+// A walk of at most this many 64-token tiles runs as one segment: the segment-state kernel and
+// the scan cost about as much as they save there (measured at L = 1024, B*H = 1..32).  Longer
+// walks with fewer than kTargetWorkgroups workgroups are always split: one workgroup walking
+// 1,024 tiles took 2.46 ms where 128 segments took 0.095 ms.
+constexpr int kShortWalkTiles = 16;
 
 struct Plan {
     int nt, nc, ndv, seg_chunks, nseg, seg_len, nsub;
@@ -119,7 +123,7 @@ int make_plan(const gla_desc *d, Plan *p) {
         sc = 1;  // the chunk-start states are materialised by the segment-state kernel and scan
     } else if (d->seg_chunks > 0) {
         sc = std::min(d->seg_chunks, p->nc);
-    } else if (wg1 >= kTargetWorkgroups || bh * d->L <= kSmallProblem) {
+    } else if (wg1 >= kTargetWorkgroups || (int64_t(d->L) + gla::kTile - 1) / gla::kTile <= kShortWalkTiles) {
         sc = p->nc;
     } else {
         const int64_t want = (kTargetWorkgroups + wg1 - 1) / wg1;

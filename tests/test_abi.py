@@ -198,6 +198,10 @@ def test_workspace_size_formula(lib):
     (1, 16, 32768, 128, 256, 8),
     (8, 8, 8192, 512, 256, 1),
     (1, 1, 256, 64, 64, 1),        # tiny: not worth segmenting
+    (1, 1, 1024, 128, 64, 1),      # a walk of 16 tiles stays one segment
+    (1, 1, 1088, 128, 64, 17),     # 17 tiles on 2 workgroups: one tile per segment
+    (1, 1, 65536, 128, 64, 128),   # short batch, long sequence: 128 segments fill the grid
+    (2, 2, 2048, 128, 64, 32),
 ])
 def test_automatic_segmentation(lib, B, H, L, Dv, chunk, expect_seg):
     big = Dv == 512  # the mLSTM-style workload: per-head gate, Dk = 256
