@@ -8,13 +8,15 @@ the workload) over one batch of synthetic, seeded inputs that are already reside
 The step first runs untimed for a fixed SETTLE_S seconds of wall clock (the GPU's clocks
 and the inputs' page-table entries reach their steady state: short runs otherwise time the
 first launches about 10% slower), then W untimed warmup steps run; then exactly K steps are
-timed between two device synchronisations.  Two input sets alternate between steps so successive steps do not
+timed between two device synchronisations.  A second pass of K steps, with HIP events
+around each launch, gives the launch durations the roofline uses.  Two input sets alternate between steps so successive steps do not
 re-read the same bytes from the 256 MB last-level cache.  Prints one JSON line.
 
 Reported beside the throughput:
 * ``roofline`` of the dominant kernel: the I/O floor (inputs and gates read once, fp32
-  output and final state written once) over the mean launch duration (HIP events recorded
-  on the stream the kernels run on; the median and the minimum beside it), against the
+  output and final state written once) over the mean launch duration of the timed region
+  (one pair of HIP events on the launch stream around the K timed launches; the median and
+  the minimum of a second, per-launch timed pass beside it), against the
   8 TB/s HBM peak.  Bytes moved beyond the floor (segment states, second reads) are ``extra_bytes``
   and not credited.  ``traffic`` is the measured HBM traffic of that kernel from rocprofv3
   counters (profiles/), or null when the counters were taken on other kernel source.
@@ -89,6 +91,31 @@ def host_cpu_model() -> str:
 
     return platform.processor() or "unknown"
 
+
+def timed_steps(torch, step, stream, K):
+    """Exactly K steps between two device synchronisations: the wall clock gives the
+    throughput and one pair of HIP events on the launch stream, around the same K launches,
+    the mean launch duration of the roofline (any gap between launches counted in).  Then K
+    more steps, each between its own pair of events, give the median and minimum launch
+    (those event packets cost about 6 us per step, so they stay out of the timed region).
+    Returns (ms per step, mean launch ms, per-launch ms)."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(K):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    torch.cuda.synchronize()
+    for i in range(K):
+        ev[i][0].record(stream)
+        step(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    return (t1 - t0) * 1e3 / K, e0.elapsed_time(e1) / K, [a.elapsed_time(b) for a, b in ev]
 
 def quantiles(xs):
     xs = sorted(xs)
@@ -519,18 +546,7 @@ def rows_bench(args, torch, gla, gin, w, wname, rule):
         step(i)
     torch.cuda.synchronize()
     K = args.steps
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(K):
-        ev[i][0].record(stream)
-        step(i)
-        ev[i][1].record(stream)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / K
-    launch_ms = [a.elapsed_time(b) for a, b in ev]
-    mean_ms = sum(launch_ms) / K
+    ms_per_step, mean_ms, launch_ms = timed_steps(torch, step, stream, K)
     med_ms, min_ms = quantiles(launch_ms)
     achieved = io / (mean_ms * 1e-3) / 1e9
     cpu = None
@@ -659,18 +675,7 @@ def main():
     torch.cuda.synchronize()
 
     K = args.steps
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(K):
-        ev[i][0].record(stream)
-        step(i)
-        ev[i][1].record(stream)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / K
-    launch_ms = [a.elapsed_time(b) for a, b in ev]
-    mean_launch_ms = sum(launch_ms) / K
+    ms_per_step, mean_launch_ms, launch_ms = timed_steps(torch, step, stream, K)
 
     med_launch_ms, min_launch_ms = quantiles(launch_ms)
 
