@@ -702,10 +702,11 @@ int bwd_plan(const gla_bwd_desc *d, BwdPlan *p) {
     p->g = gate ? take(bh * L * 4) : 0;
     p->part = take(bh * 4);
     const bool split = bwd_split_dv(d);
-    // bf16 without the value split: the dq and dk passes form q . dq and k . dk as they store
-    // (offset 0 means none: fdo is taken first for bf16)
+    // bf16: the dq and dk passes form q . dq and k . dk as they store (with the value split,
+    // the second half's passes, whose stored rows are the sums of both halves) (offset 0
+    // means none: fdo is taken first for bf16)
     const bool need_g = gate && d->dlog_alpha;
-    const bool dots = bf && !split && (need_g || d->dlog_ig);
+    const bool dots = bf && (need_g || d->dlog_ig);
     p->dqp = (dots && need_g) ? take((Dk / 64) * bh * L * 4) : 0;
     p->dkp = dots ? take((Dk / 64) * bh * L * 4) : 0;
     const int kd = split ? kDvHalf : d->Dv;  // key dimension of the dk and dq passes
@@ -898,6 +899,14 @@ int gla_bwd(const gla_bwd_desc *d, void *stream) {
                                    V(p.s0h), st_half, size_t(BH), st_half, s));
             OutMapArgs om_k = om_rev, om_d = om_q;
             om_k.acc = om_d.acc = hh;
+            if (hh == 1 && p.dkp) {
+                om_k.dot_src = d->k;
+                om_k.dot_out = F(p.dkp);
+            }
+            if (hh == 1 && p.dqp) {
+                om_d.dot_src = d->q;
+                om_d.dot_out = F(p.dqp);
+            }
             fwd(bwd_pass_desc(d, kDvHalf, Dk, V(p.vsl), V(p.dsl), rq, rgate, rla, nullptr,
                               d->dfinal_state ? F(p.s0h) : nullptr, d->dk, nullptr),
                 gla::kH16K, om_k);
