@@ -300,6 +300,7 @@ struct OutMapArgs {
     const void *dot_src = nullptr;  // dq and dk passes: rows to dot with the stored rows
     float *dot_out = nullptr;       // [Dv/64][BH][L] dot products per 64-column tile
     int state_t = 0;  // the workspace already holds the segment-entry states, transposed
+    int qk_stride = 0;  // elements between rows of the pass's q and k (0: its Dk)
 };
 
 // The forward pass; h16 marks operands given as fp16 instead of bf16 and om maps the output
@@ -358,6 +359,7 @@ int fwd_run(const gla_desc *d, int h16, void *stream, const OutMapArgs &om = Out
     a.dot_src = om.dot_src;
     a.dot_out = om.dot_out;
     a.state_t = om.state_t;
+    a.qk_stride = om.qk_stride;
     if (om.state_t && (!d->workspace || p.nseg < 2)) return GLA_ERR_INVALID_ARG;
 
     const hipError_t err = gla::launch_forward(a, d->in_dtype == GLA_DTYPE_F32, h16, d->Dk, s);
@@ -635,7 +637,7 @@ bool chan_dv_fast(const gla_bwd_desc *d) { return d->in_dtype == GLA_DTYPE_BF16 
 struct BwdPlan {
     size_t chs, rq, rk, rv, rdo, fdo, mx, mxp, s0A, lar, oA, oB, finA, finC, s0T, dfT, g, part, fws, total;
     size_t dqp, dkp;  // bf16: the dq and dk passes' dot products q . dq, k . dk per 64-column tile
-    size_t vsl, dsl, s0h, finH;  // Dv split: value and output-gradient halves, a state half, a final-state half
+    size_t s0h, finH;  // Dv split: a state half, a final-state half
     size_t fws_bytes;
 };
 
@@ -710,8 +712,6 @@ int bwd_plan(const gla_bwd_desc *d, BwdPlan *p) {
     p->dqp = (dots && need_g) ? take((Dk / 64) * bh * L * 4) : 0;
     p->dkp = dots ? take((Dk / 64) * bh * L * 4) : 0;
     const int kd = split ? kDvHalf : d->Dv;  // key dimension of the dk and dq passes
-    p->vsl = split ? take(bh * L * kDvHalf * 2) : 0;
-    p->dsl = split ? take(bh * L * kDvHalf * 2) : 0;
     p->s0h = split ? take(bh * kDvHalf * Dk * 4) : 0;
     p->finH = split ? take(bh * kDvHalf * Dk * 4) : 0;
     // the forward passes run one after the other on the stream and share one workspace
@@ -887,18 +887,18 @@ int gla_bwd(const gla_bwd_desc *d, void *stream) {
     } else {
         // the same two passes over each 256-column half of the values (and of the output
         // gradient): G splits by value columns, so dk and dq are the sums of the halves'
-        // outputs, and the dq pass's final state is the half's rows of the transposed final state
-        const size_t rows = size_t(BH) * L, half_bytes = size_t(kDvHalf) * 2, st_half = size_t(kDvHalf) * Dk * 4;
+        // outputs, and the dq pass's final state is the half's rows of the transposed final state.
+        // The passes read the halves in place: q and k rows of Dv elements, from column 256 hh.
+        const size_t half_bytes = size_t(kDvHalf) * 2, st_half = size_t(kDvHalf) * Dk * 4;
         for (int hh = 0; hh < 2 && rc == GLA_OK; ++hh) {
-            ok(gla::bwd_copy2d(static_cast<const char *>(d->v) + hh * half_bytes, size_t(Dv) * 2, V(p.vsl), half_bytes,
-                               rows, half_bytes, s));
-            ok(gla::bwd_copy2d(static_cast<const char *>(fdo) + hh * half_bytes, size_t(Dv) * 2, V(p.dsl), half_bytes,
-                               rows, half_bytes, s));
+            const void *vh = static_cast<const char *>(d->v) + hh * half_bytes;
+            const void *dh = static_cast<const char *>(fdo) + hh * half_bytes;
             if (d->dfinal_state)
                 ok(gla::bwd_copy2d(reinterpret_cast<const char *>(F(p.dfT)) + hh * st_half, size_t(Dv) * Dk * 4,
                                    V(p.s0h), st_half, size_t(BH), st_half, s));
             OutMapArgs om_k = om_rev, om_d = om_q;
             om_k.acc = om_d.acc = hh;
+            om_k.qk_stride = om_d.qk_stride = Dv;
             if (hh == 1 && p.dkp) {
                 om_k.dot_src = d->k;
                 om_k.dot_out = F(p.dkp);
@@ -907,13 +907,13 @@ int gla_bwd(const gla_bwd_desc *d, void *stream) {
                 om_d.dot_src = d->q;
                 om_d.dot_out = F(p.dqp);
             }
-            fwd(bwd_pass_desc(d, kDvHalf, Dk, V(p.vsl), V(p.dsl), rq, rgate, rla, nullptr,
+            fwd(bwd_pass_desc(d, kDvHalf, Dk, vh, dh, rq, rgate, rla, nullptr,
                               d->dfinal_state ? F(p.s0h) : nullptr, d->dk, nullptr),
                 gla::kH16K, om_k);
             if (d->initial_state)
                 ok(gla::bwd_copy2d(reinterpret_cast<const char *>(F(p.s0T)) + hh * st_half, size_t(Dv) * Dk * 4,
                                    V(p.s0h), st_half, size_t(BH), st_half, s));
-            fwd(bwd_pass_desc(d, kDvHalf, Dk, V(p.dsl), V(p.vsl), d->k, d->gate_kind, d->log_alpha, d->log_ig,
+            fwd(bwd_pass_desc(d, kDvHalf, Dk, dh, vh, d->k, d->gate_kind, d->log_alpha, d->log_ig,
                               d->initial_state ? F(p.s0h) : nullptr, d->dq, F(p.finH)),
                 gla::kH16Q, om_d);
             ok(gla::bwd_copy2d(V(p.finH), st_half, reinterpret_cast<char *>(F(p.finC)) + hh * st_half,

@@ -473,6 +473,7 @@ struct Rs {
     uint32_t gstride;  // bytes between the scalar gates of consecutive rows (0: one value or none)
     bool has_li;
     bool rev;          // backward-pass instances: token t reads q, k, v row L-1-t
+    uint32_t qks;      // backward-pass instances: elements between rows of q and k
 };
 
 // Row of q, k, v that token t reads.  Past the sequence end (t >= L) a reversed row is
@@ -496,8 +497,13 @@ __device__ __forceinline__ Rs make_rs(const KArgs &a, int bh, int h) {
     Rs r;
     const size_t bhL = (size_t)bh * a.L;
     const uint64_t L = (uint64_t)a.L;
-    r.q = make_rsrc(reinterpret_cast<const char *>(a.q) + bhL * C::DK * C::IB, L * C::DK * C::IB);
-    r.k = make_rsrc(reinterpret_cast<const char *>(a.k) + bhL * C::DK * C::IB, L * C::DK * C::IB);
+    size_t qs = C::DK;
+    if constexpr (C::H16 != 0) {
+        if (a.qk_stride) qs = (size_t)a.qk_stride;
+        r.qks = (uint32_t)qs;
+    }
+    r.q = make_rsrc(reinterpret_cast<const char *>(a.q) + bhL * qs * C::IB, L * qs * C::IB);
+    r.k = make_rsrc(reinterpret_cast<const char *>(a.k) + bhL * qs * C::IB, L * qs * C::IB);
     r.v = make_rsrc(reinterpret_cast<const char *>(a.v) + bhL * a.Dv * C::IB, L * a.Dv * C::IB);
     r.out = make_rsrc(a.out + bhL * a.Dv, L * a.Dv * 4);
     if (a.gate == GLA_GATE_CHANNEL)
@@ -521,9 +527,11 @@ template <class C, bool WQ>
 __device__ __forceinline__ void load_unit(Raw<C> &r, const Rs &rs, int T0, int sl, int w, int lane, int tid, int dv0,
                                           int Dv) {
     const int ch0 = sl * C::SLAB + C::CPL * lane;
+    uint32_t qks = C::DK;
+    if constexpr (C::H16 != 0) qks = rs.qks;
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) {
-        const uint32_t off = (in_row<C>(rs, T0 + 16 * w + rr) * C::DK + ch0) * C::IB;
+        const uint32_t off = (in_row<C>(rs, T0 + 16 * w + rr) * qks + ch0) * C::IB;
         if constexpr (C::CPL == 2 || C::F32) {
             if constexpr (WQ) r.q[rr] = bld32(rs.q, off);
             r.k[rr] = bld32(rs.k, off);
@@ -2050,9 +2058,11 @@ struct RawSg {
 template <class C>
 __device__ __forceinline__ void load_unit_sg(RawSg<C> &r, const Rs &rs, int T0, int pw, int lane, int dv0, int Dv) {
     const int ch0 = 4 * lane;  // a wave's load covers one whole row
+    uint32_t qks = C::DK;
+    if constexpr (C::H16 != 0) qks = rs.qks;
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) {
-        const uint32_t off = (in_row<C>(rs, T0 + 16 * pw + rr) * C::DK + ch0) * 2u;
+        const uint32_t off = (in_row<C>(rs, T0 + 16 * pw + rr) * qks + ch0) * 2u;
         r.q[rr] = bld64(rs.q, off);
         r.k[rr] = bld64(rs.k, off);
     }
@@ -2612,6 +2622,10 @@ static hipError_t ensure_lds_limit(const void *fn, std::atomic<uint64_t> &done) 
 template <class C>
 static hipError_t launch_cfg(const KArgs &a, hipStream_t st) {
     hipError_t err;
+    // a row stride for q and k is read by the backward instances of the scalar-gate Dk = 256
+    // kernel only
+    if (a.qk_stride != 0 && !(C::H16 != 0 && !C::F32 && !C::CH && !C::MT && C::DK == 256))
+        return hipErrorInvalidValue;
     // entry states given (state_t): only the chunk-output kernel runs
     if (a.nseg > 1 && !a.state_t) {
         const LdsPlanState l1 = lds_plan_state(C::OPB, C::DK);

@@ -280,6 +280,9 @@ struct KArgs {
     // Segment-entry states given: entry s*nsub-1 of ws_state already holds the state entering
     // segment s (prepared by the caller); the segment-state kernel and the scan do not run.
     int state_t;
+    // Backward instances of the Dk = 256 scalar-gate kernel: elements between consecutive rows
+    // of q and k (0: Dk), so a pass reads a column half of wider rows in place.
+    int qk_stride;
 };
 
 #if defined(__HIPCC__)
