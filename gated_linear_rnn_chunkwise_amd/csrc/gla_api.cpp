@@ -68,18 +68,36 @@ struct Plan {
 inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 inline size_t align256(size_t x) { return (x + 255u) & ~size_t(255u); }
 
+// An empty call (B, H or L zero) has no output rows, and the state after no tokens is the
+// state before them.  Its per-token arrays may be NULL.
+inline bool empty_call(int64_t B, int64_t H, int64_t L) { return B == 0 || H == 0 || L == 0; }
+
+// dst[i] = src[i], or 0 without src, for i < n: the final state of an empty sequence.
+__global__ __launch_bounds__(256) void state_copy_kernel(float *dst, const float *src, size_t n) {
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256)
+        dst[i] = src ? src[i] : 0.f;
+}
+int state_copy(float *dst, const float *src, size_t n, void *stream) {
+    if (!dst || n == 0) return GLA_OK;
+    const size_t blocks = std::min<size_t>((n + 255) / 256, 65536);
+    hipLaunchKernelGGL(state_copy_kernel, dim3((unsigned)blocks), dim3(256), 0, reinterpret_cast<hipStream_t>(stream),
+                       dst, src, n);
+    return hipGetLastError() == hipSuccess ? GLA_OK : GLA_ERR_HIP;
+}
+
 // Argument checks (no HIP call).  Returns GLA_OK or an error status.
 int validate(const gla_desc *d) {
     if (!d) return GLA_ERR_INVALID_ARG;
-    if (!d->q || !d->k || !d->v || !d->out) return GLA_ERR_INVALID_ARG;
-    if (d->B <= 0 || d->H <= 0 || d->L <= 0 || d->Dk <= 0 || d->Dv <= 0 || d->chunk <= 0) return GLA_ERR_INVALID_ARG;
+    if (d->B < 0 || d->H < 0 || d->L < 0 || d->Dk <= 0 || d->Dv <= 0 || d->chunk <= 0) return GLA_ERR_INVALID_ARG;
+    const bool empty = empty_call(d->B, d->H, d->L);
+    if (!empty && (!d->q || !d->k || !d->v || !d->out)) return GLA_ERR_INVALID_ARG;
     if (d->seg_chunks < 0 || (d->flags & ~int32_t(GLA_FLAG_TILE_PAIRS | GLA_FLAG_QUERY_TILES)) != 0)
         return GLA_ERR_INVALID_ARG;
     // query tiles make every chunk its own segment
     if ((d->flags & GLA_FLAG_QUERY_TILES) && d->seg_chunks > 1) return GLA_ERR_INVALID_ARG;
     if (d->in_dtype != GLA_DTYPE_BF16 && d->in_dtype != GLA_DTYPE_F32) return GLA_ERR_INVALID_ARG;
     if (d->gate_kind < GLA_GATE_NONE || d->gate_kind > GLA_GATE_HEAD_CONST) return GLA_ERR_INVALID_ARG;
-    if ((d->gate_kind == GLA_GATE_NONE) != (d->log_alpha == nullptr)) return GLA_ERR_INVALID_ARG;
+    if (!empty && (d->gate_kind == GLA_GATE_NONE) != (d->log_alpha == nullptr)) return GLA_ERR_INVALID_ARG;
     const void *ptrs[] = {d->q, d->k, d->v, d->out, d->log_alpha, d->log_ig, d->initial_state, d->final_state,
                           d->workspace};
     for (const void *p : ptrs)
@@ -96,6 +114,7 @@ int validate(const gla_desc *d) {
 
 // Support matrix and launch plan.  Returns GLA_OK, GLA_ERR_UNSUPPORTED.
 int make_plan(const gla_desc *d, Plan *p) {
+    if (empty_call(d->B, d->H, d->L)) return GLA_ERR_INVALID_ARG;  // entry points handle empty calls first
     if (d->Dk != 64 && d->Dk != 128 && d->Dk != 256) return GLA_ERR_UNSUPPORTED;
     if (d->Dv % gla::kDvTile != 0 || d->Dv > 4096) return GLA_ERR_UNSUPPORTED;
     // Chunks of 16 and 32 tokens run as 64-token tiles: the state is carried per tile, which
@@ -227,6 +246,34 @@ int pad_plan(const gla_desc *d, PadPlan *pp) {
 
 }  // namespace
 
+// The support check of an empty call: the same shape with one token of one (batch, head).
+int empty_support(const gla_desc *d) {
+    gla_desc one = *d;
+    one.B = one.H = one.L = 1;
+    const void *x = reinterpret_cast<const void *>(uintptr_t(256));
+    float *y = reinterpret_cast<float *>(uintptr_t(256));
+    one.q = one.k = one.v = x;
+    one.out = y;
+    one.log_alpha = d->gate_kind == GLA_GATE_NONE ? nullptr : y;
+    one.log_ig = d->log_ig ? y : nullptr;
+    one.workspace = nullptr;
+    one.workspace_bytes = 0;
+    if (native_shape(&one)) {
+        Plan p;
+        return make_plan(&one, &p);
+    }
+    PadPlan pp;
+    return pad_plan(&one, &pp);
+}
+
+// An empty forward call: the final state (when asked for) is the initial state, or zero.
+int fwd_empty(const gla_desc *d, void *stream) {
+    const int st = empty_support(d);
+    if (st != GLA_OK) return st;
+    if (d->L != 0) return GLA_OK;  // no (batch, head) slices
+    return state_copy(d->final_state, d->initial_state, size_t(d->B) * d->H * d->Dk * d->Dv, stream);
+}
+
 extern "C" {
 
 int gla_version(void) { return GLA_VERSION; }
@@ -246,6 +293,11 @@ int gla_workspace_size(const gla_desc *d, size_t *bytes) {
     if (!bytes) return GLA_ERR_INVALID_ARG;
     int st = validate(d);
     if (st != GLA_OK) return st;
+    if (empty_call(d->B, d->H, d->L)) {
+        if ((st = empty_support(d)) != GLA_OK) return st;
+        *bytes = 0;
+        return GLA_OK;
+    }
     if (!native_shape(d)) {
         PadPlan pp;
         if ((st = pad_plan(d, &pp)) != GLA_OK) return st;
@@ -262,6 +314,11 @@ int gla_query_plan(const gla_desc *d, gla_plan *out) {
     if (!out) return GLA_ERR_INVALID_ARG;
     int st = validate(d);
     if (st != GLA_OK) return st;
+    if (empty_call(d->B, d->H, d->L)) {
+        if ((st = empty_support(d)) != GLA_OK) return st;
+        *out = gla_plan{};  // nothing runs
+        return GLA_OK;
+    }
     Plan p;
     size_t ws_total = 0;
     if (!native_shape(d)) {
@@ -440,6 +497,7 @@ int fwd_padded(const gla_desc *d, const PadPlan &pp, char *ws, void *stream) {
 int fwd_entry(const gla_desc *d, void *stream) {
     int st = validate(d);
     if (st != GLA_OK) return st;
+    if (empty_call(d->B, d->H, d->L)) return fwd_empty(d, stream);
     if (native_shape(d)) return fwd_run(d, 0, stream);
     PadPlan pp;
     if ((st = pad_plan(d, &pp)) != GLA_OK) return st;
@@ -505,6 +563,7 @@ int gla_fwd_noalloc(const gla_desc *d, void *stream) {
     int st = validate(d);
     if (st != GLA_OK) return st;
     if (d->workspace != nullptr || d->workspace_bytes != 0) return GLA_ERR_INVALID_ARG;
+    if (empty_call(d->B, d->H, d->L)) return fwd_empty(d, stream);
     if (!native_shape(d)) {
         PadPlan pp;
         if ((st = pad_plan(d, &pp)) != GLA_OK) return st;
@@ -528,10 +587,12 @@ int gla_fwd_noalloc(const gla_desc *d, void *stream) {
 }
 
 int gla_step(const gla_step_desc *d, void *stream) {
-    if (!d || !d->q || !d->k || !d->v || !d->state || !d->out) return GLA_ERR_INVALID_ARG;
-    if (d->B <= 0 || d->H <= 0 || d->Dk <= 0 || d->Dv <= 0) return GLA_ERR_INVALID_ARG;
+    if (!d) return GLA_ERR_INVALID_ARG;
+    if (d->B < 0 || d->H < 0 || d->Dk <= 0 || d->Dv <= 0) return GLA_ERR_INVALID_ARG;
     if (d->in_dtype != GLA_DTYPE_BF16 && d->in_dtype != GLA_DTYPE_F32) return GLA_ERR_INVALID_ARG;
     if (d->gate_kind < GLA_GATE_NONE || d->gate_kind > GLA_GATE_HEAD_CONST) return GLA_ERR_INVALID_ARG;
+    if (int64_t(d->B) * d->H == 0) return GLA_OK;  // no sequences to advance
+    if (!d->q || !d->k || !d->v || !d->state || !d->out) return GLA_ERR_INVALID_ARG;
     if ((d->gate_kind == GLA_GATE_NONE) != (d->log_alpha == nullptr)) return GLA_ERR_INVALID_ARG;
     const void *ptrs[] = {d->q, d->k, d->v, d->log_alpha, d->log_ig, d->state, d->out};
     for (const void *p : ptrs)
@@ -582,13 +643,15 @@ bool bwd_split_dv(const gla_bwd_desc *d) {
 }
 
 int validate_bwd(const gla_bwd_desc *d) {
-    if (!d || !d->q || !d->k || !d->v || !d->dout || !d->dq || !d->dk || !d->dv) return GLA_ERR_INVALID_ARG;
-    if (d->B <= 0 || d->H <= 0 || d->L <= 0 || d->Dk <= 0 || d->Dv <= 0) return GLA_ERR_INVALID_ARG;
+    if (!d) return GLA_ERR_INVALID_ARG;
+    if (d->B < 0 || d->H < 0 || d->L < 0 || d->Dk <= 0 || d->Dv <= 0) return GLA_ERR_INVALID_ARG;
+    const bool empty = empty_call(d->B, d->H, d->L);
+    if (!empty && (!d->q || !d->k || !d->v || !d->dout || !d->dq || !d->dk || !d->dv)) return GLA_ERR_INVALID_ARG;
     if (d->in_dtype != GLA_DTYPE_BF16 && d->in_dtype != GLA_DTYPE_F32) return GLA_ERR_INVALID_ARG;
     if (d->gate_kind < GLA_GATE_NONE || d->gate_kind > GLA_GATE_HEAD_CONST) return GLA_ERR_INVALID_ARG;
-    if ((d->gate_kind == GLA_GATE_NONE) != (d->log_alpha == nullptr)) return GLA_ERR_INVALID_ARG;
+    if (!empty && (d->gate_kind == GLA_GATE_NONE) != (d->log_alpha == nullptr)) return GLA_ERR_INVALID_ARG;
     if (d->gate_kind == GLA_GATE_NONE && d->dlog_alpha) return GLA_ERR_INVALID_ARG;
-    if (d->dlog_ig && !d->log_ig) return GLA_ERR_INVALID_ARG;
+    if (!empty && d->dlog_ig && !d->log_ig) return GLA_ERR_INVALID_ARG;
     const void *ptrs[] = {d->q, d->k, d->v, d->log_alpha, d->log_ig, d->initial_state, d->dout, d->dfinal_state,
                           d->dq, d->dk, d->dv, d->dlog_alpha, d->dlog_ig, d->dinitial_state, d->workspace};
     for (const void *p : ptrs)
@@ -741,6 +804,10 @@ int gla_bwd_workspace_size(const gla_bwd_desc *d, size_t *bytes) {
     if (!bytes) return GLA_ERR_INVALID_ARG;
     int st = validate_bwd(d);
     if (st != GLA_OK) return st;
+    if (empty_call(d->B, d->H, d->L)) {
+        *bytes = 0;
+        return GLA_OK;
+    }
     BwdPlan p;
     if ((st = bwd_plan(d, &p)) != GLA_OK) return st;
     *bytes = p.total;
@@ -750,6 +817,16 @@ int gla_bwd_workspace_size(const gla_bwd_desc *d, size_t *bytes) {
 int gla_bwd(const gla_bwd_desc *d, void *stream) {
     int st = validate_bwd(d);
     if (st != GLA_OK) return st;
+    if (empty_call(d->B, d->H, d->L)) {
+        // no tokens: the final state is the initial state, so its gradient passes through
+        // unchanged, and a fixed per-head gate acted on nothing (its gradient is zero); the
+        // per-token gradients have no rows
+        if (d->L != 0) return GLA_OK;
+        st = state_copy(d->dinitial_state, d->dfinal_state, size_t(d->B) * d->H * d->Dk * d->Dv, stream);
+        if (st == GLA_OK && d->gate_kind == GLA_GATE_HEAD_CONST)
+            st = state_copy(d->dlog_alpha, nullptr, size_t(d->H), stream);
+        return st;
+    }
     BwdPlan p;
     if ((st = bwd_plan(d, &p)) != GLA_OK) return st;
     if (d->workspace && d->workspace_bytes < p.total) return GLA_ERR_WORKSPACE;
@@ -933,12 +1010,14 @@ int gla_bwd(const gla_bwd_desc *d, void *stream) {
 // Delta rule (delta_kernels.hip).
 
 extern "C" int gla_delta_fwd(const gla_delta_desc *d, void *stream) {
-    if (!d || !d->q || !d->k || !d->v || !d->beta || !d->out) return GLA_ERR_INVALID_ARG;
-    if (d->B <= 0 || d->H <= 0 || d->L <= 0 || d->Dk <= 0 || d->Dv <= 0 || d->chunk <= 0) return GLA_ERR_INVALID_ARG;
+    if (!d) return GLA_ERR_INVALID_ARG;
+    if (d->B < 0 || d->H < 0 || d->L < 0 || d->Dk <= 0 || d->Dv <= 0 || d->chunk <= 0) return GLA_ERR_INVALID_ARG;
+    const bool empty = empty_call(d->B, d->H, d->L);
+    if (!empty && (!d->q || !d->k || !d->v || !d->beta || !d->out)) return GLA_ERR_INVALID_ARG;
     if (d->in_dtype != GLA_DTYPE_BF16 && d->in_dtype != GLA_DTYPE_F32) return GLA_ERR_INVALID_ARG;
     if (d->gate_kind != GLA_GATE_NONE && d->gate_kind != GLA_GATE_HEAD && d->gate_kind != GLA_GATE_HEAD_CONST)
         return d->gate_kind == GLA_GATE_CHANNEL ? GLA_ERR_UNSUPPORTED : GLA_ERR_INVALID_ARG;
-    if ((d->gate_kind == GLA_GATE_NONE) != (d->log_alpha == nullptr)) return GLA_ERR_INVALID_ARG;
+    if (!empty && (d->gate_kind == GLA_GATE_NONE) != (d->log_alpha == nullptr)) return GLA_ERR_INVALID_ARG;
     const void *ptrs[] = {d->q, d->k, d->v, d->beta, d->log_alpha, d->initial_state, d->out, d->final_state};
     for (const void *p : ptrs)
         if (p && !aligned16(p)) return GLA_ERR_INVALID_ARG;
@@ -957,6 +1036,8 @@ extern "C" int gla_delta_fwd(const gla_delta_desc *d, void *stream) {
     if (gla_delta::lds_bytes(f32, d->Dk) > gla::kMaxLds) return GLA_ERR_UNSUPPORTED;
     const int64_t nwg = bh * (d->Dv / 64);
     if (nwg > INT32_MAX) return GLA_ERR_UNSUPPORTED;
+    if (empty)  // the final state of no tokens is the initial state
+        return d->L == 0 ? state_copy(d->final_state, d->initial_state, size_t(bh) * d->Dk * d->Dv, stream) : GLA_OK;
     gla_delta::DeltaArgs a{};
     a.q = d->q;
     a.k = d->k;
@@ -981,8 +1062,10 @@ extern "C" int gla_delta_fwd(const gla_delta_desc *d, void *stream) {
 // mLSTM with exponential input gate and normaliser (mlstm_kernels.hip).
 
 extern "C" int gla_mlstm_fwd(const gla_mlstm_desc *d, void *stream) {
-    if (!d || !d->q || !d->k || !d->v || !d->log_f || !d->log_i || !d->out) return GLA_ERR_INVALID_ARG;
-    if (d->B <= 0 || d->H <= 0 || d->L <= 0 || d->Dk <= 0 || d->Dv <= 0 || d->chunk <= 0) return GLA_ERR_INVALID_ARG;
+    if (!d) return GLA_ERR_INVALID_ARG;
+    if (d->B < 0 || d->H < 0 || d->L < 0 || d->Dk <= 0 || d->Dv <= 0 || d->chunk <= 0) return GLA_ERR_INVALID_ARG;
+    const bool empty = empty_call(d->B, d->H, d->L);
+    if (!empty && (!d->q || !d->k || !d->v || !d->log_f || !d->log_i || !d->out)) return GLA_ERR_INVALID_ARG;
     if (d->reserved != 0) return GLA_ERR_INVALID_ARG;
     if (d->in_dtype != GLA_DTYPE_BF16 && d->in_dtype != GLA_DTYPE_F32) return GLA_ERR_INVALID_ARG;
     const int given = (d->initial_C != nullptr) + (d->initial_n != nullptr) + (d->initial_m != nullptr);
@@ -1007,6 +1090,14 @@ extern "C" int gla_mlstm_fwd(const gla_mlstm_desc *d, void *stream) {
     if (gla_mlstm::lds_bytes(f32, d->Dk, cols) > gla::kMaxLds) return GLA_ERR_UNSUPPORTED;
     const int64_t nwg = bh * (d->Dv / cols);
     if (nwg > INT32_MAX) return GLA_ERR_UNSUPPORTED;
+    if (empty) {
+        // the final state of no tokens is the initial state, or the zero state (C', n', m) = 0
+        if (d->L != 0) return GLA_OK;
+        int st = state_copy(d->final_C, d->initial_C, size_t(bh) * d->Dk * d->Dv, stream);
+        if (st == GLA_OK) st = state_copy(d->final_n, d->initial_n, size_t(bh) * d->Dk, stream);
+        if (st == GLA_OK) st = state_copy(d->final_m, d->initial_m, size_t(bh), stream);
+        return st;
+    }
     gla_mlstm::MlstmArgs a{};
     a.q = d->q;
     a.k = d->k;

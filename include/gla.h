@@ -40,6 +40,12 @@
  * gates are computed as given but may overflow.  NaN inputs propagate to the outputs.
  * Values are not checked on the host.
  *
+ * Empty calls.  B, H or L may be zero (none negative).  Such a call has no output rows, and
+ * the pointers of its per-token arrays may then be NULL; the state after no tokens is the
+ * state before them, so with L = 0 and B*H > 0 a final state asked for is the initial state
+ * (zero without one) and the backward's initial-state gradient is the final-state gradient,
+ * written by one small copy kernel.  Sizes, dtypes and the support matrix are still checked.
+ *
  * Asynchrony and errors.  Every call validates its arguments on the host before any HIP
  * call; on a validation error it returns a negative status, launches nothing and writes
  * nothing.  Otherwise it enqueues its kernels on `stream` (a hipStream_t; NULL is the
@@ -61,12 +67,13 @@
 extern "C" {
 #endif
 
-#define GLA_VERSION 10600 /* major * 10000 + minor * 100 + patch */
+#define GLA_VERSION 10700 /* major * 10000 + minor * 100 + patch */
 
 /* Status codes.  0 is success; errors are negative. */
 enum gla_status {
     GLA_OK = 0,
-    GLA_ERR_INVALID_ARG = -1, /* NULL required pointer, size <= 0, misaligned pointer,
+    GLA_ERR_INVALID_ARG = -1, /* NULL required pointer, a negative size (a zero Dk, Dv or
+                                 chunk), misaligned pointer,
                                  size product overflow, gate layout inconsistent with kind */
     GLA_ERR_UNSUPPORTED = -2, /* valid but outside the support matrix below */
     GLA_ERR_WORKSPACE = -3,   /* caller workspace too small, or workspace allocation failed */
@@ -158,7 +165,7 @@ int gla_fwd(const void *q, const void *k, const void *v, const float *log_alpha,
  * 4096.  Dk in {64, 128, 256} with Dv a multiple of 64 runs directly; other shapes run on
  * zero-padded copies in the workspace (q, k and a per-channel gate padded to the next Dk of
  * 64, 128, 256 with zero channels, v and the output to the next multiple of 64 columns, the
- * states to both; the same result, plus the copies' bytes and workspace); L >= 1 with
+ * states to both; the same result, plus the copies' bytes and workspace); L >= 0 with
  * (L + 1024) * max(Dk, Dv) * 4 < 2^32 (one (batch, head) slice is addressed with 32-bit
  * byte offsets, which allows L up to about 1M for Dv = 1024); and the operand tiles of
  * one workgroup must fit the 160 KB of LDS of a compute unit.  That last rule only bites
@@ -215,7 +222,8 @@ typedef struct gla_step_desc {
 
 /* Recurrent step.  Support matrix (else GLA_ERR_UNSUPPORTED): Dk in [1, 4096], Dv a
  * multiple of 16 up to 4096.  Validation as for gla_fwd_ex (GLA_ERR_INVALID_ARG for NULL
- * required pointers, sizes <= 0, misalignment, a gate pointer inconsistent with its kind).
+ * required pointers, negative B or H, Dk or Dv <= 0, misalignment, a gate pointer
+ * inconsistent with its kind; B*H = 0 advances no sequence and returns GLA_OK).
  * The state must not alias q, k, v, the gates or the output.  Asynchronous on `stream`;
  * allocates nothing.  Returns a gla_status. */
 int gla_step(const gla_step_desc *d, void *stream);
@@ -362,7 +370,7 @@ typedef struct gla_mlstm_desc {
 /* mLSTM forward pass.  Support matrix (else GLA_ERR_UNSUPPORTED): chunk 64; bf16 inputs with
  * Dk in {64, 128, 256}, fp32 inputs with Dk = 64; Dv a multiple of 64 up to 4096; L as for
  * gla_fwd_ex.  One workgroup per (batch, head, 64 value columns) walks the whole sequence.
- * GLA_ERR_INVALID_ARG: a NULL required pointer, non-positive sizes, a misaligned pointer
+ * GLA_ERR_INVALID_ARG: a NULL required pointer, negative sizes, a misaligned pointer
  * (16 bytes), reserved != 0, or an initial state given in part.  Ownership and asynchrony as
  * for gla_fwd_ex; allocates nothing.  Returns a gla_status. */
 int gla_mlstm_fwd(const gla_mlstm_desc *d, void *stream);

@@ -81,7 +81,7 @@ def test_valid_descriptor_plans(lib):
 
 @pytest.mark.parametrize("field,value", [
     ("q", None), ("k", None), ("v", None), ("out", None),
-    ("B", 0), ("H", -1), ("L", 0), ("Dk", 0), ("Dv", 0), ("chunk", 0), ("seg_chunks", -1), ("flags", 4), ("flags", -1),
+    ("B", -1), ("H", -1), ("L", -1), ("Dk", 0), ("Dv", 0), ("chunk", 0), ("seg_chunks", -1), ("flags", 4), ("flags", -1),
     ("in_dtype", 7), ("gate_kind", 9), ("log_alpha", None),
     ("q", A + 2), ("v", A + 8), ("out", A + 4), ("log_alpha", A + 4), ("final_state", A + 12),
     ("initial_state", A + 1), ("log_ig", A + 2),
@@ -111,7 +111,7 @@ def test_null_descriptor_and_outputs(lib):
 def test_headline_entry_point_validates(lib):
     # gla_fwd(q, k, v, log_alpha, out, final_state, B, H, L, Dk, Dv, chunk, stream)
     assert lib.gla_fwd(None, A, A, A, A, None, 1, 1, 64, 128, 128, 64, None) == gla.GLA_ERR_INVALID_ARG
-    assert lib.gla_fwd(A, A, A, A, A, None, 1, 1, 0, 128, 128, 64, None) == gla.GLA_ERR_INVALID_ARG
+    assert lib.gla_fwd(A, A, A, A, A, None, 1, 1, -1, 128, 128, 64, None) == gla.GLA_ERR_INVALID_ARG
     assert lib.gla_fwd(A, A, A, A, A + 4, None, 1, 1, 64, 128, 128, 64, None) == gla.GLA_ERR_INVALID_ARG
     assert lib.gla_fwd(A, A, A, A, A, None, 1, 1, 64, 24, 128, 64, None) == gla.GLA_ERR_UNSUPPORTED
     assert lib.gla_fwd(A, A, A, A, A, None, 1, 1, 64, 272, 128, 64, None) == gla.GLA_ERR_UNSUPPORTED
@@ -278,7 +278,7 @@ def step_desc(**kw):
     return d
 
 
-@pytest.mark.parametrize("field,bad", [("B", 0), ("H", -1), ("Dk", 0), ("Dv", 0), ("in_dtype", 7), ("gate_kind", 9),
+@pytest.mark.parametrize("field,bad", [("B", -1), ("H", -1), ("Dk", 0), ("Dv", 0), ("in_dtype", 7), ("gate_kind", 9),
                                        ("q", None), ("state", None), ("out", None), ("v", A + 8)])
 def test_step_invalid_arguments(lib, field, bad):
     assert lib.gla_step(ctypes.byref(step_desc(**{field: bad})), None) == gla.GLA_ERR_INVALID_ARG
@@ -325,7 +325,7 @@ def test_bwd_valid_and_workspace_grows_with_length(lib):
     assert st == st2 == gla.GLA_OK and c2 > c1
 
 
-@pytest.mark.parametrize("kw", [dict(dq=None), dict(dout=None), dict(q=None), dict(L=0), dict(dq=A + 4),
+@pytest.mark.parametrize("kw", [dict(dq=None), dict(dout=None), dict(q=None), dict(L=-1), dict(dq=A + 4),
                                 dict(gate_kind=gla.GATE_NONE, log_alpha=None),  # dlog_alpha without a gate
                                 dict(dlog_ig=A),                                  # input-gate grad without one
                                 dict(gate_kind=9), dict(in_dtype=7)])
@@ -446,7 +446,7 @@ def delta_desc(**kw):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(q=None), gla.GLA_ERR_INVALID_ARG), (dict(beta=None), gla.GLA_ERR_INVALID_ARG),
-    (dict(out=None), gla.GLA_ERR_INVALID_ARG), (dict(L=0), gla.GLA_ERR_INVALID_ARG),
+    (dict(out=None), gla.GLA_ERR_INVALID_ARG), (dict(L=-1), gla.GLA_ERR_INVALID_ARG),
     (dict(gate_kind=gla.GATE_NONE), gla.GLA_ERR_INVALID_ARG),  # gate pointer given without a gate
     (dict(log_alpha=None), gla.GLA_ERR_INVALID_ARG),  # gate kind without a pointer
     (dict(beta=A + 4), gla.GLA_ERR_INVALID_ARG), (dict(in_dtype=7), gla.GLA_ERR_INVALID_ARG),
@@ -485,7 +485,7 @@ def mlstm_desc(**kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(q=None), gla.GLA_ERR_INVALID_ARG), (dict(log_f=None), gla.GLA_ERR_INVALID_ARG),
     (dict(log_i=None), gla.GLA_ERR_INVALID_ARG), (dict(out=None), gla.GLA_ERR_INVALID_ARG),
-    (dict(L=0), gla.GLA_ERR_INVALID_ARG), (dict(Dv=-64), gla.GLA_ERR_INVALID_ARG),
+    (dict(L=-1), gla.GLA_ERR_INVALID_ARG), (dict(Dv=-64), gla.GLA_ERR_INVALID_ARG),
     (dict(reserved=1), gla.GLA_ERR_INVALID_ARG), (dict(in_dtype=7), gla.GLA_ERR_INVALID_ARG),
     (dict(initial_C=A), gla.GLA_ERR_INVALID_ARG),  # an initial state given in part
     (dict(initial_C=A, initial_n=A), gla.GLA_ERR_INVALID_ARG),
@@ -560,3 +560,39 @@ def test_backward_dv512_support(lib, kw, status):
     assert lib.gla_bwd_workspace_size(ctypes.byref(bwd_desc(**kw)), ctypes.byref(n)) == status
     if status == gla.GLA_OK:
         assert n.value > 0
+
+
+# ------------------------------------------------------------------------------ empty calls
+# B, H or L of zero: no output rows, and the state after no tokens is the state before them.
+# Without a final state to write, an empty call does no device work at all, so it runs here.
+@pytest.mark.parametrize("kw", [dict(L=0), dict(B=0), dict(H=0), dict(B=0, L=0)])
+def test_empty_calls_plan_nothing(lib, kw):
+    d = desc(q=None, k=None, v=None, out=None, log_alpha=None, **kw)  # per-token arrays may be NULL
+    st, n = status(lib, d)
+    assert st == gla.GLA_OK and n == 0
+    p = gla.plan(d)
+    assert p.n_seg == 0 and p.grid_out == 0 and p.grid_state == 0 and p.workspace_bytes == 0
+    assert fwd_status(lib, d) == gla.GLA_OK
+    assert lib.gla_fwd_noalloc(ctypes.byref(d), None) == gla.GLA_OK
+    assert lib.gla_fwd(None, None, None, None, None, None, 1, 1, 0, 128, 128, 64, None) == gla.GLA_OK
+
+
+def test_empty_calls_keep_the_support_matrix_and_argument_checks(lib):
+    assert status(lib, desc(L=0, Dk=24))[0] == gla.GLA_ERR_UNSUPPORTED
+    assert status(lib, desc(L=0, chunk=48))[0] == gla.GLA_ERR_UNSUPPORTED
+    assert status(lib, desc(L=0, in_dtype=7))[0] == gla.GLA_ERR_INVALID_ARG
+    assert status(lib, desc(L=0, final_state=A + 4))[0] == gla.GLA_ERR_INVALID_ARG
+
+
+def test_empty_step_delta_mlstm_backward(lib):
+    sd = step_desc(B=0, q=None, k=None, v=None, state=None, out=None)
+    assert lib.gla_step(ctypes.byref(sd), None) == gla.GLA_OK
+    assert lib.gla_delta_fwd(ctypes.byref(delta_desc(L=0, q=None, k=None, v=None, beta=None, out=None)),
+                             None) == gla.GLA_OK
+    assert lib.gla_delta_fwd(ctypes.byref(delta_desc(L=0, Dk=96)), None) == gla.GLA_ERR_UNSUPPORTED
+    assert lib.gla_mlstm_fwd(ctypes.byref(mlstm_desc(L=0, q=None, k=None, v=None, log_f=None, log_i=None,
+                                                     out=None)), None) == gla.GLA_OK
+    bd = bdesc(L=0, q=None, k=None, v=None, dout=None, dq=None, dk=None, dv=None, dlog_alpha=None)
+    st, n = bstatus(lib, bd)
+    assert st == gla.GLA_OK and n == 0
+    assert lib.gla_bwd(ctypes.byref(bd), None) == gla.GLA_OK

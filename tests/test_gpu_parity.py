@@ -516,3 +516,57 @@ def test_step_continues_chunkwise_forward(gpu_lib, gate, ig, chunk):
     ref, rfin = run_oracle(d, w)
     check(w, got, ref[:, :, L:])
     check(w, state.cpu().double().numpy(), rfin, "final_state")
+
+
+# ------------------------------------------------------------------------------ empty calls
+def test_empty_calls(gpu_lib):
+    # B, H or L of zero: no output rows, and the state after no tokens is the state before
+    # them, bit for bit (or zero without one); the backward passes the final-state gradient
+    # through to the initial state, and a fixed per-head gate gets a zero gradient
+    dev = "cuda"
+    g = torch.Generator().manual_seed(5)
+    s0 = torch.randn(2, 3, 128, 64, generator=g).to(dev)
+    q = torch.zeros(2, 3, 0, 128, dtype=torch.bfloat16, device=dev)
+    v = torch.zeros(2, 3, 0, 64, dtype=torch.bfloat16, device=dev)
+    for gate, la in (("channel", torch.zeros(2, 3, 0, 128, device=dev)), ("head", torch.zeros(2, 3, 0, device=dev)),
+                     ("head_const", torch.full((3,), -0.1, device=dev)), ("none", None)):
+        out, fin = gpu_lib.fwd(q, q, v, la, initial_state=s0, chunk=64)
+        torch.cuda.synchronize()
+        assert out.shape == (2, 3, 0, 64), gate
+        assert torch.equal(fin, s0), gate
+        out, fin = gpu_lib.fwd(q, q, v, la, chunk=64)
+        torch.cuda.synchronize()
+        assert torch.count_nonzero(fin).item() == 0, gate
+    # no (batch, head) slices
+    out, fin = gpu_lib.fwd(q[:0], q[:0], v[:0], None, chunk=64)
+    torch.cuda.synchronize()
+    assert out.numel() == 0 and fin.numel() == 0
+    # delta rule
+    beta = torch.zeros(2, 3, 0, device=dev)
+    o, fin = gpu_lib.delta_fwd(q, q, v, beta, torch.zeros(2, 3, 0, device=dev), initial_state=s0)
+    torch.cuda.synchronize()
+    assert o.shape == (2, 3, 0, 64) and torch.equal(fin, s0)
+    # mLSTM: the stabilised state (C', n', m) passes through, or is zero
+    n0 = torch.randn(2, 3, 128, generator=g).to(dev)
+    m0 = torch.randn(2, 3, generator=g).to(dev)
+    lz = torch.zeros(2, 3, 0, device=dev)
+    h, (C, n, m) = gpu_lib.mlstm_fwd(q, q, v, lz, lz, initial_state=(s0, n0, m0))
+    torch.cuda.synchronize()
+    assert h.shape == (2, 3, 0, 64) and torch.equal(C, s0) and torch.equal(n, n0) and torch.equal(m, m0)
+    h, (C, n, m) = gpu_lib.mlstm_fwd(q, q, v, lz, lz)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(C).item() == torch.count_nonzero(n).item() == torch.count_nonzero(m).item() == 0
+    # backward
+    df = torch.randn(2, 3, 128, 64, generator=g).to(dev)
+    la = torch.full((3,), -0.1, device=dev)
+    r = gpu_lib.bwd(q, q, v, torch.zeros(2, 3, 0, 64, device=dev), la, initial_state=s0, dfinal_state=df)
+    torch.cuda.synchronize()
+    assert r["dq"].shape == (2, 3, 0, 128) and r["dv"].shape == (2, 3, 0, 64)
+    assert torch.equal(r["dinitial_state"], df)
+    assert torch.count_nonzero(r["dlog_alpha"]).item() == 0 and r["dlog_alpha"].shape == (3,)
+    # a decode step over no sequences
+    st = torch.zeros(0, 3, 128, 64, device=dev)
+    o = gpu_lib.step(q[:0, :, 0:0].reshape(0, 3, 128), q[:0, :, 0:0].reshape(0, 3, 128),
+                     v[:0, :, 0:0].reshape(0, 3, 64), st, None)
+    torch.cuda.synchronize()
+    assert o.numel() == 0
