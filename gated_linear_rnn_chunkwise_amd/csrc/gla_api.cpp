@@ -1061,6 +1061,150 @@ extern "C" int gla_delta_fwd(const gla_delta_desc *d, void *stream) {
 // ------------------------------------------------------------------------------------
 // mLSTM with exponential input gate and normaliser (mlstm_kernels.hip).
 
+namespace {
+
+// Sequence segments of the mLSTM for small B*H with long sequences.  The segments run as extra
+// heads of a sequence Ls = L / nseg tokens long ([B, H, L] viewed as [B, H*nseg, Ls]): a first
+// pass from the zero state gives every segment's own stabilised state (its outputs are
+// overwritten later), a join carries the state across the segments, and a second pass runs every
+// segment from the state entering it.  The state is C = e^m C', n = e^m n'; across segment s,
+// whose log forget gates sum to F_s, the entering state (C'_e, n'_e, m_e) and the segment's own
+// (C'_l, n'_l, m_l) join as m = max(F_s + m_e, m_l), C' = e^(F_s + m_e - m) C'_e + e^(m_l - m) C'_l
+// (and n' alike).
+constexpr float kNoState = -1.0e30f;  // m of the zero state: every weight against it is 0
+
+// Segments for a launch of nwg workgroups over L tokens: 1 (one walk) when the grid is
+// already half full, the length is not whole 64-token tiles, or a walk is short; else the
+// largest divisor of the tile count that brings the grid nearest to one workgroup per CU.
+int mlstm_segments(int64_t nwg, int L) {
+    if (nwg >= 128 || L % 64 != 0 || L / 64 < 32) return 1;
+    const int tiles = L / 64;
+    const int64_t target = std::max<int64_t>(2, 256 / nwg);
+    int best = 1;
+    for (int n = 2; n <= tiles && n <= target; ++n)
+        if (tiles % n == 0) best = n;
+    return best;
+}
+
+__global__ __launch_bounds__(256) void mlstm_fsum_kernel(const float *lf, float *F, int Ls) {
+    __shared__ float red[256];
+    const float *p = lf + (size_t)blockIdx.x * Ls;
+    float x = 0.f;
+    for (int i = (int)threadIdx.x; i < Ls; i += 256) x += p[i];
+    red[threadIdx.x] = x;
+    __syncthreads();
+    for (int o = 128; o > 0; o >>= 1) {
+        if ((int)threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) F[blockIdx.x] = red[0];
+}
+
+// One thread per element of a slice's state (C', then n', then m): the states entering the
+// segments, in order, from the initial state (or the zero state).
+__global__ __launch_bounds__(256) void mlstm_join_kernel(const float *F, const float *lC, const float *ln,
+                                                         const float *lm, const float *c0, const float *n0,
+                                                         const float *m0, float *eC, float *en, float *em, int S,
+                                                         size_t nC, size_t nN, size_t total) {
+    const size_t per = nC + nN + 1;
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (size_t)gridDim.x * 256) {
+        const size_t bh = i / per, e = i % per;
+        float me = m0 ? m0[bh] : kNoState;
+        float x = 0.f;
+        if (e < nC) x = c0 ? c0[bh * nC + e] : 0.f;
+        else if (e < nC + nN) x = n0 ? n0[bh * nN + (e - nC)] : 0.f;
+        for (int s = 0; s < S; ++s) {
+            const size_t r = bh * S + s;
+            float xl = 0.f;
+            if (e < nC) {
+                eC[r * nC + e] = x;
+                xl = lC[r * nC + e];
+            } else if (e < nC + nN) {
+                en[r * nN + (e - nC)] = x;
+                xl = ln[r * nN + (e - nC)];
+            } else {
+                em[r] = me;
+            }
+            const float md = F[r] + me, ml = lm[r];
+            const float mn = fmaxf(md, ml);
+            x = expf(md - mn) * x + expf(ml - mn) * xl;
+            me = mn;
+        }
+    }
+}
+
+// The final state: the state after the last segment of each slice.
+__global__ __launch_bounds__(256) void mlstm_last_kernel(const float *lC, const float *ln, const float *lm, float *fC,
+                                                         float *fn, float *fm, int S, size_t nC, size_t nN,
+                                                         size_t total) {
+    const size_t per = nC + nN + 1;
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (size_t)gridDim.x * 256) {
+        const size_t bh = i / per, e = i % per, r = bh * S + S - 1;
+        if (e < nC) {
+            if (fC) fC[bh * nC + e] = lC[r * nC + e];
+        } else if (e < nC + nN) {
+            if (fn) fn[bh * nN + (e - nC)] = ln[r * nN + (e - nC)];
+        } else if (fm) {
+            fm[bh] = lm[r];
+        }
+    }
+}
+
+int mlstm_segmented(const gla_mlstm_desc *d, bool f32, int cols, int nseg, void *stream) {
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    const size_t bh = size_t(d->B) * d->H, S = size_t(nseg), nC = size_t(d->Dk) * d->Dv, nN = size_t(d->Dk);
+    const size_t rows = bh * S;
+    const size_t fl = rows + 2 * (rows * (nC + nN + 1));  // F, the segments' own states, the entering states
+    float *w = nullptr;
+    if (hipMallocAsync(reinterpret_cast<void **>(&w), fl * 4, st) != hipSuccess || !w) {
+        (void)hipGetLastError();
+        return GLA_ERR_WORKSPACE;
+    }
+    float *F = w, *lC = F + rows, *ln = lC + rows * nC, *lm = ln + rows * nN;
+    float *eC = lm + rows, *en = eC + rows * nC, *em = en + rows * nN;
+    gla_mlstm::MlstmArgs a{};
+    a.q = d->q;
+    a.k = d->k;
+    a.v = d->v;
+    a.lf = d->log_f;
+    a.li = d->log_i;
+    a.out = d->out;
+    a.fin_c = lC;
+    a.fin_n = ln;
+    a.fin_m = lm;
+    a.B = d->B;
+    a.H = d->H * nseg;
+    a.L = d->L / nseg;
+    a.Dv = d->Dv;
+    a.ndv = d->Dv / cols;
+    a.nwg = (int)(rows * a.ndv);
+    int rc = GLA_OK;
+    if (gla_mlstm::launch(a, f32, d->Dk, st) != hipSuccess) rc = GLA_ERR_HIP;
+    const size_t total = bh * (nC + nN + 1);
+    const unsigned blocks = (unsigned)std::min<size_t>((total + 255) / 256, 65536);
+    if (rc == GLA_OK) {
+        hipLaunchKernelGGL(mlstm_fsum_kernel, dim3((unsigned)rows), dim3(256), 0, st, d->log_f, F, a.L);
+        hipLaunchKernelGGL(mlstm_join_kernel, dim3(blocks), dim3(256), 0, st, F, lC, ln, lm, d->initial_C, d->initial_n,
+                           d->initial_m, eC, en, em, nseg, nC, nN, total);
+        if (hipGetLastError() != hipSuccess) rc = GLA_ERR_HIP;
+    }
+    if (rc == GLA_OK) {
+        a.c0 = eC;
+        a.n0 = en;
+        a.m0 = em;
+        if (gla_mlstm::launch(a, f32, d->Dk, st) != hipSuccess) rc = GLA_ERR_HIP;
+    }
+    if (rc == GLA_OK && (d->final_C || d->final_n || d->final_m)) {
+        hipLaunchKernelGGL(mlstm_last_kernel, dim3(blocks), dim3(256), 0, st, lC, ln, lm, d->final_C, d->final_n,
+                           d->final_m, nseg, nC, nN, total);
+        if (hipGetLastError() != hipSuccess) rc = GLA_ERR_HIP;
+    }
+    (void)hipFreeAsync(w, st);
+    return rc;
+}
+
+}  // namespace
+
 extern "C" int gla_mlstm_fwd(const gla_mlstm_desc *d, void *stream) {
     if (!d) return GLA_ERR_INVALID_ARG;
     if (d->B < 0 || d->H < 0 || d->L < 0 || d->Dk <= 0 || d->Dv <= 0 || d->chunk <= 0) return GLA_ERR_INVALID_ARG;
@@ -1098,6 +1242,8 @@ extern "C" int gla_mlstm_fwd(const gla_mlstm_desc *d, void *stream) {
         if (st == GLA_OK) st = state_copy(d->final_m, d->initial_m, size_t(bh), stream);
         return st;
     }
+    const int nseg = mlstm_segments(nwg, d->L);
+    if (nseg > 1) return mlstm_segmented(d, f32, cols, nseg, stream);
     gla_mlstm::MlstmArgs a{};
     a.q = d->q;
     a.k = d->k;

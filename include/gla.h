@@ -369,10 +369,15 @@ typedef struct gla_mlstm_desc {
 
 /* mLSTM forward pass.  Support matrix (else GLA_ERR_UNSUPPORTED): chunk 64; bf16 inputs with
  * Dk in {64, 128, 256}, fp32 inputs with Dk = 64; Dv a multiple of 64 up to 4096; L as for
- * gla_fwd_ex.  One workgroup per (batch, head, 64 value columns) walks the whole sequence.
- * GLA_ERR_INVALID_ARG: a NULL required pointer, negative sizes, a misaligned pointer
- * (16 bytes), reserved != 0, or an initial state given in part.  Ownership and asynchrony as
- * for gla_fwd_ex; allocates nothing.  Returns a gla_status. */
+ * gla_fwd_ex.  One workgroup per (batch, head, value slice) walks the whole sequence; when
+ * those are fewer than 128 and L is a multiple of 64 with at least 32 tiles, the sequence
+ * runs as segments instead (every segment's own state from zero, the states joined across the
+ * segments through their summed log forget gates, every segment again from the state entering
+ * it: about twice the work, on up to 256 workgroups).  GLA_ERR_INVALID_ARG: a NULL required
+ * pointer, negative sizes, a misaligned pointer (16 bytes), reserved != 0, or an initial state
+ * given in part.  Ownership and asynchrony as for gla_fwd_ex; allocates nothing, except the
+ * segmented form's scratch (the segment states, stream-ordered on `stream`; GLA_ERR_WORKSPACE
+ * if that fails).  Returns a gla_status. */
 int gla_mlstm_fwd(const gla_mlstm_desc *d, void *stream);
 
 /* Static English text for a status code (never NULL). */

@@ -181,3 +181,17 @@ def test_mlstm_full_workload_whole_tensor(gpu_lib, name):
     ec = check(w, Cg, C, "final C")
     en = check(w, ng, n, "final n")
     print("  out max|err|/RMS = %.3e, final C %.3e, final n %.3e" % (e, ec, en), flush=True)
+
+
+@pytest.mark.parametrize("dtype,B,H,L,Dk,Dv", [("bf16", 1, 2, 4096, 256, 512), ("bf16", 1, 1, 2048, 128, 128),
+                                               ("f32", 1, 1, 3072, 64, 64), ("bf16", 2, 3, 2560, 64, 128)])
+@pytest.mark.parametrize("with_s0", [False, True])
+def test_mlstm_sequence_segments(gpu_lib, dtype, B, H, L, Dk, Dv, with_s0):
+    # few (batch, head, value-slice) workgroups and a long sequence: the sequence runs as
+    # segments (a pass from the zero state for every segment's own state, the join across
+    # the segments, a pass from the entering states); outputs and final state against the oracle
+    w = gin.custom(B, H, L, Dk, Dv, 64, dtype=dtype, gate="head", rule="mlstm")
+    d = gin.make_inputs(w, seed=L + Dk)
+    s0 = rand_state(B, H, Dk, Dv, seed=3) if with_s0 else None
+    out, fin = run_gpu(gpu_lib, d, initial_state=s0)
+    check_all(w, out, fin, run_oracle(d, s0))
